@@ -1,0 +1,213 @@
+"""CPU oracle for hybrid decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The product path (``full_kv_cache_amd``)
+never imports, links or calls it, and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64); this module builds it
+with gcc and marshals numpy arrays through ctypes.  bf16 tensors travel as
+``numpy.uint16`` bit patterns.
+
+Parity status: every exported function is pinned by the ``-m "not gpu"``
+tests listed in its C header comment; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "oracle.c"
+_LIB = _HERE / "liboracle.so"
+
+SLIDING = 0
+FULL = 1
+
+_lib = None
+
+
+def build(force: bool = False) -> Path:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc and OpenMP."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp%d" % os.getpid())
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+             "-Wall", "-Wextra", "-o", str(tmp), str(_SRC), "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(str(_LIB))
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.or_bf16_to_f64.restype = f64
+        lib.or_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.or_f64_to_bf16.restype = ctypes.c_uint16
+        lib.or_f64_to_bf16.argtypes = [f64]
+        lib.or_cache_len.restype = i64
+        lib.or_cache_len.argtypes = [i32, i64, i32, i32]
+        lib.or_kv_cache_bytes.restype = None
+        lib.or_kv_cache_bytes.argtypes = [P, i32, i64, i32, i32, i32, i32, i32, P]
+        lib.or_ring_slot.restype = i64
+        lib.or_ring_slot.argtypes = [i64, i32]
+        lib.or_rope_angles.restype = None
+        lib.or_rope_angles.argtypes = [f64, i32, i64, P, P]
+        lib.or_rope_apply.restype = None
+        lib.or_rope_apply.argtypes = [P, P, i64, i32, i32, f64, i64]
+        lib.or_rope_append.restype = None
+        lib.or_rope_append.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f64,
+                                       i32, i64, P, P, P, P]
+        lib.or_decode_attn.restype = None
+        lib.or_decode_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                       i64, P, f64, P, P]
+        lib.or_attn_chunk.restype = None
+        lib.or_attn_chunk.argtypes = [P, P, P, i64, i64, i32, f64, P, P]
+        lib.or_lse_merge.restype = None
+        lib.or_lse_merge.argtypes = [P, P, i32, i32, P, P, P]
+        lib.or_sparse_decode_attn.restype = None
+        lib.or_sparse_decode_attn.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, i32,
+                                              P, f64, P, P]
+        lib.or_num_threads.restype = ctypes.c_int
+        lib.or_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- scalars
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (vectorised, same rule as C)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_scalar(x: float) -> int:
+    return int(_load().or_f64_to_bf16(float(x)))
+
+
+def cache_len(layer_type: int, context: int, window: int, ring: bool) -> int:
+    return int(_load().or_cache_len(layer_type, context, window, int(ring)))
+
+
+def kv_cache_bytes(layer_types, context, window, ring, kv_heads, head_dim, bytes_per_elem=2):
+    lt = _i32(layer_types)
+    out = np.zeros(2, dtype=np.int64)
+    _load().or_kv_cache_bytes(_p(lt), len(lt), context, window, int(ring), kv_heads,
+                              head_dim, bytes_per_elem, _p(out))
+    return {"hybrid": int(out[0]), "uniform": int(out[1])}
+
+
+def ring_slot(pos: int, window: int) -> int:
+    return int(_load().or_ring_slot(pos, window))
+
+
+def num_threads() -> int:
+    return int(_load().or_num_threads())
+
+
+# ------------------------------------------------------------------ RoPE
+
+def rope_angles(theta: float, rot: int, pos: int):
+    c = np.zeros(rot // 2, dtype=np.float32)
+    s = np.zeros(rot // 2, dtype=np.float32)
+    _load().or_rope_angles(theta, rot, pos, _p(c), _p(s))
+    return c, s
+
+
+def rope_apply(x_bits: np.ndarray, rot: int, theta: float, pos: int) -> np.ndarray:
+    """bf16 bits [..., D] -> rotated bf16 bits [..., D]."""
+    x = _u16(x_bits)
+    D = x.shape[-1]
+    y = np.empty_like(x)
+    _load().or_rope_apply(_p(x), _p(y), x.size // D, D, rot, theta, pos)
+    return y
+
+
+def rope_append(q, k_new, v_new, pos, layer_type, rot, theta, window, k, v, kev, vev):
+    """In place on numpy copies: q [B,Hq,D], k/v [B,Hkv,cap,D], kev/vev [B,Hkv,D]."""
+    for a in (q, k, v, kev, vev):
+        assert a.dtype == np.uint16 and a.flags.c_contiguous
+    k_new, v_new, pos = _u16(k_new), _u16(v_new), _i32(pos)
+    B, Hq, D = q.shape
+    Hkv, cap = k.shape[1], k.shape[2]
+    _load().or_rope_append(_p(q), _p(k_new), _p(v_new), _p(pos), layer_type, B, Hq, Hkv,
+                           D, rot, theta, window, cap, _p(k), _p(v), _p(kev), _p(vev))
+
+
+# ------------------------------------------------------------- attention
+
+def decode_attn(q, k, v, kev, vev, seq_lens, layer_type, window, sinks, scale):
+    """Returns (out fp64 [B,Hq,D], lse fp64 [B,Hq])."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    kev = _u16(kev) if kev is not None else None
+    vev = _u16(vev) if vev is not None else None
+    seq_lens = _i32(seq_lens)
+    sinks = _f32(sinks)
+    B, Hq, D = q.shape
+    Hkv, cap = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    _load().or_decode_attn(_p(q), _p(k), _p(v), _p(kev), _p(vev), _p(seq_lens), layer_type,
+                           B, Hq, Hkv, D, window, cap, _p(sinks), scale, _p(out), _p(lse))
+    return out, lse
+
+
+def attn_chunk(qh, kblk, vblk, r0, r1, scale):
+    qh, kblk, vblk = _u16(qh), _u16(kblk), _u16(vblk)
+    D = qh.shape[-1]
+    out = np.zeros(D, dtype=np.float64)
+    lse = np.zeros(1, dtype=np.float64)
+    _load().or_attn_chunk(_p(qh), _p(kblk), _p(vblk), r0, r1, D, scale, _p(out), _p(lse))
+    return out, float(lse[0])
+
+
+def lse_merge(o_parts, lse_parts, sink=None):
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    S, D = o_parts.shape
+    out = np.zeros(D, dtype=np.float64)
+    lse = np.zeros(1, dtype=np.float64)
+    sk = None if sink is None else np.array([sink], dtype=np.float32)
+    _load().or_lse_merge(_p(o_parts), _p(lse_parts), S, D, _p(sk), _p(out), _p(lse))
+    return out, float(lse[0])
+
+
+def sparse_decode_attn(q, kv, indices, topk_length, sinks, scale, dv):
+    """q bf16 [T,Hq,Dqk], kv bf16 [N,Dqk], indices int32 [T,topk]."""
+    q, kv, indices = _u16(q), _u16(kv), _i32(indices)
+    tl = None if topk_length is None else _i32(topk_length)
+    sinks = _f32(sinks)
+    T, Hq, Dqk = q.shape
+    N = kv.shape[0]
+    topk = indices.shape[1]
+    out = np.zeros((T, Hq, dv), dtype=np.float64)
+    lse = np.zeros((T, Hq), dtype=np.float64)
+    _load().or_sparse_decode_attn(_p(q), _p(kv), N, _p(indices), topk, _p(tl), T, Hq, Dqk,
+                                  dv, _p(sinks), scale, _p(out), _p(lse))
+    return out, lse

@@ -1,0 +1,412 @@
+/*
+ * oracle.c -- plain, slow CPU reference for hybrid decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source with the HIP library.
+ *
+ * Arithmetic is IEEE fp64 except where the pages fix fp32 (the RoPE angle,
+ * see or_rope_angles).  bf16 inputs are widened exactly; bf16 outputs are
+ * rounded once, to nearest-even, straight from the fp64 value.
+ *
+ * Sources (all on the pages that define the method):
+ *   [SPARK]  vllm-omni "edge/spark_export.py" page -- Spark-X2.5 decode step
+ *            export: `_rope`, `_angles`, `SparkStepConfig.cache_len`,
+ *            `_Layer.forward` (ring and roll branches), `kv_cache_bytes`.
+ *   [SINK]   vLLM "hy_v4/nvidia/flashmla_sparse.py" page -- sink-capable
+ *            FlashMLA sparse backend: the class docstring of
+ *            `HYV4FlashMLASparseImpl` (sink formula), `_sinks_for_query`
+ *            (-inf padding is a no-op sink), `_bf16_flash_mla_kernel`
+ *            (sparse call: q, kv, indices, scale, sink, topk_length).
+ *
+ * Parity status of every function is listed in its header comment.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_SLIDING 0
+#define OR_FULL 1
+
+/* ------------------------------------------------------------------ bf16 */
+
+/* Exact widening: a bf16 is the top half of an fp32. */
+double or_bf16_to_f64(uint16_t h) {
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round an fp64 value once, to nearest-even, to bf16 (8 significant bits,
+ * fp32 exponent range, gradual underflow).  Not routed through fp32, which
+ * would round twice. */
+uint16_t or_f64_to_bf16(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int e;
+    frexp(a, &e);                  /* a = m * 2^e, m in [0.5, 1) */
+    int q = e - 8;                 /* quantum exponent for 8 significant bits */
+    if (q < -133) q = -133;        /* bf16 subnormal quantum 2^-133 */
+    double r = rint(ldexp(a, -q)); /* round half to even (default mode) */
+    r = ldexp(r, q);
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;
+    float f = (float)r;            /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------ cache rules */
+
+/* [SPARK] `SparkStepConfig.cache_len`: entries a layer holds at `context`
+ * tokens.  Full layers hold the whole context.  A sliding window counts the
+ * current token, so a ring holds window-1 previous entries; the roll layout
+ * holds window.  Parity pinned by the page's 81/235 footprint figures. */
+int64_t or_cache_len(int layer_type, int64_t context, int window, int ring) {
+    if (layer_type != OR_SLIDING) return context;
+    int64_t cap = ring ? (int64_t)(window - 1) : (int64_t)window;
+    return context < cap ? context : cap;
+}
+
+/* [SPARK] `kv_cache_bytes`: per entry 2 (K and V) * kv_heads * head_dim *
+ * bytes; hybrid = sum of cache_len over layers; uniform = layers * context.
+ * out[0] = hybrid, out[1] = uniform. */
+void or_kv_cache_bytes(const int *layer_types, int n_layers, int64_t context,
+                       int window, int ring, int kv_heads, int head_dim,
+                       int bytes_per_elem, int64_t *out) {
+    int64_t per_entry = 2LL * kv_heads * head_dim * bytes_per_elem;
+    int64_t hybrid = 0;
+    for (int i = 0; i < n_layers; ++i)
+        hybrid += or_cache_len(layer_types[i], context, window, ring);
+    out[0] = hybrid * per_entry;
+    out[1] = (int64_t)n_layers * context * per_entry;
+}
+
+/* Ring slot of the entry for position `pos`.  [SPARK] `_Layer.forward`,
+ * ring branch: the runtime drops the new entry into the slot for its
+ * position, evicting the oldest; with window-1 slots that slot is
+ * pos mod (window-1), and the evicted entry is position pos-(window-1). */
+int64_t or_ring_slot(int64_t pos, int window) { return pos % (int64_t)(window - 1); }
+
+/* ------------------------------------------------------------------ RoPE */
+
+/* [SPARK] `_angles`: inv[i] = 1 / theta^(2i/rot) for i < rot/2, built in
+ * fp32 on the page; angle = position * inv in fp32.  Here inv is the exact
+ * value rounded once to fp32 (fp64 evaluation, page order: power, then
+ * reciprocal), and the angle is the page's single fp32 multiply.  cos and
+ * sin of that fp32 angle are evaluated in fp64 and rounded to fp32, which
+ * is the page's fp32 cos/sin to within one rounding.
+ * Parity pinned: pos 0 identity, pos 1 frequency values, complex-rotation
+ * form, relative-position property (tests/test_oracle_rope.py). */
+void or_rope_angles(double theta, int rot, int64_t pos, float *cos_out, float *sin_out) {
+    int half = rot / 2;
+    for (int i = 0; i < half; ++i) {
+        double expo = (double)(2 * i) / (double)rot;
+        float inv = (float)(1.0 / pow(theta, expo));
+        float ang = (float)pos * inv;   /* one fp32 multiply */
+        cos_out[i] = (float)cos((double)ang);
+        sin_out[i] = (float)sin((double)ang);
+    }
+}
+
+/* [SPARK] `_rope`: neox-style rotation of the leading `rot` dims of each
+ * head vector; with halves x1 = x[:rot/2], x2 = x[rot/2:rot],
+ *   out = x_rot * cos + cat(-x2, x1) * sin,
+ * cos/sin duplicated over both halves; dims rot..D-1 pass through.
+ * x, y: bf16 [n_vec, D]; y may alias x.  Rotation in fp64, one rounding. */
+void or_rope_apply(const uint16_t *x, uint16_t *y, int64_t n_vec, int D, int rot,
+                   double theta, int64_t pos) {
+    int half = rot / 2;
+    float *c = (float *)malloc(sizeof(float) * (half > 0 ? half : 1));
+    float *s = (float *)malloc(sizeof(float) * (half > 0 ? half : 1));
+    or_rope_angles(theta, rot, pos, c, s);
+    for (int64_t v = 0; v < n_vec; ++v) {
+        const uint16_t *xv = x + v * D;
+        uint16_t *yv = y + v * D;
+        double *tmp = (double *)malloc(sizeof(double) * D);
+        for (int d = 0; d < D; ++d) tmp[d] = or_bf16_to_f64(xv[d]);
+        for (int j = 0; j < half; ++j) {
+            double x1 = tmp[j], x2 = tmp[j + half];
+            double r1 = x1 * (double)c[j] + (-x2) * (double)s[j];
+            double r2 = x2 * (double)c[j] + x1 * (double)s[j];
+            yv[j] = or_f64_to_bf16(r1);
+            yv[j + half] = or_f64_to_bf16(r2);
+        }
+        for (int d = rot; d < D; ++d) yv[d] = xv[d];
+        free(tmp);
+    }
+    free(c);
+    free(s);
+}
+
+/* ------------------------------------------------------- rope + append */
+
+/* One decode step's cache update for one layer, per sequence b:
+ *   q[b]  (bf16 [Hq, D])  rotated in place at position pos[b];
+ *   the new K (rotated) and V are written to the cache.
+ * Full layer: K/V[b, h, pos[b], :] <- new.
+ * Sliding layer ([SPARK] `_Layer.forward`, ring branch): slot
+ *   s = pos mod (window-1).  The old slot content is position
+ *   pos-(window-1), the oldest entry of the current window (a window counts
+ *   the current token, [SPARK] `cache_len` docstring), so it is first kept
+ *   in the side row kev/vev[b, h, :], then the slot takes the new entry.
+ *   The side row is meaningful only when pos >= window-1; below that the
+ *   slot was never written and the side row is left untouched.
+ * Layouts: k, v bf16 [B, Hkv, capacity, D]; kev, vev bf16 [B, Hkv, D];
+ *   k_new, v_new bf16 [B, Hkv, D]; pos int32 [B].
+ * Parity pinned bit-exact: slot arithmetic, untouched slots, side row =
+ * prior slot content, ring vs roll streaming (tests/test_oracle_cache.py). */
+void or_rope_append(uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                    const int32_t *pos, int layer_type, int B, int Hq, int Hkv,
+                    int D, int rot, double theta, int window, int64_t capacity,
+                    uint16_t *k, uint16_t *v, uint16_t *kev, uint16_t *vev) {
+    uint16_t *krot = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)Hkv * D);
+    for (int b = 0; b < B; ++b) {
+        int64_t p = pos[b];
+        or_rope_apply(q + (int64_t)b * Hq * D, q + (int64_t)b * Hq * D, Hq, D, rot, theta, p);
+        or_rope_apply(k_new + (int64_t)b * Hkv * D, krot, Hkv, D, rot, theta, p);
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t row;
+            uint16_t *kb = k + ((int64_t)b * Hkv + h) * capacity * D;
+            uint16_t *vb = v + ((int64_t)b * Hkv + h) * capacity * D;
+            if (layer_type == OR_SLIDING) {
+                row = or_ring_slot(p, window);
+                if (p >= window - 1) {
+                    memcpy(kev + ((int64_t)b * Hkv + h) * D, kb + row * D, sizeof(uint16_t) * D);
+                    memcpy(vev + ((int64_t)b * Hkv + h) * D, vb + row * D, sizeof(uint16_t) * D);
+                }
+            } else {
+                row = p;
+            }
+            memcpy(kb + row * D, krot + (int64_t)h * D, sizeof(uint16_t) * D);
+            memcpy(vb + row * D, v_new + ((int64_t)b * Hkv + h) * D, sizeof(uint16_t) * D);
+        }
+    }
+    free(krot);
+}
+
+/* ------------------------------------------------------ decode attention */
+
+/* Attention of one query vector over an explicit list of key/value rows.
+ * [SPARK] `_Layer.forward`: scores = q . k * scale, softmax over the keys,
+ * weighted sum of values; scale = 1/sqrt(head_dim) there (passed in here).
+ * Returns lse = ln(sum exp(scores)) (natural log, before any sink) and
+ * writes the normalised output.  Empty key set: out 0, lse -inf. */
+static void attend_rows(const double *qv, const uint16_t *const *krows,
+                        const uint16_t *const *vrows, int64_t n, int Dqk, int Dv,
+                        double scale, double *out, double *lse) {
+    for (int d = 0; d < Dv; ++d) out[d] = 0.0;
+    if (n == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double *sc = (double *)malloc(sizeof(double) * n);
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int d = 0; d < Dqk; ++d) acc += qv[d] * or_bf16_to_f64(krows[i][d]);
+        sc[i] = acc * scale;
+        if (sc[i] > m) m = sc[i];
+    }
+    double l = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double p = exp(sc[i] - m);
+        l += p;
+        for (int d = 0; d < Dv; ++d) out[d] += p * or_bf16_to_f64(vrows[i][d]);
+    }
+    for (int d = 0; d < Dv; ++d) out[d] /= l;
+    *lse = m + log(l);
+    free(sc);
+}
+
+/* [SINK] `HYV4FlashMLASparseImpl` docstring: the sink folds into the
+ * softmax denominator, out *= exp(lse) / (exp(lse) + exp(sink)), written
+ * here exactly in that form.  A -inf sink gives factor 1 (the padding
+ * no-op of `_sinks_for_query`). */
+static double sink_factor(double lse, double sink) {
+    double el = exp(lse);
+    return el / (el + exp(sink));
+}
+
+/* Decode attention for one layer after the append.
+ * For sequence b and query head h, the kv head is h / (Hq/Hkv)
+ * ([SPARK] `_Layer.forward`: q folded to (kv, group, d), GQA without
+ * expanded K/V).  Key set, with n = seq_lens[b] (= pos+1):
+ *   full:    rows 0..n-1 of K/V[b, g];
+ *   sliding: ring slots 0..min(n, window-1)-1, plus the side row when
+ *            n >= window -- i.e. the last min(n, window) positions.
+ *            Unwritten slots are excluded ([SPARK] ring comment: only
+ *            slots not yet written need masking; ring order is arbitrary).
+ * sinks: fp32 [Hq] or NULL.  out: fp64 [B, Hq, D]; lse: fp64 [B, Hq]
+ * (pre-sink).  Parity pinned: fp64 brute force vs torch SDPA, one-key and
+ * equal-key closed forms, sink as an extra zero-value key, -inf sink
+ * bitwise no-op, slot permutation, ring vs roll
+ * (tests/test_oracle_attention.py). */
+void or_decode_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const uint16_t *kev, const uint16_t *vev, const int32_t *seq_lens,
+                    int layer_type, int B, int Hq, int Hkv, int D, int window,
+                    int64_t capacity, const float *sinks, double scale,
+                    double *out, double *lse) {
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hq; ++h) {
+            int g = h / G;
+            int64_t n = seq_lens[b];
+            const uint16_t *kb = k + ((int64_t)b * Hkv + g) * capacity * D;
+            const uint16_t *vb = v + ((int64_t)b * Hkv + g) * capacity * D;
+            int64_t nrows;
+            const uint16_t **kr, **vr;
+            if (layer_type == OR_SLIDING) {
+                int64_t nring = n < window - 1 ? n : window - 1;
+                int side = n >= window;
+                nrows = nring + side;
+                kr = (const uint16_t **)malloc(sizeof(void *) * (nrows + 1));
+                vr = (const uint16_t **)malloc(sizeof(void *) * (nrows + 1));
+                for (int64_t i = 0; i < nring; ++i) {
+                    kr[i] = kb + i * D;
+                    vr[i] = vb + i * D;
+                }
+                if (side) {
+                    kr[nring] = kev + ((int64_t)b * Hkv + g) * D;
+                    vr[nring] = vev + ((int64_t)b * Hkv + g) * D;
+                }
+            } else {
+                nrows = n;
+                kr = (const uint16_t **)malloc(sizeof(void *) * (nrows + 1));
+                vr = (const uint16_t **)malloc(sizeof(void *) * (nrows + 1));
+                for (int64_t i = 0; i < n; ++i) {
+                    kr[i] = kb + i * D;
+                    vr[i] = vb + i * D;
+                }
+            }
+            double *qv = (double *)malloc(sizeof(double) * D);
+            const uint16_t *qh = q + ((int64_t)b * Hq + h) * D;
+            for (int d = 0; d < D; ++d) qv[d] = or_bf16_to_f64(qh[d]);
+            double *o = out + ((int64_t)b * Hq + h) * D;
+            double *ls = lse + (int64_t)b * Hq + h;
+            attend_rows(qv, kr, vr, nrows, D, D, scale, o, ls);
+            if (sinks) {
+                double f = sink_factor(*ls, (double)sinks[h]);
+                for (int d = 0; d < D; ++d) o[d] *= f;
+            }
+            free(qv);
+            free(kr);
+            free(vr);
+        }
+    }
+}
+
+/* ------------------------------------------------- split-K and LSE merge */
+
+/* Attention of one query over rows [r0, r1) of a contiguous K/V block
+ * ([SPARK] ring comment: softmax split over two key sets, merged online,
+ * is the same result).  out: normalised over the chunk; lse_out: chunk
+ * lse (-inf for an empty chunk). */
+void or_attn_chunk(const uint16_t *qh, const uint16_t *kblk, const uint16_t *vblk,
+                   int64_t r0, int64_t r1, int D, double scale, double *out,
+                   double *lse_out) {
+    int64_t n = r1 > r0 ? r1 - r0 : 0;
+    const uint16_t **kr = (const uint16_t **)malloc(sizeof(void *) * (n + 1));
+    const uint16_t **vr = (const uint16_t **)malloc(sizeof(void *) * (n + 1));
+    for (int64_t i = 0; i < n; ++i) {
+        kr[i] = kblk + (r0 + i) * D;
+        vr[i] = vblk + (r0 + i) * D;
+    }
+    double *qv = (double *)malloc(sizeof(double) * D);
+    for (int d = 0; d < D; ++d) qv[d] = or_bf16_to_f64(qh[d]);
+    attend_rows(qv, kr, vr, n, D, D, scale, out, lse_out);
+    free(qv);
+    free(kr);
+    free(vr);
+}
+
+/* Merge of per-chunk results into one softmax ([SPARK] ring comment on
+ * the two-key-set online softmax): with lse_c the chunk lse and o_c the
+ * chunk output,
+ *   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) o_c.
+ * Empty chunks (lse_c = -inf) weigh zero.  Then the sink ([SINK] class
+ * docstring) scales o, if given.  o_parts: [S, D]; lse_parts: [S]. */
+void or_lse_merge(const double *o_parts, const double *lse_parts, int S, int D,
+                  const float *sink, double *out, double *lse_out) {
+    double m = -INFINITY;
+    for (int c = 0; c < S; ++c)
+        if (lse_parts[c] > m) m = lse_parts[c];
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (m == -INFINITY) {
+        *lse_out = -INFINITY;
+        return;
+    }
+    double tot = 0.0;
+    for (int c = 0; c < S; ++c) tot += exp(lse_parts[c] - m);
+    double lse = m + log(tot);
+    for (int c = 0; c < S; ++c) {
+        double w = exp(lse_parts[c] - lse);
+        for (int d = 0; d < D; ++d) out[d] += w * o_parts[(int64_t)c * D + d];
+    }
+    *lse_out = lse;
+    if (sink) {
+        double f = sink_factor(lse, (double)*sink);
+        for (int d = 0; d < D; ++d) out[d] *= f;
+    }
+}
+
+/* ------------------------------------------------------ sparse top-k */
+
+/* Sparse top-k decode with a sink, [SINK] `_bf16_flash_mla_kernel`: one
+ * latent KV head shared by all query heads; query t attends to pool rows
+ * indices[t, i] for i < topk_length[t] (all topk when topk_length is NULL);
+ * keys are the full Dqk-dim rows, values their leading Dv dims (the
+ * `kv_c_and_k_pe` cache holds the latent part first; `head_dim_v` = Dv).
+ * Negative indices are skipped.  q: bf16 [T, Hq, Dqk]; kv: bf16 [N, Dqk];
+ * indices: int32 [T, topk]; out fp64 [T, Hq, Dv]; lse fp64 [T, Hq]
+ * (pre-sink).  Parity pinned: dense reduction (topk = N, identity
+ * indices) and gathered brute force vs torch SDPA; -inf sink no-op
+ * (tests/test_oracle_sparse.py). */
+void or_sparse_decode_attn(const uint16_t *q, const uint16_t *kv, int64_t N,
+                           const int32_t *indices, int topk, const int32_t *topk_length,
+                           int T, int Hq, int Dqk, int Dv, const float *sinks,
+                           double scale, double *out, double *lse) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < Hq; ++h) {
+            int len = topk_length ? topk_length[t] : topk;
+            if (len > topk) len = topk;
+            if (len < 0) len = 0;
+            const uint16_t **rows = (const uint16_t **)malloc(sizeof(void *) * (len + 1));
+            int64_t n = 0;
+            for (int i = 0; i < len; ++i) {
+                int32_t idx = indices[(int64_t)t * topk + i];
+                if (idx < 0 || idx >= N) continue;
+                rows[n++] = kv + (int64_t)idx * Dqk;
+            }
+            double *qv = (double *)malloc(sizeof(double) * Dqk);
+            const uint16_t *qh = q + ((int64_t)t * Hq + h) * Dqk;
+            for (int d = 0; d < Dqk; ++d) qv[d] = or_bf16_to_f64(qh[d]);
+            double *o = out + ((int64_t)t * Hq + h) * Dv;
+            double *ls = lse + (int64_t)t * Hq + h;
+            attend_rows(qv, rows, rows, n, Dqk, Dv, scale, o, ls);
+            if (sinks) {
+                double f = sink_factor(*ls, (double)sinks[h]);
+                for (int d = 0; d < Dv; ++d) o[d] *= f;
+            }
+            free(qv);
+            free(rows);
+        }
+    }
+}
+
+/* Threads the OpenMP runtime will use for the parallel loops above. */
+int or_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
