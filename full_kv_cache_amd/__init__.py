@@ -1,0 +1,176 @@
+"""Python binding of libhda, the hybrid decode-attention library for MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in ``include/hda.h``.  torch tensors supply
+device memory and the stream; nothing is computed here, and there is no
+CPU fallback -- if ``libhda.so`` is missing, every call raises.
+
+Function names match the C entry points.  Tensors must be contiguous, on
+the current GPU, with the dtypes the header states (bf16 as
+``torch.bfloat16``, fp32, int32).
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+SLIDING = 0
+FULL = 1
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libhda.so"
+
+HDA_OK = 0
+_STATUS = {0: "HDA_OK", 1: "HDA_ERR_INVALID_ARGUMENT", 2: "HDA_ERR_UNSUPPORTED",
+           3: "HDA_ERR_WORKSPACE", 4: "HDA_ERR_HIP"}
+
+
+class HdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of ``hda_cache_desc``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("rotary_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("rope_theta", ctypes.c_double),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_evict", ctypes.c_void_p),
+        ("v_evict", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhda.so (built by ``python -m full_kv_cache_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m full_kv_cache_amd.build`")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(CacheDesc)
+        L.hda_rope_append.restype = ctypes.c_int
+        L.hda_rope_append.argtypes = [P, P, P, P, ctypes.c_int, D, P]
+        L.hda_decode_workspace_bytes.restype = sz
+        L.hda_decode_workspace_bytes.argtypes = [D, ctypes.c_int, i32, i32]
+        L.hda_decode_attn.restype = ctypes.c_int
+        L.hda_decode_attn.argtypes = [P, D, P, ctypes.c_int, P, ctypes.c_float, P, P, i32, i32,
+                                      P, sz, P]
+        L.hda_status_string.restype = ctypes.c_char_p
+        L.hda_status_string.argtypes = [ctypes.c_int]
+        L.hda_last_error_message.restype = ctypes.c_char_p
+        L.hda_last_error_message.argtypes = []
+        if hasattr(L, "hda_sparse_decode_attn"):
+            L.hda_sparse_decode_attn.restype = ctypes.c_int
+            L.hda_sparse_decode_attn.argtypes = [P, P, ctypes.c_int64, P, i32, P, i32, P,
+                                                 ctypes.c_float, i32, P, P, i32, i32, P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != HDA_OK:
+        raise HdaError(status, lib().hda_last_error_message().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+@dataclass
+class LayerCache:
+    """One layer's KV cache tensors plus the shape facts of hda_cache_desc.
+
+    k, v: bf16 [B, Hkv, capacity, D]; k_evict, v_evict: bf16 [B, Hkv, D]
+    (sliding layers only).
+    """
+    k: torch.Tensor
+    v: torch.Tensor
+    k_evict: Optional[torch.Tensor]
+    v_evict: Optional[torch.Tensor]
+    num_q_heads: int
+    window: int
+    rotary_dim: int
+    rope_theta: float
+
+    def desc(self) -> CacheDesc:
+        B, Hkv, cap, D = self.k.shape
+        return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim, cap,
+                         float(self.rope_theta), self.k.data_ptr(), self.v.data_ptr(),
+                         None if self.k_evict is None else self.k_evict.data_ptr(),
+                         None if self.v_evict is None else self.v_evict.data_ptr())
+
+
+def hda_rope_append(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, stream=None):
+    """Rotate q in place, write the rotated new K and the new V into the cache."""
+    d = cache.desc()
+    _check(lib().hda_rope_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), int(layer_type),
+                                 ctypes.byref(d), _stream(stream)))
+
+
+def hda_decode_workspace_bytes(cache: LayerCache, layer_type: int, max_seq_len: int,
+                               chunk_keys: int = 0) -> int:
+    d = cache.desc()
+    return int(lib().hda_decode_workspace_bytes(ctypes.byref(d), int(layer_type),
+                                                int(max_seq_len), int(chunk_keys)))
+
+
+def validate_sinks(sinks: Optional[torch.Tensor], q: torch.Tensor) -> None:
+    """The sink contract of the flashmla_sparse page (`_validate_sinks`,
+    `_sinks_for_query`): fp32, shape (num_heads,), on q's device."""
+    if sinks is None:
+        return
+    if sinks.dtype != torch.float32:
+        raise ValueError(f"sinks must have dtype torch.float32, got {sinks.dtype}")
+    heads = q.shape[1]
+    if sinks.ndim != 1 or sinks.shape[0] != heads:
+        raise ValueError(f"sinks must have shape ({heads},), got {tuple(sinks.shape)}")
+    if sinks.device != q.device:
+        raise ValueError(f"sinks and q must be on the same device, got {sinks.device} and {q.device}")
+
+
+def hda_decode_attn(q, cache: LayerCache, seq_lens, layer_type: int, sinks, scale: float, out,
+                    lse=None, max_seq_len: int = 0, chunk_keys: int = 0, workspace=None,
+                    stream=None):
+    """Decode attention of one layer (after hda_rope_append)."""
+    validate_sinks(sinks, q)
+    d = cache.desc()
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hda_decode_attn(_ptr(q), ctypes.byref(d), _ptr(seq_lens), int(layer_type),
+                                 _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                                 int(max_seq_len), int(chunk_keys), _ptr(workspace), wbytes,
+                                 _stream(stream)))
+
+
+def hda_sparse_decode_attn(q, kv, indices, topk_length, sinks, scale: float, dv: int, out,
+                           lse=None, stream=None):
+    """Sparse top-k decode over one shared latent KV head, with sinks."""
+    validate_sinks(sinks, q)
+    T, H, dqk = q.shape
+    _check(lib().hda_sparse_decode_attn(_ptr(q), _ptr(kv), int(kv.shape[0]), _ptr(indices),
+                                        int(indices.shape[1]), _ptr(topk_length), int(T),
+                                        _ptr(sinks), float(scale), int(dv), _ptr(out), _ptr(lse),
+                                        int(H), int(dqk), _stream(stream)))

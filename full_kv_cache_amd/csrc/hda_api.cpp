@@ -1,0 +1,253 @@
+// hda_api.cpp -- C ABI of libhda: host-side validation, split planning and
+// kernel dispatch.  Declared in include/hda.h; every check here runs before
+// anything is enqueued, and nothing here synchronises or allocates.
+#include "../../include/hda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "hda_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+hda_status fail(hda_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+hda_status ok() {
+    g_last_error[0] = '\0';
+    return HDA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by both calls: the cache description and the layer type.
+// Mirrors the Spark export page's config checks (`__post_init__`: query
+// heads must be a multiple of KV heads; unknown layer types rejected).
+hda_status check_cache(const hda_cache_desc *c, int layer) {
+    if (!c) return fail(HDA_ERR_INVALID_ARGUMENT, "cache descriptor is NULL");
+    if (layer != HDA_SLIDING && layer != HDA_FULL)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "unknown layer type %d", layer);
+    if (c->batch < 0) return fail(HDA_ERR_INVALID_ARGUMENT, "batch %d < 0", c->batch);
+    if (c->num_q_heads <= 0 || c->num_kv_heads <= 0)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "head counts must be positive (q %d, kv %d)",
+                    c->num_q_heads, c->num_kv_heads);
+    if (c->num_q_heads % c->num_kv_heads)
+        return fail(HDA_ERR_INVALID_ARGUMENT,
+                    "num_q_heads %d is not a multiple of num_kv_heads %d", c->num_q_heads,
+                    c->num_kv_heads);
+    if (c->head_dim <= 0 || c->head_dim % 8)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "head_dim %d must be a positive multiple of 8",
+                    c->head_dim);
+    if (c->rotary_dim < 0 || c->rotary_dim % 2 || c->rotary_dim > c->head_dim)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "rotary_dim %d must be even and in [0, head_dim]",
+                    c->rotary_dim);
+    if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "rope_theta must be positive and finite");
+    if (layer == HDA_SLIDING) {
+        if (c->window < 2) return fail(HDA_ERR_INVALID_ARGUMENT, "window %d < 2", c->window);
+        if (c->capacity != (int64_t)c->window - 1)
+            return fail(HDA_ERR_INVALID_ARGUMENT,
+                        "sliding capacity %lld must be window-1 = %d ring slots",
+                        (long long)c->capacity, c->window - 1);
+        if (!c->k_evict || !c->v_evict)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "sliding layer needs k_evict and v_evict");
+        if (!aligned16(c->k_evict) || !aligned16(c->v_evict))
+            return fail(HDA_ERR_INVALID_ARGUMENT, "k_evict/v_evict must be 16-byte aligned");
+    } else {
+        if (c->capacity < 1)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "full-layer capacity %lld < 1",
+                        (long long)c->capacity);
+    }
+    if (!c->k || !c->v) return fail(HDA_ERR_INVALID_ARGUMENT, "cache k/v pointer is NULL");
+    if (!aligned16(c->k) || !aligned16(c->v))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "cache k/v must be 16-byte aligned");
+    return HDA_OK;
+}
+
+// Keys per sequence the grid must cover.
+int64_t max_keys_of(const hda_cache_desc *c, int layer, int32_t max_seq_len) {
+    if (layer == HDA_SLIDING) return max_seq_len < c->window ? max_seq_len : c->window;
+    return max_seq_len;
+}
+
+// Split plan: chunk size and chunks per (sequence, KV head).  A sliding
+// window of a large batch runs as one workgroup per (sequence, KV head)
+// and needs no merge; otherwise chunks are sized so that the grid holds
+// enough workgroups to cover the chip (256 CUs).
+struct Plan {
+    int chunk;
+    int nsplit;
+};
+
+Plan plan_split(const hda_cache_desc *c, int layer, int64_t max_keys, int32_t chunk_keys) {
+    Plan pl;
+    if (chunk_keys > 0) {
+        pl.chunk = chunk_keys;
+    } else {
+        const int64_t pairs = (int64_t)c->batch * c->num_kv_heads;
+        if (layer == HDA_SLIDING && pairs >= 128 && max_keys <= hda::kMaxChunk) {
+            pl.chunk = hda::kMaxChunk;
+        } else {
+            int64_t want = (max_keys * pairs) / 512;  // aim at ~512 workgroups or more
+            want = (want + 15) / 16 * 16;
+            if (want < 64) want = 64;
+            if (want > 256) want = 256;
+            pl.chunk = (int)want;
+        }
+    }
+    pl.nsplit = (int)((max_keys + pl.chunk - 1) / pl.chunk);
+    if (pl.nsplit < 1) pl.nsplit = 1;
+    return pl;
+}
+
+size_t workspace_for(const hda_cache_desc *c, const Plan &pl) {
+    if (pl.nsplit <= 1) return 0;
+    const size_t slots = (size_t)c->batch * c->num_q_heads * pl.nsplit;
+    size_t bytes = slots * hda::kHeadDim * sizeof(float);
+    bytes = (bytes + 255) / 256 * 256;
+    bytes += slots * sizeof(float);
+    return bytes;
+}
+
+hda_status check_decode_shape(const hda_cache_desc *c, int layer, int32_t max_seq_len,
+                              int32_t chunk_keys) {
+    hda_status st = check_cache(c, layer);
+    if (st != HDA_OK) return st;
+    if (c->head_dim != hda::kHeadDim)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels are built for head_dim %d, got %d",
+                    hda::kHeadDim, c->head_dim);
+    const int g = c->num_q_heads / c->num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+        return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
+    if (max_seq_len < 1) return fail(HDA_ERR_INVALID_ARGUMENT, "max_seq_len %d < 1", max_seq_len);
+    if (layer == HDA_FULL && max_seq_len > c->capacity)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds cache capacity %lld",
+                    max_seq_len, (long long)c->capacity);
+    if (chunk_keys != 0 && (chunk_keys < 16 || chunk_keys > hda::kMaxChunk || chunk_keys % 16))
+        return fail(HDA_ERR_INVALID_ARGUMENT,
+                    "chunk_keys %d must be 0 or a multiple of 16 in [16, %d]", chunk_keys,
+                    hda::kMaxChunk);
+    return HDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hda_status_string(hda_status s) {
+    switch (s) {
+        case HDA_OK: return "HDA_OK";
+        case HDA_ERR_INVALID_ARGUMENT: return "HDA_ERR_INVALID_ARGUMENT";
+        case HDA_ERR_UNSUPPORTED: return "HDA_ERR_UNSUPPORTED";
+        case HDA_ERR_WORKSPACE: return "HDA_ERR_WORKSPACE";
+        case HDA_ERR_HIP: return "HDA_ERR_HIP";
+    }
+    return "HDA_ERR_UNKNOWN";
+}
+
+const char *hda_last_error_message(void) { return g_last_error; }
+
+hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const int32_t *pos,
+                           hda_layer_type layer, const hda_cache_desc *cache, void *stream) {
+    hda_status st = check_cache(cache, layer);
+    if (st != HDA_OK) return st;
+    if (!q || !k_new || !v_new || !pos)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new and pos must be non-NULL");
+    if (cache->batch == 0) return ok();
+    hda::RopeAppendParams p{};
+    p.q = static_cast<uint16_t *>(q);
+    p.k_new = static_cast<const uint16_t *>(k_new);
+    p.v_new = static_cast<const uint16_t *>(v_new);
+    p.pos = pos;
+    p.k = static_cast<uint16_t *>(cache->k);
+    p.v = static_cast<uint16_t *>(cache->v);
+    p.k_evict = static_cast<uint16_t *>(cache->k_evict);
+    p.v_evict = static_cast<uint16_t *>(cache->v_evict);
+    p.capacity = cache->capacity;
+    p.theta = cache->rope_theta;
+    p.batch = cache->batch;
+    p.num_q_heads = cache->num_q_heads;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.head_dim = cache->head_dim;
+    p.rotary_dim = cache->rotary_dim;
+    p.window = cache->window;
+    p.sliding = layer == HDA_SLIDING;
+    hipError_t e = hda::launch_rope_append(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(HDA_ERR_HIP, "rope_append launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer,
+                                  int32_t max_seq_len, int32_t chunk_keys) {
+    if (check_decode_shape(cache, layer, max_seq_len, chunk_keys) != HDA_OK) return 0;
+    const int64_t mk = max_keys_of(cache, layer, max_seq_len);
+    return workspace_for(cache, plan_split(cache, layer, mk, chunk_keys));
+}
+
+hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int32_t *seq_lens,
+                           hda_layer_type layer, const float *sinks, float scale, void *out,
+                           float *lse, int32_t max_seq_len, int32_t chunk_keys, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    hda_status st = check_decode_shape(cache, layer, max_seq_len, chunk_keys);
+    if (st != HDA_OK) return st;
+    if (!q || !seq_lens || !out)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, seq_lens and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned");
+    if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (cache->batch == 0) return ok();
+
+    const int64_t mk = max_keys_of(cache, layer, max_seq_len);
+    const Plan pl = plan_split(cache, layer, mk, chunk_keys);
+    const size_t need = workspace_for(cache, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", need,
+                    workspace_bytes, workspace);
+    if (need > 0 && !aligned16(workspace))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+    hda::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(cache->k);
+    p.v = static_cast<const uint16_t *>(cache->v);
+    p.kev = static_cast<const uint16_t *>(cache->k_evict);
+    p.vev = static_cast<const uint16_t *>(cache->v_evict);
+    p.seq_lens = seq_lens;
+    p.sinks = sinks;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    if (need > 0) {
+        const size_t slots = (size_t)cache->batch * cache->num_q_heads * pl.nsplit;
+        size_t obytes = (slots * hda::kHeadDim * sizeof(float) + 255) / 256 * 256;
+        p.part_o = static_cast<float *>(workspace);
+        p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + obytes);
+    }
+    p.capacity = cache->capacity;
+    p.batch = cache->batch;
+    p.num_q_heads = cache->num_q_heads;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.window = cache->window;
+    p.chunk = pl.chunk;
+    p.nsplit = pl.nsplit;
+    p.max_keys = (int)(layer == HDA_SLIDING ? max_seq_len : mk);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    const int g = cache->num_q_heads / cache->num_kv_heads;
+    hipError_t e = hda::launch_decode(p, layer == HDA_SLIDING, g, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(HDA_ERR_HIP, "decode_attn launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,181 @@
+/*
+ * hda.h -- C ABI of the hybrid decode-attention library (libhda.so).
+ *
+ * Single-token autoregressive decode attention over an explicit KV cache
+ * for a hybrid sliding/full-attention, grouped-query model, as described by
+ * the vllm-omni "edge/spark_export.py" page (Spark-X2.5 decode step: ring
+ * cache for sliding layers, per-layer-type partial RoPE) and the vLLM
+ * "hy_v4/nvidia/flashmla_sparse.py" page (per-head attention sink, sparse
+ * top-k MLA decode).
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers on the current HIP device,
+ *     owned by the caller.  The library never allocates, frees or keeps
+ *     them; it keeps no state between calls.
+ *   - bf16 tensors are raw 16-bit bfloat16 values; fp32 tensors are IEEE
+ *     float.  Every tensor is dense, row-major (last index fastest) and
+ *     16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL: the null stream).  Calls only
+ *     enqueue work: they never synchronise, so they may be captured into a
+ *     HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns a status and enqueues nothing.  Values that live
+ *     in device memory (positions, lengths, indices) are not checked on the
+ *     host: kernels skip rows outside the cache instead of touching them.
+ *   - The library prints nothing.  hda_last_error_message() gives the
+ *     reason for the calling thread's last failure.
+ */
+#ifndef HDA_H_
+#define HDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hda_status {
+    HDA_OK = 0,
+    HDA_ERR_INVALID_ARGUMENT = 1, /* a shape, pointer or value breaks the contract */
+    HDA_ERR_UNSUPPORTED = 2,      /* well-formed, but outside what the kernels handle */
+    HDA_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+    HDA_ERR_HIP = 4               /* the HIP runtime reported an error */
+} hda_status;
+
+/* Layer types of the hybrid model (Spark export page, `layer_types`:
+ * "sliding_attention" / "full_attention"; any other value is rejected, as
+ * `SparkStepConfig.__post_init__` rejects unknown layer types). */
+typedef enum hda_layer_type {
+    HDA_SLIDING = 0,
+    HDA_FULL = 1
+} hda_layer_type;
+
+/*
+ * One layer's KV cache (Spark export page, `example_inputs`: caches are
+ * laid out (batch, kv_heads, entries, head_dim)).
+ *
+ *   k, v        bf16 [batch, num_kv_heads, capacity, head_dim]
+ *   k_evict,    bf16 [batch, num_kv_heads, head_dim]; sliding layers only
+ *   v_evict     (NULL for full layers).  The side row keeps the window's
+ *               oldest entry after the append overwrote its ring slot.
+ *   capacity    sliding: window - 1 ring slots (the window counts the
+ *               current token, `SparkStepConfig.cache_len`); full: the
+ *               longest context the cache can hold.
+ *   rotary_dim  leading dims rotated by RoPE (`rotary_dim`: head_dim times
+ *   rope_theta  the layer type's `partial_rotary_factor`), and its theta.
+ *               Spark: sliding 256 dims / 1e4, full 64 dims / 5e6.
+ */
+typedef struct hda_cache_desc {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t window;
+    int32_t rotary_dim;
+    int64_t capacity;
+    double rope_theta;
+    void *k;
+    void *v;
+    void *k_evict;
+    void *v_evict;
+} hda_cache_desc;
+
+/*
+ * hda_rope_append -- fused partial RoPE of the step's q and new K, and the
+ * KV append, for one layer.
+ *
+ * Spark export page: `_angles` (angle = position * theta^(-2i/rot), i <
+ * rot/2, in fp32), `_rope` (neox halves: out = x*cos + cat(-x2, x1)*sin on
+ * the leading rot dims, the rest pass through), `_Layer.forward` ring
+ * branch (the new entry goes into the slot for its position, evicting the
+ * oldest).
+ *
+ *   q       bf16 [batch, num_q_heads, head_dim], rotated IN PLACE.
+ *   k_new   bf16 [batch, num_kv_heads, head_dim], read only; rotated copy
+ *           is written to the cache.
+ *   v_new   bf16 [batch, num_kv_heads, head_dim], read only; copied.
+ *   pos     int32 [batch] (device): position of each sequence's new token.
+ *   layer   HDA_FULL: entry pos of the cache takes the new K/V.
+ *           HDA_SLIDING: slot s = pos mod (window-1).  When pos >= window-1
+ *           that slot holds position pos-(window-1), still inside this
+ *           step's window, so it is first copied to the side row
+ *           k_evict/v_evict; then slot s takes the new K/V.
+ *   Rows outside the cache (pos < 0, or pos >= capacity for a full layer)
+ *   are skipped.  Math in fp32 (cos/sin of the fp32 angle evaluated in
+ *   fp64), results rounded to nearest-even bf16.
+ * Errors: INVALID_ARGUMENT for null pointers, misalignment, non-positive
+ * head counts, num_q_heads % num_kv_heads != 0, odd or oversized
+ * rotary_dim, sliding capacity != window-1, unknown layer; HIP on a launch
+ * failure.  batch == 0 is a no-op.
+ */
+hda_status hda_rope_append(void *q, const void *k_new, const void *v_new,
+                           const int32_t *pos, hda_layer_type layer,
+                           const hda_cache_desc *cache, void *stream);
+
+/*
+ * hda_decode_workspace_bytes -- device workspace hda_decode_attn needs for
+ * this cache, layer, longest sequence and split size (chunk_keys = 0: the
+ * library's default).  0 means no workspace is needed.  Returns 0 for an
+ * invalid description as well; hda_decode_attn then reports why.
+ */
+size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer,
+                                  int32_t max_seq_len, int32_t chunk_keys);
+
+/*
+ * hda_decode_attn -- decode attention of one layer, after hda_rope_append.
+ *
+ * For sequence b and query head h the KV head is h / (num_q_heads /
+ * num_kv_heads) (Spark `_Layer.forward`: query heads folded per KV head,
+ * K/V never expanded).  With n = seq_lens[b] (= pos + 1) the keys are
+ *   full:    cache rows 0 .. n-1;
+ *   sliding: ring slots 0 .. min(n, window-1)-1, plus the side row when
+ *            n >= window -- the last min(n, window) positions.  Slots never
+ *            written are excluded, and ring order does not matter (Spark
+ *            ring-branch comment).
+ * scores = scale * q.k (Spark: scale 1/sqrt(head_dim)); softmax; out =
+ * sum p v.  lse = ln sum exp(scores), before any sink.  With sinks, out is
+ * multiplied by exp(lse)/(exp(lse)+exp(sink[h])) (flashmla_sparse page,
+ * `HYV4FlashMLASparseImpl` docstring); a -inf sink leaves out bit-for-bit
+ * unchanged (`_sinks_for_query`: -inf is a no-op sink).
+ *
+ * Full layers (and sliding layers when split) run split-K: each chunk of
+ * chunk_keys keys gives a partial (out, lse) in the workspace, and a merge
+ * kernel combines them, lse = ln sum_c exp(lse_c), out = sum_c
+ * exp(lse_c - lse) out_c, then applies the sink (Spark ring comment: an
+ * online softmax over key subsets gives the same result).
+ *
+ *   q          bf16 [batch, num_q_heads, head_dim] (already rotated)
+ *   seq_lens   int32 [batch] (device); n <= 0 gives out 0, lse -inf
+ *   sinks      fp32 [num_q_heads] (device) or NULL
+ *   scale      softmax scale
+ *   out        bf16 [batch, num_q_heads, head_dim]
+ *   lse        fp32 [batch, num_q_heads] or NULL
+ *   max_seq_len  host bound on seq_lens (sizes the split grid); full layers
+ *              need max_seq_len <= capacity.  Sequences longer than this
+ *              bound are cut to it.
+ *   chunk_keys keys per split chunk, a multiple of 16 in [16, 512]; 0
+ *              picks the default.
+ *   workspace  device buffer of at least hda_decode_workspace_bytes().
+ * Errors: as hda_rope_append, plus UNSUPPORTED for head_dim != 256 or a
+ * query group size outside {1, 2, 4, 8, 16}, WORKSPACE when the workspace
+ * is NULL or smaller than required, INVALID_ARGUMENT for a bad chunk_keys
+ * or max_seq_len.  The cache is only read.
+ */
+hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache,
+                           const int32_t *seq_lens, hda_layer_type layer,
+                           const float *sinks, float scale, void *out, float *lse,
+                           int32_t max_seq_len, int32_t chunk_keys,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *hda_status_string(hda_status status);
+
+/* Reason for the calling thread's most recent failed call ("" if none). */
+const char *hda_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HDA_H_ */

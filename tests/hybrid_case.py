@@ -1,0 +1,118 @@
+"""Test helper: one hybrid-layer case on both sides.
+
+Draws a layer's inputs with ``workloads``, keeps host bit copies for the
+oracle and device copies for the library, and runs the step (append, then
+attention) on each side.  Only tests import this module.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+from workloads import FULL, SLIDING
+
+BF16_NAN = 0x7FC0
+
+
+class HybridCase:
+    def __init__(self, seed, batch, layer_type, pos, lmax=None, window=512, poison=False):
+        self.lt = layer_type
+        self.pos = np.asarray(pos, dtype=np.int32)
+        assert self.pos.shape == (batch,)
+        lmax = lmax or int(self.pos.max()) + 1
+        self.shape = workloads.HybridShape(batch=batch, lmax=lmax, window=window)
+        g = workloads.generator(seed)
+        t = workloads.layer_inputs(g, self.shape, layer_type)
+        self.host = {k: workloads.bits(v).copy() for k, v in t.items()}
+        if layer_type == FULL:
+            self.host["kev"] = np.zeros((batch, self.shape.num_kv_heads, self.shape.head_dim), np.uint16)
+            self.host["vev"] = self.host["kev"].copy()
+        if poison:
+            self._poison()
+        self.seq_lens = self.pos + 1
+
+    def _poison(self):
+        """NaN in every row the step must not read: unwritten ring slots
+        and side rows below a full window, full-layer rows past pos."""
+        h = self.host
+        slots = self.shape.window - 1
+        for b, p in enumerate(self.pos):
+            if self.lt == SLIDING:
+                if p < slots:
+                    h["k"][b, :, p + 1:] = BF16_NAN
+                    h["v"][b, :, p + 1:] = BF16_NAN
+                    h["kev"][b] = BF16_NAN
+                    h["vev"][b] = BF16_NAN
+            else:
+                h["k"][b, :, p + 1:] = BF16_NAN
+                h["v"][b, :, p + 1:] = BF16_NAN
+
+    # ---------------------------------------------------------- oracle side
+    def oracle_step(self, sinks=None, scale=1 / 16):
+        h = {k: v.copy() for k, v in self.host.items()}
+        s = self.shape
+        oracle.rope_append(h["q"], h["k_new"], h["v_new"], self.pos, self.lt, s.rot(self.lt),
+                           s.theta(self.lt), s.window, h["k"], h["v"], h["kev"], h["vev"])
+        out, lse = oracle.decode_attn(h["q"], h["k"], h["v"], h["kev"], h["vev"], self.seq_lens,
+                                      self.lt, s.window, sinks, scale)
+        return h, out, lse
+
+    # ------------------------------------------------------------- GPU side
+    def device(self, dev="cuda"):
+        return {k: workloads.from_bits(v).to(dev) for k, v in self.host.items()}
+
+    def cache(self, d):
+        import full_kv_cache_amd as hda
+        s = self.shape
+        sl = self.lt == SLIDING
+        return hda.LayerCache(d["k"], d["v"], d["kev"] if sl else None, d["vev"] if sl else None,
+                              s.num_q_heads, s.window, s.rot(self.lt), s.theta(self.lt))
+
+    def gpu_step(self, sinks=None, scale=1 / 16, chunk_keys=0, max_seq_len=None, d=None,
+                 append=True):
+        import full_kv_cache_amd as hda
+        d = d or self.device()
+        cache = self.cache(d)
+        pos = torch.from_numpy(self.pos).cuda()
+        seq = torch.from_numpy(self.seq_lens).cuda()
+        if append:
+            hda.hda_rope_append(d["q"], d["k_new"], d["v_new"], pos, self.lt, cache)
+        msl = int(max_seq_len or self.seq_lens.max())
+        ws_bytes = hda.hda_decode_workspace_bytes(cache, self.lt, msl, chunk_keys)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+        s = self.shape
+        out = torch.full((s.batch, s.num_q_heads, s.head_dim), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        lse = torch.full((s.batch, s.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+        sk = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).cuda()
+        hda.hda_decode_attn(d["q"], cache, seq, self.lt, sk, scale, out, lse, msl, chunk_keys, ws)
+        torch.cuda.synchronize()
+        return d, out, lse
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return workloads.bits(t)
+
+
+def assert_attn_close(out_gpu, out_ref, max_abs=1e-2, mean_abs=1e-3):
+    """The decode tolerance for unit-normal bf16 inputs with fp32 accumulation."""
+    got = to_f64(out_gpu)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    err = np.abs(got - out_ref)
+    assert err.max() <= max_abs, f"max abs err {err.max():.3e}"
+    assert err.mean() <= mean_abs, f"mean abs err {err.mean():.3e}"
+    return float(err.max()), float(err.mean())
+
+
+def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """|a - b| in bf16 ulps (same-sign finite values; order-preserving map)."""
+    def key(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + (x & 0x7FFF))
+    return np.abs(key(a_bits) - key(b_bits))

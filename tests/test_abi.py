@@ -1,0 +1,154 @@
+"""The C-ABI library loads, exports every entry point of include/hda.h, and
+rejects bad arguments on the host before touching a GPU (CPU only).
+
+Error conventions follow the pages: the Spark export page's config checks
+(`__post_init__`: query heads not a multiple of KV heads, unknown layer
+types -> ValueError) and the flashmla_sparse page's sink checks
+(`_validate_sinks`, `_sinks_for_query`: fp32, shape (num_heads,), same
+device).  No call here reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import full_kv_cache_amd as hda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "hda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"hda_rope_append", "hda_decode_attn", "hda_decode_workspace_bytes",
+            "hda_status_string", "hda_last_error_message"} <= set(names)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", str(hda.LIB_PATH)], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = hda.lib()
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_status_strings():
+    L = hda.lib()
+    for code, name in [(0, b"HDA_OK"), (1, b"HDA_ERR_INVALID_ARGUMENT"),
+                       (2, b"HDA_ERR_UNSUPPORTED"), (3, b"HDA_ERR_WORKSPACE"), (4, b"HDA_ERR_HIP")]:
+        assert L.hda_status_string(code) == name
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def _desc(**kw):
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=256, window=512, rotary_dim=256,
+             capacity=511, rope_theta=1e4, k=FAKE, v=FAKE, k_evict=FAKE, v_evict=FAKE)
+    d.update(kw)
+    return hda.CacheDesc(**d)
+
+
+def _decode(desc, layer=hda.SLIDING, max_seq_len=512, chunk=0, q=FAKE, out=FAKE, ws=None, wsb=0,
+            scale=0.0625):
+    L = hda.lib()
+    return L.hda_decode_attn(ctypes.c_void_p(q), ctypes.byref(desc), ctypes.c_void_p(FAKE), layer,
+                             None, scale, ctypes.c_void_p(out), None, max_seq_len, chunk,
+                             ctypes.c_void_p(ws) if ws else None, wsb, None)
+
+
+def _append(desc, layer=hda.SLIDING, q=FAKE):
+    L = hda.lib()
+    return L.hda_rope_append(ctypes.c_void_p(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), layer, ctypes.byref(desc), None)
+
+
+def _msg():
+    return hda.lib().hda_last_error_message().decode()
+
+
+@pytest.mark.parametrize("fn", [_append, _decode])
+def test_heads_not_multiple(fn):
+    assert fn(_desc(num_q_heads=6, num_kv_heads=4)) == 1
+    assert "not a multiple" in _msg()
+
+
+@pytest.mark.parametrize("fn", [_append, _decode])
+def test_unknown_layer_type(fn):
+    assert fn(_desc(), layer=2) == 1
+    assert "unknown layer type" in _msg()
+
+
+def test_rotary_dim_checks():
+    assert _append(_desc(rotary_dim=255)) == 1
+    assert _append(_desc(rotary_dim=258)) == 1
+
+
+def test_sliding_capacity_must_be_window_minus_one():
+    assert _append(_desc(capacity=512)) == 1
+    assert "window-1" in _msg()
+
+
+def test_sliding_needs_side_rows():
+    assert _append(_desc(k_evict=None)) == 1
+
+
+def test_null_and_misaligned_pointers():
+    assert _append(_desc(), q=0) == 1
+    assert _append(_desc(k=FAKE + 2)) == 1
+    assert _decode(_desc(), q=FAKE + 8) == 1
+
+
+def test_decode_unsupported_shapes():
+    assert _decode(_desc(head_dim=128, rotary_dim=128)) == 2
+    assert _decode(_desc(num_q_heads=6, num_kv_heads=2)) == 2  # group of 3
+
+
+def test_decode_bounds():
+    full = _desc(capacity=1024, rotary_dim=64, rope_theta=5e6, k_evict=None, v_evict=None)
+    assert _decode(full, layer=hda.FULL, max_seq_len=1025) == 1
+    assert "capacity" in _msg()
+    assert _decode(full, layer=hda.FULL, max_seq_len=0) == 1
+    assert _decode(full, layer=hda.FULL, max_seq_len=64, chunk=24) == 1
+    assert _decode(full, layer=hda.FULL, max_seq_len=64, chunk=1024) == 1
+    assert _decode(full, layer=hda.FULL, max_seq_len=64, scale=float("nan")) == 1
+
+
+def test_workspace_sizing_and_errors():
+    L = hda.lib()
+    full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6, k_evict=None, v_evict=None)
+    need = L.hda_decode_workspace_bytes(ctypes.byref(full), hda.FULL, 4096, 256)
+    # 2 sequences x 8 heads x 16 chunks of (256 floats out + 1 float lse), padded
+    assert need == (2 * 8 * 16 * 256 * 4) + 2 * 8 * 16 * 4
+    assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256) == 3
+    assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256, ws=FAKE, wsb=need - 1) == 3
+    assert "workspace" in _msg()
+    # one chunk covering every key needs no workspace
+    assert L.hda_decode_workspace_bytes(ctypes.byref(full), hda.FULL, 512, 512) == 0
+    # invalid description -> 0
+    bad = _desc(num_q_heads=6, num_kv_heads=4)
+    assert L.hda_decode_workspace_bytes(ctypes.byref(bad), hda.SLIDING, 512, 0) == 0
+
+
+def test_batch_zero_is_noop():
+    assert _append(_desc(batch=0)) == 0
+    assert _decode(_desc(batch=0)) == 0
+
+
+def test_sink_validation_in_binding():
+    q = torch.zeros(2, 8, 256, dtype=torch.bfloat16)
+    hda.validate_sinks(None, q)
+    hda.validate_sinks(torch.zeros(8), q)
+    with pytest.raises(ValueError, match="float32"):
+        hda.validate_sinks(torch.zeros(8, dtype=torch.float16), q)
+    with pytest.raises(ValueError, match="shape"):
+        hda.validate_sinks(torch.zeros(4), q)
+    with pytest.raises(ValueError, match="shape"):
+        hda.validate_sinks(torch.zeros(8, 1), q)
