@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode-attention throughput of the hybrid model on one MI355X.
+
+One step is one decode step of the attention path for a whole batch: for
+each of the 28 layers (21 sliding with a 512-token window held as 511 ring
+slots plus a side row, 7 full; layer i is full when i % 4 == 3)
+
+    hda_rope_append  -- rotate q in place, write the rotated new K and V
+                        into the ring slot (sliding) or row pos (full);
+    hda_decode_attn  -- GQA attention over the layer's keys with a per-head
+                        sink; full layers run split-K plus the LSE merge.
+
+Every layer has its own cache, so a step streams the whole resident KV
+(about 5.2 GB at the default shape), far more than the 256 MB last-level
+cache: nothing is served from cache between steps.  Inputs are synthetic
+(seeded, unit-normal bf16), already resident in HBM when timing starts.
+
+Reported: KV GB/s (attended K and V bytes per step / step time), its
+fraction of the 8 TB/s HBM peak, decode tokens/s (batch / step time), a
+roofline entry for the dominant kernel and the CPU oracle's rate on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn KV GB/s (% HBM peak) + tokens/s, batch 64 at 4k context"
+
+CONFIGS = {
+    # name: (batch, seq_len spec, lmax, n_layers, description)
+    "throughput": dict(batch=64, lo=512, hi=4096, lmax=4096, layers=28,
+                       desc="batch 64, context lengths uniform in [512, 4096], 28 layers "
+                            "(21 sliding window 512 + 7 full), 8 q / 2 KV heads, head_dim 256, "
+                            "bf16, per-head sinks"),
+    "step28": dict(batch=1, lo=4096, hi=4096, lmax=4096, layers=28,
+                   desc="batch 1 at context 4096, 28 layers (21 sliding + 7 full)"),
+    "long": dict(batch=16, lo=32768, hi=32768, lmax=32768, layers=28,
+                 desc="batch 16 at context 32768, 28 layers (21 sliding + 7 full)"),
+    "tiny": dict(batch=1, lo=1024, hi=1024, lmax=1024, layers=2,
+                 desc="batch 1 at position 1023, one sliding and one full layer"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="throughput", choices=sorted(CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum oracle time for the CPU baseline sample")
+    ap.add_argument("--chunk-keys", type=int, default=0, help="split size for full layers (0: default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of this many MB (PMC byte calibration)")
+    return ap.parse_args()
+
+
+def layer_types(n):
+    import workloads
+    return workloads.layer_pattern(n) if n != 2 else [workloads.SLIDING, workloads.FULL]
+
+
+class Workload:
+    """All layers' tensors for one configuration, resident on the GPU."""
+
+    def __init__(self, cfg: dict, seed: int, dev="cuda"):
+        import torch
+        import workloads
+        import full_kv_cache_amd as hda
+
+        self.cfg = cfg
+        B = cfg["batch"]
+        self.shape = workloads.HybridShape(batch=B, lmax=cfg["lmax"])
+        g = workloads.generator(seed, dev)
+        self.seq_lens = workloads.uniform_seq_lens(g, B, cfg["lo"], cfg["hi"], dev)
+        self.pos = (self.seq_lens - 1).contiguous()
+        self.max_seq_len = int(self.seq_lens.max().item())
+        self.types = layer_types(cfg["layers"])
+        self.layers = []
+        s = self.shape
+        for lt in self.types:
+            t = workloads.layer_inputs(g, s, lt, dev)
+            cache = hda.LayerCache(t["k"], t["v"], t.get("kev"), t.get("vev"), s.num_q_heads,
+                                   s.window, s.rot(lt), s.theta(lt))
+            self.layers.append(dict(
+                lt=lt, q=t["q"], k_new=t["k_new"], v_new=t["v_new"], cache=cache, raw=t,
+                sinks=workloads.sinks(g, s.num_q_heads, dev),
+                out=torch.empty(B, s.num_q_heads, s.head_dim, dtype=torch.bfloat16, device=dev),
+                lse=torch.empty(B, s.num_q_heads, dtype=torch.float32, device=dev)))
+        self.scale = 1.0 / s.head_dim ** 0.5
+        ws = max(hda.hda_decode_workspace_bytes(L["cache"], L["lt"], self.max_seq_len, 0)
+                 for L in self.layers)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        sl = self.seq_lens.cpu().long()
+        self.kv_row_bytes = 2 * s.num_kv_heads * s.head_dim * 2  # K and V, all KV heads, bf16
+        self.rows = {lt: int((sl.clamp(max=s.window) if lt == workloads.SLIDING else sl).sum())
+                     for lt in (workloads.SLIDING, workloads.FULL)}
+        self.kv_bytes = sum(self.rows[lt] for lt in self.types) * self.kv_row_bytes
+
+    def step(self, chunk_keys=0):
+        import full_kv_cache_amd as hda
+        for L in self.layers:
+            hda.hda_rope_append(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"])
+            hda.hda_decode_attn(L["q"], L["cache"], self.seq_lens, L["lt"], L["sinks"], self.scale,
+                                L["out"], L["lse"], self.max_seq_len, chunk_keys, self.workspace)
+
+
+def time_graph(fn, steps, warmup, use_graph=True):
+    """Average ms per call of fn over `steps` runs, HIP events on the stream."""
+    import torch
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        fn()  # make sure every lazy init happened outside capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        run = g.replay
+    else:
+        run = fn
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    return t0.elapsed_time(t1) / steps, wall * 1e3 / steps
+
+
+def dominant_kernel(wl: Workload, steps, warmup, chunk_keys=0):
+    """Time the full-layer split-K kernel alone (the largest byte mover):
+    the 7 full layers' hda_decode_attn_partials calls captured in one graph,
+    average per launch from HIP events on the launch stream."""
+    import torch
+    import full_kv_cache_amd as hda
+    import workloads
+    full = [L for L in wl.layers if L["lt"] == workloads.FULL]
+    if not full:
+        return None
+    chunk, nsplit = hda.hda_decode_split_plan(full[0]["cache"], workloads.FULL, wl.max_seq_len,
+                                              chunk_keys)
+    B, H = wl.shape.batch, wl.shape.num_q_heads
+    part_o = torch.empty(B, H, nsplit, wl.shape.head_dim, dtype=torch.float32, device="cuda")
+    part_lse = torch.empty(B, H, nsplit, dtype=torch.float32, device="cuda")
+
+    def fn():
+        for L in full:
+            hda.hda_decode_attn_partials(L["q"], L["cache"], wl.seq_lens, workloads.FULL, wl.scale,
+                                         wl.max_seq_len, chunk_keys, part_o, part_lse)
+
+    ms, _ = time_graph(fn, steps, warmup)
+    per_launch_s = ms / len(full) / 1e3
+    algo = wl.rows[workloads.FULL] * wl.kv_row_bytes
+    achieved = algo / per_launch_s / 1e9
+    return {
+        "kernel": "decode_chunk_kernel<G=4, full, partial> (hda_decode_attn_partials)",
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "algorithmic_bytes_per_launch": algo, "avg_launch_us": round(per_launch_s * 1e6, 2),
+        "launches_timed": steps * len(full), "chunk_keys": chunk, "nsplit": nsplit,
+    }
+
+
+def cpu_baseline(wl: Workload, min_seconds: float):
+    """The oracle on host copies of the same workload: whole 28-layer steps
+    over the batch (append + attention per layer), repeated until at least
+    min_seconds have passed (at most 50 steps)."""
+    import numpy as np
+    import oracle
+    import workloads
+    s = wl.shape
+    host = []
+    for L in wl.layers:
+        h = {k: workloads.bits(v).copy() for k, v in L["raw"].items()}
+        h["q"] = workloads.bits(L["q"]).copy()
+        if L["lt"] == workloads.FULL:
+            h["kev"] = h["vev"] = np.zeros((s.batch, s.num_kv_heads, s.head_dim), np.uint16)
+        host.append((L["lt"], h, L["sinks"].cpu().numpy()))
+    pos = wl.pos.cpu().numpy()
+    seq = wl.seq_lens.cpu().numpy()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for lt, h, sk in host:
+            oracle.rope_append(h["q"], h["k_new"], h["v_new"], pos, lt, s.rot(lt), s.theta(lt),
+                               s.window, h["k"], h["v"], h["kev"], h["vev"])
+            oracle.decode_attn(h["q"], h["k"], h["v"], h["kev"], h["vev"], seq, lt, s.window, sk,
+                               wl.scale)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or steps >= 50:
+            break
+    return {
+        "value": round(wl.kv_bytes * steps / el / 1e9, 3), "unit": "GB/s",
+        "tokens_per_s": round(s.batch * steps / el, 2),
+        "cores": oracle.num_threads(), "kind": "oracle",
+        "sample": f"{steps} whole step(s) of the same workload ({s.batch} sequences x "
+                  f"{len(wl.layers)} layers, append + attention) in {el:.1f} s, fp64 C oracle",
+    }
+
+
+def copy_calibration(mb: int):
+    """A plain device copy of a known size, for scaling PMC byte counters."""
+    import torch
+    n = mb * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              "measured as one GPU's share at its full shape.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    import full_kv_cache_amd as hda
+    hda.lib()  # fail loudly if the library is missing
+
+    cfg = CONFIGS[args.config]
+    print(f"# building workload {args.config}: {cfg['desc']}", file=sys.stderr, flush=True)
+    wl = Workload(cfg, args.seed)
+    torch.cuda.synchronize()
+    step = lambda: wl.step(args.chunk_keys)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+
+    print("# timing step", file=sys.stderr, flush=True)
+    ms, wall_ms = time_graph(step, args.steps, args.warmup, use_graph=not args.no_graph)
+    eager_ms = None
+    if not args.no_graph:
+        eager_ms, _ = time_graph(step, max(3, args.steps // 5), 2, use_graph=False)
+    print("# timing dominant kernel", file=sys.stderr, flush=True)
+    roof = dominant_kernel(wl, args.steps, args.warmup, args.chunk_keys)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    gbs = wl.kv_bytes / (ms / 1e3) / 1e9
+    sl = wl.seq_lens.cpu()
+    rec = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded unit-normal bf16 q/K/V, N(0,1) fp32 sinks)",
+        "config": {"workload": f"{args.config}: {cfg['desc']}", "batch": cfg["batch"],
+                   "layers": cfg["layers"], "seq_len_min": int(sl.min()),
+                   "seq_len_max": int(sl.max()), "seq_len_mean": round(float(sl.float().mean()), 1),
+                   "graph": not args.no_graph, "chunk_keys": args.chunk_keys},
+        "tokens_per_s": round(cfg["batch"] / (ms / 1e3), 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": wl.kv_bytes,
+        "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
+        "host_wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,6 +73,14 @@ def lib() -> ctypes.CDLL:
         L.hda_decode_attn.restype = ctypes.c_int
         L.hda_decode_attn.argtypes = [P, D, P, ctypes.c_int, P, ctypes.c_float, P, P, i32, i32,
                                       P, sz, P]
+        L.hda_decode_split_plan.restype = ctypes.c_int
+        L.hda_decode_split_plan.argtypes = [D, ctypes.c_int, i32, i32, ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32)]
+        L.hda_decode_attn_partials.restype = ctypes.c_int
+        L.hda_decode_attn_partials.argtypes = [P, D, P, ctypes.c_int, ctypes.c_float, i32, i32,
+                                               P, P, P]
+        L.hda_lse_merge.restype = ctypes.c_int
+        L.hda_lse_merge.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
         L.hda_status_string.restype = ctypes.c_char_p
         L.hda_status_string.argtypes = [ctypes.c_int]
         L.hda_last_error_message.restype = ctypes.c_char_p
@@ -163,6 +171,35 @@ def hda_decode_attn(q, cache: LayerCache, seq_lens, layer_type: int, sinks, scal
                                  _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
                                  int(max_seq_len), int(chunk_keys), _ptr(workspace), wbytes,
                                  _stream(stream)))
+
+
+def hda_decode_split_plan(cache: LayerCache, layer_type: int, max_seq_len: int,
+                          chunk_keys: int = 0) -> tuple[int, int]:
+    """(keys per chunk, chunks per (sequence, KV head)) that hda_decode_attn uses."""
+    d = cache.desc()
+    c, n = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().hda_decode_split_plan(ctypes.byref(d), int(layer_type), int(max_seq_len),
+                                       int(chunk_keys), ctypes.byref(c), ctypes.byref(n)))
+    return c.value, n.value
+
+
+def hda_decode_attn_partials(q, cache: LayerCache, seq_lens, layer_type: int, scale: float,
+                             max_seq_len: int, chunk_keys: int, part_o, part_lse, stream=None):
+    """Split-K stage alone: part_o fp32 [B,Hq,nsplit,D], part_lse fp32 [B,Hq,nsplit]."""
+    d = cache.desc()
+    _check(lib().hda_decode_attn_partials(_ptr(q), ctypes.byref(d), _ptr(seq_lens),
+                                          int(layer_type), float(scale), int(max_seq_len),
+                                          int(chunk_keys), _ptr(part_o), _ptr(part_lse),
+                                          _stream(stream)))
+
+
+def hda_lse_merge(part_o, part_lse, sinks, out, lse=None, stream=None):
+    """Merge partials [B,H,nsplit,D] / [B,H,nsplit] into out bf16 [B,H,D] (+ sink)."""
+    B, H, S, D = part_o.shape
+    if sinks is not None:
+        validate_sinks(sinks, out)
+    _check(lib().hda_lse_merge(_ptr(part_o), _ptr(part_lse), int(B), int(H), int(S), int(D),
+                               _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def hda_sparse_decode_attn(q, kv, indices, topk_length, sinks, scale: float, dv: int, out,

@@ -97,8 +97,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
                 p.out[((int64_t)b * Hq + hq) * D + tid] = 0;
                 if (tid == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = -INFINITY;
             }
+        } else if (tid < G) {  // partial: a chunk without keys weighs zero in the merge
+            p.part_lse[((int64_t)b * Hq + kvh * G + tid) * p.nsplit + c] = -INFINITY;
         }
-        return;  // partial: the merge only reads chunks that hold keys
+        return;
     }
 
     // ---- Q as the MFMA A operand: lane (m = lane%16, kg = lane/16) holds
@@ -249,67 +251,70 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
     }
 }
 
-// One workgroup per (query head, sequence); thread = output dim.
-template <bool SLIDING>
-__global__ __launch_bounds__(kDecodeThreads) void lse_merge_kernel(DecodeParams p) {
+// One workgroup per (query head, sequence); thread = output dim.  Chunks
+// with lse = -inf hold no keys and are skipped (their out is never read).
+__global__ __launch_bounds__(kDecodeThreads) void lse_merge_kernel(MergeParams p) {
     constexpr int D = kHeadDim;
     const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const int Hq = p.num_q_heads;
-    const KeySpan span = key_span<SLIDING>(p, b);
-    const int S = (span.n_keys + p.chunk - 1) / p.chunk;
-    const int64_t base = ((int64_t)b * Hq + hq) * p.nsplit;
-    uint16_t *outp = p.out + ((int64_t)b * Hq + hq) * D + d;
-    if (S <= 0) {
+    const int64_t row = (int64_t)b * p.num_heads + hq;
+    const float *pl = p.part_lse + row * p.nsplit;
+    const float *po = p.part_o + row * p.nsplit * D + d;
+    float M = -INFINITY;
+    for (int c = 0; c < p.nsplit; ++c) M = fmaxf(M, pl[c]);
+    uint16_t *outp = p.out + row * D + d;
+    if (M == -INFINITY) {
         *outp = 0;
-        if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = -INFINITY;
+        if (d == 0 && p.lse) p.lse[row] = -INFINITY;
         return;
     }
-    float M = -INFINITY;
-    for (int c = 0; c < S; ++c) M = fmaxf(M, p.part_lse[base + c]);
     float L = 0.f, o = 0.f;
-    for (int c = 0; c < S; ++c) {
-        const float w = expf(p.part_lse[base + c] - M);
+    for (int c = 0; c < p.nsplit; ++c) {
+        const float lc = pl[c];
+        if (lc == -INFINITY) continue;
+        const float w = expf(lc - M);
         L += w;
-        o = fmaf(w, p.part_o[(base + c) * D + d], o);
+        o = fmaf(w, po[(int64_t)c * D], o);
     }
     const float lse = M + logf(L);
     float f = 1.f;
     if (p.sinks) f = 1.f / (1.f + expf(p.sinks[hq] - lse));
     *outp = f32_to_bf16((o / L) * f);
-    if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
+    if (d == 0 && p.lse) p.lse[row] = lse;
 }
 
-template <int G, bool SLIDING>
+template <int G, bool SLIDING, bool FINAL>
 hipError_t launch_g(const DecodeParams &p, hipStream_t s) {
     const dim3 grid(p.nsplit, p.num_kv_heads, p.batch);
-    if (p.nsplit == 1) {
-        hipLaunchKernelGGL((decode_chunk_kernel<G, SLIDING, true>), grid, dim3(kDecodeThreads), 0, s, p);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((decode_chunk_kernel<G, SLIDING, false>), grid, dim3(kDecodeThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((lse_merge_kernel<SLIDING>), dim3(p.num_q_heads, p.batch), dim3(kDecodeThreads), 0, s, p);
+    hipLaunchKernelGGL((decode_chunk_kernel<G, SLIDING, FINAL>), grid, dim3(kDecodeThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <bool SLIDING>
+template <bool SLIDING, bool FINAL>
 hipError_t launch_s(const DecodeParams &p, int group, hipStream_t s) {
     switch (group) {
-        case 1: return launch_g<1, SLIDING>(p, s);
-        case 2: return launch_g<2, SLIDING>(p, s);
-        case 4: return launch_g<4, SLIDING>(p, s);
-        case 8: return launch_g<8, SLIDING>(p, s);
-        case 16: return launch_g<16, SLIDING>(p, s);
+        case 1: return launch_g<1, SLIDING, FINAL>(p, s);
+        case 2: return launch_g<2, SLIDING, FINAL>(p, s);
+        case 4: return launch_g<4, SLIDING, FINAL>(p, s);
+        case 8: return launch_g<8, SLIDING, FINAL>(p, s);
+        case 16: return launch_g<16, SLIDING, FINAL>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams &p, bool sliding, int group, hipStream_t stream) {
+hipError_t launch_decode_chunks(const DecodeParams &p, bool sliding, int group, bool final_out,
+                               hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    return sliding ? launch_s<true>(p, group, stream) : launch_s<false>(p, group, stream);
+    if (final_out)
+        return sliding ? launch_s<true, true>(p, group, stream) : launch_s<false, true>(p, group, stream);
+    return sliding ? launch_s<true, false>(p, group, stream) : launch_s<false, false>(p, group, stream);
+}
+
+hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3(p.num_heads, p.batch), dim3(kDecodeThreads), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace hda

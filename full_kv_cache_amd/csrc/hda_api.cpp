@@ -196,28 +196,12 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
     return workspace_for(cache, plan_split(cache, layer, mk, chunk_keys));
 }
 
-hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int32_t *seq_lens,
-                           hda_layer_type layer, const float *sinks, float scale, void *out,
-                           float *lse, int32_t max_seq_len, int32_t chunk_keys, void *workspace,
-                           size_t workspace_bytes, void *stream) {
-    hda_status st = check_decode_shape(cache, layer, max_seq_len, chunk_keys);
-    if (st != HDA_OK) return st;
-    if (!q || !seq_lens || !out)
-        return fail(HDA_ERR_INVALID_ARGUMENT, "q, seq_lens and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(out))
-        return fail(HDA_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned");
-    if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
-    if (cache->batch == 0) return ok();
+namespace {
 
-    const int64_t mk = max_keys_of(cache, layer, max_seq_len);
-    const Plan pl = plan_split(cache, layer, mk, chunk_keys);
-    const size_t need = workspace_for(cache, pl);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", need,
-                    workspace_bytes, workspace);
-    if (need > 0 && !aligned16(workspace))
-        return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-
+// Fills the decode parameter block shared by the one-call and two-stage forms.
+hda::DecodeParams decode_params(const void *q, const hda_cache_desc *cache,
+                                const int32_t *seq_lens, int layer, float scale,
+                                int32_t max_seq_len, const Plan &pl) {
     hda::DecodeParams p{};
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(cache->k);
@@ -225,15 +209,6 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     p.kev = static_cast<const uint16_t *>(cache->k_evict);
     p.vev = static_cast<const uint16_t *>(cache->v_evict);
     p.seq_lens = seq_lens;
-    p.sinks = sinks;
-    p.out = static_cast<uint16_t *>(out);
-    p.lse = lse;
-    if (need > 0) {
-        const size_t slots = (size_t)cache->batch * cache->num_q_heads * pl.nsplit;
-        size_t obytes = (slots * hda::kHeadDim * sizeof(float) + 255) / 256 * 256;
-        p.part_o = static_cast<float *>(workspace);
-        p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + obytes);
-    }
     p.capacity = cache->capacity;
     p.batch = cache->batch;
     p.num_q_heads = cache->num_q_heads;
@@ -241,13 +216,127 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     p.window = cache->window;
     p.chunk = pl.chunk;
     p.nsplit = pl.nsplit;
-    p.max_keys = (int)(layer == HDA_SLIDING ? max_seq_len : mk);
+    p.max_keys = max_seq_len;
     p.scale_log2 = scale * 1.4426950408889634f;
-    const int g = cache->num_q_heads / cache->num_kv_heads;
-    hipError_t e = hda::launch_decode(p, layer == HDA_SLIDING, g, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(HDA_ERR_HIP, "decode_attn launch failed: %s", hipGetErrorString(e));
+    (void)layer;
+    return p;
+}
+
+hda_status check_decode_io(const void *q, const int32_t *seq_lens, float scale) {
+    if (!q || !seq_lens) return fail(HDA_ERR_INVALID_ARGUMENT, "q and seq_lens must be non-NULL");
+    if (!aligned16(q)) return fail(HDA_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
+    if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    return HDA_OK;
+}
+
+hda_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(HDA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+hda_status hda_decode_split_plan(const hda_cache_desc *cache, hda_layer_type layer,
+                                 int32_t max_seq_len, int32_t chunk_keys, int32_t *chunk_out,
+                                 int32_t *nsplit_out) {
+    hda_status st = check_decode_shape(cache, layer, max_seq_len, chunk_keys);
+    if (st != HDA_OK) return st;
+    if (!chunk_out || !nsplit_out)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "chunk_out and nsplit_out must be non-NULL");
+    const Plan pl = plan_split(cache, layer, max_keys_of(cache, layer, max_seq_len), chunk_keys);
+    *chunk_out = pl.chunk;
+    *nsplit_out = pl.nsplit;
+    return ok();
+}
+
+hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int32_t *seq_lens,
+                           hda_layer_type layer, const float *sinks, float scale, void *out,
+                           float *lse, int32_t max_seq_len, int32_t chunk_keys, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    hda_status st = check_decode_shape(cache, layer, max_seq_len, chunk_keys);
+    if (st != HDA_OK) return st;
+    if ((st = check_decode_io(q, seq_lens, scale)) != HDA_OK) return st;
+    if (!out || !aligned16(out))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "out must be non-NULL and 16-byte aligned");
+    if (cache->batch == 0) return ok();
+
+    const Plan pl = plan_split(cache, layer, max_keys_of(cache, layer, max_seq_len), chunk_keys);
+    const size_t need = workspace_for(cache, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", need,
+                    workspace_bytes, workspace);
+    if (need > 0 && !aligned16(workspace))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+    hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, pl);
+    p.sinks = sinks;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    const int g = cache->num_q_heads / cache->num_kv_heads;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pl.nsplit == 1)
+        return launched(hda::launch_decode_chunks(p, layer == HDA_SLIDING, g, true, s), "decode");
+
+    const size_t slots = (size_t)cache->batch * cache->num_q_heads * pl.nsplit;
+    const size_t obytes = (slots * hda::kHeadDim * sizeof(float) + 255) / 256 * 256;
+    p.part_o = static_cast<float *>(workspace);
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + obytes);
+    hipError_t e = hda::launch_decode_chunks(p, layer == HDA_SLIDING, g, false, s);
+    if (e != hipSuccess) return launched(e, "decode partials");
+    hda::MergeParams m{};
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.sinks = sinks;
+    m.out = p.out;
+    m.lse = lse;
+    m.batch = cache->batch;
+    m.num_heads = cache->num_q_heads;
+    m.nsplit = pl.nsplit;
+    return launched(hda::launch_lse_merge(m, s), "lse merge");
+}
+
+hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
+                                    const int32_t *seq_lens, hda_layer_type layer, float scale,
+                                    int32_t max_seq_len, int32_t chunk_keys, float *part_o,
+                                    float *part_lse, void *stream) {
+    hda_status st = check_decode_shape(cache, layer, max_seq_len, chunk_keys);
+    if (st != HDA_OK) return st;
+    if ((st = check_decode_io(q, seq_lens, scale)) != HDA_OK) return st;
+    if (!part_o || !part_lse || !aligned16(part_o))
+        return fail(HDA_ERR_INVALID_ARGUMENT,
+                    "part_o (16-byte aligned) and part_lse must be non-NULL");
+    if (cache->batch == 0) return ok();
+    const Plan pl = plan_split(cache, layer, max_keys_of(cache, layer, max_seq_len), chunk_keys);
+    hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, pl);
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    const int g = cache->num_q_heads / cache->num_kv_heads;
+    return launched(hda::launch_decode_chunks(p, layer == HDA_SLIDING, g, false,
+                                              static_cast<hipStream_t>(stream)),
+                    "decode partials");
+}
+
+hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t batch,
+                         int32_t num_heads, int32_t nsplit, int32_t head_dim, const float *sinks,
+                         void *out, float *lse, void *stream) {
+    if (batch < 0 || num_heads <= 0 || nsplit < 1)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "need batch >= 0, num_heads > 0, nsplit >= 1");
+    if (head_dim != hda::kHeadDim)
+        return fail(HDA_ERR_UNSUPPORTED, "merge kernel is built for head_dim %d, got %d",
+                    hda::kHeadDim, head_dim);
+    if (!part_o || !part_lse || !out)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "part_o, part_lse and out must be non-NULL");
+    if (batch == 0) return ok();
+    hda::MergeParams m{};
+    m.part_o = part_o;
+    m.part_lse = part_lse;
+    m.sinks = sinks;
+    m.out = static_cast<uint16_t *>(out);
+    m.lse = lse;
+    m.batch = batch;
+    m.num_heads = num_heads;
+    m.nsplit = nsplit;
+    return launched(hda::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "lse merge");
 }
 
 }  // extern "C"

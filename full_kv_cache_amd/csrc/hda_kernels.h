@@ -41,10 +41,23 @@ struct DecodeParams {
     float scale_log2;           // softmax scale * log2(e)
 };
 
+struct MergeParams {
+    const float *part_o;        // [B, H, nsplit, D]
+    const float *part_lse;      // [B, H, nsplit]
+    const float *sinks;         // [H] or null
+    uint16_t *out;              // [B, H, D]
+    float *lse;                 // [B, H] or null
+    int batch, num_heads, nsplit;
+};
+
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 
-// Launches the chunk kernel (final output when nsplit == 1, partials and a
-// merge otherwise).  group must be one of 1, 2, 4, 8, 16.
-hipError_t launch_decode(const DecodeParams &p, bool sliding, int group, hipStream_t stream);
+// Chunk kernel over grid (nsplit, Hkv, B).  final_out: nsplit must be 1 and
+// the kernel writes out/lse with the sink; otherwise it writes partials.
+// group must be one of 1, 2, 4, 8, 16.
+hipError_t launch_decode_chunks(const DecodeParams &p, bool sliding, int group, bool final_out,
+                               hipStream_t stream);
+
+hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 
 }  // namespace hda

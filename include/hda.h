@@ -168,6 +168,49 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache,
                            int32_t max_seq_len, int32_t chunk_keys,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * hda_decode_split_plan -- the chunking hda_decode_attn uses for these
+ * arguments: keys per chunk and chunks per (sequence, KV head).  Callers of
+ * the two-stage form below size their partial buffers from it.
+ */
+hda_status hda_decode_split_plan(const hda_cache_desc *cache, hda_layer_type layer,
+                                 int32_t max_seq_len, int32_t chunk_keys,
+                                 int32_t *chunk_out, int32_t *nsplit_out);
+
+/*
+ * hda_decode_attn_partials -- the split-K stage of hda_decode_attn alone
+ * (flash-decoding): chunk c of sequence b covers keys [c*chunk, (c+1)*chunk)
+ * of the key set hda_decode_attn defines, and yields for every query head
+ *   part_o[b, h, c, :] = softmax-weighted mean of V over the chunk's keys,
+ *   part_lse[b, h, c]  = ln sum over the chunk of exp(scores),
+ * with part_lse = -inf (part_o left unwritten) for a chunk holding no keys.
+ * Spark export page, ring-branch comment: a softmax split over key subsets
+ * and merged online equals the single pass.  Same arguments as
+ * hda_decode_attn; part_o fp32 [batch, num_q_heads, nsplit, head_dim],
+ * part_lse fp32 [batch, num_q_heads, nsplit], nsplit from
+ * hda_decode_split_plan.  No sink is applied here.
+ */
+hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
+                                    const int32_t *seq_lens, hda_layer_type layer,
+                                    float scale, int32_t max_seq_len, int32_t chunk_keys,
+                                    float *part_o, float *part_lse, void *stream);
+
+/*
+ * hda_lse_merge -- combine per-chunk partials into the attention output:
+ *   lse = ln sum_c exp(part_lse_c),  out = sum_c exp(part_lse_c - lse) part_o_c,
+ * chunks with part_lse = -inf weigh zero; then the sink factor
+ * exp(lse)/(exp(lse)+exp(sink[h])) (flashmla_sparse page, class docstring).
+ * No chunk holding keys: out 0, lse -inf.  Partials from several devices
+ * (context parallelism) merge the same way once gathered.
+ *   part_o   fp32 [batch, num_heads, nsplit, head_dim] (head_dim == 256)
+ *   part_lse fp32 [batch, num_heads, nsplit]
+ *   sinks    fp32 [num_heads] or NULL; out bf16 [batch, num_heads, head_dim];
+ *   lse      fp32 [batch, num_heads] or NULL (pre-sink).
+ */
+hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t batch,
+                         int32_t num_heads, int32_t nsplit, int32_t head_dim,
+                         const float *sinks, void *out, float *lse, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hda_status_string(hda_status status);
 
