@@ -1,7 +1,7 @@
 // hda_api.cpp -- C ABI of libhda: host-side validation, split planning and
 // kernel dispatch.  Declared in include/hda.h; every check here runs before
 // anything is enqueued, and nothing here synchronises or allocates.
-#include "../../include/hda.h"
+#include "hda.h"
 
 #include <hip/hip_runtime.h>
 
@@ -81,10 +81,9 @@ int64_t max_keys_of(const hda_cache_desc *c, int layer, int32_t max_seq_len) {
     return max_seq_len;
 }
 
-// Split plan: chunk size and chunks per (sequence, KV head).  A sliding
-// window of a large batch runs as one workgroup per (sequence, KV head)
-// and needs no merge; otherwise chunks are sized so that the grid holds
-// enough workgroups to cover the chip (256 CUs).
+// Split plan: chunk size and chunks per (sequence, KV head).  Chunks are
+// sized so that the grid holds enough workgroups to cover the chip (256
+// CUs), between 64 and 256 keys; a single chunk needs no merge.
 struct Plan {
     int chunk;
     int nsplit;
@@ -96,15 +95,11 @@ Plan plan_split(const hda_cache_desc *c, int layer, int64_t max_keys, int32_t ch
         pl.chunk = chunk_keys;
     } else {
         const int64_t pairs = (int64_t)c->batch * c->num_kv_heads;
-        if (layer == HDA_SLIDING && pairs >= 128 && max_keys <= hda::kMaxChunk) {
-            pl.chunk = hda::kMaxChunk;
-        } else {
-            int64_t want = (max_keys * pairs) / 512;  // aim at ~512 workgroups or more
-            want = (want + 15) / 16 * 16;
-            if (want < 64) want = 64;
-            if (want > 256) want = 256;
-            pl.chunk = (int)want;
-        }
+        int64_t want = (max_keys * pairs) / 512;  // aim at ~512 workgroups or more
+        want = (want + 15) / 16 * 16;
+        if (want < 64) want = 64;
+        if (want > 256) want = 256;
+        pl.chunk = (int)want;
     }
     pl.nsplit = (int)((max_keys + pl.chunk - 1) / pl.chunk);
     if (pl.nsplit < 1) pl.nsplit = 1;
@@ -164,6 +159,12 @@ hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const 
     if (st != HDA_OK) return st;
     if (!q || !k_new || !v_new || !pos)
         return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new and pos must be non-NULL");
+    if (cache->rotary_dim % 16 || cache->rotary_dim > 512)
+        return fail(HDA_ERR_UNSUPPORTED,
+                    "rope_append handles rotary_dim in multiples of 16 up to 512, got %d",
+                    cache->rotary_dim);
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new and v_new must be 16-byte aligned");
     if (cache->batch == 0) return ok();
     hda::RopeAppendParams p{};
     p.q = static_cast<uint16_t *>(q);

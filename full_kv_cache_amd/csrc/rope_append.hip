@@ -8,84 +8,165 @@
 // the cache row, copies v_new, and for a sliding layer first moves the
 // evicted slot content (still inside this step's window) to the side row.
 //
-// One workgroup per sequence.  Work is split into "units": a rotary pair
-// (dims j and j + rot/2) or one pass-through dim.  Each unit is owned by
-// exactly one thread, for every head, so the read of an old slot element
-// and the write of its replacement happen in the same thread and need no
-// barrier.  The work is a few KB per sequence: latency, not bandwidth,
-// bounds it.
+// One workgroup per sequence.  The work is cut into 16-byte tasks: a
+// rotary task owns 8 consecutive pairs (dims j..j+7 and j+h..j+h+7, h =
+// rot/2) of one head; a copy task owns 8 consecutive dims of a K
+// pass-through range or of V.  Each element belongs to exactly one task,
+// so the read of an old slot element and the write of its replacement
+// happen in one thread.  All global loads are issued first; the angle
+// table is built meanwhile (one pair index per thread: fp32 frequency
+// rounded once from fp64, fp32 angle, fp64 sin/cos rounded to fp32) and
+// shared through LDS; then results are rotated and stored.  A few KB per
+// sequence: latency, not bandwidth, bounds this kernel.
 #include "hda_device.h"
 #include "hda_kernels.h"
 
 namespace hda {
 
-__global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
+namespace {
+
+constexpr int kRopeThreads = 256;
+constexpr int kMaxHalf = 256;  // rotary_dim <= 512
+
+__device__ __forceinline__ void rotate8(const uint4 &a, const uint4 &b, const float *c,
+                                        const float *s, uint4 &ya, uint4 &yb) {
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x1l = bf16_lo(wa[i]), x1h = bf16_hi(wa[i]);
+        const float x2l = bf16_lo(wb[i]), x2h = bf16_hi(wb[i]);
+        const float cl = c[2 * i], sl = s[2 * i], ch = c[2 * i + 1], sh = s[2 * i + 1];
+        // first half: x1*cos - x2*sin; second half: x2*cos + x1*sin
+        const uint16_t y1l = f32_to_bf16(fmaf(x1l, cl, -x2l * sl));
+        const uint16_t y1h = f32_to_bf16(fmaf(x1h, ch, -x2h * sh));
+        const uint16_t y2l = f32_to_bf16(fmaf(x2l, cl, x1l * sl));
+        const uint16_t y2h = f32_to_bf16(fmaf(x2h, ch, x1h * sh));
+        ra[i] = (uint32_t)y1l | ((uint32_t)y1h << 16);
+        rb[i] = (uint32_t)y2l | ((uint32_t)y2h << 16);
+    }
+    ya = make_uint4(ra[0], ra[1], ra[2], ra[3]);
+    yb = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+__device__ __forceinline__ uint4 ld(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st(uint16_t *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+}  // namespace
+
+__global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendParams p) {
+    __shared__ float s_cos[kMaxHalf], s_sin[kMaxHalf];
     const int b = blockIdx.x;
     const int D = p.head_dim, rot = p.rotary_dim, half = rot / 2;
     const int32_t pos = p.pos[b];
     const int64_t cap = p.capacity;
 
-    int64_t row;
+    int64_t row = -1;
     bool evict = false;
     if (p.sliding) {
         const int32_t slots = p.window - 1;
-        if (pos < 0) return;
-        row = pos % slots;
-        evict = pos >= slots;
-    } else {
-        if (pos < 0 || (int64_t)pos >= cap) return;
+        if (pos >= 0) {
+            row = pos % slots;
+            evict = pos >= slots;
+        }
+    } else if (pos >= 0 && (int64_t)pos < cap) {
         row = pos;
     }
+    const bool write_cache = row >= 0;
 
-    const int n_units = half + (D - rot);
-    for (int u = threadIdx.x; u < n_units; u += blockDim.x) {
-        if (u < half) {
-            const int j = u;
-            // Frequency rounded once to fp32 from an fp64 evaluation of
-            // 1 / theta^(2j/rot); the angle is one fp32 multiply.
-            const double expo = (double)(2 * j) / (double)rot;
-            const float inv = (float)(1.0 / pow(p.theta, expo));
-            const float ang = (float)pos * inv;
-            double sd, cd;
-            sincos((double)ang, &sd, &cd);
-            const float c = (float)cd, s = (float)sd;
+    // Task space: [q rotary | k rotary | k pass-through | v], 16 bytes each.
+    const int hc = half / 8, pc = (D - rot) / 8, vc = D / 8;
+    const int n_q = p.num_q_heads * hc;
+    const int n_k = p.num_kv_heads * hc;
+    const int n_kp = p.num_kv_heads * pc;
+    const int n_v = p.num_kv_heads * vc;
+    const int n_tasks = n_q + n_k + n_kp + n_v;
 
-            for (int h = 0; h < p.num_q_heads; ++h) {
+    // Rounds of two tasks per thread; every round issues its loads first.
+    for (int base = 0; base < n_tasks; base += 2 * kRopeThreads) {
+        int task[2];
+        uint4 xa[2], xb[2], oa[2], ob[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int t = base + threadIdx.x + r * kRopeThreads;
+            task[r] = t < n_tasks ? t : -1;
+            if (task[r] < 0) continue;
+            if (t < n_q) {
+                const int h = t / hc, j = (t % hc) * 8;
+                const uint16_t *qr = p.q + ((int64_t)b * p.num_q_heads + h) * D;
+                xa[r] = ld(qr + j);
+                xb[r] = ld(qr + half + j);
+            } else if (!write_cache) {
+                task[r] = -1;
+            } else if (t < n_q + n_k) {
+                const int u = t - n_q, h = u / hc, j = (u % hc) * 8;
+                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
+                xa[r] = ld(p.k_new + bh * D + j);
+                xb[r] = ld(p.k_new + bh * D + half + j);
+                if (evict) {
+                    const uint16_t *kr = p.k + (bh * cap + row) * D;
+                    oa[r] = ld(kr + j);
+                    ob[r] = ld(kr + half + j);
+                }
+            } else if (t < n_q + n_k + n_kp) {
+                const int u = t - n_q - n_k, h = u / pc, d = rot + (u % pc) * 8;
+                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
+                xa[r] = ld(p.k_new + bh * D + d);
+                if (evict) oa[r] = ld(p.k + (bh * cap + row) * D + d);
+            } else {
+                const int u = t - n_q - n_k - n_kp, h = u / vc, d = (u % vc) * 8;
+                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
+                xa[r] = ld(p.v_new + bh * D + d);
+                if (evict) oa[r] = ld(p.v + (bh * cap + row) * D + d);
+            }
+        }
+
+        if (base == 0) {  // angle table while the first loads are in flight
+            for (int j = threadIdx.x; j < half; j += kRopeThreads) {
+                const double expo = (double)(2 * j) / (double)rot;
+                const float inv = (float)(1.0 / pow(p.theta, expo));
+                const float ang = (float)pos * inv;  // one fp32 multiply
+                double sd, cd;
+                sincos((double)ang, &sd, &cd);
+                s_cos[j] = (float)cd;
+                s_sin[j] = (float)sd;
+            }
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int t = task[r];
+            if (t < 0) continue;
+            if (t < n_q) {
+                const int h = t / hc, j = (t % hc) * 8;
                 uint16_t *qr = p.q + ((int64_t)b * p.num_q_heads + h) * D;
-                const float x1 = bf16_to_f32(qr[j]), x2 = bf16_to_f32(qr[j + half]);
-                qr[j] = f32_to_bf16(fmaf(x1, c, -x2 * s));
-                qr[j + half] = f32_to_bf16(fmaf(x2, c, x1 * s));
-            }
-            for (int h = 0; h < p.num_kv_heads; ++h) {
+                uint4 ya, yb;
+                rotate8(xa[r], xb[r], s_cos + j, s_sin + j, ya, yb);
+                st(qr + j, ya);
+                st(qr + half + j, yb);
+            } else if (t < n_q + n_k) {
+                const int u = t - n_q, h = u / hc, j = (u % hc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
-                const uint16_t *kn = p.k_new + bh * D;
-                const uint16_t *vn = p.v_new + bh * D;
-                uint16_t *kr = p.k + (bh * cap + row) * D;
-                uint16_t *vr = p.v + (bh * cap + row) * D;
                 if (evict) {
-                    p.k_evict[bh * D + j] = kr[j];
-                    p.k_evict[bh * D + j + half] = kr[j + half];
-                    p.v_evict[bh * D + j] = vr[j];
-                    p.v_evict[bh * D + j + half] = vr[j + half];
+                    st(p.k_evict + bh * D + j, oa[r]);
+                    st(p.k_evict + bh * D + half + j, ob[r]);
                 }
-                const float x1 = bf16_to_f32(kn[j]), x2 = bf16_to_f32(kn[j + half]);
-                kr[j] = f32_to_bf16(fmaf(x1, c, -x2 * s));
-                kr[j + half] = f32_to_bf16(fmaf(x2, c, x1 * s));
-                vr[j] = vn[j];
-                vr[j + half] = vn[j + half];
-            }
-        } else {
-            const int d = rot + (u - half);  // pass-through dim: q unchanged
-            for (int h = 0; h < p.num_kv_heads; ++h) {
+                uint4 ya, yb;
+                rotate8(xa[r], xb[r], s_cos + j, s_sin + j, ya, yb);
+                uint16_t *kr = p.k + (bh * cap + row) * D;
+                st(kr + j, ya);
+                st(kr + half + j, yb);
+            } else if (t < n_q + n_k + n_kp) {
+                const int u = t - n_q - n_k, h = u / pc, d = rot + (u % pc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
-                uint16_t *kr = p.k + (bh * cap + row) * D;
-                uint16_t *vr = p.v + (bh * cap + row) * D;
-                if (evict) {
-                    p.k_evict[bh * D + d] = kr[d];
-                    p.v_evict[bh * D + d] = vr[d];
-                }
-                kr[d] = p.k_new[bh * D + d];
-                vr[d] = p.v_new[bh * D + d];
+                if (evict) st(p.k_evict + bh * D + d, oa[r]);
+                st(p.k + (bh * cap + row) * D + d, xa[r]);
+            } else {
+                const int u = t - n_q - n_k - n_kp, h = u / vc, d = (u % vc) * 8;
+                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
+                if (evict) st(p.v_evict + bh * D + d, oa[r]);
+                st(p.v + (bh * cap + row) * D + d, xa[r]);
             }
         }
     }
@@ -93,7 +174,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeAppendParams p) {
 
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(rope_append_kernel, dim3(p.batch), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(rope_append_kernel, dim3(p.batch), dim3(kRopeThreads), 0, stream, p);
     return hipGetLastError();
 }
 
