@@ -70,17 +70,23 @@ __device__ __forceinline__ const uint16_t *row_ptr(const uint16_t *base, const u
     return base + (int64_t)idx * kHeadDim;
 }
 
+// Orders this wave's LDS writes before its later LDS reads (LDS executes a
+// wave's instructions in order; this stops the compiler from moving them).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int G, bool SLIDING, bool FINAL>
 __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodeParams p) {
     constexpr int D = kHeadDim;
-    constexpr int CH = kMaxChunk;
-    constexpr int SC_FLOATS = 2 * G * CH;   // scores + probabilities
-    constexpr int RED_FLOATS = 4 * G * D;   // per-wave partial outputs
-    constexpr int SMEM_FLOATS = SC_FLOATS > RED_FLOATS ? SC_FLOATS : RED_FLOATS;
-    __shared__ __align__(16) float smem[SMEM_FLOATS];
-    __shared__ float s_m[G], s_l[G];
-    float *s_sc = smem;            // [G][CH]  scores, log2 domain
-    float *s_p = smem + G * CH;    // [CH][G]  probabilities, key-major
+    constexpr int WAVES = kDecodeThreads / 64;
+    constexpr int RK = 32;                       // keys per round per wave
+    constexpr int HG = (G + 3) / 4;              // 16-lane groups holding real heads
+    constexpr int RED_FLOATS = WAVES * G * D;    // per-wave partial outputs
+    __shared__ __align__(16) float s_red[RED_FLOATS];
+    __shared__ __align__(16) float s_p[WAVES][RK * G];  // this round's probabilities
+    __shared__ float s_m[WAVES][G], s_l[WAVES][G];
 
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -103,6 +109,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
         return;
     }
 
+    // Wave w owns chunk keys [kw0, kw0 + R*RK), processed in rounds of RK.
+    const int R = (p.chunk + WAVES * RK - 1) / (WAVES * RK);
+    const int kw0 = wave * R * RK;
+    const int kw1 = min(kw0 + R * RK, n);
+    const int rounds = kw1 > kw0 ? (kw1 - kw0 + RK - 1) / RK : 0;
+
+    const uint16_t *kbase = p.k + bh * p.capacity * D;
+    const uint16_t *vbase = p.v + bh * p.capacity * D;
+    const uint16_t *kside = SLIDING ? p.kev + bh * D : nullptr;
+    const uint16_t *vside = SLIDING ? p.vev + bh * D : nullptr;
+
     // ---- Q as the MFMA A operand: lane (m = lane%16, kg = lane/16) holds
     // q[head m][32j + 8kg .. +7] for k-step j; rows m >= G are zero.
     const int mrow = lane & 15, kg = lane >> 4;
@@ -118,125 +135,145 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
         }
     }
 
-    const uint16_t *kbase = p.k + bh * p.capacity * D;
-    const uint16_t *vbase = p.v + bh * p.capacity * D;
-    const uint16_t *kside = SLIDING ? p.kev + bh * D : nullptr;
-    const uint16_t *vside = SLIDING ? p.vev + bh * D : nullptr;
-
-    // ---- 1. scores of 16-key tiles; wave w takes tiles w, w+4, ...; two
-    // tiles per iteration keep 16 loads per lane in flight.
-    const int ntiles = (n + 15) >> 4;
-    for (int t = wave; t < ntiles; t += 8) {
-        uint4 ka[8], kb[8];
-        const int keyA = t * 16 + mrow, keyB = keyA + 64;
-        const bool vA = keyA < n, vB = keyB < n;
-        const uint16_t *rA = row_ptr<SLIDING>(kbase, kside, c0 + (vA ? keyA : 0), span.n_ring) + 8 * kg;
-        const uint16_t *rB = row_ptr<SLIDING>(kbase, kside, c0 + (vB ? keyB : 0), span.n_ring) + 8 * kg;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ka[j] = vA ? ld16_stream(rA + 32 * j) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kb[j] = vB ? ld16_stream(rB + 32 * j) : make_uint4(0, 0, 0, 0);
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accB = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(ka[j]), accA, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            accB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kb[j]), accB, 0, 0, 0);
-        // lane holds heads 4*kg + i (i = 0..3) for key (tile*16 + mrow)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * kg + i;
-            if (h < G) {
-                s_sc[h * CH + keyA] = vA ? accA[i] * p.scale_log2 : -INFINITY;
-                if (t + 4 < ntiles) s_sc[h * CH + keyB] = vB ? accB[i] * p.scale_log2 : -INFINITY;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- 2. chunk softmax statistics, one wave per head.
-    for (int h = wave; h < G; h += 4) {
-        float mx = -INFINITY;
-        for (int k = lane; k < n; k += 64) mx = fmaxf(mx, s_sc[h * CH + k]);
-        mx = wave_max(mx);
-        float sum = 0.f;
-        for (int k = lane; k < n; k += 64) {
-            const float e = exp2f(s_sc[h * CH + k] - mx);
-            s_p[k * G + h] = e;
-            sum += e;
-        }
-        sum = wave_sum(sum);
-        if (lane == 0) {
-            s_m[h] = mx;
-            s_l[h] = sum;
-        }
-    }
-    __syncthreads();
-
-    // ---- 3. P.V: 8 streams (4 waves x 2 half-waves) over the keys; a
-    // half-wave reads one whole 512-byte V row per load, lane = 8 dims.
-    const int hw = lane >> 5, dl = lane & 31;
-    const int stream = wave * 2 + hw;
+    const int hw = lane >> 5, dl = lane & 31;  // V: half-wave = one row, lane = 8 dims
     float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    // Running max (log2 domain) and this lane's share of the running sum,
+    // for heads 4*kg + i; uniform within each 16-lane group.
+    float m_run[4], l_lane[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m_run[i] = -INFINITY;
+        l_lane[i] = 0.f;
+    }
+    float *pw = s_p[wave];
 
-    constexpr int U = 8;
-    for (int k0 = stream; k0 < n; k0 += 8 * U) {
-        uint4 vv[U];
+    for (int r = 0; r < rounds; ++r) {
+        const int kr = kw0 + r * RK;
+        // Every load is unconditional (tail keys read the last valid row
+        // and are masked below), so the compiler can count them exactly
+        // and V stays in flight while the scores are computed.
+        uint4 kt[2][8], vt[16];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = k0 + 8 * u;
-            vv[u] = make_uint4(0, 0, 0, 0);
-            if (k < n) vv[u] = ld16_stream(row_ptr<SLIDING>(vbase, vside, c0 + k, span.n_ring) + 8 * dl);
+        for (int t = 0; t < 2; ++t) {
+            const int key = min(kr + t * 16 + mrow, n - 1);
+            const uint16_t *rp = row_ptr<SLIDING>(kbase, kside, c0 + key, span.n_ring) + 8 * kg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kt[t][j] = ld16_stream(rp + 32 * j);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = k0 + 8 * u;
-            if (k < n) {
-                float pv[G];
+        for (int u = 0; u < 16; ++u) {
+            const int key = min(kr + 2 * u + hw, n - 1);
+            vt[u] = ld16_stream(row_ptr<SLIDING>(vbase, vside, c0 + key, span.n_ring) + 8 * dl);
+        }
+
+        // QK^T: lane holds heads 4*kg + i for key kr + 16t + mrow.
+        f32x4 sc[2];
 #pragma unroll
-                for (int h = 0; h < G; ++h) pv[h] = s_p[k * G + h];
-                const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-                float x[8];
+        for (int t = 0; t < 2; ++t) {
+            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[2 * i] = bf16_lo(w[i]);
-                    x[2 * i + 1] = bf16_hi(w[i]);
-                }
+            for (int j = 0; j < 8; ++j)
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kt[t][j]), sc[t], 0, 0, 0);
+        }
+        float alpha[4];
 #pragma unroll
-                for (int h = 0; h < G; ++h)
+        for (int i = 0; i < 4; ++i) {
+            float s0 = kr + mrow < n ? sc[0][i] * p.scale_log2 : -INFINITY;
+            float s1 = kr + 16 + mrow < n ? sc[1][i] * p.scale_log2 : -INFINITY;
+            float mx = fmaxf(s0, s1);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
+            for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            const float mn = fmaxf(m_run[i], mx);  // finite: key kr is valid
+            alpha[i] = exp2f(m_run[i] - mn);
+            s0 = exp2f(s0 - mn);
+            s1 = exp2f(s1 - mn);
+            l_lane[i] = fmaf(l_lane[i], alpha[i], s0 + s1);
+            m_run[i] = mn;
+            sc[0][i] = s0;
+            sc[1][i] = s1;
+        }
+        if (kg < HG) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * kg + i < G) pw[(t * 16 + mrow) * G + 4 * kg + i] = sc[t][i];
+        }
+        // Rescale the running output by each head's alpha (uniform per head).
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float af =
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= af;
+        }
+        wave_lds_fence();
+
+        // P.V: key kr + 2u + hw, 8 dims per lane.
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            float pv[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) pv[h] = pw[(2 * u + hw) * G + h];
+            const uint32_t w[4] = {vt[u].x, vt[u].y, vt[u].z, vt[u].w};
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = bf16_lo(w[i]);
+                x[2 * i + 1] = bf16_hi(w[i]);
             }
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
         }
+        wave_lds_fence();
     }
 
-    // ---- 4. reduce the 8 streams: halves by shuffle, waves through LDS.
+    // ---- merge the waves: halves by shuffle, waves through LDS with
+    // their own maxima rescaled to the common one.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) l_lane[i] += __shfl_xor(l_lane[i], o, 64);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
-    __syncthreads();  // s_p is dead from here: reuse smem
-    float *red = smem;  // [4][G][D]
     if (hw == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[(wave * G + h) * D + 8 * dl + e] = acc[h][e];
+            for (int e = 0; e < 8; ++e) s_red[(wave * G + h) * D + 8 * dl + e] = acc[h][e];
+    }
+    if (mrow == 0 && kg < HG) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * kg + i < G) {
+                s_m[wave][4 * kg + i] = m_run[i];
+                s_l[wave][4 * kg + i] = l_lane[i];
+            }
     }
     __syncthreads();
 
     const int d = tid;  // blockDim == D
     for (int h = 0; h < G; ++h) {
-        const float o = (red[(0 * G + h) * D + d] + red[(1 * G + h) * D + d]) +
-                        (red[(2 * G + h) * D + d] + red[(3 * G + h) * D + d]);
-        const float l = s_l[h];
-        const float on = o / l;
-        const float lse = (s_m[h] + log2f(l)) * kLn2;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float sc = exp2f(s_m[w][h] - M);  // wave without keys: 2^-inf = 0
+            L = fmaf(sc, s_l[w][h], L);
+            o = fmaf(sc, s_red[(w * G + h) * D + d], o);
+        }
+        const float on = o / L;
+        const float lse = (M + log2f(L)) * kLn2;
         const int hq = kvh * G + h;
         if (FINAL) {
             float f = 1.f;
