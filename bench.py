@@ -2,8 +2,9 @@
 """Decode-attention throughput of the hybrid model on one MI355X.
 
 One step is one decode step of the attention path for a whole batch: for
-each of the 28 layers (21 sliding with a 512-token window held as 511 ring
-slots plus a side row, 7 full; layer i is full when i % 4 == 3)
+each of the 28 layers (21 sliding with a 512-token window held as a
+512-row block -- 511 ring slots plus the evicted-entry row -- and 7 full;
+layer i is full when i % 4 == 3)
 
     hda_rope_append  -- rotate q in place, write the rotated new K and V
                         into the ring slot (sliding) or row pos (full);
@@ -94,8 +95,7 @@ class Workload:
         s = self.shape
         for lt in self.types:
             t = workloads.layer_inputs(g, s, lt, dev)
-            cache = hda.LayerCache(t["k"], t["v"], t.get("kev"), t.get("vev"), s.num_q_heads,
-                                   s.window, s.rot(lt), s.theta(lt))
+            cache = hda.LayerCache(t["k"], t["v"], s.num_q_heads, s.window, s.rot(lt), s.theta(lt))
             self.layers.append(dict(
                 lt=lt, q=t["q"], k_new=t["k_new"], v_new=t["v_new"], cache=cache, raw=t,
                 sinks=workloads.sinks(g, s.num_q_heads, dev),
@@ -104,7 +104,7 @@ class Workload:
         self.scale = 1.0 / s.head_dim ** 0.5
         ws = max(hda.hda_decode_workspace_bytes(L["cache"], L["lt"], self.max_seq_len, 0)
                  for L in self.layers)
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         sl = self.seq_lens.cpu().long()
         self.kv_row_bytes = 2 * s.num_kv_heads * s.head_dim * 2  # K and V, all KV heads, bf16
         self.rows = {lt: int((sl.clamp(max=s.window) if lt == workloads.SLIDING else sl).sum())
@@ -147,36 +147,33 @@ def time_graph(fn, steps, warmup, use_graph=True):
 
 
 def dominant_kernel(wl: Workload, steps, warmup, chunk_keys=0):
-    """Time the full-layer split-K kernel alone (the largest byte mover):
-    the 7 full layers' hda_decode_attn_partials calls captured in one graph,
-    average per launch from HIP events on the launch stream."""
-    import torch
+    """Time the full-layer decode attention alone -- the largest byte mover
+    of the step: the 7 full layers' hda_decode_attn calls (exactly as the
+    step makes them) captured in one graph, HIP events on the launch stream
+    around the replays, average per call.  One call is the streaming kernel
+    plus its LSE merge; the rocprof summary gives the split."""
     import full_kv_cache_amd as hda
     import workloads
     full = [L for L in wl.layers if L["lt"] == workloads.FULL]
     if not full:
         return None
-    chunk, nsplit = hda.hda_decode_split_plan(full[0]["cache"], workloads.FULL, wl.max_seq_len,
-                                              chunk_keys)
-    B, H = wl.shape.batch, wl.shape.num_q_heads
-    part_o = torch.empty(B, H, nsplit, wl.shape.head_dim, dtype=torch.float32, device="cuda")
-    part_lse = torch.empty(B, H, nsplit, dtype=torch.float32, device="cuda")
 
     def fn():
         for L in full:
-            hda.hda_decode_attn_partials(L["q"], L["cache"], wl.seq_lens, workloads.FULL, wl.scale,
-                                         wl.max_seq_len, chunk_keys, part_o, part_lse)
+            hda.hda_decode_attn(L["q"], L["cache"], wl.seq_lens, workloads.FULL, L["sinks"],
+                                wl.scale, L["out"], L["lse"], wl.max_seq_len, chunk_keys,
+                                wl.workspace)
 
     ms, _ = time_graph(fn, steps, warmup)
-    per_launch_s = ms / len(full) / 1e3
+    per_call_s = ms / len(full) / 1e3
     algo = wl.rows[workloads.FULL] * wl.kv_row_bytes
-    achieved = algo / per_launch_s / 1e9
+    achieved = algo / per_call_s / 1e9
     return {
-        "kernel": "decode_chunk_kernel<G=4, full, partial> (hda_decode_attn_partials)",
+        "kernel": "full-layer hda_decode_attn: decode_stream_kernel<4> + stream_merge_kernel",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "algorithmic_bytes_per_launch": algo, "avg_launch_us": round(per_launch_s * 1e6, 2),
-        "launches_timed": steps * len(full), "chunk_keys": chunk, "nsplit": nsplit,
+        "algorithmic_bytes_per_launch": algo, "avg_launch_us": round(per_call_s * 1e6, 2),
+        "launches_timed": steps * len(full),
     }
 
 
@@ -189,10 +186,16 @@ def cpu_baseline(wl: Workload, min_seconds: float):
     import workloads
     s = wl.shape
     host = []
+    W = s.window
     for L in wl.layers:
         h = {k: workloads.bits(v).copy() for k, v in L["raw"].items()}
         h["q"] = workloads.bits(L["q"]).copy()
-        if L["lt"] == workloads.FULL:
+        if L["lt"] == workloads.SLIDING:  # the oracle keeps ring and side row apart
+            for a in ("k", "v"):
+                blk = h[a]
+                h[a] = np.ascontiguousarray(blk[:, :, :W - 1])
+                h[a + "ev"] = np.ascontiguousarray(blk[:, :, W - 1])
+        else:
             h["kev"] = h["vev"] = np.zeros((s.batch, s.num_kv_heads, s.head_dim), np.uint16)
         host.append((L["lt"], h, L["sinks"].cpu().numpy()))
     pos = wl.pos.cpu().numpy()

@@ -48,8 +48,6 @@ class CacheDesc(ctypes.Structure):
         ("rope_theta", ctypes.c_double),
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
-        ("k_evict", ctypes.c_void_p),
-        ("v_evict", ctypes.c_void_p),
     ]
 
 
@@ -112,13 +110,11 @@ def _stream(stream) -> ctypes.c_void_p:
 class LayerCache:
     """One layer's KV cache tensors plus the shape facts of hda_cache_desc.
 
-    k, v: bf16 [B, Hkv, capacity, D]; k_evict, v_evict: bf16 [B, Hkv, D]
-    (sliding layers only).
+    k, v: bf16 [B, Hkv, capacity, D]; a sliding layer has capacity == window
+    (window-1 ring slots, then the evicted-entry row).
     """
     k: torch.Tensor
     v: torch.Tensor
-    k_evict: Optional[torch.Tensor]
-    v_evict: Optional[torch.Tensor]
     num_q_heads: int
     window: int
     rotary_dim: int
@@ -127,9 +123,7 @@ class LayerCache:
     def desc(self) -> CacheDesc:
         B, Hkv, cap, D = self.k.shape
         return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim, cap,
-                         float(self.rope_theta), self.k.data_ptr(), self.v.data_ptr(),
-                         None if self.k_evict is None else self.k_evict.data_ptr(),
-                         None if self.v_evict is None else self.v_evict.data_ptr())
+                         float(self.rope_theta), self.k.data_ptr(), self.v.data_ptr())
 
 
 def hda_rope_append(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, stream=None):

@@ -56,14 +56,11 @@ hda_status check_cache(const hda_cache_desc *c, int layer) {
         return fail(HDA_ERR_INVALID_ARGUMENT, "rope_theta must be positive and finite");
     if (layer == HDA_SLIDING) {
         if (c->window < 2) return fail(HDA_ERR_INVALID_ARGUMENT, "window %d < 2", c->window);
-        if (c->capacity != (int64_t)c->window - 1)
+        if (c->capacity != (int64_t)c->window)
             return fail(HDA_ERR_INVALID_ARGUMENT,
-                        "sliding capacity %lld must be window-1 = %d ring slots",
-                        (long long)c->capacity, c->window - 1);
-        if (!c->k_evict || !c->v_evict)
-            return fail(HDA_ERR_INVALID_ARGUMENT, "sliding layer needs k_evict and v_evict");
-        if (!aligned16(c->k_evict) || !aligned16(c->v_evict))
-            return fail(HDA_ERR_INVALID_ARGUMENT, "k_evict/v_evict must be 16-byte aligned");
+                        "sliding capacity %lld must equal window %d (window-1 ring slots plus "
+                        "the evicted-entry row)",
+                        (long long)c->capacity, c->window);
     } else {
         if (c->capacity < 1)
             return fail(HDA_ERR_INVALID_ARGUMENT, "full-layer capacity %lld < 1",
@@ -106,6 +103,7 @@ Plan plan_split(const hda_cache_desc *c, int layer, int64_t max_keys, int32_t ch
     return pl;
 }
 
+// Chunk path: [part_o | part_lse].
 size_t workspace_for(const hda_cache_desc *c, const Plan &pl) {
     if (pl.nsplit <= 1) return 0;
     const size_t slots = (size_t)c->batch * c->num_q_heads * pl.nsplit;
@@ -113,6 +111,43 @@ size_t workspace_for(const hda_cache_desc *c, const Plan &pl) {
     bytes = (bytes + 255) / 256 * 256;
     bytes += slots * sizeof(float);
     return bytes;
+}
+
+// Balanced streaming path (chunk_keys == 0): a grid of resident
+// single-wave workgroups shares all 16-key rounds; partial slots = waves +
+// (sequence, KV head) pairs.
+bool use_stream(const hda_cache_desc *c, int32_t chunk_keys) {
+    return chunk_keys == 0 && c->batch <= hda::kStreamMaxBatch;
+}
+
+// As many waves as fit on the device at once, but no more than ~4 rounds
+// (64 keys) each would need.
+int stream_waves(const hda_cache_desc *c, int64_t max_keys) {
+    const int64_t rounds = (int64_t)c->batch * c->num_kv_heads * ((max_keys + 15) / 16);
+    int slots = hda::stream_wave_slots(c->num_q_heads / c->num_kv_heads);
+    if (slots <= 0 || slots > hda::kStreamMaxWaves) slots = hda::kStreamMaxWaves;
+    int64_t w = (rounds + 3) / 4;
+    if (w > slots) w = slots;
+    if (w < 1) w = 1;
+    return (int)w;
+}
+
+// Workspace of the streaming path: [part_o | part_lse | round prefix],
+// each part 256-byte aligned.
+struct StreamLayout {
+    size_t o_off, lse_off, pre_off, bytes;
+};
+
+StreamLayout stream_layout(const hda_cache_desc *c, int waves) {
+    const size_t slots = (size_t)waves + (size_t)c->batch * c->num_kv_heads;
+    const size_t g = (size_t)(c->num_q_heads / c->num_kv_heads);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    StreamLayout L;
+    L.o_off = 0;
+    L.lse_off = up(slots * g * hda::kHeadDim * sizeof(float));
+    L.pre_off = L.lse_off + up(slots * g * sizeof(float));
+    L.bytes = L.pre_off + up(((size_t)c->batch + 1) * sizeof(int));
+    return L;
 }
 
 hda_status check_decode_shape(const hda_cache_desc *c, int layer, int32_t max_seq_len,
@@ -125,6 +160,9 @@ hda_status check_decode_shape(const hda_cache_desc *c, int layer, int32_t max_se
     const int g = c->num_q_heads / c->num_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
         return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
+    if (c->capacity < 16)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels need a cache of at least 16 rows, got %lld",
+                    (long long)c->capacity);
     if (max_seq_len < 1) return fail(HDA_ERR_INVALID_ARGUMENT, "max_seq_len %d < 1", max_seq_len);
     if (layer == HDA_FULL && max_seq_len > c->capacity)
         return fail(HDA_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds cache capacity %lld",
@@ -173,8 +211,6 @@ hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const 
     p.pos = pos;
     p.k = static_cast<uint16_t *>(cache->k);
     p.v = static_cast<uint16_t *>(cache->v);
-    p.k_evict = static_cast<uint16_t *>(cache->k_evict);
-    p.v_evict = static_cast<uint16_t *>(cache->v_evict);
     p.capacity = cache->capacity;
     p.theta = cache->rope_theta;
     p.batch = cache->batch;
@@ -194,6 +230,7 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
                                   int32_t max_seq_len, int32_t chunk_keys) {
     if (check_decode_shape(cache, layer, max_seq_len, chunk_keys) != HDA_OK) return 0;
     const int64_t mk = max_keys_of(cache, layer, max_seq_len);
+    if (use_stream(cache, chunk_keys)) return stream_layout(cache, stream_waves(cache, mk)).bytes;
     return workspace_for(cache, plan_split(cache, layer, mk, chunk_keys));
 }
 
@@ -207,8 +244,6 @@ hda::DecodeParams decode_params(const void *q, const hda_cache_desc *cache,
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(cache->k);
     p.v = static_cast<const uint16_t *>(cache->v);
-    p.kev = static_cast<const uint16_t *>(cache->k_evict);
-    p.vev = static_cast<const uint16_t *>(cache->v_evict);
     p.seq_lens = seq_lens;
     p.capacity = cache->capacity;
     p.batch = cache->batch;
@@ -218,8 +253,8 @@ hda::DecodeParams decode_params(const void *q, const hda_cache_desc *cache,
     p.chunk = pl.chunk;
     p.nsplit = pl.nsplit;
     p.max_keys = max_seq_len;
+    p.sliding = layer == HDA_SLIDING;
     p.scale_log2 = scale * 1.4426950408889634f;
-    (void)layer;
     return p;
 }
 
@@ -260,6 +295,29 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     if (!out || !aligned16(out))
         return fail(HDA_ERR_INVALID_ARGUMENT, "out must be non-NULL and 16-byte aligned");
     if (cache->batch == 0) return ok();
+    const int g = cache->num_q_heads / cache->num_kv_heads;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (use_stream(cache, chunk_keys)) {
+        const int64_t mk = max_keys_of(cache, layer, max_seq_len);
+        const int waves = stream_waves(cache, mk);
+        const StreamLayout L = stream_layout(cache, waves);
+        if (!workspace || workspace_bytes < L.bytes)
+            return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", L.bytes,
+                        workspace_bytes, workspace);
+        if (!aligned16(workspace))
+            return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+        Plan one{hda::kMaxChunk, 1};
+        hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, one);
+        char *ws = static_cast<char *>(workspace);
+        p.part_o = reinterpret_cast<float *>(ws + L.o_off);
+        p.part_lse = reinterpret_cast<float *>(ws + L.lse_off);
+        p.stream_pre = reinterpret_cast<int *>(ws + L.pre_off);
+        p.sinks = sinks;
+        p.out = static_cast<uint16_t *>(out);
+        p.lse = lse;
+        return launched(hda::launch_decode_stream(p, g, waves, s), "decode");
+    }
 
     const Plan pl = plan_split(cache, layer, max_keys_of(cache, layer, max_seq_len), chunk_keys);
     const size_t need = workspace_for(cache, pl);
@@ -273,16 +331,15 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     p.sinks = sinks;
     p.out = static_cast<uint16_t *>(out);
     p.lse = lse;
-    const int g = cache->num_q_heads / cache->num_kv_heads;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     if (pl.nsplit == 1)
-        return launched(hda::launch_decode_chunks(p, layer == HDA_SLIDING, g, true, s), "decode");
+        return launched(hda::launch_decode_chunks(p, g, true, s), "decode");
 
     const size_t slots = (size_t)cache->batch * cache->num_q_heads * pl.nsplit;
     const size_t obytes = (slots * hda::kHeadDim * sizeof(float) + 255) / 256 * 256;
-    p.part_o = static_cast<float *>(workspace);
-    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + obytes);
-    hipError_t e = hda::launch_decode_chunks(p, layer == HDA_SLIDING, g, false, s);
+    char *ws = static_cast<char *>(workspace);
+    p.part_o = reinterpret_cast<float *>(ws);
+    p.part_lse = reinterpret_cast<float *>(ws + obytes);
+    hipError_t e = hda::launch_decode_chunks(p, g, false, s);
     if (e != hipSuccess) return launched(e, "decode partials");
     hda::MergeParams m{};
     m.part_o = p.part_o;
@@ -312,8 +369,7 @@ hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
     p.part_o = part_o;
     p.part_lse = part_lse;
     const int g = cache->num_q_heads / cache->num_kv_heads;
-    return launched(hda::launch_decode_chunks(p, layer == HDA_SLIDING, g, false,
-                                              static_cast<hipStream_t>(stream)),
+    return launched(hda::launch_decode_chunks(p, g, false, static_cast<hipStream_t>(stream)),
                     "decode partials");
 }
 

@@ -9,14 +9,15 @@ namespace hda {
 constexpr int kHeadDim = 256;     // head dim the decode kernels are built for
 constexpr int kMaxChunk = 512;    // most keys one decode workgroup scores
 constexpr int kDecodeThreads = 256;
+constexpr int kStreamMaxBatch = 4096;  // sequences the balanced streaming path handles
+constexpr int kStreamMaxWaves = 2048;  // its grid: 256 CUs x 8 resident waves
 
 struct RopeAppendParams {
     uint16_t *q;
     const uint16_t *k_new;
     const uint16_t *v_new;
     const int32_t *pos;
-    uint16_t *k, *v;
-    uint16_t *k_evict, *v_evict;
+    uint16_t *k, *v;            // [B, Hkv, capacity, D]; sliding: row window-1 = evicted entry
     int64_t capacity;
     double theta;
     int batch, num_q_heads, num_kv_heads, head_dim, rotary_dim, window;
@@ -26,18 +27,19 @@ struct RopeAppendParams {
 struct DecodeParams {
     const uint16_t *q;          // [B, Hq, D]
     const uint16_t *k, *v;      // [B, Hkv, cap, D]
-    const uint16_t *kev, *vev;  // [B, Hkv, D] side rows (sliding)
     const int32_t *seq_lens;    // [B]
     const float *sinks;         // [Hq] or null
     uint16_t *out;              // [B, Hq, D]
     float *lse;                 // [B, Hq] or null
     float *part_o;              // [B, Hq, S, D]
     float *part_lse;            // [B, Hq, S]
+    int *stream_pre;            // [B + 1] rounds before each sequence (streaming path)
     int64_t capacity;
     int batch, num_q_heads, num_kv_heads, window;
     int chunk;                  // keys per chunk (multiple of 16, <= kMaxChunk)
     int nsplit;                 // chunks per (b, kv head) in the grid
-    int max_keys;               // host bound on keys per sequence
+    int max_keys;               // host bound on keys per sequence (max_seq_len)
+    int sliding;                // keys = min(seq_len, window) instead of seq_len
     float scale_log2;           // softmax scale * log2(e)
 };
 
@@ -54,9 +56,18 @@ hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 
 // Chunk kernel over grid (nsplit, Hkv, B).  final_out: nsplit must be 1 and
 // the kernel writes out/lse with the sink; otherwise it writes partials.
-// group must be one of 1, 2, 4, 8, 16.
-hipError_t launch_decode_chunks(const DecodeParams &p, bool sliding, int group, bool final_out,
-                               hipStream_t stream);
+// group must be one of 1, 2, 4, 8, 16.  Needs capacity >= 16.
+hipError_t launch_decode_chunks(const DecodeParams &p, int group, bool final_out, hipStream_t stream);
+
+// Balanced streaming path: `waves` resident single-wave workgroups share
+// all 16-key rounds evenly; partials in slots (wave + pair) of part_o /
+// part_lse, then the merge writes out / lse with the sink.  Needs
+// capacity >= 16 and batch <= kStreamMaxBatch.
+hipError_t launch_decode_stream(const DecodeParams &p, int group, int waves, hipStream_t stream);
+
+// Single-wave workgroups of the streaming kernel that fit on the device at
+// once (occupancy x CUs); 0 if no device is available.
+int stream_wave_slots(int group);
 
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 

@@ -6,7 +6,8 @@
 // (ring branch) drops the new entry into the slot for its position,
 // evicting the oldest.  This kernel rotates q in place, rotates k_new into
 // the cache row, copies v_new, and for a sliding layer first moves the
-// evicted slot content (still inside this step's window) to the side row.
+// evicted slot content (still inside this step's window) to the block's
+// evicted-entry row, window-1.
 //
 // One workgroup per sequence.  The work is cut into 16-byte tasks: a
 // rotary task owns 8 consecutive pairs (dims j..j+7 and j+h..j+h+7, h =
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
 
     int64_t row = -1;
     bool evict = false;
+    const int64_t erow = p.window - 1;  // evicted-entry row of a sliding block
     if (p.sliding) {
         const int32_t slots = p.window - 1;
         if (pos >= 0) {
@@ -149,8 +151,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
                 const int u = t - n_q, h = u / hc, j = (u % hc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
                 if (evict) {
-                    st(p.k_evict + bh * D + j, oa[r]);
-                    st(p.k_evict + bh * D + half + j, ob[r]);
+                    st(p.k + (bh * cap + erow) * D + j, oa[r]);
+                    st(p.k + (bh * cap + erow) * D + half + j, ob[r]);
                 }
                 uint4 ya, yb;
                 rotate8(xa[r], xb[r], s_cos + j, s_sin + j, ya, yb);
@@ -160,12 +162,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
             } else if (t < n_q + n_k + n_kp) {
                 const int u = t - n_q - n_k, h = u / pc, d = rot + (u % pc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
-                if (evict) st(p.k_evict + bh * D + d, oa[r]);
+                if (evict) st(p.k + (bh * cap + erow) * D + d, oa[r]);
                 st(p.k + (bh * cap + row) * D + d, xa[r]);
             } else {
                 const int u = t - n_q - n_k - n_kp, h = u / vc, d = (u % vc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
-                if (evict) st(p.v_evict + bh * D + d, oa[r]);
+                if (evict) st(p.v + (bh * cap + erow) * D + d, oa[r]);
                 st(p.v + (bh * cap + row) * D + d, xa[r]);
             }
         }

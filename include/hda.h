@@ -56,12 +56,15 @@ typedef enum hda_layer_type {
  * laid out (batch, kv_heads, entries, head_dim)).
  *
  *   k, v        bf16 [batch, num_kv_heads, capacity, head_dim]
- *   k_evict,    bf16 [batch, num_kv_heads, head_dim]; sliding layers only
- *   v_evict     (NULL for full layers).  The side row keeps the window's
- *               oldest entry after the append overwrote its ring slot.
- *   capacity    sliding: window - 1 ring slots (the window counts the
- *               current token, `SparkStepConfig.cache_len`); full: the
- *               longest context the cache can hold.
+ *   capacity    full: the longest context the cache can hold.
+ *               sliding: exactly `window` rows.  Rows 0 .. window-2 are the
+ *               ring (the window counts the current token, so a ring holds
+ *               window-1 previous entries: `SparkStepConfig.cache_len`);
+ *               row window-1 holds the entry the last append evicted from
+ *               its ring slot -- the oldest position of the current window.
+ *               With it the step's keys are always the leading rows
+ *               0 .. min(seq_len, window)-1 of the block, whatever the ring
+ *               offset.
  *   rotary_dim  leading dims rotated by RoPE (`rotary_dim`: head_dim times
  *   rope_theta  the layer type's `partial_rotary_factor`), and its theta.
  *               Spark: sliding 256 dims / 1e4, full 64 dims / 5e6.
@@ -77,8 +80,6 @@ typedef struct hda_cache_desc {
     double rope_theta;
     void *k;
     void *v;
-    void *k_evict;
-    void *v_evict;
 } hda_cache_desc;
 
 /*
@@ -99,14 +100,15 @@ typedef struct hda_cache_desc {
  *   layer   HDA_FULL: entry pos of the cache takes the new K/V.
  *           HDA_SLIDING: slot s = pos mod (window-1).  When pos >= window-1
  *           that slot holds position pos-(window-1), still inside this
- *           step's window, so it is first copied to the side row
- *           k_evict/v_evict; then slot s takes the new K/V.
+ *           step's window, so it is first copied to row window-1 (the
+ *           evicted-entry row); then slot s takes the new K/V.
  *   Rows outside the cache (pos < 0, or pos >= capacity for a full layer)
  *   are skipped.  Math in fp32 (cos/sin of the fp32 angle evaluated in
  *   fp64), results rounded to nearest-even bf16.
  * Errors: INVALID_ARGUMENT for null pointers, misalignment, non-positive
  * head counts, num_q_heads % num_kv_heads != 0, odd or oversized
- * rotary_dim, sliding capacity != window-1, unknown layer; HIP on a launch
+ * rotary_dim, sliding capacity != window, unknown layer; UNSUPPORTED for a
+ * rotary_dim that is not a multiple of 16 or exceeds 512; HIP on a launch
  * failure.  batch == 0 is a no-op.
  */
 hda_status hda_rope_append(void *q, const void *k_new, const void *v_new,
@@ -129,21 +131,24 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
  * num_kv_heads) (Spark `_Layer.forward`: query heads folded per KV head,
  * K/V never expanded).  With n = seq_lens[b] (= pos + 1) the keys are
  *   full:    cache rows 0 .. n-1;
- *   sliding: ring slots 0 .. min(n, window-1)-1, plus the side row when
- *            n >= window -- the last min(n, window) positions.  Slots never
- *            written are excluded, and ring order does not matter (Spark
- *            ring-branch comment).
+ *   sliding: rows 0 .. min(n, window)-1: the written ring slots plus, once
+ *            the window is full, the evicted-entry row -- the last
+ *            min(n, window) positions.  Slots never written are excluded,
+ *            and ring order does not matter (Spark ring-branch comment).
  * scores = scale * q.k (Spark: scale 1/sqrt(head_dim)); softmax; out =
  * sum p v.  lse = ln sum exp(scores), before any sink.  With sinks, out is
  * multiplied by exp(lse)/(exp(lse)+exp(sink[h])) (flashmla_sparse page,
  * `HYV4FlashMLASparseImpl` docstring); a -inf sink leaves out bit-for-bit
  * unchanged (`_sinks_for_query`: -inf is a no-op sink).
  *
- * Full layers (and sliding layers when split) run split-K: each chunk of
- * chunk_keys keys gives a partial (out, lse) in the workspace, and a merge
- * kernel combines them, lse = ln sum_c exp(lse_c), out = sum_c
- * exp(lse_c - lse) out_c, then applies the sink (Spark ring comment: an
- * online softmax over key subsets gives the same result).
+ * The keys are split into pieces whose partial softmax results (out, lse)
+ * land in the workspace; a merge kernel combines them, lse = ln sum_c
+ * exp(lse_c), out = sum_c exp(lse_c - lse) out_c, then applies the sink
+ * (Spark ring comment: an online softmax over key subsets gives the same
+ * result).  chunk_keys = 0 (the default) splits all 16-key rounds of the
+ * batch evenly over the GPU's resident waves, whatever the mix of lengths;
+ * chunk_keys > 0 cuts every sequence into chunks of that many keys, one
+ * workgroup each.
  *
  *   q          bf16 [batch, num_q_heads, head_dim] (already rotated)
  *   seq_lens   int32 [batch] (device); n <= 0 gives out 0, lse -inf
@@ -156,7 +161,8 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
  *              bound are cut to it.
  *   chunk_keys keys per split chunk, a multiple of 16 in [16, 512]; 0
  *              picks the default.
- *   workspace  device buffer of at least hda_decode_workspace_bytes().
+ *   workspace  device buffer of at least hda_decode_workspace_bytes(); calls
+ *              that share a workspace must be ordered on one stream.
  * Errors: as hda_rope_append, plus UNSUPPORTED for head_dim != 256 or a
  * query group size outside {1, 2, 4, 8, 16}, WORKSPACE when the workspace
  * is NULL or smaller than required, INVALID_ARGUMENT for a bad chunk_keys

@@ -3,6 +3,10 @@
 Draws a layer's inputs with ``workloads``, keeps host bit copies for the
 oracle and device copies for the library, and runs the step (append, then
 attention) on each side.  Only tests import this module.
+
+The library keeps a sliding layer as one block of `window` rows (ring slots
+0..window-2, evicted-entry row window-1); the oracle keeps the ring and the
+side row apart.  `to_oracle` / `from_oracle` convert between the two.
 """
 from __future__ import annotations
 
@@ -26,37 +30,47 @@ class HybridCase:
         g = workloads.generator(seed)
         t = workloads.layer_inputs(g, self.shape, layer_type)
         self.host = {k: workloads.bits(v).copy() for k, v in t.items()}
-        if layer_type == FULL:
-            self.host["kev"] = np.zeros((batch, self.shape.num_kv_heads, self.shape.head_dim), np.uint16)
-            self.host["vev"] = self.host["kev"].copy()
         if poison:
             self._poison()
         self.seq_lens = self.pos + 1
 
     def _poison(self):
         """NaN in every row the step must not read: unwritten ring slots
-        and side rows below a full window, full-layer rows past pos."""
+        and the evicted-entry row below a full window (all rows past pos in
+        the block), full-layer rows past pos."""
         h = self.host
-        slots = self.shape.window - 1
         for b, p in enumerate(self.pos):
-            if self.lt == SLIDING:
-                if p < slots:
-                    h["k"][b, :, p + 1:] = BF16_NAN
-                    h["v"][b, :, p + 1:] = BF16_NAN
-                    h["kev"][b] = BF16_NAN
-                    h["vev"][b] = BF16_NAN
-            else:
-                h["k"][b, :, p + 1:] = BF16_NAN
-                h["v"][b, :, p + 1:] = BF16_NAN
+            h["k"][b, :, p + 1:] = BF16_NAN
+            h["v"][b, :, p + 1:] = BF16_NAN
+
+    # ------------------------------------------------ block <-> oracle form
+    def to_oracle(self, h):
+        """(k, v, kev, vev) in the oracle's form from a host block dict."""
+        if self.lt == SLIDING:
+            slots = self.shape.window - 1
+            return (np.ascontiguousarray(h["k"][:, :, :slots]), np.ascontiguousarray(h["v"][:, :, :slots]),
+                    np.ascontiguousarray(h["k"][:, :, slots]), np.ascontiguousarray(h["v"][:, :, slots]))
+        z = np.zeros((self.shape.batch, self.shape.num_kv_heads, self.shape.head_dim), np.uint16)
+        return h["k"], h["v"], z, z.copy()
+
+    def from_oracle(self, k, v, kev, vev):
+        """Block form (k, v) of the oracle's cache arrays."""
+        if self.lt == SLIDING:
+            return (np.concatenate([k, kev[:, :, None]], axis=2), np.concatenate([v, vev[:, :, None]], axis=2))
+        return k, v
 
     # ---------------------------------------------------------- oracle side
     def oracle_step(self, sinks=None, scale=1 / 16):
+        """Append then attention in the oracle; returns the block-form host
+        state after the append, out and lse."""
         h = {k: v.copy() for k, v in self.host.items()}
         s = self.shape
+        k, v, kev, vev = self.to_oracle(h)
         oracle.rope_append(h["q"], h["k_new"], h["v_new"], self.pos, self.lt, s.rot(self.lt),
-                           s.theta(self.lt), s.window, h["k"], h["v"], h["kev"], h["vev"])
-        out, lse = oracle.decode_attn(h["q"], h["k"], h["v"], h["kev"], h["vev"], self.seq_lens,
-                                      self.lt, s.window, sinks, scale)
+                           s.theta(self.lt), s.window, k, v, kev, vev)
+        out, lse = oracle.decode_attn(h["q"], k, v, kev, vev, self.seq_lens, self.lt, s.window,
+                                      sinks, scale)
+        h["k"], h["v"] = self.from_oracle(k, v, kev, vev)
         return h, out, lse
 
     # ------------------------------------------------------------- GPU side
@@ -66,9 +80,8 @@ class HybridCase:
     def cache(self, d):
         import full_kv_cache_amd as hda
         s = self.shape
-        sl = self.lt == SLIDING
-        return hda.LayerCache(d["k"], d["v"], d["kev"] if sl else None, d["vev"] if sl else None,
-                              s.num_q_heads, s.window, s.rot(self.lt), s.theta(self.lt))
+        return hda.LayerCache(d["k"], d["v"], s.num_q_heads, s.window, s.rot(self.lt),
+                              s.theta(self.lt))
 
     def gpu_step(self, sinks=None, scale=1 / 16, chunk_keys=0, max_seq_len=None, d=None,
                  append=True):
@@ -81,7 +94,7 @@ class HybridCase:
             hda.hda_rope_append(d["q"], d["k_new"], d["v_new"], pos, self.lt, cache)
         msl = int(max_seq_len or self.seq_lens.max())
         ws_bytes = hda.hda_decode_workspace_bytes(cache, self.lt, msl, chunk_keys)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
         s = self.shape
         out = torch.full((s.batch, s.num_q_heads, s.head_dim), float("nan"), dtype=torch.bfloat16,
                          device="cuda")

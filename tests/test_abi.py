@@ -51,7 +51,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 def _desc(**kw):
     d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=256, window=512, rotary_dim=256,
-             capacity=511, rope_theta=1e4, k=FAKE, v=FAKE, k_evict=FAKE, v_evict=FAKE)
+             capacity=512, rope_theta=1e4, k=FAKE, v=FAKE)
     d.update(kw)
     return hda.CacheDesc(**d)
 
@@ -91,13 +91,13 @@ def test_rotary_dim_checks():
     assert _append(_desc(rotary_dim=258)) == 1
 
 
-def test_sliding_capacity_must_be_window_minus_one():
-    assert _append(_desc(capacity=512)) == 1
-    assert "window-1" in _msg()
+def test_sliding_capacity_must_be_window():
+    assert _append(_desc(capacity=511)) == 1
+    assert "must equal window" in _msg()
 
 
-def test_sliding_needs_side_rows():
-    assert _append(_desc(k_evict=None)) == 1
+def test_rotary_dim_granularity_unsupported():
+    assert _append(_desc(rotary_dim=24)) == 2
 
 
 def test_null_and_misaligned_pointers():
@@ -109,10 +109,12 @@ def test_null_and_misaligned_pointers():
 def test_decode_unsupported_shapes():
     assert _decode(_desc(head_dim=128, rotary_dim=128)) == 2
     assert _decode(_desc(num_q_heads=6, num_kv_heads=2)) == 2  # group of 3
+    tiny = _desc(capacity=8, rotary_dim=64, rope_theta=5e6)
+    assert _decode(tiny, layer=hda.FULL, max_seq_len=8) == 2  # fewer than 16 rows
 
 
 def test_decode_bounds():
-    full = _desc(capacity=1024, rotary_dim=64, rope_theta=5e6, k_evict=None, v_evict=None)
+    full = _desc(capacity=1024, rotary_dim=64, rope_theta=5e6)
     assert _decode(full, layer=hda.FULL, max_seq_len=1025) == 1
     assert "capacity" in _msg()
     assert _decode(full, layer=hda.FULL, max_seq_len=0) == 1
@@ -123,9 +125,9 @@ def test_decode_bounds():
 
 def test_workspace_sizing_and_errors():
     L = hda.lib()
-    full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6, k_evict=None, v_evict=None)
+    full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
     need = L.hda_decode_workspace_bytes(ctypes.byref(full), hda.FULL, 4096, 256)
-    # 2 sequences x 8 heads x 16 chunks of (256 floats out + 1 float lse), padded
+    # 2 sequences x 8 heads x 16 chunks of (256 floats out + 1 float lse)
     assert need == (2 * 8 * 16 * 256 * 4) + 2 * 8 * 16 * 4
     assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256) == 3
     assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256, ws=FAKE, wsb=need - 1) == 3

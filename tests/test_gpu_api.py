@@ -72,7 +72,7 @@ def test_graph_replay_matches_eager():
     seq = pos + 1
     sinks = torch.linspace(-1, 8, 8, device="cuda")
     outs = [torch.empty(3, 8, 256, dtype=torch.bfloat16, device="cuda") for _ in cases]
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
 
     def step():
         for c, d, o in zip(cases, live, outs):
@@ -110,3 +110,45 @@ def test_graph_replay_matches_eager():
         for d, e in zip(live, eager_cache):
             for k in d:
                 assert torch.equal(d[k].view(torch.int16), e[k].view(torch.int16)), (rep, k)
+
+
+def test_stream_workspace_reuse():
+    """One workspace serves call after call of the default (streaming) path
+    with identical results."""
+    print("CASE workspace_reuse", flush=True)
+    import full_kv_cache_amd as hda
+    case = HybridCase(960, 5, FULL, [100, 4000, 17, 2500, 900], lmax=4096)
+    d = case.device()
+    cache = case.cache(d)
+    seq = torch.from_numpy(case.seq_lens).cuda()
+    nbytes = hda.hda_decode_workspace_bytes(cache, FULL, 4096, 0)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.empty(5, 8, 256, dtype=torch.bfloat16, device="cuda")
+        hda.hda_decode_attn(d["q"], cache, seq, FULL, None, 1 / 16, out, None, 4096, 0, ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+def test_one_workspace_serves_both_paths():
+    """One workspace serves the streaming and the chunked path in any order
+    (a chunked call once overwrote state a later streaming call relied on)."""
+    print("CASE workspace_both_paths", flush=True)
+    import full_kv_cache_amd as hda
+    case = HybridCase(961, 6, FULL, [3000, 20, 4095, 700, 1, 2200], lmax=4096)
+    _, ref, _ = case.oracle_step()
+    d = case.device()
+    cache = case.cache(d)
+    pos = torch.from_numpy(case.pos).cuda()
+    hda.hda_rope_append(d["q"], d["k_new"], d["v_new"], pos, FULL, cache)
+    seq = torch.from_numpy(case.seq_lens).cuda()
+    nbytes = max(hda.hda_decode_workspace_bytes(cache, FULL, 4096, c) for c in (0, 64, 256))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for chunk in (0, 64, 0, 256, 0):
+        out = torch.full((6, 8, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+        hda.hda_decode_attn(d["q"], cache, seq, FULL, None, 1 / 16, out, None, 4096, chunk, ws)
+        torch.cuda.synchronize()
+        assert_attn_close(out, ref)

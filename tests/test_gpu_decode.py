@@ -26,8 +26,7 @@ def _print_case(**kw):
 def _check_append(case, d):
     """Cache and q after hda_rope_append vs the oracle's append."""
     h, _, _ = case.oracle_step()
-    for name in ("v", "vev", "kev") if case.lt == SLIDING else ("v",):
-        assert np.array_equal(bits_of(d[name]), h[name]), name
+    assert np.array_equal(bits_of(d["v"]), h["v"])
     for name in ("k", "q"):
         got, ref = bits_of(d[name]), h[name]
         ulps = bf16_ulp_diff(got, ref)
@@ -132,13 +131,14 @@ def test_zero_length_sequence():
 
 
 def test_ring_order_and_resume():
-    """Permuting written ring slots (plus the side row) leaves the output
-    unchanged up to summation order; copying the cache resumes exactly."""
+    """Permuting the window's rows (ring slots and evicted-entry row) leaves
+    the output unchanged up to summation order; copying the cache resumes
+    exactly."""
     _print_case(test="ring_order")
     import full_kv_cache_amd as hda
     case = HybridCase(700, 2, SLIDING, [900, 2000])
     d, out0, _ = case.gpu_step()
-    perm = torch.randperm(511, generator=torch.Generator().manual_seed(0)).cuda()
+    perm = torch.randperm(512, generator=torch.Generator().manual_seed(0)).cuda()
     d2 = {k: v.clone() for k, v in d.items()}
     d2["k"] = d["k"][:, :, perm].contiguous()
     d2["v"] = d["v"][:, :, perm].contiguous()

@@ -35,11 +35,18 @@ def _f(bits):
 
 
 def _case(seed, B, lt, lmax=96):
+    """Oracle-form inputs: a sliding block splits into the 511-slot ring and
+    its last row, the side row."""
     shape = workloads.HybridShape(batch=B, lmax=lmax)
     g = workloads.generator(seed)
     t = {k: workloads.bits(v).copy() for k, v in workloads.layer_inputs(g, shape, lt).items()}
     if lt == FU:
         t["kev"] = t["vev"] = None
+    else:
+        for a in ("k", "v"):
+            blk = t[a]
+            t[a] = np.ascontiguousarray(blk[:, :, :W - 1])
+            t[a + "ev"] = np.ascontiguousarray(blk[:, :, W - 1])
     return shape, t
 
 

@@ -59,10 +59,17 @@ def test_ring_slot(pos, slot):
 
 
 def _layer(seed, B, lt, lmax=64):
+    """Oracle-form inputs: a sliding block splits into the 511-slot ring and
+    its last row, the side row."""
     shape = workloads.HybridShape(batch=B, lmax=lmax)
     g = workloads.generator(seed)
-    t = workloads.layer_inputs(g, shape, lt)
-    return shape, {k: workloads.bits(v).copy() for k, v in t.items()}
+    t = {k: workloads.bits(v).copy() for k, v in workloads.layer_inputs(g, shape, lt).items()}
+    if lt == workloads.SLIDING:
+        for a in ("k", "v"):
+            blk = t[a]
+            t[a] = np.ascontiguousarray(blk[:, :, :W - 1])
+            t[a + "ev"] = np.ascontiguousarray(blk[:, :, W - 1])
+    return shape, t
 
 
 @pytest.mark.parametrize("pos", [0, 1, 509, 510, 511, 512, 1023, 4095])

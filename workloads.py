@@ -8,7 +8,8 @@ Every tensor comes from one ``torch.Generator`` in a fixed order, as fp32
 ``randn`` cast to bf16 (unit-normal values, the distribution the decode
 workloads are quoted on).  Shapes follow the hybrid model of the Spark
 export page: 8 query heads, 2 KV heads, head dim 256, a 512-token window
-held as 511 ring slots plus a side row, full layers of ``lmax`` rows; and
+held as a 512-row block (511 ring slots plus the evicted-entry row), full
+layers of ``lmax`` rows; and
 the sparse MLA layer of the FlashMLA sparse page: 64 query heads over one
 576-dim latent head.
 """
@@ -40,7 +41,7 @@ class HybridShape:
         return self.window - 1
 
     def capacity(self, layer_type: int) -> int:
-        return self.ring_slots if layer_type == SLIDING else self.lmax
+        return self.window if layer_type == SLIDING else self.lmax
 
     def rot(self, layer_type: int) -> int:
         return self.rot_sliding if layer_type == SLIDING else self.rot_full
@@ -71,7 +72,7 @@ def uniform_seq_lens(gen: torch.Generator, batch: int, lo: int, hi: int, device=
 
 
 def layer_inputs(gen: torch.Generator, shape: HybridShape, layer_type: int, device="cpu") -> dict:
-    """One layer's step inputs, drawn in the order q, k_new, v_new, K, V, side K, side V."""
+    """One layer's step inputs, drawn in the order q, k_new, v_new, K, V."""
     B, Hq, Hkv, D = shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
     cap = shape.capacity(layer_type)
     out = {
@@ -81,9 +82,6 @@ def layer_inputs(gen: torch.Generator, shape: HybridShape, layer_type: int, devi
         "k": randn_bf16(gen, (B, Hkv, cap, D), device),
         "v": randn_bf16(gen, (B, Hkv, cap, D), device),
     }
-    if layer_type == SLIDING:
-        out["kev"] = randn_bf16(gen, (B, Hkv, D), device)
-        out["vev"] = randn_bf16(gen, (B, Hkv, D), device)
     return out
 
 
