@@ -83,10 +83,11 @@ def lib() -> ctypes.CDLL:
         L.hda_status_string.argtypes = [ctypes.c_int]
         L.hda_last_error_message.restype = ctypes.c_char_p
         L.hda_last_error_message.argtypes = []
-        if hasattr(L, "hda_sparse_decode_attn"):
-            L.hda_sparse_decode_attn.restype = ctypes.c_int
-            L.hda_sparse_decode_attn.argtypes = [P, P, ctypes.c_int64, P, i32, P, i32, P,
-                                                 ctypes.c_float, i32, P, P, i32, i32, P]
+        L.hda_sparse_workspace_bytes.restype = ctypes.c_size_t
+        L.hda_sparse_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.hda_sparse_decode_attn.restype = ctypes.c_int
+        L.hda_sparse_decode_attn.argtypes = [P, P, ctypes.c_int64, P, i32, i32, P, i32, i32, i32,
+                                             P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -196,12 +197,21 @@ def hda_lse_merge(part_o, part_lse, sinks, out, lse=None, stream=None):
                                _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
 
 
-def hda_sparse_decode_attn(q, kv, indices, topk_length, sinks, scale: float, dv: int, out,
-                           lse=None, stream=None):
-    """Sparse top-k decode over one shared latent KV head, with sinks."""
+def hda_sparse_workspace_bytes(tokens: int, num_q_heads: int, topk: int, dv: int = 512) -> int:
+    return int(lib().hda_sparse_workspace_bytes(int(tokens), int(num_q_heads), int(topk), int(dv)))
+
+
+def hda_sparse_decode_attn(q, kv, indices, topk_length, sinks, scale: float, out, lse=None,
+                           workspace=None, stream=None):
+    """Sparse top-k decode over one latent KV head shared by all query heads.
+
+    q bf16 [T, Hq, Dqk]; kv bf16 [N, Dqk]; indices int32 [T, topk];
+    topk_length int32 [T] or None; sinks fp32 [Hq] or None; out bf16
+    [T, Hq, Dv] (Dv = out.shape[-1], the leading dims of each row)."""
     validate_sinks(sinks, q)
     T, H, dqk = q.shape
-    _check(lib().hda_sparse_decode_attn(_ptr(q), _ptr(kv), int(kv.shape[0]), _ptr(indices),
-                                        int(indices.shape[1]), _ptr(topk_length), int(T),
-                                        _ptr(sinks), float(scale), int(dv), _ptr(out), _ptr(lse),
-                                        int(H), int(dqk), _stream(stream)))
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hda_sparse_decode_attn(_ptr(q), _ptr(kv), int(kv.shape[0]), _ptr(indices), int(T),
+                                        int(indices.shape[1]), _ptr(topk_length), int(H), int(dqk),
+                                        int(out.shape[-1]), _ptr(sinks), float(scale), _ptr(out),
+                                        _ptr(lse), _ptr(workspace), wbytes, _stream(stream)))

@@ -224,7 +224,9 @@ struct WaveSoftmax {
 
 // Loads of one round: the 16 keys start at block row r0e (kept at most
 // capacity - 16 so that every load stays inside the block); the caller
-// masks keys outside [r0, n).
+// masks keys outside [r0, n).  Passing lane 0 for every lane makes a
+// placeholder round: the same number of load instructions, all of one
+// 16-byte address, so the wait counts stay exact at no traffic.
 __device__ __forceinline__ void issue_round(const uint16_t *kblk, const uint16_t *vblk, int r0e,
                                             int lane, uint4 *kt, uint4 *vt) {
     const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
@@ -504,15 +506,15 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     };
 
     // Every half-iteration issues the next round's loads, then computes the
-    // current round.  The last round issues a re-read of its own rows
-    // (cache hits, never used) so that the loads stay unconditional and the
-    // compiler's wait counts exact.
+    // current round.  After the last round a placeholder round is issued
+    // (never used) so that the loads stay unconditional and the compiler's
+    // wait counts exact.
     int64_t g = g0;
     while (true) {
         bool more = g + 1 < g1;
         RoundAddr nxt = more ? advance(cur) : cur;
         RoundGeo gn = geo(nxt);
-        issue_round(gn.kblk, gn.vblk, gn.r0e, lane, kB, vB);
+        issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kB, vB);
         st.round(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, lane);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         more = g + 1 < g1;
         nxt = more ? advance(cur) : cur;
         gn = geo(nxt);
-        issue_round(gn.kblk, gn.vblk, gn.r0e, lane, kA, vA);
+        issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kA, vA);
         st.round(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, lane);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);

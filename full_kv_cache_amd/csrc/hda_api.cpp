@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -171,6 +173,51 @@ hda_status check_decode_shape(const hda_cache_desc *c, int layer, int32_t max_se
         return fail(HDA_ERR_INVALID_ARGUMENT,
                     "chunk_keys %d must be 0 or a multiple of 16 in [16, %d]", chunk_keys,
                     hda::kMaxChunk);
+    return HDA_OK;
+}
+
+// ---------------------------------------------------------------- sparse
+// Key splits for the sparse decode: one workgroup per (token, split, group
+// of 16 heads); split a token's index row only when the tokens alone leave
+// the GPU short of workgroups (fewer than 256), and never below 64 keys.
+struct SparsePlan {
+    int nsplit, split_keys;
+};
+
+SparsePlan sparse_plan(int32_t tokens, int32_t heads, int32_t topk) {
+    const int64_t wgs = (int64_t)tokens * (heads / hda::kSparseHeadsPerWave);
+    int64_t ns = 1;
+    if (wgs > 0 && wgs < 256 && topk > 64) ns = std::min<int64_t>((256 + wgs - 1) / wgs, (topk + 63) / 64);
+    int64_t ks = topk > 0 ? (topk + ns - 1) / ns : 16;
+    ks = (ks + 15) / 16 * 16;
+    ns = topk > 0 ? (topk + ks - 1) / ks : 1;
+    return {(int)ns, (int)ks};
+}
+
+size_t sparse_part_o_bytes(int32_t tokens, int32_t heads, const SparsePlan &pl) {
+    const size_t b = (size_t)tokens * heads * pl.nsplit * hda::kSparseDv * sizeof(float);
+    return (b + 255) / 256 * 256;
+}
+
+size_t sparse_workspace(int32_t tokens, int32_t heads, const SparsePlan &pl) {
+    if (pl.nsplit <= 1) return 0;
+    return sparse_part_o_bytes(tokens, heads, pl) + (size_t)tokens * heads * pl.nsplit * sizeof(float);
+}
+
+hda_status check_sparse_shape(int32_t tokens, int32_t heads, int32_t topk, int32_t dqk, int32_t dv) {
+    if (tokens < 0 || topk < 0)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "tokens %d and topk %d must be >= 0", tokens, topk);
+    if (heads <= 0 || heads % hda::kSparseHeadsPerWave)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "num_q_heads %d must be a positive multiple of %d", heads,
+                    hda::kSparseHeadsPerWave);
+    if (dqk != hda::kSparseDqk || dv != hda::kSparseDv)
+        return fail(HDA_ERR_UNSUPPORTED, "sparse kernels are built for dqk %d / dv %d, got %d / %d",
+                    hda::kSparseDqk, hda::kSparseDv, dqk, dv);
+    const SparsePlan pl = sparse_plan(tokens, heads, topk);
+    const int64_t units = (int64_t)tokens * pl.nsplit;
+    const int64_t blocks = (units + 7) / 8 * 8 * (heads / hda::kSparseHeadsPerWave);
+    if (blocks > INT32_MAX || (int64_t)tokens * heads > INT32_MAX)
+        return fail(HDA_ERR_UNSUPPORTED, "%d tokens x %d heads exceed the launch grid", tokens, heads);
     return HDA_OK;
 }
 
@@ -394,6 +441,58 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
     m.num_heads = num_heads;
     m.nsplit = nsplit;
     return launched(hda::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "lse merge");
+}
+
+hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_rows,
+                                  const int32_t *indices, int32_t tokens, int32_t topk,
+                                  const int32_t *topk_length, int32_t num_q_heads, int32_t dqk,
+                                  int32_t dv, const float *sinks, float scale, void *out,
+                                  float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    hda_status st = check_sparse_shape(tokens, num_q_heads, topk, dqk, dv);
+    if (st != HDA_OK) return st;
+    if (pool_rows < 1) return fail(HDA_ERR_INVALID_ARGUMENT, "pool_rows %lld < 1", (long long)pool_rows);
+    if (!q || !kv || !indices || !out)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, kv, indices and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, kv and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(indices) & 3u) || (topk_length && (reinterpret_cast<uintptr_t>(topk_length) & 3u)) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "indices, topk_length, sinks and lse must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    const SparsePlan pl = sparse_plan(tokens, num_q_heads, topk);
+    const size_t need = sparse_workspace(tokens, num_q_heads, pl);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (need && !aligned16(workspace))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (tokens == 0) return ok();
+    hda::SparseParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.kv = static_cast<const uint16_t *>(kv);
+    p.indices = indices;
+    p.topk_length = topk_length;
+    p.sinks = sinks;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    if (need) {
+        p.part_o = static_cast<float *>(workspace);
+        p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + sparse_part_o_bytes(tokens, num_q_heads, pl));
+    }
+    p.pool_rows = pool_rows;
+    p.tokens = tokens;
+    p.num_q_heads = num_q_heads;
+    p.topk = topk;
+    p.nsplit = pl.nsplit;
+    p.split_keys = pl.split_keys;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return launched(hda::launch_sparse_decode(p, static_cast<hipStream_t>(stream)), "sparse decode");
+}
+
+size_t hda_sparse_workspace_bytes(int32_t tokens, int32_t num_q_heads, int32_t topk, int32_t dv) {
+    if (check_sparse_shape(tokens, num_q_heads, topk, hda::kSparseDqk, dv) != HDA_OK) return 0;
+    return sparse_workspace(tokens, num_q_heads, sparse_plan(tokens, num_q_heads, topk));
 }
 
 }  // extern "C"

@@ -52,7 +52,33 @@ struct MergeParams {
     int batch, num_heads, nsplit;
 };
 
+// Sparse top-k decode over one latent KV head shared by all query heads.
+constexpr int kSparseDqk = 576;    // key dims (latent + rotary part)
+constexpr int kSparseDv = 512;     // value dims: the leading part of each row
+constexpr int kSparseHeadsPerWave = 16;
+constexpr int kSparseWaves = 4;    // waves per workgroup, each takes 16-key tiles in turn
+
+struct SparseParams {
+    const uint16_t *q;          // [T, Hq, Dqk]
+    const uint16_t *kv;         // [pool_rows, Dqk]
+    const int32_t *indices;     // [T, topk]
+    const int32_t *topk_length; // [T] or null
+    const float *sinks;         // [Hq] or null
+    uint16_t *out;              // [T, Hq, Dv]
+    float *lse;                 // [T, Hq] or null
+    float *part_o;              // [T, Hq, nsplit, Dv] (nsplit > 1)
+    float *part_lse;            // [T, Hq, nsplit]
+    int64_t pool_rows;
+    int tokens, num_q_heads, topk;
+    int nsplit, split_keys;     // key splits per token; keys per split (multiple of 16)
+    float scale_log2;           // softmax scale * log2(e)
+};
+
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
+
+// Grid of (token, key split, 16-head group) workgroups; nsplit == 1 writes
+// out / lse with the sink, otherwise partials and then their merge.
+hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t stream);
 
 // Chunk kernel over grid (nsplit, Hkv, B).  final_out: nsplit must be 1 and
 // the kernel writes out/lse with the sink; otherwise it writes partials.

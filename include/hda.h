@@ -217,6 +217,53 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
                          int32_t num_heads, int32_t nsplit, int32_t head_dim,
                          const float *sinks, void *out, float *lse, void *stream);
 
+/*
+ * hda_sparse_workspace_bytes -- device workspace hda_sparse_decode_attn needs
+ * for this many tokens, query heads and index-row length (0: none).
+ * Returns 0 for an invalid shape as well; the call then reports why.
+ */
+size_t hda_sparse_workspace_bytes(int32_t tokens, int32_t num_q_heads, int32_t topk,
+                                  int32_t dv);
+
+/*
+ * hda_sparse_decode_attn -- sparse top-k decode attention with a sink over
+ * one latent KV head shared by every query head (flashmla_sparse page:
+ * `_bf16_flash_mla_kernel` -- the cache viewed as (rows, 1, Dqk), per-token
+ * top-k index rows, optional `topk_length`, the sink; `head_dim_v` = Dv).
+ *
+ * For token t the keys are the pool rows indices[t][i], i < len_t, where
+ * len_t = topk_length[t] (clamped to [0, topk]) or topk when topk_length is
+ * NULL; entries outside [0, pool_rows) (the -1 padding) name no row and are
+ * skipped.  For query head h:
+ *   s_i = scale * q[t][h] . kv[idx_i]          (all dqk dims)
+ *   out[t][h] = sum_i softmax(s)_i kv[idx_i][0 .. dv-1]
+ *   lse[t][h] = ln sum_i exp(s_i)              (before the sink)
+ * then out *= exp(lse)/(exp(lse)+exp(sinks[h])) as in hda_decode_attn.  No
+ * key at all: out 0, lse -inf.
+ *
+ *   q          bf16 [tokens, num_q_heads, dqk]
+ *   kv         bf16 [pool_rows, dqk]: the latent part first, so the value
+ *              of a row is its leading dv dims
+ *   indices    int32 [tokens, topk] (device)
+ *   topk_length int32 [tokens] (device) or NULL
+ *   sinks      fp32 [num_q_heads] (device) or NULL
+ *   out        bf16 [tokens, num_q_heads, dv]; lse fp32 [tokens, num_q_heads]
+ *              or NULL
+ *   workspace  device buffer of at least hda_sparse_workspace_bytes()
+ *              (partials of the key splits); may be NULL when that is 0.
+ * Errors: INVALID_ARGUMENT for null or misaligned pointers, negative
+ * tokens/topk, pool_rows < 1, num_q_heads not a positive multiple of 16;
+ * UNSUPPORTED for (dqk, dv) other than (576, 512); WORKSPACE when the
+ * workspace is smaller than required; HIP on a launch failure.  tokens == 0
+ * is a no-op.  The pool and indices are only read.
+ */
+hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_rows,
+                                  const int32_t *indices, int32_t tokens, int32_t topk,
+                                  const int32_t *topk_length, int32_t num_q_heads,
+                                  int32_t dqk, int32_t dv, const float *sinks, float scale,
+                                  void *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hda_status_string(hda_status status);
 

@@ -154,3 +154,51 @@ def test_sink_validation_in_binding():
         hda.validate_sinks(torch.zeros(4), q)
     with pytest.raises(ValueError, match="shape"):
         hda.validate_sinks(torch.zeros(8, 1), q)
+
+
+# ------------------------------------------------------------- sparse entry
+def _sparse(tokens=32, heads=64, topk=2048, dqk=576, dv=512, pool=32768, q=FAKE, kv=FAKE,
+            idx=FAKE, out=FAKE, ws=None, wsb=0, scale=1 / 24):
+    L = hda.lib()
+    return L.hda_sparse_decode_attn(ctypes.c_void_p(q), ctypes.c_void_p(kv), pool,
+                                    ctypes.c_void_p(idx), tokens, topk, None, heads, dqk, dv, None,
+                                    scale, ctypes.c_void_p(out), None,
+                                    ctypes.c_void_p(ws) if ws else None, wsb, None)
+
+
+def test_sparse_shape_checks():
+    assert _sparse(heads=24) == 1 and "multiple of 16" in _msg()
+    assert _sparse(heads=0) == 1
+    assert _sparse(tokens=-1) == 1
+    assert _sparse(topk=-5) == 1
+    assert _sparse(dqk=512) == 2 and "576" in _msg()
+    assert _sparse(dv=256) == 2
+    assert _sparse(pool=0) == 1 and "pool_rows" in _msg()
+    assert _sparse(q=0) == 1
+    assert _sparse(out=FAKE + 8) == 1 and "aligned" in _msg()
+    assert _sparse(idx=FAKE + 2) == 1
+
+
+def test_sparse_workspace_plan():
+    """Split only when tokens x head groups leave the GPU short of
+    workgroups; the headline shape (32 tokens, 64 heads, top-2048) splits in
+    two: partials fp32 [32, 64, 2, 512] plus lse [32, 64, 2]."""
+    ws = hda.hda_sparse_workspace_bytes
+    assert ws(32, 64, 2048) == 32 * 64 * 2 * 512 * 4 + 32 * 64 * 2 * 4
+    assert ws(128, 64, 2048) == 0       # 512 workgroups already: no split
+    assert ws(1, 16, 64) == 0           # too few keys to split
+    assert ws(1, 16, 2048) == 1 * 16 * 32 * 512 * 4 + 16 * 32 * 4  # 32 splits of 64 keys
+    assert ws(32, 64, 2048, dv=256) == 0  # invalid shape
+    need = ws(32, 64, 2048)
+    assert _sparse() == 3 and "workspace" in _msg()
+    assert _sparse(ws=FAKE, wsb=need - 1) == 3
+    assert _sparse(ws=FAKE + 4, wsb=need) == 1 and "aligned" in _msg()
+    assert _sparse(tokens=0) == 0       # no tokens: nothing to do, nothing needed
+
+
+def test_sparse_sink_validation_in_binding():
+    q = torch.zeros(2, 16, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="float32"):
+        hda.hda_sparse_decode_attn(q, None, None, None, torch.zeros(16, dtype=torch.float64), 1.0, None)
+    with pytest.raises(ValueError, match="shape"):
+        hda.hda_sparse_decode_attn(q, None, None, None, torch.zeros(8), 1.0, None)

@@ -1,0 +1,130 @@
+"""GPU parity of the sparse top-k decode (one latent KV head, 64 query
+heads, value = leading 512 of 576 dims, per-head sink) against the fp64
+oracle, through the C ABI.
+
+Tolerance: attention out max-abs <= 1e-2, mean-abs <= 1e-3 (unit-normal
+bf16 inputs, fp32 accumulation); lse within 1e-4.  Pool rows no index names
+are NaN-poisoned, so a read of one shows up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from hybrid_case import assert_attn_close, to_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_NAN = 0x7FC0
+
+
+def _case(seed, T, H, pool, topk, poison=True):
+    g = workloads.generator(seed)
+    s = workloads.SparseShape(tokens=T, num_q_heads=H, pool=pool, topk=topk)
+    t = workloads.sparse_inputs(g, s)
+    h = {"q": workloads.bits(t["q"]).copy(), "kv": workloads.bits(t["kv"]).copy(),
+         "indices": t["indices"].numpy().copy(), "sinks": t["sinks"].numpy().copy()}
+    if poison:
+        used = np.zeros(pool, bool)
+        used[h["indices"][h["indices"] >= 0]] = True
+        h["kv"][~used] = BF16_NAN
+    return h
+
+
+def _gpu(h, topk_length=None, sinks=None, scale=1 / 24):
+    import full_kv_cache_amd as hda
+    T, H, _ = h["q"].shape
+    topk = h["indices"].shape[1]
+    q = workloads.from_bits(h["q"]).cuda()
+    kv = workloads.from_bits(h["kv"]).cuda()
+    idx = torch.from_numpy(h["indices"]).cuda()
+    tl = None if topk_length is None else torch.from_numpy(np.asarray(topk_length, np.int32)).cuda()
+    sk = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
+    out = torch.full((T, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = hda.hda_sparse_workspace_bytes(T, H, topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+    hda.hda_sparse_decode_attn(q, kv, idx, tl, sk, scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _ref(h, topk_length=None, sinks=None, scale=1 / 24):
+    tl = None if topk_length is None else np.asarray(topk_length, np.int32)
+    return oracle.sparse_decode_attn(h["q"], h["kv"], h["indices"], tl, sinks, scale, 512)
+
+
+def _print_case(**kw):
+    print("CASE", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@pytest.mark.parametrize("T,H,pool,topk", [(3, 64, 4096, 300), (2, 16, 1000, 77), (64, 64, 8192, 256),
+                                           (5, 32, 2048, 1024)])
+def test_sparse_matches_oracle(T, H, pool, topk):
+    """Ragged index rows (not a multiple of 16), split and unsplit plans."""
+    _print_case(test="sparse", T=T, H=H, pool=pool, topk=topk)
+    h = _case(T * 1000 + topk, T, H, pool, topk)
+    ref, rlse = _ref(h)
+    out, lse = _gpu(h)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+def test_sparse_topk_length_and_invalid_indices():
+    """topk_length cuts each row (0 and > topk included); -1 padding and
+    indices past the pool are skipped; a token with no key gives 0 / -inf."""
+    _print_case(test="sparse_lengths")
+    T, H, pool, topk = 6, 64, 3000, 200
+    h = _case(7, T, H, pool, topk, poison=False)
+    g = np.random.default_rng(3)
+    h["indices"][1, g.choice(topk, 50, replace=False)] = -1
+    h["indices"][2, :10] = pool + 5
+    h["indices"][2, 10:20] = -7
+    h["indices"][4, :] = -1
+    lengths = [200, 150, 33, 0, 200, 1000]
+    used = np.zeros(pool, bool)
+    for t in range(T):
+        row = h["indices"][t, :min(max(lengths[t], 0), topk)]
+        used[row[(row >= 0) & (row < pool)]] = True
+    h["kv"][~used] = BF16_NAN
+    ref, rlse = _ref(h, lengths)
+    out, lse = _gpu(h, lengths)
+    live = [0, 1, 2, 5]
+    assert_attn_close(out[live], ref[live])
+    np.testing.assert_allclose(to_f64(lse)[live], rlse[live], rtol=0, atol=1e-4)
+    for t in (3, 4):
+        assert torch.all(out[t].float() == 0)
+        assert torch.all(torch.isneginf(lse[t]))
+
+
+def test_sparse_sinks():
+    _print_case(test="sparse_sinks")
+    T, H, pool, topk = 4, 64, 4096, 512
+    h = _case(11, T, H, pool, topk)
+    _, rlse = _ref(h)
+    g = np.random.default_rng(5)
+    sinks = (rlse.mean(0) + g.normal(0, 1.5, H)).astype(np.float32)  # near lse: moves the output
+    ref, _ = _ref(h, sinks=sinks)
+    out, _ = _gpu(h, sinks=sinks)
+    assert_attn_close(out, ref)
+    o_none, _ = _gpu(h)
+    o_ninf, _ = _gpu(h, sinks=np.full(H, -np.inf, np.float32))
+    assert torch.equal(o_none.view(torch.int16), o_ninf.view(torch.int16))
+    o_pinf, _ = _gpu(h, sinks=np.full(H, np.inf, np.float32))
+    assert torch.all(o_pinf.float() == 0)
+
+
+def test_sparse_headline_shape_sampled():
+    """32 tokens x 64 heads, pool 32768, top-2048 (the launch the bench
+    times); the oracle checks 4 of the tokens."""
+    _print_case(test="sparse_headline")
+    h = _case(0, 32, 64, 32768, 2048, poison=False)
+    out, lse = _gpu(h, sinks=h["sinks"])
+    sample = [0, 9, 22, 31]
+    sub = dict(h)
+    sub["q"] = h["q"][sample].copy()
+    sub["indices"] = h["indices"][sample].copy()
+    ref, rlse = _ref(sub, sinks=h["sinks"])
+    assert_attn_close(out[sample], ref)
+    np.testing.assert_allclose(to_f64(lse)[sample], rlse, rtol=0, atol=1e-4)
