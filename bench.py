@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the sparse top-k measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time for the CPU baseline sample")
     ap.add_argument("--chunk-keys", type=int, default=0, help="split size for full layers (0: default)")
@@ -177,6 +178,51 @@ def dominant_kernel(wl: Workload, steps, warmup, chunk_keys=0):
     }
 
 
+def sparse_kernel(steps, warmup, seed, pools=8):
+    """The sparse top-k decode with sinks at its page shape (32 tokens, 64
+    query heads over one 576-dim latent head, value = leading 512 dims,
+    pool of 32768 rows, top-2048 indices per token): `pools` distinct pools
+    (8 x 37.7 MB, more than the 256 MB last-level cache) are cycled through
+    one graph so that rows come from HBM, HIP events on the launch stream.
+    Gathered bytes per call = tokens x topk x 1152; flops = tokens x heads x
+    topk x 2 (576 + 512)."""
+    import torch
+    import workloads
+    import full_kv_cache_amd as hda
+    s = workloads.SparseShape()
+    g = workloads.generator(seed + 1, "cuda")
+    ins = [workloads.sparse_inputs(g, s, "cuda") for _ in range(pools)]
+    outs = [torch.empty(s.tokens, s.num_q_heads, s.dv, dtype=torch.bfloat16, device="cuda")
+            for _ in range(pools)]
+    lses = [torch.empty(s.tokens, s.num_q_heads, dtype=torch.float32, device="cuda")
+            for _ in range(pools)]
+    nbytes = hda.hda_sparse_workspace_bytes(s.tokens, s.num_q_heads, s.topk, s.dv)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / s.dqk ** 0.5
+
+    def fn():
+        for i in range(pools):
+            hda.hda_sparse_decode_attn(ins[i]["q"], ins[i]["kv"], ins[i]["indices"], None,
+                                       ins[i]["sinks"], scale, outs[i], lses[i], ws)
+
+    ms, _ = time_graph(fn, steps, warmup)
+    per_call_s = ms / pools / 1e3
+    gathered = s.tokens * s.topk * s.dqk * 2
+    flops = s.tokens * s.num_q_heads * s.topk * 2 * (s.dqk + s.dv)
+    gbs = gathered / per_call_s / 1e9
+    return {
+        "kernel": "sparse_decode_kernel + sparse_merge_kernel (hda_sparse_decode_attn)",
+        "workload": f"{s.tokens} tokens x {s.num_q_heads} heads, dqk {s.dqk} / dv {s.dv}, pool "
+                    f"{s.pool} rows, top-{s.topk}, per-head sinks, {pools} pools cycled",
+        "us_per_call": round(per_call_s * 1e6, 2), "gather_GBs": round(gbs, 1),
+        "tflops": round(flops / per_call_s / 1e12, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": gathered},
+        "mfma_bf16_frac": round(flops / per_call_s / 2.5e15, 4),
+    }
+
+
 def cpu_baseline(wl: Workload, min_seconds: float):
     """The oracle on host copies of the same workload: whole 28-layer steps
     over the batch (append + attention per layer), repeated until at least
@@ -264,6 +310,10 @@ def main():
         eager_ms, _ = time_graph(step, max(3, args.steps // 5), 2, use_graph=False)
     print("# timing dominant kernel", file=sys.stderr, flush=True)
     roof = dominant_kernel(wl, args.steps, args.warmup, args.chunk_keys)
+    sparse = None
+    if not args.no_sparse:
+        print("# timing sparse top-k decode", file=sys.stderr, flush=True)
+        sparse = sparse_kernel(args.steps, args.warmup, args.seed)
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -285,7 +335,7 @@ def main():
         "kv_bytes_per_step": wl.kv_bytes,
         "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "cpu_baseline": cpu, "sparse": sparse,
     }
     print(json.dumps(rec), flush=True)
 

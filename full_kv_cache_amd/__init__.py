@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.hda_status_string.argtypes = [ctypes.c_int]
         L.hda_last_error_message.restype = ctypes.c_char_p
         L.hda_last_error_message.argtypes = []
+        L.hda_decode_step_workspace_bytes.restype = sz
+        L.hda_decode_step_workspace_bytes.argtypes = [D, ctypes.c_int]
+        L.hda_decode_step.restype = ctypes.c_int
+        L.hda_decode_step.argtypes = [P, P, P, P, ctypes.c_int, D, P, ctypes.c_float, P, P, P, sz, P]
         L.hda_sparse_workspace_bytes.restype = ctypes.c_size_t
         L.hda_sparse_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.hda_sparse_decode_attn.restype = ctypes.c_int
@@ -195,6 +199,23 @@ def hda_lse_merge(part_o, part_lse, sinks, out, lse=None, stream=None):
         validate_sinks(sinks, out)
     _check(lib().hda_lse_merge(_ptr(part_o), _ptr(part_lse), int(B), int(H), int(S), int(D),
                                _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def hda_decode_step_workspace_bytes(cache: LayerCache, layer_type: int) -> int:
+    d = cache.desc()
+    return int(lib().hda_decode_step_workspace_bytes(ctypes.byref(d), int(layer_type)))
+
+
+def hda_decode_step(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, sinks, scale: float,
+                    out, lse=None, workspace=None, stream=None):
+    """RoPE + append + attention of one layer in one launch (q is not modified).
+    The workspace must be zero-filled before its first use."""
+    validate_sinks(sinks, q)
+    d = cache.desc()
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hda_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), int(layer_type),
+                                 ctypes.byref(d), _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), wbytes, _stream(stream)))
 
 
 def hda_sparse_workspace_bytes(tokens: int, num_q_heads: int, topk: int, dv: int = 512) -> int:

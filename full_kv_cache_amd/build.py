@@ -5,7 +5,9 @@
 Compiles every HIP source under ``csrc/`` and the host API into one shared
 library next to this file.  Packed-fp32 instructions are disabled for the
 device code (``-packed-fp32-ops``); the host pass warns that it does not
-know the feature, which is harmless.
+know the feature, which is harmless.  Type-based alias analysis is off
+(``-fno-strict-aliasing``): KV rows are loaded through one vector type and
+stored through another, and a store must never pass a load of the same row.
 """
 from __future__ import annotations
 
@@ -20,13 +22,16 @@ LIB = HERE / "libhda.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["hda_api.cpp", "rope_append.hip", "decode_attn.hip", "sparse_attn.hip"]
+SOURCES = ["hda_api.cpp", "rope_append.hip", "decode_attn.hip", "decode_step.hip", "sparse_attn.hip"]
 
 
 def compile_flags() -> list[str]:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
         "-Wno-unused-parameter", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the kernels read KV rows as one vector type and write them as another:
+        # ordering between the two must come from the addresses, not the types
+        "-fno-strict-aliasing",
         "-I", str(HERE.parent / "include"),
     ]
 

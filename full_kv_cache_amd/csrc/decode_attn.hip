@@ -39,14 +39,13 @@
 //
 // The path is HBM-bound: every K and V byte is read once and serves G heads
 // (4 flop per byte at G = 4), far below the VALU and MFMA ridge points.
-#include "hda_device.h"
-#include "hda_kernels.h"
+#include "decode_wave.h"
 
 namespace hda {
 
 namespace {
 
-constexpr float kLn2 = 0.693147180559945309f;
+using namespace wave;
 
 // Keys attended by sequence b (0 for seq_len <= 0).
 __device__ __forceinline__ int num_keys(const DecodeParams &p, int b) {
@@ -54,211 +53,6 @@ __device__ __forceinline__ int num_keys(const DecodeParams &p, int b) {
     n = n < p.max_keys ? n : p.max_keys;
     if (p.sliding) n = n < p.window ? n : p.window;
     return n > 0 ? n : 0;
-}
-
-// Orders this wave's LDS writes before its later LDS reads (LDS executes a
-// wave's instructions in order; this stops the compiler from moving them).
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ void bf16x8_to_f32(const uint4 &v, float *x) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(w[i]);
-        x[2 * i + 1] = bf16_hi(w[i]);
-    }
-}
-
-__device__ __forceinline__ float lane_value(float v, int src_lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// DPP lane moves inside each row of 16 lanes: swap neighbours, swap lane
-// pairs, mirror each half-row, mirror the row.  Applied in that order they
-// pair every lane with partners in the other quad, half-row and half, so
-// max / sum over the row land in all its 16 lanes without touching LDS.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp<kQuadSwap1>(v));
-    v = fmaxf(v, dpp<kQuadSwap2>(v));
-    v = fmaxf(v, dpp<kHalfMirror>(v));
-    return fmaxf(v, dpp<kRowMirror>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp<kQuadSwap1>(v);
-    v += dpp<kQuadSwap2>(v);
-    v += dpp<kHalfMirror>(v);
-    return v + dpp<kRowMirror>(v);
-}
-
-// 2^x on the transcendental unit; arguments here are <= 0 (and -inf), where
-// a flushed denormal result is as good as exact for a softmax weight.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// MFMA A operand for KV head kvh of sequence b: lane (m = lane%16,
-// kg = lane/16) holds q[head m][32j + 8kg .. +7] for k-step j; rows m >= G
-// are zero.
-template <int G>
-__device__ __forceinline__ void load_q_operand(const DecodeParams &p, int b, int kvh, int lane,
-                                               bf16x8 *qa) {
-    const int mrow = lane & 15, kg = lane >> 4;
-    const int hrow = mrow < G ? mrow : 0;
-    const uint16_t *qr = p.q + ((int64_t)b * p.num_q_heads + kvh * G + hrow) * kHeadDim + 8 * kg;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint4 u = ld16(qr + 32 * j);
-        if (mrow >= G) u = make_uint4(0, 0, 0, 0);
-        qa[j] = as_bf16x8(u);
-    }
-}
-
-// One wave's running softmax state over 16-key rounds.
-//   acc[h][e]: unnormalised output, head h, dim 8*(lane%32) + e, summed
-//              over this half-wave's keys (the two halves add up at the end);
-//   m_run[i] / l_lane[i]: running max (log2 domain) and this lane's share of
-//              the running sum, for head 4*(lane/16) + i.
-template <int G>
-struct WaveSoftmax {
-    float acc[G][8];
-    float m_run[4], l_lane[4];
-
-    __device__ __forceinline__ void reset() {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m_run[i] = -INFINITY;
-            l_lane[i] = 0.f;
-        }
-    }
-
-    // One 16-key round: kt = the 8 K operand loads (key = 16-lane index),
-    // vt = the 8 V row loads (keys 2u + half), key x of the round valid iff
-    // lo <= x < hi (at least one is).  pw: this wave's LDS scratch, 16*G floats.
-    __device__ __forceinline__ void round(const bf16x8 *qa, const uint4 *kt, uint4 *vt, int lo,
-                                          int hi, float scale_log2, float *pw, int lane) {
-        const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kt[j]), sc, 0, 0, 0);
-        // lane holds heads 4*kg + i of key mrow; a masked key's score is
-        // replaced, never combined, so whatever its row holds cannot leak
-        const bool valid = mrow >= lo && mrow < hi;
-        float alpha[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float s = valid ? sc[i] * scale_log2 : -INFINITY;
-            const float mn = fmaxf(m_run[i], row16_max(s));  // finite: the round holds a key
-            alpha[i] = fast_exp2(m_run[i] - mn);
-            s = fast_exp2(s - mn);
-            l_lane[i] = fmaf(l_lane[i], alpha[i], s);
-            m_run[i] = mn;
-            sc[i] = s;
-        }
-        if (4 * kg < G) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * kg + i < G) pw[mrow * G + 4 * kg + i] = sc[i];
-        }
-        // Rescale the running output only when some head's maximum moved.
-        float a_h[G];
-        bool moved = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            a_h[h] = lane_value(alpha[h & 3], 16 * (h >> 2));
-            moved |= a_h[h] != 1.f;
-        }
-        if (moved) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= a_h[h];
-        }
-        // Rows of masked keys may hold anything (even NaN, which a zero
-        // weight would not cancel): a round that has some reads them as 0.
-        if (lo > 0 || hi < 16) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int key = 2 * u + hw;
-                if (key < lo || key >= hi) vt[u] = make_uint4(0, 0, 0, 0);
-            }
-        }
-        wave_lds_fence();
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            float pv[G], x[8];
-#pragma unroll
-            for (int h = 0; h < G; ++h) pv[h] = pw[(2 * u + hw) * G + h];
-            bf16x8_to_f32(vt[u], x);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
-        }
-        wave_lds_fence();
-    }
-
-    // Wave totals for head h (wave-uniform): running max and sum.
-    __device__ __forceinline__ float max_of(int h) const { return lane_value(m_run[h & 3], 16 * (h >> 2)); }
-    __device__ __forceinline__ void sums(float *l_h) const {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) l_h[i] = row16_sum(l_lane[i]);
-    }
-};
-
-// Loads of one round: the 16 keys start at block row r0e (kept at most
-// capacity - 16 so that every load stays inside the block); the caller
-// masks keys outside [r0, n).  Passing lane 0 for every lane makes a
-// placeholder round: the same number of load instructions, all of one
-// 16-byte address, so the wait counts stay exact at no traffic.
-__device__ __forceinline__ void issue_round(const uint16_t *kblk, const uint16_t *vblk, int r0e,
-                                            int lane, uint4 *kt, uint4 *vt) {
-    const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
-    const uint16_t *rk = kblk + (int64_t)(r0e + mrow) * kHeadDim + 8 * kg;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kt[j] = ld16_stream(rk + 32 * j);
-    const uint16_t *rv = vblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) vt[u] = ld16_stream(rv + 2 * u * kHeadDim);
-}
-
-// Writes o / l for the G heads (first half-wave) and their lse.
-template <int G>
-__device__ __forceinline__ void store_partial(const WaveSoftmax<G> &st, float *po, float *plse,
-                                              int lane) {
-    const int hw = lane >> 5, dl = lane & 31;
-    float l_h[4];
-    st.sums(l_h);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
-        const float inv = 1.f / l;
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64)) * inv;
-        if (hw == 0) {
-            float *dst = po + h * kHeadDim + 8 * dl;
-            *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-        }
-        if (lane == 0) plse[h] = (st.max_of(h) + log2f(l)) * kLn2;
-    }
 }
 
 // ===================================================================
@@ -302,7 +96,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
     const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
 
     bf16x8 qa[8];
-    load_q_operand<G>(p, b, kvh, lane, qa);
+    load_q_operand<G>(p.q, p.num_q_heads, b, kvh, lane, qa);
     WaveSoftmax<G> st;
     st.reset();
     for (int kr = kw0; kr < kw1; kr += 16) {
@@ -408,10 +202,6 @@ __global__ __launch_bounds__(kDecodeThreads) void lse_merge_kernel(MergeParams p
 // MI355X: device-wide atomics serialise, and a partial per ticket adds
 // traffic.)
 // ===================================================================
-struct RoundAddr {
-    int b, kvh, rr;  // sequence, KV head, round within the pair
-};
-
 struct RoundGeo {
     const uint16_t *kblk, *vblk;
     int r0e, lo, hi;  // in-bounds first row; valid keys [lo, hi) of the round
@@ -427,22 +217,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     const int w = blockIdx.x, W = gridDim.x;
     const int B = p.batch, Hkv = p.num_kv_heads;
 
-    // prefix sum of rounds per sequence: wave scan, 64 sequences a pass
-    {
-        int carry = 0;
-        for (int base = 0; base < B; base += 64) {
-            const int b = base + lane;
-            int x = b < B ? (num_keys(p, b) + 15) >> 4 : 0;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
-            }
-            if (b < B) s_pre[b + 1] = carry + x;
-            carry += __shfl(x, 63, 64);
-        }
-        if (lane == 0) s_pre[0] = 0;
-    }
+    round_prefix(s_pre, B, lane, [&](int b) { return num_keys(p, b); });
     __syncthreads();
     if (w == 0)  // published for the merge kernel
         for (int b = lane; b <= B; b += 64) p.stream_pre[b] = s_pre[b];
@@ -450,33 +225,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     const int64_t g0 = (int64_t)w * r_tot / W, g1 = (int64_t)(w + 1) * r_tot / W;
     if (g0 >= g1) return;
 
-    // locate round g0: the sequence by binary search, then KV head and round
-    RoundAddr cur;
-    {
-        int lo = 0, hi = B;  // largest b with Hkv * pre[b] <= g0
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if ((int64_t)Hkv * s_pre[mid] <= g0) lo = mid; else hi = mid;
-        }
-        int b = lo;
-        while ((int64_t)Hkv * s_pre[b + 1] <= g0) ++b;  // sequences without rounds
-        const int rb = s_pre[b + 1] - s_pre[b];
-        const int off = (int)(g0 - (int64_t)Hkv * s_pre[b]);
-        cur.b = uniform(b);
-        cur.kvh = uniform(off / rb);
-        cur.rr = uniform(off % rb);
-    }
-    auto rounds_of = [&](int b) { return uniform(s_pre[b + 1] - s_pre[b]); };
-    auto advance = [&](RoundAddr a) {
-        if (++a.rr == rounds_of(a.b)) {
-            a.rr = 0;
-            if (++a.kvh == Hkv) {
-                a.kvh = 0;
-                do { ++a.b; } while (a.b < B && rounds_of(a.b) == 0);
-            }
-        }
-        return a;
-    };
+    RoundAddr cur = locate_round(s_pre, B, Hkv, g0);
+    auto advance = [&](RoundAddr a) { return next_round(s_pre, B, Hkv, a); };
 
     const int64_t cap = p.capacity, cap16 = cap - 16;
     auto geo = [&](const RoundAddr &a) {
@@ -497,7 +247,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     uint4 kA[8], vA[8], kB[8], vB[8];
     RoundGeo gc = geo(cur);
     issue_round(gc.kblk, gc.vblk, gc.r0e, lane, kA, vA);
-    load_q_operand<G>(p, cur.b, cur.kvh, lane, qa);
+    load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
     st.reset();
 
     auto end_segment = [&](const RoundAddr &a) {
@@ -519,7 +269,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
-            load_q_operand<G>(p, nxt.b, nxt.kvh, lane, qa);
+            load_q_operand<G>(p.q, p.num_q_heads, nxt.b, nxt.kvh, lane, qa);
             st.reset();
         }
         cur = nxt;
@@ -534,7 +284,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
-            load_q_operand<G>(p, nxt.b, nxt.kvh, lane, qa);
+            load_q_operand<G>(p.q, p.num_q_heads, nxt.b, nxt.kvh, lane, qa);
             st.reset();
         }
         cur = nxt;
@@ -562,8 +312,8 @@ __global__ __launch_bounds__(kDecodeThreads) void stream_merge_kernel(DecodePara
     const int64_t r_tot = (int64_t)Hkv * p.stream_pre[p.batch];
     const int64_t g_lo = (int64_t)Hkv * p.stream_pre[b] + (int64_t)kvh * rb;
     const int64_t g_hi = g_lo + rb - 1;
-    const int w_lo = (int)(((g_lo + 1) * W - 1) / r_tot);
-    const int w_hi = (int)(((g_hi + 1) * W - 1) / r_tot);
+    const int w_lo = wave_of_round(g_lo, r_tot, W);
+    const int w_hi = wave_of_round(g_hi, r_tot, W);
     const int64_t pair = (int64_t)b * Hkv + kvh;
     float M = -INFINITY;
     for (int w = w_lo; w <= w_hi; ++w) M = fmaxf(M, p.part_lse[(w + pair) * G + h]);

@@ -1,0 +1,461 @@
+// decode_step.hip -- one layer's decode step in one launch (gfx950): partial
+// RoPE of q and k_new, the KV append, GQA attention over the layer's keys,
+// the LSE merge of split pairs and the sink.
+//
+// What is computed is hda_rope_append followed by hda_decode_attn with
+// seq_len = pos + 1 (Spark export page: `_angles`, `_rope`, `_Layer.forward`
+// ring branch; flashmla_sparse page, `HYV4FlashMLASparseImpl` docstring, for
+// the sink), except that the rotated q lives in registers only.
+//
+// Keys of sequence b at position P are rows 0..n-1 of its block, n =
+// min(P+1, window) for a sliding layer, min(P+1, capacity) for a full one.
+// Row vrow = min(P, window-1) (sliding) or P (full) stands for the new token:
+// whatever memory holds there, the wave scoring that row replaces its K and V
+// registers by the rotated k_new and v_new.  Every other key row is read
+// before anything in this launch writes it:
+//   * full, and sliding with P < window-1: the new token belongs in row vrow;
+//     the wave that scores vrow's round stores it there.
+//   * sliding with P >= window-1: it belongs in ring slot s = P mod
+//     (window-1), whose entry (position P-window+1) is still a key of this
+//     step.  The wave that scores s's round, once its loads of that round are
+//     in, stores that entry to row window-1 (the evicted-entry row; only
+//     vrow's round reads it, and replaces what it reads) and the new token
+//     to slot s.
+// The block thus ends as hda_rope_append leaves it, and no wave waits on
+// another wave's store.
+//
+// The work is split like the balanced streaming decode: all 16-key rounds
+// of all (sequence, KV head) pairs evenly over resident single-wave
+// workgroups.  A pair inside one wave is finished there.  A pair spread over
+// several waves leaves one partial per wave; the last of them to finish
+// (device-scope counter per pair between release and acquire fences) merges
+// them once its own rounds are done, writes out and lse with the sink, and
+// resets the counter to zero for the next launch.
+#include "decode_wave.h"
+
+namespace hda {
+
+namespace {
+
+using namespace wave;
+
+// Keys of sequence b this step (0 for a negative position).
+__device__ __forceinline__ int step_keys(const StepParams &p, int b) {
+    const int P = p.pos[b];
+    if (P < 0) return 0;
+    const int64_t lim = p.sliding ? (int64_t)p.window : p.capacity;
+    const int64_t n = (int64_t)P + 1;
+    return (int)(n < lim ? n : lim);
+}
+
+struct RoundGeo {
+    const uint16_t *kblk, *vblk;
+    int r0e, lo, hi;  // in-bounds first row; valid keys [lo, hi) of the round
+};
+
+// Rows of the current pair that this launch treats specially.
+struct PairRows {
+    int vrow;  // row served by the new token (>= n: none)
+    int srow;  // sliding past the window: slot taking the new token; else -1
+    int erow;  // evicted-entry row, window-1
+};
+
+// Writes out (bf16, with the sink) and lse of a pair finished in one wave.
+template <int G>
+__device__ __forceinline__ void store_final(const WaveSoftmax<G> &st, const StepParams &p, int b,
+                                            int kvh, int lane) {
+    const int hw = lane >> 5, dl = lane & 31;
+    float l_h[4];
+    st.sums(l_h);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const int hq = kvh * G + h;
+        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
+        const float lse = (st.max_of(h) + log2f(l)) * kLn2;
+        float f = 1.f / l;
+        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = (st.acc[h][2 * e] + __shfl_xor(st.acc[h][2 * e], 32, 64)) * f;
+            const float c = (st.acc[h][2 * e + 1] + __shfl_xor(st.acc[h][2 * e + 1], 32, 64)) * f;
+            w[e] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(c) << 16);
+        }
+        const int64_t row = (int64_t)b * p.num_q_heads + hq;
+        if (hw == 0)
+            *reinterpret_cast<uint4 *>(p.out + row * kHeadDim + 8 * dl) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (lane == 0 && p.lse) p.lse[row] = lse;
+    }
+}
+
+// Merge of a pair's partials in slots [s0, s0 + nseg): lse = ln sum exp(lse_s),
+// out = sum exp(lse_s - lse) o_s, then the sink.  Lane = dims 4*lane .. +3
+// of every head; segments in batches, online rescaling between batches.
+template <int G>
+__device__ __forceinline__ void merge_pair(const StepParams &p, int64_t s0, int nseg, int b, int kvh,
+                                           int lane) {
+    constexpr int D = kHeadDim;
+    constexpr int K = G >= 16 ? 2 : 32 / G;  // segments per batch
+    float M[G], L[G];
+    float4 o[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        M[h] = -INFINITY;
+        L[h] = 0.f;
+        o[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int base = 0; base < nseg; base += K) {
+        float ls[K][G];
+        float4 ov[K][G];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const bool in = base + k < nseg;
+            const int64_t slot = s0 + (in ? base + k : nseg - 1);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float x = p.part_lse[slot * G + h];
+                ls[k][h] = in ? x : -INFINITY;
+                ov[k][h] = *reinterpret_cast<const float4 *>(p.part_o + (slot * G + h) * D + 4 * lane);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float bm = M[h];
+#pragma unroll
+            for (int k = 0; k < K; ++k) bm = fmaxf(bm, ls[k][h]);  // finite: segment 0 holds keys
+            const float sc = expf(M[h] - bm);                      // 0 on the first batch
+            L[h] *= sc;
+            o[h].x *= sc; o[h].y *= sc; o[h].z *= sc; o[h].w *= sc;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float wgt = expf(ls[k][h] - bm);  // padding: exp(-inf) = 0
+                L[h] += wgt;
+                o[h].x = fmaf(wgt, ov[k][h].x, o[h].x);
+                o[h].y = fmaf(wgt, ov[k][h].y, o[h].y);
+                o[h].z = fmaf(wgt, ov[k][h].z, o[h].z);
+                o[h].w = fmaf(wgt, ov[k][h].w, o[h].w);
+            }
+            M[h] = bm;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const int hq = kvh * G + h;
+        const float lse = M[h] + logf(L[h]);
+        float f = 1.f / L[h];
+        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        const int64_t row = (int64_t)b * p.num_q_heads + hq;
+        const uint32_t lo = (uint32_t)f32_to_bf16(o[h].x * f) | ((uint32_t)f32_to_bf16(o[h].y * f) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(o[h].z * f) | ((uint32_t)f32_to_bf16(o[h].w * f) << 16);
+        *reinterpret_cast<uint2 *>(p.out + row * D + 4 * lane) = make_uint2(lo, hi);
+        if (lane == 0 && p.lse) p.lse[row] = lse;
+    }
+}
+
+template <int G, int ROT>
+__global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
+    constexpr int D = kHeadDim;
+    static_assert(ROT % 16 == 0 && ROT <= D, "rotary dims in 16-byte chunk pairs");
+    __shared__ int s_pre[kStreamMaxBatch + 1];
+    __shared__ __align__(16) float s_pw[16 * G];
+    __shared__ __align__(16) float s_cos[ROT / 2], s_sin[ROT / 2];
+    // rotated q of the pair's G heads, then its rotated new K, then new V
+    __shared__ __align__(16) uint16_t s_rows[(G + 2) * D];
+    uint16_t *const s_knew = s_rows + G * D, *const s_vnew = s_rows + (G + 1) * D;
+
+    const int lane = threadIdx.x;
+    const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
+    const int w = blockIdx.x, W = gridDim.x;
+    const int B = p.batch, Hkv = p.num_kv_heads;
+
+    round_prefix(s_pre, B, lane, [&](int b) { return step_keys(p, b); });
+    __syncthreads();
+    // sequences without keys (negative position): out 0, lse -inf
+    for (int b = w; b < B; b += W) {
+        if (s_pre[b + 1] != s_pre[b]) continue;
+        const int64_t n_out = (int64_t)p.num_q_heads * D;
+        uint16_t *ob = p.out + (int64_t)b * n_out;
+        for (int64_t i = 8 * lane; i < n_out; i += 8 * 64)
+            *reinterpret_cast<uint4 *>(ob + i) = make_uint4(0, 0, 0, 0);
+        if (p.lse)
+            for (int h = lane; h < p.num_q_heads; h += 64) p.lse[(int64_t)b * p.num_q_heads + h] = -INFINITY;
+    }
+    const int64_t r_tot = (int64_t)Hkv * s_pre[B];
+    const int64_t g0 = (int64_t)w * r_tot / W, g1 = (int64_t)(w + 1) * r_tot / W;
+    if (g0 >= g1) return;
+
+    RoundAddr cur = locate_round(s_pre, B, Hkv, g0);
+    const int64_t cap = p.capacity, cap16 = cap - 16;
+    auto geo = [&](const RoundAddr &a) {
+        RoundGeo g;
+        const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
+        g.kblk = p.k + bh * cap * D;
+        g.vblk = p.v + bh * cap * D;
+        const int r0 = a.rr * 16;
+        g.r0e = (int)(r0 < cap16 ? r0 : cap16);
+        g.lo = r0 - g.r0e;
+        g.hi = uniform(step_keys(p, a.b)) - g.r0e;
+        return g;
+    };
+    auto same_pair = [](const RoundAddr &x, const RoundAddr &y) { return x.b == y.b && x.kvh == y.kvh; };
+
+    // Entering a pair: the angle table, then the pair's G query rows and its
+    // new K row rotated (and the new V row copied) into LDS, 16-byte chunk
+    // pairs spread over the lanes.
+    auto enter_pair = [&](const RoundAddr &a) {
+        PairRows pr;
+        const int P = uniform(p.pos[a.b]);
+        pr.erow = p.window - 1;
+        pr.vrow = p.sliding ? min(P, p.window - 1) : P;
+        pr.srow = (p.sliding && P >= p.window - 1) ? P % (p.window - 1) : -1;
+        const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
+        wave_lds_fence();  // the previous pair's LDS reads are done
+        for (int i = lane; i < ROT / 2; i += 64) {
+            const float ang = (float)P * p.inv_freq[i];  // one fp32 multiply
+            sincos_angle(ang, s_cos + i, s_sin + i);
+        }
+        wave_lds_fence();
+        // rows r < G: query heads; r = G: new K; r = G + 1: new V (copied)
+        constexpr int kRotTasks = ROT / 16, kRowTasks = kRotTasks + (D - ROT) / 8;
+        const uint16_t *qrow = p.q + ((int64_t)a.b * p.num_q_heads + a.kvh * G) * D;
+#pragma unroll 1
+        for (int t = lane; t < (G + 1) * kRowTasks + D / 8; t += 64) {
+            const int r = t / kRowTasks, c = t % kRowTasks;
+            if (r > G) {  // new V
+                const int d = 8 * (t - (G + 1) * kRowTasks);
+                *reinterpret_cast<uint4 *>(s_vnew + d) = ld16(p.v_new + bh * D + d);
+                continue;
+            }
+            const uint16_t *src = r < G ? qrow + r * D : p.k_new + bh * D;
+            uint16_t *dst = s_rows + r * D;
+            if (c < kRotTasks) {
+                const int i = 8 * c;
+                uint4 x1 = ld16(src + i), x2 = ld16(src + ROT / 2 + i);
+                rotate8(x1, x2, s_cos + i, s_sin + i, x1, x2);
+                *reinterpret_cast<uint4 *>(dst + i) = x1;
+                *reinterpret_cast<uint4 *>(dst + ROT / 2 + i) = x2;
+            } else {
+                const int d = ROT + 8 * (c - kRotTasks);
+                *reinterpret_cast<uint4 *>(dst + d) = ld16(src + d);
+            }
+        }
+        wave_lds_fence();
+        return pr;
+    };
+    // The q operand is read from LDS for every round instead of being held
+    // in registers through the loop (rows >= G read row 0 and are zeroed).
+    const uint16_t *const q_lds = s_rows + (mrow < G ? mrow : 0) * D + 8 * kg;
+    auto load_qa = [&](bf16x8 *qa) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint4 u = *reinterpret_cast<const uint4 *>(q_lds + 32 * j);
+            if (mrow >= G) u = make_uint4(0, 0, 0, 0);
+            qa[j] = as_bf16x8(u);
+        }
+    };
+
+    // Whether block row `row` is a valid key of this round (hi may exceed 16).
+    auto in_round = [](const RoundGeo &g, int row) {
+        const int x = row - g.r0e;
+        return x >= g.lo && x < g.hi && x < 16;
+    };
+    // Key of the round served by the new token, or -1.
+    auto sub_row = [&](const RoundGeo &g, const PairRows &pr) {
+        return in_round(g, pr.vrow) ? pr.vrow - g.r0e : -1;
+    };
+
+    // After scoring a round: the append's stores (see the file comment).
+    // The round's loads are consumed by then, so every old row it holds was
+    // read before anything overwrites it.
+    auto append_after = [&](const RoundAddr &a, const RoundGeo &g, const PairRows &pr, const uint4 *kt,
+                            const uint4 *vt) {
+        const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
+        const int sr = pr.srow - g.r0e;
+        const bool has_s = pr.srow >= 0 && in_round(g, pr.srow);
+        const bool has_v = pr.srow < 0 && in_round(g, pr.vrow);
+        if (!has_s && !has_v) return;
+        if (has_s) {  // the slot's old entry to the evicted-entry row
+            uint16_t *ke = p.k + (bh * cap + pr.erow) * D, *ve = p.v + (bh * cap + pr.erow) * D;
+            if (mrow == sr) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(ke + 32 * j + 8 * kg) = kt[j];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (2 * u + hw == sr) *reinterpret_cast<uint4 *>(ve + 8 * dl) = vt[u];
+        }
+        // the new token into its row: lanes 0..31 K, 32..63 V, 16 bytes each.
+        // Slot s was loaded by this round; its store must not be issued before
+        // those loads have returned, so its address is made to depend on a
+        // register of each of the round's 16 loads (the compiler then waits
+        // for all of them).
+        const int64_t drow = has_s ? pr.srow : pr.vrow;
+        int off = 8 * dl;
+        asm volatile("" : "+v"(off)
+                     : "v"(kt[0].w), "v"(kt[1].w), "v"(kt[2].w), "v"(kt[3].w), "v"(kt[4].w),
+                       "v"(kt[5].w), "v"(kt[6].w), "v"(kt[7].w), "v"(vt[0].w), "v"(vt[1].w),
+                       "v"(vt[2].w), "v"(vt[3].w), "v"(vt[4].w), "v"(vt[5].w), "v"(vt[6].w),
+                       "v"(vt[7].w));
+        uint16_t *dst = (lane < 32 ? p.k : p.v) + (bh * cap + drow) * D + off;
+        *reinterpret_cast<uint4 *>(dst) =
+            *reinterpret_cast<const uint4 *>((lane < 32 ? s_knew : s_vnew) + 8 * dl);
+    };
+
+    // Segment end: finish the pair here, or leave a partial and count in.
+    // Returns the number of segments when this wave arrived last (the merge
+    // is done after the wave's own rounds), else 0.
+    WaveSoftmax<G> st;
+    auto end_segment = [&](const RoundAddr &a, int64_t &s0) -> int {
+        const int rb = s_pre[a.b + 1] - s_pre[a.b];
+        const int64_t g_lo = (int64_t)Hkv * s_pre[a.b] + (int64_t)a.kvh * rb;
+        const int w_lo = wave_of_round(g_lo, r_tot, W);
+        const int w_hi = wave_of_round(g_lo + rb - 1, r_tot, W);
+        if (w_lo == w_hi) {
+            store_final<G>(st, p, a.b, a.kvh, lane);
+            return 0;
+        }
+        const int64_t pair = (int64_t)a.b * Hkv + a.kvh;
+        const int64_t slot = (int64_t)w + pair;
+        store_partial<G>(st, p.part_o + slot * G * D, p.part_lse + slot * G, lane);
+        __threadfence();  // release: the partial before the count
+        int old = 0;
+        if (lane == 0) old = atomicAdd(p.counters + pair, 1);
+        old = __shfl(old, 0, 64);
+        if (old != w_hi - w_lo) return 0;
+        __threadfence();  // acquire: every partial of the pair after the count
+        if (lane == 0) atomicExch(p.counters + pair, 0);
+        s0 = (int64_t)w_lo + pair;
+        return w_hi - w_lo + 1;
+    };
+
+    // At most two of a wave's pairs are shared with other waves: its first
+    // and its last.
+    int m_n[2] = {0, 0}, m_b[2] = {0, 0}, m_kvh[2] = {0, 0};
+    int64_t m_s0[2] = {0, 0};
+    int n_merge = 0;
+    auto finish = [&](const RoundAddr &a) {
+        int64_t s0 = 0;
+        const int n = end_segment(a, s0);
+        if (n && n_merge < 2) {
+            m_n[n_merge] = n;
+            m_b[n_merge] = a.b;
+            m_kvh[n_merge] = a.kvh;
+            m_s0[n_merge] = s0;
+            ++n_merge;
+        }
+    };
+
+    uint4 kA[8], vA[8], kB[8], vB[8];
+    RoundGeo gc = geo(cur);
+    issue_round(gc.kblk, gc.vblk, gc.r0e, lane, kA, vA);
+    PairRows pr = enter_pair(cur);
+    st.reset();
+
+    // Two rounds in flight, as in the streaming decode; the last round
+    // issues a placeholder round of one address.
+    int64_t g = g0;
+    while (true) {
+        bool more = g + 1 < g1;
+        RoundAddr nxt = more ? next_round(s_pre, B, Hkv, cur) : cur;
+        RoundGeo gn = geo(nxt);
+        issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kB, vB);
+        {
+            bf16x8 qa[8];
+            load_qa(qa);
+            st.template round<true>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, lane, sub_row(gc, pr),
+                                    s_knew, s_vnew);
+        }
+        append_after(cur, gc, pr, kA, vA);
+        if (!more || !same_pair(nxt, cur)) {
+            finish(cur);
+            if (!more) break;
+            pr = enter_pair(nxt);
+            st.reset();
+        }
+        cur = nxt;
+        gc = gn;
+        ++g;
+
+        more = g + 1 < g1;
+        nxt = more ? next_round(s_pre, B, Hkv, cur) : cur;
+        gn = geo(nxt);
+        issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kA, vA);
+        {
+            bf16x8 qa[8];
+            load_qa(qa);
+            st.template round<true>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, lane, sub_row(gc, pr),
+                                    s_knew, s_vnew);
+        }
+        append_after(cur, gc, pr, kB, vB);
+        if (!more || !same_pair(nxt, cur)) {
+            finish(cur);
+            if (!more) break;
+            pr = enter_pair(nxt);
+            st.reset();
+        }
+        cur = nxt;
+        gc = gn;
+        ++g;
+    }
+    for (int i = 0; i < n_merge; ++i) merge_pair<G>(p, m_s0[i], m_n[i], m_b[i], m_kvh[i], lane);
+}
+
+template <int G, int ROT>
+int step_slots_gr() {
+    static int cached = -1;
+    if (cached < 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<G, ROT>, 64, 0) !=
+                hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        cached = cus * per_cu;
+    }
+    return cached;
+}
+
+template <int G>
+int step_slots_g(int rot) {
+    return rot == 64 ? step_slots_gr<G, 64>() : rot == 256 ? step_slots_gr<G, 256>() : 0;
+}
+
+template <int G>
+hipError_t launch_step_g(const StepParams &p, int rot, int waves, hipStream_t s) {
+    if (rot == 64)
+        hipLaunchKernelGGL((decode_step_kernel<G, 64>), dim3(waves), dim3(64), 0, s, p);
+    else if (rot == 256)
+        hipLaunchKernelGGL((decode_step_kernel<G, 256>), dim3(waves), dim3(64), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int step_wave_slots(int group, int rot) {
+    switch (group) {
+        case 1: return step_slots_g<1>(rot);
+        case 2: return step_slots_g<2>(rot);
+        case 4: return step_slots_g<4>(rot);
+        case 8: return step_slots_g<8>(rot);
+        case 16: return step_slots_g<16>(rot);
+        default: return 0;
+    }
+}
+
+hipError_t launch_decode_step(const StepParams &p, int group, int rot, int waves, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    switch (group) {
+        case 1: return launch_step_g<1>(p, rot, waves, stream);
+        case 2: return launch_step_g<2>(p, rot, waves, stream);
+        case 4: return launch_step_g<4>(p, rot, waves, stream);
+        case 8: return launch_step_g<8>(p, rot, waves, stream);
+        case 16: return launch_step_g<16>(p, rot, waves, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hda

@@ -1,0 +1,306 @@
+// decode_wave.h -- the wave-level building blocks of the GQA decode kernels
+// (library-internal; included by decode_attn.hip and decode_step.hip).
+//
+// A 16-key round for one wave and one KV head:
+//   * QK^T on the matrix cores, v_mfma_f32_16x16x32_bf16: the G query heads
+//     are the 16-row A operand (rows >= G zero), the 16 keys the B
+//     operand, fed straight from HBM with 16-byte loads (8 dims of a key row
+//     per lane);
+//   * an online softmax in the log2 domain: round maximum over the 16 key
+//     lanes (DPP), rescale of the running sum and output;
+//   * P.V on the vector ALUs: each half-wave streams whole 512-byte V rows
+//     (lane = 8 dims), every row serving all G heads; the probabilities
+//     reach those lanes through LDS.
+#pragma once
+
+#include "hda_device.h"
+#include "hda_kernels.h"
+
+namespace hda {
+namespace wave {
+
+constexpr float kLn2 = 0.693147180559945309f;
+
+
+// Orders this wave's LDS writes before its later LDS reads (LDS executes a
+// wave's instructions in order; this stops the compiler from moving them).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 &v, float *x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+__device__ __forceinline__ float lane_value(float v, int src_lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// DPP lane moves inside each row of 16 lanes: swap neighbours, swap lane
+// pairs, mirror each half-row, mirror the row.  Applied in that order they
+// pair every lane with partners in the other quad, half-row and half, so
+// max / sum over the row land in all its 16 lanes without touching LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp<kQuadSwap1>(v));
+    v = fmaxf(v, dpp<kQuadSwap2>(v));
+    v = fmaxf(v, dpp<kHalfMirror>(v));
+    return fmaxf(v, dpp<kRowMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    v += dpp<kHalfMirror>(v);
+    return v + dpp<kRowMirror>(v);
+}
+
+// 2^x on the transcendental unit; arguments here are <= 0 (and -inf), where
+// a flushed denormal result is as good as exact for a softmax weight.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// MFMA A operand for KV head kvh of sequence b: lane (m = lane%16,
+// kg = lane/16) holds q[head m][32j + 8kg .. +7] for k-step j; rows m >= G
+// are zero.
+template <int G>
+__device__ __forceinline__ void load_q_operand(const uint16_t *q, int num_q_heads, int b, int kvh,
+                                               int lane, bf16x8 *qa) {
+    const int mrow = lane & 15, kg = lane >> 4;
+    const int hrow = mrow < G ? mrow : 0;
+    const uint16_t *qr = q + ((int64_t)b * num_q_heads + kvh * G + hrow) * kHeadDim + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint4 u = ld16(qr + 32 * j);
+        if (mrow >= G) u = make_uint4(0, 0, 0, 0);
+        qa[j] = as_bf16x8(u);
+    }
+}
+
+// One wave's running softmax state over 16-key rounds.
+//   acc[h][e]: unnormalised output, head h, dim 8*(lane%32) + e, summed
+//              over this half-wave's keys (the two halves add up at the end);
+//   m_run[i] / l_lane[i]: running max (log2 domain) and this lane's share of
+//              the running sum, for head 4*(lane/16) + i.
+template <int G>
+struct WaveSoftmax {
+    float acc[G][8];
+    float m_run[4], l_lane[4];
+
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m_run[i] = -INFINITY;
+            l_lane[i] = 0.f;
+        }
+    }
+
+    // One 16-key round: kt = the 8 K operand loads (key = 16-lane index),
+    // vt = the 8 V row loads (keys 2u + half), key x of the round valid iff
+    // lo <= x < hi (at least one is).  pw: this wave's LDS scratch, 16*G floats.
+    // SUB: key vr of the round (if 0 <= vr < 16) takes its K row from knew
+    // and its V row from vnew (LDS) instead of kt / vt, chunk by chunk at the
+    // point of use.
+    template <bool SUB = false>
+    __device__ __forceinline__ void round(const bf16x8 *qa, const uint4 *kt, uint4 *vt, int lo,
+                                          int hi, float scale_log2, float *pw, int lane, int vr = -1,
+                                          const uint16_t *knew = nullptr,
+                                          const uint16_t *vnew = nullptr) {
+        const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint4 kb = kt[j];
+            if (SUB && mrow == vr) kb = *reinterpret_cast<const uint4 *>(knew + 32 * j + 8 * kg);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kb), sc, 0, 0, 0);
+        }
+        // lane holds heads 4*kg + i of key mrow; a masked key's score is
+        // replaced, never combined, so whatever its row holds cannot leak
+        const bool valid = mrow >= lo && mrow < hi;
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float s = valid ? sc[i] * scale_log2 : -INFINITY;
+            const float mn = fmaxf(m_run[i], row16_max(s));  // finite: the round holds a key
+            alpha[i] = fast_exp2(m_run[i] - mn);
+            s = fast_exp2(s - mn);
+            l_lane[i] = fmaf(l_lane[i], alpha[i], s);
+            m_run[i] = mn;
+            sc[i] = s;
+        }
+        if (4 * kg < G) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kg + i < G) pw[mrow * G + 4 * kg + i] = sc[i];
+        }
+        // Rescale the running output only when some head's maximum moved.
+        float a_h[G];
+        bool moved = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            a_h[h] = lane_value(alpha[h & 3], 16 * (h >> 2));
+            moved |= a_h[h] != 1.f;
+        }
+        if (moved) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= a_h[h];
+        }
+        // Rows of masked keys may hold anything (even NaN, which a zero
+        // weight would not cancel): a round that has some reads them as 0.
+        if (lo > 0 || hi < 16) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int key = 2 * u + hw;
+                if (key < lo || key >= hi) vt[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            float pv[G], x[8];
+#pragma unroll
+            for (int h = 0; h < G; ++h) pv[h] = pw[(2 * u + hw) * G + h];
+            uint4 vv = vt[u];
+            if (SUB && 2 * u + hw == vr) vv = *reinterpret_cast<const uint4 *>(vnew + 8 * dl);
+            bf16x8_to_f32(vv, x);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], x[e], acc[h][e]);
+        }
+        wave_lds_fence();
+    }
+
+    // Wave totals for head h (wave-uniform): running max and sum.
+    __device__ __forceinline__ float max_of(int h) const { return lane_value(m_run[h & 3], 16 * (h >> 2)); }
+    __device__ __forceinline__ void sums(float *l_h) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_h[i] = row16_sum(l_lane[i]);
+    }
+};
+
+// Loads of one round: the 16 keys start at block row r0e (kept at most
+// capacity - 16 so that every load stays inside the block); the caller
+// masks keys outside [r0, n).  Passing lane 0 for every lane makes a
+// placeholder round: the same number of load instructions, all of one
+// 16-byte address, so the wait counts stay exact at no traffic.
+__device__ __forceinline__ void issue_round(const uint16_t *kblk, const uint16_t *vblk, int r0e,
+                                            int lane, uint4 *kt, uint4 *vt) {
+    const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
+    const uint16_t *rk = kblk + (int64_t)(r0e + mrow) * kHeadDim + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kt[j] = ld16_stream(rk + 32 * j);
+    const uint16_t *rv = vblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vt[u] = ld16_stream(rv + 2 * u * kHeadDim);
+}
+
+// Writes o / l for the G heads (first half-wave) and their lse.
+template <int G>
+__device__ __forceinline__ void store_partial(const WaveSoftmax<G> &st, float *po, float *plse,
+                                              int lane) {
+    const int hw = lane >> 5, dl = lane & 31;
+    float l_h[4];
+    st.sums(l_h);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
+        const float inv = 1.f / l;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64)) * inv;
+        if (hw == 0) {
+            float *dst = po + h * kHeadDim + 8 * dl;
+            *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+        if (lane == 0) plse[h] = (st.max_of(h) + log2f(l)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------
+// Balanced streaming partition.  Pair (b, kvh) holds R_b = ceil(n_b / 16)
+// rounds of 16 keys; all rounds, pair after pair, form one index space of
+// R_tot = Hkv * sum_b R_b rounds, which a grid of W single-wave workgroups
+// splits evenly: wave w takes [w*R_tot/W, (w+1)*R_tot/W).
+struct RoundAddr {
+    int b, kvh, rr;  // sequence, KV head, round within the pair
+};
+
+// s_pre[b] = rounds of sequences 0..b-1 (one KV head), keys(b) = n_b; one
+// wave, 64 sequences a pass.  The caller synchronises before reading.
+template <typename Keys>
+__device__ __forceinline__ void round_prefix(int *s_pre, int B, int lane, Keys keys) {
+    int carry = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int b = base + lane;
+        int x = b < B ? (keys(b) + 15) >> 4 : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (b < B) s_pre[b + 1] = carry + x;
+        carry += __shfl(x, 63, 64);
+    }
+    if (lane == 0) s_pre[0] = 0;
+}
+
+// Address of round g (< R_tot): the sequence by binary search, then the KV
+// head and the round within the pair.
+__device__ __forceinline__ RoundAddr locate_round(const int *s_pre, int B, int Hkv, int64_t g) {
+    int lo = 0, hi = B;  // largest b with Hkv * pre[b] <= g
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)Hkv * s_pre[mid] <= g) lo = mid; else hi = mid;
+    }
+    int b = lo;
+    while ((int64_t)Hkv * s_pre[b + 1] <= g) ++b;  // sequences without rounds
+    const int rb = s_pre[b + 1] - s_pre[b];
+    const int off = (int)(g - (int64_t)Hkv * s_pre[b]);
+    RoundAddr a;
+    a.b = uniform(b);
+    a.kvh = uniform(off / rb);
+    a.rr = uniform(off % rb);
+    return a;
+}
+
+__device__ __forceinline__ RoundAddr next_round(const int *s_pre, int B, int Hkv, RoundAddr a) {
+    auto rounds_of = [&](int b) { return uniform(s_pre[b + 1] - s_pre[b]); };
+    if (++a.rr == rounds_of(a.b)) {
+        a.rr = 0;
+        if (++a.kvh == Hkv) {
+            a.kvh = 0;
+            do { ++a.b; } while (a.b < B && rounds_of(a.b) == 0);
+        }
+    }
+    return a;
+}
+
+// Wave whose range holds round g: the largest w with w*R_tot/W <= g.
+__device__ __forceinline__ int wave_of_round(int64_t g, int64_t r_tot, int W) {
+    return (int)(((g + 1) * W - 1) / r_tot);
+}
+
+}  // namespace wave
+}  // namespace hda

@@ -105,14 +105,21 @@ Plan plan_split(const hda_cache_desc *c, int layer, int64_t max_keys, int32_t ch
     return pl;
 }
 
-// Chunk path: [part_o | part_lse].
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Every decode workspace starts with one int per (sequence, KV head): the
+// fused step's arrival counters, which it keeps at zero between calls.  The
+// other paths lay their data out after this header and never write it, so
+// one workspace can serve all of them.
+size_t counter_header(const hda_cache_desc *c) {
+    return up256((size_t)c->batch * c->num_kv_heads * sizeof(int));
+}
+
+// Chunk path: [header | part_o | part_lse].
 size_t workspace_for(const hda_cache_desc *c, const Plan &pl) {
     if (pl.nsplit <= 1) return 0;
     const size_t slots = (size_t)c->batch * c->num_q_heads * pl.nsplit;
-    size_t bytes = slots * hda::kHeadDim * sizeof(float);
-    bytes = (bytes + 255) / 256 * 256;
-    bytes += slots * sizeof(float);
-    return bytes;
+    return counter_header(c) + up256(slots * hda::kHeadDim * sizeof(float)) + slots * sizeof(float);
 }
 
 // Balanced streaming path (chunk_keys == 0): a grid of resident
@@ -143,9 +150,9 @@ struct StreamLayout {
 StreamLayout stream_layout(const hda_cache_desc *c, int waves) {
     const size_t slots = (size_t)waves + (size_t)c->batch * c->num_kv_heads;
     const size_t g = (size_t)(c->num_q_heads / c->num_kv_heads);
-    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    auto up = up256;
     StreamLayout L;
-    L.o_off = 0;
+    L.o_off = counter_header(c);
     L.lse_off = up(slots * g * hda::kHeadDim * sizeof(float));
     L.pre_off = L.lse_off + up(slots * g * sizeof(float));
     L.bytes = L.pre_off + up(((size_t)c->batch + 1) * sizeof(int));
@@ -173,6 +180,56 @@ hda_status check_decode_shape(const hda_cache_desc *c, int layer, int32_t max_se
         return fail(HDA_ERR_INVALID_ARGUMENT,
                     "chunk_keys %d must be 0 or a multiple of 16 in [16, %d]", chunk_keys,
                     hda::kMaxChunk);
+    return HDA_OK;
+}
+
+// ------------------------------------------------------------ fused step
+// Waves of the fused step: as many as fit on the device at once, but no
+// more than ~4 rounds each at the longest keys the cache can hold.
+int step_waves(const hda_cache_desc *c, int layer) {
+    const int64_t keys = layer == HDA_SLIDING ? (int64_t)c->window : c->capacity;
+    const int64_t rounds = (int64_t)c->batch * c->num_kv_heads * ((keys + 15) / 16);
+    int slots = hda::step_wave_slots(c->num_q_heads / c->num_kv_heads, c->rotary_dim);
+    if (slots <= 0 || slots > hda::kStreamMaxWaves) slots = hda::kStreamMaxWaves;
+    int64_t w = (rounds + 3) / 4;
+    if (w > slots) w = slots;
+    if (w < 1) w = 1;
+    return (int)w;
+}
+
+// [counters | part_o | part_lse]; partial slots = waves + pairs.
+struct StepLayout {
+    size_t o_off, lse_off, bytes;
+};
+
+StepLayout step_layout(const hda_cache_desc *c, int waves) {
+    const size_t slots = (size_t)waves + (size_t)c->batch * c->num_kv_heads;
+    const size_t g = (size_t)(c->num_q_heads / c->num_kv_heads);
+    StepLayout L;
+    L.o_off = counter_header(c);
+    L.lse_off = L.o_off + up256(slots * g * hda::kHeadDim * sizeof(float));
+    L.bytes = L.lse_off + up256(slots * g * sizeof(float));
+    return L;
+}
+
+hda_status check_step_shape(const hda_cache_desc *c, int layer) {
+    hda_status st = check_cache(c, layer);
+    if (st != HDA_OK) return st;
+    if (c->head_dim != hda::kHeadDim)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels are built for head_dim %d, got %d",
+                    hda::kHeadDim, c->head_dim);
+    const int g = c->num_q_heads / c->num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+        return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
+    if (c->capacity < 16)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels need a cache of at least 16 rows, got %lld",
+                    (long long)c->capacity);
+    if (c->rotary_dim != 64 && c->rotary_dim != 256)
+        return fail(HDA_ERR_UNSUPPORTED, "the fused step is built for rotary_dim 64 or 256, got %d",
+                    c->rotary_dim);
+    if (c->batch > hda::kStreamMaxBatch)
+        return fail(HDA_ERR_UNSUPPORTED, "the fused step handles at most %d sequences, got %d",
+                    hda::kStreamMaxBatch, c->batch);
     return HDA_OK;
 }
 
@@ -382,10 +439,9 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
         return launched(hda::launch_decode_chunks(p, g, true, s), "decode");
 
     const size_t slots = (size_t)cache->batch * cache->num_q_heads * pl.nsplit;
-    const size_t obytes = (slots * hda::kHeadDim * sizeof(float) + 255) / 256 * 256;
-    char *ws = static_cast<char *>(workspace);
+    char *ws = static_cast<char *>(workspace) + counter_header(cache);
     p.part_o = reinterpret_cast<float *>(ws);
-    p.part_lse = reinterpret_cast<float *>(ws + obytes);
+    p.part_lse = reinterpret_cast<float *>(ws + up256(slots * hda::kHeadDim * sizeof(float)));
     hipError_t e = hda::launch_decode_chunks(p, g, false, s);
     if (e != hipSuccess) return launched(e, "decode partials");
     hda::MergeParams m{};
@@ -441,6 +497,61 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
     m.num_heads = num_heads;
     m.nsplit = nsplit;
     return launched(hda::launch_lse_merge(m, static_cast<hipStream_t>(stream)), "lse merge");
+}
+
+size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer) {
+    if (check_step_shape(cache, layer) != HDA_OK) return 0;
+    return step_layout(cache, step_waves(cache, layer)).bytes;
+}
+
+hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, const int32_t *pos,
+                           hda_layer_type layer, const hda_cache_desc *cache, const float *sinks,
+                           float scale, void *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    hda_status st = check_step_shape(cache, layer);
+    if (st != HDA_OK) return st;
+    if (!q || !k_new || !v_new || !pos || !out)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new, pos and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(pos) & 3u) || (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "pos, sinks and lse must be 4-byte aligned");
+    if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    const int waves = step_waves(cache, layer);
+    const StepLayout L = step_layout(cache, waves);
+    if (!workspace || workspace_bytes < L.bytes)
+        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", L.bytes,
+                    workspace_bytes, workspace);
+    if (!aligned16(workspace)) return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (cache->batch == 0) return ok();
+    hda::StepParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k_new = static_cast<const uint16_t *>(k_new);
+    p.v_new = static_cast<const uint16_t *>(v_new);
+    p.pos = pos;
+    p.k = static_cast<uint16_t *>(cache->k);
+    p.v = static_cast<uint16_t *>(cache->v);
+    p.sinks = sinks;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    char *ws = static_cast<char *>(workspace);
+    p.counters = reinterpret_cast<int *>(ws);
+    p.part_o = reinterpret_cast<float *>(ws + L.o_off);
+    p.part_lse = reinterpret_cast<float *>(ws + L.lse_off);
+    p.capacity = cache->capacity;
+    p.batch = cache->batch;
+    p.num_q_heads = cache->num_q_heads;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.window = cache->window;
+    p.sliding = layer == HDA_SLIDING;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    // fp32 theta^(-2i/rot), rounded once from fp64 (Spark `_angles`)
+    for (int i = 0; i < cache->rotary_dim / 2; ++i)
+        p.inv_freq[i] = (float)(1.0 / std::pow(cache->rope_theta, (double)(2 * i) / (double)cache->rotary_dim));
+    const int g = cache->num_q_heads / cache->num_kv_heads;
+    return launched(hda::launch_decode_step(p, g, cache->rotary_dim, waves, static_cast<hipStream_t>(stream)),
+                    "decode step");
 }
 
 hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_rows,

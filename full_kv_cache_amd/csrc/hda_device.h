@@ -34,6 +34,60 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// neox RoPE of 8 consecutive dim pairs: a holds x[i .. i+7], b holds
+// x[i+h .. i+h+7] (h = rot/2), c / s the fp32 cos / sin of angles i .. i+7.
+// First half x1*cos - x2*sin, second half x2*cos + x1*sin, one fp32 fma
+// each, rounded once to bf16.
+__device__ __forceinline__ void rotate8(const uint4 &a, const uint4 &b, const float *c,
+                                        const float *s, uint4 &ya, uint4 &yb) {
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x1l = bf16_lo(wa[i]), x1h = bf16_hi(wa[i]);
+        const float x2l = bf16_lo(wb[i]), x2h = bf16_hi(wb[i]);
+        const float cl = c[2 * i], sl = s[2 * i], ch = c[2 * i + 1], sh = s[2 * i + 1];
+        // first half: x1*cos - x2*sin; second half: x2*cos + x1*sin
+        const uint16_t y1l = f32_to_bf16(fmaf(x1l, cl, -x2l * sl));
+        const uint16_t y1h = f32_to_bf16(fmaf(x1h, ch, -x2h * sh));
+        const uint16_t y2l = f32_to_bf16(fmaf(x2l, cl, x1l * sl));
+        const uint16_t y2h = f32_to_bf16(fmaf(x2h, ch, x1h * sh));
+        ra[i] = (uint32_t)y1l | ((uint32_t)y1h << 16);
+        rb[i] = (uint32_t)y2l | ((uint32_t)y2h << 16);
+    }
+    ya = make_uint4(ra[0], ra[1], ra[2], ra[3]);
+    yb = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+}
+
+// cos and sin of an fp32 angle, evaluated in fp64 and rounded once to fp32.
+// Cody-Waite reduction x = k*pi/2 + r with pi/2 split in two doubles (hi
+// = pi/2 rounded to double, lo = the remainder), each product subtracted
+// by one fma: for |k| < 2^31 the dropped third term stays below 2^-70, far
+// under half an fp32 ulp.  On |r| <= pi/4 the Taylor series of sin and cos
+// to degree 17 / 18 leave errors below 2^-60; the quadrant k mod 4 picks
+// signs and swaps the two.
+__device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
+    constexpr double kPio2Hi = 1.5707963267948966;       // pi/2 rounded to double
+    constexpr double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
+    constexpr double k2OverPi = 0.63661977236758134;
+    const double x = (double)angle;
+    const double k = rint(x * k2OverPi);
+    const double r = fma(-k, kPio2Lo, fma(-k, kPio2Hi, x));
+    const double r2 = r * r;
+    // sin r = r (1 - r^2/3! (1 - r^2/(4*5) (1 - ...))), cos likewise, Horner
+    double ps = 1.0, pc = 1.0;
+#pragma unroll
+    for (int n = 17; n >= 3; n -= 2) ps = fma(-r2 / (double)((n - 1) * n), ps, 1.0);
+#pragma unroll
+    for (int n = 18; n >= 2; n -= 2) pc = fma(-r2 / (double)((n - 1) * n), pc, 1.0);
+    const double sv = r * ps, cv = pc;
+    const long q = (long)k & 3;
+    const double so = q == 0 ? sv : q == 1 ? cv : q == 2 ? -sv : -cv;
+    const double co = q == 0 ? cv : q == 1 ? -sv : q == 2 ? -cv : sv;
+    *c = (float)co;
+    *s = (float)so;
+}
+
 // Wave64 reductions via butterfly shuffles.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

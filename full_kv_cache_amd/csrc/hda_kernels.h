@@ -43,6 +43,25 @@ struct DecodeParams {
     float scale_log2;           // softmax scale * log2(e)
 };
 
+// Fused decode step (RoPE + append + attention + merge in one launch).
+struct StepParams {
+    const uint16_t *q;          // [B, Hq, D], read only (rotated in registers)
+    const uint16_t *k_new, *v_new;  // [B, Hkv, D]
+    const int32_t *pos;         // [B]
+    uint16_t *k, *v;            // [B, Hkv, cap, D]
+    const float *sinks;         // [Hq] or null
+    uint16_t *out;              // [B, Hq, D]
+    float *lse;                 // [B, Hq] or null
+    float *part_o;              // [slots, G, D], slot = wave + pair
+    float *part_lse;            // [slots, G]
+    int *counters;              // [B * Hkv], zero before and after every launch
+    int64_t capacity;
+    int batch, num_q_heads, num_kv_heads, window;
+    int sliding;
+    float scale_log2;
+    float inv_freq[kHeadDim / 2];  // fp32 theta^(-2i/rot), i < rot/2
+};
+
 struct MergeParams {
     const float *part_o;        // [B, H, nsplit, D]
     const float *part_lse;      // [B, H, nsplit]
@@ -94,6 +113,13 @@ hipError_t launch_decode_stream(const DecodeParams &p, int group, int waves, hip
 // Single-wave workgroups of the streaming kernel that fit on the device at
 // once (occupancy x CUs); 0 if no device is available.
 int stream_wave_slots(int group);
+
+// Fused step over `waves` resident single-wave workgroups; group in
+// {1, 2, 4, 8, 16}, rotary_dim in {64, 256}.  Needs capacity >= 16 and
+// batch <= kStreamMaxBatch.
+hipError_t launch_decode_step(const StepParams &p, int group, int rotary_dim, int waves,
+                              hipStream_t stream);
+int step_wave_slots(int group, int rotary_dim);
 
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 

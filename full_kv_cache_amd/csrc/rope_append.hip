@@ -16,7 +16,8 @@
 // so the read of an old slot element and the write of its replacement
 // happen in one thread.  All global loads are issued first; the angle
 // table is built meanwhile (one pair index per thread: fp32 frequency
-// rounded once from fp64, fp32 angle, fp64 sin/cos rounded to fp32) and
+// rounded once from fp64, fp32 angle, sin/cos evaluated in fp64 and rounded
+// to fp32) and
 // shared through LDS; then results are rotated and stored.  A few KB per
 // sequence: latency, not bandwidth, bounds this kernel.
 #include "hda_device.h"
@@ -28,27 +29,6 @@ namespace {
 
 constexpr int kRopeThreads = 256;
 constexpr int kMaxHalf = 256;  // rotary_dim <= 512
-
-__device__ __forceinline__ void rotate8(const uint4 &a, const uint4 &b, const float *c,
-                                        const float *s, uint4 &ya, uint4 &yb) {
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-    uint32_t ra[4], rb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x1l = bf16_lo(wa[i]), x1h = bf16_hi(wa[i]);
-        const float x2l = bf16_lo(wb[i]), x2h = bf16_hi(wb[i]);
-        const float cl = c[2 * i], sl = s[2 * i], ch = c[2 * i + 1], sh = s[2 * i + 1];
-        // first half: x1*cos - x2*sin; second half: x2*cos + x1*sin
-        const uint16_t y1l = f32_to_bf16(fmaf(x1l, cl, -x2l * sl));
-        const uint16_t y1h = f32_to_bf16(fmaf(x1h, ch, -x2h * sh));
-        const uint16_t y2l = f32_to_bf16(fmaf(x2l, cl, x1l * sl));
-        const uint16_t y2h = f32_to_bf16(fmaf(x2h, ch, x1h * sh));
-        ra[i] = (uint32_t)y1l | ((uint32_t)y1h << 16);
-        rb[i] = (uint32_t)y2l | ((uint32_t)y2h << 16);
-    }
-    ya = make_uint4(ra[0], ra[1], ra[2], ra[3]);
-    yb = make_uint4(rb[0], rb[1], rb[2], rb[3]);
-}
 
 __device__ __forceinline__ uint4 ld(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st(uint16_t *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
@@ -128,10 +108,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
                 const double expo = (double)(2 * j) / (double)rot;
                 const float inv = (float)(1.0 / pow(p.theta, expo));
                 const float ang = (float)pos * inv;  // one fp32 multiply
-                double sd, cd;
-                sincos((double)ang, &sd, &cd);
-                s_cos[j] = (float)cd;
-                s_sin[j] = (float)sd;
+                sincos_angle(ang, s_cos + j, s_sin + j);
             }
             __syncthreads();
         }

@@ -218,6 +218,43 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
                          const float *sinks, void *out, float *lse, void *stream);
 
 /*
+ * hda_decode_step_workspace_bytes -- device workspace hda_decode_step needs
+ * for this cache and layer type (0 for an invalid description).
+ */
+size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer);
+
+/*
+ * hda_decode_step -- one layer's whole decode step in a single launch: the
+ * work of hda_rope_append followed by hda_decode_attn with seq_lens[b] =
+ * pos[b] + 1, with two differences: q is only read (its rotation stays in
+ * registers), and keys are cut at the cache (full: min(pos+1, capacity),
+ * sliding: min(pos+1, window)) rather than at a max_seq_len.  After the
+ * call the cache holds what hda_rope_append leaves (new K/V in the ring
+ * slot or row pos; for a sliding layer at pos >= window-1 the slot's
+ * previous entry in row window-1), and out / lse what hda_decode_attn
+ * returns.  The sliding window counts the current token (Spark export
+ * page, ring branch: window-1 cached entries plus the new one); sinks as in
+ * hda_decode_attn (flashmla_sparse page, class docstring).
+ *
+ *   q, k_new, v_new, pos, layer, cache   as hda_rope_append
+ *   sinks, scale, out, lse               as hda_decode_attn
+ *   workspace  device buffer of at least hda_decode_step_workspace_bytes()
+ *              bytes.  Its first 4*batch*num_kv_heads bytes (rounded up to
+ *              256) are arrival counters that must be zero before the first
+ *              call; every call leaves them zero.  Zero-fill a new workspace
+ *              once.  hda_decode_attn lays its data out after the same
+ *              header, so one workspace serves both.  Calls sharing a
+ *              workspace must be ordered on one stream.
+ * Errors: as hda_decode_attn, plus UNSUPPORTED for rotary_dim other than
+ * 64 or 256 or batch above 4096.  batch == 0 is a no-op.
+ */
+hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
+                           const int32_t *pos, hda_layer_type layer,
+                           const hda_cache_desc *cache, const float *sinks, float scale,
+                           void *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
  * hda_sparse_workspace_bytes -- device workspace hda_sparse_decode_attn needs
  * for this many tokens, query heads and index-row length (0: none).
  * Returns 0 for an invalid shape as well; the call then reports why.

@@ -105,6 +105,26 @@ class HybridCase:
         return d, out, lse
 
 
+def fused_step(case: "HybridCase", sinks=None, scale=1 / 16, d=None, workspace=None):
+    """hda_decode_step on the case's device tensors (q is not modified)."""
+    import full_kv_cache_amd as hda
+    d = d or case.device()
+    cache = case.cache(d)
+    pos = torch.from_numpy(case.pos).cuda()
+    if workspace is None:
+        nbytes = hda.hda_decode_step_workspace_bytes(cache, case.lt)
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    s = case.shape
+    out = torch.full((s.batch, s.num_q_heads, s.head_dim), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((s.batch, s.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    sk = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).cuda()
+    hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], pos, case.lt, cache, sk, scale, out, lse,
+                        workspace)
+    torch.cuda.synchronize()
+    return d, out, lse
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().double().numpy()
 

@@ -127,8 +127,9 @@ def test_workspace_sizing_and_errors():
     L = hda.lib()
     full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
     need = L.hda_decode_workspace_bytes(ctypes.byref(full), hda.FULL, 4096, 256)
+    # a 256-byte header (one counter per sequence x KV head, rounded up), then
     # 2 sequences x 8 heads x 16 chunks of (256 floats out + 1 float lse)
-    assert need == (2 * 8 * 16 * 256 * 4) + 2 * 8 * 16 * 4
+    assert need == 256 + (2 * 8 * 16 * 256 * 4) + 2 * 8 * 16 * 4
     assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256) == 3
     assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256, ws=FAKE, wsb=need - 1) == 3
     assert "workspace" in _msg()
@@ -202,3 +203,37 @@ def test_sparse_sink_validation_in_binding():
         hda.hda_sparse_decode_attn(q, None, None, None, torch.zeros(16, dtype=torch.float64), 1.0, None)
     with pytest.raises(ValueError, match="shape"):
         hda.hda_sparse_decode_attn(q, None, None, None, torch.zeros(8), 1.0, None)
+
+
+# -------------------------------------------------------- fused step entry
+def _step(desc, layer=hda.SLIDING, q=FAKE, ws=None, wsb=0, scale=0.0625):
+    L = hda.lib()
+    return L.hda_decode_step(ctypes.c_void_p(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), layer, ctypes.byref(desc), None, scale,
+                             ctypes.c_void_p(FAKE), None, ctypes.c_void_p(ws) if ws else None, wsb,
+                             None)
+
+
+def test_step_shape_checks():
+    assert _step(_desc(num_q_heads=6, num_kv_heads=4)) == 1
+    assert _step(_desc(), layer=7) == 1
+    assert _step(_desc(capacity=1024)) == 1 and "must equal window" in _msg()
+    assert _step(_desc(rotary_dim=128)) == 2 and "rotary_dim" in _msg()
+    assert _step(_desc(head_dim=128, rotary_dim=64)) == 2
+    assert _step(_desc(batch=5000)) == 2
+    assert _step(_desc(), q=0) == 1
+    assert _step(_desc(), q=FAKE + 8) == 1 and "aligned" in _msg()
+
+
+def test_step_workspace():
+    """Counter header first (shared with hda_decode_attn's layouts), then
+    one partial slot per wave and per (sequence, KV head)."""
+    L = hda.lib()
+    d = _desc()
+    need = L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.SLIDING)
+    assert need > 256 and need % 256 == 0
+    assert _step(d) == 3 and "workspace" in _msg()
+    assert _step(d, ws=FAKE, wsb=need - 1) == 3
+    assert _step(d, ws=FAKE + 4, wsb=need) == 1
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(rotary_dim=128)), hda.SLIDING) == 0
+    assert _step(_desc(batch=0), ws=FAKE, wsb=need) == 0  # nothing to do

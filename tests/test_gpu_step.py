@@ -1,0 +1,197 @@
+"""GPU parity of the fused one-launch decode step (hda_decode_step: RoPE,
+append, attention, merge, sink) against the fp64 oracle's append followed
+by its attention.
+
+Cache after the call: bit-exact for V and every untouched row, rotated K
+within one bf16 ulp (< 0.1% of values off); out max-abs <= 1e-2, mean-abs
+<= 1e-3; lse within 1e-4.  Rows the step must not read are NaN-poisoned,
+including the stale evicted-entry row of a full sliding window.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_case import (BF16_NAN, FULL, SLIDING, HybridCase, assert_attn_close, bf16_ulp_diff,
+                         bits_of, fused_step, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(**kw):
+    print("CASE", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def _check_cache(d, h):
+    assert np.array_equal(bits_of(d["v"]), h["v"])
+    ulps = bf16_ulp_diff(bits_of(d["k"]), h["k"])
+    assert ulps.max() <= 1, ulps.max()
+    assert (ulps > 0).mean() < 1e-3
+
+
+def _poison_stale_evicted_row(case):
+    """Row window-1 of a sliding block holds the entry evicted one step
+    earlier, outside this step's window: the step must not use it."""
+    if case.lt != SLIDING:
+        return
+    W = case.shape.window
+    for b, p in enumerate(case.pos):
+        if p >= W:
+            case.host["k"][b, :, W - 1] = BF16_NAN
+            case.host["v"][b, :, W - 1] = BF16_NAN
+
+
+@pytest.mark.parametrize("pos", [0, 1, 15, 16, 17, 509, 510, 511, 512, 1000, 1021, 4095])
+def test_step_sliding_positions(pos):
+    _print_case(test="step_sliding", pos=pos)
+    case = HybridCase(900 + pos, 3, SLIDING, [pos, max(0, pos - 3), pos + 511], poison=True)
+    _poison_stale_evicted_row(case)
+    h, ref, rlse = case.oracle_step()
+    d, out, lse = fused_step(case)
+    _check_cache(d, h)
+    assert np.array_equal(bits_of(d["q"]), case.host["q"])  # q is only read
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+def test_step_full_ragged():
+    pos = [0, 15, 16, 999, 2047, 3000]
+    _print_case(test="step_full", pos=pos)
+    case = HybridCase(950, len(pos), FULL, pos, lmax=3072, poison=True)
+    h, ref, rlse = case.oracle_step()
+    d, out, lse = fused_step(case)
+    _check_cache(d, h)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("lt", [SLIDING, FULL])
+def test_step_sinks(lt):
+    _print_case(test="step_sinks", lt=lt)
+    case = HybridCase(960 + lt, 2, lt, [700, 1200], lmax=2048)
+    _, ref0, lse0 = case.oracle_step()
+    g = np.random.default_rng(2)
+    sinks = (lse0.mean(0) + g.normal(0, 2, 8)).astype(np.float32)
+    _, ref, _ = case.oracle_step(sinks=sinks)
+    _, out, _ = fused_step(case, sinks=sinks)
+    assert_attn_close(out, ref)
+    _, o_none, _ = fused_step(case)
+    _, o_ninf, _ = fused_step(case, sinks=np.full(8, -np.inf, np.float32))
+    assert torch.equal(o_none.view(torch.int16), o_ninf.view(torch.int16))
+    assert_attn_close(o_none, ref0)
+    _, o_pinf, _ = fused_step(case, sinks=np.full(8, np.inf, np.float32))
+    assert torch.all(o_pinf.float() == 0)
+
+
+def test_step_outside_cache():
+    """Positions outside a full layer's cache: a negative one attends to
+    nothing and writes nothing; one past the capacity attends to the cached
+    rows only (q still rotated by its position) and appends nothing.  The
+    oracle covers the in-cache sequence and the attention of the other."""
+    _print_case(test="step_outside")
+    import oracle
+    case = HybridCase(970, 3, FULL, [10, 63, 63], lmax=64)
+    case.pos = np.array([-1, 63, 80], np.int32)
+    d, out, lse = fused_step(case)
+    k_gpu, v_gpu = bits_of(d["k"]), bits_of(d["v"])
+    for b in (0, 2):  # nothing appended
+        assert np.array_equal(k_gpu[b], case.host["k"][b])
+        assert np.array_equal(v_gpu[b], case.host["v"][b])
+    assert torch.all(out[0].float() == 0) and torch.all(torch.isneginf(lse[0]))
+    # sequence 1: an ordinary step at the last row
+    sub = HybridCase(970, 3, FULL, [10, 63, 63], lmax=64)
+    for key in sub.host:
+        sub.host[key] = sub.host[key][1:2].copy()
+    sub.pos, sub.seq_lens = np.array([63], np.int32), np.array([64], np.int32)
+    sub.shape = sub.shape.__class__(batch=1, lmax=64)
+    h, ref, rlse = sub.oracle_step()
+    assert np.array_equal(v_gpu[1:2], h["v"]) and bf16_ulp_diff(k_gpu[1:2], h["k"]).max() <= 1
+    assert_attn_close(out[1:2], ref)
+    np.testing.assert_allclose(to_f64(lse)[1:2], rlse, rtol=0, atol=1e-4)
+    # sequence 2: q rotated at 80, keys = the 64 cached rows
+    s = case.shape
+    q2 = oracle.rope_apply(case.host["q"][2:3], s.rot_full, s.theta_full, 80)
+    z = np.zeros((1, 2, 256), np.uint16)
+    ref2, rlse2 = oracle.decode_attn(q2, case.host["k"][2:3], case.host["v"][2:3], z, z.copy(),
+                                     np.array([64], np.int32), FULL, s.window, None, 1 / 16)
+    assert_attn_close(out[2:3], ref2)
+    np.testing.assert_allclose(to_f64(lse)[2:3], rlse2, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("lt", [SLIDING, FULL])
+def test_step_twice_same_workspace(lt):
+    """Two consecutive steps on one workspace: the arrival counters come
+    back to zero, and the second step sees the first one's append."""
+    _print_case(test="step_twice", lt=lt)
+    import full_kv_cache_amd as hda
+    pos0 = np.array([520, 1500, 2047], np.int32)
+    case = HybridCase(980 + lt, 3, lt, pos0, lmax=2049)
+    d = case.device()
+    ws = torch.zeros(hda.hda_decode_step_workspace_bytes(case.cache(d), lt), dtype=torch.uint8,
+                     device="cuda")
+    d, _, _ = fused_step(case, d=d, workspace=ws)
+    h1, _, _ = case.oracle_step()
+    case2 = HybridCase(981 + lt, 3, lt, pos0 + 1, lmax=2049)  # fresh q / k_new / v_new
+    for key in ("k", "v"):
+        case2.host[key] = h1[key]
+    d2 = case2.device()
+    d2["k"], d2["v"] = d["k"], d["v"]
+    d2, out, lse = fused_step(case2, d=d2, workspace=ws)
+    h2, ref, rlse = case2.oracle_step()
+    _check_cache(d2, h2)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+    assert torch.count_nonzero(ws[: 4 * 3 * 2]).item() == 0
+
+
+def test_step_graph_replay():
+    """A captured full-layer step replays to the eager result (the full
+    layer's append is idempotent for a fixed position)."""
+    _print_case(test="step_graph")
+    import full_kv_cache_amd as hda
+    case = HybridCase(990, 4, FULL, [100, 700, 1300, 2000], lmax=2048)
+    d = case.device()
+    cache = case.cache(d)
+    pos = torch.from_numpy(case.pos).cuda()
+    ws = torch.zeros(hda.hda_decode_step_workspace_bytes(cache, FULL), dtype=torch.uint8, device="cuda")
+    out = torch.empty(4, 8, 256, dtype=torch.bfloat16, device="cuda")
+    sk = torch.randn(8, generator=torch.Generator().manual_seed(0)).cuda()
+
+    def step():
+        hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], pos, FULL, cache, sk, 1 / 16, out, None, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+def test_step_batch64_sampled():
+    """Headline shape: batch 64, lengths uniform in [512, 4096], in the
+    launch configuration the bench times; the oracle checks 8 sequences."""
+    _print_case(test="step_batch64")
+    g = np.random.default_rng(64)
+    pos = g.integers(511, 4096, 64).astype(np.int32)
+    sample = np.array([0, 1, 7, 20, 33, 47, 62, 63])
+    for lt in (SLIDING, FULL):
+        case = HybridCase(1000 + lt, 64, lt, pos, lmax=4096)
+        d, out, lse = fused_step(case)
+        sub = HybridCase(1000 + lt, 64, lt, pos, lmax=4096)
+        for k in sub.host:
+            sub.host[k] = sub.host[k][sample].copy()
+        sub.pos = pos[sample]
+        sub.seq_lens = sub.pos + 1
+        sub.shape = sub.shape.__class__(batch=len(sample), lmax=4096)
+        h, ref, rlse = sub.oracle_step()
+        assert_attn_close(out[torch.from_numpy(sample).cuda()], ref)
+        np.testing.assert_allclose(to_f64(lse)[sample], rlse, rtol=0, atol=1e-4)
+        kk = bits_of(d["k"])[sample]
+        assert bf16_ulp_diff(kk, h["k"]).max() <= 1
+        assert np.array_equal(bits_of(d["v"])[sample], h["v"])
