@@ -9,7 +9,11 @@ layer i is full when i % 4 == 3)
     hda_rope_append  -- rotate q in place, write the rotated new K and V
                         into the ring slot (sliding) or row pos (full);
     hda_decode_attn  -- GQA attention over the layer's keys with a per-head
-                        sink; full layers run split-K plus the LSE merge.
+                        sink: balanced streaming kernel plus the LSE merge
+    (--path fused: hda_decode_step, the same step in one launch).
+
+Each timed step re-appends at the same positions; the rows read and the
+work done are those of one decode step either way.
 
 Every layer has its own cache, so a step streams the whole resident KV
 (about 5.2 GB at the default shape), far more than the 256 MB last-level
@@ -22,6 +26,7 @@ roofline entry for the dominant kernel and the CPU oracle's rate on a
 bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
+                    [--path fused|separate]
 """
 from __future__ import annotations
 
@@ -65,7 +70,10 @@ def parse():
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse top-k measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time for the CPU baseline sample")
-    ap.add_argument("--chunk-keys", type=int, default=0, help="split size for full layers (0: default)")
+    ap.add_argument("--chunk-keys", type=int, default=0,
+                    help="split size for full layers on the separate path (0: default)")
+    ap.add_argument("--path", default="separate", choices=["fused", "separate"],
+                    help="one launch per layer (hda_decode_step) or rope_append + decode_attn")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of this many MB (PMC byte calibration)")
     return ap.parse_args()
@@ -103,21 +111,28 @@ class Workload:
                 out=torch.empty(B, s.num_q_heads, s.head_dim, dtype=torch.bfloat16, device=dev),
                 lse=torch.empty(B, s.num_q_heads, dtype=torch.float32, device=dev)))
         self.scale = 1.0 / s.head_dim ** 0.5
-        ws = max(hda.hda_decode_workspace_bytes(L["cache"], L["lt"], self.max_seq_len, 0)
-                 for L in self.layers)
-        self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        ws = max(max(hda.hda_decode_workspace_bytes(L["cache"], L["lt"], self.max_seq_len, 0),
+                     hda.hda_decode_step_workspace_bytes(L["cache"], L["lt"])) for L in self.layers)
+        self.workspace = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)  # counters start at 0
         sl = self.seq_lens.cpu().long()
         self.kv_row_bytes = 2 * s.num_kv_heads * s.head_dim * 2  # K and V, all KV heads, bf16
         self.rows = {lt: int((sl.clamp(max=s.window) if lt == workloads.SLIDING else sl).sum())
                      for lt in (workloads.SLIDING, workloads.FULL)}
         self.kv_bytes = sum(self.rows[lt] for lt in self.types) * self.kv_row_bytes
 
-    def step(self, chunk_keys=0):
+    def layer_call(self, L, path="separate", chunk_keys=0):
         import full_kv_cache_amd as hda
-        for L in self.layers:
+        if path == "fused":
+            hda.hda_decode_step(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"],
+                                L["sinks"], self.scale, L["out"], L["lse"], self.workspace)
+        else:
             hda.hda_rope_append(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"])
             hda.hda_decode_attn(L["q"], L["cache"], self.seq_lens, L["lt"], L["sinks"], self.scale,
                                 L["out"], L["lse"], self.max_seq_len, chunk_keys, self.workspace)
+
+    def step(self, path="separate", chunk_keys=0):
+        for L in self.layers:
+            self.layer_call(L, path, chunk_keys)
 
 
 def time_graph(fn, steps, warmup, use_graph=True):
@@ -147,13 +162,19 @@ def time_graph(fn, steps, warmup, use_graph=True):
     return t0.elapsed_time(t1) / steps, wall * 1e3 / steps
 
 
-def dominant_kernel(wl: Workload, steps, warmup, chunk_keys=0):
-    """Time the full-layer decode attention alone -- the largest byte mover
-    of the step: the 7 full layers' hda_decode_attn calls (exactly as the
-    step makes them) captured in one graph, HIP events on the launch stream
-    around the replays, average per call.  One call is the streaming kernel
-    plus its LSE merge; the rocprof summary gives the split."""
-    import full_kv_cache_amd as hda
+KERNEL_NAMES = {
+    "fused": "decode_step_kernel<4, 64> (hda_decode_step, full layer: one launch)",
+    "separate": "full-layer hda_decode_attn: decode_stream_kernel<4> + stream_merge_kernel",
+}
+
+
+def dominant_kernel(wl: Workload, steps, warmup, path="separate", chunk_keys=0):
+    """Time the full-layer call alone -- the largest byte mover of the step:
+    the 7 full layers' calls (exactly as the step makes them) captured in one
+    graph, HIP events on the launch stream around the replays, average per
+    call.  On the fused path a call is one kernel launch.  Algorithmic bytes
+    per call: every attended K and V row once (sum over sequences of pos + 1
+    rows of 2 KV heads x 256 dims x 2 bytes, for K and for V)."""
     import workloads
     full = [L for L in wl.layers if L["lt"] == workloads.FULL]
     if not full:
@@ -161,21 +182,45 @@ def dominant_kernel(wl: Workload, steps, warmup, chunk_keys=0):
 
     def fn():
         for L in full:
-            hda.hda_decode_attn(L["q"], L["cache"], wl.seq_lens, workloads.FULL, L["sinks"],
-                                wl.scale, L["out"], L["lse"], wl.max_seq_len, chunk_keys,
-                                wl.workspace)
+            wl.layer_call(L, path, chunk_keys)
 
     ms, _ = time_graph(fn, steps, warmup)
     per_call_s = ms / len(full) / 1e3
     algo = wl.rows[workloads.FULL] * wl.kv_row_bytes
     achieved = algo / per_call_s / 1e9
     return {
-        "kernel": "full-layer hda_decode_attn: decode_stream_kernel<4> + stream_merge_kernel",
+        "kernel": KERNEL_NAMES[path],
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(path, algo),
         "algorithmic_bytes_per_launch": algo, "avg_launch_us": round(per_call_s * 1e6, 2),
         "launches_timed": steps * len(full),
     }
+
+
+def measured_traffic(path, algo):
+    """HBM bytes per launch of the timed kernel from the committed PMC
+    summary (FETCH_SIZE x the copy-calibrated factor + WRITE_SIZE), or None
+    when the summary is missing or was taken on other kernel sources."""
+    import hashlib
+    if path != "fused":
+        return None
+    f = os.path.join(ROOT, "profiles", "traffic_decode_step_full_b64_u512-4096.txt")
+    if not os.path.exists(f):
+        return None
+    vals = {}
+    for line in open(f):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in ("decode_step.hip", "decode_wave.h", "hda_device.h", "hda_kernels.h"):
+        h.update(open(os.path.join(ROOT, "full_kv_cache_amd", "csrc", src), "rb").read())
+    if vals.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def sparse_kernel(steps, warmup, seed, pools=8):
@@ -298,7 +343,7 @@ def main():
     print(f"# building workload {args.config}: {cfg['desc']}", file=sys.stderr, flush=True)
     wl = Workload(cfg, args.seed)
     torch.cuda.synchronize()
-    step = lambda: wl.step(args.chunk_keys)
+    step = lambda: wl.step(args.path, args.chunk_keys)
     for _ in range(2):
         step()
     torch.cuda.synchronize()
@@ -309,7 +354,7 @@ def main():
     if not args.no_graph:
         eager_ms, _ = time_graph(step, max(3, args.steps // 5), 2, use_graph=False)
     print("# timing dominant kernel", file=sys.stderr, flush=True)
-    roof = dominant_kernel(wl, args.steps, args.warmup, args.chunk_keys)
+    roof = dominant_kernel(wl, args.steps, args.warmup, args.path, args.chunk_keys)
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
@@ -329,7 +374,7 @@ def main():
         "config": {"workload": f"{args.config}: {cfg['desc']}", "batch": cfg["batch"],
                    "layers": cfg["layers"], "seq_len_min": int(sl.min()),
                    "seq_len_max": int(sl.max()), "seq_len_mean": round(float(sl.float().mean()), 1),
-                   "graph": not args.no_graph, "chunk_keys": args.chunk_keys},
+                   "graph": not args.no_graph, "path": args.path, "chunk_keys": args.chunk_keys},
         "tokens_per_s": round(cfg["batch"] / (ms / 1e3), 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": wl.kv_bytes,

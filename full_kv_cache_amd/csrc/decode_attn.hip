@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
     constexpr int WAVES = kDecodeThreads / 64;
     __shared__ __align__(16) float s_red[WAVES * G * D];
     __shared__ __align__(16) float s_pw[WAVES][16 * G];
+    __shared__ __align__(16) uint16_t s_kt[WAVES][kKTile];
     __shared__ float s_m[WAVES][G], s_l[WAVES][G];
 
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
         const int r0e = (int)(r0 < cap16 ? r0 : cap16);
         uint4 kt[8], vt[8];
         issue_round(kblk, vblk, r0e, lane, kt, vt);
-        st.round(qa, kt, vt, r0 - r0e, c0 + kw1 - r0e, p.scale_log2, s_pw[wave], lane);
+        st.round(qa, kt, vt, r0 - r0e, c0 + kw1 - r0e, p.scale_log2, s_pw[wave], s_kt[wave], lane);
     }
 
     // merge the waves: each leaves its unnormalised o and its (m, l)
@@ -210,8 +211,9 @@ struct RoundGeo {
 template <int G>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     constexpr int D = kHeadDim;
-    __shared__ int s_pre[kStreamMaxBatch + 1];     // rounds before sequence b, one KV head
+    extern __shared__ int s_pre[];                 // [B + 1] rounds before sequence b, one KV head
     __shared__ __align__(16) float s_pw[16 * G];   // this round's probabilities [key][head]
+    __shared__ __align__(16) uint16_t s_kt[kKTile];
 
     const int lane = threadIdx.x;
     const int w = blockIdx.x, W = gridDim.x;
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         RoundAddr nxt = more ? advance(cur) : cur;
         RoundGeo gn = geo(nxt);
         issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kB, vB);
-        st.round(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, lane);
+        st.round(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         nxt = more ? advance(cur) : cur;
         gn = geo(nxt);
         issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kA, vA);
-        st.round(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, lane);
+        st.round(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
@@ -293,42 +295,177 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     }
 }
 
-// Merge of the streaming partials: one workgroup per (query head,
-// sequence).  The pair's rounds [g_lo, g_hi] were covered by waves
-// wave_of(g_lo) .. wave_of(g_hi), wave_of(g) = the largest w with
-// w*R_tot/W <= g, whose partials sit in slots w + pair.
-__global__ __launch_bounds__(kDecodeThreads) void stream_merge_kernel(DecodeParams p, int W) {
+// Merge of the streaming partials: one wave per (sequence, query head),
+// lane = 4 output dims.  The pair's rounds [g_lo, g_hi] were covered by
+// waves wave_of(g_lo) .. wave_of(g_hi), whose partials sit in slots
+// w + pair.  Lane s reads segment s's lse (64 segments a pass), the wave
+// reduces max and sum, then the partials are read as float4 per lane in
+// unrolled batches so that their loads are in flight together.
+__global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W) {
     constexpr int D = kHeadDim;
-    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    constexpr int kBatch = 16;
+    const int hq = blockIdx.x % p.num_q_heads, b = blockIdx.x / p.num_q_heads;
+    const int lane = threadIdx.x;
     const int Hq = p.num_q_heads, Hkv = p.num_kv_heads, G = Hq / Hkv;
     const int kvh = hq / G, h = hq % G;
     const int rb = p.stream_pre[b + 1] - p.stream_pre[b];
-    uint16_t *outp = p.out + ((int64_t)b * Hq + hq) * D + d;
+    const int64_t row = (int64_t)b * Hq + hq;
+    uint16_t *outp = p.out + row * D + 4 * lane;
     if (rb == 0) {
-        *outp = 0;
-        if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = -INFINITY;
+        *reinterpret_cast<uint2 *>(outp) = make_uint2(0, 0);
+        if (lane == 0 && p.lse) p.lse[row] = -INFINITY;
         return;
     }
     const int64_t r_tot = (int64_t)Hkv * p.stream_pre[p.batch];
     const int64_t g_lo = (int64_t)Hkv * p.stream_pre[b] + (int64_t)kvh * rb;
-    const int64_t g_hi = g_lo + rb - 1;
     const int w_lo = wave_of_round(g_lo, r_tot, W);
-    const int w_hi = wave_of_round(g_hi, r_tot, W);
-    const int64_t pair = (int64_t)b * Hkv + kvh;
+    const int nseg = wave_of_round(g_lo + rb - 1, r_tot, W) - w_lo + 1;
+    const int64_t s0 = w_lo + (int64_t)b * Hkv + kvh;  // first slot
     float M = -INFINITY;
-    for (int w = w_lo; w <= w_hi; ++w) M = fmaxf(M, p.part_lse[(w + pair) * G + h]);
-    float L = 0.f, o = 0.f;
-    for (int w = w_lo; w <= w_hi; ++w) {
-        const int64_t slot = w + pair;
-        const float e = expf(p.part_lse[slot * G + h] - M);
-        L += e;
-        o = fmaf(e, p.part_o[(slot * G + h) * D + d], o);
+    for (int c = 0; c < nseg; c += 64)
+        if (c + lane < nseg) M = fmaxf(M, p.part_lse[(s0 + c + lane) * G + h]);
+    M = wave_max(M);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int base = 0; base < nseg; base += kBatch) {
+        float4 v[kBatch];
+        float wgt[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int s = min(base + k, nseg - 1);
+            v[k] = *reinterpret_cast<const float4 *>(p.part_o + ((s0 + s) * G + h) * D + 4 * lane);
+            wgt[k] = base + k < nseg ? p.part_lse[(s0 + s) * G + h] : -INFINITY;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const float e = expf(wgt[k] - M);  // padding: exp(-inf) = 0
+            L += e;
+            o.x = fmaf(e, v[k].x, o.x);
+            o.y = fmaf(e, v[k].y, o.y);
+            o.z = fmaf(e, v[k].z, o.z);
+            o.w = fmaf(e, v[k].w, o.w);
+        }
     }
     const float lse = M + logf(L);
-    float f = 1.f;
-    if (p.sinks) f = 1.f / (1.f + expf(p.sinks[hq] - lse));
-    *outp = f32_to_bf16((o / L) * f);
-    if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
+    float f = 1.f / L;
+    if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+    const uint32_t lo = (uint32_t)f32_to_bf16(o.x * f) | ((uint32_t)f32_to_bf16(o.y * f) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(o.z * f) | ((uint32_t)f32_to_bf16(o.w * f) << 16);
+    *reinterpret_cast<uint2 *>(outp) = make_uint2(lo, hi);
+    if (lane == 0 && p.lse) p.lse[row] = lse;
+}
+
+// ===================================================================
+// Window decomposition (sliding layers, every pair the same few hundred
+// keys): one workgroup of kPairWaves waves per (sequence, KV head, 1/S of
+// the query group).  The waves split the pair's rounds evenly, keep two
+// rounds in flight each, merge in LDS and write out / lse with the sink: no
+// partials, no merge kernel.  The S workgroups of a pair read the same K/V
+// rows; their block ids are congruent mod 8 so that they run on the same XCD
+// and the later reads hit its L2.
+// ===================================================================
+template <int GW>
+__global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodeParams p, int S) {
+    constexpr int D = kHeadDim;
+    constexpr int WAVES = kPairWaves;
+    __shared__ __align__(16) float s_red[WAVES * GW * D];
+    __shared__ __align__(16) float s_pw[WAVES][16 * GW];
+    __shared__ __align__(16) uint16_t s_kt[WAVES][kKTile];
+    __shared__ float s_m[WAVES][GW], s_l[WAVES][GW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pairs = p.batch * p.num_kv_heads;
+    const int x = blockIdx.x;
+    const int part = (x >> 3) % S;
+    const int pr = ((x >> 3) / S) * 8 + (x & 7);
+    if (pr >= pairs) return;
+    const int b = pr / p.num_kv_heads, kvh = pr % p.num_kv_heads;
+    const int hsub = kvh * S + part;  // heads hsub*GW .. +GW-1
+    const int n = num_keys(p, b);
+    const int R = (n + 15) >> 4;
+    const int r_lo = wave * R / WAVES, r_hi = (wave + 1) * R / WAVES;
+    const int64_t cap = p.capacity, cap16 = cap - 16;
+    const int64_t bh = (int64_t)b * p.num_kv_heads + kvh;
+    const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
+    auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap16 ? 16 * r : cap16); };
+
+    WaveSoftmax<GW> st;
+    st.reset();
+    if (r_lo < r_hi) {
+        bf16x8 qa[8];
+        uint4 kA[8], vA[8], kB[8], vB[8];
+        int r = r_lo;
+        issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
+        load_q_operand<GW>(p.q, p.num_q_heads, b, hsub, lane, qa);
+        while (true) {
+            bool more = r + 1 < r_hi;
+            issue_round(kblk, vblk, r0e_of(more ? r + 1 : r), more ? lane : 0, kB, vB);
+            int e = r0e_of(r);
+            st.round(qa, kA, vA, 16 * r - e, n - e, p.scale_log2, s_pw[wave], s_kt[wave], lane);
+            if (!more) break;
+            ++r;
+            more = r + 1 < r_hi;
+            issue_round(kblk, vblk, r0e_of(more ? r + 1 : r), more ? lane : 0, kA, vA);
+            e = r0e_of(r);
+            st.round(qa, kB, vB, 16 * r - e, n - e, p.scale_log2, s_pw[wave], s_kt[wave], lane);
+            if (!more) break;
+            ++r;
+        }
+    }
+
+    // merge the waves: each leaves its unnormalised o and its (m, l)
+    float l_h[4];
+    st.sums(l_h);
+    const int hw = lane >> 5, dl = lane & 31;
+#pragma unroll
+    for (int h = 0; h < GW; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
+            if (hw == 0) s_red[(wave * GW + h) * D + 8 * dl + e] = o;
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GW; ++h) {
+            s_m[wave][h] = r_lo < r_hi ? st.max_of(h) : -INFINITY;
+            s_l[wave][h] = r_lo < r_hi ? lane_value(l_h[h & 3], 16 * (h >> 2)) : 0.f;
+        }
+    }
+    __syncthreads();
+    const int Hq = p.num_q_heads;
+    for (int i = tid; i < GW * D; i += WAVES * 64) {
+        const int h = i / D, d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+        const int hq = hsub * GW + h;
+        uint16_t *outp = p.out + ((int64_t)b * Hq + hq) * D + d;
+        if (M == -INFINITY) {  // no keys
+            *outp = 0;
+            if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = -INFINITY;
+            continue;
+        }
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float sc = exp2f(s_m[w][h] - M);  // wave without keys: 2^-inf = 0
+            L = fmaf(sc, s_l[w][h], L);
+            o = fmaf(sc, s_red[(w * GW + h) * D + d], o);
+        }
+        const float lse = (M + log2f(L)) * kLn2;
+        float f = 1.f / L;
+        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        *outp = f32_to_bf16(o * f);
+        if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
+    }
+}
+
+template <int GW>
+hipError_t launch_pair_g(const DecodeParams &p, int S, hipStream_t s) {
+    const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
+    const int64_t blocks = (pairs + 7) / 8 * 8 * S;
+    hipLaunchKernelGGL((decode_pair_kernel<GW>), dim3((unsigned)blocks), dim3(kPairWaves * 64), 0, s, p, S);
+    return hipGetLastError();
 }
 
 template <int G, bool FINAL>
@@ -352,11 +489,11 @@ hipError_t launch_chunks(const DecodeParams &p, int group, hipStream_t s) {
 
 template <int G>
 hipError_t launch_stream_g(const DecodeParams &p, int waves, hipStream_t s) {
-    hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(waves), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(waves), dim3(64), (p.batch + 1) * sizeof(int), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(stream_merge_kernel, dim3(p.num_q_heads, p.batch), dim3(kDecodeThreads), 0, s,
-                       p, waves);
+    hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)), dim3(64),
+                       0, s, p, waves);
     return hipGetLastError();
 }
 
@@ -405,6 +542,19 @@ hipError_t launch_decode_stream(const DecodeParams &p, int group, int waves, hip
         case 4: return launch_stream_g<4>(p, waves, stream);
         case 8: return launch_stream_g<8>(p, waves, stream);
         case 16: return launch_stream_g<16>(p, waves, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Query heads per workgroup: half the group when it has two or more heads.
+hipError_t launch_decode_pairs(const DecodeParams &p, int group, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    switch (group) {
+        case 1: return launch_pair_g<1>(p, 1, stream);
+        case 2: return launch_pair_g<1>(p, 2, stream);
+        case 4: return launch_pair_g<2>(p, 2, stream);
+        case 8: return launch_pair_g<4>(p, 2, stream);
+        case 16: return launch_pair_g<8>(p, 2, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -27,10 +27,11 @@
 // The work is split like the balanced streaming decode: all 16-key rounds
 // of all (sequence, KV head) pairs evenly over resident single-wave
 // workgroups.  A pair inside one wave is finished there.  A pair spread over
-// several waves leaves one partial per wave; the last of them to finish
-// (device-scope counter per pair between release and acquire fences) merges
-// them once its own rounds are done, writes out and lse with the sink, and
-// resets the counter to zero for the next launch.
+// several waves leaves one partial per wave, written and read past the
+// XCD-private caches; the last of them to finish (device-scope counter per
+// pair, counted once the partial's stores are complete) merges them once its
+// own rounds are done, writes out and lse with the sink, and resets the
+// counter to zero for the next launch.
 #include "decode_wave.h"
 
 namespace hda {
@@ -59,6 +60,37 @@ struct PairRows {
     int srow;  // sliding past the window: slot taking the new token; else -1
     int erow;  // evicted-entry row, window-1
 };
+
+// Partials cross XCDs, whose L2 caches are not coherent with each other.
+// Agent-scope relaxed atomic accesses are issued with the system-coherence
+// bit, so they go past those caches; with them no L2 write-back or
+// invalidation (what a device-wide fence costs) is needed around the count.
+__device__ __forceinline__ void coherent_store(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// store_partial of decode_wave.h with coherent stores.
+template <int G>
+__device__ __forceinline__ void store_partial_coherent(const WaveSoftmax<G> &st, float *po, float *plse,
+                                                       int lane) {
+    const int hw = lane >> 5, dl = lane & 31;
+    float l_h[4];
+    st.sums(l_h);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = (st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64)) * inv;
+            if (hw == 0) coherent_store(po + h * kHeadDim + 8 * dl + e, o);
+        }
+        if (lane == 0) coherent_store(plse + h, (st.max_of(h) + log2f(l)) * kLn2);
+    }
+}
 
 // Writes out (bf16, with the sink) and lse of a pair finished in one wave.
 template <int G>
@@ -113,9 +145,11 @@ __device__ __forceinline__ void merge_pair(const StepParams &p, int64_t s0, int 
             const int64_t slot = s0 + (in ? base + k : nseg - 1);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float x = p.part_lse[slot * G + h];
+                const float x = coherent_load(p.part_lse + slot * G + h);
                 ls[k][h] = in ? x : -INFINITY;
-                ov[k][h] = *reinterpret_cast<const float4 *>(p.part_o + (slot * G + h) * D + 4 * lane);
+                const float *src = p.part_o + (slot * G + h) * D + 4 * lane;
+                ov[k][h] = make_float4(coherent_load(src), coherent_load(src + 1), coherent_load(src + 2),
+                                       coherent_load(src + 3));
             }
         }
 #pragma unroll
@@ -156,8 +190,9 @@ template <int G, int ROT>
 __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     constexpr int D = kHeadDim;
     static_assert(ROT % 16 == 0 && ROT <= D, "rotary dims in 16-byte chunk pairs");
-    __shared__ int s_pre[kStreamMaxBatch + 1];
+    extern __shared__ int s_pre[];  // [B + 1]
     __shared__ __align__(16) float s_pw[16 * G];
+    __shared__ __align__(16) uint16_t s_kt[kKTile];
     __shared__ __align__(16) float s_cos[ROT / 2], s_sin[ROT / 2];
     // rotated q of the pair's G heads, then its rotated new K, then new V
     __shared__ __align__(16) uint16_t s_rows[(G + 2) * D];
@@ -209,34 +244,41 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         pr.vrow = p.sliding ? min(P, p.window - 1) : P;
         pr.srow = (p.sliding && P >= p.window - 1) ? P % (p.window - 1) : -1;
         const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
+        // raw rows, one batch of 16-byte loads: rows r < G query heads,
+        // r = G new K, r = G + 1 new V
+        constexpr int kChunks = (G + 2) * D / 8, kPerLane = (kChunks + 63) / 64;
+        const uint16_t *qrow = p.q + ((int64_t)a.b * p.num_q_heads + a.kvh * G) * D;
+        uint4 raw[kPerLane];
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int t = min(lane + 64 * i, kChunks - 1), r = t / (D / 8), d = 8 * (t % (D / 8));
+            const uint16_t *src = r < G ? qrow + r * D : (r == G ? p.k_new : p.v_new) + bh * D;
+            raw[i] = ld16(src + d);
+        }
         wave_lds_fence();  // the previous pair's LDS reads are done
         for (int i = lane; i < ROT / 2; i += 64) {
             const float ang = (float)P * p.inv_freq[i];  // one fp32 multiply
             sincos_angle(ang, s_cos + i, s_sin + i);
         }
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int t = lane + 64 * i;
+            if (t < kChunks) *reinterpret_cast<uint4 *>(s_rows + 8 * t) = raw[i];
+        }
         wave_lds_fence();
-        // rows r < G: query heads; r = G: new K; r = G + 1: new V (copied)
-        constexpr int kRotTasks = ROT / 16, kRowTasks = kRotTasks + (D - ROT) / 8;
-        const uint16_t *qrow = p.q + ((int64_t)a.b * p.num_q_heads + a.kvh * G) * D;
-#pragma unroll 1
-        for (int t = lane; t < (G + 1) * kRowTasks + D / 8; t += 64) {
-            const int r = t / kRowTasks, c = t % kRowTasks;
-            if (r > G) {  // new V
-                const int d = 8 * (t - (G + 1) * kRowTasks);
-                *reinterpret_cast<uint4 *>(s_vnew + d) = ld16(p.v_new + bh * D + d);
-                continue;
-            }
-            const uint16_t *src = r < G ? qrow + r * D : p.k_new + bh * D;
-            uint16_t *dst = s_rows + r * D;
-            if (c < kRotTasks) {
-                const int i = 8 * c;
-                uint4 x1 = ld16(src + i), x2 = ld16(src + ROT / 2 + i);
-                rotate8(x1, x2, s_cos + i, s_sin + i, x1, x2);
-                *reinterpret_cast<uint4 *>(dst + i) = x1;
-                *reinterpret_cast<uint4 *>(dst + ROT / 2 + i) = x2;
-            } else {
-                const int d = ROT + 8 * (c - kRotTasks);
-                *reinterpret_cast<uint4 *>(dst + d) = ld16(src + d);
+        // neox rotation in place: rows 0..G, 16-byte chunk pairs (i, i + ROT/2)
+        constexpr int kRot = (G + 1) * (ROT / 16);
+#pragma unroll
+        for (int i = 0; i < (kRot + 63) / 64; ++i) {
+            const int t = lane + 64 * i;
+            if (t < kRot) {
+                const int r = t / (ROT / 16), c = 8 * (t % (ROT / 16));
+                uint16_t *row = s_rows + r * D;
+                uint4 x1 = *reinterpret_cast<const uint4 *>(row + c);
+                uint4 x2 = *reinterpret_cast<const uint4 *>(row + ROT / 2 + c);
+                rotate8(x1, x2, s_cos + c, s_sin + c, x1, x2);
+                *reinterpret_cast<uint4 *>(row + c) = x1;
+                *reinterpret_cast<uint4 *>(row + ROT / 2 + c) = x2;
             }
         }
         wave_lds_fence();
@@ -276,13 +318,12 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         if (!has_s && !has_v) return;
         if (has_s) {  // the slot's old entry to the evicted-entry row
             uint16_t *ke = p.k + (bh * cap + pr.erow) * D, *ve = p.v + (bh * cap + pr.erow) * D;
-            if (mrow == sr) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4 *>(ke + 32 * j + 8 * kg) = kt[j];
-            }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (2 * u + hw == sr) *reinterpret_cast<uint4 *>(ve + 8 * dl) = vt[u];
+                if (2 * u + hw == sr) {
+                    *reinterpret_cast<uint4 *>(ke + 8 * dl) = kt[u];
+                    *reinterpret_cast<uint4 *>(ve + 8 * dl) = vt[u];
+                }
         }
         // the new token into its row: lanes 0..31 K, 32..63 V, 16 bytes each.
         // Slot s was loaded by this round; its store must not be issued before
@@ -316,14 +357,16 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         }
         const int64_t pair = (int64_t)a.b * Hkv + a.kvh;
         const int64_t slot = (int64_t)w + pair;
-        store_partial<G>(st, p.part_o + slot * G * D, p.part_lse + slot * G, lane);
-        __threadfence();  // release: the partial before the count
+        store_partial_coherent<G>(st, p.part_o + slot * G * D, p.part_lse + slot * G, lane);
+        // The partial's stores bypass the XCD-private L2 (see
+        // store_partial_coherent); once they are complete the count may go up.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         int old = 0;
-        if (lane == 0) old = atomicAdd(p.counters + pair, 1);
+        if (lane == 0) old = __hip_atomic_fetch_add(p.counters + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         old = __shfl(old, 0, 64);
+        asm volatile("" ::: "memory");
         if (old != w_hi - w_lo) return 0;
-        __threadfence();  // acquire: every partial of the pair after the count
-        if (lane == 0) atomicExch(p.counters + pair, 0);
+        if (lane == 0) __hip_atomic_store(p.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s0 = (int64_t)w_lo + pair;
         return w_hi - w_lo + 1;
     };
@@ -362,7 +405,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         {
             bf16x8 qa[8];
             load_qa(qa);
-            st.template round<true>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, lane, sub_row(gc, pr),
+            st.template round<true>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, sub_row(gc, pr),
                                     s_knew, s_vnew);
         }
         append_after(cur, gc, pr, kA, vA);
@@ -383,7 +426,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         {
             bf16x8 qa[8];
             load_qa(qa);
-            st.template round<true>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, lane, sub_row(gc, pr),
+            st.template round<true>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, sub_row(gc, pr),
                                     s_knew, s_vnew);
         }
         append_after(cur, gc, pr, kB, vB);
@@ -425,9 +468,9 @@ int step_slots_g(int rot) {
 template <int G>
 hipError_t launch_step_g(const StepParams &p, int rot, int waves, hipStream_t s) {
     if (rot == 64)
-        hipLaunchKernelGGL((decode_step_kernel<G, 64>), dim3(waves), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((decode_step_kernel<G, 64>), dim3(waves), dim3(64), (p.batch + 1) * sizeof(int), s, p);
     else if (rot == 256)
-        hipLaunchKernelGGL((decode_step_kernel<G, 256>), dim3(waves), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((decode_step_kernel<G, 256>), dim3(waves), dim3(64), (p.batch + 1) * sizeof(int), s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

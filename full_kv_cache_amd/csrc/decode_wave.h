@@ -4,8 +4,11 @@
 // A 16-key round for one wave and one KV head:
 //   * QK^T on the matrix cores, v_mfma_f32_16x16x32_bf16: the G query heads
 //     are the 16-row A operand (rows >= G zero), the 16 keys the B
-//     operand, fed straight from HBM with 16-byte loads (8 dims of a key row
-//     per lane);
+//     operand.  K rows arrive like V rows -- each 16-byte load instruction
+//     covers two whole 512-byte rows -- and pass through a per-wave LDS
+//     tile into the operand layout (8 dims of one key per lane): loading the
+//     operand layout straight from HBM (16 rows x 64 bytes per instruction)
+//     streams about 30% slower;
 //   * an online softmax in the log2 domain: round maximum over the 16 key
 //     lanes (DPP), rescale of the running sum and output;
 //   * P.V on the vector ALUs: each half-wave streams whole 512-byte V rows
@@ -18,6 +21,11 @@
 
 namespace hda {
 namespace wave {
+
+// Per-wave LDS tile of one round's 16 K rows; the row pitch is padded by 16
+// bytes so the 16 rows of an operand read spread over the banks.
+constexpr int kKPitch = kHeadDim + 8;
+constexpr int kKTile = 16 * kKPitch;  // bf16 elements
 
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -116,20 +124,27 @@ struct WaveSoftmax {
     // One 16-key round: kt = the 8 K operand loads (key = 16-lane index),
     // vt = the 8 V row loads (keys 2u + half), key x of the round valid iff
     // lo <= x < hi (at least one is).  pw: this wave's LDS scratch, 16*G floats.
+    // kt / vt: the round's K and V rows as issue_round loads them (lane =
+    // 8 dims of row 2u + half-wave).  ktile: this wave's LDS tile.
     // SUB: key vr of the round (if 0 <= vr < 16) takes its K row from knew
-    // and its V row from vnew (LDS) instead of kt / vt, chunk by chunk at the
-    // point of use.
+    // and its V row from vnew (LDS) instead of what was loaded.
     template <bool SUB = false>
     __device__ __forceinline__ void round(const bf16x8 *qa, const uint4 *kt, uint4 *vt, int lo,
-                                          int hi, float scale_log2, float *pw, int lane, int vr = -1,
-                                          const uint16_t *knew = nullptr,
+                                          int hi, float scale_log2, float *pw, uint16_t *ktile, int lane,
+                                          int vr = -1, const uint16_t *knew = nullptr,
                                           const uint16_t *vnew = nullptr) {
         const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint4 *>(ktile + (2 * j + hw) * kKPitch + 8 * dl) = kt[j];
+        if (SUB && vr >= 0 && hw == 0)
+            *reinterpret_cast<uint4 *>(ktile + vr * kKPitch + 8 * dl) =
+                *reinterpret_cast<const uint4 *>(knew + 8 * dl);
+        wave_lds_fence();
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            uint4 kb = kt[j];
-            if (SUB && mrow == vr) kb = *reinterpret_cast<const uint4 *>(knew + 32 * j + 8 * kg);
+            const uint4 kb = *reinterpret_cast<const uint4 *>(ktile + mrow * kKPitch + 32 * j + 8 * kg);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kb), sc, 0, 0, 0);
         }
         // lane holds heads 4*kg + i of key mrow; a masked key's score is
@@ -201,15 +216,17 @@ struct WaveSoftmax {
 
 // Loads of one round: the 16 keys start at block row r0e (kept at most
 // capacity - 16 so that every load stays inside the block); the caller
-// masks keys outside [r0, n).  Passing lane 0 for every lane makes a
-// placeholder round: the same number of load instructions, all of one
-// 16-byte address, so the wait counts stay exact at no traffic.
+// masks keys outside [r0, n).  K and V alike: load u of the wave covers rows
+// r0e + 2u and r0e + 2u + 1 whole (lane = 8 dims of row 2u + half-wave).
+// Passing lane 0 for every lane makes a placeholder round: the same number
+// of load instructions, all of one 16-byte address, so the wait counts stay
+// exact at no traffic.
 __device__ __forceinline__ void issue_round(const uint16_t *kblk, const uint16_t *vblk, int r0e,
                                             int lane, uint4 *kt, uint4 *vt) {
-    const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
-    const uint16_t *rk = kblk + (int64_t)(r0e + mrow) * kHeadDim + 8 * kg;
+    const int hw = lane >> 5, dl = lane & 31;
+    const uint16_t *rk = kblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kt[j] = ld16_stream(rk + 32 * j);
+    for (int j = 0; j < 8; ++j) kt[j] = ld16_stream(rk + 2 * j * kHeadDim);
     const uint16_t *rv = vblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
 #pragma unroll
     for (int u = 0; u < 8; ++u) vt[u] = ld16_stream(rv + 2 * u * kHeadDim);

@@ -107,6 +107,13 @@ Plan plan_split(const hda_cache_desc *c, int layer, int64_t max_keys, int32_t ch
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
+// RoPE frequencies theta^(-2i/rot), i < rot/2, each rounded once from fp64
+// to fp32 (Spark export page, `_angles`: fp32 inverse frequencies).
+void fill_inv_freq(float *dst, double theta, int rot) {
+    for (int i = 0; i < rot / 2; ++i)
+        dst[i] = (float)(1.0 / std::pow(theta, (double)(2 * i) / (double)rot));
+}
+
 // Every decode workspace starts with one int per (sequence, KV head): the
 // fused step's arrival counters, which it keeps at zero between calls.  The
 // other paths lay their data out after this header and never write it, so
@@ -125,6 +132,12 @@ size_t workspace_for(const hda_cache_desc *c, const Plan &pl) {
 // Balanced streaming path (chunk_keys == 0): a grid of resident
 // single-wave workgroups shares all 16-key rounds; partial slots = waves +
 // (sequence, KV head) pairs.
+// Window path (chunk_keys == 0, every sequence at most kPairMaxKeys keys):
+// one workgroup per (sequence, KV head, half query group), no workspace.
+bool use_pairs(const hda_cache_desc *c, int layer, int32_t max_seq_len, int32_t chunk_keys) {
+    return chunk_keys == 0 && max_keys_of(c, layer, max_seq_len) <= hda::kPairMaxKeys;
+}
+
 bool use_stream(const hda_cache_desc *c, int32_t chunk_keys) {
     return chunk_keys == 0 && c->batch <= hda::kStreamMaxBatch;
 }
@@ -324,6 +337,7 @@ hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const 
     p.rotary_dim = cache->rotary_dim;
     p.window = cache->window;
     p.sliding = layer == HDA_SLIDING;
+    fill_inv_freq(p.inv_freq, cache->rope_theta, cache->rotary_dim);
     hipError_t e = hda::launch_rope_append(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(HDA_ERR_HIP, "rope_append launch failed: %s", hipGetErrorString(e));
@@ -334,6 +348,7 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
                                   int32_t max_seq_len, int32_t chunk_keys) {
     if (check_decode_shape(cache, layer, max_seq_len, chunk_keys) != HDA_OK) return 0;
     const int64_t mk = max_keys_of(cache, layer, max_seq_len);
+    if (use_pairs(cache, layer, max_seq_len, chunk_keys)) return 0;
     if (use_stream(cache, chunk_keys)) return stream_layout(cache, stream_waves(cache, mk)).bytes;
     return workspace_for(cache, plan_split(cache, layer, mk, chunk_keys));
 }
@@ -402,6 +417,14 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     const int g = cache->num_q_heads / cache->num_kv_heads;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    if (use_pairs(cache, layer, max_seq_len, chunk_keys)) {
+        Plan one{hda::kMaxChunk, 1};
+        hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, one);
+        p.sinks = sinks;
+        p.out = static_cast<uint16_t *>(out);
+        p.lse = lse;
+        return launched(hda::launch_decode_pairs(p, g, s), "decode");
+    }
     if (use_stream(cache, chunk_keys)) {
         const int64_t mk = max_keys_of(cache, layer, max_seq_len);
         const int waves = stream_waves(cache, mk);
@@ -546,9 +569,7 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
     p.window = cache->window;
     p.sliding = layer == HDA_SLIDING;
     p.scale_log2 = scale * 1.4426950408889634f;
-    // fp32 theta^(-2i/rot), rounded once from fp64 (Spark `_angles`)
-    for (int i = 0; i < cache->rotary_dim / 2; ++i)
-        p.inv_freq[i] = (float)(1.0 / std::pow(cache->rope_theta, (double)(2 * i) / (double)cache->rotary_dim));
+    fill_inv_freq(p.inv_freq, cache->rope_theta, cache->rotary_dim);
     const int g = cache->num_q_heads / cache->num_kv_heads;
     return launched(hda::launch_decode_step(p, g, cache->rotary_dim, waves, static_cast<hipStream_t>(stream)),
                     "decode step");

@@ -11,6 +11,8 @@ constexpr int kMaxChunk = 512;    // most keys one decode workgroup scores
 constexpr int kDecodeThreads = 256;
 constexpr int kStreamMaxBatch = 4096;  // sequences the balanced streaming path handles
 constexpr int kStreamMaxWaves = 2048;  // its grid: 256 CUs x 8 resident waves
+constexpr int kPairWaves = 8;          // waves per workgroup of the window decomposition
+constexpr int kPairMaxKeys = 1024;     // windows up to this size use it by default
 
 struct RopeAppendParams {
     uint16_t *q;
@@ -22,6 +24,7 @@ struct RopeAppendParams {
     double theta;
     int batch, num_q_heads, num_kv_heads, head_dim, rotary_dim, window;
     bool sliding;
+    float inv_freq[256];        // fp32 theta^(-2i/rot), i < rot/2 (rot <= 512)
 };
 
 struct DecodeParams {
@@ -113,6 +116,11 @@ hipError_t launch_decode_stream(const DecodeParams &p, int group, int waves, hip
 // Single-wave workgroups of the streaming kernel that fit on the device at
 // once (occupancy x CUs); 0 if no device is available.
 int stream_wave_slots(int group);
+
+// Window decomposition: one workgroup per (sequence, KV head, half of the
+// query group); writes out / lse with the sink directly (no workspace).
+// Needs capacity >= 16.
+hipError_t launch_decode_pairs(const DecodeParams &p, int group, hipStream_t stream);
 
 // Fused step over `waves` resident single-wave workgroups; group in
 // {1, 2, 4, 8, 16}, rotary_dim in {64, 256}.  Needs capacity >= 16 and

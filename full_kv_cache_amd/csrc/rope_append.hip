@@ -15,9 +15,9 @@
 // pass-through range or of V.  Each element belongs to exactly one task,
 // so the read of an old slot element and the write of its replacement
 // happen in one thread.  All global loads are issued first; the angle
-// table is built meanwhile (one pair index per thread: fp32 frequency
-// rounded once from fp64, fp32 angle, sin/cos evaluated in fp64 and rounded
-// to fp32) and
+// table is built meanwhile (one pair index per thread: the fp32 frequency,
+// rounded once from fp64 on the host, times the position in fp32, sin/cos
+// evaluated in fp64 and rounded to fp32) and
 // shared through LDS; then results are rotated and stored.  A few KB per
 // sequence: latency, not bandwidth, bounds this kernel.
 #include "hda_device.h"
@@ -105,9 +105,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
 
         if (base == 0) {  // angle table while the first loads are in flight
             for (int j = threadIdx.x; j < half; j += kRopeThreads) {
-                const double expo = (double)(2 * j) / (double)rot;
-                const float inv = (float)(1.0 / pow(p.theta, expo));
-                const float ang = (float)pos * inv;  // one fp32 multiply
+                const float ang = (float)pos * p.inv_freq[j];  // one fp32 multiply
                 sincos_angle(ang, s_cos + j, s_sin + j);
             }
             __syncthreads();

@@ -170,3 +170,16 @@ def test_batch64_throughput_shape_sampled():
         _, ref, rlse = sub.oracle_step()
         assert_attn_close(out[torch.from_numpy(sample).cuda()], ref)
         np.testing.assert_allclose(to_f64(lse)[sample], rlse, rtol=0, atol=1e-4)
+
+
+def test_window_path_ragged():
+    """Full layer at most 1024 keys long with a ragged length mix: the
+    default split takes the window decomposition (one workgroup per sequence,
+    KV head and half query group, no partials)."""
+    pos = [0, 15, 16, 100, 511, 1000]
+    _print_case(test="window_ragged", pos=pos)
+    case = HybridCase(410, len(pos), FULL, pos, lmax=1024, poison=True)
+    _, ref, rlse = case.oracle_step()
+    _, out, lse = case.gpu_step(chunk_keys=0, max_seq_len=1024)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
