@@ -162,65 +162,87 @@ def time_graph(fn, steps, warmup, use_graph=True):
     return t0.elapsed_time(t1) / steps, wall * 1e3 / steps
 
 
-KERNEL_NAMES = {
-    "fused": "decode_step_kernel<4, 64> (hda_decode_step, full layer: one launch)",
-    "separate": "full-layer hda_decode_attn: decode_stream_kernel<4> + stream_merge_kernel",
+# Kernels a layer call runs on each path (the window kernel serves every
+# sliding layer: keys <= 1024; full layers at this shape take the stream).
+KERNELS = {
+    ("separate", "sliding"): "decode_pair_kernel<2>",
+    ("separate", "full"): "decode_stream_kernel<4> + stream_merge_kernel",
+    ("fused", "sliding"): "decode_step_kernel<4, 256>",
+    ("fused", "full"): "decode_step_kernel<4, 64>",
 }
+# Sources whose change invalidates a committed traffic measurement.
+TRAFFIC_SOURCES = ("decode_attn.hip", "decode_wave.h", "decode_step.hip", "hda_device.h",
+                   "hda_kernels.h", "hda_api.cpp")
 
 
-def dominant_kernel(wl: Workload, steps, warmup, path="separate", chunk_keys=0):
-    """Time the full-layer call alone -- the largest byte mover of the step:
-    the 7 full layers' calls (exactly as the step makes them) captured in one
-    graph, HIP events on the launch stream around the replays, average per
-    call.  On the fused path a call is one kernel launch.  Algorithmic bytes
-    per call: every attended K and V row once (sum over sequences of pos + 1
-    rows of 2 KV heads x 256 dims x 2 bytes, for K and for V)."""
+def layer_kernel(wl: Workload, lt: int, steps, warmup, path="separate", chunk_keys=0):
+    """Time one layer type's attention calls (exactly as the step makes them,
+    without the RoPE/append) captured in one graph, HIP events on the launch
+    stream around the replays; average per call.  Algorithmic bytes per
+    call: every attended K and V row once (per sequence min(seq_len, window)
+    rows for a sliding layer, seq_len rows for a full one, of 2 KV heads x
+    256 dims x 2 bytes, for K and for V)."""
+    import full_kv_cache_amd as hda
     import workloads
-    full = [L for L in wl.layers if L["lt"] == workloads.FULL]
-    if not full:
+    Ls = [L for L in wl.layers if L["lt"] == lt]
+    if not Ls:
         return None
 
     def fn():
-        for L in full:
-            wl.layer_call(L, path, chunk_keys)
+        for L in Ls:
+            if path == "fused":
+                wl.layer_call(L, "fused")
+            else:
+                hda.hda_decode_attn(L["q"], L["cache"], wl.seq_lens, lt, L["sinks"], wl.scale,
+                                    L["out"], L["lse"], wl.max_seq_len, chunk_keys, wl.workspace)
 
     ms, _ = time_graph(fn, steps, warmup)
-    per_call_s = ms / len(full) / 1e3
-    algo = wl.rows[workloads.FULL] * wl.kv_row_bytes
+    per_call_s = ms / len(Ls) / 1e3
+    algo = wl.rows[lt] * wl.kv_row_bytes
     achieved = algo / per_call_s / 1e9
+    name = "sliding" if lt == workloads.SLIDING else "full"
     return {
-        "kernel": KERNEL_NAMES[path],
+        "kernel": f"{KERNELS[(path, name)]} ({name}-layer hda_decode_attn)" if path == "separate"
+                  else f"{KERNELS[(path, name)]} ({name}-layer hda_decode_step)",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(path, algo),
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(f"{KERNELS[(path, name)]}", wl.cfg["batch"]),
         "algorithmic_bytes_per_launch": algo, "avg_launch_us": round(per_call_s * 1e6, 2),
-        "launches_timed": steps * len(full),
+        "launches_timed": steps * len(Ls),
     }
 
 
-def measured_traffic(path, algo):
-    """HBM bytes per launch of the timed kernel from the committed PMC
-    summary (FETCH_SIZE x the copy-calibrated factor + WRITE_SIZE), or None
-    when the summary is missing or was taken on other kernel sources."""
+def sources_digest():
     import hashlib
-    if path != "fused":
-        return None
-    f = os.path.join(ROOT, "profiles", "traffic_decode_step_full_b64_u512-4096.txt")
-    if not os.path.exists(f):
-        return None
-    vals = {}
-    for line in open(f):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            vals[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for src in ("decode_step.hip", "decode_wave.h", "hda_device.h", "hda_kernels.h"):
+    for src in TRAFFIC_SOURCES:
         h.update(open(os.path.join(ROOT, "full_kv_cache_amd", "csrc", src), "rb").read())
-    if vals.get("source_sha256") != h.hexdigest():
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, batch):
+    """HBM bytes per launch from the committed PMC summary
+    (profiles/traffic_decode_b64_u512-4096.txt: FETCH_SIZE x the
+    copy-calibrated factor + WRITE_SIZE, per launch of the kernel), or None
+    when there is none for this kernel, or it was taken on other sources."""
+    f = os.path.join(ROOT, "profiles", "traffic_decode_b64_u512-4096.txt")
+    if batch != 64 or not os.path.exists(f):
         return None
-    try:
-        return int(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+    digest, table = None, {}
+    for line in open(f):
+        line = line.strip()
+        if line.startswith("source_sha256:"):
+            digest = line.split(":", 1)[1].strip()
+        elif line.startswith("|") and "bytes" not in line and "---" not in line:
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            if len(cells) >= 5:
+                try:
+                    table[cells[0]] = int(cells[4].replace(",", ""))
+                except ValueError:
+                    pass
+    if digest != sources_digest():
         return None
+    return table.get(kernel)
 
 
 def sparse_kernel(steps, warmup, seed, pools=8):
@@ -262,7 +284,8 @@ def sparse_kernel(steps, warmup, seed, pools=8):
         "us_per_call": round(per_call_s * 1e6, 2), "gather_GBs": round(gbs, 1),
         "tflops": round(flops / per_call_s / 1e12, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("sparse_decode_kernel<false> + sparse_merge_kernel", 64),
                      "algorithmic_bytes_per_launch": gathered},
         "mfma_bf16_frac": round(flops / per_call_s / 2.5e15, 4),
     }
@@ -353,8 +376,15 @@ def main():
     eager_ms = None
     if not args.no_graph:
         eager_ms, _ = time_graph(step, max(3, args.steps // 5), 2, use_graph=False)
-    print("# timing dominant kernel", file=sys.stderr, flush=True)
-    roof = dominant_kernel(wl, args.steps, args.warmup, args.path, args.chunk_keys)
+    print("# timing the layer kernels", file=sys.stderr, flush=True)
+    import workloads
+    k_slide = layer_kernel(wl, workloads.SLIDING, args.steps, args.warmup, args.path, args.chunk_keys)
+    k_full = layer_kernel(wl, workloads.FULL, args.steps, args.warmup, args.path, args.chunk_keys)
+    # the dominant kernel: the layer type with the most attention time per step
+    n_s = sum(1 for L in wl.layers if L["lt"] == workloads.SLIDING)
+    n_f = len(wl.layers) - n_s
+    cands = [(k["avg_launch_us"] * n, k) for k, n in ((k_slide, n_s), (k_full, n_f)) if k]
+    roof = max(cands, key=lambda c: c[0])[1] if cands else None
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
@@ -380,7 +410,8 @@ def main():
         "kv_bytes_per_step": wl.kv_bytes,
         "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
-        "roofline": roof, "cpu_baseline": cpu, "sparse": sparse,
+        "roofline": roof, "layer_kernels": {"sliding": k_slide, "full": k_full},
+        "cpu_baseline": cpu, "sparse": sparse,
     }
     print(json.dumps(rec), flush=True)
 
