@@ -443,6 +443,213 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     for (int i = 0; i < n_merge; ++i) merge_pair<G>(p, m_s0[i], m_n[i], m_b[i], m_kvh[i], lane);
 }
 
+// ===================================================================
+// Window form of the step (sliding layers, window <= kPairMaxKeys): one
+// workgroup of kPairWaves waves per (sequence, KV head, 1/S of the query
+// group), as decode_pair_kernel, with the rest of the step inside:
+//   * prologue: the angle table for the sequence's position, the
+//     workgroup's GW query rows and the new K rotated into LDS, the new V
+//     copied there;
+//   * rounds: the new token's row (min(pos, window-1)) is served from LDS;
+//     the round that reads ring slot s keeps its old entry (a key of this
+//     step) in LDS as well;
+//   * epilogue: the waves merge in LDS and write out / lse with the sink;
+//     then the last of the S workgroups of the pair (a counter per pair, taken
+//     once each workgroup's loads of the block are consumed) writes the
+//     append: the kept entry to the evicted-entry row, the new token to its
+//     slot (or to row pos below a full window), and resets the counter.
+// Both workgroups of a pair read every key row; neither writes one until
+// both have read them, and no data passes between them, so no fence is
+// needed around the counter.
+// ===================================================================
+template <int GW, int ROT>
+__global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(StepParams p, int S) {
+    constexpr int D = kHeadDim;
+    constexpr int WAVES = kPairWaves;
+    static_assert(ROT % 16 == 0 && ROT <= D, "rotary dims in 16-byte chunk pairs");
+    __shared__ __align__(16) float s_red[WAVES * GW * D];
+    __shared__ __align__(16) float s_pw[WAVES][16 * GW];
+    __shared__ __align__(16) uint16_t s_kt[WAVES][kKTile];
+    __shared__ __align__(16) float s_cos[ROT / 2], s_sin[ROT / 2];
+    // rows 0..GW-1 rotated q, GW rotated new K, GW+1 new V, GW+2/GW+3 the
+    // old K/V entry of the ring slot the new token takes
+    __shared__ __align__(16) uint16_t s_rows[(GW + 4) * D];
+    __shared__ float s_m[WAVES][GW], s_l[WAVES][GW];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hw = lane >> 5, dl = lane & 31, mrow = lane & 15, kg = lane >> 4;
+    const int pairs = p.batch * p.num_kv_heads;
+    const int x = blockIdx.x;
+    const int part = (x >> 3) % S;
+    const int pr = ((x >> 3) / S) * 8 + (x & 7);
+    if (pr >= pairs) return;
+    const int b = pr / p.num_kv_heads, kvh = pr % p.num_kv_heads;
+    const int hsub = kvh * S + part;  // query heads hsub*GW .. +GW-1
+    const int Hq = p.num_q_heads, W = p.window;
+    const int P = p.pos[b];
+    const int n = P < 0 ? 0 : min(P + 1, W);
+    const int vrow = min(P, W - 1);                       // the new token's row
+    const int srow = P >= W - 1 ? P % (W - 1) : -1;       // ring slot it takes
+    const int64_t cap = p.capacity;
+    const int64_t bh = (int64_t)b * p.num_kv_heads + kvh;
+    uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
+    uint16_t *const s_knew = s_rows + GW * D, *const s_vnew = s_rows + (GW + 1) * D;
+    uint16_t *const s_oldk = s_rows + (GW + 2) * D, *const s_oldv = s_rows + (GW + 3) * D;
+
+    const int R = (n + 15) >> 4;
+    const int r_lo = wave * R / WAVES, r_hi = (wave + 1) * R / WAVES;
+    auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap - 16 ? 16 * r : cap - 16); };
+
+    if (n > 0) {  // prologue: angles, then rotated rows
+        for (int i = tid; i < ROT / 2; i += WAVES * 64)
+            sincos_angle((float)P * p.inv_freq[i], s_cos + i, s_sin + i);
+        __syncthreads();
+        constexpr int kRot = ROT / 16, kRow = kRot + (D - ROT) / 8;  // tasks per rotated row
+        const uint16_t *qrow = p.q + ((int64_t)b * Hq + hsub * GW) * D;
+        for (int t = tid; t < (GW + 1) * kRow + D / 8; t += WAVES * 64) {
+            const int r = t / kRow, c = t % kRow;
+            if (r > GW) {
+                const int d = 8 * (t - (GW + 1) * kRow);
+                *reinterpret_cast<uint4 *>(s_vnew + d) = ld16(p.v_new + bh * D + d);
+                continue;
+            }
+            const uint16_t *src = r < GW ? qrow + r * D : p.k_new + bh * D;
+            uint16_t *dst = s_rows + r * D;
+            if (c < kRot) {
+                const int i = 8 * c;
+                uint4 x1 = ld16(src + i), x2 = ld16(src + ROT / 2 + i);
+                rotate8(x1, x2, s_cos + i, s_sin + i, x1, x2);
+                *reinterpret_cast<uint4 *>(dst + i) = x1;
+                *reinterpret_cast<uint4 *>(dst + ROT / 2 + i) = x2;
+            } else {
+                const int d = ROT + 8 * (c - kRot);
+                *reinterpret_cast<uint4 *>(dst + d) = ld16(src + d);
+            }
+        }
+        __syncthreads();
+    }
+
+    WaveSoftmax<GW> st;
+    st.reset();
+    if (r_lo < r_hi) {
+        // the q operand is read from LDS for every round (registers are short)
+        const uint16_t *qs = s_rows + (mrow < GW ? mrow : 0) * D + 8 * kg;
+        // a round's 16 rows start at r0e = min(16 r, capacity - 16): in bounds
+        auto one = [&](int r, uint4 *kt, uint4 *vt) {
+            bf16x8 qa[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint4 u = *reinterpret_cast<const uint4 *>(qs + 32 * j);
+                if (mrow >= GW) u = make_uint4(0, 0, 0, 0);
+                qa[j] = as_bf16x8(u);
+            }
+            const int r0e = r0e_of(r), lo = 16 * r - r0e, hi = n - r0e;
+            const int vr = vrow - r0e, sr = srow - r0e;
+            st.template round<true>(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave], s_kt[wave], lane,
+                                    (vr >= lo && vr < hi && vr < 16) ? vr : -1, s_knew, s_vnew);
+            if (srow >= 0 && sr >= lo && sr < hi && sr < 16) {  // keep the slot's old entry
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (2 * u + hw == sr) {
+                        *reinterpret_cast<uint4 *>(s_oldk + 8 * dl) = kt[u];
+                        *reinterpret_cast<uint4 *>(s_oldv + 8 * dl) = vt[u];
+                    }
+            }
+        };
+        uint4 kA[8], vA[8], kB[8], vB[8];
+        for (int r = r_lo; r < r_hi; r += 2) {
+            const bool two = r + 1 < r_hi;
+            issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
+            issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+            one(r, kA, vA);
+            if (!two) break;
+            one(r + 1, kB, vB);
+        }
+    }
+
+    // merge the waves: each leaves its unnormalised o and its (m, l)
+    float l_h[4];
+    st.sums(l_h);
+#pragma unroll
+    for (int h = 0; h < GW; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
+            if (hw == 0) s_red[(wave * GW + h) * D + 8 * dl + e] = o;
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GW; ++h) {
+            s_m[wave][h] = r_lo < r_hi ? st.max_of(h) : -INFINITY;
+            s_l[wave][h] = r_lo < r_hi ? lane_value(l_h[h & 3], 16 * (h >> 2)) : 0.f;
+        }
+    }
+    // every wave's loads of the block are consumed past this barrier
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        s_last = 0;
+        if (P >= 0) {
+            const int old = __hip_atomic_fetch_add(p.counters + pr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = old == S - 1;
+            if (s_last) __hip_atomic_store(p.counters + pr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    for (int i = tid; i < GW * D; i += WAVES * 64) {
+        const int h = i / D, d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+        const int hq = hsub * GW + h;
+        uint16_t *outp = p.out + ((int64_t)b * Hq + hq) * D + d;
+        if (M == -INFINITY) {  // no keys
+            *outp = 0;
+            if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = -INFINITY;
+            continue;
+        }
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float sc = exp2f(s_m[w][h] - M);
+            L = fmaf(sc, s_l[w][h], L);
+            o = fmaf(sc, s_red[(w * GW + h) * D + d], o);
+        }
+        const float lse = (M + log2f(L)) * kLn2;
+        float f = 1.f / L;
+        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        *outp = f32_to_bf16(o * f);
+        if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
+    }
+    __syncthreads();
+    if (s_last && tid < 128) {  // the append: 16 bytes per thread, K then V
+        const int which = tid >> 6, c = tid & 31, half = (tid >> 5) & 1;
+        uint16_t *blk = which ? vblk : kblk;
+        if (half == 0 && srow >= 0)  // the slot's old entry to the evicted-entry row
+            *reinterpret_cast<uint4 *>(blk + (int64_t)(W - 1) * D + 8 * c) =
+                *reinterpret_cast<const uint4 *>((which ? s_oldv : s_oldk) + 8 * c);
+        if (half == 1)  // the new token to its slot (row pos below a full window)
+            *reinterpret_cast<uint4 *>(blk + (int64_t)(srow >= 0 ? srow : vrow) * D + 8 * c) =
+                *reinterpret_cast<const uint4 *>((which ? s_vnew : s_knew) + 8 * c);
+    }
+}
+
+template <int GW, int ROT>
+hipError_t launch_window_gr(const StepParams &p, int S, hipStream_t s) {
+    const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
+    const int64_t blocks = (pairs + 7) / 8 * 8 * S;
+    hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT>), dim3((unsigned)blocks), dim3(kPairWaves * 64), 0, s,
+                       p, S);
+    return hipGetLastError();
+}
+
+template <int GW>
+hipError_t launch_window_g(const StepParams &p, int S, int rot, hipStream_t s) {
+    if (rot == 64) return launch_window_gr<GW, 64>(p, S, s);
+    if (rot == 256) return launch_window_gr<GW, 256>(p, S, s);
+    return hipErrorInvalidValue;
+}
+
 template <int G, int ROT>
 int step_slots_gr() {
     static int cached = -1;
@@ -486,6 +693,18 @@ int step_wave_slots(int group, int rot) {
         case 8: return step_slots_g<8>(rot);
         case 16: return step_slots_g<16>(rot);
         default: return 0;
+    }
+}
+
+hipError_t launch_decode_window_step(const StepParams &p, int group, int rot, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    switch (group) {
+        case 1: return launch_window_g<1>(p, 1, rot, stream);
+        case 2: return launch_window_g<1>(p, 2, rot, stream);
+        case 4: return launch_window_g<2>(p, 2, rot, stream);
+        case 8: return launch_window_g<4>(p, 2, rot, stream);
+        case 16: return launch_window_g<8>(p, 2, rot, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -218,6 +218,11 @@ struct StepLayout {
     size_t o_off, lse_off, bytes;
 };
 
+// Window form of the step: sliding layers whose window fits one workgroup.
+bool use_window_step(const hda_cache_desc *c, int layer) {
+    return layer == HDA_SLIDING && c->window <= hda::kPairMaxKeys;
+}
+
 StepLayout step_layout(const hda_cache_desc *c, int waves) {
     const size_t slots = (size_t)waves + (size_t)c->batch * c->num_kv_heads;
     const size_t g = (size_t)(c->num_q_heads / c->num_kv_heads);
@@ -527,6 +532,7 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
 
 size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer) {
     if (check_step_shape(cache, layer) != HDA_OK) return 0;
+    if (use_window_step(cache, layer)) return counter_header(cache);
     return step_layout(cache, step_waves(cache, layer)).bytes;
 }
 
@@ -544,10 +550,12 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
         (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fail(HDA_ERR_INVALID_ARGUMENT, "pos, sinks and lse must be 4-byte aligned");
     if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
-    const int waves = step_waves(cache, layer);
+    const bool window = use_window_step(cache, layer);
+    const int waves = window ? 0 : step_waves(cache, layer);
     const StepLayout L = step_layout(cache, waves);
-    if (!workspace || workspace_bytes < L.bytes)
-        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", L.bytes,
+    const size_t need = window ? counter_header(cache) : L.bytes;
+    if (!workspace || workspace_bytes < need)
+        return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", need,
                     workspace_bytes, workspace);
     if (!aligned16(workspace)) return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (cache->batch == 0) return ok();
@@ -574,6 +582,9 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
     p.scale_log2 = scale * 1.4426950408889634f;
     fill_inv_freq(p.inv_freq, cache->rope_theta, cache->rotary_dim);
     const int g = cache->num_q_heads / cache->num_kv_heads;
+    if (window)
+        return launched(hda::launch_decode_window_step(p, g, cache->rotary_dim, static_cast<hipStream_t>(stream)),
+                        "decode step");
     return launched(hda::launch_decode_step(p, g, cache->rotary_dim, waves, static_cast<hipStream_t>(stream)),
                     "decode step");
 }

@@ -129,6 +129,11 @@ hipError_t launch_decode_step(const StepParams &p, int group, int rotary_dim, in
                               hipStream_t stream);
 int step_wave_slots(int group, int rotary_dim);
 
+// Window form of the fused step (sliding layers with window <=
+// kPairMaxKeys == capacity): one workgroup per (sequence, KV head, half
+// query group); needs only the counters of StepParams.
+hipError_t launch_decode_window_step(const StepParams &p, int group, int rotary_dim, hipStream_t stream);
+
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);
 
 }  // namespace hda

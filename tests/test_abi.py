@@ -226,12 +226,17 @@ def test_step_shape_checks():
 
 
 def test_step_workspace():
-    """Counter header first (shared with hda_decode_attn's layouts), then
-    one partial slot per wave and per (sequence, KV head)."""
+    """Counter header first (shared with hda_decode_attn's layouts); the
+    window form (sliding layers) needs only that header, the streaming form
+    (full layers) adds one partial slot per wave and per (sequence, KV
+    head)."""
     L = hda.lib()
     d = _desc()
     need = L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.SLIDING)
-    assert need > 256 and need % 256 == 0
+    assert need == 256  # 2 sequences x 2 KV heads x 4 bytes, rounded up
+    full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
+    need_full = L.hda_decode_step_workspace_bytes(ctypes.byref(full), hda.FULL)
+    assert need_full > 256 and need_full % 256 == 0
     assert _step(d) == 3 and "workspace" in _msg()
     assert _step(d, ws=FAKE, wsb=need - 1) == 3
     assert _step(d, ws=FAKE + 4, wsb=need) == 1
