@@ -109,8 +109,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
     }
 
     // merge the waves: each leaves its unnormalised o and its (m, l)
-    float l_h[4];
-    st.sums(l_h);
+    float m_h[G], l_h[G];
+    st.totals(m_h, l_h);
     const int hw = lane >> 5, dl = lane & 31;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            s_m[wave][h] = kw1 > kw0 ? st.max_of(h) : -INFINITY;
-            s_l[wave][h] = kw1 > kw0 ? lane_value(l_h[h & 3], 16 * (h >> 2)) : 0.f;
+            s_m[wave][h] = kw1 > kw0 ? m_h[h] : -INFINITY;
+            s_l[wave][h] = kw1 > kw0 ? l_h[h] : 0.f;
         }
     }
     __syncthreads();
@@ -411,8 +411,8 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
     }
 
     // merge the waves: each leaves its unnormalised o and its (m, l)
-    float l_h[4];
-    st.sums(l_h);
+    float m_h[GW], l_h[GW];
+    st.totals(m_h, l_h);
     const int hw = lane >> 5, dl = lane & 31;
 #pragma unroll
     for (int h = 0; h < GW; ++h)
@@ -424,8 +424,8 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < GW; ++h) {
-            s_m[wave][h] = r_lo < r_hi ? st.max_of(h) : -INFINITY;
-            s_l[wave][h] = r_lo < r_hi ? lane_value(l_h[h & 3], 16 * (h >> 2)) : 0.f;
+            s_m[wave][h] = r_lo < r_hi ? m_h[h] : -INFINITY;
+            s_l[wave][h] = r_lo < r_hi ? l_h[h] : 0.f;
         }
     }
     __syncthreads();

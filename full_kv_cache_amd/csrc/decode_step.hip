@@ -77,18 +77,18 @@ template <int G>
 __device__ __forceinline__ void store_partial_coherent(const WaveSoftmax<G> &st, float *po, float *plse,
                                                        int lane) {
     const int hw = lane >> 5, dl = lane & 31;
-    float l_h[4];
-    st.sums(l_h);
+    float m_h[G], l_h[G];
+    st.totals(m_h, l_h);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
+        const float l = l_h[h];
         const float inv = 1.f / l;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float o = (st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64)) * inv;
             if (hw == 0) coherent_store(po + h * kHeadDim + 8 * dl + e, o);
         }
-        if (lane == 0) coherent_store(plse + h, (st.max_of(h) + log2f(l)) * kLn2);
+        if (lane == 0) coherent_store(plse + h, (m_h[h] + log2f(l)) * kLn2);
     }
 }
 
@@ -97,13 +97,13 @@ template <int G>
 __device__ __forceinline__ void store_final(const WaveSoftmax<G> &st, const StepParams &p, int b,
                                             int kvh, int lane) {
     const int hw = lane >> 5, dl = lane & 31;
-    float l_h[4];
-    st.sums(l_h);
+    float m_h[G], l_h[G];
+    st.totals(m_h, l_h);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const int hq = kvh * G + h;
-        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
-        const float lse = (st.max_of(h) + log2f(l)) * kLn2;
+        const float l = l_h[h];
+        const float lse = (m_h[h] + log2f(l)) * kLn2;
         float f = 1.f / l;
         if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
         uint32_t w[4];
@@ -569,8 +569,8 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     }
 
     // merge the waves: each leaves its unnormalised o and its (m, l)
-    float l_h[4];
-    st.sums(l_h);
+    float m_h[GW], l_h[GW];
+    st.totals(m_h, l_h);
 #pragma unroll
     for (int h = 0; h < GW; ++h)
 #pragma unroll
@@ -581,8 +581,8 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < GW; ++h) {
-            s_m[wave][h] = r_lo < r_hi ? st.max_of(h) : -INFINITY;
-            s_l[wave][h] = r_lo < r_hi ? lane_value(l_h[h & 3], 16 * (h >> 2)) : 0.f;
+            s_m[wave][h] = r_lo < r_hi ? m_h[h] : -INFINITY;
+            s_l[wave][h] = r_lo < r_hi ? l_h[h] : 0.f;
         }
     }
     // every wave's loads of the block are consumed past this barrier

@@ -206,11 +206,20 @@ struct WaveSoftmax {
         wave_lds_fence();
     }
 
-    // Wave totals for head h (wave-uniform): running max and sum.
-    __device__ __forceinline__ float max_of(int h) const { return lane_value(m_run[h & 3], 16 * (h >> 2)); }
-    __device__ __forceinline__ void sums(float *l_h) const {
+    // Wave totals of every head (wave-uniform): running max m_h and sum l_h.
+    // Head h lives in lanes 16*(h/4) ..; the reads of those lanes must run
+    // with the whole wave active, never inside a branch that some lane
+    // skips: the compiler may sink the last step of the row sum into such a
+    // branch, and the lanes it leaves out would then hold a partial sum.
+    __device__ __forceinline__ void totals(float (&m_h)[G], float (&l_h)[G]) const {
+        float l4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l_h[i] = row16_sum(l_lane[i]);
+        for (int i = 0; i < 4; ++i) l4[i] = row16_sum(l_lane[i]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            m_h[h] = lane_value(m_run[h & 3], 16 * (h >> 2));
+            l_h[h] = lane_value(l4[h & 3], 16 * (h >> 2));
+        }
     }
 };
 
@@ -237,11 +246,11 @@ template <int G>
 __device__ __forceinline__ void store_partial(const WaveSoftmax<G> &st, float *po, float *plse,
                                               int lane) {
     const int hw = lane >> 5, dl = lane & 31;
-    float l_h[4];
-    st.sums(l_h);
+    float m_h[G], l_h[G];
+    st.totals(m_h, l_h);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float l = lane_value(l_h[h & 3], 16 * (h >> 2));
+        const float l = l_h[h];
         const float inv = 1.f / l;
         float o[8];
 #pragma unroll
@@ -251,7 +260,7 @@ __device__ __forceinline__ void store_partial(const WaveSoftmax<G> &st, float *p
             *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
             *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
         }
-        if (lane == 0) plse[h] = (st.max_of(h) + log2f(l)) * kLn2;
+        if (lane == 0) plse[h] = (m_h[h] + log2f(l)) * kLn2;
     }
 }
 

@@ -21,12 +21,14 @@ BF16_NAN = 0x7FC0
 
 
 class HybridCase:
-    def __init__(self, seed, batch, layer_type, pos, lmax=None, window=512, poison=False):
+    def __init__(self, seed, batch, layer_type, pos, lmax=None, window=512, poison=False,
+                 num_q_heads=8, num_kv_heads=2):
         self.lt = layer_type
         self.pos = np.asarray(pos, dtype=np.int32)
         assert self.pos.shape == (batch,)
         lmax = lmax or int(self.pos.max()) + 1
-        self.shape = workloads.HybridShape(batch=batch, lmax=lmax, window=window)
+        self.shape = workloads.HybridShape(batch=batch, lmax=lmax, window=window,
+                                           num_q_heads=num_q_heads, num_kv_heads=num_kv_heads)
         g = workloads.generator(seed)
         t = workloads.layer_inputs(g, self.shape, layer_type)
         self.host = {k: workloads.bits(v).copy() for k, v in t.items()}
