@@ -10,7 +10,10 @@ layer i is full when i % 4 == 3)
                         into the ring slot (sliding) or row pos (full);
     hda_decode_attn  -- GQA attention over the layer's keys with a per-head
                         sink: balanced streaming kernel plus the LSE merge
-    (--path fused: hda_decode_step, the same step in one launch).
+    (--path fused: hda_decode_step, the same step in one launch; --path
+    auto, the default: the faster of the two per layer type, measured on
+    MI355X -- hda_decode_step for sliding layers, hda_rope_append +
+    hda_decode_attn for full layers).
 
 Each timed step re-appends at the same positions; the rows read and the
 work done are those of one decode step either way.
@@ -26,7 +29,7 @@ roofline entry for the dominant kernel and the CPU oracle's rate on a
 bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
-                    [--path fused|separate]
+                    [--path auto|fused|separate]
 """
 from __future__ import annotations
 
@@ -72,7 +75,7 @@ def parse():
                     help="minimum oracle time for the CPU baseline sample")
     ap.add_argument("--chunk-keys", type=int, default=0,
                     help="split size for full layers on the separate path (0: default)")
-    ap.add_argument("--path", default="separate", choices=["fused", "separate"],
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "separate"],
                     help="one launch per layer (hda_decode_step) or rope_append + decode_attn")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of this many MB (PMC byte calibration)")
@@ -120,9 +123,9 @@ class Workload:
                      for lt in (workloads.SLIDING, workloads.FULL)}
         self.kv_bytes = sum(self.rows[lt] for lt in self.types) * self.kv_row_bytes
 
-    def layer_call(self, L, path="separate", chunk_keys=0):
+    def layer_call(self, L, path="auto", chunk_keys=0):
         import full_kv_cache_amd as hda
-        if path == "fused":
+        if layer_path(path, L["lt"]) == "fused":
             hda.hda_decode_step(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"],
                                 L["sinks"], self.scale, L["out"], L["lse"], self.workspace)
         else:
@@ -130,7 +133,7 @@ class Workload:
             hda.hda_decode_attn(L["q"], L["cache"], self.seq_lens, L["lt"], L["sinks"], self.scale,
                                 L["out"], L["lse"], self.max_seq_len, chunk_keys, self.workspace)
 
-    def step(self, path="separate", chunk_keys=0):
+    def step(self, path="auto", chunk_keys=0):
         for L in self.layers:
             self.layer_call(L, path, chunk_keys)
 
@@ -162,12 +165,21 @@ def time_graph(fn, steps, warmup, use_graph=True):
     return t0.elapsed_time(t1) / steps, wall * 1e3 / steps
 
 
-# Kernels a layer call runs on each path (the window kernel serves every
+def layer_path(path, lt):
+    """The path a layer call takes: auto = hda_decode_step (one launch) for
+    sliding layers, hda_rope_append + hda_decode_attn for full layers."""
+    import workloads
+    if path == "auto":
+        return "fused" if lt == workloads.SLIDING else "separate"
+    return path
+
+
+# Kernels a layer call runs on each path (the window kernels serve every
 # sliding layer: keys <= 1024; full layers at this shape take the stream).
 KERNELS = {
     ("separate", "sliding"): "decode_pair_kernel<2>",
     ("separate", "full"): "decode_stream_kernel<4> + stream_merge_kernel",
-    ("fused", "sliding"): "decode_step_kernel<4, 256>",
+    ("fused", "sliding"): "decode_window_step_kernel<2, 256>",
     ("fused", "full"): "decode_step_kernel<4, 64>",
 }
 # Sources whose change invalidates a committed traffic measurement.
@@ -175,10 +187,11 @@ TRAFFIC_SOURCES = ("decode_attn.hip", "decode_wave.h", "decode_step.hip", "hda_d
                    "hda_kernels.h", "hda_api.cpp")
 
 
-def layer_kernel(wl: Workload, lt: int, steps, warmup, path="separate", chunk_keys=0):
-    """Time one layer type's attention calls (exactly as the step makes them,
-    without the RoPE/append) captured in one graph, HIP events on the launch
-    stream around the replays; average per call.  Algorithmic bytes per
+def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0):
+    """Time one layer type's attention calls (exactly as the step makes them:
+    on the separate path hda_decode_attn without the RoPE/append launch, on
+    the fused path the whole hda_decode_step) captured in one graph, HIP
+    events on the launch stream around the replays; average per call.  Algorithmic bytes per
     call: every attended K and V row once (per sequence min(seq_len, window)
     rows for a sliding layer, seq_len rows for a full one, of 2 KV heads x
     256 dims x 2 bytes, for K and for V)."""
@@ -187,6 +200,7 @@ def layer_kernel(wl: Workload, lt: int, steps, warmup, path="separate", chunk_ke
     Ls = [L for L in wl.layers if L["lt"] == lt]
     if not Ls:
         return None
+    path = layer_path(path, lt)
 
     def fn():
         for L in Ls:

@@ -196,6 +196,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     __shared__ __align__(16) float s_cos[ROT / 2], s_sin[ROT / 2];
     // rotated q of the pair's G heads, then its rotated new K, then new V
     __shared__ __align__(16) uint16_t s_rows[(G + 2) * D];
+    __shared__ int s_merge[1 + 2 * 5];  // count, then (n, b, kvh, s0 lo, s0 hi) per merge owed
     uint16_t *const s_knew = s_rows + G * D, *const s_vnew = s_rows + (G + 1) * D;
 
     const int lane = threadIdx.x;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
 
     RoundAddr cur = locate_round(s_pre, B, Hkv, g0);
     const int64_t cap = p.capacity, cap16 = cap - 16;
-    auto geo = [&](const RoundAddr &a) {
+    auto geo = [&](const RoundAddr &a) HDA_INLINE {
         RoundGeo g;
         const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
         g.kblk = p.k + bh * cap * D;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     // Entering a pair: the angle table, then the pair's G query rows and its
     // new K row rotated (and the new V row copied) into LDS, 16-byte chunk
     // pairs spread over the lanes.
-    auto enter_pair = [&](const RoundAddr &a) {
+    auto enter_pair = [&](const RoundAddr &a) HDA_INLINE {
         PairRows pr;
         const int P = uniform(p.pos[a.b]);
         pr.erow = p.window - 1;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     // The q operand is read from LDS for every round instead of being held
     // in registers through the loop (rows >= G read row 0 and are zeroed).
     const uint16_t *const q_lds = s_rows + (mrow < G ? mrow : 0) * D + 8 * kg;
-    auto load_qa = [&](bf16x8 *qa) {
+    auto load_qa = [&](bf16x8 *qa) HDA_INLINE {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint4 u = *reinterpret_cast<const uint4 *>(q_lds + 32 * j);
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         return x >= g.lo && x < g.hi && x < 16;
     };
     // Key of the round served by the new token, or -1.
-    auto sub_row = [&](const RoundGeo &g, const PairRows &pr) {
+    auto sub_row = [&](const RoundGeo &g, const PairRows &pr) HDA_INLINE {
         return in_round(g, pr.vrow) ? pr.vrow - g.r0e : -1;
     };
 
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     // The round's loads are consumed by then, so every old row it holds was
     // read before anything overwrites it.
     auto append_after = [&](const RoundAddr &a, const RoundGeo &g, const PairRows &pr, const uint4 *kt,
-                            const uint4 *vt) {
+                            const uint4 *vt) HDA_INLINE {
         const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
         const int sr = pr.srow - g.r0e;
         const bool has_s = pr.srow >= 0 && in_round(g, pr.srow);
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     // Returns the number of segments when this wave arrived last (the merge
     // is done after the wave's own rounds), else 0.
     WaveSoftmax<G> st;
-    auto end_segment = [&](const RoundAddr &a, int64_t &s0) -> int {
+    auto end_segment = [&](const RoundAddr &a, int64_t &s0) HDA_INLINE -> int {
         const int rb = s_pre[a.b + 1] - s_pre[a.b];
         const int64_t g_lo = (int64_t)Hkv * s_pre[a.b] + (int64_t)a.kvh * rb;
         const int w_lo = wave_of_round(g_lo, r_tot, W);
@@ -372,19 +373,22 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     };
 
     // At most two of a wave's pairs are shared with other waves: its first
-    // and its last.
-    int m_n[2] = {0, 0}, m_b[2] = {0, 0}, m_kvh[2] = {0, 0};
-    int64_t m_s0[2] = {0, 0};
-    int n_merge = 0;
-    auto finish = [&](const RoundAddr &a) {
+    // and its last.  The merges this wave owes are recorded in LDS (the
+    // workgroup is this one wave) and done after its last round; carried in
+    // registers through the loop they cost occupancy.
+    if (lane == 0) s_merge[0] = 0;
+    auto finish = [&](const RoundAddr &a) HDA_INLINE {
         int64_t s0 = 0;
-        const int n = end_segment(a, s0);
-        if (n && n_merge < 2) {
-            m_n[n_merge] = n;
-            m_b[n_merge] = a.b;
-            m_kvh[n_merge] = a.kvh;
-            m_s0[n_merge] = s0;
-            ++n_merge;
+        const int n = uniform(end_segment(a, s0));
+        if (n && lane == 0) {
+            const int k = s_merge[0];
+            int *rec = s_merge + 1 + 5 * k;
+            rec[0] = n;
+            rec[1] = a.b;
+            rec[2] = a.kvh;
+            rec[3] = (int)(s0 & 0xffffffff);
+            rec[4] = (int)(s0 >> 32);
+            s_merge[0] = k + 1;
         }
     };
 
@@ -440,7 +444,13 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         gc = gn;
         ++g;
     }
-    for (int i = 0; i < n_merge; ++i) merge_pair<G>(p, m_s0[i], m_n[i], m_b[i], m_kvh[i], lane);
+    wave_lds_fence();
+    const int n_merge = uniform(s_merge[0]);
+    for (int k = 0; k < n_merge; ++k) {
+        const int *rec = s_merge + 1 + 5 * k;
+        const int64_t s0 = (int64_t)(uint32_t)uniform(rec[3]) | ((int64_t)uniform(rec[4]) << 32);
+        merge_pair<G>(p, s0, uniform(rec[0]), uniform(rec[1]), uniform(rec[2]), lane);
+    }
 }
 
 // ===================================================================
@@ -501,33 +511,77 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     const int r_lo = wave * R / WAVES, r_hi = (wave + 1) * R / WAVES;
     auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap - 16 ? 16 * r : cap - 16); };
 
-    if (n > 0) {  // prologue: angles, then rotated rows
-        for (int i = tid; i < ROT / 2; i += WAVES * 64)
-            sincos_angle((float)P * p.inv_freq[i], s_cos + i, s_sin + i);
-        __syncthreads();
-        constexpr int kRot = ROT / 16, kRow = kRot + (D - ROT) / 8;  // tasks per rotated row
-        const uint16_t *qrow = p.q + ((int64_t)b * Hq + hsub * GW) * D;
-        for (int t = tid; t < (GW + 1) * kRow + D / 8; t += WAVES * 64) {
-            const int r = t / kRow, c = t % kRow;
-            if (r > GW) {
-                const int d = 8 * (t - (GW + 1) * kRow);
-                *reinterpret_cast<uint4 *>(s_vnew + d) = ld16(p.v_new + bh * D + d);
-                continue;
-            }
-            const uint16_t *src = r < GW ? qrow + r * D : p.k_new + bh * D;
-            uint16_t *dst = s_rows + r * D;
-            if (c < kRot) {
-                const int i = 8 * c;
-                uint4 x1 = ld16(src + i), x2 = ld16(src + ROT / 2 + i);
-                rotate8(x1, x2, s_cos + i, s_sin + i, x1, x2);
-                *reinterpret_cast<uint4 *>(dst + i) = x1;
-                *reinterpret_cast<uint4 *>(dst + ROT / 2 + i) = x2;
-            } else {
-                const int d = ROT + 8 * (c - kRot);
-                *reinterpret_cast<uint4 *>(dst + d) = ld16(src + d);
-            }
+    // Prologue loads first, one 16-byte task per thread: the GW query rows
+    // and the new K row as rotary chunk pairs (dims i..i+7 and i+ROT/2..)
+    // or pass-through chunks, then the new V row; and this thread's
+    // frequency.  Being older than every K/V load, they can be waited for
+    // while the K/V loads stay in flight.  Branch-free: the row bases are
+    // wave-uniform and the two loads of a thread are unconditional.
+    constexpr int kRot = ROT / 16, kRow = kRot + (D - ROT) / 8;  // tasks per rotated row
+    constexpr int kTasks = (GW + 1) * kRow + D / 8;
+    static_assert(kTasks <= WAVES * 64 && ROT / 2 <= WAVES * 64, "one prologue task per thread");
+    const int tt = tid < kTasks ? tid : kTasks - 1;  // idle threads repeat the last task's loads
+    const int tr = tt / kRow, tc = tt % kRow;
+    const bool rotary = tr <= GW && tc < kRot;
+    const uint16_t *qbase = uniform_ptr(p.q + ((int64_t)b * Hq + hsub * GW) * D);
+    const uint16_t *kbase = uniform_ptr(p.k_new + bh * D), *vbase = uniform_ptr(p.v_new + bh * D);
+    const uint16_t *src = tr < GW ? qbase + tr * D : tr == GW ? kbase : vbase;
+    const int off = tr > GW ? 8 * (tt - (GW + 1) * kRow) : rotary ? 8 * tc : ROT + 8 * (tc - kRot);
+    const uint4 x1_in = ld16_global(src + off), x2_in = ld16_global(src + off + (rotary ? ROT / 2 : 0));
+
+    // The first round goes out before the rotation is computed (a wave
+    // without one issues a placeholder round, so that every wave has the
+    // same loads outstanding here), the second after it: measured on MI355X,
+    // both rounds ahead of the prologue delay it more than they gain.
+    uint4 kA[8], vA[8], kB[8], vB[8];
+    issue_round(kblk, vblk, r0e_of(r_lo), r_lo < r_hi ? lane : 0, kA, vA);
+    // no load above may be moved below this point (next to its use)
+    asm volatile("" ::: "memory");
+
+    // Angle i = 16 * wave + lane (lanes 0..15): the wave reads its 16
+    // frequencies with scalar loads, whose wait counter is not the vector
+    // loads' (waiting for them does not wait for the K/V rows), and each
+    // lane keeps its own.
+    static_assert(ROT / 2 <= 16 * WAVES, "16 angles per wave");
+    const int ai = 16 * uniform(wave) + (lane & 15);
+    float freq = 0.f;
+    if (16 * uniform(wave) < ROT / 2) {
+        const float4 *f4 = reinterpret_cast<const float4 *>(p.inv_freq + 16 * uniform(wave));
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 v = f4[k];
+            f[4 * k] = v.x;
+            f[4 * k + 1] = v.y;
+            f[4 * k + 2] = v.z;
+            f[4 * k + 3] = v.w;
         }
-        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if ((lane & 15) == k) freq = f[k];
+    }
+
+    // Angles, then the rotated rows into LDS.  Done for an inactive
+    // sequence too (nothing reads them then): a branch here would let the
+    // compiler move the prologue loads behind the K/V loads.
+    if (lane < 16 && ai < ROT / 2) sincos_angle((float)P * freq, s_cos + ai, s_sin + ai);
+    __syncthreads();
+    if (tid < kTasks) {
+        // the new V row (s_vnew) follows the new K row in s_rows
+        uint16_t *dst = s_rows + tr * D;
+        if (rotary) {
+            uint4 y1, y2;
+            rotate8(x1_in, x2_in, s_cos + off, s_sin + off, y1, y2);
+            *reinterpret_cast<uint4 *>(dst + off) = y1;
+            *reinterpret_cast<uint4 *>(dst + off + ROT / 2) = y2;
+        } else {
+            *reinterpret_cast<uint4 *>((tr > GW ? s_vnew : dst) + off) = x1_in;
+        }
+    }
+    __syncthreads();
+    {
+        const bool has2 = r_lo + 1 < r_hi;
+        issue_round(kblk, vblk, r0e_of(has2 ? r_lo + 1 : r_lo), has2 ? lane : 0, kB, vB);
     }
 
     WaveSoftmax<GW> st;
@@ -536,7 +590,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
         // the q operand is read from LDS for every round (registers are short)
         const uint16_t *qs = s_rows + (mrow < GW ? mrow : 0) * D + 8 * kg;
         // a round's 16 rows start at r0e = min(16 r, capacity - 16): in bounds
-        auto one = [&](int r, uint4 *kt, uint4 *vt) {
+        auto one = [&](int r, uint4 *kt, uint4 *vt) HDA_INLINE {
             bf16x8 qa[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -546,8 +600,13 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
             }
             const int r0e = r0e_of(r), lo = 16 * r - r0e, hi = n - r0e;
             const int vr = vrow - r0e, sr = srow - r0e;
-            st.template round<true>(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave], s_kt[wave], lane,
-                                    (vr >= lo && vr < hi && vr < 16) ? vr : -1, s_knew, s_vnew);
+            // only the round holding the new token's row takes the
+            // substituting form (the condition is wave-uniform)
+            if (vr >= lo && vr < hi && vr < 16)
+                st.template round<true>(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave], s_kt[wave], lane, vr,
+                                        s_knew, s_vnew);
+            else
+                st.round(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave], s_kt[wave], lane);
             if (srow >= 0 && sr >= lo && sr < hi && sr < 16) {  // keep the slot's old entry
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
@@ -557,11 +616,12 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
                     }
             }
         };
-        uint4 kA[8], vA[8], kB[8], vB[8];
         for (int r = r_lo; r < r_hi; r += 2) {
             const bool two = r + 1 < r_hi;
-            issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
-            issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+            if (r != r_lo) {
+                issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
+                issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+            }
             one(r, kA, vA);
             if (!two) break;
             one(r + 1, kB, vB);

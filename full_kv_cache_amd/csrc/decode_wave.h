@@ -52,6 +52,17 @@ __device__ __forceinline__ float lane_value(float v, int src_lane) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// A wave-uniform pointer as an opaque scalar value: selecting between such
+// pointers compiles to a register select, never to a load of the selected
+// pointer field from the kernel arguments.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
 // DPP lane moves inside each row of 16 lanes: swap neighbours, swap lane
 // pairs, mirror each half-row, mirror the row.  Applied in that order they
 // pair every lane with partners in the other quad, half-row and half, so

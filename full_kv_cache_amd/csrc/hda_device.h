@@ -4,6 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Lambdas that capture kernel arguments by reference must be inlined: an
+// out-of-line call makes the compiler copy the whole argument block to
+// scratch memory.
+#define HDA_INLINE __attribute__((always_inline))
+
 namespace hda {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -33,6 +38,13 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// A 16-byte load from a pointer known to address device (global) memory,
+// for pointers whose address space the compiler cannot see.
+__device__ __forceinline__ uint4 ld16_global(const void *p) {
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // neox RoPE of 8 consecutive dim pairs: a holds x[i .. i+7], b holds
 // x[i+h .. i+h+7] (h = rot/2), c / s the fp32 cos / sin of angles i .. i+7.
@@ -65,7 +77,9 @@ __device__ __forceinline__ void rotate8(const uint4 &a, const uint4 &b, const fl
 // by one fma: for |k| < 2^31 the dropped third term stays below 2^-70, far
 // under half an fp32 ulp.  On |r| <= pi/4 the Taylor series of sin and cos
 // to degree 17 / 18 leave errors below 2^-60; the quadrant k mod 4 picks
-// signs and swaps the two.
+// signs and swaps the two.  The Horner factors 1/((n-1) n) are constants
+// rounded once to double at compile time (a multiply, not a divide, per
+// term: the whole evaluation is a short chain of fp64 fmas).
 __device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
     constexpr double kPio2Hi = 1.5707963267948966;       // pi/2 rounded to double
     constexpr double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
@@ -77,9 +91,9 @@ __device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
     // sin r = r (1 - r^2/3! (1 - r^2/(4*5) (1 - ...))), cos likewise, Horner
     double ps = 1.0, pc = 1.0;
 #pragma unroll
-    for (int n = 17; n >= 3; n -= 2) ps = fma(-r2 / (double)((n - 1) * n), ps, 1.0);
+    for (int n = 17; n >= 3; n -= 2) ps = fma(-r2 * (1.0 / (double)((n - 1) * n)), ps, 1.0);
 #pragma unroll
-    for (int n = 18; n >= 2; n -= 2) pc = fma(-r2 / (double)((n - 1) * n), pc, 1.0);
+    for (int n = 18; n >= 2; n -= 2) pc = fma(-r2 * (1.0 / (double)((n - 1) * n)), pc, 1.0);
     const double sv = r * ps, cv = pc;
     const long q = (long)k & 3;
     const double so = q == 0 ? sv : q == 1 ? cv : q == 2 ? -sv : -cv;
