@@ -15,9 +15,9 @@
 //
 // The building block is a 16-key round for one wave and one KV head:
 //   * QK^T on the matrix cores, v_mfma_f32_16x16x32_bf16: the G query heads
-//     are the 16-row A operand (rows >= G zero), the 16 keys the B
-//     operand, fed straight from HBM with 16-byte loads (8 dims of a key row
-//     per lane): no conversion and no LDS staging for K;
+//     are the 16-row A operand (rows >= G repeat row 0, never read), the 16
+//     keys the B operand, staged through a per-wave LDS tile from row-wise
+//     16-byte loads;
 //   * an online softmax in the log2 domain: the round maximum over the 16
 //     key lanes, rescale of the running sum and output;
 //   * P.V on the vector ALUs: each half-wave streams whole 512-byte V rows
@@ -395,13 +395,22 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
         // Rounds in batches of two: both issued, then both scored (measured
         // on MI355X to stream faster here than keeping one round ahead).  An
         // odd last batch issues a placeholder second round.
+        // The q operand goes out between the first batch's two rounds, so
+        // that the first round waits for it and not for the second.
         bf16x8 qa[8];
         uint4 kA[8], vA[8], kB[8], vB[8];
-        load_q_operand<GW>(p.q, p.num_q_heads, b, hsub, lane, qa);
+        {
+            const bool two = r_lo + 1 < r_hi;
+            issue_round(kblk, vblk, r0e_of(r_lo), lane, kA, vA);
+            load_q_operand<GW>(p.q, p.num_q_heads, b, hsub, lane, qa);
+            issue_round(kblk, vblk, r0e_of(two ? r_lo + 1 : r_lo), two ? lane : 0, kB, vB);
+        }
         for (int r = r_lo; r < r_hi; r += 2) {
             const bool two = r + 1 < r_hi;
-            issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
-            issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+            if (r != r_lo) {
+                issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
+                issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+            }
             int e = r0e_of(r);
             st.round(qa, kA, vA, 16 * r - e, n - e, p.scale_log2, s_pw[wave], s_kt[wave], lane);
             if (!two) break;
@@ -489,9 +498,7 @@ hipError_t launch_stream_g(const DecodeParams &p, int waves, hipStream_t s) {
     hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(waves), dim3(64), (p.batch + 1) * sizeof(int), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)), dim3(64),
-                       0, s, p, waves);
-    return hipGetLastError();
+    return launch_stream_merge(p, waves, s);
 }
 
 }  // namespace
@@ -554,6 +561,13 @@ hipError_t launch_decode_pairs(const DecodeParams &p, int group, hipStream_t str
         case 16: return launch_pair_g<8>(p, 2, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_stream_merge(const DecodeParams &p, int waves, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)), dim3(64), 0,
+                       stream, p, waves);
+    return hipGetLastError();
 }
 
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream) {

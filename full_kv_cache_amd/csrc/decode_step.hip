@@ -286,14 +286,13 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
         return pr;
     };
     // The q operand is read from LDS for every round instead of being held
-    // in registers through the loop (rows >= G read row 0 and are zeroed).
+    // in registers through the loop (rows >= G repeat row 0, as in
+    // load_q_operand).
     const uint16_t *const q_lds = s_rows + (mrow < G ? mrow : 0) * D + 8 * kg;
     auto load_qa = [&](bf16x8 *qa) HDA_INLINE {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            uint4 u = *reinterpret_cast<const uint4 *>(q_lds + 32 * j);
-            if (mrow >= G) u = make_uint4(0, 0, 0, 0);
-            qa[j] = as_bf16x8(u);
+            qa[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(q_lds + 32 * j));
         }
     };
 
@@ -594,9 +593,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
             bf16x8 qa[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                uint4 u = *reinterpret_cast<const uint4 *>(qs + 32 * j);
-                if (mrow >= GW) u = make_uint4(0, 0, 0, 0);
-                qa[j] = as_bf16x8(u);
+                qa[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(qs + 32 * j));  // rows >= GW repeat row 0
             }
             const int r0e = r0e_of(r), lo = 16 * r - r0e, hi = n - r0e;
             const int vr = vrow - r0e, sr = srow - r0e;

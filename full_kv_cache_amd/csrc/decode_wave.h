@@ -3,8 +3,8 @@
 //
 // A 16-key round for one wave and one KV head:
 //   * QK^T on the matrix cores, v_mfma_f32_16x16x32_bf16: the G query heads
-//     are the 16-row A operand (rows >= G zero), the 16 keys the B
-//     operand.  K rows arrive like V rows -- each 16-byte load instruction
+//     are the 16-row A operand (rows >= G repeat row 0; their scores are
+//     never read), the 16 keys the B operand.  K rows arrive like V rows -- each 16-byte load instruction
 //     covers two whole 512-byte rows -- and pass through a per-wave LDS
 //     tile into the operand layout (8 dims of one key per lane): loading the
 //     operand layout straight from HBM (16 rows x 64 bytes per instruction)
@@ -94,8 +94,11 @@ __device__ __forceinline__ float row16_sum(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // MFMA A operand for KV head kvh of sequence b: lane (m = lane%16,
-// kg = lane/16) holds q[head m][32j + 8kg .. +7] for k-step j; rows m >= G
-// are zero.
+// kg = lane/16) holds q[head m][32j + 8kg .. +7] for k-step j.  Rows m >= G
+// repeat row 0: an output row of the product depends on its own A row
+// only, and the softmax never reads those heads.  (Zeroing them instead is
+// a select on the loaded values that the compiler hoists ahead of the K/V
+// loads, so the stream would wait for q.)
 template <int G>
 __device__ __forceinline__ void load_q_operand(const uint16_t *q, int num_q_heads, int b, int kvh,
                                                int lane, bf16x8 *qa) {
@@ -103,11 +106,7 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *q, int num_q_head
     const int hrow = mrow < G ? mrow : 0;
     const uint16_t *qr = q + ((int64_t)b * num_q_heads + kvh * G + hrow) * kHeadDim + 8 * kg;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint4 u = ld16(qr + 32 * j);
-        if (mrow >= G) u = make_uint4(0, 0, 0, 0);
-        qa[j] = as_bf16x8(u);
-    }
+    for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(ld16(qr + 32 * j));
 }
 
 // One wave's running softmax state over 16-key rounds.

@@ -80,28 +80,41 @@ __device__ __forceinline__ void rotate8(const uint4 &a, const uint4 &b, const fl
 // signs and swaps the two.  The Horner factors 1/((n-1) n) are constants
 // rounded once to double at compile time (a multiply, not a divide, per
 // term: the whole evaluation is a short chain of fp64 fmas).
-__device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
+struct SinCosReduced {
+    double r, r2;
+    long q;
+};
+__device__ __forceinline__ SinCosReduced sincos_reduce(float angle) {
     constexpr double kPio2Hi = 1.5707963267948966;       // pi/2 rounded to double
     constexpr double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
     constexpr double k2OverPi = 0.63661977236758134;
     const double x = (double)angle;
     const double k = rint(x * k2OverPi);
-    const double r = fma(-k, kPio2Lo, fma(-k, kPio2Hi, x));
-    const double r2 = r * r;
-    // sin r = r (1 - r^2/3! (1 - r^2/(4*5) (1 - ...))), cos likewise, Horner
-    double ps = 1.0, pc = 1.0;
-#pragma unroll
-    for (int n = 17; n >= 3; n -= 2) ps = fma(-r2 * (1.0 / (double)((n - 1) * n)), ps, 1.0);
-#pragma unroll
-    for (int n = 18; n >= 2; n -= 2) pc = fma(-r2 * (1.0 / (double)((n - 1) * n)), pc, 1.0);
-    const double sv = r * ps, cv = pc;
-    const long q = (long)k & 3;
+    SinCosReduced red;
+    red.r = fma(-k, kPio2Lo, fma(-k, kPio2Hi, x));
+    red.r2 = red.r * red.r;
+    red.q = (long)k & 3;
+    return red;
+}
+__device__ __forceinline__ void sincos_finish(const SinCosReduced &red, double ps, double pc, float *c,
+                                              float *s) {
+    const double sv = red.r * ps, cv = pc;
+    const long q = red.q;
     const double so = q == 0 ? sv : q == 1 ? cv : q == 2 ? -sv : -cv;
     const double co = q == 0 ? cv : q == 1 ? -sv : q == 2 ? -cv : sv;
     *c = (float)co;
     *s = (float)so;
 }
-
+__device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
+    const SinCosReduced red = sincos_reduce(angle);
+    // sin r = r (1 - r^2/3! (1 - r^2/(4*5) (1 - ...))), cos likewise, Horner
+    double ps = 1.0, pc = 1.0;
+#pragma unroll
+    for (int n = 17; n >= 3; n -= 2) ps = fma(-red.r2 * (1.0 / (double)((n - 1) * n)), ps, 1.0);
+#pragma unroll
+    for (int n = 18; n >= 2; n -= 2) pc = fma(-red.r2 * (1.0 / (double)((n - 1) * n)), pc, 1.0);
+    sincos_finish(red, ps, pc, c, s);
+}
 // Wave64 reductions via butterfly shuffles.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -129,6 +129,10 @@ hipError_t launch_decode_step(const StepParams &p, int group, int rotary_dim, in
                               hipStream_t stream);
 int step_wave_slots(int group, int rotary_dim);
 
+// The streaming merge alone (partials of `waves` streaming waves, prefix in
+// p.stream_pre): out / lse with the sink.
+hipError_t launch_stream_merge(const DecodeParams &p, int waves, hipStream_t stream);
+
 // Window form of the fused step (sliding layers with window <=
 // kPairMaxKeys == capacity): one workgroup per (sequence, KV head, half
 // query group); needs only the counters of StepParams.
