@@ -184,7 +184,7 @@ KERNELS = {
 }
 # Sources whose change invalidates a committed traffic measurement.
 TRAFFIC_SOURCES = ("decode_attn.hip", "decode_wave.h", "decode_step.hip", "hda_device.h",
-                   "hda_kernels.h", "hda_api.cpp")
+                   "hda_kernels.h", "hda_api.cpp", "rope_append.hip", "sparse_attn.hip")
 
 
 def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0):
