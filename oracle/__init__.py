@@ -72,6 +72,8 @@ def _load():
         lib.or_attn_chunk.argtypes = [P, P, P, i64, i64, i32, f64, P, P]
         lib.or_lse_merge.restype = None
         lib.or_lse_merge.argtypes = [P, P, i32, i32, P, P, P]
+        lib.or_output_gate.restype = None
+        lib.or_output_gate.argtypes = [P, i32, i32, i32, P]
         lib.or_sparse_decode_attn.restype = None
         lib.or_sparse_decode_attn.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, i32,
                                               P, f64, P, P]
@@ -162,8 +164,9 @@ def rope_append(q, k_new, v_new, pos, layer_type, rot, theta, window, k, v, kev,
 
 # ------------------------------------------------------------- attention
 
-def decode_attn(q, k, v, kev, vev, seq_lens, layer_type, window, sinks, scale):
-    """Returns (out fp64 [B,Hq,D], lse fp64 [B,Hq])."""
+def decode_attn(q, k, v, kev, vev, seq_lens, layer_type, window, sinks, scale, gate=None):
+    """Returns (out fp64 [B,Hq,D], lse fp64 [B,Hq]).  gate: fp32 [B,Hq] logits
+    of the per-head output gate, or None."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     kev = _u16(kev) if kev is not None else None
     vev = _u16(vev) if vev is not None else None
@@ -175,7 +178,18 @@ def decode_attn(q, k, v, kev, vev, seq_lens, layer_type, window, sinks, scale):
     lse = np.zeros((B, Hq), dtype=np.float64)
     _load().or_decode_attn(_p(q), _p(k), _p(v), _p(kev), _p(vev), _p(seq_lens), layer_type,
                            B, Hq, Hkv, D, window, cap, _p(sinks), scale, _p(out), _p(lse))
+    if gate is not None:
+        output_gate(out, gate)
     return out, lse
+
+
+def output_gate(out, gate):
+    """In place: out fp64 [B,Hq,D] times the sigmoid of gate fp32 [B,Hq]."""
+    assert out.dtype == np.float64 and out.flags.c_contiguous
+    gate = _f32(gate)
+    B, Hq, D = out.shape
+    assert gate.shape == (B, Hq)
+    _load().or_output_gate(_p(out), B, Hq, D, _p(gate))
 
 
 def attn_chunk(qh, kblk, vblk, r0, r1, scale):
@@ -187,7 +201,7 @@ def attn_chunk(qh, kblk, vblk, r0, r1, scale):
     return out, float(lse[0])
 
 
-def lse_merge(o_parts, lse_parts, sink=None):
+def lse_merge(o_parts, lse_parts, sink=None, gate=None):
     o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
     lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
     S, D = o_parts.shape
@@ -195,6 +209,8 @@ def lse_merge(o_parts, lse_parts, sink=None):
     lse = np.zeros(1, dtype=np.float64)
     sk = None if sink is None else np.array([sink], dtype=np.float32)
     _load().or_lse_merge(_p(o_parts), _p(lse_parts), S, D, _p(sk), _p(out), _p(lse))
+    if gate is not None:
+        output_gate(out.reshape(1, 1, D), np.array([[gate]], dtype=np.float32))
     return out, float(lse[0])
 
 

@@ -356,6 +356,24 @@ void or_lse_merge(const double *o_parts, const double *lse_parts, int S, int D,
     }
 }
 
+/* Per-head output gate, [SPARK] `_Layer.forward`: every query head's
+ * attention output is multiplied by that head's gate, the logistic sigmoid
+ * of its g_proj value (one value per head, broadcast over head_dim):
+ *   out[b][h][:] *= 1 / (1 + exp(-gate[b][h])).
+ * The gate does not enter lse.  out: fp64 [B, Hq, D] in place; gate: fp32
+ * logits [B, Hq].  Parity pinned: gate 0 halves out exactly, +inf leaves it
+ * bit-for-bit unchanged, -inf zeroes it, ln 3 gives 3/4 (the sign of the
+ * exponent), sigmoid(g) + sigmoid(-g) = 1, per-(b, h) indexing with B != Hq,
+ * composition with the sink. */
+void or_output_gate(double *out, int B, int Hq, int D, const float *gate) {
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hq; ++h) {
+            const double f = 1.0 / (1.0 + exp(-(double)gate[(int64_t)b * Hq + h]));
+            double *o = out + ((int64_t)b * Hq + h) * D;
+            for (int d = 0; d < D; ++d) o[d] *= f;
+        }
+}
+
 /* ------------------------------------------------------ sparse top-k */
 
 /* Sparse top-k decode with a sink, [SINK] `_bf16_flash_mla_kernel`: one
