@@ -26,7 +26,9 @@ cache: nothing is served from cache between steps.  Inputs are synthetic
 Reported: KV GB/s (attended K and V bytes per step / step time), its
 fraction of the 8 TB/s HBM peak, decode tokens/s (batch / step time), a
 roofline entry for the dominant kernel and the CPU oracle's rate on a
-bounded sample of the same workload.
+bounded sample of the same workload; also the same step with the per-head
+output gate (Spark export page, `_Layer.forward`) applied in every
+attention epilogue (gated_ms_per_step).
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
                     [--path auto|fused|separate]
@@ -113,6 +115,11 @@ class Workload:
                 sinks=workloads.sinks(g, s.num_q_heads, dev),
                 out=torch.empty(B, s.num_q_heads, s.head_dim, dtype=torch.bfloat16, device=dev),
                 lse=torch.empty(B, s.num_q_heads, dtype=torch.float32, device=dev)))
+        # output-gate logits from a generator of their own (the draws above
+        # stay what they were)
+        gg = workloads.generator(seed + 2, dev)
+        for L in self.layers:
+            L["gate"] = workloads.gate_logits(gg, B, s.num_q_heads, dev)
         self.scale = 1.0 / s.head_dim ** 0.5
         ws = max(max(hda.hda_decode_workspace_bytes(L["cache"], L["lt"], self.max_seq_len, 0),
                      hda.hda_decode_step_workspace_bytes(L["cache"], L["lt"])) for L in self.layers)
@@ -123,19 +130,21 @@ class Workload:
                      for lt in (workloads.SLIDING, workloads.FULL)}
         self.kv_bytes = sum(self.rows[lt] for lt in self.types) * self.kv_row_bytes
 
-    def layer_call(self, L, path="auto", chunk_keys=0):
+    def layer_call(self, L, path="auto", chunk_keys=0, gate=False):
         import full_kv_cache_amd as hda
+        g = L["gate"] if gate else None
         if layer_path(path, L["lt"]) == "fused":
             hda.hda_decode_step(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"],
-                                L["sinks"], self.scale, L["out"], L["lse"], self.workspace)
+                                L["sinks"], self.scale, L["out"], L["lse"], self.workspace, gate=g)
         else:
             hda.hda_rope_append(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"])
             hda.hda_decode_attn(L["q"], L["cache"], self.seq_lens, L["lt"], L["sinks"], self.scale,
-                                L["out"], L["lse"], self.max_seq_len, chunk_keys, self.workspace)
+                                L["out"], L["lse"], self.max_seq_len, chunk_keys, self.workspace,
+                                gate=g)
 
-    def step(self, path="auto", chunk_keys=0):
+    def step(self, path="auto", chunk_keys=0, gate=False):
         for L in self.layers:
-            self.layer_call(L, path, chunk_keys)
+            self.layer_call(L, path, chunk_keys, gate)
 
 
 def time_graph(fn, steps, warmup, use_graph=True):
@@ -390,6 +399,9 @@ def main():
     eager_ms = None
     if not args.no_graph:
         eager_ms, _ = time_graph(step, max(3, args.steps // 5), 2, use_graph=False)
+    # the same step with the per-head output gate applied in every epilogue
+    gated_ms, _ = time_graph(lambda: wl.step(args.path, args.chunk_keys, gate=True), args.steps,
+                             args.warmup, use_graph=not args.no_graph)
     print("# timing the layer kernels", file=sys.stderr, flush=True)
     import workloads
     k_slide = layer_kernel(wl, workloads.SLIDING, args.steps, args.warmup, args.path, args.chunk_keys)
@@ -423,6 +435,7 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": wl.kv_bytes,
         "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
+        "gated_ms_per_step": round(gated_ms, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": roof, "layer_kernels": {"sliding": k_slide, "full": k_full},
         "cpu_baseline": cpu, "sparse": sparse,

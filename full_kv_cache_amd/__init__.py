@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.hda_decode_workspace_bytes.restype = sz
         L.hda_decode_workspace_bytes.argtypes = [D, ctypes.c_int, i32, i32]
         L.hda_decode_attn.restype = ctypes.c_int
-        L.hda_decode_attn.argtypes = [P, D, P, ctypes.c_int, P, ctypes.c_float, P, P, i32, i32,
+        L.hda_decode_attn.argtypes = [P, D, P, ctypes.c_int, P, P, ctypes.c_float, P, P, i32, i32,
                                       P, sz, P]
         L.hda_decode_split_plan.restype = ctypes.c_int
         L.hda_decode_split_plan.argtypes = [D, ctypes.c_int, i32, i32, ctypes.POINTER(i32),
@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.hda_decode_attn_partials.argtypes = [P, D, P, ctypes.c_int, ctypes.c_float, i32, i32,
                                                P, P, P]
         L.hda_lse_merge.restype = ctypes.c_int
-        L.hda_lse_merge.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
+        L.hda_lse_merge.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P]
         L.hda_status_string.restype = ctypes.c_char_p
         L.hda_status_string.argtypes = [ctypes.c_int]
         L.hda_last_error_message.restype = ctypes.c_char_p
@@ -86,7 +86,8 @@ def lib() -> ctypes.CDLL:
         L.hda_decode_step_workspace_bytes.restype = sz
         L.hda_decode_step_workspace_bytes.argtypes = [D, ctypes.c_int]
         L.hda_decode_step.restype = ctypes.c_int
-        L.hda_decode_step.argtypes = [P, P, P, P, ctypes.c_int, D, P, ctypes.c_float, P, P, P, sz, P]
+        L.hda_decode_step.argtypes = [P, P, P, P, ctypes.c_int, D, P, P, ctypes.c_float, P, P, P, sz,
+                                      P]
         L.hda_sparse_workspace_bytes.restype = ctypes.c_size_t
         L.hda_sparse_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.hda_sparse_decode_attn.restype = ctypes.c_int
@@ -159,15 +160,34 @@ def validate_sinks(sinks: Optional[torch.Tensor], q: torch.Tensor) -> None:
         raise ValueError(f"sinks and q must be on the same device, got {sinks.device} and {q.device}")
 
 
+def validate_gate(gate: Optional[torch.Tensor], out: torch.Tensor) -> None:
+    """Per-head output-gate logits (Spark export page, `_Layer.forward`: one
+    g_proj value per query head): fp32, shape (batch, num_heads), on out's
+    device, contiguous."""
+    if gate is None:
+        return
+    if gate.dtype != torch.float32:
+        raise ValueError(f"gate must have dtype torch.float32, got {gate.dtype}")
+    want = tuple(out.shape[:2])
+    if tuple(gate.shape) != want:
+        raise ValueError(f"gate must have shape {want}, got {tuple(gate.shape)}")
+    if gate.device != out.device:
+        raise ValueError(f"gate and out must be on the same device, got {gate.device} and {out.device}")
+    if not gate.is_contiguous():
+        raise ValueError("gate must be contiguous")
+
+
 def hda_decode_attn(q, cache: LayerCache, seq_lens, layer_type: int, sinks, scale: float, out,
                     lse=None, max_seq_len: int = 0, chunk_keys: int = 0, workspace=None,
-                    stream=None):
-    """Decode attention of one layer (after hda_rope_append)."""
+                    stream=None, gate=None):
+    """Decode attention of one layer (after hda_rope_append); gate: optional
+    fp32 [B, Hq] output-gate logits."""
     validate_sinks(sinks, q)
+    validate_gate(gate, out)
     d = cache.desc()
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hda_decode_attn(_ptr(q), ctypes.byref(d), _ptr(seq_lens), int(layer_type),
-                                 _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                                 _ptr(sinks), _ptr(gate), float(scale), _ptr(out), _ptr(lse),
                                  int(max_seq_len), int(chunk_keys), _ptr(workspace), wbytes,
                                  _stream(stream)))
 
@@ -192,13 +212,14 @@ def hda_decode_attn_partials(q, cache: LayerCache, seq_lens, layer_type: int, sc
                                           _stream(stream)))
 
 
-def hda_lse_merge(part_o, part_lse, sinks, out, lse=None, stream=None):
-    """Merge partials [B,H,nsplit,D] / [B,H,nsplit] into out bf16 [B,H,D] (+ sink)."""
+def hda_lse_merge(part_o, part_lse, sinks, out, lse=None, stream=None, gate=None):
+    """Merge partials [B,H,nsplit,D] / [B,H,nsplit] into out bf16 [B,H,D] (+ sink, gate)."""
     B, H, S, D = part_o.shape
     if sinks is not None:
         validate_sinks(sinks, out)
+    validate_gate(gate, out)
     _check(lib().hda_lse_merge(_ptr(part_o), _ptr(part_lse), int(B), int(H), int(S), int(D),
-                               _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream)))
+                               _ptr(sinks), _ptr(gate), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def hda_decode_step_workspace_bytes(cache: LayerCache, layer_type: int) -> int:
@@ -207,14 +228,17 @@ def hda_decode_step_workspace_bytes(cache: LayerCache, layer_type: int) -> int:
 
 
 def hda_decode_step(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, sinks, scale: float,
-                    out, lse=None, workspace=None, stream=None):
+                    out, lse=None, workspace=None, stream=None, gate=None):
     """RoPE + append + attention of one layer in one launch (q is not modified).
-    The workspace must be zero-filled before its first use."""
+    The workspace must be zero-filled before its first use; gate: optional
+    fp32 [B, Hq] output-gate logits."""
     validate_sinks(sinks, q)
+    validate_gate(gate, out)
     d = cache.desc()
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hda_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), int(layer_type),
-                                 ctypes.byref(d), _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                                 ctypes.byref(d), _ptr(sinks), _ptr(gate), float(scale), _ptr(out),
+                                 _ptr(lse),
                                  _ptr(workspace), wbytes, _stream(stream)))
 
 

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
         if (FINAL) {
             float f = 1.f;
             if (p.sinks) f = 1.f / (1.f + expf(p.sinks[hq] - lse));
+            if (p.gate) f *= gate_factor(p.gate[(int64_t)b * Hq + hq]);
             p.out[((int64_t)b * Hq + hq) * D + d] = f32_to_bf16(on * f);
             if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
         } else {
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(kDecodeThreads) void lse_merge_kernel(MergeParams p
     const float lse = M + logf(L);
     float f = 1.f;
     if (p.sinks) f = 1.f / (1.f + expf(p.sinks[hq] - lse));
+    if (p.gate) f *= gate_factor(p.gate[row]);
     *outp = f32_to_bf16((o / L) * f);
     if (d == 0 && p.lse) p.lse[row] = lse;
 }
@@ -349,6 +351,7 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W)
     const float lse = M + logf(L);
     float f = 1.f / L;
     if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+    if (p.gate) f *= gate_factor(p.gate[row]);
     const uint32_t lo = (uint32_t)f32_to_bf16(o.x * f) | ((uint32_t)f32_to_bf16(o.y * f) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(o.z * f) | ((uint32_t)f32_to_bf16(o.w * f) << 16);
     *reinterpret_cast<uint2 *>(outp) = make_uint2(lo, hi);
@@ -461,6 +464,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
         const float lse = (M + log2f(L)) * kLn2;
         float f = 1.f / L;
         if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        if (p.gate) f *= gate_factor(p.gate[(int64_t)b * Hq + hq]);
         *outp = f32_to_bf16(o * f);
         if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
     }

@@ -106,6 +106,7 @@ __device__ __forceinline__ void store_final(const WaveSoftmax<G> &st, const Step
         const float lse = (m_h[h] + log2f(l)) * kLn2;
         float f = 1.f / l;
         if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        if (p.gate) f *= gate_factor(p.gate[(int64_t)b * p.num_q_heads + hq]);
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -178,6 +179,7 @@ __device__ __forceinline__ void merge_pair(const StepParams &p, int64_t s0, int 
         const float lse = M[h] + logf(L[h]);
         float f = 1.f / L[h];
         if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        if (p.gate) f *= gate_factor(p.gate[(int64_t)b * p.num_q_heads + hq]);
         const int64_t row = (int64_t)b * p.num_q_heads + hq;
         const uint32_t lo = (uint32_t)f32_to_bf16(o[h].x * f) | ((uint32_t)f32_to_bf16(o[h].y * f) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16(o[h].z * f) | ((uint32_t)f32_to_bf16(o[h].w * f) << 16);
@@ -675,6 +677,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
         const float lse = (M + log2f(L)) * kLn2;
         float f = 1.f / L;
         if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        if (p.gate) f *= gate_factor(p.gate[(int64_t)b * Hq + hq]);
         *outp = f32_to_bf16(o * f);
         if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
     }

@@ -392,6 +392,14 @@ hda_status check_decode_io(const void *q, const int32_t *seq_lens, float scale) 
     return HDA_OK;
 }
 
+// Optional fp32 arrays (sinks, gate logits, lse out): NULL or 4-byte aligned.
+hda_status check_f32_ptrs(const float *sinks, const float *gate, const float *lse) {
+    auto bad = [](const float *x) { return x && (reinterpret_cast<uintptr_t>(x) & 3u); };
+    if (bad(sinks) || bad(gate) || bad(lse))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "sinks, gate and lse must be 4-byte aligned");
+    return HDA_OK;
+}
+
 hda_status launched(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(HDA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
     return ok();
@@ -413,12 +421,13 @@ hda_status hda_decode_split_plan(const hda_cache_desc *cache, hda_layer_type lay
 }
 
 hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int32_t *seq_lens,
-                           hda_layer_type layer, const float *sinks, float scale, void *out,
-                           float *lse, int32_t max_seq_len, int32_t chunk_keys, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+                           hda_layer_type layer, const float *sinks, const float *gate, float scale,
+                           void *out, float *lse, int32_t max_seq_len, int32_t chunk_keys,
+                           void *workspace, size_t workspace_bytes, void *stream) {
     hda_status st = check_decode_shape(cache, layer, max_seq_len, chunk_keys);
     if (st != HDA_OK) return st;
     if ((st = check_decode_io(q, seq_lens, scale)) != HDA_OK) return st;
+    if ((st = check_f32_ptrs(sinks, gate, lse)) != HDA_OK) return st;
     if (!out || !aligned16(out))
         return fail(HDA_ERR_INVALID_ARGUMENT, "out must be non-NULL and 16-byte aligned");
     if (cache->batch == 0) return ok();
@@ -429,6 +438,7 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
         Plan one{hda::kMaxChunk, 1};
         hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, one);
         p.sinks = sinks;
+        p.gate = gate;
         p.out = static_cast<uint16_t *>(out);
         p.lse = lse;
         return launched(hda::launch_decode_pairs(p, g, s), "decode");
@@ -449,6 +459,7 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
         p.part_lse = reinterpret_cast<float *>(ws + L.lse_off);
         p.stream_pre = reinterpret_cast<int *>(ws + L.pre_off);
         p.sinks = sinks;
+        p.gate = gate;
         p.out = static_cast<uint16_t *>(out);
         p.lse = lse;
         return launched(hda::launch_decode_stream(p, g, waves, s), "decode");
@@ -464,6 +475,7 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
 
     hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, pl);
     p.sinks = sinks;
+    p.gate = gate;
     p.out = static_cast<uint16_t *>(out);
     p.lse = lse;
     if (pl.nsplit == 1)
@@ -479,6 +491,7 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     m.part_o = p.part_o;
     m.part_lse = p.part_lse;
     m.sinks = sinks;
+    m.gate = gate;
     m.out = p.out;
     m.lse = lse;
     m.batch = cache->batch;
@@ -509,7 +522,7 @@ hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
 
 hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t batch,
                          int32_t num_heads, int32_t nsplit, int32_t head_dim, const float *sinks,
-                         void *out, float *lse, void *stream) {
+                         const float *gate, void *out, float *lse, void *stream) {
     if (batch < 0 || num_heads <= 0 || nsplit < 1)
         return fail(HDA_ERR_INVALID_ARGUMENT, "need batch >= 0, num_heads > 0, nsplit >= 1");
     if (head_dim != hda::kHeadDim)
@@ -517,11 +530,14 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
                     hda::kHeadDim, head_dim);
     if (!part_o || !part_lse || !out)
         return fail(HDA_ERR_INVALID_ARGUMENT, "part_o, part_lse and out must be non-NULL");
+    hda_status st = check_f32_ptrs(sinks, gate, lse);
+    if (st != HDA_OK) return st;
     if (batch == 0) return ok();
     hda::MergeParams m{};
     m.part_o = part_o;
     m.part_lse = part_lse;
     m.sinks = sinks;
+    m.gate = gate;
     m.out = static_cast<uint16_t *>(out);
     m.lse = lse;
     m.batch = batch;
@@ -538,7 +554,7 @@ size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_ty
 
 hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, const int32_t *pos,
                            hda_layer_type layer, const hda_cache_desc *cache, const float *sinks,
-                           float scale, void *out, float *lse, void *workspace,
+                           const float *gate, float scale, void *out, float *lse, void *workspace,
                            size_t workspace_bytes, void *stream) {
     hda_status st = check_step_shape(cache, layer);
     if (st != HDA_OK) return st;
@@ -546,9 +562,9 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
         return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new, pos and out must be non-NULL");
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
         return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new and out must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(pos) & 3u) || (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)) ||
-        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-        return fail(HDA_ERR_INVALID_ARGUMENT, "pos, sinks and lse must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(pos) & 3u)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "pos must be 4-byte aligned");
+    if ((st = check_f32_ptrs(sinks, gate, lse)) != HDA_OK) return st;
     if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
     const bool window = use_window_step(cache, layer);
     const int waves = window ? 0 : step_waves(cache, layer);
@@ -567,6 +583,7 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
     p.k = static_cast<uint16_t *>(cache->k);
     p.v = static_cast<uint16_t *>(cache->v);
     p.sinks = sinks;
+    p.gate = gate;
     p.out = static_cast<uint16_t *>(out);
     p.lse = lse;
     char *ws = static_cast<char *>(workspace);

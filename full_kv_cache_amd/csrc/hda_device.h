@@ -115,6 +115,11 @@ __device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
     for (int n = 18; n >= 2; n -= 2) pc = fma(-red.r2 * (1.0 / (double)((n - 1) * n)), pc, 1.0);
     sincos_finish(red, ps, pc, c, s);
 }
+// Factor of the per-head output gate: the logistic sigmoid of its logit
+// (Spark export page, `_Layer.forward`: sigmoid of g_proj, one value per
+// query head, multiplying that head's attention output).
+__device__ __forceinline__ float gate_factor(float logit) { return 1.f / (1.f + expf(-logit)); }
+
 // Wave64 reductions via butterfly shuffles.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -32,6 +32,7 @@ struct DecodeParams {
     const uint16_t *k, *v;      // [B, Hkv, cap, D]
     const int32_t *seq_lens;    // [B]
     const float *sinks;         // [Hq] or null
+    const float *gate;          // [B, Hq] output-gate logits or null
     uint16_t *out;              // [B, Hq, D]
     float *lse;                 // [B, Hq] or null
     float *part_o;              // [B, Hq, S, D]
@@ -53,6 +54,7 @@ struct StepParams {
     const int32_t *pos;         // [B]
     uint16_t *k, *v;            // [B, Hkv, cap, D]
     const float *sinks;         // [Hq] or null
+    const float *gate;          // [B, Hq] output-gate logits or null
     uint16_t *out;              // [B, Hq, D]
     float *lse;                 // [B, Hq] or null
     float *part_o;              // [slots, G, D], slot = wave + pair
@@ -69,6 +71,7 @@ struct MergeParams {
     const float *part_o;        // [B, H, nsplit, D]
     const float *part_lse;      // [B, H, nsplit]
     const float *sinks;         // [H] or null
+    const float *gate;          // [B, H] output-gate logits or null
     uint16_t *out;              // [B, H, D]
     float *lse;                 // [B, H] or null
     int batch, num_heads, nsplit;

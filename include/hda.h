@@ -139,7 +139,10 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
  * sum p v.  lse = ln sum exp(scores), before any sink.  With sinks, out is
  * multiplied by exp(lse)/(exp(lse)+exp(sink[h])) (flashmla_sparse page,
  * `HYV4FlashMLASparseImpl` docstring); a -inf sink leaves out bit-for-bit
- * unchanged (`_sinks_for_query`: -inf is a no-op sink).
+ * unchanged (`_sinks_for_query`: -inf is a no-op sink).  With gate, out of
+ * head h of sequence b is also multiplied by 1/(1+exp(-gate[b][h])) (Spark
+ * export page, `_Layer.forward`: the sigmoid of g_proj, one value per query
+ * head, multiplies that head's attention output); lse is not affected.
  *
  * The keys are split into pieces whose partial softmax results (out, lse)
  * land in the workspace; a merge kernel combines them, lse = ln sum_c
@@ -153,6 +156,7 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
  *   q          bf16 [batch, num_q_heads, head_dim] (already rotated)
  *   seq_lens   int32 [batch] (device); n <= 0 gives out 0, lse -inf
  *   sinks      fp32 [num_q_heads] (device) or NULL
+ *   gate       fp32 [batch, num_q_heads] (device) output-gate logits, or NULL
  *   scale      softmax scale
  *   out        bf16 [batch, num_q_heads, head_dim]
  *   lse        fp32 [batch, num_q_heads] or NULL
@@ -170,8 +174,8 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
  */
 hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache,
                            const int32_t *seq_lens, hda_layer_type layer,
-                           const float *sinks, float scale, void *out, float *lse,
-                           int32_t max_seq_len, int32_t chunk_keys,
+                           const float *sinks, const float *gate, float scale, void *out,
+                           float *lse, int32_t max_seq_len, int32_t chunk_keys,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -194,7 +198,7 @@ hda_status hda_decode_split_plan(const hda_cache_desc *cache, hda_layer_type lay
  * and merged online equals the single pass.  Same arguments as
  * hda_decode_attn; part_o fp32 [batch, num_q_heads, nsplit, head_dim],
  * part_lse fp32 [batch, num_q_heads, nsplit], nsplit from
- * hda_decode_split_plan.  No sink is applied here.
+ * hda_decode_split_plan.  No sink or gate is applied here.
  */
 hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
                                     const int32_t *seq_lens, hda_layer_type layer,
@@ -205,17 +209,21 @@ hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
  * hda_lse_merge -- combine per-chunk partials into the attention output:
  *   lse = ln sum_c exp(part_lse_c),  out = sum_c exp(part_lse_c - lse) part_o_c,
  * chunks with part_lse = -inf weigh zero; then the sink factor
- * exp(lse)/(exp(lse)+exp(sink[h])) (flashmla_sparse page, class docstring).
+ * exp(lse)/(exp(lse)+exp(sink[h])) (flashmla_sparse page, class docstring)
+ * and the output gate 1/(1+exp(-gate[b][h])) (Spark export page,
+ * `_Layer.forward`).
  * No chunk holding keys: out 0, lse -inf.  Partials from several devices
  * (context parallelism) merge the same way once gathered.
  *   part_o   fp32 [batch, num_heads, nsplit, head_dim] (head_dim == 256)
  *   part_lse fp32 [batch, num_heads, nsplit]
- *   sinks    fp32 [num_heads] or NULL; out bf16 [batch, num_heads, head_dim];
+ *   sinks    fp32 [num_heads] or NULL; gate fp32 [batch, num_heads] logits or
+ *            NULL; out bf16 [batch, num_heads, head_dim];
  *   lse      fp32 [batch, num_heads] or NULL (pre-sink).
  */
 hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t batch,
                          int32_t num_heads, int32_t nsplit, int32_t head_dim,
-                         const float *sinks, void *out, float *lse, void *stream);
+                         const float *sinks, const float *gate, void *out, float *lse,
+                         void *stream);
 
 /*
  * hda_decode_step_workspace_bytes -- device workspace hda_decode_step needs
@@ -237,7 +245,7 @@ size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_ty
  * hda_decode_attn (flashmla_sparse page, class docstring).
  *
  *   q, k_new, v_new, pos, layer, cache   as hda_rope_append
- *   sinks, scale, out, lse               as hda_decode_attn
+ *   sinks, gate, scale, out, lse         as hda_decode_attn
  *   workspace  device buffer of at least hda_decode_step_workspace_bytes()
  *              bytes.  Its first 4*batch*num_kv_heads bytes (rounded up to
  *              256) are arrival counters that must be zero before the first
@@ -250,9 +258,9 @@ size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_ty
  */
 hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
                            const int32_t *pos, hda_layer_type layer,
-                           const hda_cache_desc *cache, const float *sinks, float scale,
-                           void *out, float *lse, void *workspace, size_t workspace_bytes,
-                           void *stream);
+                           const hda_cache_desc *cache, const float *sinks,
+                           const float *gate, float scale, void *out, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * hda_sparse_workspace_bytes -- device workspace hda_sparse_decode_attn needs

@@ -62,16 +62,16 @@ class HybridCase:
         return k, v
 
     # ---------------------------------------------------------- oracle side
-    def oracle_step(self, sinks=None, scale=1 / 16):
+    def oracle_step(self, sinks=None, scale=1 / 16, gate=None):
         """Append then attention in the oracle; returns the block-form host
-        state after the append, out and lse."""
+        state after the append, out and lse.  gate: fp32 [B, Hq] logits."""
         h = {k: v.copy() for k, v in self.host.items()}
         s = self.shape
         k, v, kev, vev = self.to_oracle(h)
         oracle.rope_append(h["q"], h["k_new"], h["v_new"], self.pos, self.lt, s.rot(self.lt),
                            s.theta(self.lt), s.window, k, v, kev, vev)
         out, lse = oracle.decode_attn(h["q"], k, v, kev, vev, self.seq_lens, self.lt, s.window,
-                                      sinks, scale)
+                                      sinks, scale, gate=gate)
         h["k"], h["v"] = self.from_oracle(k, v, kev, vev)
         return h, out, lse
 
@@ -86,7 +86,7 @@ class HybridCase:
                               s.theta(self.lt))
 
     def gpu_step(self, sinks=None, scale=1 / 16, chunk_keys=0, max_seq_len=None, d=None,
-                 append=True):
+                 append=True, gate=None):
         import full_kv_cache_amd as hda
         d = d or self.device()
         cache = self.cache(d)
@@ -102,12 +102,14 @@ class HybridCase:
                          device="cuda")
         lse = torch.full((s.batch, s.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
         sk = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).cuda()
-        hda.hda_decode_attn(d["q"], cache, seq, self.lt, sk, scale, out, lse, msl, chunk_keys, ws)
+        gt = None if gate is None else torch.as_tensor(gate, dtype=torch.float32).cuda()
+        hda.hda_decode_attn(d["q"], cache, seq, self.lt, sk, scale, out, lse, msl, chunk_keys, ws,
+                            gate=gt)
         torch.cuda.synchronize()
         return d, out, lse
 
 
-def fused_step(case: "HybridCase", sinks=None, scale=1 / 16, d=None, workspace=None):
+def fused_step(case: "HybridCase", sinks=None, scale=1 / 16, d=None, workspace=None, gate=None):
     """hda_decode_step on the case's device tensors (q is not modified)."""
     import full_kv_cache_amd as hda
     d = d or case.device()
@@ -121,8 +123,9 @@ def fused_step(case: "HybridCase", sinks=None, scale=1 / 16, d=None, workspace=N
                      device="cuda")
     lse = torch.full((s.batch, s.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
     sk = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).cuda()
+    gt = None if gate is None else torch.as_tensor(gate, dtype=torch.float32).cuda()
     hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], pos, case.lt, cache, sk, scale, out, lse,
-                        workspace)
+                        workspace, gate=gt)
     torch.cuda.synchronize()
     return d, out, lse
 

@@ -60,7 +60,7 @@ def _decode(desc, layer=hda.SLIDING, max_seq_len=512, chunk=0, q=FAKE, out=FAKE,
             scale=0.0625):
     L = hda.lib()
     return L.hda_decode_attn(ctypes.c_void_p(q), ctypes.byref(desc), ctypes.c_void_p(FAKE), layer,
-                             None, scale, ctypes.c_void_p(out), None, max_seq_len, chunk,
+                             None, None, scale, ctypes.c_void_p(out), None, max_seq_len, chunk,
                              ctypes.c_void_p(ws) if ws else None, wsb, None)
 
 
@@ -209,7 +209,7 @@ def test_sparse_sink_validation_in_binding():
 def _step(desc, layer=hda.SLIDING, q=FAKE, ws=None, wsb=0, scale=0.0625):
     L = hda.lib()
     return L.hda_decode_step(ctypes.c_void_p(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
-                             ctypes.c_void_p(FAKE), layer, ctypes.byref(desc), None, scale,
+                             ctypes.c_void_p(FAKE), layer, ctypes.byref(desc), None, None, scale,
                              ctypes.c_void_p(FAKE), None, ctypes.c_void_p(ws) if ws else None, wsb,
                              None)
 
@@ -242,3 +242,35 @@ def test_step_workspace():
     assert _step(d, ws=FAKE + 4, wsb=need) == 1
     assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(rotary_dim=128)), hda.SLIDING) == 0
     assert _step(_desc(batch=0), ws=FAKE, wsb=need) == 0  # nothing to do
+
+
+# ------------------------------------------------------------ output gate
+def test_gate_pointer_alignment():
+    """A misaligned gate pointer is refused before anything is enqueued."""
+    L = hda.lib()
+    r = L.hda_decode_attn(ctypes.c_void_p(FAKE), ctypes.byref(_desc()), ctypes.c_void_p(FAKE),
+                          hda.SLIDING, None, ctypes.c_void_p(FAKE + 2), 0.0625, ctypes.c_void_p(FAKE),
+                          None, 512, 0, None, 0, None)
+    assert r == 1 and "gate" in _msg()
+    r = L.hda_lse_merge(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 2, 8, 2, 256, None,
+                        ctypes.c_void_p(FAKE + 1), ctypes.c_void_p(FAKE), None, None)
+    assert r == 1 and "gate" in _msg()
+    r = L.hda_decode_step(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                          ctypes.c_void_p(FAKE), hda.SLIDING, ctypes.byref(_desc()), None,
+                          ctypes.c_void_p(FAKE + 2), 0.0625, ctypes.c_void_p(FAKE), None, None, 0,
+                          None)
+    assert r == 1 and "gate" in _msg()
+
+
+def test_gate_binding_checks():
+    """The binding checks the gate's dtype, shape and device like the sinks'."""
+    q = torch.zeros(2, 8, 256, dtype=torch.bfloat16)
+    out = torch.zeros(2, 8, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dtype"):
+        hda.validate_gate(torch.zeros(2, 8, dtype=torch.float16), out)
+    with pytest.raises(ValueError, match="shape"):
+        hda.validate_gate(torch.zeros(8, dtype=torch.float32), out)
+    with pytest.raises(ValueError, match="contiguous"):
+        hda.validate_gate(torch.zeros(8, 2, dtype=torch.float32).t(), out)
+    hda.validate_gate(torch.zeros(2, 8, dtype=torch.float32), out)
+    hda.validate_gate(None, q)

@@ -89,6 +89,11 @@ def sinks(gen: torch.Generator, num_heads: int, device="cpu") -> torch.Tensor:
     return torch.randn(num_heads, generator=gen, device=device, dtype=torch.float32)
 
 
+def gate_logits(gen: torch.Generator, batch: int, num_heads: int, device="cpu") -> torch.Tensor:
+    """Synthetic g_proj outputs for the per-head output gate: N(0, 1) fp32 [B, Hq]."""
+    return torch.randn(batch, num_heads, generator=gen, device=device, dtype=torch.float32)
+
+
 @dataclass(frozen=True)
 class SparseShape:
     tokens: int = 32
