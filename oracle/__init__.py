@@ -74,6 +74,8 @@ def _load():
         lib.or_lse_merge.argtypes = [P, P, i32, i32, P, P, P]
         lib.or_output_gate.restype = None
         lib.or_output_gate.argtypes = [P, i32, i32, i32, P]
+        lib.or_page_gather.restype = None
+        lib.or_page_gather.argtypes = [P, P, i32, i32, i32, i32, i32, i64, P]
         lib.or_sparse_decode_attn.restype = None
         lib.or_sparse_decode_attn.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, i32,
                                               P, f64, P, P]
@@ -190,6 +192,18 @@ def output_gate(out, gate):
     B, Hq, D = out.shape
     assert gate.shape == (B, Hq)
     _load().or_output_gate(_p(out), B, Hq, D, _p(gate))
+
+
+def page_gather(pool, block_table):
+    """Paged pool bf16 [num_pages, Hkv, page_size, D] + block_table int32
+    [B, max_pages] -> contiguous bf16 [B, Hkv, max_pages*page_size, D]."""
+    pool, bt = _u16(pool), _i32(block_table)
+    num_pages, Hkv, page_size, D = pool.shape
+    B, max_pages = bt.shape
+    out = np.zeros((B, Hkv, max_pages * page_size, D), dtype=np.uint16)
+    _load().or_page_gather(_p(pool), _p(bt), B, Hkv, D, page_size, max_pages, num_pages,
+                           _p(out))
+    return out
 
 
 def attn_chunk(qh, kblk, vblk, r0, r1, scale):

@@ -374,6 +374,41 @@ void or_output_gate(double *out, int B, int Hq, int D, const float *gate) {
         }
 }
 
+/* ---------------------------------------------------------- paged KV */
+
+/* Paged cache addressing, [SINK] `_fp8_flash_mla_kernel`: the attention
+ * call takes a block table and per-sequence cache lengths, i.e. each
+ * sequence's rows live in fixed-size pages of a shared pool.  Reading (the
+ * page's own layout is not printed; this is the plain one): row r of
+ * sequence b is row r % page_size of pool page block_table[b][r / page_size].
+ * Copies every sequence's rows 0 .. max_pages*page_size-1 out of the pool
+ * into contiguous blocks, so that every other oracle function runs
+ * unchanged on a paged cache.
+ *   pool  bf16 [num_pages, Hkv, page_size, D]
+ *   bt    int32 [B, max_pages]; an entry outside [0, num_pages) leaves its
+ *         rows zero (no caller reads them)
+ *   out   bf16 [B, Hkv, max_pages*page_size, D]
+ * Parity pinned: a one-page-per-sequence table with the pool holding the
+ * blocks in order is the identity; element-by-element brute force on a tiny
+ * case; relabelling pool pages (permuting pool and table together) leaves
+ * the result unchanged; each row lands at its page/offset position. */
+void or_page_gather(const uint16_t *pool, const int32_t *bt, int B, int Hkv, int D,
+                    int page_size, int max_pages, int64_t num_pages, uint16_t *out) {
+    const int64_t cap = (int64_t)max_pages * page_size;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h)
+            for (int64_t r = 0; r < cap; ++r) {
+                uint16_t *dst = out + (((int64_t)b * Hkv + h) * cap + r) * D;
+                const int32_t pg = bt[(int64_t)b * max_pages + r / page_size];
+                if (pg < 0 || pg >= num_pages) {
+                    memset(dst, 0, (size_t)D * sizeof(uint16_t));
+                    continue;
+                }
+                const uint16_t *src = pool + (((int64_t)pg * Hkv + h) * page_size + r % page_size) * D;
+                memcpy(dst, src, (size_t)D * sizeof(uint16_t));
+            }
+}
+
 /* ------------------------------------------------------ sparse top-k */
 
 /* Sparse top-k decode with a sink, [SINK] `_bf16_flash_mla_kernel`: one
