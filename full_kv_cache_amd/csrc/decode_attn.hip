@@ -194,9 +194,10 @@ __global__ __launch_bounds__(kDecodeThreads) void lse_merge_kernel(MergeParams p
 //
 // Pair p = (b, kvh) holds R_b = ceil(n_b / 16) rounds of 16 keys; all
 // rounds, pair after pair, form one index space of R_tot rounds.  Wave w of
-// the W-wave grid (every wave resident at once) takes rounds
+// the W-wave grid (every wave resident at once; W is cut to R_tot when the
+// lengths hold fewer rounds than the grid has waves) takes rounds
 // [w*R_tot/W, (w+1)*R_tot/W): each wave streams the same number of keys
-// (+-16) whatever the length mix.  A wave's range is cut at pair boundaries
+// (+-16) whatever the length mix, and no wave's range is empty.  A wave's range is cut at pair boundaries
 // into segments; each leaves one partial in slot w + p -- unique, because
 // the (wave, pair) overlaps are ordered the same way along both indices.
 // Rounds are pipelined two deep: the next round's 16 loads are in flight
@@ -226,8 +227,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     if (w == 0)  // published for the merge kernel
         for (int b = lane; b <= B; b += 64) p.stream_pre[b] = s_pre[b];
     const int64_t r_tot = (int64_t)Hkv * s_pre[B];
-    const int64_t g0 = (int64_t)w * r_tot / W, g1 = (int64_t)(w + 1) * r_tot / W;
-    if (g0 >= g1) return;
+    const int We = split_waves(W, r_tot);
+    if (w >= We) return;
+    const int64_t g0 = (int64_t)w * r_tot / We, g1 = (int64_t)(w + 1) * r_tot / We;
 
     RoundAddr cur = locate_round(s_pre, B, Hkv, g0);
     auto advance = [&](RoundAddr a) { return next_round(s_pre, B, Hkv, a); };
@@ -319,9 +321,10 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W)
         return;
     }
     const int64_t r_tot = (int64_t)Hkv * p.stream_pre[p.batch];
+    const int We = split_waves(W, r_tot);
     const int64_t g_lo = (int64_t)Hkv * p.stream_pre[b] + (int64_t)kvh * rb;
-    const int w_lo = wave_of_round(g_lo, r_tot, W);
-    const int nseg = wave_of_round(g_lo + rb - 1, r_tot, W) - w_lo + 1;
+    const int w_lo = wave_of_round(g_lo, r_tot, We);
+    const int nseg = wave_of_round(g_lo + rb - 1, r_tot, We) - w_lo + 1;
     const int64_t s0 = w_lo + (int64_t)b * Hkv + kvh;  // first slot
     float M = -INFINITY;
     for (int c = 0; c < nseg; c += 64)

@@ -219,8 +219,9 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
             for (int h = lane; h < p.num_q_heads; h += 64) p.lse[(int64_t)b * p.num_q_heads + h] = -INFINITY;
     }
     const int64_t r_tot = (int64_t)Hkv * s_pre[B];
-    const int64_t g0 = (int64_t)w * r_tot / W, g1 = (int64_t)(w + 1) * r_tot / W;
-    if (g0 >= g1) return;
+    const int We = split_waves(W, r_tot);
+    if (w >= We) return;
+    const int64_t g0 = (int64_t)w * r_tot / We, g1 = (int64_t)(w + 1) * r_tot / We;
 
     RoundAddr cur = locate_round(s_pre, B, Hkv, g0);
     const int64_t cap = p.capacity, cap16 = cap - 16;
@@ -351,8 +352,8 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     auto end_segment = [&](const RoundAddr &a, int64_t &s0) HDA_INLINE -> int {
         const int rb = s_pre[a.b + 1] - s_pre[a.b];
         const int64_t g_lo = (int64_t)Hkv * s_pre[a.b] + (int64_t)a.kvh * rb;
-        const int w_lo = wave_of_round(g_lo, r_tot, W);
-        const int w_hi = wave_of_round(g_lo + rb - 1, r_tot, W);
+        const int w_lo = wave_of_round(g_lo, r_tot, We);
+        const int w_hi = wave_of_round(g_lo + rb - 1, r_tot, We);
         if (w_lo == w_hi) {
             store_final<G>(st, p, a.b, a.kvh, lane);
             return 0;

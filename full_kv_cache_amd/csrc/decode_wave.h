@@ -333,7 +333,16 @@ __device__ __forceinline__ RoundAddr next_round(const int *s_pre, int B, int Hkv
     return a;
 }
 
-// Wave whose range holds round g: the largest w with w*R_tot/W <= g.
+// Waves the rounds are split over: the grid's W, but never more than there
+// are rounds (the grid is sized before the lengths are known), so that every
+// wave holds at least one round and the waves from the first to the last
+// of a pair's rounds each hold one of its segments.
+__device__ __forceinline__ int split_waves(int W, int64_t r_tot) {
+    return (int)(r_tot < W ? r_tot : W);
+}
+
+// Wave whose range holds round g: the largest w with w*R_tot/W <= g
+// (W = split_waves(...), so that range is not empty).
 __device__ __forceinline__ int wave_of_round(int64_t g, int64_t r_tot, int W) {
     return (int)(((g + 1) * W - 1) / r_tot);
 }

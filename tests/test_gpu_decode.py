@@ -96,6 +96,22 @@ def test_full_chunks_ragged(chunk):
     np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
 
 
+@pytest.mark.parametrize("pos", [
+    [0, 15, 16, 300, 2047],            # 302 rounds for a 320-wave grid
+    [0, 0, 0, 0, 0, 0, 0, 2047],      # 270 rounds for a 512-wave grid
+])
+def test_stream_fewer_rounds_than_waves(pos):
+    """The streaming grid is sized from max_seq_len for every sequence; a
+    ragged batch can hold fewer rounds than the grid has waves.  Every
+    sequence must still be merged from exactly its own segments."""
+    _print_case(test="stream_few_rounds", pos=pos)
+    case = HybridCase(410 + len(pos), len(pos), FULL, pos, lmax=2048, poison=True)
+    _, ref, rlse = case.oracle_step()
+    _, out, lse = case.gpu_step()
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
 @pytest.mark.parametrize("lt", [SLIDING, FULL])
 def test_sinks(lt):
     _print_case(test="sinks", lt=lt)

@@ -117,6 +117,27 @@ def test_step_outside_cache():
     np.testing.assert_allclose(to_f64(lse)[2:3], rlse2, rtol=0, atol=1e-4)
 
 
+def test_step_full_short_batch_twice():
+    """The step's grid is sized from the cache capacity; short sequences in
+    a large cache hold far fewer rounds (22) than the grid has waves (512).
+    Every pair is still merged, and the arrival counters come back to zero
+    so that a second call on the same workspace is right as well."""
+    _print_case(test="step_full_short")
+    import full_kv_cache_amd as hda
+    pos = np.array([0, 3, 20, 100], np.int32)
+    case = HybridCase(990, 4, FULL, pos, lmax=4096, poison=True)
+    d = case.device()
+    ws = torch.zeros(hda.hda_decode_step_workspace_bytes(case.cache(d), FULL), dtype=torch.uint8,
+                     device="cuda")
+    h, ref, rlse = case.oracle_step()
+    for _ in range(2):  # the second call re-appends the same rows
+        d, out, lse = fused_step(case, d=d, workspace=ws)
+        _check_cache(d, h)
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+        assert torch.count_nonzero(ws[: 4 * 4 * 2]).item() == 0
+
+
 @pytest.mark.parametrize("lt", [SLIDING, FULL])
 def test_step_twice_same_workspace(lt):
     """Two consecutive steps on one workspace: the arrival counters come
