@@ -28,7 +28,10 @@ fraction of the 8 TB/s HBM peak, decode tokens/s (batch / step time), a
 roofline entry for the dominant kernel and the CPU oracle's rate on a
 bounded sample of the same workload; also the same step with the per-head
 output gate (Spark export page, `_Layer.forward`) applied in every
-attention epilogue (gated_ms_per_step).
+attention epilogue (gated_ms_per_step), and the same step with every full
+layer's cache held in a shuffled pool of 64-row pages read through a block
+table (flashmla_sparse page, `_fp8_flash_mla_kernel`; paged_ms_per_step and
+the paged full-layer kernel in "paged").
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
                     [--path auto|fused|separate]
@@ -79,6 +82,8 @@ def parse():
                     help="split size for full layers on the separate path (0: default)")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "separate"],
                     help="one launch per layer (hda_decode_step) or rope_append + decode_attn")
+    ap.add_argument("--page-size", type=int, default=64,
+                    help="rows per page of the paged full-layer measurement (0: skip it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of this many MB (PMC byte calibration)")
     return ap.parse_args()
@@ -130,9 +135,43 @@ class Workload:
                      for lt in (workloads.SLIDING, workloads.FULL)}
         self.kv_bytes = sum(self.rows[lt] for lt in self.types) * self.kv_row_bytes
 
-    def layer_call(self, L, path="auto", chunk_keys=0, gate=False):
+    def make_paged(self, page_size, seed):
+        """Give every full layer a paged copy of its cache: the blocks cut
+        into page_size-row pages, scattered over a pool in a random order,
+        and a block table [B, max_pages] naming them."""
+        import torch
+        import workloads
+        import full_kv_cache_amd as hda
+        s, B = self.shape, self.cfg["batch"]
+        cap = s.capacity(workloads.FULL)
+        assert cap % page_size == 0, "capacity must be a whole number of pages"
+        mp = cap // page_size
+        g = torch.Generator().manual_seed(seed + 3)
+        for L in self.layers:
+            if L["lt"] != workloads.FULL:
+                continue
+            perm = torch.randperm(B * mp, generator=g).to(L["raw"]["k"].device)
+            pools = []
+            for blk in (L["cache"].k, L["cache"].v):
+                pages = blk.view(B, s.num_kv_heads, mp, page_size, s.head_dim).permute(0, 2, 1, 3, 4)
+                pool = torch.empty((B * mp, s.num_kv_heads, page_size, s.head_dim),
+                                   dtype=blk.dtype, device=blk.device)
+                pool[perm] = pages.reshape(B * mp, s.num_kv_heads, page_size, s.head_dim)
+                pools.append(pool)
+            table = perm.view(B, mp).to(torch.int32).contiguous()
+            L["pcache"] = hda.LayerCache(pools[0], pools[1], s.num_q_heads, s.window,
+                                         s.rot(workloads.FULL), s.theta(workloads.FULL),
+                                         block_table=table)
+
+    def layer_call(self, L, path="auto", chunk_keys=0, gate=False, paged=False):
         import full_kv_cache_amd as hda
         g = L["gate"] if gate else None
+        if paged and "pcache" in L:
+            hda.hda_rope_append(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["pcache"])
+            hda.hda_decode_attn(L["q"], L["pcache"], self.seq_lens, L["lt"], L["sinks"],
+                                self.scale, L["out"], L["lse"], self.max_seq_len, 0,
+                                self.workspace, gate=g)
+            return
         if layer_path(path, L["lt"]) == "fused":
             hda.hda_decode_step(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["cache"],
                                 L["sinks"], self.scale, L["out"], L["lse"], self.workspace, gate=g)
@@ -142,9 +181,9 @@ class Workload:
                                 L["out"], L["lse"], self.max_seq_len, chunk_keys, self.workspace,
                                 gate=g)
 
-    def step(self, path="auto", chunk_keys=0, gate=False):
+    def step(self, path="auto", chunk_keys=0, gate=False, paged=False):
         for L in self.layers:
-            self.layer_call(L, path, chunk_keys, gate)
+            self.layer_call(L, path, chunk_keys, gate, paged)
 
 
 def time_graph(fn, steps, warmup, use_graph=True):
@@ -196,7 +235,7 @@ TRAFFIC_SOURCES = ("decode_attn.hip", "decode_wave.h", "decode_step.hip", "hda_d
                    "hda_kernels.h", "hda_api.cpp", "rope_append.hip", "sparse_attn.hip")
 
 
-def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0):
+def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0, paged=False):
     """Time one layer type's attention calls (exactly as the step makes them:
     on the separate path hda_decode_attn without the RoPE/append launch, on
     the fused path the whole hda_decode_step) captured in one graph, HIP
@@ -207,16 +246,17 @@ def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0
     import full_kv_cache_amd as hda
     import workloads
     Ls = [L for L in wl.layers if L["lt"] == lt]
-    if not Ls:
+    if not Ls or (paged and "pcache" not in Ls[0]):
         return None
-    path = layer_path(path, lt)
+    path = "separate" if paged else layer_path(path, lt)
+    key = "pcache" if paged else "cache"
 
     def fn():
         for L in Ls:
             if path == "fused":
                 wl.layer_call(L, "fused")
             else:
-                hda.hda_decode_attn(L["q"], L["cache"], wl.seq_lens, lt, L["sinks"], wl.scale,
+                hda.hda_decode_attn(L["q"], L[key], wl.seq_lens, lt, L["sinks"], wl.scale,
                                     L["out"], L["lse"], wl.max_seq_len, chunk_keys, wl.workspace)
 
     ms, _ = time_graph(fn, steps, warmup)
@@ -224,6 +264,15 @@ def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0
     algo = wl.rows[lt] * wl.kv_row_bytes
     achieved = algo / per_call_s / 1e9
     name = "sliding" if lt == workloads.SLIDING else "full"
+    if paged:
+        p = Ls[0]["pcache"].desc()
+        return {
+            "kernel": f"{KERNELS[(path, name)]} (full-layer hda_decode_attn, paged)",
+            "page_size": p.page_size, "pool_pages": p.num_pages,
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": algo,
+            "avg_launch_us": round(per_call_s * 1e6, 2), "launches_timed": steps * len(Ls),
+        }
     return {
         "kernel": f"{KERNELS[(path, name)]} ({name}-layer hda_decode_attn)" if path == "separate"
                   else f"{KERNELS[(path, name)]} ({name}-layer hda_decode_step)",
@@ -406,6 +455,15 @@ def main():
     import workloads
     k_slide = layer_kernel(wl, workloads.SLIDING, args.steps, args.warmup, args.path, args.chunk_keys)
     k_full = layer_kernel(wl, workloads.FULL, args.steps, args.warmup, args.path, args.chunk_keys)
+    paged_ms, k_paged = None, None
+    if args.page_size and wl.shape.capacity(workloads.FULL) % args.page_size == 0:
+        print(f"# timing the step with paged full layers ({args.page_size}-row pages)",
+              file=sys.stderr, flush=True)
+        wl.make_paged(args.page_size, args.seed)
+        torch.cuda.synchronize()
+        paged_ms, _ = time_graph(lambda: wl.step(args.path, args.chunk_keys, paged=True),
+                                 args.steps, args.warmup, use_graph=not args.no_graph)
+        k_paged = layer_kernel(wl, workloads.FULL, args.steps, args.warmup, paged=True)
     # the dominant kernel: the layer type with the most attention time per step
     n_s = sum(1 for L in wl.layers if L["lt"] == workloads.SLIDING)
     n_f = len(wl.layers) - n_s
@@ -436,9 +494,10 @@ def main():
         "kv_bytes_per_step": wl.kv_bytes,
         "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
         "gated_ms_per_step": round(gated_ms, 4),
+        "paged_ms_per_step": None if paged_ms is None else round(paged_ms, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": roof, "layer_kernels": {"sliding": k_slide, "full": k_full},
-        "cpu_baseline": cpu, "sparse": sparse,
+        "cpu_baseline": cpu, "sparse": sparse, "paged": k_paged,
     }
     print(json.dumps(rec), flush=True)
 

@@ -48,6 +48,10 @@ class CacheDesc(ctypes.Structure):
         ("rope_theta", ctypes.c_double),
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
     ]
 
 
@@ -117,7 +121,9 @@ class LayerCache:
     """One layer's KV cache tensors plus the shape facts of hda_cache_desc.
 
     k, v: bf16 [B, Hkv, capacity, D]; a sliding layer has capacity == window
-    (window-1 ring slots, then the evicted-entry row).
+    (window-1 ring slots, then the evicted-entry row).  Paged (full layers):
+    block_table int32 [B, max_pages] and k, v page pools bf16 [num_pages, Hkv,
+    page_size, D].
     """
     k: torch.Tensor
     v: torch.Tensor
@@ -125,11 +131,22 @@ class LayerCache:
     window: int
     rotary_dim: int
     rope_theta: float
+    block_table: Optional[torch.Tensor] = None
 
     def desc(self) -> CacheDesc:
-        B, Hkv, cap, D = self.k.shape
-        return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim, cap,
-                         float(self.rope_theta), self.k.data_ptr(), self.v.data_ptr())
+        if self.block_table is None:
+            B, Hkv, cap, D = self.k.shape
+            return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim, cap,
+                             float(self.rope_theta), self.k.data_ptr(), self.v.data_ptr(),
+                             None, 0, 0, 0)
+        if self.block_table.dtype != torch.int32 or not self.block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 tensor")
+        num_pages, Hkv, page, D = self.k.shape
+        B, max_pages = self.block_table.shape
+        return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim,
+                         max_pages * page, float(self.rope_theta), self.k.data_ptr(),
+                         self.v.data_ptr(), self.block_table.data_ptr(), page, max_pages,
+                         num_pages)
 
 
 def hda_rope_append(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, stream=None):

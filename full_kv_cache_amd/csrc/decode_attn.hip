@@ -237,10 +237,22 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     const int64_t cap = p.capacity, cap16 = cap - 16;
     auto geo = [&](const RoundAddr &a) {
         RoundGeo g;
+        const int r0 = a.rr * 16;
+        if (p.pages.block_table) {
+            // paged: a round's 16 rows lie in one page (page_size is a
+            // multiple of 16), rows r0 % page_size .. +15 of it
+            const int ps = p.pages.page_size;
+            const int64_t pg = uniform((int)page_of(p.pages, a.b, r0));
+            g.kblk = p.k + (pg * Hkv + a.kvh) * ps * D;
+            g.vblk = p.v + (pg * Hkv + a.kvh) * ps * D;
+            g.r0e = r0 % ps;
+            g.lo = 0;
+            g.hi = uniform(num_keys(p, a.b)) - r0;
+            return g;
+        }
         const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
         g.kblk = p.k + bh * cap * D;
         g.vblk = p.v + bh * cap * D;
-        const int r0 = a.rr * 16;
         g.r0e = (int)(r0 < cap16 ? r0 : cap16);
         g.lo = r0 - g.r0e;
         g.hi = uniform(num_keys(p, a.b)) - g.r0e;

@@ -71,7 +71,34 @@ hda_status check_cache(const hda_cache_desc *c, int layer) {
     if (!c->k || !c->v) return fail(HDA_ERR_INVALID_ARGUMENT, "cache k/v pointer is NULL");
     if (!aligned16(c->k) || !aligned16(c->v))
         return fail(HDA_ERR_INVALID_ARGUMENT, "cache k/v must be 16-byte aligned");
+    if (c->block_table) {
+        if (layer != HDA_FULL)
+            return fail(HDA_ERR_UNSUPPORTED, "the paged layout is for full layers (a sliding "
+                        "layer's window is a fixed block)");
+        if (c->page_size < 16 || c->page_size % 16)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "page_size %d must be a positive multiple of 16",
+                        c->page_size);
+        if (c->max_pages < 1 || c->num_pages < 1)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "max_pages %d and num_pages %lld must be >= 1",
+                        c->max_pages, (long long)c->num_pages);
+        if (c->capacity != (int64_t)c->max_pages * c->page_size)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "paged capacity %lld must be max_pages * "
+                        "page_size = %lld", (long long)c->capacity,
+                        (long long)c->max_pages * c->page_size);
+        if (reinterpret_cast<uintptr_t>(c->block_table) & 3u)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "block_table must be 4-byte aligned");
+    }
     return HDA_OK;
+}
+
+// The page table of a cache (block_table NULL: contiguous blocks).
+hda::PageTable page_table(const hda_cache_desc *c) {
+    hda::PageTable t{};
+    t.block_table = c->block_table;
+    t.page_size = c->page_size;
+    t.max_pages = c->max_pages;
+    t.num_pages = c->num_pages;
+    return t;
 }
 
 // Keys per sequence the grid must cover.
@@ -135,7 +162,7 @@ size_t workspace_for(const hda_cache_desc *c, const Plan &pl) {
 // Window path (chunk_keys == 0, every sequence at most kPairMaxKeys keys):
 // one workgroup per (sequence, KV head, half query group), no workspace.
 bool use_pairs(const hda_cache_desc *c, int layer, int32_t max_seq_len, int32_t chunk_keys) {
-    return chunk_keys == 0 && max_keys_of(c, layer, max_seq_len) <= hda::kPairMaxKeys;
+    return chunk_keys == 0 && !c->block_table && max_keys_of(c, layer, max_seq_len) <= hda::kPairMaxKeys;
 }
 
 bool use_stream(const hda_cache_desc *c, int32_t chunk_keys) {
@@ -251,6 +278,8 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
     if (c->batch > hda::kStreamMaxBatch)
         return fail(HDA_ERR_UNSUPPORTED, "the fused step handles at most %d sequences, got %d",
                     hda::kStreamMaxBatch, c->batch);
+    if (c->block_table)
+        return fail(HDA_ERR_UNSUPPORTED, "the one-launch step is built for contiguous caches only");
     return HDA_OK;
 }
 
@@ -336,6 +365,7 @@ hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const 
     p.pos = pos;
     p.k = static_cast<uint16_t *>(cache->k);
     p.v = static_cast<uint16_t *>(cache->v);
+    p.pages = page_table(cache);
     p.capacity = cache->capacity;
     p.theta = cache->rope_theta;
     p.batch = cache->batch;
@@ -371,6 +401,7 @@ hda::DecodeParams decode_params(const void *q, const hda_cache_desc *cache,
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(cache->k);
     p.v = static_cast<const uint16_t *>(cache->v);
+    p.pages = page_table(cache);
     p.seq_lens = seq_lens;
     p.capacity = cache->capacity;
     p.batch = cache->batch;
@@ -430,6 +461,9 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     if ((st = check_f32_ptrs(sinks, gate, lse)) != HDA_OK) return st;
     if (!out || !aligned16(out))
         return fail(HDA_ERR_INVALID_ARGUMENT, "out must be non-NULL and 16-byte aligned");
+    if (cache->block_table && !use_stream(cache, chunk_keys))
+        return fail(HDA_ERR_UNSUPPORTED, "a paged cache takes the streaming path: chunk_keys must "
+                    "be 0 and batch at most %d", hda::kStreamMaxBatch);
     if (cache->batch == 0) return ok();
     const int g = cache->num_q_heads / cache->num_kv_heads;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -510,6 +544,8 @@ hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
     if (!part_o || !part_lse || !aligned16(part_o))
         return fail(HDA_ERR_INVALID_ARGUMENT,
                     "part_o (16-byte aligned) and part_lse must be non-NULL");
+    if (cache->block_table)
+        return fail(HDA_ERR_UNSUPPORTED, "partials are built for contiguous caches only");
     if (cache->batch == 0) return ok();
     const Plan pl = plan_split(cache, layer, max_keys_of(cache, layer, max_seq_len), chunk_keys);
     hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, pl);

@@ -14,12 +14,28 @@ constexpr int kStreamMaxWaves = 2048;  // its grid: 256 CUs x 8 resident waves
 constexpr int kPairWaves = 8;          // waves per workgroup of the window decomposition
 constexpr int kPairMaxKeys = 1024;     // windows up to this size use it by default
 
+// Paged cache addressing (block_table null: contiguous [B, Hkv, cap, D]
+// blocks): row r of sequence b is row r % page_size of pool page
+// block_table[b * max_pages + r / page_size], clamped into [0, num_pages).
+struct PageTable {
+    const int32_t *block_table;  // [B, max_pages] or null
+    int page_size, max_pages;
+    int64_t num_pages;
+};
+
+// Pool page holding row `row` of sequence b, clamped into [0, num_pages).
+__device__ __forceinline__ int64_t page_of(const PageTable &pt, int b, int64_t row) {
+    const int64_t pg = pt.block_table[(int64_t)b * pt.max_pages + row / pt.page_size];
+    return pg < 0 ? 0 : pg >= pt.num_pages ? pt.num_pages - 1 : pg;
+}
+
 struct RopeAppendParams {
     uint16_t *q;
     const uint16_t *k_new;
     const uint16_t *v_new;
     const int32_t *pos;
     uint16_t *k, *v;            // [B, Hkv, capacity, D]; sliding: row window-1 = evicted entry
+    PageTable pages;            // full layers: paged pools instead of blocks
     int64_t capacity;
     double theta;
     int batch, num_q_heads, num_kv_heads, head_dim, rotary_dim, window;
@@ -29,7 +45,8 @@ struct RopeAppendParams {
 
 struct DecodeParams {
     const uint16_t *q;          // [B, Hq, D]
-    const uint16_t *k, *v;      // [B, Hkv, cap, D]
+    const uint16_t *k, *v;      // [B, Hkv, cap, D], or page pools [pages, Hkv, page_size, D]
+    PageTable pages;
     const int32_t *seq_lens;    // [B]
     const float *sinks;         // [Hq] or null
     const float *gate;          // [B, Hq] output-gate logits or null

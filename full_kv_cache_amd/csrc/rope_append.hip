@@ -7,7 +7,8 @@
 // evicting the oldest.  This kernel rotates q in place, rotates k_new into
 // the cache row, copies v_new, and for a sliding layer first moves the
 // evicted slot content (still inside this step's window) to the block's
-// evicted-entry row, window-1.
+// evicted-entry row, window-1.  A paged full layer writes row pos of the
+// pool page its block table names for that row.
 //
 // One workgroup per sequence.  The work is cut into 16-byte tasks: a
 // rotary task owns 8 consecutive pairs (dims j..j+7 and j+h..j+h+7, h =
@@ -55,6 +56,15 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
         row = pos;
     }
     const bool write_cache = row >= 0;
+    // element offset of cache row r of KV head h of this sequence: its
+    // block's row, or (paged, full layers) the row in the page holding it
+    auto row_off = [&](int h, int64_t r) -> int64_t {
+        if (p.pages.block_table) {
+            const int64_t pg = page_of(p.pages, b, r), ps = p.pages.page_size;
+            return ((pg * p.num_kv_heads + h) * ps + r % ps) * D;
+        }
+        return (((int64_t)b * p.num_kv_heads + h) * cap + r) * D;
+    };
 
     // Task space: [q rotary | k rotary | k pass-through | v], 16 bytes each.
     const int hc = half / 8, pc = (D - rot) / 8, vc = D / 8;
@@ -86,7 +96,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
                 xa[r] = ld(p.k_new + bh * D + j);
                 xb[r] = ld(p.k_new + bh * D + half + j);
                 if (evict) {
-                    const uint16_t *kr = p.k + (bh * cap + row) * D;
+                    const uint16_t *kr = p.k + row_off(h, row);
                     oa[r] = ld(kr + j);
                     ob[r] = ld(kr + half + j);
                 }
@@ -94,12 +104,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
                 const int u = t - n_q - n_k, h = u / pc, d = rot + (u % pc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
                 xa[r] = ld(p.k_new + bh * D + d);
-                if (evict) oa[r] = ld(p.k + (bh * cap + row) * D + d);
+                if (evict) oa[r] = ld(p.k + row_off(h, row) + d);
             } else {
                 const int u = t - n_q - n_k - n_kp, h = u / vc, d = (u % vc) * 8;
                 const int64_t bh = (int64_t)b * p.num_kv_heads + h;
                 xa[r] = ld(p.v_new + bh * D + d);
-                if (evict) oa[r] = ld(p.v + (bh * cap + row) * D + d);
+                if (evict) oa[r] = ld(p.v + row_off(h, row) + d);
             }
         }
 
@@ -124,26 +134,23 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
                 st(qr + half + j, yb);
             } else if (t < n_q + n_k) {
                 const int u = t - n_q, h = u / hc, j = (u % hc) * 8;
-                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
                 if (evict) {
-                    st(p.k + (bh * cap + erow) * D + j, oa[r]);
-                    st(p.k + (bh * cap + erow) * D + half + j, ob[r]);
+                    st(p.k + row_off(h, erow) + j, oa[r]);
+                    st(p.k + row_off(h, erow) + half + j, ob[r]);
                 }
                 uint4 ya, yb;
                 rotate8(xa[r], xb[r], s_cos + j, s_sin + j, ya, yb);
-                uint16_t *kr = p.k + (bh * cap + row) * D;
+                uint16_t *kr = p.k + row_off(h, row);
                 st(kr + j, ya);
                 st(kr + half + j, yb);
             } else if (t < n_q + n_k + n_kp) {
                 const int u = t - n_q - n_k, h = u / pc, d = rot + (u % pc) * 8;
-                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
-                if (evict) st(p.k + (bh * cap + erow) * D + d, oa[r]);
-                st(p.k + (bh * cap + row) * D + d, xa[r]);
+                if (evict) st(p.k + row_off(h, erow) + d, oa[r]);
+                st(p.k + row_off(h, row) + d, xa[r]);
             } else {
                 const int u = t - n_q - n_k - n_kp, h = u / vc, d = (u % vc) * 8;
-                const int64_t bh = (int64_t)b * p.num_kv_heads + h;
-                if (evict) st(p.v + (bh * cap + erow) * D + d, oa[r]);
-                st(p.v + (bh * cap + row) * D + d, xa[r]);
+                if (evict) st(p.v + row_off(h, erow) + d, oa[r]);
+                st(p.v + row_off(h, row) + d, xa[r]);
             }
         }
     }

@@ -68,6 +68,21 @@ typedef enum hda_layer_type {
  *   rotary_dim  leading dims rotated by RoPE (`rotary_dim`: head_dim times
  *   rope_theta  the layer type's `partial_rotary_factor`), and its theta.
  *               Spark: sliding 256 dims / 1e4, full 64 dims / 5e6.
+ *
+ * Paged layout (full layers only; block_table NULL selects the contiguous
+ * layout above).  The flashmla_sparse page's attention call takes a
+ * block table and per-sequence cache lengths for serving many sequences of
+ * different lengths from one pool of fixed-size pages:
+ *   k, v         page pool bf16 [num_pages, num_kv_heads, page_size, head_dim]
+ *   block_table  int32 [batch, max_pages] (device): row r of sequence b is
+ *                row r % page_size of page block_table[b][r / page_size]
+ *   page_size    rows per page, a positive multiple of 16
+ *   capacity     max_pages * page_size
+ * Entries must name pool pages for every page that holds one of the
+ * sequence's rows; an entry outside [0, num_pages) is clamped into that
+ * range (the result is then meaningless, but no access leaves the pool).
+ * Pages may be shared between sequences for reading; an append writes row
+ * pos of the page its sequence names.
  */
 typedef struct hda_cache_desc {
     int32_t batch;
@@ -80,6 +95,10 @@ typedef struct hda_cache_desc {
     double rope_theta;
     void *k;
     void *v;
+    const int32_t *block_table;
+    int32_t page_size;
+    int32_t max_pages;
+    int64_t num_pages;
 } hda_cache_desc;
 
 /*
@@ -109,7 +128,11 @@ typedef struct hda_cache_desc {
  * head counts, num_q_heads % num_kv_heads != 0, odd or oversized
  * rotary_dim, sliding capacity != window, unknown layer; UNSUPPORTED for a
  * rotary_dim that is not a multiple of 16 or exceeds 512; HIP on a launch
- * failure.  batch == 0 is a no-op.
+ * failure.  batch == 0 is a no-op.  Paged cache: row pos is written into
+ * the page the sequence's block table names for it; INVALID_ARGUMENT for
+ * a page_size that is not a positive multiple of 16, max_pages or
+ * num_pages < 1, capacity != max_pages * page_size or a misaligned table;
+ * UNSUPPORTED for a paged sliding layer.
  */
 hda_status hda_rope_append(void *q, const void *k_new, const void *v_new,
                            const int32_t *pos, hda_layer_type layer,
@@ -170,7 +193,10 @@ size_t hda_decode_workspace_bytes(const hda_cache_desc *cache, hda_layer_type la
  * Errors: as hda_rope_append, plus UNSUPPORTED for head_dim != 256 or a
  * query group size outside {1, 2, 4, 8, 16}, WORKSPACE when the workspace
  * is NULL or smaller than required, INVALID_ARGUMENT for a bad chunk_keys
- * or max_seq_len.  The cache is only read.
+ * or max_seq_len.  The cache is only read.  A paged cache is read by the
+ * balanced streaming kernel (the same rounds, summed in the same order as
+ * for contiguous blocks): UNSUPPORTED for chunk_keys != 0 or batch above
+ * 4096 with a paged cache.
  */
 hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache,
                            const int32_t *seq_lens, hda_layer_type layer,
@@ -198,7 +224,8 @@ hda_status hda_decode_split_plan(const hda_cache_desc *cache, hda_layer_type lay
  * and merged online equals the single pass.  Same arguments as
  * hda_decode_attn; part_o fp32 [batch, num_q_heads, nsplit, head_dim],
  * part_lse fp32 [batch, num_q_heads, nsplit], nsplit from
- * hda_decode_split_plan.  No sink or gate is applied here.
+ * hda_decode_split_plan.  No sink or gate is applied here.  UNSUPPORTED
+ * for a paged cache.
  */
 hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
                                     const int32_t *seq_lens, hda_layer_type layer,
@@ -227,7 +254,8 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
 
 /*
  * hda_decode_step_workspace_bytes -- device workspace hda_decode_step needs
- * for this cache and layer type (0 for an invalid description).
+ * for this cache and layer type (0 for a description it refuses, a paged
+ * one included).
  */
 size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer);
 
@@ -254,7 +282,8 @@ size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_ty
  *              header, so one workspace serves both.  Calls sharing a
  *              workspace must be ordered on one stream.
  * Errors: as hda_decode_attn, plus UNSUPPORTED for rotary_dim other than
- * 64 or 256 or batch above 4096.  batch == 0 is a no-op.
+ * 64 or 256, batch above 4096 or a paged cache (use hda_rope_append +
+ * hda_decode_attn).  batch == 0 is a no-op.
  */
 hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
                            const int32_t *pos, hda_layer_type layer,

@@ -274,3 +274,54 @@ def test_gate_binding_checks():
         hda.validate_gate(torch.zeros(8, 2, dtype=torch.float32).t(), out)
     hda.validate_gate(torch.zeros(2, 8, dtype=torch.float32), out)
     hda.validate_gate(None, q)
+
+
+# ------------------------------------------------------------- paged cache
+_PAGED = dict(capacity=1024, rotary_dim=64, rope_theta=5e6, block_table=FAKE, page_size=64,
+              max_pages=16, num_pages=40)
+
+
+def test_paged_descriptor_checks():
+    """The paged layout is refused on sliding layers and checked for a
+    page size that keeps each 16-key round inside one page, a capacity of
+    max_pages * page_size, and an aligned table."""
+    assert _append(_desc(block_table=FAKE, page_size=64, max_pages=8, num_pages=8)) == 2
+    assert "full layers" in _msg()
+    for bad in (dict(page_size=24), dict(page_size=0), dict(page_size=-16),
+                dict(max_pages=0, capacity=0), dict(num_pages=0), dict(capacity=1040),
+                dict(block_table=FAKE + 2)):
+        d = _desc(**{**_PAGED, **bad})
+        assert _append(d, layer=hda.FULL) == 1, bad
+        assert _decode(d, layer=hda.FULL, max_seq_len=16) == 1, bad
+
+
+def test_paged_routing():
+    """A paged cache is read only by the streaming kernel: split-K chunks,
+    the partials stage, the fused one-launch step and batches above the
+    streaming limit are refused before anything is enqueued."""
+    L = hda.lib()
+    d = _desc(**_PAGED)
+    assert _decode(d, layer=hda.FULL, max_seq_len=1024, chunk=256) == 2
+    assert "paged" in _msg()
+    big = _desc(**{**_PAGED, "batch": 5000})
+    assert _decode(big, layer=hda.FULL, max_seq_len=1024) == 2
+    r = L.hda_decode_attn_partials(ctypes.c_void_p(FAKE), ctypes.byref(d), ctypes.c_void_p(FAKE),
+                                   hda.FULL, 0.0625, 1024, 256, ctypes.c_void_p(FAKE),
+                                   ctypes.c_void_p(FAKE), None)
+    assert r == 2 and "contiguous" in _msg()
+    assert _step(d, layer=hda.FULL) == 2 and "contiguous" in _msg()
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.FULL) == 0
+    assert _decode(_desc(**{**_PAGED, "batch": 0}), layer=hda.FULL, max_seq_len=16) == 0
+
+
+def test_paged_binding_desc():
+    """LayerCache with a block table describes the pool and the table."""
+    import torch
+    pool = torch.zeros(12, 2, 32, 256, dtype=torch.bfloat16)
+    table = torch.arange(12, dtype=torch.int32).reshape(3, 4)
+    c = hda.LayerCache(pool, pool, 8, 512, 64, 5e6, block_table=table).desc()
+    assert (c.batch, c.num_kv_heads, c.capacity, c.page_size, c.max_pages, c.num_pages) == \
+        (3, 2, 128, 32, 4, 12)
+    assert c.block_table == table.data_ptr()
+    with pytest.raises(ValueError):
+        hda.LayerCache(pool, pool, 8, 512, 64, 5e6, block_table=table.long()).desc()
