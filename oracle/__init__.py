@@ -74,6 +74,20 @@ def _load():
         lib.or_lse_merge.argtypes = [P, P, i32, i32, P, P, P]
         lib.or_output_gate.restype = None
         lib.or_output_gate.argtypes = [P, i32, i32, i32, P]
+        lib.or_e4m3_to_f64.restype = f64
+        lib.or_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.or_f32_to_e4m3.restype = ctypes.c_uint8
+        lib.or_f32_to_e4m3.argtypes = [ctypes.c_float]
+        lib.or_quant_rows.restype = None
+        lib.or_quant_rows.argtypes = [P, i64, i32, P, P]
+        lib.or_dequant_rows.restype = None
+        lib.or_dequant_rows.argtypes = [P, P, i64, i32, P]
+        lib.or_rope_append_fp8.restype = None
+        lib.or_rope_append_fp8.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f64, i32,
+                                           i64, P, P, P, P, P, P, P, P]
+        lib.or_decode_attn_f64.restype = None
+        lib.or_decode_attn_f64.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                           i64, P, f64, P, P]
         lib.or_page_gather.restype = None
         lib.or_page_gather.argtypes = [P, P, i32, i32, i32, i32, i32, i64, P]
         lib.or_sparse_decode_attn.restype = None
@@ -192,6 +206,84 @@ def output_gate(out, gate):
     B, Hq, D = out.shape
     assert gate.shape == (B, Hq)
     _load().or_output_gate(_p(out), B, Hq, D, _p(gate))
+
+
+# ------------------------------------------------------------- FP8 KV
+
+def e4m3_to_f64(code: int) -> float:
+    return _load().or_e4m3_to_f64(int(code))
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(_load().or_f32_to_e4m3(float(x)))
+
+
+def quant_rows(x_bits):
+    """bf16 bits [..., D] -> (codes uint8 [..., D], scales fp32 [...])."""
+    x = _u16(x_bits)
+    D = x.shape[-1]
+    rows = x.size // D
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.zeros(x.shape[:-1], dtype=np.float32)
+    _load().or_quant_rows(_p(x), rows, D, _p(codes), _p(scales))
+    return codes, scales
+
+
+def dequant_rows(codes, scales):
+    """codes uint8 [..., D], scales fp32 [...] -> fp64 [..., D]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = _f32(scales)
+    D = codes.shape[-1]
+    out = np.zeros(codes.shape, dtype=np.float64)
+    _load().or_dequant_rows(_p(codes), _p(scales), codes.size // D, D, _p(out))
+    return out
+
+
+def rope_append_fp8(q, k_new, v_new, pos, layer_type, rot, theta, window, kc, vc, ks, vs,
+                    kevc, vevc, kevs, vevs):
+    """In place on numpy copies: q bf16 [B,Hq,D]; codes kc/vc uint8 [B,Hkv,cap,D],
+    scales ks/vs fp32 [B,Hkv,cap]; side rows kevc/vevc uint8 [B,Hkv,D],
+    kevs/vevs fp32 [B,Hkv]."""
+    assert q.dtype == np.uint16 and q.flags.c_contiguous
+    for a in (kc, vc, kevc, vevc):
+        assert a.dtype == np.uint8 and a.flags.c_contiguous
+    for a in (ks, vs, kevs, vevs):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    k_new, v_new, pos = _u16(k_new), _u16(v_new), _i32(pos)
+    B, Hq, D = q.shape
+    Hkv, cap = kc.shape[1], kc.shape[2]
+    _load().or_rope_append_fp8(_p(q), _p(k_new), _p(v_new), _p(pos), layer_type, B, Hq, Hkv, D,
+                               rot, theta, window, cap, _p(kc), _p(vc), _p(ks), _p(vs),
+                               _p(kevc), _p(vevc), _p(kevs), _p(vevs))
+
+
+def decode_attn_f64(q, k, v, kev, vev, seq_lens, layer_type, window, sinks, scale, gate=None):
+    """decode_attn over fp64 K/V values [B,Hkv,cap,D] (+ side rows [B,Hkv,D])."""
+    q = _u16(q)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    kev = None if kev is None else np.ascontiguousarray(kev, dtype=np.float64)
+    vev = None if vev is None else np.ascontiguousarray(vev, dtype=np.float64)
+    seq_lens, sinks = _i32(seq_lens), _f32(sinks)
+    B, Hq, D = q.shape
+    Hkv, cap = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    _load().or_decode_attn_f64(_p(q), _p(k), _p(v), _p(kev), _p(vev), _p(seq_lens), layer_type,
+                               B, Hq, Hkv, D, window, cap, _p(sinks), scale, _p(out), _p(lse))
+    if gate is not None:
+        output_gate(out, gate)
+    return out, lse
+
+
+def decode_attn_fp8(q, kc, vc, ks, vs, kevc, vevc, kevs, vevs, seq_lens, layer_type, window,
+                    sinks, scale, gate=None):
+    """Attention over an fp8 cache: every row dequantized (value = e4m3
+    code x row scale), then decode_attn_f64."""
+    k, v = dequant_rows(kc, ks), dequant_rows(vc, vs)
+    kev = None if kevc is None else dequant_rows(kevc, kevs)
+    vev = None if vevc is None else dequant_rows(vevc, vevs)
+    return decode_attn_f64(q, k, v, kev, vev, seq_lens, layer_type, window, sinks, scale, gate)
 
 
 def page_gather(pool, block_table):

@@ -374,6 +374,213 @@ void or_output_gate(double *out, int B, int Hq, int D, const float *gate) {
         }
 }
 
+/* ------------------------------------------------------------ FP8 KV */
+
+/* FP8 KV cache, [SINK] `_fp8_flash_mla_kernel`: the cache is handed to the
+ * kernel as raw bytes with an fp8 flag; the page prints no element format
+ * and no scaling rule.  Reading (the plainest one the call supports):
+ * elements are e4m3 -- 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ * no infinities, S.1111.111 is NaN, largest finite 448 -- and every cached
+ * row (one token, one KV head, head_dim elements) carries one fp32 scale:
+ * value = decode(code) * scale. */
+
+/* Value of an e4m3 code, from the format's definition. */
+double or_e4m3_to_f64(uint8_t c) {
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double a;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        a = ldexp((double)m, -9);            /* subnormal: m/8 * 2^-6 */
+    else
+        a = ldexp(8.0 + m, e - 7 - 3);       /* (1 + m/8) * 2^(e-7) */
+    return sgn ? -a : a;
+}
+
+/* fp32 -> e4m3, round to nearest, ties to even, saturating to +-448 (a
+ * scaled row never exceeds 448 by more than its own rounding; saturation
+ * keeps such a value finite).  NaN -> 0x7F.  Parity pinned against torch's
+ * float8_e4m3fn cast on |x| <= 448 (incl. exact ties and subnormals). */
+uint8_t or_f32_to_e4m3(float x) {
+    if (isnan(x)) return 0x7F;
+    const uint8_t sgn = signbit(x) ? 0x80 : 0;
+    double a = fabs((double)x);
+    if (a == 0.0) return sgn;
+    if (isinf(a)) return sgn | 0x7E;
+    int e;
+    frexp(a, &e);                  /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;                /* unbiased exponent of a */
+    if (ex < -6) ex = -6;          /* subnormal range shares 2^-6's quantum */
+    const double step = ldexp(1.0, ex - 3);
+    double qn = rint(a / step);    /* exact quotient, half to even */
+    /* qn in [0, 16]: 16 carries into the next binade (8 of its steps) */
+    int code;
+    if (ex == -6 && qn < 8)
+        code = (int)qn;            /* subnormal (or zero) */
+    else {
+        if (qn >= 16) {
+            qn = 8;
+            ++ex;
+        }
+        code = ((ex + 7) << 3) | ((int)qn - 8);
+    }
+    if (code > 0x7E) code = 0x7E;  /* saturate at 448 */
+    return sgn | (uint8_t)code;
+}
+
+/* Quantize rows of bf16 values: scale = amax / 448 (fp32 division; amax =
+ * largest |x| of the row), code = e4m3(x / scale) with x / scale an fp32
+ * division.  An all-zero row has scale 0 and zero codes.
+ * x: bf16 [rows, D]; codes: [rows, D]; scales: fp32 [rows].
+ * Parity pinned: the amax element maps to +-448, sign symmetry, zero row,
+ * relative error <= 2^-4 (normal codes), agreement with dividing and
+ * casting through torch. */
+void or_quant_rows(const uint16_t *x, int64_t rows, int D, uint8_t *codes, float *scales) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * D;
+        float amax = 0.f;
+        for (int d = 0; d < D; ++d) {
+            const float a = fabsf((float)or_bf16_to_f64(xr[d]));
+            if (a > amax) amax = a;
+        }
+        const float sc = amax / 448.0f;
+        scales[r] = sc;
+        for (int d = 0; d < D; ++d)
+            codes[r * D + d] = sc == 0.f ? 0 : or_f32_to_e4m3((float)or_bf16_to_f64(xr[d]) / sc);
+    }
+}
+
+/* value = decode(code) * scale, in fp64 (exact: 4 + 24 significant bits).
+ * codes: [rows, D], scales fp32 [rows] -> out fp64 [rows, D]. */
+void or_dequant_rows(const uint8_t *codes, const float *scales, int64_t rows, int D, double *out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int d = 0; d < D; ++d)
+            out[r * D + d] = or_e4m3_to_f64(codes[r * D + d]) * (double)scales[r];
+}
+
+/* The decode step's cache update on an fp8 cache: q rotated in place and
+ * the new K rotated and rounded to bf16 exactly as or_rope_append does;
+ * then the new K and V rows are quantized (or_quant_rows) into the slot.
+ * Sliding: the old slot's codes and scale move to the side row first (when
+ * pos >= window-1), as in or_rope_append.  Full: row pos (skipped outside
+ * [0, capacity)).  Layouts: kc, vc [B, Hkv, capacity, D] codes; ks, vs fp32
+ * [B, Hkv, capacity]; side rows kevc, vevc [B, Hkv, D] and kevs, vevs fp32
+ * [B, Hkv].  Parity pinned: equals the bf16 append followed by quantizing
+ * the written rows; side row = prior slot content. */
+void or_rope_append_fp8(uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                        const int32_t *pos, int layer_type, int B, int Hq, int Hkv, int D,
+                        int rot, double theta, int window, int64_t capacity, uint8_t *kc,
+                        uint8_t *vc, float *ks, float *vs, uint8_t *kevc, uint8_t *vevc,
+                        float *kevs, float *vevs) {
+    uint16_t *krot = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)Hkv * D);
+    for (int b = 0; b < B; ++b) {
+        const int64_t p = pos[b];
+        or_rope_apply(q + (int64_t)b * Hq * D, q + (int64_t)b * Hq * D, Hq, D, rot, theta, p);
+        or_rope_apply(k_new + (int64_t)b * Hkv * D, krot, Hkv, D, rot, theta, p);
+        for (int h = 0; h < Hkv; ++h) {
+            const int64_t bh = (int64_t)b * Hkv + h;
+            int64_t row;
+            if (layer_type == OR_SLIDING) {
+                if (p < 0) continue;
+                row = or_ring_slot(p, window);
+                if (p >= window - 1) {
+                    memcpy(kevc + bh * D, kc + (bh * capacity + row) * D, (size_t)D);
+                    memcpy(vevc + bh * D, vc + (bh * capacity + row) * D, (size_t)D);
+                    kevs[bh] = ks[bh * capacity + row];
+                    vevs[bh] = vs[bh * capacity + row];
+                }
+            } else {
+                if (p < 0 || p >= capacity) continue;
+                row = p;
+            }
+            or_quant_rows(krot + (int64_t)h * D, 1, D, kc + (bh * capacity + row) * D,
+                          ks + bh * capacity + row);
+            or_quant_rows(v_new + bh * D, 1, D, vc + (bh * capacity + row) * D,
+                          vs + bh * capacity + row);
+        }
+    }
+    free(krot);
+}
+
+/* Attention of one query over rows given as fp64 vectors (the dequantized
+ * fp8 cache); otherwise attend_rows. */
+static void attend_rows_f64(const double *qv, const double *const *krows,
+                            const double *const *vrows, int64_t n, int D, double scale,
+                            double *out, double *lse) {
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (n == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double *sc = (double *)malloc(sizeof(double) * n);
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += qv[d] * krows[i][d];
+        sc[i] = acc * scale;
+        if (sc[i] > m) m = sc[i];
+    }
+    double l = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double p = exp(sc[i] - m);
+        l += p;
+        for (int d = 0; d < D; ++d) out[d] += p * vrows[i][d];
+    }
+    for (int d = 0; d < D; ++d) out[d] /= l;
+    *lse = m + log(l);
+    free(sc);
+}
+
+/* or_decode_attn over a cache held as fp64 values (an fp8 cache after
+ * or_dequant_rows): the same key set, GQA map, softmax, lse and sink.
+ * k, v fp64 [B, Hkv, capacity, D]; kev, vev fp64 [B, Hkv, D] (sliding).
+ * Parity pinned: bit-identical to or_decode_attn when the values are
+ * bf16-representable (power-of-two scales). */
+void or_decode_attn_f64(const uint16_t *q, const double *k, const double *v, const double *kev,
+                        const double *vev, const int32_t *seq_lens, int layer_type, int B,
+                        int Hq, int Hkv, int D, int window, int64_t capacity,
+                        const float *sinks, double scale, double *out, double *lse) {
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hq; ++h) {
+            const int g = h / G;
+            const int64_t n = seq_lens[b];
+            const double *kb = k + ((int64_t)b * Hkv + g) * capacity * D;
+            const double *vb = v + ((int64_t)b * Hkv + g) * capacity * D;
+            int64_t nrows = n, nblk = n;
+            int side = 0;
+            if (layer_type == OR_SLIDING) {
+                nblk = n < window - 1 ? n : window - 1;
+                side = n >= window;
+                nrows = nblk + side;
+            }
+            const double **kr = (const double **)malloc(sizeof(void *) * (nrows + 1));
+            const double **vr = (const double **)malloc(sizeof(void *) * (nrows + 1));
+            for (int64_t i = 0; i < nblk; ++i) {
+                kr[i] = kb + i * D;
+                vr[i] = vb + i * D;
+            }
+            if (side) {
+                kr[nblk] = kev + ((int64_t)b * Hkv + g) * D;
+                vr[nblk] = vev + ((int64_t)b * Hkv + g) * D;
+            }
+            double *qv = (double *)malloc(sizeof(double) * D);
+            const uint16_t *qh = q + ((int64_t)b * Hq + h) * D;
+            for (int d = 0; d < D; ++d) qv[d] = or_bf16_to_f64(qh[d]);
+            double *o = out + ((int64_t)b * Hq + h) * D;
+            double *ls = lse + (int64_t)b * Hq + h;
+            attend_rows_f64(qv, kr, vr, nrows, D, scale, o, ls);
+            if (sinks) {
+                const double f = sink_factor(*ls, (double)sinks[h]);
+                for (int d = 0; d < D; ++d) o[d] *= f;
+            }
+            free(qv);
+            free(kr);
+            free(vr);
+        }
+    }
+}
+
 /* ---------------------------------------------------------- paged KV */
 
 /* Paged cache addressing, [SINK] `_fp8_flash_mla_kernel`: the attention
