@@ -31,7 +31,9 @@ output gate (Spark export page, `_Layer.forward`) applied in every
 attention epilogue (gated_ms_per_step), and the same step with every full
 layer's cache held in a shuffled pool of 64-row pages read through a block
 table (flashmla_sparse page, `_fp8_flash_mla_kernel`; paged_ms_per_step and
-the paged full-layer kernel in "paged").
+the paged full-layer kernel in "paged"), and the same step on an FP8 KV
+cache -- e4m3 codes with one fp32 scale per row, quantized on append, the
+reading of that page's fp8 call -- in "fp8".
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
                     [--path auto|fused|separate]
@@ -84,6 +86,7 @@ def parse():
                     help="one launch per layer (hda_decode_step) or rope_append + decode_attn")
     ap.add_argument("--page-size", type=int, default=64,
                     help="rows per page of the paged full-layer measurement (0: skip it)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of this many MB (PMC byte calibration)")
     return ap.parse_args()
@@ -162,6 +165,29 @@ class Workload:
             L["pcache"] = hda.LayerCache(pools[0], pools[1], s.num_q_heads, s.window,
                                          s.rot(workloads.FULL), s.theta(workloads.FULL),
                                          block_table=table)
+
+    def make_fp8(self, seed):
+        """Give every layer an fp8 cache of the same shape: seeded random
+        e4m3 codes (never NaN) and per-row scales in [1, 2) / 448."""
+        import workloads
+        import full_kv_cache_amd as hda
+        s = self.shape
+        g = workloads.generator(seed + 4, self.seq_lens.device)
+        for L in self.layers:
+            c = L["cache"]
+            shp = tuple(c.k.shape)
+            L["fcache"] = hda.LayerCache(
+                workloads.fp8_codes(g, shp, c.k.device), workloads.fp8_codes(g, shp, c.k.device),
+                s.num_q_heads, s.window, c.rotary_dim, c.rope_theta,
+                k_scale=workloads.fp8_scales(g, shp[:-1], c.k.device),
+                v_scale=workloads.fp8_scales(g, shp[:-1], c.k.device))
+        self.fp8_row_bytes = 2 * s.num_kv_heads * (s.head_dim + 4)  # K and V codes + scales
+
+    def fp8_call(self, L):
+        import full_kv_cache_amd as hda
+        hda.hda_rope_append(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["fcache"])
+        hda.hda_decode_attn(L["q"], L["fcache"], self.seq_lens, L["lt"], L["sinks"], self.scale,
+                            L["out"], L["lse"], self.max_seq_len, 0, self.workspace)
 
     def layer_call(self, L, path="auto", chunk_keys=0, gate=False, paged=False):
         import full_kv_cache_amd as hda
@@ -469,6 +495,36 @@ def main():
     n_f = len(wl.layers) - n_s
     cands = [(k["avg_launch_us"] * n, k) for k, n in ((k_slide, n_s), (k_full, n_f)) if k]
     roof = max(cands, key=lambda c: c[0])[1] if cands else None
+    fp8 = None
+    if not args.no_fp8:
+        print("# timing the step on an fp8 cache", file=sys.stderr, flush=True)
+        wl.make_fp8(args.seed)
+        torch.cuda.synchronize()
+
+        def fp8_step():
+            for L in wl.layers:
+                wl.fp8_call(L)
+        fp8_ms, _ = time_graph(fp8_step, args.steps, args.warmup, use_graph=not args.no_graph)
+        fp8 = {"ms_per_step": round(fp8_ms, 4),
+               "tokens_per_s": round(cfg["batch"] / (fp8_ms / 1e3), 1),
+               "kv_bytes_per_step": sum(wl.rows[L["lt"]] for L in wl.layers) * wl.fp8_row_bytes,
+               "path": "hda_rope_append + hda_decode_attn on every layer (window kernel for "
+                       "sliding layers, streaming kernel + merge for full layers)"}
+        fp8["GB/s"] = round(fp8["kv_bytes_per_step"] / (fp8_ms / 1e3) / 1e9, 1)
+        for lt, name in ((workloads.SLIDING, "sliding"), (workloads.FULL, "full")):
+            Ls = [L for L in wl.layers if L["lt"] == lt]
+            if not Ls:
+                continue
+
+            def attn(Ls=Ls, lt=lt):
+                for L in Ls:
+                    hda.hda_decode_attn(L["q"], L["fcache"], wl.seq_lens, lt, L["sinks"], wl.scale,
+                                        L["out"], L["lse"], wl.max_seq_len, 0, wl.workspace)
+            ms_l, _ = time_graph(attn, args.steps, args.warmup)
+            us = ms_l / len(Ls) * 1e3
+            byts = wl.rows[lt] * wl.fp8_row_bytes
+            fp8[f"{name}_attn_us"] = round(us, 2)
+            fp8[f"{name}_attn_GB/s"] = round(byts / (us / 1e6) / 1e9, 1)
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
@@ -497,7 +553,7 @@ def main():
         "paged_ms_per_step": None if paged_ms is None else round(paged_ms, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": roof, "layer_kernels": {"sliding": k_slide, "full": k_full},
-        "cpu_baseline": cpu, "sparse": sparse, "paged": k_paged,
+        "cpu_baseline": cpu, "sparse": sparse, "paged": k_paged, "fp8": fp8,
     }
     print(json.dumps(rec), flush=True)
 

@@ -20,6 +20,8 @@ import torch
 
 SLIDING = 0
 FULL = 1
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
 
 _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libhda.so"
@@ -52,6 +54,9 @@ class CacheDesc(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("max_pages", ctypes.c_int32),
         ("num_pages", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -123,7 +128,9 @@ class LayerCache:
     k, v: bf16 [B, Hkv, capacity, D]; a sliding layer has capacity == window
     (window-1 ring slots, then the evicted-entry row).  Paged (full layers):
     block_table int32 [B, max_pages] and k, v page pools bf16 [num_pages, Hkv,
-    page_size, D].
+    page_size, D].  FP8: k, v uint8 e4m3 codes of the same shape, and
+    k_scale, v_scale fp32 with one scale per row ([B, Hkv, capacity], paged
+    [num_pages, Hkv, page_size]).
     """
     k: torch.Tensor
     v: torch.Tensor
@@ -132,13 +139,30 @@ class LayerCache:
     rotary_dim: int
     rope_theta: float
     block_table: Optional[torch.Tensor] = None
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+
+    def _dtype_fields(self):
+        if self.k.dtype == torch.bfloat16 and self.v.dtype == torch.bfloat16:
+            if self.k_scale is not None or self.v_scale is not None:
+                raise ValueError("scales belong to an fp8 (uint8) cache")
+            return KV_BF16, None, None
+        if self.k.dtype != torch.uint8 or self.v.dtype != torch.uint8:
+            raise ValueError("k, v must both be bf16, or both uint8 e4m3 codes")
+        rows = self.k.shape[:-1]
+        for s in (self.k_scale, self.v_scale):
+            if s is None or s.dtype != torch.float32 or not s.is_contiguous() or s.shape != rows:
+                raise ValueError(f"an fp8 cache needs contiguous fp32 k_scale and v_scale of "
+                                 f"shape {tuple(rows)}")
+        return KV_FP8_E4M3, self.k_scale.data_ptr(), self.v_scale.data_ptr()
 
     def desc(self) -> CacheDesc:
+        dt, ks, vs = self._dtype_fields()
         if self.block_table is None:
             B, Hkv, cap, D = self.k.shape
             return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim, cap,
                              float(self.rope_theta), self.k.data_ptr(), self.v.data_ptr(),
-                             None, 0, 0, 0)
+                             None, 0, 0, 0, dt, ks, vs)
         if self.block_table.dtype != torch.int32 or not self.block_table.is_contiguous():
             raise ValueError("block_table must be a contiguous int32 tensor")
         num_pages, Hkv, page, D = self.k.shape
@@ -146,7 +170,7 @@ class LayerCache:
         return CacheDesc(B, self.num_q_heads, Hkv, D, self.window, self.rotary_dim,
                          max_pages * page, float(self.rope_theta), self.k.data_ptr(),
                          self.v.data_ptr(), self.block_table.data_ptr(), page, max_pages,
-                         num_pages)
+                         num_pages, dt, ks, vs)
 
 
 def hda_rope_append(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, stream=None):

@@ -39,6 +39,8 @@
 //
 // The path is HBM-bound: every K and V byte is read once and serves G heads
 // (4 flop per byte at G = 4), far below the VALU and MFMA ridge points.
+#include <type_traits>
+
 #include "decode_wave.h"
 
 namespace hda {
@@ -207,11 +209,12 @@ __global__ __launch_bounds__(kDecodeThreads) void lse_merge_kernel(MergeParams p
 // traffic.)
 // ===================================================================
 struct RoundGeo {
-    const uint16_t *kblk, *vblk;
+    int64_t base;     // cache row index of the block (or page) row 0: codes at base * D
     int r0e, lo, hi;  // in-bounds first row; valid keys [lo, hi) of the round
 };
 
-template <int G>
+// F8: the cache holds e4m3 codes and per-row scales (kq, vq, ks, vs).
+template <int G, bool F8>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     constexpr int D = kHeadDim;
     extern __shared__ int s_pre[];                 // [B + 1] rounds before sequence b, one KV head
@@ -243,16 +246,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
             // multiple of 16), rows r0 % page_size .. +15 of it
             const int ps = p.pages.page_size;
             const int64_t pg = uniform((int)page_of(p.pages, a.b, r0));
-            g.kblk = p.k + (pg * Hkv + a.kvh) * ps * D;
-            g.vblk = p.v + (pg * Hkv + a.kvh) * ps * D;
+            g.base = (pg * Hkv + a.kvh) * ps;
             g.r0e = r0 % ps;
             g.lo = 0;
             g.hi = uniform(num_keys(p, a.b)) - r0;
             return g;
         }
-        const int64_t bh = (int64_t)a.b * Hkv + a.kvh;
-        g.kblk = p.k + bh * cap * D;
-        g.vblk = p.v + bh * cap * D;
+        g.base = ((int64_t)a.b * Hkv + a.kvh) * cap;
         g.r0e = (int)(r0 < cap16 ? r0 : cap16);
         g.lo = r0 - g.r0e;
         g.hi = uniform(num_keys(p, a.b)) - g.r0e;
@@ -260,11 +260,21 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     };
     auto same_pair = [](const RoundAddr &x, const RoundAddr &y) { return x.b == y.b && x.kvh == y.kvh; };
 
+    using KV = std::conditional_t<F8, uint2, uint4>;
+    auto issue = [&](const RoundGeo &g, int ln, KV *kt, KV *vt, float &ks, float &vs) {
+        if constexpr (F8)
+            issue_round8(p.kq + g.base * D, p.vq + g.base * D, p.ks + g.base, p.vs + g.base, g.r0e,
+                         ln, kt, vt, ks, vs);
+        else
+            issue_round(p.k + g.base * D, p.v + g.base * D, g.r0e, ln, kt, vt);
+    };
+
     bf16x8 qa[8];
     WaveSoftmax<G> st;
-    uint4 kA[8], vA[8], kB[8], vB[8];
+    KV kA[8], vA[8], kB[8], vB[8];
+    float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
     RoundGeo gc = geo(cur);
-    issue_round(gc.kblk, gc.vblk, gc.r0e, lane, kA, vA);
+    issue(gc, lane, kA, vA, ksA, vsA);
     load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
     st.reset();
 
@@ -282,8 +292,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         bool more = g + 1 < g1;
         RoundAddr nxt = more ? advance(cur) : cur;
         RoundGeo gn = geo(nxt);
-        issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kB, vB);
-        st.round(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane);
+        issue(gn, more ? lane : 0, kB, vB, ksB, vsB);
+        st.template round<false, F8>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
+                                     nullptr, nullptr, ksA, vsA);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
@@ -297,8 +308,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         more = g + 1 < g1;
         nxt = more ? advance(cur) : cur;
         gn = geo(nxt);
-        issue_round(gn.kblk, gn.vblk, gn.r0e, more ? lane : 0, kA, vA);
-        st.round(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane);
+        issue(gn, more ? lane : 0, kA, vA, ksA, vsA);
+        st.template round<false, F8>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
+                                     nullptr, nullptr, ksB, vsB);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W)
 // rows; their block ids are congruent mod 8 so that they run on the same XCD
 // and the later reads hit its L2.
 // ===================================================================
-template <int GW>
+template <int GW, bool F8>
 __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodeParams p, int S) {
     constexpr int D = kHeadDim;
     constexpr int WAVES = kPairWaves;
@@ -404,8 +416,15 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
     const int r_lo = wave * R / WAVES, r_hi = (wave + 1) * R / WAVES;
     const int64_t cap = p.capacity, cap16 = cap - 16;
     const int64_t bh = (int64_t)b * p.num_kv_heads + kvh;
-    const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
     auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap16 ? 16 * r : cap16); };
+    using KV = std::conditional_t<F8, uint2, uint4>;
+    auto issue = [&](int r0e, int ln, KV *kt, KV *vt, float &ks, float &vs) {
+        if constexpr (F8)
+            issue_round8(p.kq + bh * cap * D, p.vq + bh * cap * D, p.ks + bh * cap,
+                         p.vs + bh * cap, r0e, ln, kt, vt, ks, vs);
+        else
+            issue_round(p.k + bh * cap * D, p.v + bh * cap * D, r0e, ln, kt, vt);
+    };
 
     WaveSoftmax<GW> st;
     st.reset();
@@ -416,24 +435,28 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
         // The q operand goes out between the first batch's two rounds, so
         // that the first round waits for it and not for the second.
         bf16x8 qa[8];
-        uint4 kA[8], vA[8], kB[8], vB[8];
+        KV kA[8], vA[8], kB[8], vB[8];
+        float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
         {
             const bool two = r_lo + 1 < r_hi;
-            issue_round(kblk, vblk, r0e_of(r_lo), lane, kA, vA);
+            issue(r0e_of(r_lo), lane, kA, vA, ksA, vsA);
             load_q_operand<GW>(p.q, p.num_q_heads, b, hsub, lane, qa);
-            issue_round(kblk, vblk, r0e_of(two ? r_lo + 1 : r_lo), two ? lane : 0, kB, vB);
+            issue(r0e_of(two ? r_lo + 1 : r_lo), two ? lane : 0, kB, vB, ksB, vsB);
         }
         for (int r = r_lo; r < r_hi; r += 2) {
             const bool two = r + 1 < r_hi;
             if (r != r_lo) {
-                issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
-                issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+                issue(r0e_of(r), lane, kA, vA, ksA, vsA);
+                issue(r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB, ksB, vsB);
             }
             int e = r0e_of(r);
-            st.round(qa, kA, vA, 16 * r - e, n - e, p.scale_log2, s_pw[wave], s_kt[wave], lane);
+            st.template round<false, F8>(qa, kA, vA, 16 * r - e, n - e, p.scale_log2, s_pw[wave],
+                                         s_kt[wave], lane, -1, nullptr, nullptr, ksA, vsA);
             if (!two) break;
             e = r0e_of(r + 1);
-            st.round(qa, kB, vB, 16 * (r + 1) - e, n - e, p.scale_log2, s_pw[wave], s_kt[wave], lane);
+            st.template round<false, F8>(qa, kB, vB, 16 * (r + 1) - e, n - e, p.scale_log2,
+                                         s_pw[wave], s_kt[wave], lane, -1, nullptr, nullptr, ksB,
+                                         vsB);
         }
     }
 
@@ -489,7 +512,12 @@ template <int GW>
 hipError_t launch_pair_g(const DecodeParams &p, int S, hipStream_t s) {
     const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
     const int64_t blocks = (pairs + 7) / 8 * 8 * S;
-    hipLaunchKernelGGL((decode_pair_kernel<GW>), dim3((unsigned)blocks), dim3(kPairWaves * 64), 0, s, p, S);
+    if (p.kq)
+        hipLaunchKernelGGL((decode_pair_kernel<GW, true>), dim3((unsigned)blocks), dim3(kPairWaves * 64),
+                           0, s, p, S);
+    else
+        hipLaunchKernelGGL((decode_pair_kernel<GW, false>), dim3((unsigned)blocks), dim3(kPairWaves * 64),
+                           0, s, p, S);
     return hipGetLastError();
 }
 
@@ -514,7 +542,12 @@ hipError_t launch_chunks(const DecodeParams &p, int group, hipStream_t s) {
 
 template <int G>
 hipError_t launch_stream_g(const DecodeParams &p, int waves, hipStream_t s) {
-    hipLaunchKernelGGL((decode_stream_kernel<G>), dim3(waves), dim3(64), (p.batch + 1) * sizeof(int), s, p);
+    if (p.kq)
+        hipLaunchKernelGGL((decode_stream_kernel<G, true>), dim3(waves), dim3(64),
+                           (p.batch + 1) * sizeof(int), s, p);
+    else
+        hipLaunchKernelGGL((decode_stream_kernel<G, false>), dim3(waves), dim3(64),
+                           (p.batch + 1) * sizeof(int), s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_stream_merge(p, waves, s);
@@ -536,7 +569,7 @@ int stream_slots_g() {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_stream_kernel<G>, 64, 0) !=
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_stream_kernel<G, false>, 64, 0) !=
                 hipSuccess) {
             (void)hipGetLastError();
             return 0;

@@ -138,15 +138,25 @@ struct WaveSoftmax {
     // 8 dims of row 2u + half-wave).  ktile: this wave's LDS tile.
     // SUB: key vr of the round (if 0 <= vr < 16) takes its K row from knew
     // and its V row from vnew (LDS) instead of what was loaded.
-    template <bool SUB = false>
-    __device__ __forceinline__ void round(const bf16x8 *qa, const uint4 *kt, uint4 *vt, int lo,
+    // FP8 (KV = uint2: 8 e4m3 codes of the same 8 dims): the K codes become
+    // bf16 on their way into the tile (exact), the round's scores take the
+    // key's K scale (ksc, lane = key mrow's scale), the probabilities sent to
+    // the P.V lanes its V scale (vsc) -- the running sum keeps the unscaled
+    // ones -- and the V codes become fp32 (exact).
+    template <bool SUB = false, bool F8 = false, typename KV = uint4>
+    __device__ __forceinline__ void round(const bf16x8 *qa, const KV *kt, KV *vt, int lo,
                                           int hi, float scale_log2, float *pw, uint16_t *ktile, int lane,
                                           int vr = -1, const uint16_t *knew = nullptr,
-                                          const uint16_t *vnew = nullptr) {
+                                          const uint16_t *vnew = nullptr, float ksc = 1.f,
+                                          float vsc = 1.f) {
         const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4 *>(ktile + (2 * j + hw) * kKPitch + 8 * dl) = kt[j];
+        for (int j = 0; j < 8; ++j) {
+            uint4 kw;
+            if constexpr (F8) kw = e4m3x8_to_bf16x8(kt[j]);
+            else kw = kt[j];
+            *reinterpret_cast<uint4 *>(ktile + (2 * j + hw) * kKPitch + 8 * dl) = kw;
+        }
         if (SUB && vr >= 0 && hw == 0)
             *reinterpret_cast<uint4 *>(ktile + vr * kKPitch + 8 * dl) =
                 *reinterpret_cast<const uint4 *>(knew + 8 * dl);
@@ -160,10 +170,11 @@ struct WaveSoftmax {
         // lane holds heads 4*kg + i of key mrow; a masked key's score is
         // replaced, never combined, so whatever its row holds cannot leak
         const bool valid = mrow >= lo && mrow < hi;
+        const float kf = F8 ? scale_log2 * ksc : scale_log2;
         float alpha[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float s = valid ? sc[i] * scale_log2 : -INFINITY;
+            float s = valid ? sc[i] * kf : -INFINITY;
             const float mn = fmaxf(m_run[i], row16_max(s));  // finite: the round holds a key
             alpha[i] = fast_exp2(m_run[i] - mn);
             s = fast_exp2(s - mn);
@@ -172,9 +183,10 @@ struct WaveSoftmax {
             sc[i] = s;
         }
         if (4 * kg < G) {
+            const float vf = valid ? vsc : 0.f;  // a masked key's scale may be anything
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (4 * kg + i < G) pw[mrow * G + 4 * kg + i] = sc[i];
+                if (4 * kg + i < G) pw[mrow * G + 4 * kg + i] = F8 ? sc[i] * vf : sc[i];
         }
         // Rescale the running output only when some head's maximum moved.
         float a_h[G];
@@ -196,7 +208,12 @@ struct WaveSoftmax {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int key = 2 * u + hw;
-                if (key < lo || key >= hi) vt[u] = make_uint4(0, 0, 0, 0);
+                if (key < lo || key >= hi) {
+                    // (make_*, not KV{}: value-initialising the vector class
+                    // kept the K/V arrays of some callers out of registers)
+                    if constexpr (F8) vt[u] = make_uint2(0, 0);
+                    else vt[u] = make_uint4(0, 0, 0, 0);
+                }
             }
         }
         wave_lds_fence();
@@ -205,9 +222,13 @@ struct WaveSoftmax {
             float pv[G], x[8];
 #pragma unroll
             for (int h = 0; h < G; ++h) pv[h] = pw[(2 * u + hw) * G + h];
-            uint4 vv = vt[u];
-            if (SUB && 2 * u + hw == vr) vv = *reinterpret_cast<const uint4 *>(vnew + 8 * dl);
-            bf16x8_to_f32(vv, x);
+            if constexpr (F8) {
+                e4m3x8_to_f32(vt[u], x);
+            } else {
+                uint4 vv = vt[u];
+                if (SUB && 2 * u + hw == vr) vv = *reinterpret_cast<const uint4 *>(vnew + 8 * dl);
+                bf16x8_to_f32(vv, x);
+            }
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -249,6 +270,25 @@ __device__ __forceinline__ void issue_round(const uint16_t *kblk, const uint16_t
     const uint16_t *rv = vblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
 #pragma unroll
     for (int u = 0; u < 8; ++u) vt[u] = ld16_stream(rv + 2 * u * kHeadDim);
+}
+
+// Loads of one fp8 round, the same rows and lanes as issue_round at half
+// the bytes (lane = the 8 codes of row 2u + half-wave), plus each lane's
+// key scales: lane l takes those of key l % 16, the key whose scores it
+// holds after the QK^T product.  ksb / vsb: the scales of the block's rows.
+__device__ __forceinline__ void issue_round8(const uint8_t *kblk, const uint8_t *vblk,
+                                             const float *ksb, const float *vsb, int r0e,
+                                             int lane, uint2 *kt, uint2 *vt, float &ksc,
+                                             float &vsc) {
+    const int hw = lane >> 5, dl = lane & 31;
+    const uint8_t *rk = kblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kt[j] = ld8_stream(rk + 2 * j * kHeadDim);
+    const uint8_t *rv = vblk + (int64_t)(r0e + hw) * kHeadDim + 8 * dl;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vt[u] = ld8_stream(rv + 2 * u * kHeadDim);
+    ksc = ksb[r0e + (lane & 15)];
+    vsc = vsb[r0e + (lane & 15)];
 }
 
 // Writes o / l for the G heads (first half-wave) and their lse.

@@ -71,6 +71,17 @@ hda_status check_cache(const hda_cache_desc *c, int layer) {
     if (!c->k || !c->v) return fail(HDA_ERR_INVALID_ARGUMENT, "cache k/v pointer is NULL");
     if (!aligned16(c->k) || !aligned16(c->v))
         return fail(HDA_ERR_INVALID_ARGUMENT, "cache k/v must be 16-byte aligned");
+    if (c->kv_dtype != HDA_KV_BF16 && c->kv_dtype != HDA_KV_FP8_E4M3)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "unknown kv_dtype %d", c->kv_dtype);
+    if (c->kv_dtype == HDA_KV_FP8_E4M3) {
+        if (!c->k_scale || !c->v_scale)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "an fp8 cache needs k_scale and v_scale");
+        if ((reinterpret_cast<uintptr_t>(c->k_scale) | reinterpret_cast<uintptr_t>(c->v_scale)) & 3u)
+            return fail(HDA_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be 4-byte aligned");
+        if (c->head_dim != hda::kHeadDim)
+            return fail(HDA_ERR_UNSUPPORTED, "the fp8 cache is built for head_dim %d, got %d",
+                        hda::kHeadDim, c->head_dim);
+    }
     if (c->block_table) {
         if (layer != HDA_FULL)
             return fail(HDA_ERR_UNSUPPORTED, "the paged layout is for full layers (a sliding "
@@ -278,8 +289,9 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
     if (c->batch > hda::kStreamMaxBatch)
         return fail(HDA_ERR_UNSUPPORTED, "the fused step handles at most %d sequences, got %d",
                     hda::kStreamMaxBatch, c->batch);
-    if (c->block_table)
-        return fail(HDA_ERR_UNSUPPORTED, "the one-launch step is built for contiguous caches only");
+    if (c->block_table || c->kv_dtype != HDA_KV_BF16)
+        return fail(HDA_ERR_UNSUPPORTED,
+                    "the one-launch step is built for contiguous bf16 caches only");
     return HDA_OK;
 }
 
@@ -366,6 +378,13 @@ hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const 
     p.k = static_cast<uint16_t *>(cache->k);
     p.v = static_cast<uint16_t *>(cache->v);
     p.pages = page_table(cache);
+    const bool fp8 = cache->kv_dtype == HDA_KV_FP8_E4M3;
+    if (fp8) {
+        p.kq = static_cast<uint8_t *>(cache->k);
+        p.vq = static_cast<uint8_t *>(cache->v);
+        p.ks = cache->k_scale;
+        p.vs = cache->v_scale;
+    }
     p.capacity = cache->capacity;
     p.theta = cache->rope_theta;
     p.batch = cache->batch;
@@ -376,7 +395,8 @@ hda_status hda_rope_append(void *q, const void *k_new, const void *v_new, const 
     p.window = cache->window;
     p.sliding = layer == HDA_SLIDING;
     fill_inv_freq(p.inv_freq, cache->rope_theta, cache->rotary_dim);
-    hipError_t e = hda::launch_rope_append(p, static_cast<hipStream_t>(stream));
+    hipError_t e = fp8 ? hda::launch_rope_append_fp8(p, static_cast<hipStream_t>(stream))
+                       : hda::launch_rope_append(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(HDA_ERR_HIP, "rope_append launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -402,6 +422,12 @@ hda::DecodeParams decode_params(const void *q, const hda_cache_desc *cache,
     p.k = static_cast<const uint16_t *>(cache->k);
     p.v = static_cast<const uint16_t *>(cache->v);
     p.pages = page_table(cache);
+    if (cache->kv_dtype == HDA_KV_FP8_E4M3) {
+        p.kq = static_cast<const uint8_t *>(cache->k);
+        p.vq = static_cast<const uint8_t *>(cache->v);
+        p.ks = cache->k_scale;
+        p.vs = cache->v_scale;
+    }
     p.seq_lens = seq_lens;
     p.capacity = cache->capacity;
     p.batch = cache->batch;
@@ -464,6 +490,10 @@ hda_status hda_decode_attn(const void *q, const hda_cache_desc *cache, const int
     if (cache->block_table && !use_stream(cache, chunk_keys))
         return fail(HDA_ERR_UNSUPPORTED, "a paged cache takes the streaming path: chunk_keys must "
                     "be 0 and batch at most %d", hda::kStreamMaxBatch);
+    if (cache->kv_dtype == HDA_KV_FP8_E4M3 && !use_pairs(cache, layer, max_seq_len, chunk_keys) &&
+        !use_stream(cache, chunk_keys))
+        return fail(HDA_ERR_UNSUPPORTED, "an fp8 cache takes the window or streaming path: "
+                    "chunk_keys must be 0 and batch at most %d", hda::kStreamMaxBatch);
     if (cache->batch == 0) return ok();
     const int g = cache->num_q_heads / cache->num_kv_heads;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -544,8 +574,8 @@ hda_status hda_decode_attn_partials(const void *q, const hda_cache_desc *cache,
     if (!part_o || !part_lse || !aligned16(part_o))
         return fail(HDA_ERR_INVALID_ARGUMENT,
                     "part_o (16-byte aligned) and part_lse must be non-NULL");
-    if (cache->block_table)
-        return fail(HDA_ERR_UNSUPPORTED, "partials are built for contiguous caches only");
+    if (cache->block_table || cache->kv_dtype != HDA_KV_BF16)
+        return fail(HDA_ERR_UNSUPPORTED, "partials are built for contiguous bf16 caches only");
     if (cache->batch == 0) return ok();
     const Plan pl = plan_split(cache, layer, max_keys_of(cache, layer, max_seq_len), chunk_keys);
     hda::DecodeParams p = decode_params(q, cache, seq_lens, layer, scale, max_seq_len, pl);

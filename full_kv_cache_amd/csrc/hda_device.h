@@ -37,7 +37,37 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8_stream(const void *p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return make_uint2(v.x, v.y);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// e4m3 codes -> values, exact (every e4m3 value is a bf16 and an fp32 value):
+// the gfx950 conversions, two codes per instruction (word_sel picks bytes
+// 0-1 or 2-3 of the source register; the lower byte becomes the lower
+// element).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+    const bf16x2_t r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)
+                          : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
+    return make_uint4(e4m3x2_to_bf16x2(w.x, false), e4m3x2_to_bf16x2(w.x, true),
+                      e4m3x2_to_bf16x2(w.y, false), e4m3x2_to_bf16x2(w.y, true));
+}
+__device__ __forceinline__ void e4m3x8_to_f32(uint2 w, float *x) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    x[0] = a.x; x[1] = a.y; x[2] = b.x; x[3] = b.y;
+    x[4] = c.x; x[5] = c.y; x[6] = d.x; x[7] = d.y;
+}
 
 // A 16-byte load from a pointer known to address device (global) memory,
 // for pointers whose address space the compiler cannot see.

@@ -36,6 +36,8 @@ struct RopeAppendParams {
     const int32_t *pos;
     uint16_t *k, *v;            // [B, Hkv, capacity, D]; sliding: row window-1 = evicted entry
     PageTable pages;            // full layers: paged pools instead of blocks
+    uint8_t *kq, *vq;           // fp8 cache: e4m3 codes in place of k, v (else null)
+    float *ks, *vs;             // fp8 cache: one scale per row [B, Hkv, capacity]
     int64_t capacity;
     double theta;
     int batch, num_q_heads, num_kv_heads, head_dim, rotary_dim, window;
@@ -47,6 +49,8 @@ struct DecodeParams {
     const uint16_t *q;          // [B, Hq, D]
     const uint16_t *k, *v;      // [B, Hkv, cap, D], or page pools [pages, Hkv, page_size, D]
     PageTable pages;
+    const uint8_t *kq, *vq;     // fp8 cache: e4m3 codes, same layout (else null)
+    const float *ks, *vs;       // fp8 cache: one scale per row
     const int32_t *seq_lens;    // [B]
     const float *sinks;         // [Hq] or null
     const float *gate;          // [B, Hq] output-gate logits or null
@@ -117,6 +121,9 @@ struct SparseParams {
 };
 
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
+// The same for an fp8 cache (kq/vq/ks/vs set; head_dim 256): the new K and
+// V rows are quantized into e4m3 codes with one scale per row.
+hipError_t launch_rope_append_fp8(const RopeAppendParams &p, hipStream_t stream);
 
 // Grid of (token, key split, 16-head group) workgroups; nsplit == 1 writes
 // out / lse with the sink, otherwise partials and then their merge.

@@ -156,6 +156,146 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
     }
 }
 
+// -------------------------------------------------------------------
+// FP8 cache (e4m3 codes + one fp32 scale per row).  The same rotation as
+// above -- identical arithmetic, so the rotated new K is the bf16 row the
+// bf16 cache would hold -- then each new K and V row is quantized:
+// scale = amax / 448, code = e4m3(x / scale), both fp32 divisions rounded
+// to nearest.  One workgroup per sequence: the rotation tasks of the bf16
+// kernel (q in place, K into LDS), then one wave per new row for the
+// quantization (lane = 4 dims; amax by a wave reduction).
+// -------------------------------------------------------------------
+namespace {
+
+// fp32 -> e4m3 (bias 7, 3 mantissa bits, largest finite 448, S.1111.111
+// NaN), round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sgn = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;                  // NaN
+    if (a >= 0x43E00000u) return sgn | 0x7Eu;           // >= 448 (and inf): saturate
+    if (a < 0x3C800000u) {                              // below 2^-6: steps of 2^-9
+        const float q = rintf(__uint_as_float(a) * 512.f);  // exact scaling, half to even
+        return sgn | (uint32_t)q;                       // 8 is 2^-6's own code
+    }
+    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xFFFFFu;
+    const uint32_t up = rem > 0x80000u || (rem == 0x80000u && (keep & 1u));
+    uint32_t v = (((a >> 23) - 127u + 7u) << 3) + keep + up;  // a carry moves into the exponent
+    if (v > 0x7Eu) v = 0x7Eu;
+    return sgn | v;
+}
+
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kRopeThreads) void rope_append_fp8_kernel(RopeAppendParams p) {
+    __shared__ float s_cos[kMaxHalf], s_sin[kMaxHalf];
+    extern __shared__ __align__(16) uint16_t s_krow[];  // [Hkv, D] rotated new K, bf16
+    constexpr int D = kHeadDim;
+    const int b = blockIdx.x;
+    const int rot = p.rotary_dim, half = rot / 2;
+    const int32_t pos = p.pos[b];
+    const int64_t cap = p.capacity;
+    const int Hkv = p.num_kv_heads;
+
+    int64_t row = -1;
+    bool evict = false;
+    const int64_t erow = p.window - 1;
+    if (p.sliding) {
+        const int32_t slots = p.window - 1;
+        if (pos >= 0) {
+            row = pos % slots;
+            evict = pos >= slots;
+        }
+    } else if (pos >= 0 && (int64_t)pos < cap) {
+        row = pos;
+    }
+    const bool write_cache = row >= 0;
+    // cache row index (codes at index * D, scale at index) of row r of KV head h
+    auto row_index = [&](int h, int64_t r) -> int64_t {
+        if (p.pages.block_table) {
+            const int64_t pg = page_of(p.pages, b, r), ps = p.pages.page_size;
+            return (pg * Hkv + h) * ps + r % ps;
+        }
+        return ((int64_t)b * Hkv + h) * cap + r;
+    };
+
+    for (int j = threadIdx.x; j < half; j += kRopeThreads) {
+        const float ang = (float)pos * p.inv_freq[j];  // one fp32 multiply
+        sincos_angle(ang, s_cos + j, s_sin + j);
+    }
+    __syncthreads();
+
+    // rotation tasks, 16 bytes each: [q rotary | k rotary | k pass-through]
+    const int hc = half / 8, pc = (D - rot) / 8;
+    const int n_q = p.num_q_heads * hc, n_k = Hkv * hc, n_kp = Hkv * pc;
+    const int n_tasks = n_q + (write_cache ? n_k + n_kp : 0);
+    for (int t = threadIdx.x; t < n_tasks; t += kRopeThreads) {
+        if (t < n_q) {
+            const int h = t / hc, j = (t % hc) * 8;
+            uint16_t *qr = p.q + ((int64_t)b * p.num_q_heads + h) * D;
+            uint4 ya, yb;
+            rotate8(ld(qr + j), ld(qr + half + j), s_cos + j, s_sin + j, ya, yb);
+            st(qr + j, ya);
+            st(qr + half + j, yb);
+        } else if (t < n_q + n_k) {
+            const int u = t - n_q, h = u / hc, j = (u % hc) * 8;
+            const uint16_t *kr = p.k_new + ((int64_t)b * Hkv + h) * D;
+            uint4 ya, yb;
+            rotate8(ld(kr + j), ld(kr + half + j), s_cos + j, s_sin + j, ya, yb);
+            st(s_krow + h * D + j, ya);
+            st(s_krow + h * D + half + j, yb);
+        } else {
+            const int u = t - n_q - n_k, h = u / pc, d = rot + (u % pc) * 8;
+            st(s_krow + h * D + d, ld(p.k_new + ((int64_t)b * Hkv + h) * D + d));
+        }
+    }
+    __syncthreads();
+    if (!write_cache) return;
+
+    // quantization: rows [K heads | V heads], one wave each, lane = 4 dims
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int r = wave; r < 2 * Hkv; r += kRopeThreads / 64) {
+        const bool is_v = r >= Hkv;
+        const int h = is_v ? r - Hkv : r;
+        uint8_t *codes = is_v ? p.vq : p.kq;
+        float *scales = is_v ? p.vs : p.ks;
+        const int64_t slot = row_index(h, row);
+        if (evict) {  // the slot's entry moves to the evicted-entry row first (same lane)
+            const int64_t er = row_index(h, erow);
+            const uint32_t old = *reinterpret_cast<const uint32_t *>(codes + slot * D + 4 * lane);
+            const float old_s = scales[slot];
+            *reinterpret_cast<uint32_t *>(codes + er * D + 4 * lane) = old;
+            if (lane == 0) scales[er] = old_s;
+        }
+        const uint2 w = is_v ? *reinterpret_cast<const uint2 *>(p.v_new + ((int64_t)b * Hkv + h) * D + 4 * lane)
+                             : *reinterpret_cast<const uint2 *>(s_krow + h * D + 4 * lane);
+        const float x[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+        amax = wave_max64(amax);
+        const float sc = __fdiv_rn(amax, 448.f);
+        uint32_t packed = 0;
+        if (sc != 0.f) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) packed |= e4m3_rne(__fdiv_rn(x[e], sc)) << (8 * e);
+        }
+        *reinterpret_cast<uint32_t *>(codes + slot * D + 4 * lane) = packed;
+        if (lane == 0) scales[slot] = sc;
+    }
+}
+
+hipError_t launch_rope_append_fp8(const RopeAppendParams &p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    const size_t lds = (size_t)p.num_kv_heads * kHeadDim * sizeof(uint16_t);
+    hipLaunchKernelGGL(rope_append_fp8_kernel, dim3(p.batch), dim3(kRopeThreads), lds, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
     hipLaunchKernelGGL(rope_append_kernel, dim3(p.batch), dim3(kRopeThreads), 0, stream, p);

@@ -51,6 +51,12 @@ typedef enum hda_layer_type {
     HDA_FULL = 1
 } hda_layer_type;
 
+/* Element type of a KV cache (hda_cache_desc.kv_dtype). */
+typedef enum hda_kv_dtype {
+    HDA_KV_BF16 = 0,
+    HDA_KV_FP8_E4M3 = 1
+} hda_kv_dtype;
+
 /*
  * One layer's KV cache (Spark export page, `example_inputs`: caches are
  * laid out (batch, kv_heads, entries, head_dim)).
@@ -83,6 +89,27 @@ typedef enum hda_layer_type {
  * range (the result is then meaningless, but no access leaves the pool).
  * Pages may be shared between sequences for reading; an append writes row
  * pos of the page its sequence names.
+ *
+ * FP8 cache (kv_dtype HDA_KV_FP8_E4M3; HDA_KV_BF16, 0, is the bf16 cache
+ * above).  The flashmla_sparse page's FP8 call hands the cache to the
+ * kernel as raw bytes with an fp8 flag; the element format and scaling
+ * used here: every element an e4m3 code (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; no infinities, S.1111.111 is NaN; largest finite
+ * 448), every cached row -- one token of one KV head -- one fp32 scale:
+ *   value = e4m3(code) * scale,   scale = amax(row) / 448.
+ *   k, v        uint8 codes, same shapes as the bf16 cache (row = head_dim
+ *               bytes); head_dim must be 256
+ *   k_scale,    fp32 [batch, num_kv_heads, capacity] (paged: [num_pages,
+ *   v_scale     num_kv_heads, page_size]), 4-byte aligned, device memory;
+ *               a sliding layer's evicted-entry row has its scale at index
+ *               window-1 like its codes
+ * hda_rope_append quantizes the rotated new K row (rounded to bf16 first,
+ * as the bf16 cache would store it) and the new V row: scale = amax / 448
+ * in fp32, code = e4m3 of x / scale (fp32 division), round to nearest
+ * even, saturating at +-448; an all-zero row gets scale 0 and zero codes.
+ * The attention dequantizes exactly: K codes to bf16 for the matrix cores
+ * with the K scale applied to each key's score, V codes to fp32 with the V
+ * scale applied to each key's probability.
  */
 typedef struct hda_cache_desc {
     int32_t batch;
@@ -99,6 +126,9 @@ typedef struct hda_cache_desc {
     int32_t page_size;
     int32_t max_pages;
     int64_t num_pages;
+    int32_t kv_dtype;
+    float *k_scale;
+    float *v_scale;
 } hda_cache_desc;
 
 /*

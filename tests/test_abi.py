@@ -325,3 +325,46 @@ def test_paged_binding_desc():
     assert c.block_table == table.data_ptr()
     with pytest.raises(ValueError):
         hda.LayerCache(pool, pool, 8, 512, 64, 5e6, block_table=table.long()).desc()
+
+
+# ---------------------------------------------------------------- fp8 cache
+_FP8 = dict(kv_dtype=1, k_scale=FAKE, v_scale=FAKE)
+
+
+def test_fp8_descriptor_checks():
+    """An fp8 cache needs both scale arrays, 4-byte aligned, and head_dim 256;
+    an unknown element type is refused."""
+    assert _append(_desc(kv_dtype=2)) == 1 and "kv_dtype" in _msg()
+    assert _append(_desc(kv_dtype=1)) == 1 and "scale" in _msg()
+    assert _append(_desc(kv_dtype=1, k_scale=FAKE)) == 1
+    assert _append(_desc(**{**_FP8, "v_scale": FAKE + 2})) == 1 and "aligned" in _msg()
+    assert _append(_desc(**{**_FP8, "head_dim": 128, "rotary_dim": 128})) == 2
+
+
+def test_fp8_routing():
+    """The fp8 cache is read by the window and streaming kernels only."""
+    L = hda.lib()
+    full = _desc(**{**_FP8, "capacity": 4096, "rotary_dim": 64, "rope_theta": 5e6})
+    assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256) == 2 and "fp8" in _msg()
+    assert _step(_desc(**_FP8)) == 2 and "bf16" in _msg()
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(**_FP8)), hda.SLIDING) == 0
+    r = L.hda_decode_attn_partials(ctypes.c_void_p(FAKE), ctypes.byref(full), ctypes.c_void_p(FAKE),
+                                   hda.FULL, 0.0625, 4096, 256, ctypes.c_void_p(FAKE),
+                                   ctypes.c_void_p(FAKE), None)
+    assert r == 2 and "bf16" in _msg()
+
+
+def test_fp8_binding_desc():
+    import torch
+    codes = torch.zeros(2, 2, 512, 256, dtype=torch.uint8)
+    sc = torch.zeros(2, 2, 512, dtype=torch.float32)
+    c = hda.LayerCache(codes, codes, 8, 512, 256, 1e4, k_scale=sc, v_scale=sc).desc()
+    assert c.kv_dtype == 1 and c.k_scale == sc.data_ptr() and c.v_scale == sc.data_ptr()
+    assert hda.LayerCache(torch.zeros(2, 2, 512, 256, dtype=torch.bfloat16),
+                          torch.zeros(2, 2, 512, 256, dtype=torch.bfloat16), 8, 512, 256,
+                          1e4).desc().kv_dtype == 0
+    with pytest.raises(ValueError):
+        hda.LayerCache(codes, codes, 8, 512, 256, 1e4).desc()  # scales missing
+    with pytest.raises(ValueError):
+        hda.LayerCache(codes, codes, 8, 512, 256, 1e4, k_scale=sc[:, :, :10],
+                       v_scale=sc).desc()

@@ -94,6 +94,19 @@ def gate_logits(gen: torch.Generator, batch: int, num_heads: int, device="cpu") 
     return torch.randn(batch, num_heads, generator=gen, device=device, dtype=torch.float32)
 
 
+def fp8_codes(gen: torch.Generator, shape, device="cpu") -> torch.Tensor:
+    """Uniformly random e4m3 codes, uint8, never NaN (0x7F / 0xFF): every
+    sign, exponent and mantissa equally likely."""
+    c = torch.randint(0, 254, tuple(shape), generator=gen, device=device, dtype=torch.int32)
+    c = c + (c >= 0x7F).to(torch.int32)  # skip 0x7F; 0xFF is never reached
+    return c.to(torch.uint8)
+
+
+def fp8_scales(gen: torch.Generator, shape, device="cpu") -> torch.Tensor:
+    """Per-row scales, fp32 uniform in [1, 2) / 448 (largest values 1 .. 2)."""
+    return (torch.rand(tuple(shape), generator=gen, device=device, dtype=torch.float32) + 1.0) / 448.0
+
+
 @dataclass(frozen=True)
 class SparseShape:
     tokens: int = 32
