@@ -169,6 +169,7 @@ class Workload:
     def make_fp8(self, seed):
         """Give every layer an fp8 cache of the same shape: seeded random
         e4m3 codes (never NaN) and per-row scales in [1, 2) / 448."""
+        import torch
         import workloads
         import full_kv_cache_amd as hda
         s = self.shape
@@ -182,6 +183,10 @@ class Workload:
                 k_scale=workloads.fp8_scales(g, shp[:-1], c.k.device),
                 v_scale=workloads.fp8_scales(g, shp[:-1], c.k.device))
         self.fp8_row_bytes = 2 * s.num_kv_heads * (s.head_dim + 4)  # K and V codes + scales
+        need = max(hda.hda_decode_workspace_bytes(L["fcache"], L["lt"], self.max_seq_len, 0)
+                   for L in self.layers)
+        if need > self.workspace.numel():
+            self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.workspace.device)
 
     def fp8_call(self, L):
         import full_kv_cache_amd as hda

@@ -271,17 +271,65 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
 
     bf16x8 qa[8];
     WaveSoftmax<G> st;
+    auto end_segment = [&](const RoundAddr &a) {
+        const int64_t slot = (int64_t)w + a.b * Hkv + a.kvh;
+        store_partial<G>(st, p.part_o + slot * G * D, p.part_lse + slot * G, lane);
+    };
+
+    if constexpr (F8) {
+        // Rounds pipelined NB deep.  Buffer i % NB holds round g0 + i; the
+        // loop body is unrolled NB times so that every buffer index is a
+        // constant.  Rounds past g1 are placeholders (lane 0 addresses,
+        // never computed).  Measured on MI355X: fp8 rounds are bound by
+        // their compute chain, not by bytes in flight -- 4 deep at one wave
+        // per SIMD ran slower than 2 deep with the grid at every resident
+        // slot (two waves per SIMD hide each other's chains).
+        constexpr int NB = 2;
+        KV kb[NB][8], vb[NB][8];
+        float ksb[NB], vsb[NB];
+        RoundAddr ad[NB];
+        RoundGeo ge[NB];
+        ad[0] = cur;
+#pragma unroll
+        for (int i = 1; i < NB - 1; ++i) ad[i] = g0 + i < g1 ? advance(ad[i - 1]) : ad[i - 1];
+        load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) {
+            ge[i] = geo(ad[i]);
+            issue(ge[i], g0 + i < g1 ? lane : 0, kb[i], vb[i], ksb[i], vsb[i]);
+        }
+        st.reset();
+        int64_t g = g0;
+        while (true) {
+#pragma unroll
+            for (int s = 0; s < NB; ++s) {
+                const int t = (s + NB - 1) % NB, prv = (s + NB - 2) % NB;
+                const bool live = g + NB - 1 < g1;
+                ad[t] = live ? advance(ad[prv]) : ad[prv];
+                ge[t] = geo(ad[t]);
+                issue(ge[t], live ? lane : 0, kb[t], vb[t], ksb[t], vsb[t]);
+                st.template round<false, true>(qa, kb[s], vb[s], ge[s].lo, ge[s].hi, p.scale_log2,
+                                               s_pw, s_kt, lane, -1, nullptr, nullptr, ksb[s],
+                                               vsb[s]);
+                const bool more = g + 1 < g1;
+                const RoundAddr &nx = ad[(s + 1) % NB];
+                if (!more || !same_pair(nx, ad[s])) {
+                    end_segment(ad[s]);
+                    if (!more) return;
+                    load_q_operand<G>(p.q, p.num_q_heads, nx.b, nx.kvh, lane, qa);
+                    st.reset();
+                }
+                ++g;
+            }
+        }
+    }
+
     KV kA[8], vA[8], kB[8], vB[8];
     float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
     RoundGeo gc = geo(cur);
     issue(gc, lane, kA, vA, ksA, vsA);
     load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
     st.reset();
-
-    auto end_segment = [&](const RoundAddr &a) {
-        const int64_t slot = (int64_t)w + a.b * Hkv + a.kvh;
-        store_partial<G>(st, p.part_o + slot * G * D, p.part_lse + slot * G, lane);
-    };
 
     // Every half-iteration issues the next round's loads, then computes the
     // current round.  After the last round a placeholder round is issued
@@ -435,6 +483,29 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
         // The q operand goes out between the first batch's two rounds, so
         // that the first round waits for it and not for the second.
         bf16x8 qa[8];
+        if constexpr (F8) {
+            // Batches of NB rounds issued together (2 measured slightly
+            // faster than 4 here).
+            constexpr int NB = 2;
+            KV kb[NB][8], vb[NB][8];
+            float ksb[NB], vsb[NB];
+            load_q_operand<GW>(p.q, p.num_q_heads, b, hsub, lane, qa);
+            for (int r = r_lo; r < r_hi; r += NB) {
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    const bool live = r + i < r_hi;
+                    issue(r0e_of(live ? r + i : r), live ? lane : 0, kb[i], vb[i], ksb[i], vsb[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    if (r + i >= r_hi) break;
+                    const int e = r0e_of(r + i);
+                    st.template round<false, true>(qa, kb[i], vb[i], 16 * (r + i) - e, n - e,
+                                                   p.scale_log2, s_pw[wave], s_kt[wave], lane, -1,
+                                                   nullptr, nullptr, ksb[i], vsb[i]);
+                }
+            }
+        } else {
         KV kA[8], vA[8], kB[8], vB[8];
         float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
         {
@@ -457,6 +528,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
             st.template round<false, F8>(qa, kB, vB, 16 * (r + 1) - e, n - e, p.scale_log2,
                                          s_pw[wave], s_kt[wave], lane, -1, nullptr, nullptr, ksB,
                                          vsB);
+        }
         }
     }
 
