@@ -208,6 +208,38 @@ def output_gate(out, gate):
     _load().or_output_gate(_p(out), B, Hq, D, _p(gate))
 
 
+# ------------------------------------------------------ multi-token decode
+
+def decode_multi(q, k_new, v_new, pos, layer_type, rot, theta, window, k, v, kev, vev, sinks,
+                 scale, gate=None):
+    """A chunk of T new tokens per sequence (q [B,T,Hq,D], k_new / v_new
+    [B,T,Hkv,D], bf16 bits; pos [B] = position of token 0).  Spark export
+    page, `SparkStepConfig.cache_len` docstring: a ring holds the window's
+    previous entries and the new token is scored with them, so a chunk
+    means token t attends to what is cached in its window plus new tokens
+    0..t -- the plain definition is T single-token decode steps in order:
+    step t appends token t at pos + t (or_rope_append) and attends with
+    seq_len pos + t + 1 (or_decode_attn).  The cache (oracle form: k, v
+    [B,Hkv,cap,D], side rows kev, vev [B,Hkv,D]) is updated in place and q
+    is rotated in place, as the single-token functions do.
+    gate: fp32 [B,T,Hq] logits or None.  Returns out fp64 [B,T,Hq,D], lse
+    fp64 [B,T,Hq]."""
+    assert q.dtype == np.uint16 and q.flags.c_contiguous and q.ndim == 4
+    B, T, Hq, D = q.shape
+    pos = _i32(pos)
+    out = np.zeros((B, T, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, T, Hq), dtype=np.float64)
+    for t in range(T):
+        qt = np.ascontiguousarray(q[:, t])
+        rope_append(qt, np.ascontiguousarray(k_new[:, t]), np.ascontiguousarray(v_new[:, t]),
+                    pos + t, layer_type, rot, theta, window, k, v, kev, vev)
+        q[:, t] = qt
+        g = None if gate is None else np.ascontiguousarray(np.asarray(gate)[:, t])
+        out[:, t], lse[:, t] = decode_attn(qt, k, v, kev, vev, pos + t + 1, layer_type, window,
+                                           sinks, scale, gate=g)
+    return out, lse
+
+
 # ------------------------------------------------------------- FP8 KV
 
 def e4m3_to_f64(code: int) -> float:
