@@ -33,7 +33,10 @@ layer's cache held in a shuffled pool of 64-row pages read through a block
 table (flashmla_sparse page, `_fp8_flash_mla_kernel`; paged_ms_per_step and
 the paged full-layer kernel in "paged"), and the same step on an FP8 KV
 cache -- e4m3 codes with one fp32 scale per row, quantized on append, the
-reading of that page's fp8 call -- in "fp8".
+reading of that page's fp8 call -- in "fp8"; and chunks of 4 new tokens
+per sequence through hda_decode_multi on every layer (Spark export page,
+`SparkStepConfig.cache_len` docstring: each token attends to its own
+window) in "multi".
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
                     [--path auto|fused|separate]
@@ -87,6 +90,8 @@ def parse():
     ap.add_argument("--page-size", type=int, default=64,
                     help="rows per page of the paged full-layer measurement (0: skip it)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache measurement")
+    ap.add_argument("--multi-tokens", type=int, default=4,
+                    help="tokens per chunk of the chunk-decode measurement (0: skip it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of this many MB (PMC byte calibration)")
     return ap.parse_args()
@@ -187,6 +192,31 @@ class Workload:
                    for L in self.layers)
         if need > self.workspace.numel():
             self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.workspace.device)
+
+    def make_multi(self, T, seed):
+        """Chunk inputs for every layer: q [B,T,Hq,D], k_new / v_new
+        [B,T,Hkv,D], out [B,T,Hq,D]; token 0 at seq_len - T, so the last
+        token of a chunk attends to as many keys as the one-token step."""
+        import torch
+        import workloads
+        s, B = self.shape, self.cfg["batch"]
+        g = workloads.generator(seed + 5, self.seq_lens.device)
+        self.multi_T = T
+        self.multi_pos = (self.seq_lens - T).clamp(min=0).to(torch.int32).contiguous()
+        for L in self.layers:
+            L["mq"] = workloads.randn_bf16(g, (B, T, s.num_q_heads, s.head_dim), self.seq_lens.device)
+            L["mk"] = workloads.randn_bf16(g, (B, T, s.num_kv_heads, s.head_dim), self.seq_lens.device)
+            L["mv"] = workloads.randn_bf16(g, (B, T, s.num_kv_heads, s.head_dim), self.seq_lens.device)
+            L["mout"] = torch.empty(B, T, s.num_q_heads, s.head_dim, dtype=torch.bfloat16,
+                                    device=self.seq_lens.device)
+        old = self.multi_pos.cpu().long()
+        self.multi_rows = {lt: int((old.clamp(max=s.window - 1) if lt == workloads.SLIDING else old).sum()
+                                   + B * T) for lt in (workloads.SLIDING, workloads.FULL)}
+
+    def multi_call(self, L):
+        import full_kv_cache_amd as hda
+        hda.hda_decode_multi(L["mq"], L["mk"], L["mv"], self.multi_pos, L["lt"], L["cache"],
+                             L["sinks"], self.scale, L["mout"])
 
     def fp8_call(self, L):
         import full_kv_cache_amd as hda
@@ -530,6 +560,22 @@ def main():
             byts = wl.rows[lt] * wl.fp8_row_bytes
             fp8[f"{name}_attn_us"] = round(us, 2)
             fp8[f"{name}_attn_GB/s"] = round(byts / (us / 1e6) / 1e9, 1)
+    multi = None
+    if args.multi_tokens:
+        T = args.multi_tokens
+        print(f"# timing chunk decode, {T} tokens per sequence", file=sys.stderr, flush=True)
+        wl.make_multi(T, args.seed)
+        torch.cuda.synchronize()
+
+        def multi_step():
+            for L in wl.layers:
+                wl.multi_call(L)
+        m_ms, _ = time_graph(multi_step, args.steps, args.warmup, use_graph=not args.no_graph)
+        m_bytes = sum(wl.multi_rows[L["lt"]] for L in wl.layers) * wl.kv_row_bytes
+        multi = {"tokens_per_chunk": T, "ms_per_step": round(m_ms, 4),
+                 "tokens_per_s": round(cfg["batch"] * T / (m_ms / 1e3), 1),
+                 "kv_bytes_per_step": m_bytes, "GB/s": round(m_bytes / (m_ms / 1e3) / 1e9, 1),
+                 "path": "hda_decode_multi on every layer (RoPE, attention, append: 3 launches)"}
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
@@ -558,7 +604,7 @@ def main():
         "paged_ms_per_step": None if paged_ms is None else round(paged_ms, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": roof, "layer_kernels": {"sliding": k_slide, "full": k_full},
-        "cpu_baseline": cpu, "sparse": sparse, "paged": k_paged, "fp8": fp8,
+        "cpu_baseline": cpu, "sparse": sparse, "paged": k_paged, "fp8": fp8, "multi": multi,
     }
     print(json.dumps(rec), flush=True)
 

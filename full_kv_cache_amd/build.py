@@ -22,7 +22,8 @@ LIB = HERE / "libhda.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["hda_api.cpp", "rope_append.hip", "decode_attn.hip", "decode_step.hip", "sparse_attn.hip"]
+SOURCES = ["hda_api.cpp", "rope_append.hip", "decode_attn.hip", "decode_step.hip", "sparse_attn.hip",
+           "decode_multi.hip"]
 
 
 def compile_flags() -> list[str]:

@@ -143,12 +143,16 @@ struct WaveSoftmax {
     // key's K scale (ksc, lane = key mrow's scale), the probabilities sent to
     // the P.V lanes its V scale (vsc) -- the running sum keeps the unscaled
     // ones -- and the V codes become fp32 (exact).
-    template <bool SUB = false, bool F8 = false, typename KV = uint4>
+    // ROWMASK (several query rows per head group, e.g. the tokens of a
+    // chunk): row 4*kg + i also needs dkey >= trow[i] for this lane's key.
+    // A row may then see no key in a round, so -inf maxima are guarded.
+    template <bool SUB = false, bool F8 = false, typename KV = uint4, bool ROWMASK = false>
     __device__ __forceinline__ void round(const bf16x8 *qa, const KV *kt, KV *vt, int lo,
                                           int hi, float scale_log2, float *pw, uint16_t *ktile, int lane,
                                           int vr = -1, const uint16_t *knew = nullptr,
                                           const uint16_t *vnew = nullptr, float ksc = 1.f,
-                                          float vsc = 1.f) {
+                                          float vsc = 1.f, int dkey = 0,
+                                          const int *trow = nullptr) {
         const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -174,10 +178,18 @@ struct WaveSoftmax {
         float alpha[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float s = valid ? sc[i] * kf : -INFINITY;
+            bool vi = valid;
+            if constexpr (ROWMASK) vi = vi && dkey >= trow[i];
+            float s = vi ? sc[i] * kf : -INFINITY;
             const float mn = fmaxf(m_run[i], row16_max(s));  // finite: the round holds a key
-            alpha[i] = fast_exp2(m_run[i] - mn);
-            s = fast_exp2(s - mn);
+            if constexpr (ROWMASK) {
+                const bool none = mn == -INFINITY;  // no key for this row yet
+                alpha[i] = none ? 1.f : fast_exp2(m_run[i] - mn);
+                s = none ? 0.f : fast_exp2(s - mn);
+            } else {
+                alpha[i] = fast_exp2(m_run[i] - mn);
+                s = fast_exp2(s - mn);
+            }
             l_lane[i] = fmaf(l_lane[i], alpha[i], s);
             m_run[i] = mn;
             sc[i] = s;

@@ -674,6 +674,61 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
                     "decode step");
 }
 
+hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32_t *pos,
+                            int32_t tokens, hda_layer_type layer, const hda_cache_desc *cache,
+                            const float *sinks, const float *gate, float scale, void *out,
+                            float *lse, void *stream) {
+    hda_status st = check_cache(cache, layer);
+    if (st != HDA_OK) return st;
+    if (!q || !k_new || !v_new || !pos || !out)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new, pos and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new and out must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(pos) & 3u)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "pos must be 4-byte aligned");
+    if ((st = check_f32_ptrs(sinks, gate, lse)) != HDA_OK) return st;
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
+    if (cache->head_dim != hda::kHeadDim)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels are built for head_dim %d, got %d",
+                    hda::kHeadDim, cache->head_dim);
+    const int g = cache->num_q_heads / cache->num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+        return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
+    if (tokens < 1 || tokens > 4 || g * tokens > 16)
+        return fail(HDA_ERR_UNSUPPORTED, "a chunk holds 1..4 tokens with tokens x group <= 16 "
+                    "query rows, got %d tokens for group %d", tokens, g);
+    if (cache->rotary_dim % 16)
+        return fail(HDA_ERR_UNSUPPORTED, "rotary_dim %d is not a multiple of 16", cache->rotary_dim);
+    if (cache->capacity < 16)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels need a cache of at least 16 rows");
+    if (cache->block_table || cache->kv_dtype != HDA_KV_BF16)
+        return fail(HDA_ERR_UNSUPPORTED, "chunk decode is built for contiguous bf16 caches");
+    if (cache->batch == 0) return ok();
+    hda::MultiParams p{};
+    p.q = static_cast<uint16_t *>(q);
+    p.k_new = static_cast<uint16_t *>(k_new);
+    p.v_new = static_cast<const uint16_t *>(v_new);
+    p.pos = pos;
+    p.k = static_cast<uint16_t *>(cache->k);
+    p.v = static_cast<uint16_t *>(cache->v);
+    p.sinks = sinks;
+    p.gate = gate;
+    p.out = static_cast<uint16_t *>(out);
+    p.lse = lse;
+    p.capacity = cache->capacity;
+    p.batch = cache->batch;
+    p.tokens = tokens;
+    p.num_q_heads = cache->num_q_heads;
+    p.num_kv_heads = cache->num_kv_heads;
+    p.rotary_dim = cache->rotary_dim;
+    p.window = cache->window;
+    p.sliding = layer == HDA_SLIDING;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    fill_inv_freq(p.inv_freq, cache->rope_theta, cache->rotary_dim);
+    return launched(hda::launch_decode_multi(p, g, static_cast<hipStream_t>(stream)), "chunk decode");
+}
+
 hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_rows,
                                   const int32_t *indices, int32_t tokens, int32_t topk,
                                   const int32_t *topk_length, int32_t num_q_heads, int32_t dqk,

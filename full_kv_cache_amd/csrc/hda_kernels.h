@@ -120,6 +120,26 @@ struct SparseParams {
     float scale_log2;           // softmax scale * log2(e)
 };
 
+// Decode of a chunk of `tokens` new tokens per sequence (q [B, T, Hq, D],
+// k_new / v_new [B, T, Hkv, D]; contiguous bf16 cache).
+struct MultiParams {
+    uint16_t *q;                // rotated in place
+    uint16_t *k_new;            // rotated in place
+    const uint16_t *v_new;
+    const int32_t *pos;         // [B] position of token 0
+    uint16_t *k, *v;            // [B, Hkv, cap, D]
+    const float *sinks;         // [Hq] or null
+    const float *gate;          // [B, T, Hq] or null
+    uint16_t *out;              // [B, T, Hq, D]
+    float *lse;                 // [B, T, Hq] or null
+    int64_t capacity;
+    int batch, tokens, num_q_heads, num_kv_heads, rotary_dim, window;
+    int sliding;
+    float scale_log2;
+    float inv_freq[kHeadDim / 2];
+};
+hipError_t launch_decode_multi(const MultiParams &p, int group, hipStream_t stream);
+
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 // The same for an fp8 cache (kq/vq/ks/vs set; head_dim 256): the new K and
 // V rows are quantized into e4m3 codes with one scale per row.

@@ -322,6 +322,35 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * hda_decode_multi -- decode of a chunk of `tokens` new tokens per sequence
+ * in one call.  Spark export page, `SparkStepConfig.cache_len` docstring: a
+ * ring holds a window's previous entries and the new token is scored with
+ * them; for a chunk, token t (position pos[b] + t) attends to the entries
+ * of its own window -- the cached ones and new tokens 0..t -- exactly as
+ * `tokens` single-token steps (hda_rope_append + hda_decode_attn with
+ * seq_len pos + t + 1) in order would, and the cache ends as they leave it.
+ *   q       bf16 [batch, tokens, num_q_heads, head_dim], rotated in place
+ *   k_new   bf16 [batch, tokens, num_kv_heads, head_dim], rotated in place
+ *   v_new   bf16 [batch, tokens, num_kv_heads, head_dim], read only
+ *   pos     int32 [batch] (device): position of token 0; a negative value
+ *           leaves the sequence's cache alone and its out 0, lse -inf
+ *   out     bf16 [batch, tokens, num_q_heads, head_dim]
+ *   lse     fp32 [batch, tokens, num_q_heads] or NULL (before the sink)
+ *   sinks   fp32 [num_q_heads] or NULL; gate fp32 [batch, tokens,
+ *           num_q_heads] logits or NULL (as in hda_decode_attn)
+ * The cache is read as it was before the chunk and written after the
+ * attention (full: rows pos + t below capacity; sliding: ring slots, the
+ * evicted-entry row taking what the last token's slot held).  No
+ * workspace.  Errors: as hda_decode_attn, plus UNSUPPORTED for tokens
+ * outside 1..4 or tokens x (num_q_heads / num_kv_heads) > 16, rotary_dim
+ * not a multiple of 16, a paged or fp8 cache.  batch == 0 is a no-op.
+ */
+hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32_t *pos,
+                            int32_t tokens, hda_layer_type layer, const hda_cache_desc *cache,
+                            const float *sinks, const float *gate, float scale, void *out,
+                            float *lse, void *stream);
+
+/*
  * hda_sparse_workspace_bytes -- device workspace hda_sparse_decode_attn needs
  * for this many tokens, query heads and index-row length (0: none).
  * Returns 0 for an invalid shape as well; the call then reports why.

@@ -368,3 +368,27 @@ def test_fp8_binding_desc():
     with pytest.raises(ValueError):
         hda.LayerCache(codes, codes, 8, 512, 256, 1e4, k_scale=sc[:, :, :10],
                        v_scale=sc).desc()
+
+
+# ------------------------------------------------------------- chunk decode
+def _multi(desc, tokens=2, layer=hda.SLIDING, q=FAKE, pos=FAKE, scale=0.0625):
+    L = hda.lib()
+    return L.hda_decode_multi(ctypes.c_void_p(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                              ctypes.c_void_p(pos), tokens, layer, ctypes.byref(desc), None, None,
+                              scale, ctypes.c_void_p(FAKE), None, None)
+
+
+def test_multi_checks():
+    """Chunk decode: 1..4 tokens with tokens x group <= 16 rows, contiguous
+    bf16 caches, the usual pointer and shape checks."""
+    assert _multi(_desc(), tokens=0) == 2 and "tokens" in _msg()
+    assert _multi(_desc(), tokens=5) == 2
+    assert _multi(_desc(num_q_heads=32, num_kv_heads=2), tokens=2) == 2  # 16 x 2 rows
+    assert _multi(_desc(), q=0) == 1
+    assert _multi(_desc(), pos=FAKE + 2) == 1 and "aligned" in _msg()
+    assert _multi(_desc(), scale=0.0) == 1
+    assert _multi(_desc(head_dim=128, rotary_dim=128)) == 2
+    assert _multi(_desc(rotary_dim=24)) == 2
+    assert _multi(_desc(**_FP8)) == 2 and "bf16" in _msg()
+    assert _multi(_desc(**{**_PAGED, "rotary_dim": 64}), layer=hda.FULL) == 2
+    assert _multi(_desc(batch=0)) == 0

@@ -1,0 +1,161 @@
+"""GPU parity of the chunk decode (hda_decode_multi: T new tokens per
+sequence in one call; Spark export page, `SparkStepConfig.cache_len`
+docstring -- token t attends to the entries of its own window, cached ones
+and new tokens 0..t) against the oracle's T single-token steps in order.
+
+Checked: out (max-abs <= 1e-2, mean-abs <= 1e-3) and lse (1e-4) for every
+token; q and the new K rotated in place within one bf16 ulp; the cache
+after the call -- V bit-exact, rotated K within one bf16 ulp, the sliding
+block's evicted-entry row holding what the last token's slot held.  Rows
+the chunk must not read (full: at and past pos; sliding: unwritten slots
+and the evicted-entry row) are NaN.  Cases: windows crossing the ring's
+511/512 boundaries inside the chunk, an empty cache, T = 1..4, group sizes
+1 to 16, sinks and the output gate, a negative position.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from hybrid_case import BF16_NAN, assert_attn_close, bf16_ulp_diff, bits_of, to_f64
+from workloads import FULL, SLIDING
+
+pytestmark = pytest.mark.gpu
+W = 512
+D = 256
+
+
+class MultiCase:
+    def __init__(self, seed, lt, pos, T, cap=None, hq=8, hkv=2):
+        self.lt, self.T = lt, T
+        self.pos = np.asarray(pos, np.int32)
+        B = len(pos)
+        self.hq, self.hkv = hq, hkv
+        cap = W if lt == SLIDING else (cap or int(self.pos.max()) + T)
+        g = workloads.generator(seed)
+        rb = lambda shp: workloads.bits(workloads.randn_bf16(g, shp)).copy()
+        self.q = rb((B, T, hq, D))
+        self.k_new, self.v_new = rb((B, T, hkv, D)), rb((B, T, hkv, D))
+        self.k, self.v = rb((B, hkv, cap, D)), rb((B, hkv, cap, D))
+        for b, p in enumerate(self.pos):
+            lo = max(p, 0) if lt == FULL else (max(p, 0) if p < W - 1 else W - 1)
+            for a in (self.k, self.v):
+                a[b, :, lo:] = BF16_NAN
+                if lt == SLIDING:
+                    a[b, :, W - 1] = BF16_NAN  # the chunk never reads the evicted-entry row
+        shape = workloads.HybridShape(batch=B, lmax=16, num_q_heads=hq, num_kv_heads=hkv)
+        self.rot, self.theta = shape.rot(lt), shape.theta(lt)
+
+    def oracle(self, sinks=None, gate=None):
+        q, k, v = self.q.copy(), self.k.copy(), self.v.copy()
+        if self.lt == SLIDING:
+            kr, vr = np.ascontiguousarray(k[:, :, :W - 1]), np.ascontiguousarray(v[:, :, :W - 1])
+            kev, vev = np.ascontiguousarray(k[:, :, W - 1]), np.ascontiguousarray(v[:, :, W - 1])
+        else:
+            kr, vr = k, v
+            kev = np.zeros((k.shape[0], self.hkv, D), np.uint16)
+            vev = kev.copy()
+        live = self.pos >= 0
+        out = np.zeros(q.shape, np.float64)
+        lse = np.full(q.shape[:3], -np.inf)
+        if live.any():
+            sub = lambda a: np.ascontiguousarray(a[live])
+            qs, krs, vrs, kevs, vevs = sub(q), sub(kr), sub(vr), sub(kev), sub(vev)
+            o, l = oracle.decode_multi(qs, sub(self.k_new), sub(self.v_new), self.pos[live],
+                                       self.lt, self.rot, self.theta, W, krs, vrs, kevs, vevs,
+                                       sinks, 1 / 16, None if gate is None else sub(gate))
+            out[live], lse[live] = o, l
+            q[live], kr[live], vr[live], kev[live], vev[live] = qs, krs, vrs, kevs, vevs
+        if self.lt == SLIDING:
+            k = np.concatenate([kr, kev[:, :, None]], axis=2)
+            v = np.concatenate([vr, vev[:, :, None]], axis=2)
+        return q, k, v, out, lse
+
+    def gpu(self, sinks=None, gate=None):
+        import full_kv_cache_amd as hda
+        dev = {n: workloads.from_bits(getattr(self, n)).cuda()
+               for n in ("q", "k_new", "v_new", "k", "v")}
+        cache = hda.LayerCache(dev["k"], dev["v"], self.hq, W, self.rot, self.theta)
+        out = torch.full(self.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full(self.q.shape[:3], float("nan"), device="cuda")
+        sk = None if sinks is None else torch.as_tensor(sinks).cuda()
+        gt = None if gate is None else torch.as_tensor(gate).cuda()
+        hda.hda_decode_multi(dev["q"], dev["k_new"], dev["v_new"], torch.from_numpy(self.pos).cuda(),
+                             self.lt, cache, sk, 1 / 16, out, lse, gate=gt)
+        torch.cuda.synchronize()
+        return dev, out, lse
+
+
+def _check(case, sinks=None, gate=None):
+    q_ref, k_ref, v_ref, ref, rlse = case.oracle(sinks, gate)
+    dev, out, lse = case.gpu(sinks, gate)
+    for name, got, want in (("q", bits_of(dev["q"]), q_ref), ("k", bits_of(dev["k"]), k_ref)):
+        ulps = bf16_ulp_diff(got, want)
+        assert ulps.max() <= 1, (name, ulps.max())
+        assert (ulps > 0).mean() < 1e-3, name
+    assert np.array_equal(bits_of(dev["v"]), v_ref)
+    live = case.pos >= 0
+    assert_attn_close(out[torch.from_numpy(live)], ref[live])
+    np.testing.assert_allclose(to_f64(lse)[live], rlse[live], rtol=0, atol=1e-4)
+    if not live.all():
+        dead = torch.from_numpy(~live)
+        assert torch.all(out[dead].float() == 0) and torch.all(torch.isneginf(lse[dead]))
+
+
+@pytest.mark.parametrize("lt,pos,T", [
+    (SLIDING, [0, 509, 2000, 510], 4),    # empty ring; chunks crossing slots 510 / 511; wrapped
+    (SLIDING, [300, 1021], 3),
+    (SLIDING, [5, 511, 4095], 1),
+    (FULL, [0, 40, 1500, 17], 4),
+    (FULL, [7, 999], 2),
+    (FULL, [3, 2000, 64], 3),
+])
+def test_multi_parity(lt, pos, T):
+    print("CASE multi", lt, pos, T, flush=True)
+    case = MultiCase(3000 + 10 * T + lt, lt, pos, T, cap=2048 if lt == FULL else None)
+    Hq = case.hq
+    sk = np.linspace(-1.0, 3.0, Hq).astype(np.float32)
+    g = np.random.default_rng(T).uniform(-3, 3, size=(len(pos), T, Hq)).astype(np.float32)
+    _check(case, sinks=sk, gate=g)
+
+
+@pytest.mark.parametrize("hq,hkv,T", [(2, 2, 4), (4, 2, 4), (16, 2, 2), (32, 2, 1)])
+def test_multi_groups(hq, hkv, T):
+    """Query groups 1, 2, 8, 16: tokens x group query rows per KV head."""
+    for lt, pos in ((SLIDING, [700, 100]), (FULL, [900, 33])):
+        print("CASE multi groups", hq, hkv, T, lt, flush=True)
+        case = MultiCase(3100 + hq + T + lt, lt, pos, T, cap=1024, hq=hq, hkv=hkv)
+        _check(case)
+
+
+def test_multi_negative_position():
+    print("CASE multi negative", flush=True)
+    case = MultiCase(3200, FULL, [50, -1, 7], 2, cap=128)
+    _check(case)
+    import full_kv_cache_amd as hda
+    dev, _, _ = case.gpu()
+    assert np.array_equal(bits_of(dev["k"])[1], case.k[1])  # nothing appended
+
+
+def test_multi_equals_single_steps_on_device():
+    """T = 1 through hda_decode_multi and the single-token path agree within
+    the decode tolerance (different kernels, same keys)."""
+    import full_kv_cache_amd as hda
+    print("CASE multi vs single", flush=True)
+    case = MultiCase(3300, SLIDING, [600, 20, 1500], 1)
+    dev, out, lse = case.gpu()
+    d2 = {n: workloads.from_bits(getattr(case, n)).cuda() for n in ("q", "k_new", "v_new", "k", "v")}
+    cache = hda.LayerCache(d2["k"], d2["v"], case.hq, W, case.rot, case.theta)
+    pos = torch.from_numpy(case.pos).cuda()
+    q1 = d2["q"][:, 0].contiguous()
+    hda.hda_rope_append(q1, d2["k_new"][:, 0].contiguous(), d2["v_new"][:, 0].contiguous(), pos,
+                        SLIDING, cache)
+    o1 = torch.empty_like(q1)
+    l1 = torch.empty(q1.shape[:2], device="cuda")
+    hda.hda_decode_attn(q1, cache, pos + 1, SLIDING, None, 1 / 16, o1, l1, W, 0, None)
+    torch.cuda.synchronize()
+    assert_attn_close(out[:, 0], to_f64(o1))
+    np.testing.assert_allclose(to_f64(lse[:, 0]), to_f64(l1), rtol=0, atol=1e-4)
+    assert torch.equal(dev["k"].view(torch.int16), d2["k"].view(torch.int16))
+    assert torch.equal(dev["v"].view(torch.int16), d2["v"].view(torch.int16))
