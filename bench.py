@@ -286,14 +286,15 @@ def layer_path(path, lt):
 # Kernels a layer call runs on each path (the window kernels serve every
 # sliding layer: keys <= 1024; full layers at this shape take the stream).
 KERNELS = {
-    ("separate", "sliding"): "decode_pair_kernel<2>",
-    ("separate", "full"): "decode_stream_kernel<4> + stream_merge_kernel",
+    ("separate", "sliding"): "decode_pair_kernel<2, false>",
+    ("separate", "full"): "decode_stream_kernel<4, false> + stream_merge_kernel",
     ("fused", "sliding"): "decode_window_step_kernel<2, 256>",
     ("fused", "full"): "decode_step_kernel<4, 64>",
 }
 # Sources whose change invalidates a committed traffic measurement.
 TRAFFIC_SOURCES = ("decode_attn.hip", "decode_wave.h", "decode_step.hip", "hda_device.h",
-                   "hda_kernels.h", "hda_api.cpp", "rope_append.hip", "sparse_attn.hip")
+                   "hda_kernels.h", "hda_api.cpp", "rope_append.hip", "sparse_attn.hip",
+                   "decode_multi.hip")
 
 
 def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0, paged=False):
