@@ -209,6 +209,10 @@ class Workload:
             L["mv"] = workloads.randn_bf16(g, (B, T, s.num_kv_heads, s.head_dim), self.seq_lens.device)
             L["mout"] = torch.empty(B, T, s.num_q_heads, s.head_dim, dtype=torch.bfloat16,
                                     device=self.seq_lens.device)
+        import full_kv_cache_amd as hda
+        need = max(hda.hda_decode_multi_workspace_bytes(L["cache"], L["lt"], T, self.max_seq_len)
+                   for L in self.layers)
+        self.multi_ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.seq_lens.device)
         old = self.multi_pos.cpu().long()
         self.multi_rows = {lt: int((old.clamp(max=s.window - 1) if lt == workloads.SLIDING else old).sum()
                                    + B * T) for lt in (workloads.SLIDING, workloads.FULL)}
@@ -216,7 +220,8 @@ class Workload:
     def multi_call(self, L):
         import full_kv_cache_amd as hda
         hda.hda_decode_multi(L["mq"], L["mk"], L["mv"], self.multi_pos, L["lt"], L["cache"],
-                             L["sinks"], self.scale, L["mout"])
+                             L["sinks"], self.scale, L["mout"], max_seq_len=self.max_seq_len,
+                             workspace=self.multi_ws)
 
     def fp8_call(self, L):
         import full_kv_cache_amd as hda
@@ -576,7 +581,8 @@ def main():
         multi = {"tokens_per_chunk": T, "ms_per_step": round(m_ms, 4),
                  "tokens_per_s": round(cfg["batch"] * T / (m_ms / 1e3), 1),
                  "kv_bytes_per_step": m_bytes, "GB/s": round(m_bytes / (m_ms / 1e3) / 1e9, 1),
-                 "path": "hda_decode_multi on every layer (RoPE, attention, append: 3 launches)"}
+                 "path": "hda_decode_multi on every layer (RoPE, attention split over workgroups "
+                         "+ merge, append: 4 launches)"}
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)

@@ -99,7 +99,9 @@ def lib() -> ctypes.CDLL:
                                       P]
         L.hda_decode_multi.restype = ctypes.c_int
         L.hda_decode_multi.argtypes = [P, P, P, P, i32, ctypes.c_int, D, P, P, ctypes.c_float, P,
-                                       P, P]
+                                       P, i32, P, sz, P]
+        L.hda_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+        L.hda_decode_multi_workspace_bytes.argtypes = [D, ctypes.c_int, i32, i32]
         L.hda_sparse_workspace_bytes.restype = ctypes.c_size_t
         L.hda_sparse_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.hda_sparse_decode_attn.restype = ctypes.c_int
@@ -286,20 +288,33 @@ def hda_decode_step(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, si
                                  _ptr(workspace), wbytes, _stream(stream)))
 
 
+def hda_decode_multi_workspace_bytes(cache: LayerCache, layer_type: int, tokens: int,
+                                     max_seq_len: int) -> int:
+    d = cache.desc()
+    return int(lib().hda_decode_multi_workspace_bytes(ctypes.byref(d), int(layer_type),
+                                                      int(tokens), int(max_seq_len)))
+
+
 def hda_decode_multi(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, sinks,
-                     scale: float, out, lse=None, stream=None, gate=None):
+                     scale: float, out, lse=None, stream=None, gate=None, max_seq_len=None,
+                     workspace=None):
     """Decode of a chunk of T new tokens per sequence: q [B, T, Hq, D] and
     k_new [B, T, Hkv, D] are rotated in place, v_new [B, T, Hkv, D] is read;
-    out [B, T, Hq, D], lse [B, T, Hq]; gate: optional fp32 [B, T, Hq] logits."""
+    out [B, T, Hq, D], lse [B, T, Hq]; gate: optional fp32 [B, T, Hq] logits.
+    max_seq_len: host bound on pos + T (default: the cache capacity);
+    workspace: hda_decode_multi_workspace_bytes() bytes of device memory."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, Hq, D]")
     validate_sinks(sinks, q[:, 0])
     if gate is not None:
         validate_gate(gate.reshape(-1, gate.shape[-1]), out.reshape(-1, *out.shape[2:]))
     d = cache.desc()
+    msl = int(d.capacity if max_seq_len is None else max_seq_len)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hda_decode_multi(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos), int(q.shape[1]),
                                   int(layer_type), ctypes.byref(d), _ptr(sinks), _ptr(gate),
-                                  float(scale), _ptr(out), _ptr(lse), _stream(stream)))
+                                  float(scale), _ptr(out), _ptr(lse), msl, _ptr(workspace),
+                                  wbytes, _stream(stream)))
 
 
 def hda_sparse_workspace_bytes(tokens: int, num_q_heads: int, topk: int, dv: int = 512) -> int:

@@ -9,14 +9,16 @@
 //   1. rope_multi_kernel: q and the new K rotated in place at pos + t
 //      (the single-token kernel's arithmetic, so the same bf16 values);
 //   2. decode_multi_kernel: attention over the cache as it was before the
-//      chunk plus the chunk's own rows.  One workgroup per (sequence, KV
-//      head); the chunk's T x G query rows (row t*G + h) fill the MFMA A
-//      operand, so every K/V row loaded serves all T tokens.  Cache keys
-//      are masked per row: on a sliding layer token t drops the t oldest
-//      entries (ring slots pos .. pos+t-1 mod window-1, which tokens
-//      0..t-1 replace); the new tokens are one more round, key x visible to
-//      rows of token t >= x.  Waves split the cache rounds; the last one
-//      adds the chunk round; the waves merge in LDS;
+//      chunk plus the chunk's own rows.  `split` workgroups per (sequence,
+//      KV head) share its cache rounds; the chunk's T x G query rows (row
+//      t*G + h) fill the MFMA A operand, so every K/V row loaded serves all
+//      T tokens.  Cache keys are masked per row: on a sliding layer token t
+//      drops the t oldest entries (ring slots pos .. pos+t-1 mod window-1,
+//      which tokens 0..t-1 replace); the new tokens are one more round, key
+//      x visible to rows of token t >= x, taken by the last wave of the
+//      last workgroup.  Each workgroup merges its waves in LDS and writes
+//      out directly (split 1) or a partial (o, lse) per row that
+//      multi_merge_kernel combines;
 //   3. append_multi_kernel: the rotated new K and V rows into the cache
 //      (full: rows pos + t; sliding: ring slots, and the block's
 //      evicted-entry row receives what the last token's slot held, as a
@@ -116,15 +118,17 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int mrow = lane & 15, kg = lane >> 4;
     const int Hkv = p.num_kv_heads, Hq = p.num_q_heads;
-    const int b = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+    const int S = p.split, pair = blockIdx.x / S, part = blockIdx.x % S;
+    const int b = pair / Hkv, kvh = pair % Hkv;
     const int32_t p0 = p.pos[b];
     const int64_t cap = p.capacity, cap16 = cap - 16;
     const int W1 = p.window - 1;
     int n_old = 0;  // cached keys before the chunk: rows / ring slots [0, n_old)
     if (p0 > 0) n_old = p.sliding ? min(p0, W1) : (int)min((int64_t)p0, cap);
-    const int R = (n_old + 15) >> 4;
-    const int r_lo = wave * R / WAVES, r_hi = (wave + 1) * R / WAVES;
-    const bool last = wave == WAVES - 1;  // also takes the chunk's own round
+    const int Rall = (n_old + 15) >> 4;
+    const int R0 = part * Rall / S, R = (part + 1) * Rall / S - R0;  // this workgroup's rounds
+    const int r_lo = R0 + wave * R / WAVES, r_hi = R0 + (wave + 1) * R / WAVES;
+    const bool last = part == S - 1 && wave == WAVES - 1;  // also takes the chunk's own round
     const int64_t bh = (int64_t)b * Hkv + kvh;
     const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
     auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap16 ? 16 * r : cap16); };
@@ -218,7 +222,13 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][m]);
         uint16_t *outp = p.out + orow * D + d;
-        if (M == -INFINITY) {  // no keys (negative position)
+        const int64_t prow = (int64_t)blockIdx.x * RG + m;  // partial row (split > 1)
+        if (M == -INFINITY) {  // no keys here (a negative position, or none in this part)
+            if (S > 1) {
+                p.part_o[prow * D + d] = 0.f;
+                if (d == 0) p.part_lse[prow] = -INFINITY;
+                continue;
+            }
             *outp = 0;
             if (d == 0 && p.lse) p.lse[orow] = -INFINITY;
             continue;
@@ -231,6 +241,11 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
             o = fmaf(sc, s_red[(w * RG + m) * D + d], o);
         }
         const float lse = (M + log2f(L)) * kLn2;
+        if (S > 1) {  // normalised partial and its lse
+            p.part_o[prow * D + d] = o / L;
+            if (d == 0) p.part_lse[prow] = lse;
+            continue;
+        }
         float f = 1.f / L;
         if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
         if (p.gate) f *= gate_factor(p.gate[orow]);
@@ -239,10 +254,47 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
     }
 }
 
+// The split partials of one (sequence, KV head): out = sum_s e^(lse_s - lse)
+// o_s with lse = ln sum_s e^(lse_s) (parts without keys weigh 0), then the
+// sink and the gate.  One workgroup per pair, a thread per (row, dim).
+__global__ __launch_bounds__(256) void multi_merge_kernel(MultiParams p, int RG, int G) {
+    constexpr int D = kHeadDim;
+    const int S = p.split, Hkv = p.num_kv_heads, Hq = p.num_q_heads;
+    const int pair = blockIdx.x, b = pair / Hkv, kvh = pair % Hkv;
+    for (int i = threadIdx.x; i < RG * D; i += 256) {
+        const int m = i / D, d = i % D, t = m / G, hq = kvh * G + m % G;
+        const int64_t orow = ((int64_t)b * p.tokens + t) * Hq + hq;
+        float M = -INFINITY;
+        for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_lse[((int64_t)pair * S + s) * RG + m]);
+        if (M == -INFINITY) {
+            p.out[orow * D + d] = 0;
+            if (d == 0 && p.lse) p.lse[orow] = -INFINITY;
+            continue;
+        }
+        float L = 0.f, o = 0.f;
+        for (int s = 0; s < S; ++s) {
+            const int64_t prow = ((int64_t)pair * S + s) * RG + m;
+            const float e = expf(p.part_lse[prow] - M);  // -inf part: 0
+            L += e;
+            o = fmaf(e, p.part_o[prow * D + d], o);
+        }
+        const float lse = M + logf(L);
+        float f = 1.f / L;
+        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        if (p.gate) f *= gate_factor(p.gate[orow]);
+        p.out[orow * D + d] = f32_to_bf16(o * f);
+        if (d == 0 && p.lse) p.lse[orow] = lse;
+    }
+}
+
 template <int G, int T>
 hipError_t launch_multi_gt(const MultiParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_multi_kernel<G, T>), dim3(p.batch * p.num_kv_heads),
+    hipLaunchKernelGGL((decode_multi_kernel<G, T>), dim3(p.batch * p.num_kv_heads * p.split),
                        dim3(MultiShape<G, T>::WAVES * 64), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.split == 1) return e;
+    hipLaunchKernelGGL(multi_merge_kernel, dim3(p.batch * p.num_kv_heads), dim3(256), 0, s, p,
+                       G * T, G);
     return hipGetLastError();
 }
 

@@ -674,11 +674,77 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
                     "decode step");
 }
 
+namespace {
+
+hda_status check_multi_shape(const hda_cache_desc *c, int layer, int32_t tokens,
+                             int32_t max_seq_len) {
+    hda_status st = check_cache(c, layer);
+    if (st != HDA_OK) return st;
+    if (c->head_dim != hda::kHeadDim)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels are built for head_dim %d, got %d",
+                    hda::kHeadDim, c->head_dim);
+    const int g = c->num_q_heads / c->num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+        return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
+    if (tokens < 1 || tokens > 4 || g * tokens > 16)
+        return fail(HDA_ERR_UNSUPPORTED, "a chunk holds 1..4 tokens with tokens x group <= 16 "
+                    "query rows, got %d tokens for group %d", tokens, g);
+    if (c->rotary_dim % 16)
+        return fail(HDA_ERR_UNSUPPORTED, "rotary_dim %d is not a multiple of 16", c->rotary_dim);
+    if (c->capacity < 16)
+        return fail(HDA_ERR_UNSUPPORTED, "decode kernels need a cache of at least 16 rows");
+    if (c->block_table || c->kv_dtype != HDA_KV_BF16)
+        return fail(HDA_ERR_UNSUPPORTED, "chunk decode is built for contiguous bf16 caches");
+    if (max_seq_len < 1)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "max_seq_len %d < 1", max_seq_len);
+    return HDA_OK;
+}
+
+// Workgroups per (sequence, KV head) of the chunk decode.  Measured on
+// MI355X (4-token chunks): a split pays its merge launch and partials only
+// where the pairs alone leave the chip idle or a pair has many rounds --
+// at 128 pairs a 32-round sliding window is fastest unsplit, a 4k full
+// layer split in 2; at 16 pairs splits of 4 and 8.  So: about 256
+// workgroups (128 when there are few pairs), each with at least 32 rounds
+// (8 with few pairs).  max_seq_len bounds pos + tokens; it only sizes the
+// split (every workgroup takes its share of the rounds the sequence has).
+int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_seq_len) {
+    int64_t n_old = (int64_t)max_seq_len - tokens;
+    if (n_old < 0) n_old = 0;
+    const int64_t lim = layer == HDA_SLIDING ? (int64_t)c->window - 1 : c->capacity;
+    if (n_old > lim) n_old = lim;
+    const int64_t rounds = (n_old + 15) / 16;
+    const int64_t pairs = (int64_t)c->batch * c->num_kv_heads;
+    const bool many = pairs >= 64;
+    const int64_t target = many ? 256 : 128, min_rounds = many ? 32 : 8;
+    int64_t s = pairs > 0 ? (target + pairs - 1) / pairs : 1;
+    const int64_t by_rounds = rounds / min_rounds;
+    if (s > by_rounds) s = by_rounds;
+    if (s > 64) s = 64;
+    return s < 1 ? 1 : (int)s;
+}
+
+size_t multi_workspace(const hda_cache_desc *c, int split, int32_t tokens) {
+    if (split <= 1) return 0;
+    const size_t rows = (size_t)c->batch * c->num_kv_heads * split * tokens *
+                        (c->num_q_heads / c->num_kv_heads);
+    return up256(rows * hda::kHeadDim * sizeof(float)) + rows * sizeof(float);
+}
+
+}  // namespace
+
+size_t hda_decode_multi_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer,
+                                        int32_t tokens, int32_t max_seq_len) {
+    if (check_multi_shape(cache, layer, tokens, max_seq_len) != HDA_OK) return 0;
+    return multi_workspace(cache, multi_split(cache, layer, tokens, max_seq_len), tokens);
+}
+
 hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32_t *pos,
                             int32_t tokens, hda_layer_type layer, const hda_cache_desc *cache,
                             const float *sinks, const float *gate, float scale, void *out,
-                            float *lse, void *stream) {
-    hda_status st = check_cache(cache, layer);
+                            float *lse, int32_t max_seq_len, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    hda_status st = check_multi_shape(cache, layer, tokens, max_seq_len);
     if (st != HDA_OK) return st;
     if (!q || !k_new || !v_new || !pos || !out)
         return fail(HDA_ERR_INVALID_ARGUMENT, "q, k_new, v_new, pos and out must be non-NULL");
@@ -689,23 +755,23 @@ hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32
     if ((st = check_f32_ptrs(sinks, gate, lse)) != HDA_OK) return st;
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be positive and finite");
-    if (cache->head_dim != hda::kHeadDim)
-        return fail(HDA_ERR_UNSUPPORTED, "decode kernels are built for head_dim %d, got %d",
-                    hda::kHeadDim, cache->head_dim);
     const int g = cache->num_q_heads / cache->num_kv_heads;
-    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
-        return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
-    if (tokens < 1 || tokens > 4 || g * tokens > 16)
-        return fail(HDA_ERR_UNSUPPORTED, "a chunk holds 1..4 tokens with tokens x group <= 16 "
-                    "query rows, got %d tokens for group %d", tokens, g);
-    if (cache->rotary_dim % 16)
-        return fail(HDA_ERR_UNSUPPORTED, "rotary_dim %d is not a multiple of 16", cache->rotary_dim);
-    if (cache->capacity < 16)
-        return fail(HDA_ERR_UNSUPPORTED, "decode kernels need a cache of at least 16 rows");
-    if (cache->block_table || cache->kv_dtype != HDA_KV_BF16)
-        return fail(HDA_ERR_UNSUPPORTED, "chunk decode is built for contiguous bf16 caches");
+    const int split = multi_split(cache, layer, tokens, max_seq_len);
+    const size_t need = multi_workspace(cache, split, tokens);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(HDA_ERR_WORKSPACE, "chunk decode needs a %zu-byte workspace, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need && !aligned16(workspace))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (cache->batch == 0) return ok();
     hda::MultiParams p{};
+    p.split = split;
+    if (need) {
+        const size_t rows = (size_t)cache->batch * cache->num_kv_heads * split * tokens * g;
+        p.part_o = static_cast<float *>(workspace);
+        p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                               up256(rows * hda::kHeadDim * sizeof(float)));
+    }
     p.q = static_cast<uint16_t *>(q);
     p.k_new = static_cast<uint16_t *>(k_new);
     p.v_new = static_cast<const uint16_t *>(v_new);

@@ -135,6 +135,9 @@ struct MultiParams {
     int64_t capacity;
     int batch, tokens, num_q_heads, num_kv_heads, rotary_dim, window;
     int sliding;
+    int split;                  // workgroups per (sequence, KV head); > 1: partials + merge
+    float *part_o;              // [B * Hkv * split, T * G, D] (split > 1)
+    float *part_lse;            // [B * Hkv * split, T * G]
     float scale_log2;
     float inv_freq[kHeadDim / 2];
 };

@@ -338,17 +338,32 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
  *   lse     fp32 [batch, tokens, num_q_heads] or NULL (before the sink)
  *   sinks   fp32 [num_q_heads] or NULL; gate fp32 [batch, tokens,
  *           num_q_heads] logits or NULL (as in hda_decode_attn)
+ *   max_seq_len host bound on pos + tokens (sizes how many workgroups share
+ *           each sequence's keys; results do not depend on it)
+ *   workspace  device buffer of at least hda_decode_multi_workspace_bytes()
+ *           (NULL when that is 0); calls sharing one must be ordered on one
+ *           stream
  * The cache is read as it was before the chunk and written after the
  * attention (full: rows pos + t below capacity; sliding: ring slots, the
- * evicted-entry row taking what the last token's slot held).  No
- * workspace.  Errors: as hda_decode_attn, plus UNSUPPORTED for tokens
- * outside 1..4 or tokens x (num_q_heads / num_kv_heads) > 16, rotary_dim
- * not a multiple of 16, a paged or fp8 cache.  batch == 0 is a no-op.
+ * evicted-entry row taking what the last token's slot held).  Errors: as
+ * hda_decode_attn, plus UNSUPPORTED for tokens outside 1..4 or tokens x
+ * (num_q_heads / num_kv_heads) > 16, rotary_dim not a multiple of 16, a
+ * paged or fp8 cache; INVALID_ARGUMENT for max_seq_len < 1; WORKSPACE for a
+ * missing or short workspace.  batch == 0 is a no-op.
  */
 hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32_t *pos,
                             int32_t tokens, hda_layer_type layer, const hda_cache_desc *cache,
                             const float *sinks, const float *gate, float scale, void *out,
-                            float *lse, void *stream);
+                            float *lse, int32_t max_seq_len, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * hda_decode_multi_workspace_bytes -- device workspace hda_decode_multi
+ * needs for this cache, layer type, chunk size and max_seq_len (0: none, or
+ * an invalid description).
+ */
+size_t hda_decode_multi_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer,
+                                        int32_t tokens, int32_t max_seq_len);
 
 /*
  * hda_sparse_workspace_bytes -- device workspace hda_sparse_decode_attn needs

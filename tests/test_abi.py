@@ -371,11 +371,13 @@ def test_fp8_binding_desc():
 
 
 # ------------------------------------------------------------- chunk decode
-def _multi(desc, tokens=2, layer=hda.SLIDING, q=FAKE, pos=FAKE, scale=0.0625):
+def _multi(desc, tokens=2, layer=hda.SLIDING, q=FAKE, pos=FAKE, scale=0.0625, msl=16, ws=None,
+           wsb=0):
     L = hda.lib()
     return L.hda_decode_multi(ctypes.c_void_p(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
                               ctypes.c_void_p(pos), tokens, layer, ctypes.byref(desc), None, None,
-                              scale, ctypes.c_void_p(FAKE), None, None)
+                              scale, ctypes.c_void_p(FAKE), None, msl,
+                              ctypes.c_void_p(ws) if ws else None, wsb, None)
 
 
 def test_multi_checks():
@@ -392,3 +394,22 @@ def test_multi_checks():
     assert _multi(_desc(**_FP8)) == 2 and "bf16" in _msg()
     assert _multi(_desc(**{**_PAGED, "rotary_dim": 64}), layer=hda.FULL) == 2
     assert _multi(_desc(batch=0)) == 0
+    assert _multi(_desc(), msl=0) == 1
+
+
+def test_multi_workspace():
+    """Short contexts need no workspace (one workgroup per sequence and KV
+    head); long ones split each pair's keys over several workgroups, whose
+    partials (fp32 out + lse per query row) live in the workspace."""
+    L = hda.lib()
+    full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 2, 20) == 0
+    need = L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 2, 4096)
+    # 4 pairs: 128 / 4 = 32 workgroups wanted and 256 rounds allow 32 (8 rounds each);
+    # partial rows = pairs x 32 x (2 tokens x 4 heads)
+    rows = 2 * 2 * 32 * 2 * 4
+    assert need == (rows * 256 * 4 + 255) // 256 * 256 + rows * 4
+    assert _multi(full, layer=hda.FULL, msl=4096) == 3 and "workspace" in _msg()
+    assert _multi(full, layer=hda.FULL, msl=4096, ws=FAKE, wsb=need - 1) == 3
+    assert _multi(full, layer=hda.FULL, msl=4096, ws=FAKE + 4, wsb=need) == 1
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 4096) == 0

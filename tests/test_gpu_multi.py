@@ -3,7 +3,9 @@ sequence in one call; Spark export page, `SparkStepConfig.cache_len`
 docstring -- token t attends to the entries of its own window, cached ones
 and new tokens 0..t) against the oracle's T single-token steps in order.
 
-Checked: out (max-abs <= 1e-2, mean-abs <= 1e-3) and lse (1e-4) for every
+Each case runs with the workgroup split its max_seq_len selects (long
+contexts: several workgroups per sequence and KV head, partials merged;
+short: one).  Checked: out (max-abs <= 1e-2, mean-abs <= 1e-3) and lse (1e-4) for every
 token; q and the new K rotated in place within one bf16 ulp; the cache
 after the call -- V bit-exact, rotated K within one bf16 ulp, the sliding
 block's evicted-entry row holding what the last token's slot held.  Rows
@@ -81,8 +83,13 @@ class MultiCase:
         lse = torch.full(self.q.shape[:3], float("nan"), device="cuda")
         sk = None if sinks is None else torch.as_tensor(sinks).cuda()
         gt = None if gate is None else torch.as_tensor(gate).cuda()
+        msl = max(int(self.pos.max()) + self.T, 1)
+        nbytes = hda.hda_decode_multi_workspace_bytes(cache, self.lt, self.T, msl)
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        self.split_used = nbytes > 0
         hda.hda_decode_multi(dev["q"], dev["k_new"], dev["v_new"], torch.from_numpy(self.pos).cuda(),
-                             self.lt, cache, sk, 1 / 16, out, lse, gate=gt)
+                             self.lt, cache, sk, 1 / 16, out, lse, gate=gt, max_seq_len=msl,
+                             workspace=ws)
         torch.cuda.synchronize()
         return dev, out, lse
 
@@ -127,6 +134,33 @@ def test_multi_groups(hq, hkv, T):
         print("CASE multi groups", hq, hkv, T, lt, flush=True)
         case = MultiCase(3100 + hq + T + lt, lt, pos, T, cap=1024, hq=hq, hkv=hkv)
         _check(case)
+
+
+def test_multi_split_and_single_workgroup_agree():
+    """The same chunk with max_seq_len small enough for one workgroup per
+    pair and with the real bound (split keys + merge): both within the
+    tolerance of the oracle and of each other."""
+    import full_kv_cache_amd as hda
+    print("CASE multi split vs single", flush=True)
+    case = MultiCase(3400, FULL, [1900, 1200], 4, cap=2048)
+    q_ref, k_ref, v_ref, ref, rlse = case.oracle()
+    outs = []
+    for msl in (4, 1904):
+        dev = {n: workloads.from_bits(getattr(case, n)).cuda()
+               for n in ("q", "k_new", "v_new", "k", "v")}
+        cache = hda.LayerCache(dev["k"], dev["v"], case.hq, W, case.rot, case.theta)
+        nbytes = hda.hda_decode_multi_workspace_bytes(cache, FULL, 4, msl)
+        assert (nbytes > 0) == (msl > 4)
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        out = torch.empty(case.q.shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(case.q.shape[:3], device="cuda")
+        hda.hda_decode_multi(dev["q"], dev["k_new"], dev["v_new"], torch.from_numpy(case.pos).cuda(),
+                             FULL, cache, None, 1 / 16, out, lse, max_seq_len=msl, workspace=ws)
+        torch.cuda.synchronize()
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+        outs.append(to_f64(out))
+    assert np.abs(outs[0] - outs[1]).max() <= 1e-2
 
 
 def test_multi_negative_position():
