@@ -224,7 +224,14 @@ class Workload:
                              workspace=self.multi_ws)
 
     def fp8_call(self, L):
+        """The layer's step on its fp8 cache, as path auto: one launch for a
+        sliding layer, append + attention for a full one."""
         import full_kv_cache_amd as hda
+        import workloads
+        if L["lt"] == workloads.SLIDING:
+            hda.hda_decode_step(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["fcache"],
+                                L["sinks"], self.scale, L["out"], L["lse"], self.workspace)
+            return
         hda.hda_rope_append(L["q"], L["k_new"], L["v_new"], self.pos, L["lt"], L["fcache"])
         hda.hda_decode_attn(L["q"], L["fcache"], self.seq_lens, L["lt"], L["sinks"], self.scale,
                             L["out"], L["lse"], self.max_seq_len, 0, self.workspace)
@@ -549,16 +556,19 @@ def main():
         fp8 = {"ms_per_step": round(fp8_ms, 4),
                "tokens_per_s": round(cfg["batch"] / (fp8_ms / 1e3), 1),
                "kv_bytes_per_step": sum(wl.rows[L["lt"]] for L in wl.layers) * wl.fp8_row_bytes,
-               "path": "hda_rope_append + hda_decode_attn on every layer (window kernel for "
-                       "sliding layers, streaming kernel + merge for full layers)"}
+               "path": "hda_decode_step (one launch) for sliding layers, hda_rope_append + "
+                       "hda_decode_attn (streaming kernel + merge) for full layers"}
         fp8["GB/s"] = round(fp8["kv_bytes_per_step"] / (fp8_ms / 1e3) / 1e9, 1)
         for lt, name in ((workloads.SLIDING, "sliding"), (workloads.FULL, "full")):
             Ls = [L for L in wl.layers if L["lt"] == lt]
             if not Ls:
                 continue
 
-            def attn(Ls=Ls, lt=lt):
+            def attn(Ls=Ls, lt=lt):  # sliding: the whole one-launch step; full: attention
                 for L in Ls:
+                    if lt == workloads.SLIDING:
+                        wl.fp8_call(L)
+                        continue
                     hda.hda_decode_attn(L["q"], L["fcache"], wl.seq_lens, lt, L["sinks"], wl.scale,
                                         L["out"], L["lse"], wl.max_seq_len, 0, wl.workspace)
             ms_l, _ = time_graph(attn, args.steps, args.warmup)

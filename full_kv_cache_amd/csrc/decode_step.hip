@@ -32,6 +32,8 @@
 // pair, counted once the partial's stores are complete) merges them once its
 // own rounds are done, writes out and lse with the sink, and resets the
 // counter to zero for the next launch.
+#include <type_traits>
+
 #include "decode_wave.h"
 
 namespace hda {
@@ -473,8 +475,13 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
 // Both workgroups of a pair read every key row; neither writes one until
 // both have read them, and no data passes between them, so no fence is
 // needed around the counter.
+// F8 (fp8 cache: e4m3 codes + a scale per row): rounds load codes and the
+// key scales (as the streaming kernel's fp8 form); the prologue quantizes
+// the new K and V rows (scale = amax / 448) into LDS; the round holding the
+// new token's row takes its codes and scales there; the kept old entry and
+// the append move codes and scales together.
 // ===================================================================
-template <int GW, int ROT>
+template <int GW, int ROT, bool F8>
 __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(StepParams p, int S) {
     constexpr int D = kHeadDim;
     constexpr int WAVES = kPairWaves;
@@ -488,6 +495,9 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     __shared__ __align__(16) uint16_t s_rows[(GW + 4) * D];
     __shared__ float s_m[WAVES][GW], s_l[WAVES][GW];
     __shared__ int s_last;
+    // F8: codes of the new K, new V, old K, old V rows and their scales
+    __shared__ __align__(16) uint8_t s_c8[F8 ? 4 * D : 16];
+    __shared__ float s_c8s[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hw = lane >> 5, dl = lane & 31, mrow = lane & 15, kg = lane >> 4;
@@ -506,6 +516,14 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     const int64_t cap = p.capacity;
     const int64_t bh = (int64_t)b * p.num_kv_heads + kvh;
     uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
+    using KV = std::conditional_t<F8, uint2, uint4>;
+    auto issue = [&](int r0e, int ln, KV *kt, KV *vt, float &ks, float &vs) HDA_INLINE {
+        if constexpr (F8)
+            issue_round8(p.kq + bh * cap * D, p.vq + bh * cap * D, p.ks + bh * cap, p.vs + bh * cap,
+                         r0e, ln, kt, vt, ks, vs);
+        else
+            issue_round(kblk, vblk, r0e, ln, kt, vt);
+    };
     uint16_t *const s_knew = s_rows + GW * D, *const s_vnew = s_rows + (GW + 1) * D;
     uint16_t *const s_oldk = s_rows + (GW + 2) * D, *const s_oldv = s_rows + (GW + 3) * D;
 
@@ -535,8 +553,9 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     // without one issues a placeholder round, so that every wave has the
     // same loads outstanding here), the second after it: measured on MI355X,
     // both rounds ahead of the prologue delay it more than they gain.
-    uint4 kA[8], vA[8], kB[8], vB[8];
-    issue_round(kblk, vblk, r0e_of(r_lo), r_lo < r_hi ? lane : 0, kA, vA);
+    KV kA[8], vA[8], kB[8], vB[8];
+    float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+    issue(r0e_of(r_lo), r_lo < r_hi ? lane : 0, kA, vA, ksA, vsA);
     // no load above may be moved below this point (next to its use)
     asm volatile("" ::: "memory");
 
@@ -583,7 +602,18 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     __syncthreads();
     {
         const bool has2 = r_lo + 1 < r_hi;
-        issue_round(kblk, vblk, r0e_of(has2 ? r_lo + 1 : r_lo), has2 ? lane : 0, kB, vB);
+        issue(r0e_of(has2 ? r_lo + 1 : r_lo), has2 ? lane : 0, kB, vB, ksB, vsB);
+    }
+    if constexpr (F8) {  // the new rows' codes: wave 0 quantizes K, wave 1 V
+        if (wave < 2) {
+            const uint2 w = *reinterpret_cast<const uint2 *>((wave ? s_vnew : s_knew) + 4 * lane);
+            const float xv[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+            float sc;
+            const uint32_t c = quantize_row4(xv, sc);
+            *reinterpret_cast<uint32_t *>(s_c8 + wave * D + 4 * lane) = c;
+            if (lane == 0) s_c8s[wave] = sc;
+        }
+        __syncthreads();
     }
 
     WaveSoftmax<GW> st;
@@ -592,7 +622,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
         // the q operand is read from LDS for every round (registers are short)
         const uint16_t *qs = s_rows + (mrow < GW ? mrow : 0) * D + 8 * kg;
         // a round's 16 rows start at r0e = min(16 r, capacity - 16): in bounds
-        auto one = [&](int r, uint4 *kt, uint4 *vt) HDA_INLINE {
+        auto one = [&](int r, KV *kt, KV *vt, float ksc, float vsc) HDA_INLINE {
             bf16x8 qa[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -600,6 +630,35 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
             }
             const int r0e = r0e_of(r), lo = 16 * r - r0e, hi = n - r0e;
             const int vr = vrow - r0e, sr = srow - r0e;
+            if constexpr (F8) {
+                if (vr >= lo && vr < hi && vr < 16) {  // the new token's row from LDS (wave-uniform)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (2 * j + hw == vr) {
+                            kt[j] = *reinterpret_cast<const uint2 *>(s_c8 + 8 * dl);
+                            vt[j] = *reinterpret_cast<const uint2 *>(s_c8 + D + 8 * dl);
+                        }
+                    if (mrow == vr) {
+                        ksc = s_c8s[0];
+                        vsc = s_c8s[1];
+                    }
+                }
+                st.template round<false, true>(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave],
+                                               s_kt[wave], lane, -1, nullptr, nullptr, ksc, vsc);
+                if (srow >= 0 && sr >= lo && sr < hi && sr < 16) {  // keep the slot's old entry
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (2 * u + hw == sr) {
+                            *reinterpret_cast<uint2 *>(s_c8 + 2 * D + 8 * dl) = kt[u];
+                            *reinterpret_cast<uint2 *>(s_c8 + 3 * D + 8 * dl) = vt[u];
+                        }
+                    if (lane == sr) {  // lane l holds key l's scales
+                        s_c8s[2] = ksc;
+                        s_c8s[3] = vsc;
+                    }
+                }
+                return;
+            } else {
             // only the round holding the new token's row takes the
             // substituting form (the condition is wave-uniform)
             if (vr >= lo && vr < hi && vr < 16)
@@ -615,16 +674,17 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
                         *reinterpret_cast<uint4 *>(s_oldv + 8 * dl) = vt[u];
                     }
             }
+            }
         };
         for (int r = r_lo; r < r_hi; r += 2) {
             const bool two = r + 1 < r_hi;
             if (r != r_lo) {
-                issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
-                issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
+                issue(r0e_of(r), lane, kA, vA, ksA, vsA);
+                issue(r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB, ksB, vsB);
             }
-            one(r, kA, vA);
+            one(r, kA, vA, ksA, vsA);
             if (!two) break;
-            one(r + 1, kB, vB);
+            one(r + 1, kB, vB, ksB, vsB);
         }
     }
 
@@ -683,6 +743,25 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
         if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
     }
     __syncthreads();
+    if constexpr (F8) {
+        if (s_last && tid < 128) {  // the append: 8 code bytes per thread, K then V
+            const int which = tid >> 6, c = tid & 31, half = (tid >> 5) & 1;
+            uint8_t *blk = (which ? p.vq : p.kq) + bh * cap * D;
+            float *sblk = (which ? p.vs : p.ks) + bh * cap;
+            if (half == 0 && srow >= 0) {  // the slot's old entry to the evicted-entry row
+                *reinterpret_cast<uint2 *>(blk + (int64_t)(W - 1) * D + 8 * c) =
+                    *reinterpret_cast<const uint2 *>(s_c8 + (2 + which) * D + 8 * c);
+                if (c == 0) sblk[W - 1] = s_c8s[2 + which];
+            }
+            if (half == 1) {  // the new token to its slot (row pos below a full window)
+                const int row = srow >= 0 ? srow : vrow;
+                *reinterpret_cast<uint2 *>(blk + (int64_t)row * D + 8 * c) =
+                    *reinterpret_cast<const uint2 *>(s_c8 + which * D + 8 * c);
+                if (c == 0) sblk[row] = s_c8s[which];
+            }
+        }
+        return;
+    }
     if (s_last && tid < 128) {  // the append: 16 bytes per thread, K then V
         const int which = tid >> 6, c = tid & 31, half = (tid >> 5) & 1;
         uint16_t *blk = which ? vblk : kblk;
@@ -699,8 +778,12 @@ template <int GW, int ROT>
 hipError_t launch_window_gr(const StepParams &p, int S, hipStream_t s) {
     const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
     const int64_t blocks = (pairs + 7) / 8 * 8 * S;
-    hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT>), dim3((unsigned)blocks), dim3(kPairWaves * 64), 0, s,
-                       p, S);
+    if (p.kq)
+        hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT, true>), dim3((unsigned)blocks),
+                           dim3(kPairWaves * 64), 0, s, p, S);
+    else
+        hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT, false>), dim3((unsigned)blocks),
+                           dim3(kPairWaves * 64), 0, s, p, S);
     return hipGetLastError();
 }
 

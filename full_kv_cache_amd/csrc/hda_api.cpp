@@ -291,9 +291,11 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
     if (c->batch > hda::kStreamMaxBatch)
         return fail(HDA_ERR_UNSUPPORTED, "the fused step handles at most %d sequences, got %d",
                     hda::kStreamMaxBatch, c->batch);
-    if (c->block_table || c->kv_dtype != HDA_KV_BF16)
-        return fail(HDA_ERR_UNSUPPORTED,
-                    "the one-launch step is built for contiguous bf16 caches only");
+    if (c->block_table)
+        return fail(HDA_ERR_UNSUPPORTED, "the one-launch step is built for contiguous caches only");
+    if (c->kv_dtype != HDA_KV_BF16 && !(layer == HDA_SLIDING && c->window <= hda::kPairMaxKeys))
+        return fail(HDA_ERR_UNSUPPORTED, "the one-launch step on an fp8 cache is built for "
+                    "sliding windows of at most %d keys (bf16 otherwise)", hda::kPairMaxKeys);
     return HDA_OK;
 }
 
@@ -650,6 +652,12 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
     p.pos = pos;
     p.k = static_cast<uint16_t *>(cache->k);
     p.v = static_cast<uint16_t *>(cache->v);
+    if (cache->kv_dtype == HDA_KV_FP8_E4M3) {
+        p.kq = static_cast<uint8_t *>(cache->k);
+        p.vq = static_cast<uint8_t *>(cache->v);
+        p.ks = cache->k_scale;
+        p.vs = cache->v_scale;
+    }
     p.sinks = sinks;
     p.gate = gate;
     p.out = static_cast<uint16_t *>(out);

@@ -60,6 +60,46 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
     return make_uint4(e4m3x2_to_bf16x2(w.x, false), e4m3x2_to_bf16x2(w.x, true),
                       e4m3x2_to_bf16x2(w.y, false), e4m3x2_to_bf16x2(w.y, true));
 }
+// fp32 -> e4m3 (bias 7, 3 mantissa bits, largest finite 448, S.1111.111
+// NaN), round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sgn = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;                  // NaN
+    if (a >= 0x43E00000u) return sgn | 0x7Eu;           // >= 448 (and inf): saturate
+    if (a < 0x3C800000u) {                              // below 2^-6: steps of 2^-9
+        const float q = rintf(__uint_as_float(a) * 512.f);  // exact scaling, half to even
+        return sgn | (uint32_t)q;                       // 8 is 2^-6's own code
+    }
+    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xFFFFFu;
+    const uint32_t up = rem > 0x80000u || (rem == 0x80000u && (keep & 1u));
+    uint32_t v = (((a >> 23) - 127u + 7u) << 3) + keep + up;  // a carry moves into the exponent
+    if (v > 0x7Eu) v = 0x7Eu;
+    return sgn | v;
+}
+
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// One row of 4 * 64 values quantized by a wave (lane = 4 consecutive
+// values): scale = amax / 448 and code = e4m3(x / scale), both fp32
+// divisions rounded to nearest; an all-zero row gets scale 0, codes 0.
+// Returns this lane's 4 codes packed (lowest value in the low byte).
+__device__ __forceinline__ uint32_t quantize_row4(const float (&x)[4], float &scale) {
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    amax = wave_max64(amax);
+    scale = __fdiv_rn(amax, 448.f);
+    uint32_t packed = 0;
+    if (scale != 0.f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) packed |= e4m3_rne(__fdiv_rn(x[e], scale)) << (8 * e);
+    }
+    return packed;
+}
+
 __device__ __forceinline__ void e4m3x8_to_f32(uint2 w, float *x) {
     const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
     const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);

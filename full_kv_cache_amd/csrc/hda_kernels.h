@@ -74,6 +74,8 @@ struct StepParams {
     const uint16_t *k_new, *v_new;  // [B, Hkv, D]
     const int32_t *pos;         // [B]
     uint16_t *k, *v;            // [B, Hkv, cap, D]
+    uint8_t *kq, *vq;           // fp8 cache (window form): e4m3 codes in place of k, v
+    float *ks, *vs;             // fp8 cache: one scale per row [B, Hkv, cap]
     const float *sinks;         // [Hq] or null
     const float *gate;          // [B, Hq] output-gate logits or null
     uint16_t *out;              // [B, Hq, D]

@@ -165,34 +165,6 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeAppendPar
 // kernel (q in place, K into LDS), then one wave per new row for the
 // quantization (lane = 4 dims; amax by a wave reduction).
 // -------------------------------------------------------------------
-namespace {
-
-// fp32 -> e4m3 (bias 7, 3 mantissa bits, largest finite 448, S.1111.111
-// NaN), round to nearest even, saturating at +-448.
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sgn = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;                  // NaN
-    if (a >= 0x43E00000u) return sgn | 0x7Eu;           // >= 448 (and inf): saturate
-    if (a < 0x3C800000u) {                              // below 2^-6: steps of 2^-9
-        const float q = rintf(__uint_as_float(a) * 512.f);  // exact scaling, half to even
-        return sgn | (uint32_t)q;                       // 8 is 2^-6's own code
-    }
-    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xFFFFFu;
-    const uint32_t up = rem > 0x80000u || (rem == 0x80000u && (keep & 1u));
-    uint32_t v = (((a >> 23) - 127u + 7u) << 3) + keep + up;  // a carry moves into the exponent
-    if (v > 0x7Eu) v = 0x7Eu;
-    return sgn | v;
-}
-
-__device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-}  // namespace
-
 __global__ __launch_bounds__(kRopeThreads) void rope_append_fp8_kernel(RopeAppendParams p) {
     __shared__ float s_cos[kMaxHalf], s_sin[kMaxHalf];
     extern __shared__ __align__(16) uint16_t s_krow[];  // [Hkv, D] rotated new K, bf16
@@ -276,14 +248,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_fp8_kernel(RopeAppen
         const uint2 w = is_v ? *reinterpret_cast<const uint2 *>(p.v_new + ((int64_t)b * Hkv + h) * D + 4 * lane)
                              : *reinterpret_cast<const uint2 *>(s_krow + h * D + 4 * lane);
         const float x[4] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-        float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-        amax = wave_max64(amax);
-        const float sc = __fdiv_rn(amax, 448.f);
-        uint32_t packed = 0;
-        if (sc != 0.f) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) packed |= e4m3_rne(__fdiv_rn(x[e], sc)) << (8 * e);
-        }
+        float sc;
+        const uint32_t packed = quantize_row4(x, sc);
         *reinterpret_cast<uint32_t *>(codes + slot * D + 4 * lane) = packed;
         if (lane == 0) scales[slot] = sc;
     }

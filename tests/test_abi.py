@@ -346,8 +346,10 @@ def test_fp8_routing():
     L = hda.lib()
     full = _desc(**{**_FP8, "capacity": 4096, "rotary_dim": 64, "rope_theta": 5e6})
     assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256) == 2 and "fp8" in _msg()
-    assert _step(_desc(**_FP8)) == 2 and "bf16" in _msg()
-    assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(**_FP8)), hda.SLIDING) == 0
+    assert _step(full, layer=hda.FULL) == 2 and "fp8" in _msg()  # streaming form: bf16 only
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(full), hda.FULL) == 0
+    # the window form takes an fp8 cache: only the counter header as workspace
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(**_FP8)), hda.SLIDING) == 256
     r = L.hda_decode_attn_partials(ctypes.c_void_p(FAKE), ctypes.byref(full), ctypes.c_void_p(FAKE),
                                    hda.FULL, 0.0625, 4096, 256, ctypes.c_void_p(FAKE),
                                    ctypes.c_void_p(FAKE), None)

@@ -113,10 +113,13 @@ class Fp8Case:
         return d, out, lse
 
 
-def _check_append(case, d, q_ref, blocks):
+def _check_append(case, d, q_ref, blocks, q_rotated=True):
     kc_ref, vc_ref, ks_ref, vs_ref = blocks
-    ulps = bf16_ulp_diff(bits_of(d["q"]), q_ref)
-    assert ulps.max() <= 1 and (ulps > 0).mean() < 1e-3
+    if q_rotated:
+        ulps = bf16_ulp_diff(bits_of(d["q"]), q_ref)
+        assert ulps.max() <= 1 and (ulps > 0).mean() < 1e-3
+    else:  # the one-launch step only reads q
+        assert np.array_equal(bits_of(d["q"]), case.q)
     kc, vc = d["kc"].cpu().numpy(), d["vc"].cpu().numpy()
     ks, vs = d["ks"].cpu().numpy(), d["vs"].cpu().numpy()
     assert np.array_equal(vc, vc_ref)
@@ -214,3 +217,35 @@ def test_fp8_paged_matches_contiguous():
     assert torch.equal(lse, lse_c)
     assert_attn_close(out, ref)
     np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("pos", [[0, 15, 510, 511, 1500], [3, 700, 4095, 1022]])
+def test_fp8_window_step(pos):
+    """hda_decode_step on an fp8 sliding cache (one launch: RoPE, quantized
+    append, attention): the cache after it and out / lse as for the
+    two-call path; twice, from the same cache, on one workspace (the
+    arrival counters return to zero)."""
+    import full_kv_cache_amd as hda
+    print("CASE fp8 window step", pos, flush=True)
+    case = Fp8Case(2300 + len(pos), SLIDING, pos)
+    Hq = case.shape.num_q_heads
+    sk = np.linspace(-1.0, 3.0, Hq).astype(np.float32)
+    g = np.random.default_rng(7).uniform(-3, 3, size=(len(pos), Hq)).astype(np.float32)
+    q_ref, blocks, ref, rlse = case.oracle_step(sinks=sk, gate=g)
+    ws = None
+    for _ in range(2):  # the same step on a fresh copy of the cache, same workspace
+        d = case.device()
+        cache = case.cache(d)
+        if ws is None:
+            ws = torch.zeros(hda.hda_decode_step_workspace_bytes(cache, SLIDING), dtype=torch.uint8,
+                             device="cuda")
+        out = torch.full((len(pos), Hq, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((len(pos), Hq), float("nan"), device="cuda")
+        hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], torch.from_numpy(case.pos).cuda(),
+                            SLIDING, cache, torch.from_numpy(sk).cuda(), 1 / 16, out, lse, ws,
+                            gate=torch.from_numpy(g).cuda())
+        torch.cuda.synchronize()
+        _check_append(case, d, q_ref, blocks, q_rotated=False)
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+        assert torch.count_nonzero(ws[:4 * len(pos) * 2]).item() == 0
