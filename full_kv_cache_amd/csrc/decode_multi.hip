@@ -254,22 +254,25 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
     }
 }
 
-// The split partials of one (sequence, KV head): out = sum_s e^(lse_s - lse)
-// o_s with lse = ln sum_s e^(lse_s) (parts without keys weigh 0), then the
-// sink and the gate.  One workgroup per pair, a thread per (row, dim).
-__global__ __launch_bounds__(256) void multi_merge_kernel(MultiParams p, int RG, int G) {
+// The split partials of one (sequence, KV head, query row): out = sum_s
+// e^(lse_s - lse) o_s with lse = ln sum_s e^(lse_s) (parts without keys
+// weigh 0), then the sink and the gate.  One workgroup per (pair, row), a
+// thread per dim (the row's S lse values are read by every thread: one
+// cached broadcast).
+__global__ __launch_bounds__(kHeadDim) void multi_merge_kernel(MultiParams p, int RG, int G) {
     constexpr int D = kHeadDim;
     const int S = p.split, Hkv = p.num_kv_heads, Hq = p.num_q_heads;
-    const int pair = blockIdx.x, b = pair / Hkv, kvh = pair % Hkv;
-    for (int i = threadIdx.x; i < RG * D; i += 256) {
-        const int m = i / D, d = i % D, t = m / G, hq = kvh * G + m % G;
+    const int pair = blockIdx.x / RG, m = blockIdx.x % RG, d = threadIdx.x;
+    const int b = pair / Hkv, kvh = pair % Hkv;
+    {
+        const int t = m / G, hq = kvh * G + m % G;
         const int64_t orow = ((int64_t)b * p.tokens + t) * Hq + hq;
         float M = -INFINITY;
         for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_lse[((int64_t)pair * S + s) * RG + m]);
         if (M == -INFINITY) {
             p.out[orow * D + d] = 0;
             if (d == 0 && p.lse) p.lse[orow] = -INFINITY;
-            continue;
+            return;
         }
         float L = 0.f, o = 0.f;
         for (int s = 0; s < S; ++s) {
@@ -293,8 +296,8 @@ hipError_t launch_multi_gt(const MultiParams &p, hipStream_t s) {
                        dim3(MultiShape<G, T>::WAVES * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split == 1) return e;
-    hipLaunchKernelGGL(multi_merge_kernel, dim3(p.batch * p.num_kv_heads), dim3(256), 0, s, p,
-                       G * T, G);
+    hipLaunchKernelGGL(multi_merge_kernel, dim3(p.batch * p.num_kv_heads * G * T), dim3(kHeadDim),
+                       0, s, p, G * T, G);
     return hipGetLastError();
 }
 
