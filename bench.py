@@ -300,7 +300,7 @@ def layer_path(path, lt):
 KERNELS = {
     ("separate", "sliding"): "decode_pair_kernel<2, false>",
     ("separate", "full"): "decode_stream_kernel<4, false> + stream_merge_kernel",
-    ("fused", "sliding"): "decode_window_step_kernel<2, 256>",
+    ("fused", "sliding"): "decode_window_step_kernel<2, 256, false>",
     ("fused", "full"): "decode_step_kernel<4, 64>",
 }
 # Sources whose change invalidates a committed traffic measurement.
