@@ -167,13 +167,13 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
             issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
             issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
             int e = r0e_of(r);
-            st.template round<false, false, uint4, true>(qa, kA, vA, 16 * r - e, n_old - e,
+            st.template round<false, false, uint4, true, true>(qa, kA, vA, 16 * r - e, n_old - e,
                                                          p.scale_log2, s_pw[wave], s_kt[wave],
                                                          lane, -1, nullptr, nullptr, 1.f, 1.f,
                                                          dkey_of(e), trow);
             if (!two) break;
             e = r0e_of(r + 1);
-            st.template round<false, false, uint4, true>(qa, kB, vB, 16 * (r + 1) - e, n_old - e,
+            st.template round<false, false, uint4, true, true>(qa, kB, vB, 16 * (r + 1) - e, n_old - e,
                                                          p.scale_log2, s_pw[wave], s_kt[wave],
                                                          lane, -1, nullptr, nullptr, 1.f, 1.f,
                                                          dkey_of(e), trow);
@@ -189,7 +189,7 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
                 kA[j] = ld16(p.k_new + row);
                 vA[j] = ld16(p.v_new + row);
             }
-            st.template round<false, false, uint4, true>(qa, kA, vA, 0, T, p.scale_log2,
+            st.template round<false, false, uint4, true, true>(qa, kA, vA, 0, T, p.scale_log2,
                                                          s_pw[wave], s_kt[wave], lane, -1,
                                                          nullptr, nullptr, 1.f, 1.f, -mrow, ntrow);
         }

@@ -146,7 +146,13 @@ struct WaveSoftmax {
     // ROWMASK (several query rows per head group, e.g. the tokens of a
     // chunk): row 4*kg + i also needs dkey >= trow[i] for this lane's key.
     // A row may then see no key in a round, so -inf maxima are guarded.
-    template <bool SUB = false, bool F8 = false, typename KV = uint4, bool ROWMASK = false>
+    // PVDOT (bf16 cache, no SUB): the probabilities go to LDS as bf16, the
+    // two keys a lane multiplies together (rows 2u + hw and 2u + 2 + hw)
+    // side by side in one word, and P.V runs on v_dot2c_f32_bf16 -- half the
+    // multiplies and no unpacking of V, for many query rows.  (pw holds
+    // 16 * G floats; the bf16 layout uses half of it.)
+    template <bool SUB = false, bool F8 = false, typename KV = uint4, bool ROWMASK = false,
+              bool PVDOT = false>
     __device__ __forceinline__ void round(const bf16x8 *qa, const KV *kt, KV *vt, int lo,
                                           int hi, float scale_log2, float *pw, uint16_t *ktile, int lane,
                                           int vr = -1, const uint16_t *knew = nullptr,
@@ -194,7 +200,17 @@ struct WaveSoftmax {
             m_run[i] = mn;
             sc[i] = s;
         }
-        if (4 * kg < G) {
+        if constexpr (PVDOT) {
+            // key k's slot in its row: 4 (k >> 2) + 2 (k & 1) + ((k >> 1) & 1)
+            uint16_t *pw16 = reinterpret_cast<uint16_t *>(pw);
+            const int slot = 4 * (mrow >> 2) + 2 * (mrow & 1) + ((mrow >> 1) & 1);
+            if (4 * kg < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * kg + i < G)
+                        pw16[(4 * kg + i) * 16 + slot] = __builtin_bit_cast(uint16_t, (__bf16)sc[i]);
+            }
+        } else if (4 * kg < G) {
             const float vf = valid ? vsc : 0.f;  // a masked key's scale may be anything
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -229,6 +245,32 @@ struct WaveSoftmax {
             }
         }
         wave_lds_fence();
+        if constexpr (PVDOT) {
+            const uint32_t *pw32 = reinterpret_cast<const uint32_t *>(pw);
+#pragma unroll
+            for (int up = 0; up < 4; ++up) {
+                // keys 4 up + hw and 4 up + 2 + hw: their dims paired per word
+                const uint4 va = vt[2 * up], vb = vt[2 * up + 1];
+                const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+                uint32_t vp[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vp[2 * i] = __builtin_amdgcn_perm(wb[i], wa[i], 0x05040100u);
+                    vp[2 * i + 1] = __builtin_amdgcn_perm(wb[i], wa[i], 0x07060302u);
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint32_t pp = pw32[h * 8 + 2 * up + hw];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(bf16x2_t, vp[e]), __builtin_bit_cast(bf16x2_t, pp),
+                            acc[h][e], false);
+                }
+            }
+            wave_lds_fence();
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             float pv[G], x[8];
