@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         RoundAddr nxt = more ? advance(cur) : cur;
         RoundGeo gn = geo(nxt);
         issue(gn, more ? lane : 0, kB, vB, ksB, vsB);
-        st.template round<false, F8>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
+        st.template round<false, F8, KV, false, !F8>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
                                      nullptr, nullptr, ksA, vsA);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         nxt = more ? advance(cur) : cur;
         gn = geo(nxt);
         issue(gn, more ? lane : 0, kA, vA, ksA, vsA);
-        st.template round<false, F8>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
+        st.template round<false, F8, KV, false, !F8>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
                                      nullptr, nullptr, ksB, vsB);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
@@ -521,11 +521,11 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
                 issue(r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB, ksB, vsB);
             }
             int e = r0e_of(r);
-            st.template round<false, F8>(qa, kA, vA, 16 * r - e, n - e, p.scale_log2, s_pw[wave],
+            st.template round<false, false, KV, false, true>(qa, kA, vA, 16 * r - e, n - e, p.scale_log2, s_pw[wave],
                                          s_kt[wave], lane, -1, nullptr, nullptr, ksA, vsA);
             if (!two) break;
             e = r0e_of(r + 1);
-            st.template round<false, F8>(qa, kB, vB, 16 * (r + 1) - e, n - e, p.scale_log2,
+            st.template round<false, false, KV, false, true>(qa, kB, vB, 16 * (r + 1) - e, n - e, p.scale_log2,
                                          s_pw[wave], s_kt[wave], lane, -1, nullptr, nullptr, ksB,
                                          vsB);
         }

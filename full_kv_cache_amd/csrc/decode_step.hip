@@ -659,13 +659,18 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
                 }
                 return;
             } else {
-            // only the round holding the new token's row takes the
-            // substituting form (the condition is wave-uniform)
-            if (vr >= lo && vr < hi && vr < 16)
-                st.template round<true>(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave], s_kt[wave], lane, vr,
-                                        s_knew, s_vnew);
-            else
-                st.round(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave], s_kt[wave], lane);
+            // the round holding the new token's row takes it from LDS
+            // (the condition is wave-uniform); P.V on bf16 dot products
+            if (vr >= lo && vr < hi && vr < 16) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (2 * j + hw == vr) {
+                        kt[j] = *reinterpret_cast<const uint4 *>(s_knew + 8 * dl);
+                        vt[j] = *reinterpret_cast<const uint4 *>(s_vnew + 8 * dl);
+                    }
+            }
+            st.template round<false, false, uint4, false, true>(qa, kt, vt, lo, hi, p.scale_log2,
+                                                                s_pw[wave], s_kt[wave], lane);
             if (srow >= 0 && sr >= lo && sr < hi && sr < 16) {  // keep the slot's old entry
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
