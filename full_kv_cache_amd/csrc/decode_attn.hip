@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
                 ad[t] = live ? advance(ad[prv]) : ad[prv];
                 ge[t] = geo(ad[t]);
                 issue(ge[t], live ? lane : 0, kb[t], vb[t], ksb[t], vsb[t]);
-                st.template round<false, true>(qa, kb[s], vb[s], ge[s].lo, ge[s].hi, p.scale_log2,
+                st.template round<false, F8, KV, false, true>(qa, kb[s], vb[s], ge[s].lo, ge[s].hi, p.scale_log2,
                                                s_pw, s_kt, lane, -1, nullptr, nullptr, ksb[s],
                                                vsb[s]);
                 const bool more = g + 1 < g1;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
                 for (int i = 0; i < NB; ++i) {
                     if (r + i >= r_hi) break;
                     const int e = r0e_of(r + i);
-                    st.template round<false, true>(qa, kb[i], vb[i], 16 * (r + i) - e, n - e,
+                    st.template round<false, true, KV, false, true>(qa, kb[i], vb[i], 16 * (r + i) - e, n - e,
                                                    p.scale_log2, s_pw[wave], s_kt[wave], lane, -1,
                                                    nullptr, nullptr, ksb[i], vsb[i]);
                 }

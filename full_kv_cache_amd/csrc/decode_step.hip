@@ -643,8 +643,9 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
                         vsc = s_c8s[1];
                     }
                 }
-                st.template round<false, true>(qa, kt, vt, lo, hi, p.scale_log2, s_pw[wave],
-                                               s_kt[wave], lane, -1, nullptr, nullptr, ksc, vsc);
+                st.template round<false, true, KV, false, true>(qa, kt, vt, lo, hi, p.scale_log2,
+                                                                s_pw[wave], s_kt[wave], lane, -1,
+                                                                nullptr, nullptr, ksc, vsc);
                 if (srow >= 0 && sr >= lo && sr < hi && sr < 16) {  // keep the slot's old entry
 #pragma unroll
                     for (int u = 0; u < 8; ++u)

@@ -146,7 +146,7 @@ struct WaveSoftmax {
     // ROWMASK (several query rows per head group, e.g. the tokens of a
     // chunk): row 4*kg + i also needs dkey >= trow[i] for this lane's key.
     // A row may then see no key in a round, so -inf maxima are guarded.
-    // PVDOT (bf16 cache, no SUB): the probabilities go to LDS as bf16, the
+    // PVDOT (no SUB): the probabilities go to LDS as bf16, the
     // two keys a lane multiplies together (rows 2u + hw and 2u + 2 + hw)
     // side by side in one word, and P.V runs on v_dot2c_f32_bf16 -- half the
     // multiplies and no unpacking of V, for many query rows.  (pw holds
@@ -205,10 +205,12 @@ struct WaveSoftmax {
             uint16_t *pw16 = reinterpret_cast<uint16_t *>(pw);
             const int slot = 4 * (mrow >> 2) + 2 * (mrow & 1) + ((mrow >> 1) & 1);
             if (4 * kg < G) {
+                const float vf = F8 ? (valid ? vsc : 0.f) : 1.f;  // fp8: the key's V scale
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (4 * kg + i < G)
-                        pw16[(4 * kg + i) * 16 + slot] = __builtin_bit_cast(uint16_t, (__bf16)sc[i]);
+                        pw16[(4 * kg + i) * 16 + slot] =
+                            __builtin_bit_cast(uint16_t, (__bf16)(F8 ? sc[i] * vf : sc[i]));
             }
         } else if (4 * kg < G) {
             const float vf = valid ? vsc : 0.f;  // a masked key's scale may be anything
@@ -250,7 +252,15 @@ struct WaveSoftmax {
 #pragma unroll
             for (int up = 0; up < 4; ++up) {
                 // keys 4 up + hw and 4 up + 2 + hw: their dims paired per word
-                const uint4 va = vt[2 * up], vb = vt[2 * up + 1];
+                // (fp8 codes become bf16 first: exact)
+                uint4 va, vb;
+                if constexpr (F8) {
+                    va = e4m3x8_to_bf16x8(vt[2 * up]);
+                    vb = e4m3x8_to_bf16x8(vt[2 * up + 1]);
+                } else {
+                    va = vt[2 * up];
+                    vb = vt[2 * up + 1];
+                }
                 const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
                 uint32_t vp[8];
 #pragma unroll

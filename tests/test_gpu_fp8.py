@@ -181,11 +181,13 @@ def test_fp8_quantize_ties_subnormals_zero():
     assert d["vs"][0, 0, 3].item() == 1.0 and d["vs"][0, 1, 3].item() == 0.5
     assert np.all(vc[2, :, 77] == 0) and torch.all(d["vs"][2, :, 77] == 0)
     assert torch.all(d["ks"][2, :, 77] == 0)
-    # sequence 0 attends to values up to 448: its outputs reach ~100, where
-    # bf16 itself rounds by 2^-9 relative -- a relative bound there
+    # sequence 0 attends to values up to 448: its outputs reach ~100, so the
+    # bound there is relative -- P.V takes each probability rounded to bf16
+    # (2^-9 relative) while the sum keeps fp32 weights (up to 2 x 2^-9), and
+    # out itself is bf16 (2^-9): 3 x 2^-9 < 6e-3, bounded by 8e-3
     assert_attn_close(out[1:], ref[1:])
     got0 = to_f64(out[0])
-    assert np.all(np.abs(got0 - ref[0]) <= 4e-3 * np.abs(ref[0]) + 1e-2)
+    assert np.all(np.abs(got0 - ref[0]) <= 8e-3 * np.abs(ref[0]) + 1e-2)
     np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
 
 
