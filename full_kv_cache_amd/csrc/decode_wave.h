@@ -13,7 +13,10 @@
 //     lanes (DPP), rescale of the running sum and output;
 //   * P.V on the vector ALUs: each half-wave streams whole 512-byte V rows
 //     (lane = 8 dims), every row serving all G heads; the probabilities
-//     reach those lanes through LDS.
+//     reach those lanes through LDS -- in the PVDOT form (the decode
+//     kernels' default) as bf16, two keys per word, multiplied with
+//     v_dot2c_f32_bf16 (fp32 accumulation; the running sum keeps the fp32
+//     weights).
 #pragma once
 
 #include "hda_device.h"
