@@ -281,7 +281,11 @@ struct WaveSoftmax {
                             acc[h][e], false);
                 }
             }
-            wave_lds_fence();
+            // No wait here: the next round's tile and probability stores
+            // come after these reads in this wave's LDS queue, which runs
+            // in order; the barrier only keeps the compiler from moving them
+            // (measured: 0.3 us off a sliding layer).
+            __builtin_amdgcn_wave_barrier();
             return;
         }
 #pragma unroll
