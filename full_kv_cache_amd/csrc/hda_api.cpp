@@ -709,12 +709,11 @@ hda_status check_multi_shape(const hda_cache_desc *c, int layer, int32_t tokens,
 }
 
 // Workgroups per (sequence, KV head) of the chunk decode.  Measured on
-// MI355X (4-token chunks): a split pays its merge launch and partials only
-// where the pairs alone leave the chip idle or a pair has many rounds --
-// at 128 pairs a 32-round sliding window is fastest unsplit, a 4k full
-// layer split in 2; at 16 pairs splits of 4 and 8.  So: about 256
-// workgroups (128 when there are few pairs), each with at least 32 rounds
-// (8 with few pairs).  max_seq_len bounds pos + tokens; it only sizes the
+// MI355X (4-token chunks, bf16-dot P.V): at 128 pairs a 32-round sliding
+// window and a 4k full layer are fastest split in 2; at 16 pairs splits of
+// 4 and 8 -- more parts than that pay more in merge traffic than they
+// gain.  So: about 256 workgroups (128 when there are few pairs), each with
+// at least 16 rounds (8 with few pairs).  max_seq_len bounds pos + tokens; it only sizes the
 // split (every workgroup takes its share of the rounds the sequence has).
 int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_seq_len) {
     int64_t n_old = (int64_t)max_seq_len - tokens;
@@ -724,7 +723,7 @@ int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_
     const int64_t rounds = (n_old + 15) / 16;
     const int64_t pairs = (int64_t)c->batch * c->num_kv_heads;
     const bool many = pairs >= 64;
-    const int64_t target = many ? 256 : 128, min_rounds = many ? 32 : 8;
+    const int64_t target = many ? 256 : 128, min_rounds = many ? 16 : 8;
     int64_t s = pairs > 0 ? (target + pairs - 1) / pairs : 1;
     const int64_t by_rounds = rounds / min_rounds;
     if (s > by_rounds) s = by_rounds;
