@@ -213,19 +213,47 @@ struct RoundGeo {
     int r0e, lo, hi;  // in-bounds first row; valid keys [lo, hi) of the round
 };
 
+template <bool STEP>
+using StepArg = std::conditional_t<STEP, StreamStep, NoStep>;
+
+// Keys of sequence b in the step form: the rows its block held before this
+// token (the new one is scored by the merge).
+__device__ __forceinline__ int held_keys(const StreamStep &ss, int64_t capacity, int b) {
+    const int P = ss.pos[b];
+    return P < 0 ? 0 : (int)((int64_t)P < capacity ? P : capacity);
+}
+
 // F8: the cache holds e4m3 codes and per-row scales (kq, vq, ks, vs).
-template <int G, bool F8>
-__global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
+// ROT > 0: the step form (bf16, rotary_dim ROT): keys are the held rows, q
+// is rotated in registers at each pair's position.
+template <int G, bool F8, int ROT = 0>
+__global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepArg<(ROT > 0)> ss) {
+    constexpr bool STEP = ROT > 0;
+    static_assert(!(STEP && F8), "the step form is built for bf16 caches");
     constexpr int D = kHeadDim;
     extern __shared__ int s_pre[];                 // [B + 1] rounds before sequence b, one KV head
     __shared__ __align__(16) float s_pw[16 * G];   // this round's probabilities [key][head]
     __shared__ __align__(16) uint16_t s_kt[kKTile];
+    __shared__ __align__(16) float2 s_cs[STEP ? D / 2 : 1];  // step form: (cos, sin) per angle
+    __shared__ float s_freq[STEP ? D / 2 : 1];                // step form: frequencies
 
     const int lane = threadIdx.x;
     const int w = blockIdx.x, W = gridDim.x;
     const int B = p.batch, Hkv = p.num_kv_heads;
+    auto keys_of = [&](int b) HDA_INLINE {
+        if constexpr (STEP)
+            return held_keys(ss, p.capacity, b);
+        else
+            return num_keys(p, b);
+    };
+    // step form: the frequencies into LDS before any K/V row is loaded
+    if constexpr (STEP) {
+#pragma unroll
+        for (int i = 0; i < (ROT / 2 + 63) / 64; ++i)
+            if (lane + 64 * i < ROT / 2) s_freq[lane + 64 * i] = ss.inv_freq[lane + 64 * i];
+    }
 
-    round_prefix(s_pre, B, lane, [&](int b) { return num_keys(p, b); });
+    round_prefix(s_pre, B, lane, [&](int b) { return keys_of(b); });
     __syncthreads();
     if (w == 0)  // published for the merge kernel
         for (int b = lane; b <= B; b += 64) p.stream_pre[b] = s_pre[b];
@@ -249,13 +277,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
             g.base = (pg * Hkv + a.kvh) * ps;
             g.r0e = r0 % ps;
             g.lo = 0;
-            g.hi = uniform(num_keys(p, a.b)) - r0;
+            g.hi = uniform(keys_of(a.b)) - r0;
             return g;
         }
         g.base = ((int64_t)a.b * Hkv + a.kvh) * cap;
         g.r0e = (int)(r0 < cap16 ? r0 : cap16);
         g.lo = r0 - g.r0e;
-        g.hi = uniform(num_keys(p, a.b)) - g.r0e;
+        g.hi = uniform(keys_of(a.b)) - g.r0e;
         return g;
     };
     auto same_pair = [](const RoundAddr &x, const RoundAddr &y) { return x.b == y.b && x.kvh == y.kvh; };
@@ -327,9 +355,35 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
     KV kA[8], vA[8], kB[8], vB[8];
     float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
     RoundGeo gc = geo(cur);
-    issue(gc, lane, kA, vA, ksA, vsA);
-    load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
+    if constexpr (STEP) {
+        // q before the first round's rows: its rotation waits for q alone
+        load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
+        issue(gc, lane, kA, vA, ksA, vsA);
+        rope_angles<ROT>(s_cs, s_freq, uniform(ss.pos[cur.b]), lane);
+        rotate_q_operand<ROT>(qa, s_cs, lane);
+    } else {
+        issue(gc, lane, kA, vA, ksA, vsA);
+        load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
+    }
     st.reset();
+    // Step form, entering a pair: its q rows are loaded and its angles put
+    // in LDS at once, but the rotation waits until the next round's loads
+    // are issued (q is then older than every load in flight but those of
+    // the round about to be scored, so the pipeline keeps its depth).
+    bool rot_pending = false;
+    auto enter_pair = [&](const RoundAddr &a) HDA_INLINE {
+        load_q_operand<G>(p.q, p.num_q_heads, a.b, a.kvh, lane, qa);
+        if constexpr (STEP) {
+            rope_angles<ROT>(s_cs, s_freq, uniform(ss.pos[a.b]), lane);
+            rot_pending = true;
+        }
+    };
+    auto rotate_pending = [&]() HDA_INLINE {
+        if constexpr (STEP) {
+            if (rot_pending) rotate_q_operand<ROT>(qa, s_cs, lane);
+            rot_pending = false;
+        }
+    };
 
     // Every half-iteration issues the next round's loads, then computes the
     // current round.  After the last round a placeholder round is issued
@@ -341,12 +395,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         RoundAddr nxt = more ? advance(cur) : cur;
         RoundGeo gn = geo(nxt);
         issue(gn, more ? lane : 0, kB, vB, ksB, vsB);
+        rotate_pending();
         st.template round<false, F8, KV, false, !F8>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
                                      nullptr, nullptr, ksA, vsA);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
-            load_q_operand<G>(p.q, p.num_q_heads, nxt.b, nxt.kvh, lane, qa);
+            enter_pair(nxt);
             st.reset();
         }
         cur = nxt;
@@ -357,12 +412,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
         nxt = more ? advance(cur) : cur;
         gn = geo(nxt);
         issue(gn, more ? lane : 0, kA, vA, ksA, vsA);
+        rotate_pending();
         st.template round<false, F8, KV, false, !F8>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
                                      nullptr, nullptr, ksB, vsB);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
-            load_q_operand<G>(p.q, p.num_q_heads, nxt.b, nxt.kvh, lane, qa);
+            enter_pair(nxt);
             st.reset();
         }
         cur = nxt;
@@ -377,7 +433,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p) {
 // w + pair.  Lane s reads segment s's lse (64 segments a pass), the wave
 // reduces max and sum, then the partials are read as float4 per lane in
 // unrolled batches so that their loads are in flight together.
-__global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W) {
+//
+// STEP (hda_decode_step, full layer): the new token is one more key, row
+// pos of its block when pos < capacity.  Each wave rotates its head's q
+// and the new K at pos (4 dims per lane; the partner dim i +- rot/2 read
+// from memory, the same fp32 fma and bf16 rounding as the append kernel),
+// scores them, and takes (score, v_new) as one more partial; the wave of
+// the group's first head appends the rotated K and V to row pos (nothing
+// in this launch reads the cache).
+template <bool STEP>
+__global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W, StepArg<STEP> ss) {
     constexpr int D = kHeadDim;
     constexpr int kBatch = 16;
     const int hq = blockIdx.x % p.num_q_heads, b = blockIdx.x / p.num_q_heads;
@@ -387,7 +452,13 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W)
     const int rb = p.stream_pre[b + 1] - p.stream_pre[b];
     const int64_t row = (int64_t)b * Hq + hq;
     uint16_t *outp = p.out + row * D + 4 * lane;
-    if (rb == 0) {
+    bool fresh = false;  // step form: the new token is a key
+    int P = 0;
+    if constexpr (STEP) {
+        P = ss.pos[b];
+        fresh = P >= 0 && (int64_t)P < p.capacity;
+    }
+    if (rb == 0 && !fresh) {
         *reinterpret_cast<uint2 *>(outp) = make_uint2(0, 0);
         if (lane == 0 && p.lse) p.lse[row] = -INFINITY;
         return;
@@ -395,24 +466,91 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W)
     const int64_t r_tot = (int64_t)Hkv * p.stream_pre[p.batch];
     const int We = split_waves(W, r_tot);
     const int64_t g_lo = (int64_t)Hkv * p.stream_pre[b] + (int64_t)kvh * rb;
-    const int w_lo = wave_of_round(g_lo, r_tot, We);
-    const int nseg = wave_of_round(g_lo + rb - 1, r_tot, We) - w_lo + 1;
+    const int w_lo = rb > 0 ? wave_of_round(g_lo, r_tot, We) : 0;
+    const int nseg = rb > 0 ? wave_of_round(g_lo + rb - 1, r_tot, We) - w_lo + 1 : 0;
     const int64_t s0 = w_lo + (int64_t)b * Hkv + kvh;  // first slot
-    float M = -INFINITY;
-    for (int c = 0; c < nseg; c += 64)
-        if (c + lane < nseg) M = fmaxf(M, p.part_lse[(s0 + c + lane) * G + h]);
-    M = wave_max(M);
-    float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int base = 0; base < nseg; base += kBatch) {
-        float4 v[kBatch];
-        float wgt[kBatch];
+    // The first batch of partials and their lse go out first; the lse
+    // maximum and (step form) the new token's chain run while they are in
+    // flight.
+    float4 v[kBatch];
+    float wgt[kBatch];
+    auto load_batch = [&](int base) HDA_INLINE {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int s = min(base + k, nseg - 1);
             v[k] = *reinterpret_cast<const float4 *>(p.part_o + ((s0 + s) * G + h) * D + 4 * lane);
             wgt[k] = base + k < nseg ? p.part_lse[(s0 + s) * G + h] : -INFINITY;
         }
+    };
+    if (nseg > 0) load_batch(0);
+    float M = -INFINITY;
+    for (int c = 0; c < nseg; c += 64)
+        if (c + lane < nseg) M = fmaxf(M, p.part_lse[(s0 + c + lane) * G + h]);
+    float s_new = -INFINITY;
+    float vn[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (STEP) {
+        if (fresh) {
+            const int d0 = 4 * lane, rot = ss.rotary_dim, half = rot >> 1;
+            const int64_t kvrow = ((int64_t)b * Hkv + kvh) * D;
+            const uint16_t *qr = p.q + row * D, *kr = ss.k_new + kvrow;
+            const uint2 qw = *reinterpret_cast<const uint2 *>(qr + d0);
+            const uint2 kw = *reinterpret_cast<const uint2 *>(kr + d0);
+            const uint2 vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
+            float qx[4] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y)};
+            float kx[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
+            vn[0] = bf16_lo(vw.x);
+            vn[1] = bf16_hi(vw.x);
+            vn[2] = bf16_lo(vw.y);
+            vn[3] = bf16_hi(vw.y);
+            uint2 krot = kw;
+            if (d0 < rot) {
+                const bool first = d0 < half;  // x1 (first half) or x2
+                const int pd = first ? d0 + half : d0 - half, i0 = first ? d0 : d0 - half;
+                const uint2 qp = *reinterpret_cast<const uint2 *>(qr + pd);
+                const uint2 kp = *reinterpret_cast<const uint2 *>(kr + pd);
+                const float qy[4] = {bf16_lo(qp.x), bf16_hi(qp.x), bf16_lo(qp.y), bf16_hi(qp.y)};
+                const float ky[4] = {bf16_lo(kp.x), bf16_hi(kp.x), bf16_lo(kp.y), bf16_hi(kp.y)};
+                uint16_t kb[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float c, sn;
+                    sincos_angle((float)P * ss.inv_freq[i0 + e], &c, &sn);
+                    // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
+                    const uint16_t qb = f32_to_bf16(first ? fmaf(qx[e], c, -qy[e] * sn) : fmaf(qx[e], c, qy[e] * sn));
+                    kb[e] = f32_to_bf16(first ? fmaf(kx[e], c, -ky[e] * sn) : fmaf(kx[e], c, ky[e] * sn));
+                    qx[e] = bf16_to_f32(qb);
+                    kx[e] = bf16_to_f32(kb[e]);
+                }
+                krot = make_uint2((uint32_t)kb[0] | ((uint32_t)kb[1] << 16),
+                                  (uint32_t)kb[2] | ((uint32_t)kb[3] << 16));
+            }
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dot = fmaf(qx[e], kx[e], dot);
+            s_new = wave_sum(dot) * (p.scale_log2 * kLn2);  // natural-log units, as the partials
+            if (h == 0) {
+                int64_t base;
+                if (p.pages.block_table) {
+                    const int ps = p.pages.page_size;
+                    base = (page_of(p.pages, b, P) * Hkv + kvh) * ps + P % ps;
+                } else {
+                    base = ((int64_t)b * Hkv + kvh) * p.capacity + P;
+                }
+                *reinterpret_cast<uint2 *>(ss.k + base * D + d0) = krot;
+                *reinterpret_cast<uint2 *>(ss.v + base * D + d0) = vw;
+            }
+        }
+    }
+    M = fmaxf(wave_max(M), s_new);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (STEP && fresh) {
+        const float e = expf(s_new - M);
+        L = e;
+        o = make_float4(e * vn[0], e * vn[1], e * vn[2], e * vn[3]);
+    }
+    for (int base = 0; base < nseg; base += kBatch) {
+        if (base > 0) load_batch(base);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const float e = expf(wgt[k] - M);  // padding: exp(-inf) = 0
@@ -616,13 +754,30 @@ template <int G>
 hipError_t launch_stream_g(const DecodeParams &p, int waves, hipStream_t s) {
     if (p.kq)
         hipLaunchKernelGGL((decode_stream_kernel<G, true>), dim3(waves), dim3(64),
-                           (p.batch + 1) * sizeof(int), s, p);
+                           (p.batch + 1) * sizeof(int), s, p, NoStep{});
     else
         hipLaunchKernelGGL((decode_stream_kernel<G, false>), dim3(waves), dim3(64),
-                           (p.batch + 1) * sizeof(int), s, p);
+                           (p.batch + 1) * sizeof(int), s, p, NoStep{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_stream_merge(p, waves, s);
+}
+
+template <int G>
+hipError_t launch_stream_step_g(const DecodeParams &p, const StreamStep &ss, int waves, hipStream_t s) {
+    if (ss.rotary_dim == 64)
+        hipLaunchKernelGGL((decode_stream_kernel<G, false, 64>), dim3(waves), dim3(64),
+                           (p.batch + 1) * sizeof(int), s, p, ss);
+    else if (ss.rotary_dim == 256)
+        hipLaunchKernelGGL((decode_stream_kernel<G, false, 256>), dim3(waves), dim3(64),
+                           (p.batch + 1) * sizeof(int), s, p, ss);
+    else
+        return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(stream_merge_kernel<true>, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)),
+                       dim3(64), 0, s, p, waves, ss);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -662,6 +817,19 @@ int stream_wave_slots(int group) {
     }
 }
 
+hipError_t launch_decode_stream_step(const DecodeParams &p, const StreamStep &ss, int group, int waves,
+                                     hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    switch (group) {
+        case 1: return launch_stream_step_g<1>(p, ss, waves, stream);
+        case 2: return launch_stream_step_g<2>(p, ss, waves, stream);
+        case 4: return launch_stream_step_g<4>(p, ss, waves, stream);
+        case 8: return launch_stream_step_g<8>(p, ss, waves, stream);
+        case 16: return launch_stream_step_g<16>(p, ss, waves, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_decode_stream(const DecodeParams &p, int group, int waves, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
     switch (group) {
@@ -689,8 +857,8 @@ hipError_t launch_decode_pairs(const DecodeParams &p, int group, hipStream_t str
 
 hipError_t launch_stream_merge(const DecodeParams &p, int waves, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(stream_merge_kernel, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)), dim3(64), 0,
-                       stream, p, waves);
+    hipLaunchKernelGGL(stream_merge_kernel<false>, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)),
+                       dim3(64), 0, stream, p, waves, NoStep{});
     return hipGetLastError();
 }
 

@@ -7,6 +7,11 @@
 // ring branch; flashmla_sparse page, `HYV4FlashMLASparseImpl` docstring, for
 // the sink), except that the rotated q lives in registers only.
 //
+// hda_decode_step takes this kernel for sliding windows past one workgroup
+// (more than 1024 keys); full layers take the streaming kernel's step form
+// and sliding windows up to 1024 keys the window step below.  Its
+// full-layer handling (sliding == 0) stays correct but is not routed to.
+//
 // Keys of sequence b at position P are rows 0..n-1 of its block, n =
 // min(P+1, window) for a sliding layer, min(P+1, capacity) for a full one.
 // Row vrow = min(P, window-1) (sliding) or P (full) stands for the new token:

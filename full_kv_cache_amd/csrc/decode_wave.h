@@ -112,6 +112,52 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *q, int num_q_head
     for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(ld16(qr + 32 * j));
 }
 
+// Neox RoPE of the q operand in registers.  A lane holds dims 32j +
+// 8(lane/16) .. +7 of chunk j; with rot = 64 NC, dim i < rot/2 pairs with
+// i + rot/2, which sits in chunk j + NC of the same lane, so the rotation
+// needs no lane exchange.  s_cs[i] holds (cos, sin) of angle i, shared
+// through LDS (one fp64 evaluation per angle, written by rope_angles).
+template <int NC>
+__device__ __forceinline__ void rotate_q_chunks(bf16x8 *qa, const float2 *s_cs, int kg) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        float c[8], s[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float2 cs = s_cs[32 * j + 8 * kg + e];
+            c[e] = cs.x;
+            s[e] = cs.y;
+        }
+        uint4 ya, yb;
+        rotate8(__builtin_bit_cast(uint4, qa[j]), __builtin_bit_cast(uint4, qa[j + NC]), c, s, ya, yb);
+        qa[j] = as_bf16x8(ya);
+        qa[j + NC] = as_bf16x8(yb);
+    }
+}
+template <int ROT>
+__device__ __forceinline__ void rotate_q_operand(bf16x8 *qa, const float2 *s_cs, int lane) {
+    static_assert(ROT % 64 == 0 && ROT >= 64 && ROT <= 256, "rot = 64 NC, NC in 1..4");
+    wave_lds_fence();  // rope_angles' stores are in
+    rotate_q_chunks<ROT / 64>(qa, s_cs, lane >> 4);
+}
+// (cos, sin) of angles i < ROT/2 at position P into s_cs; s_freq holds
+// the fp32 frequencies (kept in LDS: no register stays live for them
+// through the rounds).  The angle is one fp32 product, as everywhere the
+// rotation is applied.
+template <int ROT>
+__device__ __forceinline__ void rope_angles(float2 *s_cs, const float *s_freq, int P, int lane) {
+    wave_lds_fence();  // earlier reads of s_cs are done
+    float c, s;
+#pragma unroll
+    for (int i = 0; i < (ROT / 2 + 63) / 64; ++i) {
+        const int a = lane + 64 * i;
+        if (a < ROT / 2) {
+            sincos_angle((float)P * s_freq[a], &c, &s);
+            s_cs[a] = make_float2(c, s);
+        }
+    }
+}
+
 // One wave's running softmax state over 16-key rounds.
 //   acc[h][e]: unnormalised output, head h, dim 8*(lane%32) + e, summed
 //              over this half-wave's keys (the two halves add up at the end);

@@ -291,13 +291,22 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
     if (c->batch > hda::kStreamMaxBatch)
         return fail(HDA_ERR_UNSUPPORTED, "the fused step handles at most %d sequences, got %d",
                     hda::kStreamMaxBatch, c->batch);
-    if (c->block_table)
-        return fail(HDA_ERR_UNSUPPORTED, "the one-launch step is built for contiguous caches only");
+    if (c->block_table && layer != HDA_FULL)
+        return fail(HDA_ERR_UNSUPPORTED, "the step on a paged cache is built for full layers");
     if (c->kv_dtype != HDA_KV_BF16 && !(layer == HDA_SLIDING && c->window <= hda::kPairMaxKeys))
-        return fail(HDA_ERR_UNSUPPORTED, "the one-launch step on an fp8 cache is built for "
-                    "sliding windows of at most %d keys (bf16 otherwise)", hda::kPairMaxKeys);
+        return fail(HDA_ERR_UNSUPPORTED, "the step on an fp8 cache is built for sliding windows "
+                    "of at most %d keys (bf16 otherwise)", hda::kPairMaxKeys);
     return HDA_OK;
 }
+
+// Full layers: the streaming decode in its step form -- two launches, the
+// stream over the rows held before this token with q rotated in registers,
+// then the merge, which scores the new token and appends it.  Measured on
+// MI355X faster than the one-launch form (whose merge across waves and
+// in-loop append need about 330 registers) and than hda_rope_append +
+// hda_decode_attn (one launch fewer).  Its workspace is the streaming
+// path's, sized for a full block of keys.
+int stream_step_waves(const hda_cache_desc *c) { return stream_waves(c, c->capacity); }
 
 // ---------------------------------------------------------------- sparse
 // Key splits for the sparse decode: one workgroup per (token, split, group
@@ -619,6 +628,7 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
 size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer) {
     if (check_step_shape(cache, layer) != HDA_OK) return 0;
     if (use_window_step(cache, layer)) return counter_header(cache);
+    if (layer == HDA_FULL) return stream_layout(cache, stream_step_waves(cache)).bytes;
     return step_layout(cache, step_waves(cache, layer)).bytes;
 }
 
@@ -636,6 +646,37 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
         return fail(HDA_ERR_INVALID_ARGUMENT, "pos must be 4-byte aligned");
     if ((st = check_f32_ptrs(sinks, gate, lse)) != HDA_OK) return st;
     if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (layer == HDA_FULL) {
+        const int waves = stream_step_waves(cache);
+        const StreamLayout L = stream_layout(cache, waves);
+        if (!workspace || workspace_bytes < L.bytes)
+            return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", L.bytes,
+                        workspace_bytes, workspace);
+        if (!aligned16(workspace))
+            return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+        if (cache->batch == 0) return ok();
+        Plan one{hda::kMaxChunk, 1};
+        hda::DecodeParams p = decode_params(q, cache, nullptr, layer, scale, 0, one);
+        char *ws = static_cast<char *>(workspace);
+        p.part_o = reinterpret_cast<float *>(ws + L.o_off);
+        p.part_lse = reinterpret_cast<float *>(ws + L.lse_off);
+        p.stream_pre = reinterpret_cast<int *>(ws + L.pre_off);
+        p.sinks = sinks;
+        p.gate = gate;
+        p.out = static_cast<uint16_t *>(out);
+        p.lse = lse;
+        hda::StreamStep ss{};
+        ss.pos = pos;
+        ss.k_new = static_cast<const uint16_t *>(k_new);
+        ss.v_new = static_cast<const uint16_t *>(v_new);
+        ss.k = static_cast<uint16_t *>(cache->k);
+        ss.v = static_cast<uint16_t *>(cache->v);
+        ss.rotary_dim = cache->rotary_dim;
+        fill_inv_freq(ss.inv_freq, cache->rope_theta, cache->rotary_dim);
+        const int g = cache->num_q_heads / cache->num_kv_heads;
+        return launched(hda::launch_decode_stream_step(p, ss, g, waves, static_cast<hipStream_t>(stream)),
+                        "decode step");
+    }
     const bool window = use_window_step(cache, layer);
     const int waves = window ? 0 : step_waves(cache, layer);
     const StepLayout L = step_layout(cache, waves);

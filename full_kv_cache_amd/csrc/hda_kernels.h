@@ -90,6 +90,20 @@ struct StepParams {
     float inv_freq[kHeadDim / 2];  // fp32 theta^(-2i/rot), i < rot/2
 };
 
+// Step form of the streaming decode (hda_decode_step on a full layer): the
+// keys of sequence b are the rows its block held before this token,
+// min(pos, capacity) (none for pos < 0); the streaming kernel rotates q in
+// registers; the merge adds the new token's key (row pos when pos <
+// capacity) and appends it.
+struct StreamStep {
+    const int32_t *pos;              // [B]
+    const uint16_t *k_new, *v_new;   // [B, Hkv, D]
+    uint16_t *k, *v;                 // the cache (or page pools), written at row pos
+    int rotary_dim;                  // 64 or 256
+    float inv_freq[kHeadDim / 2];    // fp32 theta^(-2i/rot), i < rot/2
+};
+struct NoStep {};
+
 struct MergeParams {
     const float *part_o;        // [B, H, nsplit, D]
     const float *part_lse;      // [B, H, nsplit]
@@ -164,6 +178,10 @@ hipError_t launch_decode_chunks(const DecodeParams &p, int group, bool final_out
 // part_lse, then the merge writes out / lse with the sink.  Needs
 // capacity >= 16 and batch <= kStreamMaxBatch.
 hipError_t launch_decode_stream(const DecodeParams &p, int group, int waves, hipStream_t stream);
+// Streaming kernel in its step form, then the merge with the new token and
+// the append (p.seq_lens unused).
+hipError_t launch_decode_stream_step(const DecodeParams &p, const StreamStep &s, int group, int waves,
+                                     hipStream_t stream);
 
 // Single-wave workgroups of the streaming kernel that fit on the device at
 // once (occupancy x CUs); 0 if no device is available.

@@ -284,17 +284,19 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
 
 /*
  * hda_decode_step_workspace_bytes -- device workspace hda_decode_step needs
- * for this cache and layer type (0 for a description it refuses, a paged
- * one included).
+ * for this cache and layer type (0 for a description it refuses).
  */
 size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer);
 
 /*
- * hda_decode_step -- one layer's whole decode step in a single launch: the
- * work of hda_rope_append followed by hda_decode_attn with seq_lens[b] =
- * pos[b] + 1, with two differences: q is only read (its rotation stays in
+ * hda_decode_step -- one layer's whole decode step in one call: the work of
+ * hda_rope_append followed by hda_decode_attn with seq_lens[b] = pos[b] +
+ * 1, with two differences: q is only read (its rotation stays in
  * registers), and keys are cut at the cache (full: min(pos+1, capacity),
- * sliding: min(pos+1, window)) rather than at a max_seq_len.  After the
+ * sliding: min(pos+1, window)) rather than at a max_seq_len.  A sliding
+ * layer is one launch; a full layer two (the streaming kernel over the rows
+ * held before the token, then the merge, which scores the new token and
+ * writes it to row pos; a paged full-layer cache is accepted).  After the
  * call the cache holds what hda_rope_append leaves (new K/V in the ring
  * slot or row pos; for a sliding layer at pos >= window-1 the slot's
  * previous entry in row window-1), and out / lse what hda_decode_attn
@@ -312,9 +314,9 @@ size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_ty
  *              header, so one workspace serves both.  Calls sharing a
  *              workspace must be ordered on one stream.
  * Errors: as hda_decode_attn, plus UNSUPPORTED for rotary_dim other than
- * 64 or 256, batch above 4096, a paged cache, or an fp8 cache outside the
- * window form (sliding layers with window <= 1024; use hda_rope_append +
- * hda_decode_attn otherwise).  On an fp8 cache the new K and V rows are
+ * 64 or 256, batch above 4096, a paged sliding cache, or an fp8 cache
+ * outside the window form (sliding layers with window <= 1024; use
+ * hda_rope_append + hda_decode_attn otherwise).  On an fp8 cache the new K and V rows are
  * quantized as hda_rope_append quantizes them.  batch == 0 is a no-op.
  */
 hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,

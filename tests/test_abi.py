@@ -297,8 +297,9 @@ def test_paged_descriptor_checks():
 
 def test_paged_routing():
     """A paged cache is read only by the streaming kernel: split-K chunks,
-    the partials stage, the fused one-launch step and batches above the
-    streaming limit are refused before anything is enqueued."""
+    the partials stage and batches above the streaming limit are refused
+    before anything is enqueued; the full-layer step (the streaming
+    kernel's step form) takes it, with the streaming path's workspace."""
     L = hda.lib()
     d = _desc(**_PAGED)
     assert _decode(d, layer=hda.FULL, max_seq_len=1024, chunk=256) == 2
@@ -309,8 +310,9 @@ def test_paged_routing():
                                    hda.FULL, 0.0625, 1024, 256, ctypes.c_void_p(FAKE),
                                    ctypes.c_void_p(FAKE), None)
     assert r == 2 and "contiguous" in _msg()
-    assert _step(d, layer=hda.FULL) == 2 and "contiguous" in _msg()
-    assert L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.FULL) == 0
+    assert _step(d, layer=hda.FULL) == 3 and "workspace" in _msg()
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.FULL) == \
+        L.hda_decode_workspace_bytes(ctypes.byref(d), hda.FULL, 1024, 0) > 0
     assert _decode(_desc(**{**_PAGED, "batch": 0}), layer=hda.FULL, max_seq_len=16) == 0
 
 

@@ -216,3 +216,75 @@ def test_step_batch64_sampled():
         kk = bits_of(d["k"])[sample]
         assert bf16_ulp_diff(kk, h["k"]).max() <= 1
         assert np.array_equal(bits_of(d["v"])[sample], h["v"])
+
+
+def test_step_full_rotary_256():
+    """Full layer with the whole head rotated (rotary_dim 256: the q
+    operand's chunk j pairs with chunk j + 4 in the step form's in-register
+    rotation; the merge rotates 4 dims per lane against dim +- 128)."""
+    import dataclasses
+    pos = [0, 40, 1100, 2047]
+    _print_case(test="step_full_rot256", pos=pos)
+    case = HybridCase(1100, len(pos), FULL, pos, lmax=2048, poison=True)
+    case.shape = dataclasses.replace(case.shape, rot_full=256, theta_full=1e4)
+    h, ref, rlse = case.oracle_step()
+    d, out, lse = fused_step(case)
+    _check_cache(d, h)
+    assert np.array_equal(bits_of(d["q"]), case.host["q"])
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_step_full_paged(page_size):
+    """The full-layer step on a paged cache: the new row lands in the page
+    its table names (no spare page changes), out/lse match the oracle and
+    are bit-identical to the same step on the contiguous cache."""
+    import full_kv_cache_amd as hda
+    import oracle
+    import workloads
+    from test_gpu_paged import _page
+    pos = [0, 15, 16, 300, 2047]
+    _print_case(test="step_full_paged", page_size=page_size, pos=pos)
+    case = HybridCase(1200 + page_size, len(pos), FULL, pos, lmax=2048, poison=True)
+    s = case.shape
+    h, ref, rlse = case.oracle_step()
+    pk, pv, table, spare = _page(case, page_size)
+    pool_k, pool_v = workloads.from_bits(pk).cuda(), workloads.from_bits(pv).cuda()
+    d = case.device()
+    cache = hda.LayerCache(pool_k, pool_v, s.num_q_heads, s.window, s.rot(FULL), s.theta(FULL),
+                           block_table=torch.from_numpy(table).cuda())
+    ws = torch.zeros(hda.hda_decode_step_workspace_bytes(cache, FULL), dtype=torch.uint8, device="cuda")
+    out = torch.full((s.batch, s.num_q_heads, s.head_dim), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((s.batch, s.num_q_heads), float("nan"), device="cuda")
+    hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], torch.from_numpy(case.pos).cuda(), FULL, cache,
+                        None, 1 / 16, out, lse, ws)
+    torch.cuda.synchronize()
+    gk, gv = oracle.page_gather(bits_of(pool_k), table), oracle.page_gather(bits_of(pool_v), table)
+    for b, n in enumerate(case.seq_lens):
+        assert np.array_equal(gv[b, :, :n], h["v"][b, :, :n]), b
+        assert bf16_ulp_diff(gk[b, :, :n], h["k"][b, :, :n]).max() <= 1, b
+    assert np.array_equal(bits_of(pool_k)[spare], pk[spare])
+    assert np.array_equal(bits_of(pool_v)[spare], pv[spare])
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+    _, out_c, lse_c = fused_step(case)
+    assert torch.equal(out.view(torch.int16), out_c.view(torch.int16))
+    assert torch.equal(lse, lse_c)
+
+
+def test_step_full_matches_two_calls():
+    """The full-layer step against hda_rope_append + hda_decode_attn on
+    the same inputs: the same cache bit for bit, out within the decode
+    tolerance of each other (the new key is scored by the merge instead of
+    a round, so the sums differ in order only)."""
+    pos = [3, 500, 1999, 4095]
+    _print_case(test="step_full_vs_two_calls", pos=pos)
+    case = HybridCase(1300, len(pos), FULL, pos, lmax=4096, poison=True)
+    d1, out1, lse1 = fused_step(case)
+    d2, out2, lse2 = case.gpu_step(max_seq_len=4096)
+    assert torch.equal(d1["k"].view(torch.int16), d2["k"].view(torch.int16))
+    assert torch.equal(d1["v"].view(torch.int16), d2["v"].view(torch.int16))
+    assert_attn_close(out1, to_f64(out2))
+    np.testing.assert_allclose(to_f64(lse1), to_f64(lse2), rtol=0, atol=1e-5)
