@@ -236,6 +236,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
     __shared__ __align__(16) uint16_t s_kt[kKTile];
     __shared__ __align__(16) float2 s_cs[STEP ? D / 2 : 1];  // step form: (cos, sin) per angle
     __shared__ float s_freq[STEP ? D / 2 : 1];                // step form: frequencies
+    __shared__ __align__(16) uint16_t s_q[STEP ? G * D : 1];  // step form: the pair's rotated q rows
 
     const int lane = threadIdx.x;
     const int w = blockIdx.x, W = gridDim.x;
@@ -355,34 +356,47 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
     KV kA[8], vA[8], kB[8], vB[8];
     float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
     RoundGeo gc = geo(cur);
+    // Step form: the current pair's rotated q rows live in LDS, and every
+    // round reads its operand from there (rows >= G repeat row 0), so no q
+    // registers are carried through the loop: with them, the rotation code
+    // at pair entry had changed the loop's register allocation (AGPR
+    // copies) and slowed every round.
+    const int mrow = lane & 15, kg = lane >> 4;
+    auto rotate_store_q = [&](int P) HDA_INLINE {
+        if constexpr (STEP) {
+            rope_angles<ROT>(s_cs, s_freq, P, lane);
+            rotate_q_operand<ROT>(qa, s_cs, lane);
+            if (mrow < G) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<uint4 *>(s_q + mrow * D + 32 * j + 8 * kg) =
+                        __builtin_bit_cast(uint4, qa[j]);
+            }
+            wave_lds_fence();
+        }
+    };
+    auto read_q = [&]() HDA_INLINE {
+        if constexpr (STEP) {
+            const uint16_t *qs = s_q + (mrow < G ? mrow : 0) * D + 8 * kg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(qs + 32 * j));
+        }
+    };
     if constexpr (STEP) {
         // q before the first round's rows: its rotation waits for q alone
         load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
         issue(gc, lane, kA, vA, ksA, vsA);
-        rope_angles<ROT>(s_cs, s_freq, uniform(ss.pos[cur.b]), lane);
-        rotate_q_operand<ROT>(qa, s_cs, lane);
+        rotate_store_q(uniform(ss.pos[cur.b]));
     } else {
         issue(gc, lane, kA, vA, ksA, vsA);
         load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
     }
     st.reset();
-    // Step form, entering a pair: its q rows are loaded and its angles put
-    // in LDS at once, but the rotation waits until the next round's loads
-    // are issued (q is then older than every load in flight but those of
-    // the round about to be scored, so the pipeline keeps its depth).
-    bool rot_pending = false;
+    // Entering a pair (step form: rotated at once; the wait for its q rows
+    // also waits for the next round's loads, once per pair per wave)
     auto enter_pair = [&](const RoundAddr &a) HDA_INLINE {
         load_q_operand<G>(p.q, p.num_q_heads, a.b, a.kvh, lane, qa);
-        if constexpr (STEP) {
-            rope_angles<ROT>(s_cs, s_freq, uniform(ss.pos[a.b]), lane);
-            rot_pending = true;
-        }
-    };
-    auto rotate_pending = [&]() HDA_INLINE {
-        if constexpr (STEP) {
-            if (rot_pending) rotate_q_operand<ROT>(qa, s_cs, lane);
-            rot_pending = false;
-        }
+        if constexpr (STEP) rotate_store_q(uniform(ss.pos[a.b]));
     };
 
     // Every half-iteration issues the next round's loads, then computes the
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
         RoundAddr nxt = more ? advance(cur) : cur;
         RoundGeo gn = geo(nxt);
         issue(gn, more ? lane : 0, kB, vB, ksB, vsB);
-        rotate_pending();
+        read_q();
         st.template round<false, F8, KV, false, !F8>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
                                      nullptr, nullptr, ksA, vsA);
         if (!more || !same_pair(nxt, cur)) {
@@ -412,7 +426,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
         nxt = more ? advance(cur) : cur;
         gn = geo(nxt);
         issue(gn, more ? lane : 0, kA, vA, ksA, vsA);
-        rotate_pending();
+        read_q();
         st.template round<false, F8, KV, false, !F8>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
                                      nullptr, nullptr, ksB, vsB);
         if (!more || !same_pair(nxt, cur)) {
@@ -469,9 +483,34 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
     const int w_lo = rb > 0 ? wave_of_round(g_lo, r_tot, We) : 0;
     const int nseg = rb > 0 ? wave_of_round(g_lo + rb - 1, r_tot, We) - w_lo + 1 : 0;
     const int64_t s0 = w_lo + (int64_t)b * Hkv + kvh;  // first slot
-    // The first batch of partials and their lse go out first; the lse
-    // maximum and (step form) the new token's chain run while they are in
-    // flight.
+    // The new token's rows (step form), then the first batch of partials
+    // and their lse go out first; the lse maximum and the new token's
+    // rotation and score run while they are in flight.
+    uint2 qw = make_uint2(0, 0), kw = qw, vw = qw, qp = qw, kp = qw;
+    float fr[4] = {0.f, 0.f, 0.f, 0.f};
+    const int d0 = 4 * lane;
+    int rot = 0, half = 0, i0 = 0, pd = 0;
+    bool first = false;
+    const int64_t kvrow = ((int64_t)b * Hkv + kvh) * D;
+    if constexpr (STEP) {
+        if (fresh) {
+            rot = ss.rotary_dim;
+            half = rot >> 1;
+            first = d0 < half;  // x1 (first half) or x2
+            pd = first ? d0 + half : d0 - half;
+            i0 = first ? d0 : d0 - half;
+            const uint16_t *qr = p.q + row * D, *kr = ss.k_new + kvrow;
+            qw = *reinterpret_cast<const uint2 *>(qr + d0);
+            kw = *reinterpret_cast<const uint2 *>(kr + d0);
+            vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
+            if (d0 < rot) {
+                qp = *reinterpret_cast<const uint2 *>(qr + pd);
+                kp = *reinterpret_cast<const uint2 *>(kr + pd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fr[e] = ss.inv_freq[i0 + e];
+            }
+        }
+    }
     float4 v[kBatch];
     float wgt[kBatch];
     auto load_batch = [&](int base) HDA_INLINE {
@@ -490,12 +529,6 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
     float vn[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (STEP) {
         if (fresh) {
-            const int d0 = 4 * lane, rot = ss.rotary_dim, half = rot >> 1;
-            const int64_t kvrow = ((int64_t)b * Hkv + kvh) * D;
-            const uint16_t *qr = p.q + row * D, *kr = ss.k_new + kvrow;
-            const uint2 qw = *reinterpret_cast<const uint2 *>(qr + d0);
-            const uint2 kw = *reinterpret_cast<const uint2 *>(kr + d0);
-            const uint2 vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
             float qx[4] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y)};
             float kx[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
             vn[0] = bf16_lo(vw.x);
@@ -504,17 +537,13 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
             vn[3] = bf16_hi(vw.y);
             uint2 krot = kw;
             if (d0 < rot) {
-                const bool first = d0 < half;  // x1 (first half) or x2
-                const int pd = first ? d0 + half : d0 - half, i0 = first ? d0 : d0 - half;
-                const uint2 qp = *reinterpret_cast<const uint2 *>(qr + pd);
-                const uint2 kp = *reinterpret_cast<const uint2 *>(kr + pd);
                 const float qy[4] = {bf16_lo(qp.x), bf16_hi(qp.x), bf16_lo(qp.y), bf16_hi(qp.y)};
                 const float ky[4] = {bf16_lo(kp.x), bf16_hi(kp.x), bf16_lo(kp.y), bf16_hi(kp.y)};
                 uint16_t kb[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float c, sn;
-                    sincos_angle((float)P * ss.inv_freq[i0 + e], &c, &sn);
+                    sincos_angle((float)P * fr[e], &c, &sn);
                     // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
                     const uint16_t qb = f32_to_bf16(first ? fmaf(qx[e], c, -qy[e] * sn) : fmaf(qx[e], c, qy[e] * sn));
                     kb[e] = f32_to_bf16(first ? fmaf(kx[e], c, -ky[e] * sn) : fmaf(kx[e], c, ky[e] * sn));
