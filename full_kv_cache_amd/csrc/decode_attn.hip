@@ -362,15 +362,71 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
     // at pair entry had changed the loop's register allocation (AGPR
     // copies) and slowed every round.
     const int mrow = lane & 15, kg = lane >> 4;
-    auto rotate_store_q = [&](int P) HDA_INLINE {
+    // Entering a pair, the step form loads the new K and V rows with the q
+    // rows (every lane, in the q operand's layout, whether or not it owns
+    // the token: no value is then carried through the loop), rotates q and
+    // K with the pair's angles and keeps the rotated q rows in LDS.  The
+    // wave holding the pair's first round owns the new token: it scores it
+    // against the G rotated rows (into the workspace, for the merge) and
+    // writes the rotated K and the V row to row pos.  Other waves may read
+    // row pos meanwhile only as a masked key.
+    bf16x8 kn[8];
+    uint4 vn8[8];
+    auto load_pair = [&](const RoundAddr &a) HDA_INLINE {
+        load_q_operand<G>(p.q, p.num_q_heads, a.b, a.kvh, lane, qa);
         if constexpr (STEP) {
+            const int64_t nrow = ((int64_t)a.b * Hkv + a.kvh) * D + 8 * kg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                kn[j] = as_bf16x8(ld16(ss.k_new + nrow + 32 * j));
+                vn8[j] = ld16(ss.v_new + nrow + 32 * j);
+            }
+        }
+    };
+    auto finish_pair = [&](const RoundAddr &a) HDA_INLINE {
+        if constexpr (STEP) {
+            const int P = uniform(ss.pos[a.b]);
             rope_angles<ROT>(s_cs, s_freq, P, lane);
             rotate_q_operand<ROT>(qa, s_cs, lane);
+            rotate_q_operand<ROT>(kn, s_cs, lane);
             if (mrow < G) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     *reinterpret_cast<uint4 *>(s_q + mrow * D + 32 * j + 8 * kg) =
                         __builtin_bit_cast(uint4, qa[j]);
+            }
+            // the pair has held rows, so P >= 1; P >= capacity: no new key
+            if (a.rr == 0 && (int64_t)P < p.capacity) {
+                float d = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint4 qu = __builtin_bit_cast(uint4, qa[j]), ku = __builtin_bit_cast(uint4, kn[j]);
+                    const uint32_t qw4[4] = {qu.x, qu.y, qu.z, qu.w}, kw4[4] = {ku.x, ku.y, ku.z, ku.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        d = fmaf(bf16_lo(qw4[e]), bf16_lo(kw4[e]), d);
+                        d = fmaf(bf16_hi(qw4[e]), bf16_hi(kw4[e]), d);
+                    }
+                }
+                d += __shfl_xor(d, 16, 64);
+                d += __shfl_xor(d, 32, 64);
+                const int64_t pr = (int64_t)a.b * Hkv + a.kvh;
+                if (kg == 0 && mrow < G) ss.s_new[pr * G + mrow] = d * (p.scale_log2 * kLn2);
+                if (mrow == 0) {
+                    int64_t base;
+                    if (p.pages.block_table) {
+                        const int ps = p.pages.page_size;
+                        base = (page_of(p.pages, a.b, P) * Hkv + a.kvh) * ps + P % ps;
+                    } else {
+                        base = pr * p.capacity + P;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        *reinterpret_cast<uint4 *>(ss.k + base * D + 32 * j + 8 * kg) =
+                            __builtin_bit_cast(uint4, kn[j]);
+                        *reinterpret_cast<uint4 *>(ss.v + base * D + 32 * j + 8 * kg) = vn8[j];
+                    }
+                }
             }
             wave_lds_fence();
         }
@@ -383,20 +439,21 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
         }
     };
     if constexpr (STEP) {
-        // q before the first round's rows: its rotation waits for q alone
-        load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
+        // the pair's rows before the first round's: rotating them waits for
+        // them alone
+        load_pair(cur);
         issue(gc, lane, kA, vA, ksA, vsA);
-        rotate_store_q(uniform(ss.pos[cur.b]));
+        finish_pair(cur);
     } else {
         issue(gc, lane, kA, vA, ksA, vsA);
         load_q_operand<G>(p.q, p.num_q_heads, cur.b, cur.kvh, lane, qa);
     }
     st.reset();
-    // Entering a pair (step form: rotated at once; the wait for its q rows
+    // Entering a pair (step form: rotated at once; the wait for its rows
     // also waits for the next round's loads, once per pair per wave)
     auto enter_pair = [&](const RoundAddr &a) HDA_INLINE {
-        load_q_operand<G>(p.q, p.num_q_heads, a.b, a.kvh, lane, qa);
-        if constexpr (STEP) rotate_store_q(uniform(ss.pos[a.b]));
+        load_pair(a);
+        finish_pair(a);
     };
 
     // Every half-iteration issues the next round's loads, then computes the
@@ -449,12 +506,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
 // unrolled batches so that their loads are in flight together.
 //
 // STEP (hda_decode_step, full layer): the new token is one more key, row
-// pos of its block when pos < capacity.  Each wave rotates its head's q
-// and the new K at pos (4 dims per lane; the partner dim i +- rot/2 read
-// from memory, the same fp32 fma and bf16 rounding as the append kernel),
-// scores them, and takes (score, v_new) as one more partial; the wave of
-// the group's first head appends the rotated K and V to row pos (nothing
-// in this launch reads the cache).
+// pos of its block when pos < capacity, taken as one more partial (its
+// score, v_new).  The streaming kernel scored and appended it for every
+// pair with held rows; for a pair without (pos 0) each wave rotates its
+// head's q and the new K here (4 dims per lane; the partner dim i +- rot/2
+// read from memory, the same fp32 fma and bf16 rounding as the append
+// kernel) and scores them, and the wave of the group's first head appends
+// the rotated K and V to row pos (nothing in this launch reads the cache).
 template <bool STEP>
 __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W, StepArg<STEP> ss) {
     constexpr int D = kHeadDim;
@@ -484,16 +542,22 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
     const int nseg = rb > 0 ? wave_of_round(g_lo + rb - 1, r_tot, We) - w_lo + 1 : 0;
     const int64_t s0 = w_lo + (int64_t)b * Hkv + kvh;  // first slot
     // The new token's rows (step form), then the first batch of partials
-    // and their lse go out first; the lse maximum and the new token's
-    // rotation and score run while they are in flight.
+    // and their lse go out first; the lse maximum (and for a pair with no
+    // held rows the new token's rotation and score) run while they are in
+    // flight.  A pair with held rows had its new key scored and appended by
+    // the streaming wave that holds its first round.
+    const bool self_score = fresh && rb == 0;
     uint2 qw = make_uint2(0, 0), kw = qw, vw = qw, qp = qw, kp = qw;
     float fr[4] = {0.f, 0.f, 0.f, 0.f};
+    float s_ws = -INFINITY;
     const int d0 = 4 * lane;
     int rot = 0, half = 0, i0 = 0, pd = 0;
     bool first = false;
     const int64_t kvrow = ((int64_t)b * Hkv + kvh) * D;
     if constexpr (STEP) {
-        if (fresh) {
+        if (fresh) vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
+        if (fresh && !self_score) s_ws = ss.s_new[row];
+        if (self_score) {
             rot = ss.rotary_dim;
             half = rot >> 1;
             first = d0 < half;  // x1 (first half) or x2
@@ -502,7 +566,6 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
             const uint16_t *qr = p.q + row * D, *kr = ss.k_new + kvrow;
             qw = *reinterpret_cast<const uint2 *>(qr + d0);
             kw = *reinterpret_cast<const uint2 *>(kr + d0);
-            vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
             if (d0 < rot) {
                 qp = *reinterpret_cast<const uint2 *>(qr + pd);
                 kp = *reinterpret_cast<const uint2 *>(kr + pd);
@@ -525,16 +588,12 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
     float M = -INFINITY;
     for (int c = 0; c < nseg; c += 64)
         if (c + lane < nseg) M = fmaxf(M, p.part_lse[(s0 + c + lane) * G + h]);
-    float s_new = -INFINITY;
-    float vn[4] = {0.f, 0.f, 0.f, 0.f};
+    float s_new = s_ws;
+    const float vn[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
     if constexpr (STEP) {
-        if (fresh) {
+        if (self_score) {
             float qx[4] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y)};
             float kx[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
-            vn[0] = bf16_lo(vw.x);
-            vn[1] = bf16_hi(vw.x);
-            vn[2] = bf16_lo(vw.y);
-            vn[3] = bf16_hi(vw.y);
             uint2 krot = kw;
             if (d0 < rot) {
                 const float qy[4] = {bf16_lo(qp.x), bf16_hi(qp.x), bf16_lo(qp.y), bf16_hi(qp.y)};

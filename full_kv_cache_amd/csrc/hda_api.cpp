@@ -305,8 +305,13 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
 // MI355X faster than the one-launch form (whose merge across waves and
 // in-loop append need about 330 registers) and than hda_rope_append +
 // hda_decode_attn (one launch fewer).  Its workspace is the streaming
-// path's, sized for a full block of keys.
+// path's, sized for a full block of keys, then the new keys' scores
+// [batch, num_q_heads].
 int stream_step_waves(const hda_cache_desc *c) { return stream_waves(c, c->capacity); }
+size_t stream_step_bytes(const hda_cache_desc *c) {
+    return stream_layout(c, stream_step_waves(c)).bytes +
+           up256((size_t)c->batch * c->num_q_heads * sizeof(float));
+}
 
 // ---------------------------------------------------------------- sparse
 // Key splits for the sparse decode: one workgroup per (token, split, group
@@ -628,7 +633,7 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
 size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer) {
     if (check_step_shape(cache, layer) != HDA_OK) return 0;
     if (use_window_step(cache, layer)) return counter_header(cache);
-    if (layer == HDA_FULL) return stream_layout(cache, stream_step_waves(cache)).bytes;
+    if (layer == HDA_FULL) return stream_step_bytes(cache);
     return step_layout(cache, step_waves(cache, layer)).bytes;
 }
 
@@ -649,8 +654,9 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
     if (layer == HDA_FULL) {
         const int waves = stream_step_waves(cache);
         const StreamLayout L = stream_layout(cache, waves);
-        if (!workspace || workspace_bytes < L.bytes)
-            return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", L.bytes,
+        const size_t need = stream_step_bytes(cache);
+        if (!workspace || workspace_bytes < need)
+            return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", need,
                         workspace_bytes, workspace);
         if (!aligned16(workspace))
             return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
@@ -671,6 +677,7 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
         ss.v_new = static_cast<const uint16_t *>(v_new);
         ss.k = static_cast<uint16_t *>(cache->k);
         ss.v = static_cast<uint16_t *>(cache->v);
+        ss.s_new = reinterpret_cast<float *>(ws + L.bytes);
         ss.rotary_dim = cache->rotary_dim;
         fill_inv_freq(ss.inv_freq, cache->rope_theta, cache->rotary_dim);
         const int g = cache->num_q_heads / cache->num_kv_heads;

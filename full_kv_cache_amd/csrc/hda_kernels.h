@@ -93,12 +93,14 @@ struct StepParams {
 // Step form of the streaming decode (hda_decode_step on a full layer): the
 // keys of sequence b are the rows its block held before this token,
 // min(pos, capacity) (none for pos < 0); the streaming kernel rotates q in
-// registers; the merge adds the new token's key (row pos when pos <
-// capacity) and appends it.
+// registers, and the wave holding a pair's first round scores the new key
+// (row pos when pos < capacity) and appends it; the merge folds that score
+// in (and does both itself for a pair with no held rows).
 struct StreamStep {
     const int32_t *pos;              // [B]
     const uint16_t *k_new, *v_new;   // [B, Hkv, D]
     uint16_t *k, *v;                 // the cache (or page pools), written at row pos
+    float *s_new;                    // [B, Hq] the new key's score (natural log units)
     int rotary_dim;                  // 64 or 256
     float inv_freq[kHeadDim / 2];    // fp32 theta^(-2i/rot), i < rot/2
 };

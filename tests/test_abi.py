@@ -229,7 +229,7 @@ def test_step_workspace():
     """Counter header first (shared with hda_decode_attn's layouts); the
     window form (sliding layers) needs only that header, the streaming form
     (full layers) adds one partial slot per wave and per (sequence, KV
-    head)."""
+    head), and one new-key score per (sequence, query head)."""
     L = hda.lib()
     d = _desc()
     need = L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.SLIDING)
@@ -311,8 +311,9 @@ def test_paged_routing():
                                    ctypes.c_void_p(FAKE), None)
     assert r == 2 and "contiguous" in _msg()
     assert _step(d, layer=hda.FULL) == 3 and "workspace" in _msg()
+    # the streaming path's workspace, then one score per (sequence, query head)
     assert L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.FULL) == \
-        L.hda_decode_workspace_bytes(ctypes.byref(d), hda.FULL, 1024, 0) > 0
+        L.hda_decode_workspace_bytes(ctypes.byref(d), hda.FULL, 1024, 0) + 256 > 256
     assert _decode(_desc(**{**_PAGED, "batch": 0}), layer=hda.FULL, max_seq_len=16) == 0
 
 
