@@ -229,7 +229,6 @@ __device__ __forceinline__ int held_keys(const StreamStep &ss, int64_t capacity,
 template <int G, bool F8, int ROT = 0>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepArg<(ROT > 0)> ss) {
     constexpr bool STEP = ROT > 0;
-    static_assert(!(STEP && F8), "the step form is built for bf16 caches");
     constexpr int D = kHeadDim;
     extern __shared__ int s_pre[];                 // [B + 1] rounds before sequence b, one KV head
     __shared__ __align__(16) float s_pw[16 * G];   // this round's probabilities [key][head]
@@ -305,7 +304,140 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
         store_partial<G>(st, p.part_o + slot * G * D, p.part_lse + slot * G, lane);
     };
 
-    if constexpr (F8) {
+    // Step form: the current pair's rotated q rows live in LDS, and every
+    // round reads its operand from there (rows >= G repeat row 0), so no q
+    // registers are carried through the loop: with them, the rotation code
+    // at pair entry had changed the loop's register allocation (AGPR
+    // copies) and slowed every round.
+    const int mrow = lane & 15, kg = lane >> 4;
+    // Entering a pair, the step form loads the new K and V rows with the q
+    // rows (every lane, in the q operand's layout, whether or not it owns
+    // the token: no value is then carried through the loop), rotates q and
+    // K with the pair's angles and keeps the rotated q rows in LDS.  The
+    // wave holding the pair's first round owns the new token: it scores it
+    // against the G rotated rows (into the workspace, for the merge) and
+    // writes the rotated K and the V row to row pos.  Other waves may read
+    // row pos meanwhile only as a masked key.
+    bf16x8 kn[8];
+    uint4 vn8[8];
+    auto load_pair = [&](const RoundAddr &a) HDA_INLINE {
+        load_q_operand<G>(p.q, p.num_q_heads, a.b, a.kvh, lane, qa);
+        if constexpr (STEP) {
+            const int64_t nrow = ((int64_t)a.b * Hkv + a.kvh) * D + 8 * kg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                kn[j] = as_bf16x8(ld16(ss.k_new + nrow + 32 * j));
+                vn8[j] = ld16(ss.v_new + nrow + 32 * j);
+            }
+        }
+    };
+    auto finish_pair = [&](const RoundAddr &a) HDA_INLINE {
+        if constexpr (STEP) {
+            const int P = uniform(ss.pos[a.b]);
+            rope_angles<ROT>(s_cs, s_freq, P, lane);
+            rotate_q_operand<ROT>(qa, s_cs, lane);
+            rotate_q_operand<ROT>(kn, s_cs, lane);
+            if (mrow < G) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<uint4 *>(s_q + mrow * D + 32 * j + 8 * kg) =
+                        __builtin_bit_cast(uint4, qa[j]);
+            }
+            // the pair has held rows, so P >= 1; P >= capacity: no new key
+            if (a.rr == 0 && (int64_t)P < p.capacity) {
+                const int64_t pr = (int64_t)a.b * Hkv + a.kvh;
+                int64_t base;  // cache row index of row P
+                if (p.pages.block_table) {
+                    const int ps = p.pages.page_size;
+                    base = (page_of(p.pages, a.b, P) * Hkv + a.kvh) * ps + P % ps;
+                } else {
+                    base = pr * p.capacity + P;
+                }
+                if constexpr (!F8) {
+                    // score against the G rotated rows from registers (a
+                    // lane's 64 dims of its row, then the 4 lane groups),
+                    // the rows written as they are
+                    float d = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint4 qu = __builtin_bit_cast(uint4, qa[j]), ku = __builtin_bit_cast(uint4, kn[j]);
+                        const uint32_t qw4[4] = {qu.x, qu.y, qu.z, qu.w}, kw4[4] = {ku.x, ku.y, ku.z, ku.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            d = fmaf(bf16_lo(qw4[e]), bf16_lo(kw4[e]), d);
+                            d = fmaf(bf16_hi(qw4[e]), bf16_hi(kw4[e]), d);
+                        }
+                    }
+                    d += __shfl_xor(d, 16, 64);
+                    d += __shfl_xor(d, 32, 64);
+                    if (kg == 0 && mrow < G) ss.s_new[pr * G + mrow] = d * (p.scale_log2 * kLn2);
+                    if (mrow == 0) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            *reinterpret_cast<uint4 *>(ss.k + base * D + 32 * j + 8 * kg) =
+                                __builtin_bit_cast(uint4, kn[j]);
+                            *reinterpret_cast<uint4 *>(ss.v + base * D + 32 * j + 8 * kg) = vn8[j];
+                        }
+                    }
+                } else {
+                    // The rotated K and the V row through LDS (the K tile is
+                    // free between rounds), then 4 dims a lane as the append
+                    // kernels lay a row out: fp8 rows are quantized as there
+                    // (per-row amax / 448, codes e4m3(x / scale)), and the score
+                    // reads the key as stored, times its scale, as a round does.
+                    uint16_t *s_row = s_kt;  // [K row | V row]
+                    if (mrow == 0) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            *reinterpret_cast<uint4 *>(s_row + 32 * j + 8 * kg) = __builtin_bit_cast(uint4, kn[j]);
+                            *reinterpret_cast<uint4 *>(s_row + D + 32 * j + 8 * kg) = vn8[j];
+                        }
+                    }
+                    wave_lds_fence();
+                    const uint2 k4 = *reinterpret_cast<const uint2 *>(s_row + 4 * lane);
+                    const uint2 v4 = *reinterpret_cast<const uint2 *>(s_row + D + 4 * lane);
+                    float kx[4] = {bf16_lo(k4.x), bf16_hi(k4.x), bf16_lo(k4.y), bf16_hi(k4.y)};
+                    float kscale;
+                    {
+                        const float vx[4] = {bf16_lo(v4.x), bf16_hi(v4.x), bf16_lo(v4.y), bf16_hi(v4.y)};
+                        float vscale;
+                        const uint32_t kc = quantize_row4(kx, kscale), vc = quantize_row4(vx, vscale);
+                        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(ss.k) + base * D + 4 * lane) = kc;
+                        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(ss.v) + base * D + 4 * lane) = vc;
+                        if (lane == 0) {
+                            ss.k_scale[base] = kscale;
+                            ss.v_scale[base] = vscale;
+                        }
+                        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)kc, false);
+                        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)kc, true);
+                        kx[0] = lo.x;
+                        kx[1] = lo.y;
+                        kx[2] = hi.x;
+                        kx[3] = hi.y;
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const uint2 q4 = *reinterpret_cast<const uint2 *>(s_q + h * D + 4 * lane);
+                        float d = bf16_lo(q4.x) * kx[0];
+                        d = fmaf(bf16_hi(q4.x), kx[1], d);
+                        d = fmaf(bf16_lo(q4.y), kx[2], d);
+                        d = fmaf(bf16_hi(q4.y), kx[3], d);
+                        d = wave_sum(d);
+                        if (lane == 0) ss.s_new[pr * G + h] = d * kscale * (p.scale_log2 * kLn2);
+                    }
+                }
+            }
+            wave_lds_fence();
+        }
+    };
+    auto read_q = [&]() HDA_INLINE {
+        if constexpr (STEP) {
+            const uint16_t *qs = s_q + (mrow < G ? mrow : 0) * D + 8 * kg;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(qs + 32 * j));
+        }
+    };
+    if constexpr (F8 && !STEP) {
         // Rounds pipelined NB deep.  Buffer i % NB holds round g0 + i; the
         // loop body is unrolled NB times so that every buffer index is a
         // constant.  Rounds past g1 are placeholders (lane 0 addresses,
@@ -356,88 +488,6 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
     KV kA[8], vA[8], kB[8], vB[8];
     float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
     RoundGeo gc = geo(cur);
-    // Step form: the current pair's rotated q rows live in LDS, and every
-    // round reads its operand from there (rows >= G repeat row 0), so no q
-    // registers are carried through the loop: with them, the rotation code
-    // at pair entry had changed the loop's register allocation (AGPR
-    // copies) and slowed every round.
-    const int mrow = lane & 15, kg = lane >> 4;
-    // Entering a pair, the step form loads the new K and V rows with the q
-    // rows (every lane, in the q operand's layout, whether or not it owns
-    // the token: no value is then carried through the loop), rotates q and
-    // K with the pair's angles and keeps the rotated q rows in LDS.  The
-    // wave holding the pair's first round owns the new token: it scores it
-    // against the G rotated rows (into the workspace, for the merge) and
-    // writes the rotated K and the V row to row pos.  Other waves may read
-    // row pos meanwhile only as a masked key.
-    bf16x8 kn[8];
-    uint4 vn8[8];
-    auto load_pair = [&](const RoundAddr &a) HDA_INLINE {
-        load_q_operand<G>(p.q, p.num_q_heads, a.b, a.kvh, lane, qa);
-        if constexpr (STEP) {
-            const int64_t nrow = ((int64_t)a.b * Hkv + a.kvh) * D + 8 * kg;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                kn[j] = as_bf16x8(ld16(ss.k_new + nrow + 32 * j));
-                vn8[j] = ld16(ss.v_new + nrow + 32 * j);
-            }
-        }
-    };
-    auto finish_pair = [&](const RoundAddr &a) HDA_INLINE {
-        if constexpr (STEP) {
-            const int P = uniform(ss.pos[a.b]);
-            rope_angles<ROT>(s_cs, s_freq, P, lane);
-            rotate_q_operand<ROT>(qa, s_cs, lane);
-            rotate_q_operand<ROT>(kn, s_cs, lane);
-            if (mrow < G) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<uint4 *>(s_q + mrow * D + 32 * j + 8 * kg) =
-                        __builtin_bit_cast(uint4, qa[j]);
-            }
-            // the pair has held rows, so P >= 1; P >= capacity: no new key
-            if (a.rr == 0 && (int64_t)P < p.capacity) {
-                float d = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint4 qu = __builtin_bit_cast(uint4, qa[j]), ku = __builtin_bit_cast(uint4, kn[j]);
-                    const uint32_t qw4[4] = {qu.x, qu.y, qu.z, qu.w}, kw4[4] = {ku.x, ku.y, ku.z, ku.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        d = fmaf(bf16_lo(qw4[e]), bf16_lo(kw4[e]), d);
-                        d = fmaf(bf16_hi(qw4[e]), bf16_hi(kw4[e]), d);
-                    }
-                }
-                d += __shfl_xor(d, 16, 64);
-                d += __shfl_xor(d, 32, 64);
-                const int64_t pr = (int64_t)a.b * Hkv + a.kvh;
-                if (kg == 0 && mrow < G) ss.s_new[pr * G + mrow] = d * (p.scale_log2 * kLn2);
-                if (mrow == 0) {
-                    int64_t base;
-                    if (p.pages.block_table) {
-                        const int ps = p.pages.page_size;
-                        base = (page_of(p.pages, a.b, P) * Hkv + a.kvh) * ps + P % ps;
-                    } else {
-                        base = pr * p.capacity + P;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        *reinterpret_cast<uint4 *>(ss.k + base * D + 32 * j + 8 * kg) =
-                            __builtin_bit_cast(uint4, kn[j]);
-                        *reinterpret_cast<uint4 *>(ss.v + base * D + 32 * j + 8 * kg) = vn8[j];
-                    }
-                }
-            }
-            wave_lds_fence();
-        }
-    };
-    auto read_q = [&]() HDA_INLINE {
-        if constexpr (STEP) {
-            const uint16_t *qs = s_q + (mrow < G ? mrow : 0) * D + 8 * kg;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(qs + 32 * j));
-        }
-    };
     if constexpr (STEP) {
         // the pair's rows before the first round's: rotating them waits for
         // them alone
@@ -467,8 +517,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
         RoundGeo gn = geo(nxt);
         issue(gn, more ? lane : 0, kB, vB, ksB, vsB);
         read_q();
-        st.template round<false, F8, KV, false, !F8>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
-                                     nullptr, nullptr, ksA, vsA);
+        st.template round<false, F8, KV, false, true>(qa, kA, vA, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
+                                      nullptr, nullptr, ksA, vsA);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
@@ -484,8 +534,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
         gn = geo(nxt);
         issue(gn, more ? lane : 0, kA, vA, ksA, vsA);
         read_q();
-        st.template round<false, F8, KV, false, !F8>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
-                                     nullptr, nullptr, ksB, vsB);
+        st.template round<false, F8, KV, false, true>(qa, kB, vB, gc.lo, gc.hi, p.scale_log2, s_pw, s_kt, lane, -1,
+                                      nullptr, nullptr, ksB, vsB);
         if (!more || !same_pair(nxt, cur)) {
             end_segment(cur);
             if (!more) break;
@@ -554,9 +604,27 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
     int rot = 0, half = 0, i0 = 0, pd = 0;
     bool first = false;
     const int64_t kvrow = ((int64_t)b * Hkv + kvh) * D;
+    const bool f8 = p.kq != nullptr;  // fp8 cache: the new key and value as stored (codes x scale)
+    int64_t nbase = 0;                // cache row index of row P
+    uint32_t vcode = 0;
+    float vsc = 1.f;
     if constexpr (STEP) {
-        if (fresh) vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
-        if (fresh && !self_score) s_ws = ss.s_new[row];
+        if (fresh && (self_score || f8)) {
+            if (p.pages.block_table) {
+                const int ps = p.pages.page_size;
+                nbase = (page_of(p.pages, b, P) * Hkv + kvh) * ps + P % ps;
+            } else {
+                nbase = ((int64_t)b * Hkv + kvh) * p.capacity + P;
+            }
+        }
+        if (fresh && (self_score || !f8)) vw = *reinterpret_cast<const uint2 *>(ss.v_new + kvrow + d0);
+        if (fresh && !self_score) {
+            s_ws = ss.s_new[row];
+            if (f8) {  // written by the streaming kernel
+                vcode = *reinterpret_cast<const uint32_t *>(p.vq + nbase * D + d0);
+                vsc = p.vs[nbase];
+            }
+        }
         if (self_score) {
             rot = ss.rotary_dim;
             half = rot >> 1;
@@ -589,8 +657,18 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
     for (int c = 0; c < nseg; c += 64)
         if (c + lane < nseg) M = fmaxf(M, p.part_lse[(s0 + c + lane) * G + h]);
     float s_new = s_ws;
-    const float vn[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
+    float vn[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
+    // an fp8 row's 4 codes of this lane, decoded and scaled
+    auto decode4 = [](uint32_t c, float sc, float *x) HDA_INLINE {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+        x[0] = lo.x * sc;
+        x[1] = lo.y * sc;
+        x[2] = hi.x * sc;
+        x[3] = hi.y * sc;
+    };
     if constexpr (STEP) {
+        if (fresh && !self_score && f8) decode4(vcode, vsc, vn);
         if (self_score) {
             float qx[4] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y)};
             float kx[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
@@ -612,20 +690,31 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(DecodeParams p, int W,
                 krot = make_uint2((uint32_t)kb[0] | ((uint32_t)kb[1] << 16),
                                   (uint32_t)kb[2] | ((uint32_t)kb[3] << 16));
             }
+            float ksc = 1.f;
+            uint32_t kc = 0, vc = 0;
+            float vs_new = 0.f;
+            if (f8) {  // quantized as the fp8 append kernel does; scores and P.V read the codes
+                kc = quantize_row4(kx, ksc);
+                vc = quantize_row4(vn, vs_new);
+                decode4(kc, 1.f, kx);
+                decode4(vc, vs_new, vn);
+            }
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dot = fmaf(qx[e], kx[e], dot);
-            s_new = wave_sum(dot) * (p.scale_log2 * kLn2);  // natural-log units, as the partials
+            s_new = wave_sum(dot) * ksc * (p.scale_log2 * kLn2);  // natural-log units, as the partials
             if (h == 0) {
-                int64_t base;
-                if (p.pages.block_table) {
-                    const int ps = p.pages.page_size;
-                    base = (page_of(p.pages, b, P) * Hkv + kvh) * ps + P % ps;
+                if (f8) {
+                    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(ss.k) + nbase * D + d0) = kc;
+                    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(ss.v) + nbase * D + d0) = vc;
+                    if (lane == 0) {
+                        ss.k_scale[nbase] = ksc;
+                        ss.v_scale[nbase] = vs_new;
+                    }
                 } else {
-                    base = ((int64_t)b * Hkv + kvh) * p.capacity + P;
+                    *reinterpret_cast<uint2 *>(ss.k + nbase * D + d0) = krot;
+                    *reinterpret_cast<uint2 *>(ss.v + nbase * D + d0) = vw;
                 }
-                *reinterpret_cast<uint2 *>(ss.k + base * D + d0) = krot;
-                *reinterpret_cast<uint2 *>(ss.v + base * D + d0) = vw;
             }
         }
     }
@@ -851,16 +940,23 @@ hipError_t launch_stream_g(const DecodeParams &p, int waves, hipStream_t s) {
     return launch_stream_merge(p, waves, s);
 }
 
-template <int G>
-hipError_t launch_stream_step_g(const DecodeParams &p, const StreamStep &ss, int waves, hipStream_t s) {
+template <int G, bool F8>
+void launch_stream_step_kernel(const DecodeParams &p, const StreamStep &ss, int waves, hipStream_t s) {
     if (ss.rotary_dim == 64)
-        hipLaunchKernelGGL((decode_stream_kernel<G, false, 64>), dim3(waves), dim3(64),
-                           (p.batch + 1) * sizeof(int), s, p, ss);
-    else if (ss.rotary_dim == 256)
-        hipLaunchKernelGGL((decode_stream_kernel<G, false, 256>), dim3(waves), dim3(64),
+        hipLaunchKernelGGL((decode_stream_kernel<G, F8, 64>), dim3(waves), dim3(64),
                            (p.batch + 1) * sizeof(int), s, p, ss);
     else
-        return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_stream_kernel<G, F8, 256>), dim3(waves), dim3(64),
+                           (p.batch + 1) * sizeof(int), s, p, ss);
+}
+
+template <int G>
+hipError_t launch_stream_step_g(const DecodeParams &p, const StreamStep &ss, int waves, hipStream_t s) {
+    if (ss.rotary_dim != 64 && ss.rotary_dim != 256) return hipErrorInvalidValue;
+    if (p.kq)
+        launch_stream_step_kernel<G, true>(p, ss, waves, s);
+    else
+        launch_stream_step_kernel<G, false>(p, ss, waves, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(stream_merge_kernel<true>, dim3((unsigned)((int64_t)p.num_q_heads * p.batch)),

@@ -293,9 +293,9 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
                     hda::kStreamMaxBatch, c->batch);
     if (c->block_table && layer != HDA_FULL)
         return fail(HDA_ERR_UNSUPPORTED, "the step on a paged cache is built for full layers");
-    if (c->kv_dtype != HDA_KV_BF16 && !(layer == HDA_SLIDING && c->window <= hda::kPairMaxKeys))
-        return fail(HDA_ERR_UNSUPPORTED, "the step on an fp8 cache is built for sliding windows "
-                    "of at most %d keys (bf16 otherwise)", hda::kPairMaxKeys);
+    if (c->kv_dtype != HDA_KV_BF16 && layer == HDA_SLIDING && c->window > hda::kPairMaxKeys)
+        return fail(HDA_ERR_UNSUPPORTED, "the step on an fp8 cache is built for full layers and "
+                    "sliding windows of at most %d keys (bf16 otherwise)", hda::kPairMaxKeys);
     return HDA_OK;
 }
 
@@ -307,7 +307,12 @@ hda_status check_step_shape(const hda_cache_desc *c, int layer) {
 // hda_decode_attn (one launch fewer).  Its workspace is the streaming
 // path's, sized for a full block of keys, then the new keys' scores
 // [batch, num_q_heads].
-int stream_step_waves(const hda_cache_desc *c) { return stream_waves(c, c->capacity); }
+// (An fp8 cache as well takes half the resident slots here: the step form
+// of its streaming kernel needs more than 256 registers, one wave per SIMD.)
+int stream_step_waves(const hda_cache_desc *c) {
+    const int w = stream_waves(c, c->capacity);
+    return c->kv_dtype == HDA_KV_BF16 || w < 2 ? w : w / 2;
+}
 size_t stream_step_bytes(const hda_cache_desc *c) {
     return stream_layout(c, stream_step_waves(c)).bytes +
            up256((size_t)c->batch * c->num_q_heads * sizeof(float));
@@ -678,6 +683,10 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
         ss.k = static_cast<uint16_t *>(cache->k);
         ss.v = static_cast<uint16_t *>(cache->v);
         ss.s_new = reinterpret_cast<float *>(ws + L.bytes);
+        if (cache->kv_dtype == HDA_KV_FP8_E4M3) {
+            ss.k_scale = cache->k_scale;
+            ss.v_scale = cache->v_scale;
+        }
         ss.rotary_dim = cache->rotary_dim;
         fill_inv_freq(ss.inv_freq, cache->rope_theta, cache->rotary_dim);
         const int g = cache->num_q_heads / cache->num_kv_heads;

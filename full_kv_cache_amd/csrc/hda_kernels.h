@@ -100,6 +100,7 @@ struct StreamStep {
     const int32_t *pos;              // [B]
     const uint16_t *k_new, *v_new;   // [B, Hkv, D]
     uint16_t *k, *v;                 // the cache (or page pools), written at row pos
+    float *k_scale, *v_scale;        // fp8 cache: per-row scales (else null); codes at k, v
     float *s_new;                    // [B, Hq] the new key's score (natural log units)
     int rotary_dim;                  // 64 or 256
     float inv_freq[kHeadDim / 2];    // fp32 theta^(-2i/rot), i < rot/2

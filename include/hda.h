@@ -314,10 +314,11 @@ size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_ty
  *              header, so one workspace serves both.  Calls sharing a
  *              workspace must be ordered on one stream.
  * Errors: as hda_decode_attn, plus UNSUPPORTED for rotary_dim other than
- * 64 or 256, batch above 4096, a paged sliding cache, or an fp8 cache
- * outside the window form (sliding layers with window <= 1024; use
- * hda_rope_append + hda_decode_attn otherwise).  On an fp8 cache the new K and V rows are
- * quantized as hda_rope_append quantizes them.  batch == 0 is a no-op.
+ * 64 or 256, batch above 4096, a paged sliding cache, or an fp8 sliding
+ * cache whose window exceeds 1024 keys (use hda_rope_append +
+ * hda_decode_attn there).  On an fp8 cache the new K and V rows are
+ * quantized as hda_rope_append quantizes them, and the new key is scored
+ * as stored.  batch == 0 is a no-op.
  */
 hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
                            const int32_t *pos, hda_layer_type layer,

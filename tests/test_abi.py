@@ -345,12 +345,17 @@ def test_fp8_descriptor_checks():
 
 
 def test_fp8_routing():
-    """The fp8 cache is read by the window and streaming kernels only."""
+    """The fp8 cache is read by the window and streaming kernels only: the
+    full-layer step (streaming step form) takes it, a sliding window past
+    one workgroup's 1024 keys does not."""
     L = hda.lib()
     full = _desc(**{**_FP8, "capacity": 4096, "rotary_dim": 64, "rope_theta": 5e6})
     assert _decode(full, layer=hda.FULL, max_seq_len=4096, chunk=256) == 2 and "fp8" in _msg()
-    assert _step(full, layer=hda.FULL) == 2 and "fp8" in _msg()  # streaming form: bf16 only
-    assert L.hda_decode_step_workspace_bytes(ctypes.byref(full), hda.FULL) == 0
+    assert _step(full, layer=hda.FULL) == 3 and "workspace" in _msg()
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(full), hda.FULL) > 0
+    wide = _desc(**{**_FP8, "window": 2048, "capacity": 2048})
+    assert _step(wide) == 2 and "fp8" in _msg()
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(wide), hda.SLIDING) == 0
     # the window form takes an fp8 cache: only the counter header as workspace
     assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(**_FP8)), hda.SLIDING) == 256
     r = L.hda_decode_attn_partials(ctypes.c_void_p(FAKE), ctypes.byref(full), ctypes.c_void_p(FAKE),

@@ -251,3 +251,86 @@ def test_fp8_window_step(pos):
         assert_attn_close(out, ref)
         np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
         assert torch.count_nonzero(ws[:4 * len(pos) * 2]).item() == 0
+
+
+@pytest.mark.parametrize("pos,lmax", [([0, 17, 300, 2047], 2048), ([5, 700, 4095, 1100, 1], 4096)])
+def test_fp8_full_step(pos, lmax):
+    """hda_decode_step on an fp8 full-layer cache (the streaming kernel's
+    step form: the wave owning a pair's first round quantizes and appends
+    the new row; the merge scores it, and for pos 0 -- no held rows --
+    quantizes and appends it itself): the cache as the oracle's (one code
+    step) and bit-identical to the two-call path's, out / lse within the
+    decode tolerance, with sinks and the gate; contiguous and paged."""
+    import full_kv_cache_amd as hda
+    print("CASE fp8 full step", pos, flush=True)
+    case = Fp8Case(2400 + len(pos), FULL, pos, lmax)
+    Hq = case.shape.num_q_heads
+    sk = np.linspace(-1.0, 3.0, Hq).astype(np.float32)
+    g = np.random.default_rng(8).uniform(-3, 3, size=(len(pos), Hq)).astype(np.float32)
+    q_ref, blocks, ref, rlse = case.oracle_step(sinks=sk, gate=g)
+    d2, _, _ = case.gpu_step(sinks=sk, gate=g)  # hda_rope_append + hda_decode_attn
+    d = case.device()
+    cache = case.cache(d)
+    ws = torch.zeros(hda.hda_decode_step_workspace_bytes(cache, FULL), dtype=torch.uint8, device="cuda")
+    out = torch.full((len(pos), Hq, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((len(pos), Hq), float("nan"), device="cuda")
+    hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], torch.from_numpy(case.pos).cuda(), FULL,
+                        cache, torch.from_numpy(sk).cuda(), 1 / 16, out, lse, ws,
+                        gate=torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    _check_append(case, d, q_ref, blocks, q_rotated=False)
+    for n in ("kc", "vc"):
+        assert torch.equal(d[n], d2[n]), n
+    for n in ("ks", "vs"):
+        assert torch.equal(d[n].view(torch.int32), d2[n].view(torch.int32)), n
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+def test_fp8_full_step_paged():
+    """The fp8 full-layer step through a shuffled pool of 64-row pages: the
+    same out / lse as on the contiguous cache, bit for bit, and the new rows
+    in the pages the table names."""
+    import full_kv_cache_amd as hda
+    print("CASE fp8 full step paged", flush=True)
+    ps = 64
+    case = Fp8Case(2500, FULL, [0, 63, 64, 1500, 2047], 2048)
+    Hq = case.shape.num_q_heads
+    B, Hkv, cap, D = case.kc.shape
+    mp = cap // ps
+    perm = np.random.default_rng(10).permutation(B * mp + 3)
+
+    def pool(a):
+        out = np.zeros((B * mp + 3, Hkv, ps) + a.shape[3:], a.dtype)
+        pages = a.reshape((B, Hkv, mp, ps) + a.shape[3:]).swapaxes(1, 2).reshape((B * mp, Hkv, ps) + a.shape[3:])
+        out[perm[:B * mp]] = pages
+        return torch.from_numpy(out).cuda()
+
+    res = []
+    for paged in (False, True):
+        d = case.device()
+        if paged:
+            kp, vp, ksp, vsp = (pool(getattr(case, n)) for n in ("kc", "vc", "ks", "vs"))
+            table = torch.from_numpy(perm[:B * mp].reshape(B, mp).astype(np.int32)).cuda()
+            cache = case.cache(d, block_table=table, kc=kp, vc=vp, ks=ksp, vs=vsp)
+        else:
+            cache = case.cache(d)
+        ws = torch.zeros(hda.hda_decode_step_workspace_bytes(cache, FULL), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty((B, Hq, 256), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq), device="cuda")
+        hda.hda_decode_step(d["q"], d["k_new"], d["v_new"], torch.from_numpy(case.pos).cuda(), FULL,
+                            cache, None, 1 / 16, out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((out, lse))
+        if paged:  # gather the pool back through the table: as the contiguous step left it
+            for n, pl in (("kc", kp), ("ks", ksp)):
+                back = pl[torch.from_numpy(perm[:B * mp]).cuda()].reshape((B, mp, Hkv, ps) + pl.shape[3:])
+                back = back.transpose(1, 2).reshape((B, Hkv, cap) + pl.shape[3:])
+                for b, p in enumerate(case.pos):
+                    got, want = back[b, :, p].contiguous(), cont[n][b, :, p].contiguous()
+                    assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), n
+        else:
+            cont = {"kc": d["kc"], "ks": d["ks"]}
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1], res[1][1])
