@@ -4,9 +4,11 @@ compiler's resource-usage report, no GPU).
 A kernel whose per-lane arrays leave registers for scratch memory still
 computes the right result but streams far slower (a value-initialised
 vector in shared code once pushed the sliding-layer step from 20 to 48 us).
-Every kernel on a default path -- the one-launch window step and the
-streaming and window kernels, bf16 and fp8, the chunk-decode kernels, the
-merges and the appends -- must use no scratch and spill nothing.
+Every kernel on a default path -- the one-launch window step, the
+streaming kernel (plain and in its step form) and the window kernels, bf16
+and fp8, the chunk-decode kernels, the merges and the appends -- and the
+one-launch step for sliding windows past one workgroup must use no scratch
+and spill nothing.
 """
 import os
 import re
