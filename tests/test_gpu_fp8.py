@@ -30,15 +30,16 @@ NAN8 = 0x7F
 
 
 class Fp8Case:
-    def __init__(self, seed, lt, pos, lmax=None):
+    def __init__(self, seed, lt, pos, lmax=None, hq=8, hkv=2):
         self.lt = lt
         self.pos = np.asarray(pos, np.int32)
         B = len(pos)
         lmax = lmax or int(self.pos.max()) + 1
-        self.shape = workloads.HybridShape(batch=B, lmax=lmax)
+        self.shape = workloads.HybridShape(batch=B, lmax=lmax, num_q_heads=hq, num_kv_heads=hkv)
         s = self.shape
         g = workloads.generator(seed)
-        t = workloads.layer_inputs(g, workloads.HybridShape(batch=B, lmax=16), lt)
+        t = workloads.layer_inputs(g, workloads.HybridShape(batch=B, lmax=16, num_q_heads=hq,
+                                                            num_kv_heads=hkv), lt)
         self.q, self.k_new, self.v_new = (workloads.bits(t[n]).copy() for n in ("q", "k_new", "v_new"))
         cap = s.capacity(lt)
         g8 = workloads.generator(seed + 1)
@@ -253,8 +254,12 @@ def test_fp8_window_step(pos):
         assert torch.count_nonzero(ws[:4 * len(pos) * 2]).item() == 0
 
 
-@pytest.mark.parametrize("pos,lmax", [([0, 17, 300, 2047], 2048), ([5, 700, 4095, 1100, 1], 4096)])
-def test_fp8_full_step(pos, lmax):
+@pytest.mark.parametrize("pos,lmax,hq,hkv", [
+    ([0, 17, 300, 2047], 2048, 8, 2), ([5, 700, 4095, 1100, 1], 4096, 8, 2),
+    ([0, 900, 2047], 2048, 4, 4), ([3, 1500, 640], 2048, 8, 4),      # groups 1, 2
+    ([0, 1300, 2047], 2048, 16, 2), ([7, 2000, 129], 2048, 32, 2),  # groups 8, 16
+])
+def test_fp8_full_step(pos, lmax, hq, hkv):
     """hda_decode_step on an fp8 full-layer cache (the streaming kernel's
     step form: the wave owning a pair's first round quantizes and appends
     the new row; the merge scores it, and for pos 0 -- no held rows --
@@ -262,8 +267,8 @@ def test_fp8_full_step(pos, lmax):
     step) and bit-identical to the two-call path's, out / lse within the
     decode tolerance, with sinks and the gate; contiguous and paged."""
     import full_kv_cache_amd as hda
-    print("CASE fp8 full step", pos, flush=True)
-    case = Fp8Case(2400 + len(pos), FULL, pos, lmax)
+    print("CASE fp8 full step", pos, hq, hkv, flush=True)
+    case = Fp8Case(2400 + len(pos) + hq, FULL, pos, lmax, hq=hq, hkv=hkv)
     Hq = case.shape.num_q_heads
     sk = np.linspace(-1.0, 3.0, Hq).astype(np.float32)
     g = np.random.default_rng(8).uniform(-3, 3, size=(len(pos), Hq)).astype(np.float32)
