@@ -217,15 +217,17 @@ template <bool STEP>
 using StepArg = std::conditional_t<STEP, StreamStep, NoStep>;
 
 // Keys of sequence b in the step form: the rows its block held before this
-// token (the new one is scored by the merge).
+// token (the new one is scored apart and folded in by the merge).
 __device__ __forceinline__ int held_keys(const StreamStep &ss, int64_t capacity, int b) {
     const int P = ss.pos[b];
     return P < 0 ? 0 : (int)((int64_t)P < capacity ? P : capacity);
 }
 
 // F8: the cache holds e4m3 codes and per-row scales (kq, vq, ks, vs).
-// ROT > 0: the step form (bf16, rotary_dim ROT): keys are the held rows, q
-// is rotated in registers at each pair's position.
+// ROT > 0: the step form (rotary_dim ROT; bf16 or fp8): keys are the held
+// rows, q is rotated at each pair's position, and the wave holding a pair's
+// first round scores and appends the new token.  The fp8 step form runs
+// the two-buffer loop below, not the plain fp8 loop.
 template <int G, bool F8, int ROT = 0>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepArg<(ROT > 0)> ss) {
     constexpr bool STEP = ROT > 0;
