@@ -288,3 +288,28 @@ def test_step_full_matches_two_calls():
     assert torch.equal(d1["v"].view(torch.int16), d2["v"].view(torch.int16))
     assert_attn_close(out1, to_f64(out2))
     np.testing.assert_allclose(to_f64(lse1), to_f64(lse2), rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("pos", [[0, 100, 2046, 2047, 5000], [1023, 1024, 4095]])
+def test_step_wide_sliding_window(pos):
+    """A sliding window of 2048 keys (past one workgroup's 1024): the step
+    takes the one-launch streaming form (decode_step_kernel: RoPE, the ring
+    append with eviction, attention, last-arriver merge); against the
+    oracle, with sinks, twice on one workspace (counters back at zero)."""
+    import full_kv_cache_amd as hda
+    _print_case(test="step_wide_window", pos=pos)
+    case = HybridCase(1400 + len(pos), len(pos), SLIDING, pos, window=2048, poison=True)
+    _poison_stale_evicted_row(case)
+    sinks = np.linspace(-1.0, 3.0, case.shape.num_q_heads).astype(np.float32)
+    h, ref, rlse = case.oracle_step(sinks=sinks)
+    ws = None
+    for _ in range(2):
+        d = case.device()
+        if ws is None:
+            ws = torch.zeros(hda.hda_decode_step_workspace_bytes(case.cache(d), SLIDING),
+                             dtype=torch.uint8, device="cuda")
+        d, out, lse = fused_step(case, sinks=sinks, d=d, workspace=ws)
+        _check_cache(d, h)
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+        assert torch.count_nonzero(ws[: 4 * len(pos) * 2]).item() == 0
