@@ -46,7 +46,7 @@ def build(verbose: bool = False) -> Path:
     for src in SOURCES:
         path = CSRC / src
         if not path.exists():
-            continue
+            raise FileNotFoundError(f"library source {path} is missing")
         obj = build_dir / (src + ".o")
         cmd = [HIPCC, *compile_flags(), "-c", "-x", "hip", str(path), "-o", str(obj)]
         if verbose:

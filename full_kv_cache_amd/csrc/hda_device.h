@@ -154,7 +154,7 @@ struct SinCosReduced {
     double r, r2;
     long q;
 };
-__device__ __forceinline__ SinCosReduced sincos_reduce(float angle) {
+__host__ __device__ __forceinline__ SinCosReduced sincos_reduce(float angle) {
     constexpr double kPio2Hi = 1.5707963267948966;       // pi/2 rounded to double
     constexpr double kPio2Lo = 6.123233995736766e-17;    // pi/2 - kPio2Hi
     constexpr double k2OverPi = 0.63661977236758134;
@@ -166,7 +166,7 @@ __device__ __forceinline__ SinCosReduced sincos_reduce(float angle) {
     red.q = (long)k & 3;
     return red;
 }
-__device__ __forceinline__ void sincos_finish(const SinCosReduced &red, double ps, double pc, float *c,
+__host__ __device__ __forceinline__ void sincos_finish(const SinCosReduced &red, double ps, double pc, float *c,
                                               float *s) {
     const double sv = red.r * ps, cv = pc;
     const long q = red.q;
@@ -175,7 +175,7 @@ __device__ __forceinline__ void sincos_finish(const SinCosReduced &red, double p
     *c = (float)co;
     *s = (float)so;
 }
-__device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
+__host__ __device__ __forceinline__ void sincos_angle(float angle, float *c, float *s) {
     const SinCosReduced red = sincos_reduce(angle);
     // sin r = r (1 - r^2/3! (1 - r^2/(4*5) (1 - ...))), cos likewise, Horner
     double ps = 1.0, pc = 1.0;

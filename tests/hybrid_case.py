@@ -130,6 +130,15 @@ def fused_step(case: "HybridCase", sinks=None, scale=1 / 16, d=None, workspace=N
     return d, out, lse
 
 
+def near_lse_sinks(lse, seed, spread=2.0):
+    """Per-head sinks drawn near the heads' lse (mean over sequences plus
+    N(0, spread)): factors 1/(1+exp(sink-lse)) spread over (0, 1), so the
+    sink moves the output (an N(0, 1) sink next to lse ~ 8 barely does)."""
+    g = np.random.default_rng(seed)
+    lse = np.asarray(lse, np.float64)
+    return (lse.reshape(-1, lse.shape[-1]).mean(0) + g.normal(0, spread, lse.shape[-1])).astype(np.float32)
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().double().numpy()
 
@@ -154,3 +163,30 @@ def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
         x = x.astype(np.int32)
         return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + (x & 0x7FFF))
     return np.abs(key(a_bits) - key(b_bits))
+
+
+def assert_rotated_close(got_bits, ref_bits, rot=None, max_frac=1e-3):
+    """Rotated bf16 values (last axis = head dims, rotary pairs j and
+    j + rot/2) against the oracle's.  Both sides use the same fp32 cos /
+    sin; the kernel forms x1 c - x2 s in fp32 (one rounded product, one
+    fma), the oracle in fp64, and each rounds once to bf16.  So a value is
+    within one bf16 ulp of the oracle's, except where the rotation cancels
+    (a result far below its pair's norm): there the fp32 product's rounding,
+    at most 2^-24 of the pair's norm, can be many ulps of the small result,
+    and the bound is 2^-22 of the norm.  Fewer than max_frac of the values
+    differ at all."""
+    got_bits = np.asarray(got_bits)
+    ref_bits = np.asarray(ref_bits)
+    ulps = bf16_ulp_diff(got_bits, ref_bits)
+    g, r = oracle.bf16_to_f64(got_bits), oracle.bf16_to_f64(ref_bits)
+    rot = rot or r.shape[-1]
+    h = rot // 2
+    norm = np.zeros_like(r)
+    pn = np.sqrt(r[..., :h] ** 2 + r[..., h:rot] ** 2)
+    norm[..., :h] = pn
+    norm[..., h:rot] = pn
+    ok = (ulps <= 1) | (np.abs(g - r) <= 2.0 ** -22 * norm)
+    assert ok.all(), f"{(~ok).sum()} rotated values off by more than the fp32 rounding bound"
+    frac = (ulps > 0).mean()
+    assert frac < max_frac, f"{frac:.2e} of rotated values differ"
+

@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from hybrid_case import (BF16_NAN, FULL, SLIDING, HybridCase, assert_attn_close, bf16_ulp_diff,
-                         bits_of, fused_step, to_f64)
+from hybrid_case import (BF16_NAN, FULL, SLIDING, HybridCase, assert_attn_close, assert_rotated_close,
+                         bits_of, fused_step, near_lse_sinks, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +23,7 @@ def _print_case(**kw):
 
 def _check_cache(d, h):
     assert np.array_equal(bits_of(d["v"]), h["v"])
-    ulps = bf16_ulp_diff(bits_of(d["k"]), h["k"])
-    assert ulps.max() <= 1, ulps.max()
-    assert (ulps > 0).mean() < 1e-3
+    assert_rotated_close(bits_of(d["k"]), h["k"])
 
 
 def _poison_stale_evicted_row(case):
@@ -104,7 +102,8 @@ def test_step_outside_cache():
     sub.pos, sub.seq_lens = np.array([63], np.int32), np.array([64], np.int32)
     sub.shape = sub.shape.__class__(batch=1, lmax=64)
     h, ref, rlse = sub.oracle_step()
-    assert np.array_equal(v_gpu[1:2], h["v"]) and bf16_ulp_diff(k_gpu[1:2], h["k"]).max() <= 1
+    assert np.array_equal(v_gpu[1:2], h["v"])
+    assert_rotated_close(k_gpu[1:2], h["k"])
     assert_attn_close(out[1:2], ref)
     np.testing.assert_allclose(to_f64(lse)[1:2], rlse, rtol=0, atol=1e-4)
     # sequence 2: q rotated at 80, keys = the 64 cached rows
@@ -194,28 +193,23 @@ def test_step_graph_replay():
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
 
 
-def test_step_batch64_sampled():
-    """Headline shape: batch 64, lengths uniform in [512, 4096], in the
-    launch configuration the bench times; the oracle checks 8 sequences."""
+def test_step_batch64_all():
+    """Headline shape: batch 64, lengths uniform in [512, 4096], sinks drawn
+    near lse, in the launch configuration the bench times; every sequence
+    is checked against the oracle (the balanced streaming partition of a
+    full layer cuts sequences at data-dependent places)."""
     _print_case(test="step_batch64")
     g = np.random.default_rng(64)
     pos = g.integers(511, 4096, 64).astype(np.int32)
-    sample = np.array([0, 1, 7, 20, 33, 47, 62, 63])
     for lt in (SLIDING, FULL):
         case = HybridCase(1000 + lt, 64, lt, pos, lmax=4096)
-        d, out, lse = fused_step(case)
-        sub = HybridCase(1000 + lt, 64, lt, pos, lmax=4096)
-        for k in sub.host:
-            sub.host[k] = sub.host[k][sample].copy()
-        sub.pos = pos[sample]
-        sub.seq_lens = sub.pos + 1
-        sub.shape = sub.shape.__class__(batch=len(sample), lmax=4096)
-        h, ref, rlse = sub.oracle_step()
-        assert_attn_close(out[torch.from_numpy(sample).cuda()], ref)
-        np.testing.assert_allclose(to_f64(lse)[sample], rlse, rtol=0, atol=1e-4)
-        kk = bits_of(d["k"])[sample]
-        assert bf16_ulp_diff(kk, h["k"]).max() <= 1
-        assert np.array_equal(bits_of(d["v"])[sample], h["v"])
+        _, _, lse0 = case.oracle_step()
+        sinks = near_lse_sinks(lse0, 70 + lt)
+        h, ref, rlse = case.oracle_step(sinks=sinks)
+        d, out, lse = fused_step(case, sinks=sinks)
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+        _check_cache(d, h)
 
 
 def test_step_full_rotary_256():
@@ -264,7 +258,7 @@ def test_step_full_paged(page_size):
     gk, gv = oracle.page_gather(bits_of(pool_k), table), oracle.page_gather(bits_of(pool_v), table)
     for b, n in enumerate(case.seq_lens):
         assert np.array_equal(gv[b, :, :n], h["v"][b, :, :n]), b
-        assert bf16_ulp_diff(gk[b, :, :n], h["k"][b, :, :n]).max() <= 1, b
+        assert_rotated_close(gk[b, :, :n], h["k"][b, :, :n])
     assert np.array_equal(bits_of(pool_k)[spare], pk[spare])
     assert np.array_equal(bits_of(pool_v)[spare], pv[spare])
     assert_attn_close(out, ref)

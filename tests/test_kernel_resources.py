@@ -26,7 +26,7 @@ CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 # mangled-name fragments of the kernels that must stay in registers
 DEFAULT_PATH = {
     "decode_step.hip": ["decode_window_step_kernelILi2ELi256ELb0E", "decode_window_step_kernelILi2ELi256ELb1E",
-                        "decode_window_step_kernelILi2ELi64ELb0E", "decode_step_kernelILi4ELi64E"],
+                        "decode_window_step_kernelILi2ELi64ELb0E", "decode_step_kernelILi4ELi256E"],
     "decode_attn.hip": ["decode_stream_kernelILi4ELb0E", "decode_stream_kernelILi4ELb1E",
                         "decode_pair_kernelILi2ELb0E", "decode_pair_kernelILi2ELb1E",
                         "stream_merge_kernel", "lse_merge_kernel"],
