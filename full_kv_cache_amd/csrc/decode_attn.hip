@@ -977,19 +977,8 @@ hipError_t launch_decode_chunks(const DecodeParams &p, int group, bool final_out
 // its occupancy per CU times the CU count (0 when no device answers).
 template <int G>
 int stream_slots_g() {
-    static int cached = -1;
-    if (cached < 0) {
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_stream_kernel<G, false>, 64, 0) !=
-                hipSuccess) {
-            (void)hipGetLastError();
-            return 0;
-        }
-        cached = cus * per_cu;
-    }
-    return cached;
+    static std::atomic<int> cache[kMaxDevices];
+    return resident_slots(reinterpret_cast<const void *>(decode_stream_kernel<G, false>), 64, cache);
 }
 
 int stream_wave_slots(int group) {

@@ -462,37 +462,55 @@ __global__ __launch_bounds__(64) void decode_step_kernel(StepParams p) {
     }
 }
 
+#ifndef HDA_WINDOW_WAVES
+#define HDA_WINDOW_WAVES 8
+#endif
+constexpr int kWindowWaves = HDA_WINDOW_WAVES;
+
 // ===================================================================
-// Window form of the step (sliding layers, window <= kPairMaxKeys): one
-// workgroup of kPairWaves waves per (sequence, KV head, 1/S of the query
-// group), as decode_pair_kernel, with the rest of the step inside:
+// Window form of the step (sliding layers, window <= kPairMaxKeys): S
+// workgroups of kWindowWaves waves per (sequence, KV head), with the whole
+// step inside:
 //   * prologue: the angle table for the sequence's position, the
-//     workgroup's GW query rows and the new K rotated into LDS, the new V
+//     workgroup's query rows and the new K rotated into LDS, the new V
 //     copied there;
 //   * rounds: the new token's row (min(pos, window-1)) is served from LDS;
 //     the round that reads ring slot s keeps its old entry (a key of this
 //     step) in LDS as well;
-//   * epilogue: the waves merge in LDS and write out / lse with the sink;
-//     then the last of the S workgroups of the pair (a counter per pair, taken
-//     once each workgroup's loads of the block are consumed) writes the
-//     append: the kept entry to the evicted-entry row, the new token to its
-//     slot (or to row pos below a full window), and resets the counter.
-// Both workgroups of a pair read every key row; neither writes one until
-// both have read them, and no data passes between them, so no fence is
-// needed around the counter.
+//   * epilogue: the waves merge in LDS.
+// Two ways to split a pair over its S workgroups:
+//   * KS (key split; query groups up to 4): workgroup `part` scores rounds
+//     [part R / S, (part+1) R / S) of the pair's R 16-key rounds for every
+//     query head of the group, so each key row is read once.  With S > 1
+//     each workgroup leaves a normalised partial (o, lse in log2 units),
+//     written and read past the XCD-private caches; the last of the S to
+//     count in (a counter per pair, taken once its partial's stores are
+//     complete) merges them, writes out / lse with the sink and resets the
+//     counter.  The append is written by the workgroup whose rounds hold
+//     the row the new token takes (its ring slot, or row pos below a full
+//     window), once its own loads are consumed: that row is read by no
+//     other workgroup, and the evicted-entry row it also writes is only
+//     read where the new token's row replaces what was loaded.
+//   * head split (query groups of 8 and 16, whose accumulators would not
+//     fit two rounds in flight): workgroup `part` serves query heads part
+//     GW .. +GW-1 (GW = 4) over every key; it writes out / lse itself, and the last
+//     of the S workgroups (the counter again, taken once each workgroup's
+//     loads of the block are consumed) writes the append.
+// No data passes between the workgroups of a pair except the partials.
 // F8 (fp8 cache: e4m3 codes + a scale per row): rounds load codes and the
 // key scales (as the streaming kernel's fp8 form); the prologue quantizes
 // the new K and V rows (scale = amax / 448) into LDS; the round holding the
 // new token's row takes its codes and scales there; the kept old entry and
 // the append move codes and scales together.
 // ===================================================================
-template <int GW, int ROT, bool F8>
-__global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(StepParams p, int S) {
+template <int GW, int ROT, bool F8, bool KS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepParams p, int S) {
     constexpr int D = kHeadDim;
-    constexpr int WAVES = kPairWaves;
+    constexpr int NT = WAVES * 64;
     static_assert(ROT % 16 == 0 && ROT <= D, "rotary dims in 16-byte chunk pairs");
-    __shared__ __align__(16) float s_red[WAVES * GW * D];
+    static_assert(GW * D * sizeof(float) <= kKTile * sizeof(uint16_t), "a wave's o rows fit its K tile");
     __shared__ __align__(16) float s_pw[WAVES][16 * GW];
+    // a wave's K tile; after its last round, its unnormalised o rows
     __shared__ __align__(16) uint16_t s_kt[WAVES][kKTile];
     __shared__ __align__(16) float s_cos[ROT / 2], s_sin[ROT / 2];
     // rows 0..GW-1 rotated q, GW rotated new K, GW+1 new V, GW+2/GW+3 the
@@ -512,9 +530,17 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     const int pr = ((x >> 3) / S) * 8 + (x & 7);
     if (pr >= pairs) return;
     const int b = pr / p.num_kv_heads, kvh = pr % p.num_kv_heads;
-    const int hsub = kvh * S + part;  // query heads hsub*GW .. +GW-1
+    const int hsub = KS ? kvh : kvh * S + part;  // query heads hsub*GW .. +GW-1
     const int Hq = p.num_q_heads, W = p.window;
     const int P = p.pos[b];
+    // the heads' sinks and output-gate logits, for the epilogue: uniform
+    // addresses (scalar loads, which no wait for the K/V rows holds up)
+    float sink[GW], glog[GW];
+#pragma unroll
+    for (int h = 0; h < GW; ++h) {
+        sink[h] = p.sinks ? p.sinks[hsub * GW + h] : 0.f;
+        glog[h] = p.gate ? p.gate[(int64_t)b * Hq + hsub * GW + h] : 0.f;
+    }
     const int n = P < 0 ? 0 : min(P + 1, W);
     const int vrow = min(P, W - 1);                       // the new token's row
     const int srow = P >= W - 1 ? P % (W - 1) : -1;       // ring slot it takes
@@ -532,8 +558,10 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     uint16_t *const s_knew = s_rows + GW * D, *const s_vnew = s_rows + (GW + 1) * D;
     uint16_t *const s_oldk = s_rows + (GW + 2) * D, *const s_oldv = s_rows + (GW + 3) * D;
 
+    // this workgroup's rounds [q_lo, q_hi), then this wave's share of them
     const int R = (n + 15) >> 4;
-    const int r_lo = wave * R / WAVES, r_hi = (wave + 1) * R / WAVES;
+    const int q_lo = KS ? part * R / S : 0, q_hi = KS ? (part + 1) * R / S : R;
+    const int r_lo = q_lo + wave * (q_hi - q_lo) / WAVES, r_hi = q_lo + (wave + 1) * (q_hi - q_lo) / WAVES;
     auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap - 16 ? 16 * r : cap - 16); };
 
     // Prologue loads first, one 16-byte task per thread: the GW query rows
@@ -544,7 +572,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     // wave-uniform and the two loads of a thread are unconditional.
     constexpr int kRot = ROT / 16, kRow = kRot + (D - ROT) / 8;  // tasks per rotated row
     constexpr int kTasks = (GW + 1) * kRow + D / 8;
-    static_assert(kTasks <= WAVES * 64 && ROT / 2 <= WAVES * 64, "one prologue task per thread");
+    static_assert(kTasks <= NT && ROT / 2 <= NT, "one prologue task per thread");
     const int tt = tid < kTasks ? tid : kTasks - 1;  // idle threads repeat the last task's loads
     const int tr = tt / kRow, tc = tt % kRow;
     const bool rotary = tr <= GW && tc < kRot;
@@ -564,18 +592,19 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     // no load above may be moved below this point (next to its use)
     asm volatile("" ::: "memory");
 
-    // Angle i = 16 * wave + lane (lanes 0..15): the wave reads its 16
+    // Angle i = APW * wave + lane (lanes 0..APW-1): the wave reads its APW
     // frequencies with scalar loads, whose wait counter is not the vector
     // loads' (waiting for them does not wait for the K/V rows), and each
     // lane keeps its own.
-    static_assert(ROT / 2 <= 16 * WAVES, "16 angles per wave");
-    const int ai = 16 * uniform(wave) + (lane & 15);
+    constexpr int APW = ROT / 2 <= 16 * WAVES ? 16 : 32;  // angles per wave
+    static_assert(ROT / 2 <= APW * WAVES, "every angle has a lane");
+    const int ai = APW * uniform(wave) + (lane & (APW - 1));
     float freq = 0.f;
-    if (16 * uniform(wave) < ROT / 2) {
-        const float4 *f4 = reinterpret_cast<const float4 *>(p.inv_freq + 16 * uniform(wave));
-        float f[16];
+    if (APW * uniform(wave) < ROT / 2) {
+        const float4 *f4 = reinterpret_cast<const float4 *>(p.inv_freq + APW * uniform(wave));
+        float f[APW];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < APW / 4; ++k) {
             const float4 v = f4[k];
             f[4 * k] = v.x;
             f[4 * k + 1] = v.y;
@@ -583,14 +612,14 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
             f[4 * k + 3] = v.w;
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-            if ((lane & 15) == k) freq = f[k];
+        for (int k = 0; k < APW; ++k)
+            if ((lane & (APW - 1)) == k) freq = f[k];
     }
 
     // Angles, then the rotated rows into LDS.  Done for an inactive
     // sequence too (nothing reads them then): a branch here would let the
     // compiler move the prologue loads behind the K/V loads.
-    if (lane < 16 && ai < ROT / 2) sincos_angle((float)P * freq, s_cos + ai, s_sin + ai);
+    if (lane < APW && ai < ROT / 2) sincos_angle((float)P * freq, s_cos + ai, s_sin + ai);
     __syncthreads();
     if (tid < kTasks) {
         // the new V row (s_vnew) follows the new K row in s_rows
@@ -699,15 +728,19 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
         }
     }
 
-    // merge the waves: each leaves its unnormalised o and its (m, l)
+    // merge the waves: each leaves its unnormalised o rows in its own K
+    // tile (its last round's reads of it come first in its LDS queue) and
+    // its (m, l)
     float m_h[GW], l_h[GW];
     st.totals(m_h, l_h);
+    float *red = reinterpret_cast<float *>(s_kt[wave]);
+    wave_lds_fence();
 #pragma unroll
     for (int h = 0; h < GW; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
-            if (hw == 0) s_red[(wave * GW + h) * D + 8 * dl + e] = o;
+            if (hw == 0) red[h * D + 8 * dl + e] = o;
         }
     if (lane == 0) {
 #pragma unroll
@@ -719,43 +752,150 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     // every wave's loads of the block are consumed past this barrier
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) {
-        s_last = 0;
-        if (P >= 0) {
-            const int old = __hip_atomic_fetch_add(p.counters + pr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = old == S - 1;
-            if (s_last) __hip_atomic_store(p.counters + pr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    for (int i = tid; i < GW * D; i += WAVES * 64) {
-        const int h = i / D, d = i % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+
+    // out of head h (of this workgroup's GW), dim d, with the sink and gate
+    auto write_out = [&](int h, int d, float o, float L, float lse) HDA_INLINE {
         const int hq = hsub * GW + h;
         uint16_t *outp = p.out + ((int64_t)b * Hq + hq) * D + d;
-        if (M == -INFINITY) {  // no keys
+        if (L == 0.f) {  // no keys
             *outp = 0;
             if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = -INFINITY;
-            continue;
+            return;
         }
-        float L = 0.f, o = 0.f;
+        float sk = 0.f, gl = 0.f;
+#pragma unroll
+        for (int j = 0; j < GW; ++j)
+            if (j == h) {
+                sk = sink[j];
+                gl = glog[j];
+            }
+        float f = 1.f / L;
+        if (p.sinks) f *= 1.f / (1.f + expf(sk - lse));
+        if (p.gate) f *= gate_factor(gl);
+        *outp = f32_to_bf16(o * f);
+        if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
+    };
+    // this workgroup's (o, l, max) of element i = h * D + d, merged over waves
+    auto wave_merge = [&](int i, float &o, float &L, float &M) HDA_INLINE {
+        const int h = i / D, d = i % D;
+        M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+        L = 0.f;
+        o = 0.f;
+        if (M == -INFINITY) return;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             const float sc = exp2f(s_m[w][h] - M);
             L = fmaf(sc, s_l[w][h], L);
-            o = fmaf(sc, s_red[(w * GW + h) * D + d], o);
+            o = fmaf(sc, reinterpret_cast<const float *>(s_kt[w])[h * D + d], o);
         }
-        const float lse = (M + log2f(L)) * kLn2;
-        float f = 1.f / L;
-        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
-        if (p.gate) f *= gate_factor(p.gate[(int64_t)b * Hq + hq]);
-        *outp = f32_to_bf16(o * f);
-        if (d == 0 && p.lse) p.lse[(int64_t)b * Hq + hq] = lse;
+    };
+
+    if (!KS || S == 1) {
+        for (int i = tid; i < GW * D; i += NT) {
+            float o, L, M;
+            wave_merge(i, o, L, M);
+            write_out(i / D, i % D, o, L, L == 0.f ? -INFINITY : (M + log2f(L)) * kLn2);
+        }
+    } else if (P < 0) {  // no keys in any workgroup of the pair: the first writes
+        if (part == 0)
+            for (int i = tid; i < GW * D; i += NT) write_out(i / D, i % D, 0.f, 0.f, -INFINITY);
+    } else {
+        // this workgroup's normalised partial, lse in log2 units (-inf and
+        // o = 0 without keys), past the XCD-private caches
+        constexpr int EPT = (GW * D + NT - 1) / NT;  // elements per thread
+        float own_o[EPT], own_l2[EPT];
+        float *po = p.part_o + ((int64_t)pr * S + part) * GW * D;
+        float *pl = p.part_lse + ((int64_t)pr * S + part) * GW;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int i = tid + k * NT;
+            own_o[k] = 0.f;
+            own_l2[k] = -INFINITY;
+            if (i < GW * D) {
+                float o, L, M;
+                wave_merge(i, o, L, M);
+                if (L > 0.f) {
+                    own_o[k] = o / L;
+                    own_l2[k] = M + log2f(L);
+                }
+                coherent_store(po + i, own_o[k]);
+                if (i % D == 0) coherent_store(pl + i / D, own_l2[k]);
+            }
+        }
+        // count in once this workgroup's partial stores are complete
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(p.counters + pr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = old == S - 1;
+            if (s_last) __hip_atomic_store(p.counters + pr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (s_last) {
+            // every partial's loads go out before the first is used (S <= 8)
+            const float *po0 = p.part_o + (int64_t)pr * S * GW * D;
+            const float *pl0 = p.part_lse + (int64_t)pr * S * GW;
+            float l2[EPT][8], ov[EPT][8];
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int i = min(tid + k * NT, GW * D - 1), h = i / D;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int sl = s < S && s != part ? s : (s == part ? part : S - 1);
+                    l2[k][s] = coherent_load(pl0 + sl * GW + h);
+                    ov[k][s] = coherent_load(po0 + (int64_t)sl * GW * D + i);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                const int i = tid + k * NT;
+                if (i >= GW * D) continue;
+                float Mx = -INFINITY;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    if (s == part) {
+                        l2[k][s] = own_l2[k];
+                        ov[k][s] = own_o[k];
+                    }
+                    if (s >= S) l2[k][s] = -INFINITY;
+                    Mx = fmaxf(Mx, l2[k][s]);
+                }
+                float L = 0.f, o = 0.f;  // Mx is finite: the last part holds a round
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float w = s < S ? exp2f(l2[k][s] - Mx) : 0.f;
+                    L += w;
+                    o = fmaf(w, s < S ? ov[k][s] : 0.f, o);
+                }
+                write_out(i / D, i % D, o, L, (Mx + log2f(L)) * kLn2);
+            }
+        }
     }
-    __syncthreads();
+
+    // The append: key split -- the workgroup whose rounds hold the row the
+    // new token takes; head split -- the last of the pair's workgroups to
+    // finish reading the block.
+    bool app;
+    if constexpr (KS) {
+        const int trow = srow >= 0 ? srow : vrow;
+        app = P >= 0 && (trow >> 4) >= q_lo && (trow >> 4) < q_hi;
+    } else {
+        __syncthreads();
+        if (tid == 0) {
+            s_last = 0;
+            if (P >= 0) {
+                const int old = __hip_atomic_fetch_add(p.counters + pr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_last = old == S - 1;
+                if (s_last) __hip_atomic_store(p.counters + pr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+        app = s_last;
+    }
     if constexpr (F8) {
-        if (s_last && tid < 128) {  // the append: 8 code bytes per thread, K then V
+        if (app && tid < 128) {  // 8 code bytes per thread, K then V
             const int which = tid >> 6, c = tid & 31, half = (tid >> 5) & 1;
             uint8_t *blk = (which ? p.vq : p.kq) + bh * cap * D;
             float *sblk = (which ? p.vs : p.ks) + bh * cap;
@@ -773,7 +913,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
         }
         return;
     }
-    if (s_last && tid < 128) {  // the append: 16 bytes per thread, K then V
+    if (app && tid < 128) {  // 16 bytes per thread, K then V
         const int which = tid >> 6, c = tid & 31, half = (tid >> 5) & 1;
         uint16_t *blk = which ? vblk : kblk;
         if (half == 0 && srow >= 0)  // the slot's old entry to the evicted-entry row
@@ -785,41 +925,31 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_window_step_kernel(Ste
     }
 }
 
-template <int GW, int ROT>
+template <int GW, int ROT, bool KS>
 hipError_t launch_window_gr(const StepParams &p, int S, hipStream_t s) {
+    constexpr int WAVES = kWindowWaves;
     const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
     const int64_t blocks = (pairs + 7) / 8 * 8 * S;
     if (p.kq)
-        hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT, true>), dim3((unsigned)blocks),
-                           dim3(kPairWaves * 64), 0, s, p, S);
+        hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT, true, KS, WAVES>), dim3((unsigned)blocks),
+                           dim3(WAVES * 64), 0, s, p, S);
     else
-        hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT, false>), dim3((unsigned)blocks),
-                           dim3(kPairWaves * 64), 0, s, p, S);
+        hipLaunchKernelGGL((decode_window_step_kernel<GW, ROT, false, KS, WAVES>), dim3((unsigned)blocks),
+                           dim3(WAVES * 64), 0, s, p, S);
     return hipGetLastError();
 }
 
-template <int GW>
+template <int GW, bool KS>
 hipError_t launch_window_g(const StepParams &p, int S, int rot, hipStream_t s) {
-    if (rot == 64) return launch_window_gr<GW, 64>(p, S, s);
-    if (rot == 256) return launch_window_gr<GW, 256>(p, S, s);
+    if (rot == 64) return launch_window_gr<GW, 64, KS>(p, S, s);
+    if (rot == 256) return launch_window_gr<GW, 256, KS>(p, S, s);
     return hipErrorInvalidValue;
 }
 
 template <int G, int ROT>
 int step_slots_gr() {
-    static int cached = -1;
-    if (cached < 0) {
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<G, ROT>, 64, 0) !=
-                hipSuccess) {
-            (void)hipGetLastError();
-            return 0;
-        }
-        cached = cus * per_cu;
-    }
-    return cached;
+    static std::atomic<int> cache[kMaxDevices];
+    return resident_slots(reinterpret_cast<const void *>(decode_step_kernel<G, ROT>), 64, cache);
 }
 
 template <int G>
@@ -853,12 +983,19 @@ int step_wave_slots(int group, int rot) {
 
 hipError_t launch_decode_window_step(const StepParams &p, int group, int rot, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    switch (group) {
-        case 1: return launch_window_g<1>(p, 1, rot, stream);
-        case 2: return launch_window_g<1>(p, 2, rot, stream);
-        case 4: return launch_window_g<2>(p, 2, rot, stream);
-        case 8: return launch_window_g<4>(p, 2, rot, stream);
-        case 16: return launch_window_g<8>(p, 2, rot, stream);
+    const WindowPlan w = window_step_plan(group, (int64_t)p.batch * p.num_kv_heads, p.window);
+    if (w.key_split) {
+        switch (group) {
+            case 1: return launch_window_g<1, true>(p, w.parts, rot, stream);
+            case 2: return launch_window_g<2, true>(p, w.parts, rot, stream);
+            case 4: return launch_window_g<4, true>(p, w.parts, rot, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (w.heads_per_part) {
+        case 1: return launch_window_g<1, false>(p, w.parts, rot, stream);
+        case 2: return launch_window_g<2, false>(p, w.parts, rot, stream);
+        case 4: return launch_window_g<4, false>(p, w.parts, rot, stream);
         default: return hipErrorInvalidValue;
     }
 }

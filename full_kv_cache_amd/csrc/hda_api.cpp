@@ -263,6 +263,25 @@ bool use_window_step(const hda_cache_desc *c, int layer) {
     return layer == HDA_SLIDING && c->window <= hda::kPairMaxKeys;
 }
 
+// Window step workspace: the counters, then (a key split over S
+// workgroups) each workgroup's partial o [pairs * S, G, D] and lse
+// [pairs * S, G], fp32.
+StepLayout window_layout(const hda_cache_desc *c) {
+    const int g = c->num_q_heads / c->num_kv_heads;
+    const int64_t pairs = (int64_t)c->batch * c->num_kv_heads;
+    const hda::WindowPlan plan = hda::window_step_plan(g, pairs, c->window);
+    StepLayout L;
+    L.o_off = counter_header(c);
+    if (!plan.key_split) {
+        L.lse_off = L.bytes = L.o_off;
+        return L;
+    }
+    const size_t slots = (size_t)pairs * plan.parts * g;
+    L.lse_off = L.o_off + up256(slots * hda::kHeadDim * sizeof(float));
+    L.bytes = L.lse_off + up256(slots * sizeof(float));
+    return L;
+}
+
 StepLayout step_layout(const hda_cache_desc *c, int waves) {
     const size_t slots = (size_t)waves + (size_t)c->batch * c->num_kv_heads;
     const size_t g = (size_t)(c->num_q_heads / c->num_kv_heads);
@@ -637,7 +656,7 @@ hda_status hda_lse_merge(const float *part_o, const float *part_lse, int32_t bat
 
 size_t hda_decode_step_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer) {
     if (check_step_shape(cache, layer) != HDA_OK) return 0;
-    if (use_window_step(cache, layer)) return counter_header(cache);
+    if (use_window_step(cache, layer)) return window_layout(cache).bytes;
     if (layer == HDA_FULL) return stream_step_bytes(cache);
     return step_layout(cache, step_waves(cache, layer)).bytes;
 }
@@ -695,8 +714,8 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new, 
     }
     const bool window = use_window_step(cache, layer);
     const int waves = window ? 0 : step_waves(cache, layer);
-    const StepLayout L = step_layout(cache, waves);
-    const size_t need = window ? counter_header(cache) : L.bytes;
+    const StepLayout L = window ? window_layout(cache) : step_layout(cache, waves);
+    const size_t need = L.bytes;
     if (!workspace || workspace_bytes < need)
         return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu at %p", need,
                     workspace_bytes, workspace);

@@ -4,7 +4,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace hda {
+
+// Workgroups of `kernel` (blocks of `threads`, no dynamic LDS) resident on
+// the current device at once: CUs x occupancy per CU, cached per device
+// ordinal (several host threads may ask; 0 in a cache entry = not known
+// yet).  Returns 0 when no device answers.
+constexpr int kMaxDevices = 64;
+inline int resident_slots(const void *kernel, int threads, std::atomic<int> (&cache)[kMaxDevices]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    cache[dev].store(cus * per_cu, std::memory_order_relaxed);
+    return cus * per_cu;
+}
 
 constexpr int kHeadDim = 256;     // head dim the decode kernels are built for
 constexpr int kMaxChunk = 512;    // most keys one decode workgroup scores
@@ -206,9 +231,37 @@ int step_wave_slots(int group, int rotary_dim);
 // p.stream_pre): out / lse with the sink.
 hipError_t launch_stream_merge(const DecodeParams &p, int waves, hipStream_t stream);
 
+// Split of the window step over the workgroups of one (sequence, KV head).
+// Head split: each of `parts` workgroups serves heads_per_part query heads
+// over every key (the pair's rows are read once per part, the second time
+// mostly from the XCD's L2).  Key split: each of `parts` workgroups serves
+// every query head over 1/parts of the keys, then the last to finish
+// merges the partials (measured on MI355X: the merge's round trip through
+// memory costs more than re-reading rows from L2, so it is taken only when
+// head parts alone would leave CUs idle).  Query groups of 8 and 16 always
+// split heads, 4 per workgroup.  Up to 4: two head parts (G = 4: 2 heads
+// each; G = 2: 1; G = 1: one part) while that gives at least 256
+// workgroups; otherwise a key split that doubles while the pairs give
+// fewer than 256 workgroups, up to 8 parts of at least 4 rounds of 16 keys.
+struct WindowPlan {
+    bool key_split;
+    int parts, heads_per_part;
+};
+inline WindowPlan window_step_plan(int group, int64_t pairs, int window) {
+    if (group >= 8) return {false, group / 4, 4};
+    const int hp = group >= 2 ? 2 : 1;  // head parts
+    if (pairs * hp >= 256) return {false, hp, group / hp};
+    const int rounds = (window + 15) / 16;
+    int s = 1;
+    while (s < 8 && pairs * s < 256 && rounds / (2 * s) >= 4) s *= 2;
+    if (s == 1) return {false, hp, group / hp};
+    return {true, s, group};
+}
+
 // Window form of the fused step (sliding layers with window <=
-// kPairMaxKeys == capacity): one workgroup per (sequence, KV head, half
-// query group); needs only the counters of StepParams.
+// kPairMaxKeys == capacity), split as window_step_plan says.  Needs the
+// counters of StepParams and, for a key split over S parts, part_o
+// [pairs * S, G, D] and part_lse [pairs * S, G].
 hipError_t launch_decode_window_step(const StepParams &p, int group, int rotary_dim, hipStream_t stream);
 
 hipError_t launch_lse_merge(const MergeParams &p, hipStream_t stream);

@@ -227,13 +227,17 @@ def test_step_shape_checks():
 
 def test_step_workspace():
     """Counter header first (shared with hda_decode_attn's layouts); the
-    window form (sliding layers) needs only that header, the streaming form
-    (full layers) adds one partial slot per wave and per (sequence, KV
-    head), and one new-key score per (sequence, query head)."""
+    window form (sliding layers) adds, for a key split over S workgroups, a
+    partial (o fp32 [G, 256], lse fp32 [G]) per workgroup; the streaming
+    form (full layers) adds one partial slot per wave and per (sequence,
+    KV head), and one new-key score per (sequence, query head)."""
     L = hda.lib()
     d = _desc()
     need = L.hda_decode_step_workspace_bytes(ctypes.byref(d), hda.SLIDING)
-    assert need == 256  # 2 sequences x 2 KV heads x 4 bytes, rounded up
+    # 2 sequences x 2 KV heads: 4 pairs, too few for 256 workgroups, so a
+    # 512-key window splits 8 ways (4 rounds each); group 4
+    pairs, S, G = 4, 8, 4
+    assert need == 256 + pairs * S * G * 256 * 4 + 512
     full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
     need_full = L.hda_decode_step_workspace_bytes(ctypes.byref(full), hda.FULL)
     assert need_full > 256 and need_full % 256 == 0
@@ -356,8 +360,9 @@ def test_fp8_routing():
     wide = _desc(**{**_FP8, "window": 2048, "capacity": 2048})
     assert _step(wide) == 2 and "fp8" in _msg()
     assert L.hda_decode_step_workspace_bytes(ctypes.byref(wide), hda.SLIDING) == 0
-    # the window form takes an fp8 cache: only the counter header as workspace
-    assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(**_FP8)), hda.SLIDING) == 256
+    # the window form takes an fp8 cache: the same workspace as on bf16
+    assert L.hda_decode_step_workspace_bytes(ctypes.byref(_desc(**_FP8)), hda.SLIDING) == \
+        L.hda_decode_step_workspace_bytes(ctypes.byref(_desc()), hda.SLIDING)
     r = L.hda_decode_attn_partials(ctypes.c_void_p(FAKE), ctypes.byref(full), ctypes.c_void_p(FAKE),
                                    hda.FULL, 0.0625, 4096, 256, ctypes.c_void_p(FAKE),
                                    ctypes.c_void_p(FAKE), None)
