@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.hda_decode_step.restype = ctypes.c_int
         L.hda_decode_step.argtypes = [P, P, P, P, ctypes.c_int, D, P, P, ctypes.c_float, P, P, P, sz,
                                       P]
+        L.hda_decode_step_noalloc.restype = ctypes.c_int
+        L.hda_decode_step_noalloc.argtypes = [P, P, P, P, ctypes.c_int, D, P, P, ctypes.c_float, P, P,
+                                              P]
         L.hda_decode_multi.restype = ctypes.c_int
         L.hda_decode_multi.argtypes = [P, P, P, P, i32, ctypes.c_int, D, P, P, ctypes.c_float, P,
                                        P, i32, P, sz, P]
@@ -286,6 +289,19 @@ def hda_decode_step(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, si
                                  ctypes.byref(d), _ptr(sinks), _ptr(gate), float(scale), _ptr(out),
                                  _ptr(lse),
                                  _ptr(workspace), wbytes, _stream(stream)))
+
+
+def hda_decode_step_noalloc(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, sinks,
+                            scale: float, out, lse=None, stream=None, gate=None):
+    """hda_decode_step with the library's static per-device scratch as its
+    workspace (nothing allocated by the call); calls on one GPU must not
+    overlap."""
+    validate_sinks(sinks, q)
+    validate_gate(gate, out)
+    d = cache.desc()
+    _check(lib().hda_decode_step_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(pos),
+                                         int(layer_type), ctypes.byref(d), _ptr(sinks), _ptr(gate),
+                                         float(scale), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def hda_decode_multi_workspace_bytes(cache: LayerCache, layer_type: int, tokens: int,

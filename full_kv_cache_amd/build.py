@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["hda_api.cpp", "rope_append.hip", "decode_attn.hip", "decode_step.hip", "sparse_attn.hip",
-           "decode_multi.hip"]
+           "decode_multi.hip", "noalloc.hip"]
 
 
 def compile_flags() -> list[str]:

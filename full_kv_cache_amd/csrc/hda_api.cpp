@@ -384,6 +384,12 @@ hda_status check_sparse_shape(int32_t tokens, int32_t heads, int32_t topk, int32
 
 }  // namespace
 
+namespace hda {
+// Records msg as the calling thread's last error (for entry points defined
+// in other sources of the library).
+hda_status report_error(hda_status st, const char *msg) { return fail(st, "%s", msg); }
+}  // namespace hda
+
 extern "C" {
 
 const char *hda_status_string(hda_status s) {

@@ -327,6 +327,26 @@ hda_status hda_decode_step(const void *q, const void *k_new, const void *v_new,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * hda_decode_step_noalloc -- hda_decode_step without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The workspace is
+ * a static device array of the library: 16 MiB, one per GPU the library runs
+ * on, held until the process ends.  Arguments, results and errors as
+ * hda_decode_step, plus WORKSPACE when the step needs more than that array
+ * holds (hda_decode_step_workspace_bytes() > 16 MiB: full layers past about
+ * 1,500 sequences), and HIP when no device is current.  The first call on a
+ * device also enqueues, on `stream`, one zero fill of the array.  Every call
+ * on a GPU uses that GPU's one array, which keeps the last call's contents:
+ * calls that overlap on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller.  Nothing here allocates or frees.
+ */
+hda_status hda_decode_step_noalloc(const void *q, const void *k_new, const void *v_new,
+                                   const int32_t *pos, hda_layer_type layer,
+                                   const hda_cache_desc *cache, const float *sinks,
+                                   const float *gate, float scale, void *out, float *lse,
+                                   void *stream);
+
+/*
  * hda_decode_multi -- decode of a chunk of `tokens` new tokens per sequence
  * in one call.  Spark export page, `SparkStepConfig.cache_len` docstring: a
  * ring holds a window's previous entries and the new token is scored with
