@@ -93,6 +93,9 @@ def _load():
         lib.or_sparse_decode_attn.restype = None
         lib.or_sparse_decode_attn.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, i32,
                                               P, f64, P, P]
+        lib.or_sparse_decode_attn_fp8.restype = None
+        lib.or_sparse_decode_attn_fp8.argtypes = [P, P, P, i64, P, i32, i32, i32, i32, i32,
+                                                  P, f64, P, P]
         lib.or_num_threads.restype = ctypes.c_int
         lib.or_num_threads.argtypes = []
         _lib = lib
@@ -364,4 +367,21 @@ def sparse_decode_attn(q, kv, indices, topk_length, sinks, scale, dv):
     lse = np.zeros((T, Hq), dtype=np.float64)
     _load().or_sparse_decode_attn(_p(q), _p(kv), N, _p(indices), topk, _p(tl), T, Hq, Dqk,
                                   dv, _p(sinks), scale, _p(out), _p(lse))
+    return out, lse
+
+
+def sparse_decode_attn_fp8(q, codes, scales, indices, sinks, scale, dv):
+    """q bf16 [T,Hq,Dqk], codes uint8 [N,Dqk] (e4m3), scales fp32 [N],
+    indices int32 [T,topk]; a row's value is code x scale."""
+    q, indices = _u16(q), _i32(indices)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = _f32(scales)
+    sinks = _f32(sinks)
+    T, Hq, Dqk = q.shape
+    N = codes.shape[0]
+    topk = indices.shape[1]
+    out = np.zeros((T, Hq, dv), dtype=np.float64)
+    lse = np.zeros((T, Hq), dtype=np.float64)
+    _load().or_sparse_decode_attn_fp8(_p(q), _p(codes), _p(scales), N, _p(indices), topk, T, Hq,
+                                      Dqk, dv, _p(sinks), scale, _p(out), _p(lse))
     return out, lse

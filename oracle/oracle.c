@@ -581,6 +581,35 @@ void or_decode_attn_f64(const uint16_t *q, const double *k, const double *v, con
     }
 }
 
+/* Attention over fp64 rows whose keys are all Dqk dims and whose values
+ * are the leading Dv dims (the sparse path's latent rows); the arithmetic
+ * of attend_rows. */
+static void attend_rows_kv_f64(const double *qv, const double *const *rows, int64_t n, int Dqk,
+                               int Dv, double scale, double *out, double *lse) {
+    for (int d = 0; d < Dv; ++d) out[d] = 0.0;
+    if (n == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double *sc = (double *)malloc(sizeof(double) * n);
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int d = 0; d < Dqk; ++d) acc += qv[d] * rows[i][d];
+        sc[i] = acc * scale;
+        if (sc[i] > m) m = sc[i];
+    }
+    double l = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double p = exp(sc[i] - m);
+        l += p;
+        for (int d = 0; d < Dv; ++d) out[d] += p * rows[i][d];
+    }
+    for (int d = 0; d < Dv; ++d) out[d] /= l;
+    *lse = m + log(l);
+    free(sc);
+}
+
 /* ---------------------------------------------------------- paged KV */
 
 /* Paged cache addressing, [SINK] `_fp8_flash_mla_kernel`: the attention
@@ -658,6 +687,55 @@ void or_sparse_decode_attn(const uint16_t *q, const uint16_t *kv, int64_t N,
             free(qv);
             free(rows);
         }
+    }
+}
+
+/* Sparse top-k decode with a sink over an fp8 latent pool, [SINK]
+ * `_fp8_flash_mla_kernel`: the same attention as or_sparse_decode_attn (no
+ * topk_length in that call: every index entry counts, negative ones are
+ * skipped), the cache handed over as bytes.  Reading (the call's layout is
+ * named, not printed): e4m3 codes, one fp32 scale per pool row, the value
+ * of element d of row r is or_e4m3_to_f64(codes[r][d]) * scales[r] -- for
+ * the key dims and the leading Dv value dims alike (the same row).
+ * Dequantization is exact in fp64; the attention is the fp64 one of
+ * or_decode_attn_f64 (attend_rows_f64 with separate key and value dims).
+ * q: bf16 [T, Hq, Dqk]; codes: uint8 [N, Dqk]; scales: fp32 [N]; indices:
+ * int32 [T, topk]; out fp64 [T, Hq, Dv]; lse fp64 [T, Hq] (pre-sink).
+ * Parity pinned: with power-of-two scales it equals or_sparse_decode_attn
+ * over the bf16 pool holding the same values, bit for bit; brute force in
+ * numpy fp64 on tiny inputs; -inf sink no-op (tests/test_oracle_sparse.py). */
+void or_sparse_decode_attn_fp8(const uint16_t *q, const uint8_t *codes, const float *scales, int64_t N,
+                               const int32_t *indices, int topk, int T, int Hq, int Dqk, int Dv,
+                               const float *sinks, double scale, double *out, double *lse) {
+    for (int t = 0; t < T; ++t) {
+        /* the token's rows, dequantized once */
+        double *rowv = (double *)malloc(sizeof(double) * ((size_t)topk * Dqk + 1));
+        const double **rows = (const double **)malloc(sizeof(void *) * (topk + 1));
+        int64_t n = 0;
+        for (int i = 0; i < topk; ++i) {
+            const int32_t idx = indices[(int64_t)t * topk + i];
+            if (idx < 0 || idx >= N) continue;
+            double *dst = rowv + n * Dqk;
+            for (int d = 0; d < Dqk; ++d)
+                dst[d] = or_e4m3_to_f64(codes[(int64_t)idx * Dqk + d]) * (double)scales[idx];
+            rows[n++] = dst;
+        }
+#pragma omp parallel for schedule(dynamic)
+        for (int h = 0; h < Hq; ++h) {
+            double *qv = (double *)malloc(sizeof(double) * Dqk);
+            const uint16_t *qh = q + ((int64_t)t * Hq + h) * Dqk;
+            for (int d = 0; d < Dqk; ++d) qv[d] = or_bf16_to_f64(qh[d]);
+            double *o = out + ((int64_t)t * Hq + h) * Dv;
+            double *ls = lse + (int64_t)t * Hq + h;
+            attend_rows_kv_f64(qv, rows, n, Dqk, Dv, scale, o, ls);
+            if (sinks) {
+                const double f = sink_factor(*ls, (double)sinks[h]);
+                for (int d = 0; d < Dv; ++d) o[d] *= f;
+            }
+            free(qv);
+        }
+        free(rows);
+        free(rowv);
     }
 }
 

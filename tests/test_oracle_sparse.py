@@ -93,3 +93,79 @@ def test_neg_inf_sink_noop():
     b, lb = oracle.sparse_decode_attn(t["q"], t["kv"], t["indices"], None,
                                       np.full(8, -np.inf, np.float32), 0.1, 64)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# ------------------------------------------------------------ fp8 pool
+# [SINK] `_fp8_flash_mla_kernel`: the same sparse attention over a pool handed
+# to the kernel as bytes.  Reading: e4m3 codes with one fp32 scale per row
+# (value = code x scale, key and value dims alike).  The codes are decoded
+# here with torch's float8_e4m3fn, independently of the oracle's decoder.
+
+
+def _fp8_pool(seed, N, D, pow2):
+    g = workloads.generator(seed)
+    codes = workloads.fp8_codes(g, (N, D))
+    if pow2:
+        e = torch.randint(-12, 1, (N,), generator=g).to(torch.float32)
+        scales = torch.pow(2.0, e)
+    else:
+        scales = workloads.fp8_scales(g, (N,))
+    return codes.numpy(), scales.numpy()
+
+
+def _dequant_torch(codes, scales):
+    v = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+    return v * torch.from_numpy(scales.astype(np.float64))[:, None]
+
+
+def test_fp8_pool_pow2_scales_equal_bf16_pool():
+    """Power-of-two scales keep every value a bf16 number: the fp8 oracle
+    equals the bf16 one on the pool holding those values, bit for bit."""
+    T, H, dqk, dv, N, topk = 3, 16, 576, 512, 200, 48
+    t = _inputs(20, T, H, dqk, dv, N, topk)
+    codes, scales = _fp8_pool(21, N, dqk, pow2=True)
+    vals = _dequant_torch(codes, scales)
+    kv_bits = workloads.bits(vals.to(torch.bfloat16))
+    assert np.array_equal(oracle.bf16_to_f64(kv_bits), vals.numpy())  # exact in bf16
+    t["indices"][0, 5] = -1
+    for sinks in (None, t["sinks"]):
+        a, la = oracle.sparse_decode_attn_fp8(t["q"], codes, scales, t["indices"], sinks, 1 / 24, dv)
+        b, lb = oracle.sparse_decode_attn(t["q"], kv_bits, t["indices"], None, sinks, 1 / 24, dv)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_fp8_pool_brute_force(with_sink):
+    T, H, dqk, dv, N, topk = 2, 16, 576, 512, 150, 40
+    t = _inputs(22, T, H, dqk, dv, N, topk)
+    codes, scales = _fp8_pool(23, N, dqk, pow2=False)
+    vals = _dequant_torch(codes, scales)
+    scale = 1 / np.sqrt(dqk)
+    sinks = t["sinks"] if with_sink else None
+    out, lse = oracle.sparse_decode_attn_fp8(t["q"], codes, scales, t["indices"], sinks, scale, dv)
+    for i in range(T):
+        K = vals[t["indices"][i]]                                   # [n, dqk]
+        s = (K @ _f(t["q"][i]).T) * scale                           # [n, H]
+        ref_lse = torch.logsumexp(s, 0)
+        p = torch.softmax(s, 0)
+        o = p.T @ K[:, :dv]                                         # [H, dv]
+        if sinks is not None:
+            o = o / (1 + torch.exp(torch.from_numpy(sinks.astype(np.float64)) - ref_lse))[:, None]
+        np.testing.assert_allclose(out[i], o.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[i], ref_lse.numpy(), rtol=0, atol=1e-12)
+
+
+def test_fp8_pool_skips_negative_indices_and_neg_inf_sink():
+    T, H, dqk, dv, N, topk = 2, 16, 576, 512, 80, 12
+    t = _inputs(24, T, H, dqk, dv, N, topk)
+    codes, scales = _fp8_pool(25, N, dqk, pow2=False)
+    a, la = oracle.sparse_decode_attn_fp8(t["q"], codes, scales, t["indices"], None, 0.05, dv)
+    b, lb = oracle.sparse_decode_attn_fp8(t["q"], codes, scales, t["indices"],
+                                          np.full(H, -np.inf, np.float32), 0.05, dv)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    idx2 = t["indices"].copy()
+    idx2[:, 3:] = -1
+    c, _ = oracle.sparse_decode_attn_fp8(t["q"], codes, scales, idx2, None, 0.05, dv)
+    d, _ = oracle.sparse_decode_attn_fp8(t["q"], codes, scales, np.ascontiguousarray(t["indices"][:, :3]),
+                                         None, 0.05, dv)
+    assert np.array_equal(c, d)
