@@ -399,20 +399,28 @@ def measured_traffic(kernel, batch):
     return table.get(kernel)
 
 
-def sparse_kernel(steps, warmup, seed, pools=8):
+def sparse_kernel(steps, warmup, seed, pools=8, fp8=False):
     """The sparse top-k decode with sinks at its page shape (32 tokens, 64
     query heads over one 576-dim latent head, value = leading 512 dims,
     pool of 32768 rows, top-2048 indices per token): `pools` distinct pools
-    (8 x 37.7 MB, more than the 256 MB last-level cache) are cycled through
-    one graph so that rows come from HBM, HIP events on the launch stream.
-    Gathered bytes per call = tokens x topk x 1152; flops = tokens x heads x
-    topk x 2 (576 + 512)."""
+    (8 x 37.7 MB bf16, more than the 256 MB last-level cache) are cycled
+    through one graph so that rows come from HBM, HIP events on the launch
+    stream.  Gathered bytes per call = tokens x topk x row bytes (1152 bf16;
+    fp8: 576 codes + a 4-byte scale); flops = tokens x heads x topk x 2
+    (576 + 512).  fp8: the pools hold e4m3 codes with per-row scales
+    (hda_sparse_decode_attn_fp8)."""
     import torch
     import workloads
     import full_kv_cache_amd as hda
     s = workloads.SparseShape()
     g = workloads.generator(seed + 1, "cuda")
     ins = [workloads.sparse_inputs(g, s, "cuda") for _ in range(pools)]
+    if fp8:
+        g8 = workloads.generator(seed + 7, "cuda")
+        for t in ins:
+            t["codes"] = workloads.fp8_codes(g8, (s.pool, s.dqk), "cuda")
+            t["scales"] = workloads.fp8_scales(g8, (s.pool,), "cuda")
+            del t["kv"]
     outs = [torch.empty(s.tokens, s.num_q_heads, s.dv, dtype=torch.bfloat16, device="cuda")
             for _ in range(pools)]
     lses = [torch.empty(s.tokens, s.num_q_heads, dtype=torch.float32, device="cuda")
@@ -423,23 +431,31 @@ def sparse_kernel(steps, warmup, seed, pools=8):
 
     def fn():
         for i in range(pools):
-            hda.hda_sparse_decode_attn(ins[i]["q"], ins[i]["kv"], ins[i]["indices"], None,
-                                       ins[i]["sinks"], scale, outs[i], lses[i], ws)
+            if fp8:
+                hda.hda_sparse_decode_attn_fp8(ins[i]["q"], ins[i]["codes"], ins[i]["scales"],
+                                               ins[i]["indices"], ins[i]["sinks"], scale, outs[i],
+                                               lses[i], ws)
+            else:
+                hda.hda_sparse_decode_attn(ins[i]["q"], ins[i]["kv"], ins[i]["indices"], None,
+                                           ins[i]["sinks"], scale, outs[i], lses[i], ws)
 
     ms, _ = time_graph(fn, steps, warmup)
     per_call_s = ms / pools / 1e3
-    gathered = s.tokens * s.topk * s.dqk * 2
+    row_bytes = s.dqk + 4 if fp8 else s.dqk * 2
+    gathered = s.tokens * s.topk * row_bytes
     flops = s.tokens * s.num_q_heads * s.topk * 2 * (s.dqk + s.dv)
     gbs = gathered / per_call_s / 1e9
+    kname = "sparse_decode_kernel<false, %s> + sparse_merge_kernel" % ("true" if fp8 else "false")
     return {
-        "kernel": "sparse_decode_kernel + sparse_merge_kernel (hda_sparse_decode_attn)",
+        "kernel": f"{kname} (hda_sparse_decode_attn{'_fp8' if fp8 else ''})",
         "workload": f"{s.tokens} tokens x {s.num_q_heads} heads, dqk {s.dqk} / dv {s.dv}, pool "
-                    f"{s.pool} rows, top-{s.topk}, per-head sinks, {pools} pools cycled",
+                    f"{s.pool} rows{' (e4m3 codes + row scales)' if fp8 else ''}, top-{s.topk}, "
+                    f"per-head sinks, {pools} pools cycled",
         "us_per_call": round(per_call_s * 1e6, 2), "gather_GBs": round(gbs, 1),
         "tflops": round(flops / per_call_s / 1e12, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("sparse_decode_kernel<false> + sparse_merge_kernel", 64),
+                     "traffic": measured_traffic(kname, 64),
                      "algorithmic_bytes_per_launch": gathered},
         "mfma_bf16_frac": round(flops / per_call_s / 2.5e15, 4),
     }
@@ -611,6 +627,7 @@ def main():
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
         sparse = sparse_kernel(args.steps, args.warmup, args.seed)
+        sparse["fp8"] = sparse_kernel(args.steps, args.warmup, args.seed, fp8=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -110,6 +110,9 @@ def lib() -> ctypes.CDLL:
         L.hda_sparse_decode_attn.restype = ctypes.c_int
         L.hda_sparse_decode_attn.argtypes = [P, P, ctypes.c_int64, P, i32, i32, P, i32, i32, i32,
                                              P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        L.hda_sparse_decode_attn_fp8.restype = ctypes.c_int
+        L.hda_sparse_decode_attn_fp8.argtypes = [P, P, P, ctypes.c_int64, P, i32, i32, i32, i32, i32,
+                                                 P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -351,3 +354,18 @@ def hda_sparse_decode_attn(q, kv, indices, topk_length, sinks, scale: float, out
                                         int(indices.shape[1]), _ptr(topk_length), int(H), int(dqk),
                                         int(out.shape[-1]), _ptr(sinks), float(scale), _ptr(out),
                                         _ptr(lse), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def hda_sparse_decode_attn_fp8(q, kv_codes, kv_scales, indices, sinks, scale: float, out, lse=None,
+                               workspace=None, stream=None):
+    """Sparse top-k decode over an fp8 latent pool: kv_codes uint8 [N, Dqk]
+    (e4m3), kv_scales fp32 [N] (a row's value is code x scale); q, indices,
+    sinks, out, lse and workspace as hda_sparse_decode_attn."""
+    validate_sinks(sinks, q)
+    T, H, dqk = q.shape
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hda_sparse_decode_attn_fp8(_ptr(q), _ptr(kv_codes), _ptr(kv_scales),
+                                            int(kv_codes.shape[0]), _ptr(indices), int(T),
+                                            int(indices.shape[1]), int(H), int(dqk), int(out.shape[-1]),
+                                            _ptr(sinks), float(scale), _ptr(out), _ptr(lse),
+                                            _ptr(workspace), wbytes, _stream(stream)))

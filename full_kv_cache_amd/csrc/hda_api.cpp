@@ -884,22 +884,28 @@ hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32
     return launched(hda::launch_decode_multi(p, g, static_cast<hipStream_t>(stream)), "chunk decode");
 }
 
-hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_rows,
-                                  const int32_t *indices, int32_t tokens, int32_t topk,
-                                  const int32_t *topk_length, int32_t num_q_heads, int32_t dqk,
-                                  int32_t dv, const float *sinks, float scale, void *out,
-                                  float *lse, void *workspace, size_t workspace_bytes,
-                                  void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the bf16 and fp8 sparse calls: kv is the bf16 pool, or kv8 /
+// kv_scale the fp8 one.
+hda_status sparse_call(const void *q, const void *kv, const uint8_t *kv8, const float *kv_scale,
+                       int64_t pool_rows, const int32_t *indices, int32_t tokens, int32_t topk,
+                       const int32_t *topk_length, int32_t num_q_heads, int32_t dqk, int32_t dv,
+                       const float *sinks, float scale, void *out, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream) {
     hda_status st = check_sparse_shape(tokens, num_q_heads, topk, dqk, dv);
     if (st != HDA_OK) return st;
     if (pool_rows < 1) return fail(HDA_ERR_INVALID_ARGUMENT, "pool_rows %lld < 1", (long long)pool_rows);
-    if (!q || !kv || !indices || !out)
-        return fail(HDA_ERR_INVALID_ARGUMENT, "q, kv, indices and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(kv) || !aligned16(out))
-        return fail(HDA_ERR_INVALID_ARGUMENT, "q, kv and out must be 16-byte aligned");
+    if (!q || !(kv || kv8) || !indices || !out || (kv8 && !kv_scale))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, the pool (codes and scales for fp8), indices and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(kv ? kv : kv8) || !aligned16(out))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "q, the pool and out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(indices) & 3u) || (topk_length && (reinterpret_cast<uintptr_t>(topk_length) & 3u)) ||
-        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)))
-        return fail(HDA_ERR_INVALID_ARGUMENT, "indices, topk_length, sinks and lse must be 4-byte aligned");
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (sinks && (reinterpret_cast<uintptr_t>(sinks) & 3u)) ||
+        (kv_scale && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)))
+        return fail(HDA_ERR_INVALID_ARGUMENT, "indices, topk_length, sinks, scales and lse must be 4-byte aligned");
     if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
     const SparsePlan pl = sparse_plan(tokens, num_q_heads, topk);
     const size_t need = sparse_workspace(tokens, num_q_heads, pl);
@@ -912,6 +918,8 @@ hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_ro
     hda::SparseParams p{};
     p.q = static_cast<const uint16_t *>(q);
     p.kv = static_cast<const uint16_t *>(kv);
+    p.kv8 = kv8;
+    p.kv_scale = kv_scale;
     p.indices = indices;
     p.topk_length = topk_length;
     p.sinks = sinks;
@@ -929,6 +937,32 @@ hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_ro
     p.split_keys = pl.split_keys;
     p.scale_log2 = scale * 1.4426950408889634f;
     return launched(hda::launch_sparse_decode(p, static_cast<hipStream_t>(stream)), "sparse decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_rows,
+                                  const int32_t *indices, int32_t tokens, int32_t topk,
+                                  const int32_t *topk_length, int32_t num_q_heads, int32_t dqk,
+                                  int32_t dv, const float *sinks, float scale, void *out,
+                                  float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    if (!kv) return fail(HDA_ERR_INVALID_ARGUMENT, "kv must be non-NULL");
+    return sparse_call(q, kv, nullptr, nullptr, pool_rows, indices, tokens, topk, topk_length,
+                       num_q_heads, dqk, dv, sinks, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+hda_status hda_sparse_decode_attn_fp8(const void *q, const uint8_t *kv_codes, const float *kv_scales,
+                                      int64_t pool_rows, const int32_t *indices, int32_t tokens,
+                                      int32_t topk, int32_t num_q_heads, int32_t dqk, int32_t dv,
+                                      const float *sinks, float scale, void *out, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (!kv_codes || !kv_scales)
+        return fail(HDA_ERR_INVALID_ARGUMENT, "kv_codes and kv_scales must be non-NULL");
+    return sparse_call(q, nullptr, kv_codes, kv_scales, pool_rows, indices, tokens, topk, nullptr,
+                       num_q_heads, dqk, dv, sinks, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 size_t hda_sparse_workspace_bytes(int32_t tokens, int32_t num_q_heads, int32_t topk, int32_t dv) {

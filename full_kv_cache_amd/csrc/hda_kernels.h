@@ -146,11 +146,16 @@ struct MergeParams {
 constexpr int kSparseDqk = 576;    // key dims (latent + rotary part)
 constexpr int kSparseDv = 512;     // value dims: the leading part of each row
 constexpr int kSparseHeadsPerWave = 16;
-constexpr int kSparseWaves = 4;    // waves per workgroup, each takes 16-key tiles in turn
+#ifndef HDA_SPARSE_WAVES
+#define HDA_SPARSE_WAVES 4
+#endif
+constexpr int kSparseWaves = HDA_SPARSE_WAVES;  // waves per workgroup, each takes 16-key tiles in turn
 
 struct SparseParams {
     const uint16_t *q;          // [T, Hq, Dqk]
-    const uint16_t *kv;         // [pool_rows, Dqk]
+    const uint16_t *kv;         // [pool_rows, Dqk] (bf16 pool)
+    const uint8_t *kv8;         // [pool_rows, Dqk] e4m3 codes (fp8 pool; kv unused), else null
+    const float *kv_scale;      // [pool_rows] fp8 pool: each row's scale
     const int32_t *indices;     // [T, topk]
     const int32_t *topk_length; // [T] or null
     const float *sinks;         // [Hq] or null
@@ -193,7 +198,8 @@ hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 hipError_t launch_rope_append_fp8(const RopeAppendParams &p, hipStream_t stream);
 
 // Grid of (token, key split, 16-head group) workgroups; nsplit == 1 writes
-// out / lse with the sink, otherwise partials and then their merge.
+// out / lse with the sink, otherwise partials and then their merge.  An fp8
+// pool (kv8 / kv_scale set) takes the kernel's fp8 form.
 hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t stream);
 
 // Chunk kernel over grid (nsplit, Hkv, B).  final_out: nsplit must be 1 and

@@ -8,22 +8,41 @@
 //     s_i = scale * q_h . kv[idx_i]                 all Dqk = 576 dims
 //     out_h = sum_i softmax(s)_i kv[idx_i][0:Dv]     Dv = 512 leading dims
 //     lse_h = ln sum_i exp(s_i);  out_h *= 1 / (1 + exp(sink_h - lse_h)).
+// The fp8 form (the same page's `_fp8_flash_mla_kernel`: the cache handed
+// over as bytes) reads e4m3 codes with one fp32 scale per pool row: a row's
+// value is code x scale, for its key and its value dims alike.
 //
 // With 64 query heads per shared row the path does about 121 flop per
 // gathered byte, so both products run on the matrix cores:
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: 16 gathered rows form the A
 //     operand, loaded straight from memory with 16-byte loads (8 dims of a
-//     row per lane); the wave's 16 query heads form the B operand, held in
-//     registers for the whole call;
+//     row per lane; fp8: 8 codes, widened to bf16 exactly); the workgroup's
+//     16 query heads form the B operand, read from LDS (registers hold the
+//     accumulators and the tiles in flight);
 //   * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: the S^T accumulator
 //     already holds P^T in operand layout (4 keys of one head per lane), and
 //     V^T comes out of LDS through the transposing read ds_read_b64_tr_b16
 //     from the rows the wave has just stored there.
+// A wave keeps two tiles of rows in flight behind the one it scores: the
+// next tile's loads are issued as soon as the current tile's registers are
+// stored, before its softmax and P.V.
+// The softmax needs no running rescale: probabilities are taken against a
+// fixed reference m_ref (log2 units), the maximum of each head's first
+// scored tile, so weights 2^(s - m_ref) stay below 2^kSlack as long as no
+// later score exceeds m_ref by more than kSlack (bf16 and fp32 hold such
+// weights as well as ones below 1; the final normalisation divides by the
+// sum taken against the same reference, so the result is the softmax).
+// The 128 accumulator registers are then only ever touched by the matrix
+// cores (a rescale of them in the loop pushed the compiler into spilling).
+// Should a later score exceed the reference by more than that, the wave
+// scores its keys again against the exact maximum, which it tracks.
 // Work split: one workgroup of 4 waves per (token, key split, group of 16
 // heads); the waves take the split's 16-key tiles in turn, each with its own
 // online softmax, and merge in LDS at the end.  The head-group workgroups of
 // one (token, split) get block ids congruent mod 8, so they run on the same
 // XCD and meet the gathered rows in its L2.
+#include <type_traits>
+
 #include "hda_device.h"
 #include "hda_kernels.h"
 
@@ -36,6 +55,9 @@ constexpr int kVChunks = kSparseDv / 32;   // 16-byte chunks of the value part p
 constexpr int kDimTiles = kSparseDv / 16;  // 16-dim output tiles
 constexpr int kVPitch = kSparseDv + 16;    // LDS row pitch of a V tile (bf16)
 constexpr int kOPitch = kSparseDv + 4;     // LDS row pitch of the merge buffer (fp32)
+constexpr int kQPitch = kSparseDqk + 8;    // LDS row pitch of the q block (bf16): reads of 16 heads hit 16 bank groups
+constexpr int kIdxBatch = 16;              // tiles whose row indices a lane holds at once
+constexpr float kSlack = 32.f;             // largest weight 2^32 against the fixed reference
 constexpr float kLn2 = 0.693147180559945309f;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -46,27 +68,58 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Pool row of key kk for this lane, or -1 when the key is masked.
-__device__ __forceinline__ int row_of(const SparseParams &p, const int32_t *idx, int kk, int k1) {
-    if (kk >= k1) return -1;
-    const int r = idx[kk];
-    return (r >= 0 && (int64_t)r < p.pool_rows) ? r : -1;
-}
-
-__device__ __forceinline__ void load_rows(const SparseParams &p, int row, int kg, uint4 *kr) {
-    const uint16_t *src = p.kv + (int64_t)(row < 0 ? 0 : row) * kSparseDqk + 8 * kg;
-#pragma unroll
-    for (int j = 0; j < kKSteps; ++j) kr[j] = ld16(src + 32 * j);
-}
-
 __device__ __forceinline__ short bf16_bits(float f) { return (short)f32_to_bf16(f); }
 
-template <bool FINAL>
-__global__ __launch_bounds__(kSparseWaves * 64) void sparse_decode_kernel(SparseParams p) {
+// One tile's rows for this lane: row `row` (< 0: masked, row 0 is read and
+// the key dropped), dims 32j + 8kg .. +7 for every k-step j; fp8 also the
+// row's scale.
+template <bool F8>
+struct TileRegs {
+    std::conditional_t<F8, uint2, uint4> k[kKSteps];
+    float rs;
+};
+
+template <bool F8>
+__device__ __forceinline__ void load_tile(const SparseParams &p, int row, int kg, TileRegs<F8> &t) {
+    const int64_t r = row < 0 ? 0 : row;
+    if constexpr (F8) {
+        const uint8_t *src = p.kv8 + r * kSparseDqk + 8 * kg;
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) t.k[j] = *reinterpret_cast<const uint2 *>(src + 32 * j);
+        t.rs = p.kv_scale[r];
+    } else {
+        const uint16_t *src = p.kv + r * kSparseDqk + 8 * kg;
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) t.k[j] = ld16(src + 32 * j);
+        t.rs = 1.f;
+    }
+}
+
+template <bool F8>
+__device__ __forceinline__ bf16x8 operand(const TileRegs<F8> &t, int j) {
+    if constexpr (F8)
+        return as_bf16x8(e4m3x8_to_bf16x8(t.k[j]));
+    else
+        return as_bf16x8(t.k[j]);
+}
+
+// Pool row of key kk (< k1 names a list entry; k0 <= kk) for this lane, or
+// -1 when the key is masked.  Branch-free: the entry is read at a clamped
+// position whatever kk is, so that the loads of a batch issue back to back.
+__device__ __forceinline__ int row_of(const SparseParams &p, const int32_t *idx, int kk, int k0, int k1) {
+    const int r = idx[max(min(kk, k1 - 1), k0)];
+    return (kk < k1 && r >= 0 && (int64_t)r < p.pool_rows) ? r : -1;
+}
+
+
+template <bool FINAL, bool F8>
+__global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(SparseParams p) {
+    constexpr int W = kSparseWaves;
     constexpr int kTileBytes = 16 * kVPitch * 2;
-    __shared__ __align__(16) unsigned char s_buf[kSparseWaves * kTileBytes];
-    __shared__ float s_m[kSparseWaves][16], s_l[kSparseWaves][16];
-    static_assert(16 * kOPitch * 4 <= kSparseWaves * kTileBytes, "merge buffer fits the V tiles");
+    __shared__ __align__(16) unsigned char s_buf[W * kTileBytes];
+    __shared__ float s_m[W][16], s_l[W][16];
+    __shared__ __align__(16) uint16_t s_q[16 * kQPitch];
+    static_assert(16 * kOPitch * 4 <= W * kTileBytes, "merge buffer fits the V tiles");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int mrow = lane & 15, kg = lane >> 4;
@@ -80,100 +133,142 @@ __global__ __launch_bounds__(kSparseWaves * 64) void sparse_decode_kernel(Sparse
     len = len < 0 ? 0 : (len > p.topk ? p.topk : len);
     const int k0 = sp * p.split_keys;
     const int k1 = min(k0 + p.split_keys, len);
+    const int ntile = k1 > k0 ? (k1 - k0 + 15) >> 4 : 0;
     const int h0 = g * kSparseHeadsPerWave;
     const int32_t *idx = p.indices + (int64_t)t * p.topk;
 
-    // B operand: lane (head mrow, kg) holds q[t][h0 + mrow][32j + 8kg .. +7]
-    bf16x8 qb[kKSteps];
+    // the workgroup's 16 query rows into LDS, 16 bytes per thread a pass
     {
-        const uint16_t *qr = p.q + ((int64_t)t * Hq + h0 + mrow) * kSparseDqk + 8 * kg;
-#pragma unroll
-        for (int j = 0; j < kKSteps; ++j) qb[j] = as_bf16x8(ld16(qr + 32 * j));
+        const uint16_t *qg = p.q + ((int64_t)t * Hq + h0) * kSparseDqk;
+        constexpr int kChunks = 16 * kSparseDqk / 8;
+        for (int c = tid; c < kChunks; c += W * 64) {
+            const int hr = c / (kSparseDqk / 8), cc = c % (kSparseDqk / 8);
+            *reinterpret_cast<uint4 *>(s_q + hr * kQPitch + 8 * cc) = ld16(qg + (int64_t)hr * kSparseDqk + 8 * cc);
+        }
     }
+    __syncthreads();
+    // B operand: lane (head mrow, kg) reads q[t][h0 + mrow][32j + 8kg .. +7]
+    const uint16_t *qs = s_q + mrow * kQPitch + 8 * kg;
     f32x4 acc[kDimTiles];
 #pragma unroll
     for (int d = 0; d < kDimTiles; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_lane = 0.f;  // head mrow; l over this lane's keys
+    // head mrow: weights are 2^(s - m_ref); l over this lane's keys; m_max
+    // the largest score seen, over in case a score passed m_ref + kSlack
+    float m_ref = -INFINITY, l_lane = 0.f, m_max = -INFINITY;
+    bool over = false;
 
     uint16_t *vt = reinterpret_cast<uint16_t *>(s_buf + wave * kTileBytes);
     const uint16_t *trb = vt + (4 * kg + (mrow >> 2)) * kVPitch + 4 * (mrow & 3);
 
-    int kb = k0 + 16 * wave;
-    int r_cur = row_of(p, idx, kb + mrow, k1);
-    uint4 kr[kKSteps];
-    if (kb < k1) load_rows(p, r_cur, kg, kr);
-    int r_nxt = row_of(p, idx, kb + 16 * kSparseWaves + mrow, k1);
-
-    while (kb < k1) {
+    // One tile: scores, V rows to LDS, then (once `tr`'s registers are
+    // free) the loads of the tile two ahead, the softmax and P.V.
+    auto process = [&](TileRegs<F8> &tr, int row, int row_next2) HDA_INLINE {
         // scores of the tile: lane (head mrow, kg) gets keys 4kg + i
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[j]), qb[j], sc, 0, 0, 0);
-        const uint32_t vmask = (uint32_t)__ballot(r_cur >= 0) & 0xFFFFu;
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(operand<F8>(tr, j),
+                                                         *reinterpret_cast<const bf16x8 *>(qs + 32 * j), sc, 0, 0, 0);
+        const uint32_t vmask = (uint32_t)__ballot(row >= 0) & 0xFFFFu;
         // value part of the rows into this wave's LDS tile; masked rows as 0
         // (a zero weight would not cancel a NaN they might hold)
         {
             uint16_t *dst = vt + mrow * kVPitch + 8 * kg;
-            const bool keep = r_cur >= 0;
+            const bool keep = row >= 0;
 #pragma unroll
             for (int j = 0; j < kVChunks; ++j) {
-                uint4 v = kr[j];
+                uint4 v = __builtin_bit_cast(uint4, operand<F8>(tr, j));
                 if (vmask != 0xFFFFu && !keep) v = make_uint4(0, 0, 0, 0);
                 *reinterpret_cast<uint4 *>(dst + 32 * j) = v;
             }
         }
-        // next tile's rows go in flight while this one is finished
-        const int kn = kb + 16 * kSparseWaves;
-        r_cur = r_nxt;
-        if (kn < k1) load_rows(p, r_cur, kg, kr);
-        r_nxt = row_of(p, idx, kn + 16 * kSparseWaves + mrow, k1);
+        // key 4kg + i's row scale (fp8), from the lane that loaded that row;
+        // 1 for a masked key (the row read in its place may hold anything)
+        float rsk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rsk[i] = 1.f;
+            if constexpr (F8) {
+                const float r = __shfl(tr.rs, 4 * kg + i, 64);
+                if ((vmask >> (4 * kg + i)) & 1u) rsk[i] = r;
+            }
+        }
+        // the tile two ahead goes in flight in these registers (not before:
+        // hoisted above the stores it would need a third tile's registers).
+        // Unconditional -- past the last tile it reads row 0 for nothing --
+        // so that every tile finds the same loads outstanding behind it and
+        // its wait counts stay exact.
+        asm volatile("" ::: "memory");
+        load_tile<F8>(p, row_next2, kg, tr);
 
-        // online softmax (log2 domain) for head mrow over keys 4kg + i
+        // softmax against the fixed reference (log2 domain)
         float s[4], tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = ((vmask >> (4 * kg + i)) & 1u) ? sc[i] * p.scale_log2 : -INFINITY;
+            s[i] = ((vmask >> (4 * kg + i)) & 1u) ? sc[i] * (p.scale_log2 * rsk[i]) : -INFINITY;
             tmax = fmaxf(tmax, s[i]);
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.f;
-        v4i16 pb;
-        if (m_new == -INFINITY) {  // nothing valid yet
-            pb = v4i16{0, 0, 0, 0};
-        } else {
-            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float ps = 0.f, pv[4];
+        m_max = fmaxf(m_max, tmax);
+        if (m_ref == -INFINITY) m_ref = tmax;  // first keys: nothing accumulated yet
+        over |= tmax > m_ref + kSlack;
+        const float mr = m_ref == -INFINITY ? 0.f : m_ref;  // -inf: this head has no key yet
+        float pv[4], ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pv[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-                ps += pv[i];
-            }
-            l_lane = fmaf(l_lane, alpha, ps);
-            pb = v4i16{bf16_bits(pv[0]), bf16_bits(pv[1]), bf16_bits(pv[2]), bf16_bits(pv[3])};
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = __builtin_amdgcn_exp2f(s[i] - mr);
+            ps += pv[i];
         }
-        m_run = m_new;
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int d = 0; d < kDimTiles; ++d) acc[d] *= alpha;
-        }
+        l_lane += ps;
+        const v4i16 pb = {bf16_bits(pv[0] * rsk[0]), bf16_bits(pv[1] * rsk[1]), bf16_bits(pv[2] * rsk[2]),
+                          bf16_bits(pv[3] * rsk[3])};
         wave_lds_fence();  // the tile's rows are in LDS
 #pragma unroll
         for (int d = 0; d < kDimTiles; ++d) {
             const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(trb + 16 * d));
             acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[d], 0, 0, 0);
         }
-        wave_lds_fence();  // reads done before the next tile is stored
-        kb = kn;
+        // The next tile's stores follow these reads in this wave's LDS
+        // queue, which runs in order; keep the compiler from moving them.
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // this wave's tiles: wave, wave + W, ...; row indices a batch at a time
+    TileRegs<F8> ta, tb;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int base = wave; base < ntile; base += W * kIdxBatch) {
+            int rows[kIdxBatch];
+#pragma unroll
+            for (int i = 0; i < kIdxBatch; ++i) rows[i] = row_of(p, idx, k0 + 16 * (base + W * i) + mrow, k0, k1);
+            const int nt = min(kIdxBatch, (ntile - base + W - 1) / W);  // this batch's tiles (>= 1)
+            // Unrolled over the batch: loads stay in flight from one tile to
+            // the next, and the compiler places exact waits only in straight
+            // code (across a loop's back edge it waited for every load).
+            load_tile<F8>(p, rows[0], kg, ta);
+            load_tile<F8>(p, rows[1], kg, tb);
+#pragma unroll
+            for (int i = 0; i < kIdxBatch; i += 2) {
+                if (i >= nt) break;  // an odd count ends on a tile of masked keys
+                process(ta, rows[i], i + 2 < kIdxBatch ? rows[i + 2] : -1);
+                process(tb, rows[i + 1], i + 3 < kIdxBatch ? rows[i + 3] : -1);
+            }
+        }
+        if (!__ballot(over)) break;
+        // a score passed the reference by more than kSlack: start over
+        // against the exact maximum (weights <= 1)
+#pragma unroll
+        for (int d = 0; d < kDimTiles; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_lane = 0.f;
+        m_ref = m_max;
+        over = false;
     }
 
     // merge the 4 waves: o = sum_w 2^(m_w - M) o_w, l likewise
     float l_w = l_lane + __shfl_xor(l_lane, 16, 64);
     l_w += __shfl_xor(l_w, 32, 64);
     if (kg == 0) {
-        s_m[wave][mrow] = m_run;
+        s_m[wave][mrow] = m_ref;
         s_l[wave][mrow] = l_w;
     }
     __syncthreads();  // also: every wave is done with its V tile
@@ -181,10 +276,10 @@ __global__ __launch_bounds__(kSparseWaves * 64) void sparse_decode_kernel(Sparse
     {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kSparseWaves; ++w) M = fmaxf(M, s_m[w][mrow]);
-        const float c = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][mrow]);
+        const float c = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
 #pragma unroll
-        for (int w = 0; w < kSparseWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             if (wave == w) {
 #pragma unroll
                 for (int d = 0; d < kDimTiles; ++d) {
@@ -205,11 +300,11 @@ __global__ __launch_bounds__(kSparseWaves * 64) void sparse_decode_kernel(Sparse
     const int n = tid >> 4, c32 = (tid & 15) * 32;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSparseWaves; ++w) M = fmaxf(M, s_m[w][n]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][n]);
     float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < kSparseWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             const float mw = s_m[w][n];
             if (mw != -INFINITY) L += __builtin_amdgcn_exp2f(mw - M) * s_l[w][n];
         }
@@ -275,24 +370,29 @@ __global__ __launch_bounds__(128) void sparse_merge_kernel(SparseParams p) {
     if (threadIdx.x == 0 && p.lse) p.lse[(int64_t)t * p.num_q_heads + hq] = lse;
 }
 
-}  // namespace
-
-hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t s) {
+template <bool F8>
+hipError_t launch_sparse(const SparseParams &p, hipStream_t s) {
     const int groups = p.num_q_heads / kSparseHeadsPerWave;
     const int64_t units = (int64_t)p.tokens * p.nsplit;
     const int64_t blocks = (units + 7) / 8 * 8 * groups;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL(sparse_decode_kernel<true>, dim3((unsigned)blocks), dim3(kSparseWaves * 64), 0,
-                           s, p);
+        hipLaunchKernelGGL((sparse_decode_kernel<true, F8>), dim3((unsigned)blocks), dim3(kSparseWaves * 64),
+                           0, s, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(sparse_decode_kernel<false>, dim3((unsigned)blocks), dim3(kSparseWaves * 64), 0, s,
-                       p);
+    hipLaunchKernelGGL((sparse_decode_kernel<false, F8>), dim3((unsigned)blocks), dim3(kSparseWaves * 64), 0,
+                       s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sparse_merge_kernel, dim3((unsigned)((int64_t)p.tokens * p.num_q_heads)),
                        dim3(kSparseDv / 4), 0, s, p);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t s) {
+    return p.kv8 ? launch_sparse<true>(p, s) : launch_sparse<false>(p, s);
 }
 
 }  // namespace hda

@@ -437,6 +437,28 @@ hda_status hda_sparse_decode_attn(const void *q, const void *kv, int64_t pool_ro
                                   void *out, float *lse, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/*
+ * hda_sparse_decode_attn_fp8 -- hda_sparse_decode_attn over an fp8 latent
+ * pool (flashmla_sparse page, `_fp8_flash_mla_kernel`: the cache handed to
+ * the kernel as bytes, `head_dim_v` 512, top-k indices, the sink).  The page
+ * names its fp8 layout without printing it; the reading taken is the one of
+ * the fp8 decode cache above: e4m3 codes (bias 7, largest finite 448,
+ * S.1111.111 NaN) with one fp32 scale per pool row, so the value of element
+ * d of row r is decode(kv_codes[r][d]) * kv_scales[r] for its key dims and
+ * its leading dv value dims alike.  Everything else -- indices, skipped
+ * entries, the softmax, lse, the sink, the workspace -- as
+ * hda_sparse_decode_attn (there is no topk_length: -1 padding ends a row).
+ *
+ *   kv_codes   uint8 [pool_rows, dqk], 16-byte aligned
+ *   kv_scales  fp32 [pool_rows]
+ * Errors: as hda_sparse_decode_attn.  The pool and indices are only read.
+ */
+hda_status hda_sparse_decode_attn_fp8(const void *q, const uint8_t *kv_codes, const float *kv_scales,
+                                      int64_t pool_rows, const int32_t *indices, int32_t tokens,
+                                      int32_t topk, int32_t num_q_heads, int32_t dqk, int32_t dv,
+                                      const float *sinks, float scale, void *out, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hda_status_string(hda_status status);
 

@@ -128,3 +128,113 @@ def test_sparse_headline_shape_all():
     ref, rlse = _ref(h, sinks=sinks)
     assert_attn_close(out, ref)
     np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+# ------------------------------------------------------------ fp8 pool
+# hda_sparse_decode_attn_fp8: e4m3 codes with one fp32 scale per pool row
+# (the reading of the flashmla_sparse page's fp8 call), against the oracle's
+# fp8 sparse decode; rows no index names hold NaN codes and NaN scales.
+
+NAN8 = 0x7F
+
+
+def _case8(seed, T, H, pool, topk, poison=True):
+    h = _case(seed, T, H, pool, topk, poison=False)
+    g = workloads.generator(seed + 1)
+    h["codes"] = workloads.fp8_codes(g, (pool, 576)).numpy()
+    h["scales"] = workloads.fp8_scales(g, (pool,)).numpy()
+    if poison:
+        used = np.zeros(pool, bool)
+        used[h["indices"][h["indices"] >= 0]] = True
+        h["codes"][~used] = NAN8
+        h["scales"][~used] = np.nan
+    return h
+
+
+def _gpu8(h, sinks=None, scale=1 / 24):
+    import full_kv_cache_amd as hda
+    T, H, _ = h["q"].shape
+    topk = h["indices"].shape[1]
+    q = workloads.from_bits(h["q"]).cuda()
+    codes = torch.from_numpy(h["codes"]).cuda()
+    scales = torch.from_numpy(h["scales"]).cuda()
+    idx = torch.from_numpy(h["indices"]).cuda()
+    sk = None if sinks is None else torch.from_numpy(np.asarray(sinks, np.float32)).cuda()
+    out = torch.full((T, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = hda.hda_sparse_workspace_bytes(T, H, topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+    hda.hda_sparse_decode_attn_fp8(q, codes, scales, idx, sk, scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _ref8(h, sinks=None, scale=1 / 24):
+    return oracle.sparse_decode_attn_fp8(h["q"], h["codes"], h["scales"], h["indices"], sinks, scale, 512)
+
+
+@pytest.mark.parametrize("T,H,pool,topk", [(4, 64, 4096, 512), (3, 16, 1000, 100), (2, 128, 2048, 300),
+                                           (1, 64, 600, 17)])
+def test_sparse_fp8_parity(T, H, pool, topk):
+    _print_case(test="sparse_fp8", T=T, H=H, pool=pool, topk=topk)
+    h = _case8(30 + T + H, T, H, pool, topk)
+    h["indices"][0, topk // 2] = -1   # padding inside the list
+    _, lse0 = _ref8(h)
+    g = np.random.default_rng(T + H)
+    sinks = (lse0.mean(0) + g.normal(0, 2.0, H)).astype(np.float32)
+    ref, rlse = _ref8(h, sinks=sinks)
+    out, lse = _gpu8(h, sinks=sinks)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+    o_none, _ = _gpu8(h)
+    o_ninf, _ = _gpu8(h, sinks=np.full(H, -np.inf, np.float32))
+    assert torch.equal(o_none.view(torch.int16), o_ninf.view(torch.int16))
+
+
+def test_sparse_fp8_headline_shape_all():
+    """32 tokens x 64 heads, pool 32768, top-2048 (the launch the bench
+    times), sinks drawn near lse; every token against the oracle."""
+    _print_case(test="sparse_fp8_headline")
+    h = _case8(40, 32, 64, 32768, 2048, poison=False)
+    _, lse0 = _ref8(h)
+    g = np.random.default_rng(40)
+    sinks = (lse0.mean(0) + g.normal(0, 2.0, 64)).astype(np.float32)
+    out, lse = _gpu8(h, sinks=sinks)
+    ref, rlse = _ref8(h, sinks=sinks)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_sparse_late_large_score(fp8):
+    """A key far into the list scoring ~46 above the first tile's maximum
+    for one head (more than the 2^32 weight slack against the kernel's
+    fixed softmax reference): the wave scores its keys again against the
+    exact maximum; results as the oracle's."""
+    _print_case(test="sparse_late_large", fp8=fp8)
+    # 64 tokens x 4 head groups: no key split, so list position 900 is tile
+    # 56 of its token, the 15th tile of the wave that scores it
+    T, H, pool, topk = 64, 64, 4096, 1024
+    h = _case(50, T, H, pool, topk, poison=False)
+    qrow = oracle.bf16_to_f64(h["q"][0, 5])
+    big = int(h["indices"][0, 900])
+    h["kv"][big] = workloads.bits(torch.from_numpy(2.0 * qrow).to(torch.bfloat16))
+    if fp8:
+        codes, scales = oracle.quant_rows(h["kv"])
+        h["codes"], h["scales"] = codes, scales
+        ref, rlse = _ref8(h)
+        out, lse = _gpu8(h)
+    else:
+        ref, rlse = _ref(h)
+        out, lse = _gpu(h)
+    assert rlse[0, 5] > 40
+    # head 5 of token 0 is that row's value (2 q, entries up to ~8): its
+    # bf16 roundings (the weight times the row scale, out itself) are
+    # relative, so the bound scales with |out| there
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= 1e-2 * np.maximum(1.0, np.abs(ref)))
+    rest = np.ones(ref.shape[:2], bool)
+    rest[0, 5] = False
+    assert_attn_close(out[torch.from_numpy(rest)], ref[rest])
+    np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
