@@ -317,11 +317,12 @@ def hda_decode_multi_workspace_bytes(cache: LayerCache, layer_type: int, tokens:
 def hda_decode_multi(q, k_new, v_new, pos, layer_type: int, cache: LayerCache, sinks,
                      scale: float, out, lse=None, stream=None, gate=None, max_seq_len=None,
                      workspace=None):
-    """Decode of a chunk of T new tokens per sequence: q [B, T, Hq, D] and
-    k_new [B, T, Hkv, D] are rotated in place, v_new [B, T, Hkv, D] is read;
-    out [B, T, Hq, D], lse [B, T, Hq]; gate: optional fp32 [B, T, Hq] logits.
-    max_seq_len: host bound on pos + T (default: the cache capacity);
-    workspace: hda_decode_multi_workspace_bytes() bytes of device memory."""
+    """Decode of a chunk of T (<= 512) new tokens per sequence: q [B, T, Hq, D]
+    is rotated in place (as hda_rope_append does); k_new and v_new
+    [B, T, Hkv, D] are only read; out [B, T, Hq, D], lse [B, T, Hq]; gate:
+    optional fp32 [B, T, Hq] logits.  max_seq_len: host bound on pos + T
+    (default: the cache capacity); workspace: hda_decode_multi_workspace_bytes()
+    bytes of device memory (it holds the rotated new K)."""
     if q.dim() != 4:
         raise ValueError("q must be [B, T, Hq, D]")
     validate_sinks(sinks, q[:, 0])

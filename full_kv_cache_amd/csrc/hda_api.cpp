@@ -776,13 +776,13 @@ hda_status check_multi_shape(const hda_cache_desc *c, int layer, int32_t tokens,
     const int g = c->num_q_heads / c->num_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
         return fail(HDA_ERR_UNSUPPORTED, "query group size %d not in {1,2,4,8,16}", g);
-    if (tokens < 1 || tokens > 4 || g * tokens > 16)
-        return fail(HDA_ERR_UNSUPPORTED, "a chunk holds 1..4 tokens with tokens x group <= 16 "
-                    "query rows, got %d tokens for group %d", tokens, g);
+    if (tokens < 1 || tokens > hda::kMultiMaxTokens)
+        return fail(HDA_ERR_UNSUPPORTED, "a chunk holds 1..%d tokens, got %d", hda::kMultiMaxTokens, tokens);
     if (c->rotary_dim % 16)
         return fail(HDA_ERR_UNSUPPORTED, "rotary_dim %d is not a multiple of 16", c->rotary_dim);
-    if (c->capacity < 16)
-        return fail(HDA_ERR_UNSUPPORTED, "decode kernels need a cache of at least 16 rows");
+    if (c->capacity < 16 || (g * tokens > 16 && c->capacity < 32))
+        return fail(HDA_ERR_UNSUPPORTED, "chunk decode needs a cache of at least %d rows",
+                    g * tokens > 16 ? 32 : 16);
     if (c->block_table || c->kv_dtype != HDA_KV_BF16)
         return fail(HDA_ERR_UNSUPPORTED, "chunk decode is built for contiguous bf16 caches");
     if (max_seq_len < 1)
@@ -798,6 +798,7 @@ hda_status check_multi_shape(const hda_cache_desc *c, int layer, int32_t tokens,
 // at least 16 rounds (8 with few pairs).  max_seq_len bounds pos + tokens; it only sizes the
 // split (every workgroup takes its share of the rounds the sequence has).
 int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_seq_len) {
+    if ((c->num_q_heads / c->num_kv_heads) * tokens > 16) return 1;  // the prefill kernel: no split
     int64_t n_old = (int64_t)max_seq_len - tokens;
     if (n_old < 0) n_old = 0;
     const int64_t lim = layer == HDA_SLIDING ? (int64_t)c->window - 1 : c->capacity;
@@ -813,11 +814,17 @@ int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_
     return s < 1 ? 1 : (int)s;
 }
 
+// Chunk-decode workspace: the rotated new K rows (bf16 [B, T, Hkv, D]),
+// then, for a split, each part's partial o [rows, D] and lse [rows].
+size_t multi_krot_bytes(const hda_cache_desc *c, int32_t tokens) {
+    return up256((size_t)c->batch * tokens * c->num_kv_heads * hda::kHeadDim * sizeof(uint16_t));
+}
 size_t multi_workspace(const hda_cache_desc *c, int split, int32_t tokens) {
-    if (split <= 1) return 0;
+    size_t bytes = multi_krot_bytes(c, tokens);
+    if (split <= 1) return bytes;
     const size_t rows = (size_t)c->batch * c->num_kv_heads * split * tokens *
                         (c->num_q_heads / c->num_kv_heads);
-    return up256(rows * hda::kHeadDim * sizeof(float)) + rows * sizeof(float);
+    return bytes + up256(rows * hda::kHeadDim * sizeof(float)) + rows * sizeof(float);
 }
 
 }  // namespace
@@ -828,7 +835,7 @@ size_t hda_decode_multi_workspace_bytes(const hda_cache_desc *cache, hda_layer_t
     return multi_workspace(cache, multi_split(cache, layer, tokens, max_seq_len), tokens);
 }
 
-hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32_t *pos,
+hda_status hda_decode_multi(void *q, const void *k_new, const void *v_new, const int32_t *pos,
                             int32_t tokens, hda_layer_type layer, const hda_cache_desc *cache,
                             const float *sinks, const float *gate, float scale, void *out,
                             float *lse, int32_t max_seq_len, void *workspace,
@@ -847,22 +854,24 @@ hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32
     const int g = cache->num_q_heads / cache->num_kv_heads;
     const int split = multi_split(cache, layer, tokens, max_seq_len);
     const size_t need = multi_workspace(cache, split, tokens);
-    if (need && (!workspace || workspace_bytes < need))
+    if (cache->batch == 0) return ok();
+    if (!workspace || workspace_bytes < need)
         return fail(HDA_ERR_WORKSPACE, "chunk decode needs a %zu-byte workspace, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
-    if (need && !aligned16(workspace))
+    if (!aligned16(workspace))
         return fail(HDA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-    if (cache->batch == 0) return ok();
     hda::MultiParams p{};
     p.split = split;
-    if (need) {
+    char *ws = static_cast<char *>(workspace);
+    p.k_rot = reinterpret_cast<uint16_t *>(ws);
+    if (split > 1) {
         const size_t rows = (size_t)cache->batch * cache->num_kv_heads * split * tokens * g;
-        p.part_o = static_cast<float *>(workspace);
-        p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+        p.part_o = reinterpret_cast<float *>(ws + multi_krot_bytes(cache, tokens));
+        p.part_lse = reinterpret_cast<float *>(ws + multi_krot_bytes(cache, tokens) +
                                                up256(rows * hda::kHeadDim * sizeof(float)));
     }
     p.q = static_cast<uint16_t *>(q);
-    p.k_new = static_cast<uint16_t *>(k_new);
+    p.k_new = static_cast<const uint16_t *>(k_new);
     p.v_new = static_cast<const uint16_t *>(v_new);
     p.pos = pos;
     p.k = static_cast<uint16_t *>(cache->k);

@@ -170,10 +170,13 @@ struct SparseParams {
 };
 
 // Decode of a chunk of `tokens` new tokens per sequence (q [B, T, Hq, D],
-// k_new / v_new [B, T, Hkv, D]; contiguous bf16 cache).
+// k_new / v_new [B, T, Hkv, D]; contiguous bf16 cache; tokens <= 512).
+constexpr int kMultiMaxTokens = 512;  // a chunk's tokens: the window never drops a chunk key
+
 struct MultiParams {
     uint16_t *q;                // rotated in place
-    uint16_t *k_new;            // rotated in place
+    const uint16_t *k_new;      // read only
+    uint16_t *k_rot;            // [B, T, Hkv, D] workspace: the rotated new K
     const uint16_t *v_new;
     const int32_t *pos;         // [B] position of token 0
     uint16_t *k, *v;            // [B, Hkv, cap, D]

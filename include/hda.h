@@ -348,14 +348,17 @@ hda_status hda_decode_step_noalloc(const void *q, const void *k_new, const void 
 
 /*
  * hda_decode_multi -- decode of a chunk of `tokens` new tokens per sequence
- * in one call.  Spark export page, `SparkStepConfig.cache_len` docstring: a
- * ring holds a window's previous entries and the new token is scored with
- * them; for a chunk, token t (position pos[b] + t) attends to the entries
- * of its own window -- the cached ones and new tokens 0..t -- exactly as
- * `tokens` single-token steps (hda_rope_append + hda_decode_attn with
- * seq_len pos + t + 1) in order would, and the cache ends as they leave it.
+ * in one call, up to a prefill chunk of 512.  Spark export page,
+ * `SparkStepConfig.cache_len` docstring: a ring holds a window's previous
+ * entries and the new token is scored with them; for a chunk, token t
+ * (position pos[b] + t) attends to the entries of its own window -- the
+ * cached ones and new tokens 0..t -- exactly as `tokens` single-token steps
+ * (hda_rope_append + hda_decode_attn with seq_len pos + t + 1) in order
+ * would, and the cache ends as they leave it.
  *   q       bf16 [batch, tokens, num_q_heads, head_dim], rotated in place
- *   k_new   bf16 [batch, tokens, num_kv_heads, head_dim], rotated in place
+ *           (as hda_rope_append rotates it)
+ *   k_new   bf16 [batch, tokens, num_kv_heads, head_dim], read only (its
+ *           rotation goes to the workspace and the cache)
  *   v_new   bf16 [batch, tokens, num_kv_heads, head_dim], read only
  *   pos     int32 [batch] (device): position of token 0; a negative value
  *           leaves the sequence's cache alone and its out 0, lse -inf
@@ -364,19 +367,22 @@ hda_status hda_decode_step_noalloc(const void *q, const void *k_new, const void 
  *   sinks   fp32 [num_q_heads] or NULL; gate fp32 [batch, tokens,
  *           num_q_heads] logits or NULL (as in hda_decode_attn)
  *   max_seq_len host bound on pos + tokens (sizes how many workgroups share
- *           each sequence's keys; results do not depend on it)
+ *           each sequence's keys for small chunks; results do not depend on it)
  *   workspace  device buffer of at least hda_decode_multi_workspace_bytes()
- *           (NULL when that is 0); calls sharing one must be ordered on one
- *           stream
+ *           (the rotated new K rows, and partials when the keys are split);
+ *           calls sharing one must be ordered on one stream
  * The cache is read as it was before the chunk and written after the
- * attention (full: rows pos + t below capacity; sliding: ring slots, the
- * evicted-entry row taking what the last token's slot held).  Errors: as
- * hda_decode_attn, plus UNSUPPORTED for tokens outside 1..4 or tokens x
- * (num_q_heads / num_kv_heads) > 16, rotary_dim not a multiple of 16, a
- * paged or fp8 cache; INVALID_ARGUMENT for max_seq_len < 1; WORKSPACE for a
- * missing or short workspace.  batch == 0 is a no-op.
+ * attention (full: rows pos + t below capacity; sliding: the ring slots of
+ * the last window-1 tokens, the evicted-entry row taking the entry of
+ * position pos + tokens - window).  Chunks of more than 16 query rows per
+ * KV head (tokens x num_q_heads / num_kv_heads) run the prefill kernel:
+ * both attention products on the matrix cores.  Errors: as hda_decode_attn,
+ * plus UNSUPPORTED for tokens outside 1..512, rotary_dim not a multiple of
+ * 16, a cache of fewer than 16 rows (32 for the prefill kernel), a paged or
+ * fp8 cache; INVALID_ARGUMENT for max_seq_len < 1; WORKSPACE for a missing
+ * or short workspace.  batch == 0 is a no-op.
  */
-hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32_t *pos,
+hda_status hda_decode_multi(void *q, const void *k_new, const void *v_new, const int32_t *pos,
                             int32_t tokens, hda_layer_type layer, const hda_cache_desc *cache,
                             const float *sinks, const float *gate, float scale, void *out,
                             float *lse, int32_t max_seq_len, void *workspace,
@@ -384,8 +390,8 @@ hda_status hda_decode_multi(void *q, void *k_new, const void *v_new, const int32
 
 /*
  * hda_decode_multi_workspace_bytes -- device workspace hda_decode_multi
- * needs for this cache, layer type, chunk size and max_seq_len (0: none, or
- * an invalid description).
+ * needs for this cache, layer type, chunk size and max_seq_len (0 for an
+ * invalid description).
  */
 size_t hda_decode_multi_workspace_bytes(const hda_cache_desc *cache, hda_layer_type layer,
                                         int32_t tokens, int32_t max_seq_len);

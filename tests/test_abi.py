@@ -396,11 +396,15 @@ def _multi(desc, tokens=2, layer=hda.SLIDING, q=FAKE, pos=FAKE, scale=0.0625, ms
 
 
 def test_multi_checks():
-    """Chunk decode: 1..4 tokens with tokens x group <= 16 rows, contiguous
-    bf16 caches, the usual pointer and shape checks."""
+    """Chunk decode: 1..512 tokens, a cache of at least 16 rows (32 for
+    chunks of more than 16 query rows per KV head), contiguous bf16 caches,
+    the usual pointer and shape checks."""
     assert _multi(_desc(), tokens=0) == 2 and "tokens" in _msg()
-    assert _multi(_desc(), tokens=5) == 2
-    assert _multi(_desc(num_q_heads=32, num_kv_heads=2), tokens=2) == 2  # 16 x 2 rows
+    assert _multi(_desc(), tokens=513) == 2 and "512" in _msg()
+    assert _multi(_desc(), tokens=512) == 3  # accepted: only the workspace is missing
+    tiny = _desc(capacity=16, rotary_dim=64, rope_theta=5e6)
+    assert _multi(tiny, layer=hda.FULL, tokens=4, msl=16) == 3
+    assert _multi(tiny, layer=hda.FULL, tokens=5, msl=16) == 2 and "32 rows" in _msg()
     assert _multi(_desc(), q=0) == 1
     assert _multi(_desc(), pos=FAKE + 2) == 1 and "aligned" in _msg()
     assert _multi(_desc(), scale=0.0) == 1
@@ -413,18 +417,20 @@ def test_multi_checks():
 
 
 def test_multi_workspace():
-    """Short contexts need no workspace (one workgroup per sequence and KV
-    head); long ones split each pair's keys over several workgroups, whose
-    partials (fp32 out + lse per query row) live in the workspace."""
+    """The workspace holds the rotated new K rows (bf16 [B, T, Hkv, D]);
+    long contexts also split each pair's keys over several workgroups, whose
+    partials (fp32 out + lse per query row) follow.  Prefill-sized chunks
+    (more than 16 query rows per KV head) are never split."""
     L = hda.lib()
     full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
-    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 2, 20) == 0
+    krot = lambda T: (2 * T * 2 * 256 * 2 + 255) // 256 * 256
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 2, 20) == krot(2)
     need = L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 2, 4096)
     # 4 pairs: 128 / 4 = 32 workgroups wanted and 256 rounds allow 32 (8 rounds each);
     # partial rows = pairs x 32 x (2 tokens x 4 heads)
     rows = 2 * 2 * 32 * 2 * 4
-    assert need == (rows * 256 * 4 + 255) // 256 * 256 + rows * 4
+    assert need == krot(2) + (rows * 256 * 4 + 255) // 256 * 256 + rows * 4
     assert _multi(full, layer=hda.FULL, msl=4096) == 3 and "workspace" in _msg()
     assert _multi(full, layer=hda.FULL, msl=4096, ws=FAKE, wsb=need - 1) == 3
     assert _multi(full, layer=hda.FULL, msl=4096, ws=FAKE + 4, wsb=need) == 1
-    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 4096) == 0
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 4096) == krot(5)
