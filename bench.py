@@ -37,7 +37,13 @@ cache -- e4m3 codes with one fp32 scale per row, quantized on append, the
 reading of that page's fp8 call -- in "fp8"; and chunks of 4 new tokens
 per sequence through hda_decode_multi on every layer (Spark export page,
 `SparkStepConfig.cache_len` docstring: each token attends to its own
-window) in "multi".
+window) in "multi"; chunked prefill of 256 tokens into the first 8
+sequences' caches on every layer (the prefill kernel: both products on the
+matrix cores) in "prefill"; the batch-1 28-layer step at context 4096 in
+"step28" and the batch-16 step at context 32768 in "long" (graph and eager,
+with their layer kernels' rooflines).  Step times are the median of 5
+windows of the timed steps; the line also records the device, ROCm version,
+clocks and host CPU model.
 
     python bench.py [--steps K] [--warmup W] [--config throughput|step28|long|tiny]
                     [--path auto|fused|separate]
@@ -93,6 +99,12 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache measurement")
     ap.add_argument("--multi-tokens", type=int, default=4,
                     help="tokens per chunk of the chunk-decode measurement (0: skip it)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the batch-1 and 16 x 32k step measurements")
+    ap.add_argument("--prefill-tokens", type=int, default=256,
+                    help="tokens per chunk of the chunked-prefill measurement (0: skip it)")
+    ap.add_argument("--prefill-batch", type=int, default=8,
+                    help="sequences of the chunked-prefill measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of this many MB (PMC byte calibration)")
     return ap.parse_args()
@@ -218,6 +230,50 @@ class Workload:
         self.multi_rows = {lt: int((old.clamp(max=s.window - 1) if lt == workloads.SLIDING else old).sum()
                                    + B * T) for lt in (workloads.SLIDING, workloads.FULL)}
 
+    def make_prefill(self, B, T, seed):
+        """Prefill chunks: the first B sequences of the batch, T new tokens
+        each ending at the sequence's length (token 0 at seq_len - T), on
+        every layer's cache (its first B blocks: a view, so the chunk
+        appends where those sequences' rows are)."""
+        import torch
+        import workloads
+        import full_kv_cache_amd as hda
+        s = self.shape
+        dev = self.seq_lens.device
+        g = workloads.generator(seed + 6, dev)
+        self.pf_B, self.pf_T = B, T
+        self.pf_pos = (self.seq_lens[:B] - T).clamp(min=0).to(torch.int32).contiguous()
+        for L in self.layers:
+            L["pq"] = workloads.randn_bf16(g, (B, T, s.num_q_heads, s.head_dim), dev)
+            L["pk"] = workloads.randn_bf16(g, (B, T, s.num_kv_heads, s.head_dim), dev)
+            L["pv"] = workloads.randn_bf16(g, (B, T, s.num_kv_heads, s.head_dim), dev)
+            L["pout"] = torch.empty(B, T, s.num_q_heads, s.head_dim, dtype=torch.bfloat16, device=dev)
+            c = L["cache"]
+            L["pcache_b"] = hda.LayerCache(c.k[:B], c.v[:B], s.num_q_heads, s.window, c.rotary_dim,
+                                           c.rope_theta)
+        need = max(hda.hda_decode_multi_workspace_bytes(L["pcache_b"], L["lt"], T, self.max_seq_len)
+                   for L in self.layers)
+        self.pf_ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        old = self.pf_pos.cpu().long()
+        # attended keys: token t sees its cached window entries plus tokens 0..t
+        G = s.num_q_heads // s.num_kv_heads
+        keys = {}
+        for lt in (workloads.SLIDING, workloads.FULL):
+            n = 0
+            for p0 in old.tolist():
+                for t in range(T):
+                    cached = min(p0, s.window - 1 - t) if lt == workloads.SLIDING else p0
+                    n += max(cached, 0) + t + 1
+            keys[lt] = n
+        self.pf_flops = sum(keys[L["lt"]] for L in self.layers) * s.num_kv_heads * G * s.head_dim * 4
+        self.pf_rows = sum((old.clamp(max=s.window - 1) if L["lt"] == workloads.SLIDING else old).sum().item()
+                           + B * T for L in self.layers)
+
+    def prefill_call(self, L):
+        import full_kv_cache_amd as hda
+        hda.hda_decode_multi(L["pq"], L["pk"], L["pv"], self.pf_pos, L["lt"], L["pcache_b"], L["sinks"],
+                             self.scale, L["pout"], max_seq_len=self.max_seq_len, workspace=self.pf_ws)
+
     def multi_call(self, L):
         import full_kv_cache_amd as hda
         hda.hda_decode_multi(L["mq"], L["mk"], L["mv"], self.multi_pos, L["lt"], L["cache"],
@@ -264,8 +320,12 @@ class Workload:
             self.layer_call(L, path, chunk_keys, gate, paged)
 
 
-def time_graph(fn, steps, warmup, use_graph=True):
-    """Average ms per call of fn over `steps` runs, HIP events on the stream."""
+def time_graph(fn, steps, warmup, use_graph=True, windows=5):
+    """Milliseconds per call of fn: `steps` runs split into up to `windows`
+    consecutive windows with HIP events on the stream at every boundary
+    (no synchronisation between windows), the median window's per-call
+    time.  Also returns the host wall clock per call over all steps and the
+    per-window times."""
     import torch
     if use_graph:
         g = torch.cuda.CUDAGraph()
@@ -279,16 +339,22 @@ def time_graph(fn, steps, warmup, use_graph=True):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    nw = max(1, min(windows, steps))
+    sizes = [steps // nw + (1 if i < steps % nw else 0) for i in range(nw)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nw + 1)]
     wall = time.perf_counter()
-    t0.record()
-    for _ in range(steps):
-        run()
-    t1.record()
+    ev[0].record()
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            run()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall
-    return t0.elapsed_time(t1) / steps, wall * 1e3 / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) / n for i, n in enumerate(sizes))
+    median = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
+    time_graph.last_windows = [round(x, 4) for x in per]
+    time_graph.last_mean = ev[0].elapsed_time(ev[-1]) / steps
+    return median, wall * 1e3 / steps
 
 
 def layer_path(path, lt):
@@ -461,6 +527,73 @@ def sparse_kernel(steps, warmup, seed, pools=8, fp8=False):
     }
 
 
+def device_info():
+    """Device name, architecture, ROCm/HIP version and current clocks (as
+    rocm-smi prints them, when it is there) and the host CPU model."""
+    import subprocess
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"device": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip,
+            "torch": torch.__version__, "cpu_model": cpu_model()}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        clk = json.loads(r.stdout) if r.returncode == 0 else {}
+        card = next(iter(clk.values()), {}) if clk else {}
+        info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()} or None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        info["clocks"] = None
+    return info
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def other_config(name, args):
+    """Step time of another configuration on its own workload: graph and
+    eager timing of the whole 28-layer step, KV GB/s and tokens/s, and the
+    full-layer kernel's roofline entry."""
+    import torch
+    import workloads
+    cfg = CONFIGS[name]
+    print(f"# timing {name}: {cfg['desc']}", file=sys.stderr, flush=True)
+    wl = Workload(cfg, args.seed)
+    torch.cuda.synchronize()
+    step = lambda: wl.step(args.path, args.chunk_keys)
+    ms, _ = time_graph(step, args.steps, args.warmup)
+    win = time_graph.last_windows
+    eager, _ = time_graph(step, max(5, args.steps // 5), 2, use_graph=False)
+    gbs = wl.kv_bytes / (ms / 1e3) / 1e9
+    sl = wl.seq_lens.cpu()
+    rec = {"workload": f"{name}: {cfg['desc']}", "batch": cfg["batch"],
+           "seq_len_min": int(sl.min()), "seq_len_max": int(sl.max()),
+           "ms_per_step": round(ms, 4), "window_ms_per_step": win,
+           "eager_ms_per_step": round(eager, 4), "tokens_per_s": round(cfg["batch"] / (ms / 1e3), 1),
+           "kv_bytes_per_step": wl.kv_bytes, "GB/s": round(gbs, 1),
+           "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "layer_kernels": {
+               "sliding": layer_kernel(wl, workloads.SLIDING, args.steps, args.warmup, args.path,
+                                       args.chunk_keys),
+               "full": layer_kernel(wl, workloads.FULL, args.steps, args.warmup, args.path,
+                                    args.chunk_keys)}}
+    del wl
+    torch.cuda.empty_cache()
+    return rec
+
+
 def cpu_baseline(wl: Workload, min_seconds: float):
     """The oracle on host copies of the same workload: whole 28-layer steps
     over the batch (append + attention per layer), repeated until at least
@@ -499,7 +632,7 @@ def cpu_baseline(wl: Workload, min_seconds: float):
     return {
         "value": round(wl.kv_bytes * steps / el / 1e9, 3), "unit": "GB/s",
         "tokens_per_s": round(s.batch * steps / el, 2),
-        "cores": oracle.num_threads(), "kind": "oracle",
+        "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
         "sample": f"{steps} whole step(s) of the same workload ({s.batch} sequences x "
                   f"{len(wl.layers)} layers, append + attention) in {el:.1f} s, fp64 C oracle",
     }
@@ -543,6 +676,7 @@ def main():
 
     print("# timing step", file=sys.stderr, flush=True)
     ms, wall_ms = time_graph(step, args.steps, args.warmup, use_graph=not args.no_graph)
+    windows, mean_ms = time_graph.last_windows, time_graph.last_mean
     eager_ms = None
     if not args.no_graph:
         eager_ms, _ = time_graph(step, max(3, args.steps // 5), 2, use_graph=False)
@@ -623,11 +757,33 @@ def main():
                  "kv_bytes_per_step": m_bytes, "GB/s": round(m_bytes / (m_ms / 1e3) / 1e9, 1),
                  "path": "hda_decode_multi on every layer (RoPE, attention split over workgroups "
                          "+ merge, append: 4 launches)"}
+    prefill = None
+    if args.prefill_tokens:
+        B, T = args.prefill_batch, args.prefill_tokens
+        print(f"# timing chunked prefill, {B} sequences x {T} tokens", file=sys.stderr, flush=True)
+        wl.make_prefill(B, T, args.seed)
+        torch.cuda.synchronize()
+
+        def prefill_step():
+            for L in wl.layers:
+                wl.prefill_call(L)
+        p_ms, _ = time_graph(prefill_step, args.steps, args.warmup, use_graph=not args.no_graph)
+        prefill = {"batch": B, "tokens_per_chunk": T, "ms_per_step": round(p_ms, 4),
+                   "tokens_per_s": round(B * T / (p_ms / 1e3), 1),
+                   "attn_tflops": round(wl.pf_flops / (p_ms / 1e3) / 1e12, 1),
+                   "mfma_bf16_frac": round(wl.pf_flops / (p_ms / 1e3) / 2.5e15, 4),
+                   "kv_GB/s": round(wl.pf_rows * wl.kv_row_bytes / (p_ms / 1e3) / 1e9, 1),
+                   "path": "hda_decode_multi on every layer (RoPE, prefill_chunk_kernel: both "
+                           "products on MFMA, append: 3 launches)"}
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
         sparse = sparse_kernel(args.steps, args.warmup, args.seed)
         sparse["fp8"] = sparse_kernel(args.steps, args.warmup, args.seed, fp8=True)
+    others = {}
+    if args.config == "throughput" and not args.no_other_configs:
+        for name in ("step28", "long"):
+            others[name] = other_config(name, args)
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -645,6 +801,9 @@ def main():
                    "seq_len_max": int(sl.max()), "seq_len_mean": round(float(sl.float().mean()), 1),
                    "graph": not args.no_graph, "path": args.path, "chunk_keys": args.chunk_keys},
         "tokens_per_s": round(cfg["batch"] / (ms / 1e3), 1),
+        "timing": f"median of {len(windows)} windows of the {args.steps} timed steps (HIP events "
+                  "on the stream at each window boundary)",
+        "window_ms_per_step": windows, "mean_ms_per_step": round(mean_ms, 4),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": wl.kv_bytes,
         "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 4),
@@ -653,6 +812,8 @@ def main():
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": roof, "layer_kernels": {"sliding": k_slide, "full": k_full},
         "cpu_baseline": cpu, "sparse": sparse, "paged": k_paged, "fp8": fp8, "multi": multi,
+        "prefill": prefill, "step28": others.get("step28"), "long": others.get("long"),
+        "device": device_info(),
     }
     print(json.dumps(rec), flush=True)
 
