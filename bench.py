@@ -366,14 +366,28 @@ def layer_path(path, lt):
     return path
 
 
-# Kernels a layer call runs on each path (the window kernels serve every
-# sliding layer: keys <= 1024; full layers at this shape take the stream).
+# Kernels a layer call runs on each path at G = 4 (the window kernels serve
+# every sliding layer: keys <= 1024; full layers at these shapes take the
+# stream).
 KERNELS = {
     ("separate", "sliding"): "decode_pair_kernel<2, false>",
     ("separate", "full"): "decode_stream_kernel<4, false, 0> + stream_merge_kernel<false>",
-    ("fused", "sliding"): "decode_window_step_kernel<2, 256, false>",
+    ("fused", "sliding"): "decode_window_step_kernel<2, 256, false, false, 8>",
     ("fused", "full"): "decode_stream_kernel<4, false, 64> + stream_merge_kernel<true>",
 }
+
+
+def kernel_name(path, name, batch):
+    """The kernel names of a layer call.  The one-launch sliding step splits
+    a (sequence, KV head) pair by heads when there are at least 128 pairs
+    (two workgroups, two heads each) and by keys below that (four heads,
+    last-arriver merge): the library's window_step_plan at G = 4, window
+    512, two KV heads."""
+    if (path, name) == ("fused", "sliding") and batch * 2 < 128:
+        return "decode_window_step_kernel<4, 256, false, true, 8>"
+    return KERNELS[(path, name)]
+
+
 # Sources whose change invalidates a committed traffic measurement.
 TRAFFIC_SOURCES = ("decode_attn.hip", "decode_wave.h", "decode_step.hip", "hda_device.h",
                    "hda_kernels.h", "hda_api.cpp", "rope_append.hip", "sparse_attn.hip",
@@ -409,26 +423,27 @@ def layer_kernel(wl: Workload, lt: int, steps, warmup, path="auto", chunk_keys=0
     algo = wl.rows[lt] * wl.kv_row_bytes
     achieved = algo / per_call_s / 1e9
     name = "sliding" if lt == workloads.SLIDING else "full"
+    kname = kernel_name(path, name, wl.cfg["batch"])
     if paged:
         p = Ls[0]["pcache"].desc()
         return {
-            "kernel": f"{KERNELS[(path, name)]} (full-layer hda_decode_attn, paged)",
+            "kernel": f"{kname} (full-layer hda_decode_attn, paged)",
             "page_size": p.page_size, "pool_pages": p.num_pages,
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": algo,
             "avg_launch_us": round(per_call_s * 1e6, 2), "launches_timed": steps * len(Ls),
-            "launches_per_call": KERNELS[(path, name)].count(" + ") + 1,
+            "launches_per_call": kname.count(" + ") + 1,
         }
     return {
-        "kernel": f"{KERNELS[(path, name)]} ({name}-layer hda_decode_attn)" if path == "separate"
-                  else f"{KERNELS[(path, name)]} ({name}-layer hda_decode_step)",
+        "kernel": f"{kname} ({name}-layer hda_decode_attn)" if path == "separate"
+                  else f"{kname} ({name}-layer hda_decode_step)",
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(f"{KERNELS[(path, name)]}", wl.cfg["batch"]),
+        "traffic": measured_traffic(kname, wl.cfg["batch"]),
         "algorithmic_bytes_per_launch": algo, "avg_launch_us": round(per_call_s * 1e6, 2),
         "launches_timed": steps * len(Ls),
         # avg_launch_us is per call: per launch when the call is one launch
-        "launches_per_call": KERNELS[(path, name)].count(" + ") + 1,
+        "launches_per_call": kname.count(" + ") + 1,
     }
 
 
@@ -528,9 +543,9 @@ def sparse_kernel(steps, warmup, seed, pools=8, fp8=False):
 
 
 def device_info():
-    """Device name, architecture, ROCm/HIP version and current clocks (as
-    rocm-smi prints them, when it is there) and the host CPU model."""
-    import subprocess
+    """Device name, architecture, ROCm/HIP version, the current clock
+    levels the driver exposes in sysfs, and the host CPU model."""
+    import glob
     import torch
     p = torch.cuda.get_device_properties(0)
     info = {"device": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
@@ -541,14 +556,22 @@ def device_info():
         info["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:
         info["rocm"] = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        clk = json.loads(r.stdout) if r.returncode == 0 else {}
-        card = next(iter(clk.values()), {}) if clk else {}
-        info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()} or None
-    except (OSError, ValueError, subprocess.SubprocessError):
-        info["clocks"] = None
+    clocks = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("product_name", "pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                text = open(os.path.join(dev, name)).read()
+            except OSError:
+                continue
+            if name == "product_name":
+                clocks.setdefault("product_name", text.strip())
+            else:  # the level the driver marks as current
+                cur = [ln.split(":", 1)[-1].strip(" *") for ln in text.splitlines() if ln.endswith("*")]
+                if cur:
+                    clocks.setdefault(name[-4:], cur[0])
+        if clocks:
+            break
+    info["clocks"] = clocks or None
     return info
 
 
