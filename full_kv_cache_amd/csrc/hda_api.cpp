@@ -338,19 +338,26 @@ size_t stream_step_bytes(const hda_cache_desc *c) {
 }
 
 // ---------------------------------------------------------------- sparse
-// Key splits for the sparse decode: one workgroup per (token, split, group
-// of 16 heads); split a token's index row only when the tokens alone leave
-// the GPU short of workgroups (fewer than 256), and never below 64 keys.
+// Key splits for the sparse decode.  Shared-tile kernel (bf16 pool, up to 64
+// heads): one workgroup per (token, split), so a token's index row is split
+// until there are 256 workgroups (never below 64 keys a split, never above
+// kSparseMaxSplitKeys), in multiples of 32 keys.  Head-group kernel: one
+// workgroup per (token, split, group of 16 heads), split only when the
+// tokens and head groups alone leave fewer than 256 workgroups, in
+// multiples of 16 keys.
 struct SparsePlan {
     int nsplit, split_keys;
 };
 
-SparsePlan sparse_plan(int32_t tokens, int32_t heads, int32_t topk) {
-    const int64_t wgs = (int64_t)tokens * (heads / hda::kSparseHeadsPerWave);
+SparsePlan sparse_plan(int32_t tokens, int32_t heads, int32_t topk, bool fp8) {
+    const bool tiles = hda::sparse_uses_tiles(heads, fp8);
+    const int64_t wgs = tiles ? (int64_t)tokens : (int64_t)tokens * (heads / hda::kSparseHeadsPerWave);
+    const int64_t mult = tiles ? 32 : 16;
     int64_t ns = 1;
     if (wgs > 0 && wgs < 256 && topk > 64) ns = std::min<int64_t>((256 + wgs - 1) / wgs, (topk + 63) / 64);
-    int64_t ks = topk > 0 ? (topk + ns - 1) / ns : 16;
-    ks = (ks + 15) / 16 * 16;
+    if (tiles) ns = std::max<int64_t>(ns, ((int64_t)topk + hda::kSparseMaxSplitKeys - 1) / hda::kSparseMaxSplitKeys);
+    int64_t ks = topk > 0 ? (topk + ns - 1) / ns : mult;
+    ks = (ks + mult - 1) / mult * mult;
     ns = topk > 0 ? (topk + ks - 1) / ks : 1;
     return {(int)ns, (int)ks};
 }
@@ -374,9 +381,13 @@ hda_status check_sparse_shape(int32_t tokens, int32_t heads, int32_t topk, int32
     if (dqk != hda::kSparseDqk || dv != hda::kSparseDv)
         return fail(HDA_ERR_UNSUPPORTED, "sparse kernels are built for dqk %d / dv %d, got %d / %d",
                     hda::kSparseDqk, hda::kSparseDv, dqk, dv);
-    const SparsePlan pl = sparse_plan(tokens, heads, topk);
-    const int64_t units = (int64_t)tokens * pl.nsplit;
-    const int64_t blocks = (units + 7) / 8 * 8 * (heads / hda::kSparseHeadsPerWave);
+    int64_t blocks = 0;
+    for (const bool fp8 : {false, true}) {
+        const SparsePlan pl = sparse_plan(tokens, heads, topk, fp8);
+        const int64_t units = ((int64_t)tokens + 7) / 8 * 8 * pl.nsplit;
+        blocks = std::max(blocks, hda::sparse_uses_tiles(heads, fp8) ? units
+                                                                     : units * (heads / hda::kSparseHeadsPerWave));
+    }
     if (blocks > INT32_MAX || (int64_t)tokens * heads > INT32_MAX)
         return fail(HDA_ERR_UNSUPPORTED, "%d tokens x %d heads exceed the launch grid", tokens, heads);
     return HDA_OK;
@@ -916,7 +927,7 @@ hda_status sparse_call(const void *q, const void *kv, const uint8_t *kv8, const 
         (kv_scale && (reinterpret_cast<uintptr_t>(kv_scale) & 3u)))
         return fail(HDA_ERR_INVALID_ARGUMENT, "indices, topk_length, sinks, scales and lse must be 4-byte aligned");
     if (!std::isfinite(scale)) return fail(HDA_ERR_INVALID_ARGUMENT, "scale must be finite");
-    const SparsePlan pl = sparse_plan(tokens, num_q_heads, topk);
+    const SparsePlan pl = sparse_plan(tokens, num_q_heads, topk, kv8 != nullptr);
     const size_t need = sparse_workspace(tokens, num_q_heads, pl);
     if (need && (!workspace || workspace_bytes < need))
         return fail(HDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need, workspace_bytes,
@@ -976,7 +987,9 @@ hda_status hda_sparse_decode_attn_fp8(const void *q, const uint8_t *kv_codes, co
 
 size_t hda_sparse_workspace_bytes(int32_t tokens, int32_t num_q_heads, int32_t topk, int32_t dv) {
     if (check_sparse_shape(tokens, num_q_heads, topk, hda::kSparseDqk, dv) != HDA_OK) return 0;
-    return sparse_workspace(tokens, num_q_heads, sparse_plan(tokens, num_q_heads, topk));
+    // enough for either pool type
+    return std::max(sparse_workspace(tokens, num_q_heads, sparse_plan(tokens, num_q_heads, topk, false)),
+                    sparse_workspace(tokens, num_q_heads, sparse_plan(tokens, num_q_heads, topk, true)));
 }
 
 }  // extern "C"

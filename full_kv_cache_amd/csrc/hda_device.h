@@ -27,6 +27,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two floats rounded to bf16 (nearest even) in one word, a low; the
+// hardware conversion (v_cvt_pk_bf16_f32), branch-free.
+typedef __bf16 hda_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hda_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((hda_f32x2){a, b}, hda_bf16x2));
+}
+
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 // Streaming 16-byte load of data read exactly once (KV rows): non-temporal

@@ -146,6 +146,7 @@ struct MergeParams {
 constexpr int kSparseDqk = 576;    // key dims (latent + rotary part)
 constexpr int kSparseDv = 512;     // value dims: the leading part of each row
 constexpr int kSparseHeadsPerWave = 16;
+constexpr int kSparseMaxSplitKeys = 2048;  // keys of one split of the shared-tile kernel
 #ifndef HDA_SPARSE_WAVES
 #define HDA_SPARSE_WAVES 4
 #endif
@@ -204,6 +205,10 @@ hipError_t launch_rope_append_fp8(const RopeAppendParams &p, hipStream_t stream)
 // out / lse with the sink, otherwise partials and then their merge.  An fp8
 // pool (kv8 / kv_scale set) takes the kernel's fp8 form.
 hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t stream);
+// Whether the sparse call runs the shared-tile kernel (one workgroup per
+// (token, split) for all heads; its splits hold at most kSparseMaxSplitKeys
+// keys, a multiple of 32) or the head-group kernel (splits a multiple of 16).
+bool sparse_uses_tiles(int num_q_heads, bool fp8);
 
 // Chunk kernel over grid (nsplit, Hkv, B).  final_out: nsplit must be 1 and
 // the kernel writes out/lse with the sink; otherwise it writes partials.

@@ -339,6 +339,294 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
     }
 }
 
+// ---------------------------------------------------------------------------
+// Shared-tile form (bf16 pool, up to 64 query heads): one 4-wave workgroup
+// per (token, key split) serves every head -- wave w owns heads 16w..16w+15
+// -- so each gathered row crosses from L2 into the CU once, not once per
+// head group.  A tile is 32 keys, two 16-row halves of 18 one-KiB blocks;
+// block j of a half holds, at byte 16 l, lane l = r + 16 c's 16 bytes: row
+// r, dims 32j + 8c .. +7.  The rows go straight from memory into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), each
+// wave issuing 9 of the tile's 36 blocks; three tile buffers rotate, so two
+// tiles are in flight while one is scored.  Per wave and tile:
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: block j of a half is k-step
+//     j's A operand as it lies (one ds_read_b128 at 16 l), q is the B
+//     operand, held in registers for the call;
+//   * O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with 32 key slots: slot
+//     8c + i is key 4c + i of the first half, slot 8c + 4 + i the same key
+//     of the second half -- the S^T accumulators' lane layout -- and V^T's
+//     operand is two transposing reads (ds_read_b64_tr_b16), one per half.
+// Keys without a row (past the split's end, or an index outside the pool)
+// read a zero row and are masked out of the softmax, so a NaN never meets a
+// zero weight.  Softmax against a fixed reference as in the kernel above.
+
+constexpr int kTileKeys = 32;
+constexpr int kHalfBytes = 16 * kSparseDqk * 2;  // one 16-row half: 18 blocks of 1 KiB
+constexpr int kTileBlocks = 2 * kKSteps;         // 36 blocks per tile
+constexpr int kTileWaves = 4;
+constexpr int kTrAhead = 6;  // V^T read pairs in flight (lgkmcnt counts up to 15)
+constexpr int kKAhead = 4;   // K operand read pairs in flight
+constexpr int kBlocksPerWave = kTileBlocks / kTileWaves;
+static_assert(kBlocksPerWave * kTileWaves == kTileBlocks, "blocks split evenly over the waves");
+
+// Stands in for the row of a key without one.
+__device__ __align__(16) const uint16_t g_zero_row[kSparseDqk] = {};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes a lane from src to LDS at dst + 16 lane (dst wave-uniform).
+// Written in asm so that the compiler, which cannot tell the tile buffers
+// apart behind a computed address, does not wait for every such load before
+// each LDS read; the waits on these loads are the explicit vmcnt waits of
+// the tile loop.  No register receives data.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
+__device__ __forceinline__ void load_to_lds(const void *src, unsigned char *dst) {
+    // the LDS aperture is 4 GiB aligned: a shared pointer's low word is its LDS address
+    const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool FINAL>
+__global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseParams p) {
+    __shared__ __align__(1024) unsigned char s_b0[2 * kHalfBytes];
+    __shared__ __align__(1024) unsigned char s_b1[2 * kHalfBytes];
+    __shared__ __align__(1024) unsigned char s_b2[2 * kHalfBytes];
+    __shared__ int s_idx[kSparseMaxSplitKeys];
+    __shared__ int s_over[kTileWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int mrow = lane & 15, kg = lane >> 4;
+    const int x = blockIdx.x, j8 = x >> 3;
+    const int t = (j8 / p.nsplit) * 8 + (x & 7), sp = j8 % p.nsplit;
+    if (t >= p.tokens) return;  // the whole workgroup
+    int len = p.topk_length ? p.topk_length[t] : p.topk;
+    len = len < 0 ? 0 : (len > p.topk ? p.topk : len);
+    const int k0 = sp * p.split_keys;
+    const int nk = max(min(k0 + p.split_keys, len) - k0, 0);
+    const int ntile = (nk + kTileKeys - 1) / kTileKeys;
+    const int Hq = p.num_q_heads, h0 = wave * kSparseHeadsPerWave;
+    const bool active = h0 < Hq;  // wave-uniform: a wave past the heads only loads
+
+    const int32_t *idx = p.indices + (int64_t)t * p.topk + k0;
+    auto row_at = [&](int i) HDA_INLINE {  // pool row of the split's key i, or -1
+        int r = -1;
+        if (i < nk) {
+            r = idx[i];
+            if (r < 0 || (int64_t)r >= p.pool_rows) r = -1;
+        }
+        return r;
+    };
+    // This wave's blocks of a tile whose halves' rows for this lane are ra
+    // and rb (blocks wave, wave + 4, ...; -1 reads the zero row).
+    auto issue_rows = [&](int ra, int rb, unsigned char *buf) HDA_INLINE {
+        const uint16_t *pa = ra < 0 ? g_zero_row : p.kv + (int64_t)ra * kSparseDqk;
+        const uint16_t *pb = rb < 0 ? g_zero_row : p.kv + (int64_t)rb * kSparseDqk;
+#pragma unroll
+        for (int m = 0; m < kBlocksPerWave; ++m) {
+            const int blk = wave + kTileWaves * m;  // 0..35, wave-uniform
+            const bool hb = blk >= kKSteps;
+            const int j = hb ? blk - kKSteps : blk;
+            const uint16_t *src = (hb ? pb : pa) + 32 * j + 8 * kg;
+            load_to_lds(src, buf + 1024 * blk);
+        }
+    };
+    // Tiles 0 and 1 go in flight first, their rows read straight from the
+    // index row; then q and the rest of the split's rows (into s_idx).
+    {
+        const int r0a = row_at(mrow), r0b = row_at(16 + mrow);
+        const int r1a = row_at(kTileKeys + mrow), r1b = row_at(kTileKeys + 16 + mrow);
+        issue_rows(r0a, r0b, s_b0);
+        issue_rows(r1a, r1b, s_b1);
+    }
+    for (int i = tid; i < ntile * kTileKeys; i += kTileWaves * 64) s_idx[i] = row_at(i);
+    // q: lane (head mrow, c) holds dims 32j + 8c .. +7 of its head, every j
+    uint4 qb[kKSteps];
+    if (active) {
+        const uint16_t *qr = p.q + ((int64_t)t * Hq + h0 + mrow) * kSparseDqk + 8 * kg;
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) qb[j] = ld16(qr + 32 * j);
+    }
+    if (tid < kTileWaves) s_over[tid] = 0;
+    // q, the indices and tiles 0 and 1 in: the tile loop's waits count only
+    // the loads it issues
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    // This wave's blocks of tile i into `buf`; past the last tile every lane
+    // reads the zero row, so that each tile leaves the same number of loads
+    // behind it.
+    auto issue = [&](int i, unsigned char *buf) HDA_INLINE {
+        int ra = -1, rb = -1;
+        if (i < ntile) {
+            ra = s_idx[kTileKeys * i + mrow];
+            rb = s_idx[kTileKeys * i + 16 + mrow];
+        }
+        issue_rows(ra, rb, buf);
+    };
+
+    f32x4 acc[kDimTiles];
+#pragma unroll
+    for (int d = 0; d < kDimTiles; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_lane = 0.f, m_max = -INFINITY;
+    bool over = false;
+    // V^T transposing read of dim tile d in a half: row 4c + a, dims
+    // 16d + 8b + 4e .. +3 for mrow = 4a + 2b + e, at 512 d + this offset
+    const int tr_off = 64 * kg + 16 * (mrow >> 2) + 256 * ((mrow >> 1) & 1) + 8 * (mrow & 1);
+
+    auto compute = [&](int i, const unsigned char *buf) HDA_INLINE {
+        const int ra = s_idx[kTileKeys * i + mrow], rb = s_idx[kTileKeys * i + 16 + mrow];
+        const uint32_t va = (uint32_t)__ballot(ra >= 0) & 0xFFFFu;
+        const uint32_t vb = (uint32_t)__ballot(rb >= 0) & 0xFFFFu;
+        if (!active) return;
+        // scores: lane (head mrow, c) gets keys 4c + i of each half
+        // (the K operand reads run kKAhead k-steps ahead of their products)
+        f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
+        uint4 ka[kKAhead], kb[kKAhead];
+        auto k_read = [&](int j) HDA_INLINE {
+            ka[j % kKAhead] = ld16(buf + 1024 * j + 16 * lane);
+            kb[j % kKAhead] = ld16(buf + kHalfBytes + 1024 * j + 16 * lane);
+        };
+#pragma unroll
+        for (int j = 0; j < kKAhead; ++j) k_read(j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) {
+            const bf16x8 a = as_bf16x8(ka[j % kKAhead]), b = as_bf16x8(kb[j % kKAhead]);
+            if (j + kKAhead < kKSteps) k_read(j + kKAhead);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (the scheduler would sink them)
+            const bf16x8 qj = as_bf16x8(qb[j]);
+            if (j & 1) {
+                sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qj, sa1, 0, 0, 0);
+                sb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qj, sb1, 0, 0, 0);
+            } else {
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qj, sa0, 0, 0, 0);
+                sb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qj, sb0, 0, 0, 0);
+            }
+        }
+        float s[8], tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[e] = ((va >> (4 * kg + e)) & 1u) ? (sa0[e] + sa1[e]) * p.scale_log2 : -INFINITY;
+            s[4 + e] = ((vb >> (4 * kg + e)) & 1u) ? (sb0[e] + sb1[e]) * p.scale_log2 : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        m_max = fmaxf(m_max, tmax);
+        if (m_ref == -INFINITY) m_ref = tmax;  // first keys: nothing accumulated yet
+        over |= tmax > m_ref + kSlack;
+        const float mr = m_ref == -INFINITY ? 0.f : m_ref;
+        float pw[8], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pw[e] = __builtin_amdgcn_exp2f(s[e] - mr);
+            ps += pw[e];
+        }
+        l_lane += ps;
+        const uint4 pu = make_uint4(pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
+                                    pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7]));
+        const bf16x8 pb = as_bf16x8(pu);
+        // V^T reads run kTrAhead dim tiles ahead of the products that use
+        // them (each product would otherwise wait out a whole LDS round trip)
+        v4i16 vlo[kTrAhead], vhi[kTrAhead];
+        auto tr_read = [&](int d) HDA_INLINE {
+            vlo[d % kTrAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(buf + tr_off + 512 * d));
+            vhi[d % kTrAhead] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(buf + kHalfBytes + tr_off + 512 * d));
+        };
+#pragma unroll
+        for (int d = 0; d < kTrAhead; ++d) tr_read(d);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < kDimTiles; ++d) {
+            const v4i16 lo = vlo[d % kTrAhead], hi = vhi[d % kTrAhead];
+            if (d + kTrAhead < kDimTiles) tr_read(d + kTrAhead);
+            __builtin_amdgcn_sched_barrier(0);
+            uint4 vu;
+            vu.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+            vu.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+            vu.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+            vu.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+            acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pb, acc[d], 0, 0, 0);
+        }
+    };
+
+    // One tile: wait for this wave's blocks of tile i (tile i + 1's 9 may
+    // still be in flight), meet the other waves (their blocks are in, and
+    // all are done with tile i - 1's buffer), refill that buffer with tile
+    // i + 2, score tile i.
+    auto step = [&](int i, const unsigned char *cur, unsigned char *refill) HDA_INLINE {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kBlocksPerWave);  // vmcnt(9)
+        raw_barrier();
+        issue(i + 2, refill);
+        compute(i, cur);
+    };
+    static_assert(kBlocksPerWave < 16, "vmcnt immediate");
+
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass > 0) {  // tiles 0 and 1 again
+            issue(0, s_b0);
+            issue(1, s_b1);
+        }
+        for (int i = 0; i < ntile; i += 3) {
+            step(i, s_b0, s_b2);
+            if (i + 1 >= ntile) break;
+            step(i + 1, s_b1, s_b0);
+            if (i + 2 >= ntile) break;
+            step(i + 2, s_b2, s_b1);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads past the end have landed
+        const bool any_over = __ballot(over) != 0;  // the whole wave votes
+        if (lane == 0) s_over[wave] = (active && any_over) ? 1 : 0;
+        __syncthreads();
+        const bool again = s_over[0] | s_over[1] | s_over[2] | s_over[3];
+        __syncthreads();
+        if (!again) break;
+        // a score passed its head's reference by more than kSlack: every
+        // wave scores its keys again against the exact maximum
+#pragma unroll
+        for (int d = 0; d < kDimTiles; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_lane = 0.f;
+        m_ref = m_max;
+        over = false;
+    }
+    if (!active) return;
+
+    float l = l_lane + __shfl_xor(l_lane, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int hq = h0 + mrow;
+    const float lse = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+    float f = l > 0.f ? 1.f / l : 0.f;
+    if (FINAL) {
+        if (p.sinks && l > 0.f) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+        uint16_t *dst = p.out + ((int64_t)t * Hq + hq) * kSparseDv + 4 * kg;
+#pragma unroll
+        for (int d = 0; d < kDimTiles; ++d)
+            *reinterpret_cast<uint2 *>(dst + 16 * d) =
+                make_uint2(pack_bf16x2(acc[d][0] * f, acc[d][1] * f), pack_bf16x2(acc[d][2] * f, acc[d][3] * f));
+        if (kg == 0 && p.lse) p.lse[(int64_t)t * Hq + hq] = lse;
+    } else {
+        const int64_t slot = ((int64_t)t * Hq + hq) * p.nsplit + sp;
+        float *dst = p.part_o + slot * kSparseDv + 4 * kg;
+#pragma unroll
+        for (int d = 0; d < kDimTiles; ++d)
+            *reinterpret_cast<float4 *>(dst + 16 * d) =
+                make_float4(acc[d][0] * f, acc[d][1] * f, acc[d][2] * f, acc[d][3] * f);
+        if (kg == 0) p.part_lse[slot] = lse;
+    }
+}
+
 // LSE merge of the key splits, then the sink: one workgroup per (token,
 // head), 128 threads x 4 dims.
 __global__ __launch_bounds__(128) void sparse_merge_kernel(SparseParams p) {
@@ -389,9 +677,28 @@ hipError_t launch_sparse(const SparseParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_sparse_tile(const SparseParams &p, hipStream_t s) {
+    const int64_t blocks = ((int64_t)p.tokens + 7) / 8 * 8 * p.nsplit;
+    if (p.nsplit == 1) {
+        hipLaunchKernelGGL((sparse_tile_kernel<true>), dim3((unsigned)blocks), dim3(kTileWaves * 64), 0, s, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((sparse_tile_kernel<false>), dim3((unsigned)blocks), dim3(kTileWaves * 64), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sparse_merge_kernel, dim3((unsigned)((int64_t)p.tokens * p.num_q_heads)),
+                       dim3(kSparseDv / 4), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
+bool sparse_uses_tiles(int num_q_heads, bool fp8) {
+    return !fp8 && num_q_heads <= kTileWaves * kSparseHeadsPerWave;
+}
+
 hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t s) {
+    if (sparse_uses_tiles(p.num_q_heads, p.kv8 != nullptr)) return launch_sparse_tile(p, s);
     return p.kv8 ? launch_sparse<true>(p, s) : launch_sparse<false>(p, s);
 }
 

@@ -181,12 +181,17 @@ def test_sparse_shape_checks():
 
 
 def test_sparse_workspace_plan():
-    """Split only when tokens x head groups leave the GPU short of
-    workgroups; the headline shape (32 tokens, 64 heads, top-2048) splits in
-    two: partials fp32 [32, 64, 2, 512] plus lse [32, 64, 2]."""
+    """Split only when the workgroups would leave the GPU short (fewer than
+    256): one per token for a bf16 pool and up to 64 heads (the shared-tile
+    kernel), one per (token, 16 heads) otherwise; the size covers either
+    pool.  The headline shape (32 tokens, 64 heads, top-2048) splits in
+    eight for the bf16 pool: partials fp32 [32, 64, 8, 512] plus lse
+    [32, 64, 8]."""
     ws = hda.hda_sparse_workspace_bytes
-    assert ws(32, 64, 2048) == 32 * 64 * 2 * 512 * 4 + 32 * 64 * 2 * 4
-    assert ws(128, 64, 2048) == 0       # 512 workgroups already: no split
+    assert ws(32, 64, 2048) == 32 * 64 * 8 * 512 * 4 + 32 * 64 * 8 * 4
+    assert ws(128, 64, 2048) == 128 * 64 * 2 * 512 * 4 + 128 * 64 * 2 * 4  # bf16: 2 splits; fp8: none
+    assert ws(256, 64, 2048) == 0       # 256 workgroups already: no split
+    assert ws(256, 16, 4096) == 256 * 16 * 2 * 512 * 4 + 256 * 16 * 2 * 4  # splits of at most 2048 keys
     assert ws(1, 16, 64) == 0           # too few keys to split
     assert ws(1, 16, 2048) == 1 * 16 * 32 * 512 * 4 + 16 * 32 * 4  # 32 splits of 64 keys
     assert ws(32, 64, 2048, dv=256) == 0  # invalid shape

@@ -60,9 +60,13 @@ def _print_case(**kw):
 
 
 @pytest.mark.parametrize("T,H,pool,topk", [(3, 64, 4096, 300), (2, 16, 1000, 77), (64, 64, 8192, 256),
-                                           (5, 32, 2048, 1024)])
+                                           (5, 32, 2048, 1024), (7, 48, 3000, 500), (300, 16, 4096, 2080),
+                                           (9, 128, 2048, 700)])
 def test_sparse_matches_oracle(T, H, pool, topk):
-    """Ragged index rows (not a multiple of 16), split and unsplit plans."""
+    """Ragged index rows (not a multiple of 16 or 32), split and unsplit
+    plans: 48 heads leave a wave of the shared-tile kernel without heads;
+    300 tokens x top-2080 need no split for the grid but two for the
+    2048-key cap of a split; 128 heads take the head-group kernel."""
     _print_case(test="sparse", T=T, H=H, pool=pool, topk=topk)
     h = _case(T * 1000 + topk, T, H, pool, topk)
     ref, rlse = _ref(h)
@@ -212,8 +216,10 @@ def test_sparse_late_large_score(fp8):
     fixed softmax reference): the wave scores its keys again against the
     exact maximum; results as the oracle's."""
     _print_case(test="sparse_late_large", fp8=fp8)
-    # 64 tokens x 4 head groups: no key split, so list position 900 is tile
-    # 56 of its token, the 15th tile of the wave that scores it
+    # bf16: 64 tokens in 4 key splits of 256, so list position 900 is the
+    # fifth 32-key tile of its split, scored after the first set the
+    # reference; fp8: 64 tokens x 4 head groups, no split, so it is tile 56
+    # of its token, the 15th tile of the wave that scores it
     T, H, pool, topk = 64, 64, 4096, 1024
     h = _case(50, T, H, pool, topk, poison=False)
     qrow = oracle.bf16_to_f64(h["q"][0, 5])

@@ -37,7 +37,7 @@ DEFAULT_PATH = {
     "rope_append.hip": ["rope_append_kernel", "rope_append_fp8_kernel"],
     "sparse_attn.hip": ["sparse_decode_kernelILb0ELb0E", "sparse_decode_kernelILb0ELb1E",
                         "sparse_decode_kernelILb1ELb0E", "sparse_decode_kernelILb1ELb1E",
-                        "sparse_merge_kernel"],
+                        "sparse_merge_kernel", "sparse_tile_kernelILb0E", "sparse_tile_kernelILb1E"],
     "noalloc.hip": ["zero_fill_kernel"],
 }
 
