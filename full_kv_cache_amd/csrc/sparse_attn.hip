@@ -628,33 +628,50 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
 }
 
 // LSE merge of the key splits, then the sink: one workgroup per (token,
-// head), 128 threads x 4 dims.
+// head), 128 threads x 4 dims.  The splits are read kMergeBatch at a time,
+// every load of a batch issued before the first is used.
+constexpr int kMergeBatch = 16;
+
 __global__ __launch_bounds__(128) void sparse_merge_kernel(SparseParams p) {
     const int hq = blockIdx.x % p.num_q_heads, t = blockIdx.x / p.num_q_heads;
     const int d = 4 * threadIdx.x;
     const int S = p.nsplit;
     const int64_t base = ((int64_t)t * p.num_q_heads + hq) * S;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_lse[base + s]);
+    for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+        float lv[kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) lv[k] = p.part_lse[base + min(s0 + k, S - 1)];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, lv[k]);
+    }
     float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float w = expf(p.part_lse[base + s] - M);
-            const float4 v = *reinterpret_cast<const float4 *>(p.part_o + (base + s) * kSparseDv + d);
-            L += w;
-            o[0] = fmaf(w, v.x, o[0]);
-            o[1] = fmaf(w, v.y, o[1]);
-            o[2] = fmaf(w, v.z, o[2]);
-            o[3] = fmaf(w, v.w, o[3]);
+        for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+            float lv[kMergeBatch];
+            float4 ov[kMergeBatch];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const int64_t sl = base + min(s0 + k, S - 1);
+                lv[k] = p.part_lse[sl];
+                ov[k] = *reinterpret_cast<const float4 *>(p.part_o + sl * kSparseDv + d);
+            }
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const float w = s0 + k < S ? expf(lv[k] - M) : 0.f;  // clamped repeats weigh nothing
+                L += w;
+                o[0] = fmaf(w, ov[k].x, o[0]);
+                o[1] = fmaf(w, ov[k].y, o[1]);
+                o[2] = fmaf(w, ov[k].z, o[2]);
+                o[3] = fmaf(w, ov[k].w, o[3]);
+            }
         }
     }
     const float lse = L > 0.f ? M + logf(L) : -INFINITY;
     float f = L > 0.f ? 1.f / L : 0.f;
-    if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+    if (p.sinks && L > 0.f) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
     uint16_t *dst = p.out + ((int64_t)t * p.num_q_heads + hq) * kSparseDv + d;
-    const uint32_t lo = (uint32_t)f32_to_bf16(o[0] * f) | ((uint32_t)f32_to_bf16(o[1] * f) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(o[2] * f) | ((uint32_t)f32_to_bf16(o[3] * f) << 16);
-    *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(o[0] * f, o[1] * f), pack_bf16x2(o[2] * f, o[3] * f));
     if (threadIdx.x == 0 && p.lse) p.lse[(int64_t)t * p.num_q_heads + hq] = lse;
 }
 
