@@ -368,6 +368,7 @@ constexpr int kTrAhead = 6;  // V^T read pairs in flight (lgkmcnt counts up to 1
 constexpr int kKAhead = 4;   // K operand read pairs in flight
 constexpr int kBlocksPerWave = kTileBlocks / kTileWaves;
 static_assert(kBlocksPerWave * kTileWaves == kTileBlocks, "blocks split evenly over the waves");
+static_assert(kTileWaves * kSparseHeadsPerWave == kSparseTileHeads, "a wave per 16 heads");
 
 // Stands in for the row of a key without one.
 __device__ __align__(16) const uint16_t g_zero_row[kSparseDqk] = {};
@@ -709,10 +710,6 @@ hipError_t launch_sparse_tile(const SparseParams &p, hipStream_t s) {
 }
 
 }  // namespace
-
-bool sparse_uses_tiles(int num_q_heads, bool fp8) {
-    return !fp8 && num_q_heads <= kTileWaves * kSparseHeadsPerWave;
-}
 
 hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t s) {
     if (sparse_uses_tiles(p.num_q_heads, p.kv8 != nullptr)) return launch_sparse_tile(p, s);

@@ -44,8 +44,12 @@ def build(force: bool = False) -> Path:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(str(_LIB))
+        # HDA_ORACLE_LIB: a build of oracle.c made elsewhere (the sanitizer
+        # test loads an AddressSanitizer / UBSan build this way)
+        path = os.environ.get("HDA_ORACLE_LIB")
+        if not path:
+            path = str(build())
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.or_bf16_to_f64.restype = f64
