@@ -326,32 +326,47 @@ __global__ __launch_bounds__(kHeadDim) void multi_merge_kernel(MultiParams p, in
 // block (row m = t*G + h: token t, head h), so the waves never merge.  The
 // keys -- the cache as it was before the chunk, then the chunk's own rows
 // up to the block's last token -- pass through LDS in tiles of 32 that all
-// waves of the workgroup score, the next tile's loads in flight while one
-// is scored.  Per 16-key half of a tile, as the sparse kernel:
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the keys' rows from LDS as
-//     the A operand, the wave's 16 rotated query rows as B, in registers);
-//   * an online softmax per query row (4 keys of one row per lane);
-//   * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, the S^T accumulator
-//     already P^T's operand layout, V^T through ds_read_b64_tr_b16.
+// waves of the workgroup score.  A tile is two 16-row halves of K then V,
+// each in one-KiB blocks: block j of a half holds, at byte 16 l, lane
+// l = r + 16 c's 16 bytes (row r, dims 32j + 8c .. +7).  The rows go
+// straight from memory into LDS (global_load_lds_dwordx4), each of the 8
+// waves issuing 4 of a tile's 32 blocks; four tile buffers rotate, so three
+// tiles are in flight while one is scored, and two waves share a SIMD.
+// Per tile and wave:
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: block j of a K half is k-step
+//     j's A operand as it lies, the wave's 16 rotated query rows are B (in
+//     registers);
+//   * an online softmax per query row (8 keys of one row per lane);
+//   * O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with 32 key slots (slot
+//     8c + i: key 4c + i of the first half, 8c + 4 + i the same key of the
+//     second), V^T's operand two transposing reads (ds_read_b64_tr_b16).
 // Masks: a cached key is dropped for token t as in decode_multi_kernel
 // (sliding: the ring slots tokens 0..t-1 replace); chunk key x is seen by
 // token t iff x <= t (tokens <= 512, so the window never excludes one).
-constexpr int kPfWaves = 4;
-constexpr int kPfRows = 16 * kPfWaves;        // query rows per workgroup
-constexpr int kPfTile = 32;                   // keys per LDS tile
-constexpr int kPfPitch = kHeadDim + 8;        // LDS row pitch (bf16)
-constexpr int kPfStage = 2 * kPfTile * kPfPitch;  // K then V rows of one tile
-constexpr int kPfLoads = 2 * kPfTile * (kHeadDim / 8) / (kPfWaves * 64);  // 16-byte loads a thread
-static_assert(kPfLoads * kPfWaves * 64 == 2 * kPfTile * (kHeadDim / 8), "tile loads divide evenly");
+// Rows no query may read (past the cache's live rows or the chunk) are
+// loaded from a zero row.
+constexpr int kPfWaves = 8;
+constexpr int kPfRows = 16 * kPfWaves;       // query rows per workgroup
+constexpr int kPfTile = 32;                  // keys per LDS tile
+constexpr int kPfHalf = 16 * kHeadDim * 2;   // bytes of one 16-row half of K (or V)
+constexpr int kPfKSteps = kHeadDim / 32;     // 8 blocks per half
+constexpr int kPfBlocks = 4 * kPfKSteps;     // K a, K b, V a, V b
+constexpr int kPfBlocksPerWave = kPfBlocks / kPfWaves;
+constexpr int kPfBufs = 4;
+constexpr int kPfAhead = 4;                  // K operand reads in flight
+constexpr int kPfTrAhead = 6;                // V^T read pairs in flight
+static_assert(kPfBlocksPerWave * kPfWaves == kPfBlocks && kPfBlocksPerWave < 16, "blocks split evenly");
+static_assert(kHeadDim <= 576, "the zero row covers a row");
 
 template <int G>
-__global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_chunk_kernel(MultiParams p, int nrb) {
+__global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiParams p, int nrb) {
     constexpr int D = kHeadDim;
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    __shared__ __align__(16) uint16_t s_tile[2][kPfStage];
+    __shared__ __align__(1024) unsigned char s_buf[kPfBufs][4 * kPfHalf];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mrow = lane & 15, kg = lane >> 4;
     const int Hkv = p.num_kv_heads, Hq = p.num_q_heads, T = p.tokens;
     const int RG = T * G;
@@ -385,126 +400,186 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_chunk_kernel(MultiPa
     const int64_t bh = (int64_t)b * Hkv + kvh;
     const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
 
-    // Tile i's 16-byte loads for this thread: chunk c = tid + 256 u covers
-    // row (c / 32) % 32 of K (c < 1024) or V, dims 8 (c % 32) .. +7.
-    auto load = [&](int i, uint4 *r) HDA_INLINE {
-#pragma unroll
-        for (int u = 0; u < kPfLoads; ++u) {
-            const int c = tid + kPfWaves * 64 * u;
-            const bool isv = c >= kPfTile * (D / 8);
-            const int row = (c / (D / 8)) % kPfTile, d8 = 8 * (c % (D / 8));
-            const uint16_t *src;
-            bool keep = true;
-            if (i < n_ct) {  // cache rows, the last tile kept inside the block
-                const int64_t r0 = min((int64_t)kPfTile * i, cap - kPfTile);
-                src = (isv ? vblk : kblk) + (r0 + row) * D + d8;
-                // a row no query may read (unwritten, or the previous tile's)
-                // goes in as 0: a zero weight would not cancel a NaN there
-                keep = r0 + row >= (int64_t)kPfTile * i && r0 + row < n_old;
-            } else {          // chunk rows: rotated K from the workspace, V from v_new
-                const int tok = min(kPfTile * (i - n_ct) + row, T - 1);
-                const int64_t nr = (((int64_t)b * T + tok) * Hkv + kvh) * D + d8;
-                src = (isv ? p.v_new : p.k_rot) + nr;
+    // Row r of half h of tile i for this lane: K and V sources (the zero
+    // row for a row no query reads).  Cache tiles keep their last rows
+    // inside the block (r0 = min(32 i, cap - 32)).
+    auto rows_of = [&](int i, int h, const uint16_t *&ks, const uint16_t *&vs) HDA_INLINE {
+        ks = vs = g_zero_row;
+        if (i < n_ct) {
+            const int64_t r0 = min((int64_t)kPfTile * i, cap - kPfTile);
+            const int64_t r = r0 + 16 * h + mrow;
+            if (r >= (int64_t)kPfTile * i && r < n_old) {
+                ks = kblk + r * D;
+                vs = vblk + r * D;
             }
-            const uint4 v = ld16(src);
-            r[u] = keep ? v : make_uint4(0, 0, 0, 0);
+        } else if (i < n_tiles) {  // chunk rows: rotated K from the workspace, V from v_new
+            const int tok = kPfTile * (i - n_ct) + 16 * h + mrow;
+            if (tok < T) {
+                const int64_t nr = (((int64_t)b * T + tok) * Hkv + kvh) * D;
+                ks = p.k_rot + nr;
+                vs = p.v_new + nr;
+            }
         }
     };
-    auto store = [&](int stage, const uint4 *r) HDA_INLINE {
+    // This wave's blocks of tile i (blocks wave, wave + 4, ...: K of half
+    // 0, K of half 1, V of half 0, V of half 1); past the last tile every
+    // lane reads the zero row, so that each tile leaves the same number of
+    // loads behind it.
+    auto issue = [&](int i, unsigned char *buf) HDA_INLINE {
+        const uint16_t *k0, *v0, *k1, *v1;
+        rows_of(i, 0, k0, v0);
+        rows_of(i, 1, k1, v1);
 #pragma unroll
-        for (int u = 0; u < kPfLoads; ++u) {
-            const int c = tid + kPfWaves * 64 * u;
-            const int kv = c / (kPfTile * (D / 8)), row = (c / (D / 8)) % kPfTile, d8 = 8 * (c % (D / 8));
-            *reinterpret_cast<uint4 *>(&s_tile[stage][(kv * kPfTile + row) * kPfPitch + d8]) = r[u];
+        for (int m = 0; m < kPfBlocksPerWave; ++m) {
+            const int blk = wave + kPfWaves * m;  // 0..31, wave-uniform
+            const int sec = blk / kPfKSteps, j = blk % kPfKSteps;  // K a, K b, V a, V b
+            const uint16_t *row = sec == 0 ? k0 : sec == 1 ? k1 : sec == 2 ? v0 : v1;
+            load_to_lds(row + 32 * j + 8 * kg, buf + 1024 * blk);
         }
     };
 
     // B operand: lane (row mrow, kg) holds q[row][32j + 8kg .. +7] (rotated in place)
-    bf16x8 qb[8];
+    uint4 qb[kPfKSteps];
     {
         const uint16_t *qr = p.q + out_row(min(my_row, RG - 1)) * D + 8 * kg;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qb[j] = as_bf16x8(ld16(qr + 32 * j));
+        for (int j = 0; j < kPfKSteps; ++j) qb[j] = ld16(qr + 32 * j);
     }
+    issue(0, s_buf[0]);
+    issue(1, s_buf[1]);
+    issue(2, s_buf[2]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q and tiles 0..2 in
+    __syncthreads();
+
     f32x4 acc[D / 16];
 #pragma unroll
     for (int d = 0; d < D / 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_lane = 0.f;  // row mrow; l over this lane's keys
+    // V^T transposing read of dim tile d in a half: row 4c + a, dims
+    // 16d + 8b + 4e .. +3 for mrow = 4a + 2b + e, at 512 d + this offset
+    const int tr_off = 64 * kg + 16 * (mrow >> 2) + 256 * ((mrow >> 1) & 1) + 8 * (mrow & 1);
 
-    uint4 regs[kPfLoads];
-    load(0, regs);
-    store(0, regs);
-    __syncthreads();
-    for (int i = 0; i < n_tiles; ++i) {
-        const int stage = i & 1;
-        if (i + 1 < n_tiles) load(i + 1, regs);
-        const uint16_t *kt = &s_tile[stage][0], *vt = &s_tile[stage][kPfTile * kPfPitch];
+    auto compute = [&](int i, const unsigned char *buf) HDA_INLINE {
+        // key 4kg + e of each half: its validity for this lane's row
+        bool ok[8];
+        const int64_t r0 = min((int64_t)kPfTile * i, cap - kPfTile);
+        int dbase = 0;  // (r0 - p0) mod (window - 1): the tile's first slot's distance
+        if (i < n_ct && p.sliding) {
+            dbase = (int)((r0 - p0) % W1);
+            dbase += dbase < 0 ? W1 : 0;
+        }
 #pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-            // key k = 4kg + e of this half: its validity for this lane's row
-            bool ok[4];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int kk = kPfTile * i + 16 * hlf + 4 * kg + e;  // key index over the sequence's key list
+                const int k = 16 * h + 4 * kg + e;
+                bool v;
                 if (i < n_ct) {
-                    const int64_t r0 = min((int64_t)kPfTile * i, cap - kPfTile);
-                    const int slot = (int)(r0 + 16 * hlf + 4 * kg + e);
-                    bool v = slot >= kPfTile * i && slot < n_old;
+                    const int slot = (int)(r0 + k);
+                    v = slot >= kPfTile * i && slot < n_old;
                     if (p.sliding) {
-                        int dk = (slot - p0) % W1;
-                        dk = dk < 0 ? dk + W1 : dk;
+                        int dk = dbase + k;
+                        if (W1 >= kPfTile) dk -= dk >= W1 ? W1 : 0;  // one wrap at most
+                        else dk %= W1;                              // a window under a tile
                         v = v && dk >= t_row;
                     }
-                    ok[e] = v;
                 } else {
-                    const int xk = kk - kPfTile * n_ct;  // chunk token
-                    ok[e] = xk <= t_row && xk < T;
+                    const int xk = kPfTile * (i - n_ct) + k;  // chunk token
+                    v = xk <= t_row && xk < T;
                 }
+                ok[4 * h + e] = v;
             }
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        // scores: lane (row mrow, kg) gets keys 4kg + e of each half
+        f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
+        uint4 ka[kPfAhead], kb[kPfAhead];
+        auto k_read = [&](int j) HDA_INLINE {
+            ka[j % kPfAhead] = ld16(buf + 1024 * j + 16 * lane);
+            kb[j % kPfAhead] = ld16(buf + kPfHalf + 1024 * j + 16 * lane);
+        };
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint4 ka = *reinterpret_cast<const uint4 *>(kt + (16 * hlf + mrow) * kPfPitch + 32 * j + 8 * kg);
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], sc, 0, 0, 0);
-            }
-            float s[4], tmax = -INFINITY;
+        for (int j = 0; j < kPfAhead; ++j) k_read(j);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s[e] = ok[e] ? sc[e] * p.scale_log2 : -INFINITY;
-                tmax = fmaxf(tmax, s[e]);
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run, tmax);
-            const float mr = m_new == -INFINITY ? 0.f : m_new;  // no key for this row yet
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mr);  // -inf - x: 0
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int d = 0; d < D / 16; ++d) acc[d] *= alpha;
-            }
-            float pv[4], ps = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(s[e] - mr);
-                ps += pv[e];
-            }
-            l_lane = fmaf(l_lane, alpha, ps);
-            m_run = m_new;
-            const v4i16 pb = {(short)f32_to_bf16(pv[0]), (short)f32_to_bf16(pv[1]), (short)f32_to_bf16(pv[2]),
-                              (short)f32_to_bf16(pv[3])};
-            const uint16_t *trb = vt + (16 * hlf + 4 * kg + (mrow >> 2)) * kPfPitch + 4 * (mrow & 3);
-#pragma unroll
-            for (int d = 0; d < D / 16; ++d) {
-                const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(trb + 16 * d));
-                acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[d], 0, 0, 0);
+        for (int j = 0; j < kPfKSteps; ++j) {
+            const bf16x8 a = as_bf16x8(ka[j % kPfAhead]), bb = as_bf16x8(kb[j % kPfAhead]);
+            if (j + kPfAhead < kPfKSteps) k_read(j + kPfAhead);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead
+            const bf16x8 qj = as_bf16x8(qb[j]);
+            if (j & 1) {
+                sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qj, sa1, 0, 0, 0);
+                sb1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb, qj, sb1, 0, 0, 0);
+            } else {
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qj, sa0, 0, 0, 0);
+                sb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb, qj, sb0, 0, 0, 0);
             }
         }
-        if (i + 1 < n_tiles) {
-            __syncthreads();  // every wave is done with the other stage
-            store(stage ^ 1, regs);
-            __syncthreads();
+        float s[8], tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[e] = ok[e] ? (sa0[e] + sa1[e]) * p.scale_log2 : -INFINITY;
+            s[4 + e] = ok[4 + e] ? (sb0[e] + sb1[e]) * p.scale_log2 : -INFINITY;
         }
-    }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float mr = m_new == -INFINITY ? 0.f : m_new;  // no key for this row yet
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mr);  // -inf - x: 0
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int d = 0; d < D / 16; ++d) acc[d] *= alpha;
+        }
+        float pw[8], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pw[e] = __builtin_amdgcn_exp2f(s[e] - mr);
+            ps += pw[e];
+        }
+        l_lane = fmaf(l_lane, alpha, ps);
+        m_run = m_new;
+        const bf16x8 pb = as_bf16x8(make_uint4(pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
+                                               pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7])));
+        // V^T reads run kPfTrAhead dim tiles ahead of the products that use them
+        const unsigned char *vt = buf + 2 * kPfHalf;
+        v4i16 vlo[kPfTrAhead], vhi[kPfTrAhead];
+        auto tr_read = [&](int d) HDA_INLINE {
+            vlo[d % kPfTrAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vt + tr_off + 512 * d));
+            vhi[d % kPfTrAhead] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vt + kPfHalf + tr_off + 512 * d));
+        };
+#pragma unroll
+        for (int d = 0; d < kPfTrAhead; ++d) tr_read(d);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < D / 16; ++d) {
+            const v4i16 lo = vlo[d % kPfTrAhead], hi = vhi[d % kPfTrAhead];
+            if (d + kPfTrAhead < D / 16) tr_read(d + kPfTrAhead);
+            __builtin_amdgcn_sched_barrier(0);
+            uint4 vu;
+            vu.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+            vu.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+            vu.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+            vu.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+            acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vu), pb, acc[d], 0, 0, 0);
+        }
+    };
+
+    // One tile: wait for this wave's blocks of tile i (tiles i + 1 and i + 2
+    // may still be in flight), meet the other waves (their blocks are in,
+    // and all are done with tile i - 1's buffer), refill that buffer with
+    // tile i + 3, score tile i.
+    auto step = [&](int i, const unsigned char *cur, unsigned char *refill) HDA_INLINE {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPfBlocksPerWave));  // tiles i + 1, i + 2 may be out
+        raw_barrier();
+        issue(i + 3, refill);
+        compute(i, cur);
+    };
+    static_assert(2 * kPfBlocksPerWave < 64, "vmcnt counts to 63");
+    // (the tile loads are asm the compiler does not see, so a loop over
+    // computed buffers keeps its waits exact)
+    for (int i = 0; i < n_tiles; ++i) step(i, s_buf[i % kPfBufs], s_buf[(i + kPfBufs - 1) % kPfBufs]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads past the end have landed
 
     // out / lse of this lane's row: dims 16d + 4kg .. +3 of every tile d
     float l = l_lane + __shfl_xor(l_lane, 16, 64);
@@ -517,11 +592,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void prefill_chunk_kernel(MultiPa
     if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
     if (p.gate) f *= gate_factor(p.gate[orow]);
 #pragma unroll
-    for (int d = 0; d < D / 16; ++d) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(acc[d][0] * f) | ((uint32_t)f32_to_bf16(acc[d][1] * f) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(acc[d][2] * f) | ((uint32_t)f32_to_bf16(acc[d][3] * f) << 16);
-        *reinterpret_cast<uint2 *>(p.out + orow * D + 16 * d + 4 * kg) = make_uint2(lo, hi);
-    }
+    for (int d = 0; d < D / 16; ++d)
+        *reinterpret_cast<uint2 *>(p.out + orow * D + 16 * d + 4 * kg) =
+            make_uint2(pack_bf16x2(acc[d][0] * f, acc[d][1] * f), pack_bf16x2(acc[d][2] * f, acc[d][3] * f));
     if (kg == 0 && p.lse) p.lse[orow] = lse;
 }
 

@@ -210,4 +210,41 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------- LDS tiles
+// Stands in for the row of a key without one (a zero weight would not
+// cancel a NaN that the row it replaces might hold); 576 bf16, the longest
+// row any kernel reads.
+static __device__ __align__(16) const uint16_t g_zero_row[576] = {};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes a lane from src to LDS at dst + 16 lane (dst wave-uniform), with
+// global_load_lds_dwordx4.  Written in asm so that the compiler, which
+// cannot tell tile buffers apart behind a computed address, does not wait
+// for every such load before each LDS read; the waits on these loads are
+// the callers' explicit vmcnt waits, so a caller issues no other vector
+// memory loads between them.  No register receives data.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
+__device__ __forceinline__ void load_to_lds(const void *src, unsigned char *dst) {
+    // the LDS aperture is 4 GiB aligned: a shared pointer's low word is its LDS address
+    const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate for vmcnt(n) alone (expcnt and lgkmcnt at their
+// maxima): vmcnt's low four bits at [3:0], its high two at [15:14].
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// A workgroup barrier without the memory fences __syncthreads() brings
+// (those wait for every outstanding load); the compiler may not move memory
+// accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace hda

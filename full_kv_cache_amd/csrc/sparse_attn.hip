@@ -370,32 +370,6 @@ constexpr int kBlocksPerWave = kTileBlocks / kTileWaves;
 static_assert(kBlocksPerWave * kTileWaves == kTileBlocks, "blocks split evenly over the waves");
 static_assert(kTileWaves * kSparseHeadsPerWave == kSparseTileHeads, "a wave per 16 heads");
 
-// Stands in for the row of a key without one.
-__device__ __align__(16) const uint16_t g_zero_row[kSparseDqk] = {};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes a lane from src to LDS at dst + 16 lane (dst wave-uniform).
-// Written in asm so that the compiler, which cannot tell the tile buffers
-// apart behind a computed address, does not wait for every such load before
-// each LDS read; the waits on these loads are the explicit vmcnt waits of
-// the tile loop.  No register receives data.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
-__device__ __forceinline__ void load_to_lds(const void *src, unsigned char *dst) {
-    // the LDS aperture is 4 GiB aligned: a shared pointer's low word is its LDS address
-    const uint32_t m0 = (uint32_t)(uintptr_t)dst;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(src) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ void raw_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 template <bool FINAL>
 __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseParams p) {
     __shared__ __align__(1024) unsigned char s_b0[2 * kHalfBytes];
