@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kHeadDim) void multi_merge_kernel(MultiParams p, in
 // up to the block's last token -- pass through LDS in tiles of 32 that all
 // waves of the workgroup score.  A tile is two 16-row halves of K then V,
 // each in one-KiB blocks: block j of a half holds, at byte 16 l, lane
-// l = r + 16 c's 16 bytes (row r, dims 32j + 8c .. +7).  The rows go
+// l = r' + 16 c's 16 bytes (row r = r' ^ 12 (c & 1), dims 32j + 8c .. +7).  The rows go
 // straight from memory into LDS (global_load_lds_dwordx4), each of the 8
 // waves issuing 4 of a tile's 32 blocks; four tile buffers rotate, so three
 // tiles are in flight while one is scored, and two waves share a SIMD.
@@ -368,6 +368,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mrow = lane & 15, kg = lane >> 4;
+    // the row whose 16 bytes land in this lane's slot of a block (odd
+    // 16-byte columns swizzled, xor 12, for the transposing reads' banks)
+    const int drow = mrow ^ (12 * (kg & 1));
     const int Hkv = p.num_kv_heads, Hq = p.num_q_heads, T = p.tokens;
     const int RG = T * G;
     // block ids: the row blocks of a pair are congruent mod 8 (one XCD, so
@@ -407,13 +410,13 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
         ks = vs = g_zero_row;
         if (i < n_ct) {
             const int64_t r0 = min((int64_t)kPfTile * i, cap - kPfTile);
-            const int64_t r = r0 + 16 * h + mrow;
+            const int64_t r = r0 + 16 * h + drow;
             if (r >= (int64_t)kPfTile * i && r < n_old) {
                 ks = kblk + r * D;
                 vs = vblk + r * D;
             }
         } else if (i < n_tiles) {  // chunk rows: rotated K from the workspace, V from v_new
-            const int tok = kPfTile * (i - n_ct) + 16 * h + mrow;
+            const int tok = kPfTile * (i - n_ct) + 16 * h + drow;
             if (tok < T) {
                 const int64_t nr = (((int64_t)b * T + tok) * Hkv + kvh) * D;
                 ks = p.k_rot + nr;
@@ -457,7 +460,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     float m_run = -INFINITY, l_lane = 0.f;  // row mrow; l over this lane's keys
     // V^T transposing read of dim tile d in a half: row 4c + a, dims
     // 16d + 8b + 4e .. +3 for mrow = 4a + 2b + e, at 512 d + this offset
-    const int tr_off = 64 * kg + 16 * (mrow >> 2) + 256 * ((mrow >> 1) & 1) + 8 * (mrow & 1);
+    // (the row's slot swizzled as the loads place it)
+    const int tr_b = (mrow >> 1) & 1;
+    const int tr_off = 256 * tr_b + 16 * ((4 * kg + (mrow >> 2)) ^ (12 * tr_b)) + 8 * (mrow & 1);
 
     auto compute = [&](int i, const unsigned char *buf) HDA_INLINE {
         // key 4kg + e of each half: its validity for this lane's row
@@ -493,8 +498,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
         f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
         uint4 ka[kPfAhead], kb[kPfAhead];
         auto k_read = [&](int j) HDA_INLINE {
-            ka[j % kPfAhead] = ld16(buf + 1024 * j + 16 * lane);
-            kb[j % kPfAhead] = ld16(buf + kPfHalf + 1024 * j + 16 * lane);
+            ka[j % kPfAhead] = ld16(buf + 1024 * j + 16 * (drow + 16 * kg));
+            kb[j % kPfAhead] = ld16(buf + kPfHalf + 1024 * j + 16 * (drow + 16 * kg));
         };
 #pragma unroll
         for (int j = 0; j < kPfAhead; ++j) k_read(j);

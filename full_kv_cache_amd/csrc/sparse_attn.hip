@@ -344,8 +344,8 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
 // per (token, key split) serves every head -- wave w owns heads 16w..16w+15
 // -- so each gathered row crosses from L2 into the CU once, not once per
 // head group.  A tile is 32 keys, two 16-row halves of 18 one-KiB blocks;
-// block j of a half holds, at byte 16 l, lane l = r + 16 c's 16 bytes: row
-// r, dims 32j + 8c .. +7.  The rows go straight from memory into LDS
+// block j of a half holds, at byte 16 l, lane l = r' + 16 c's 16 bytes: row
+// r = r' ^ 12 (c & 1), dims 32j + 8c .. +7.  The rows go straight from memory into LDS
 // (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), each
 // wave issuing 9 of the tile's 36 blocks; three tile buffers rotate, so two
 // tiles are in flight while one is scored.  Per wave and tile:
@@ -381,6 +381,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mrow = lane & 15, kg = lane >> 4;
+    // the row whose 16 bytes land in this lane's slot of a block: rows of the
+    // odd 16-byte columns are swizzled (xor 12) so that the transposing reads
+    // of a block's two column halves meet different banks
+    const int drow = mrow ^ (12 * (kg & 1));
     const int x = blockIdx.x, j8 = x >> 3;
     const int t = (j8 / p.nsplit) * 8 + (x & 7), sp = j8 % p.nsplit;
     if (t >= p.tokens) return;  // the whole workgroup
@@ -418,8 +422,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     // Tiles 0 and 1 go in flight first, their rows read straight from the
     // index row; then q and the rest of the split's rows (into s_idx).
     {
-        const int r0a = row_at(mrow), r0b = row_at(16 + mrow);
-        const int r1a = row_at(kTileKeys + mrow), r1b = row_at(kTileKeys + 16 + mrow);
+        const int r0a = row_at(drow), r0b = row_at(16 + drow);
+        const int r1a = row_at(kTileKeys + drow), r1b = row_at(kTileKeys + 16 + drow);
         issue_rows(r0a, r0b, s_b0);
         issue_rows(r1a, r1b, s_b1);
     }
@@ -443,8 +447,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     auto issue = [&](int i, unsigned char *buf) HDA_INLINE {
         int ra = -1, rb = -1;
         if (i < ntile) {
-            ra = s_idx[kTileKeys * i + mrow];
-            rb = s_idx[kTileKeys * i + 16 + mrow];
+            ra = s_idx[kTileKeys * i + drow];
+            rb = s_idx[kTileKeys * i + 16 + drow];
         }
         issue_rows(ra, rb, buf);
     };
@@ -456,7 +460,9 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     bool over = false;
     // V^T transposing read of dim tile d in a half: row 4c + a, dims
     // 16d + 8b + 4e .. +3 for mrow = 4a + 2b + e, at 512 d + this offset
-    const int tr_off = 64 * kg + 16 * (mrow >> 2) + 256 * ((mrow >> 1) & 1) + 8 * (mrow & 1);
+    // (the row's slot swizzled as the loads place it)
+    const int tr_b = (mrow >> 1) & 1;
+    const int tr_off = 256 * tr_b + 16 * ((4 * kg + (mrow >> 2)) ^ (12 * tr_b)) + 8 * (mrow & 1);
 
     auto compute = [&](int i, const unsigned char *buf) HDA_INLINE {
         const int ra = s_idx[kTileKeys * i + mrow], rb = s_idx[kTileKeys * i + 16 + mrow];
@@ -468,8 +474,8 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
         f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = sa0, sb0 = sa0, sb1 = sa0;
         uint4 ka[kKAhead], kb[kKAhead];
         auto k_read = [&](int j) HDA_INLINE {
-            ka[j % kKAhead] = ld16(buf + 1024 * j + 16 * lane);
-            kb[j % kKAhead] = ld16(buf + kHalfBytes + 1024 * j + 16 * lane);
+            ka[j % kKAhead] = ld16(buf + 1024 * j + 16 * (drow + 16 * kg));
+            kb[j % kKAhead] = ld16(buf + kHalfBytes + 1024 * j + 16 * (drow + 16 * kg));
         };
 #pragma unroll
         for (int j = 0; j < kKAhead; ++j) k_read(j);
