@@ -422,8 +422,17 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     // Tiles 0 and 1 go in flight first, their rows read straight from the
     // index row; then q and the rest of the split's rows (into s_idx).
     {
-        const int r0a = row_at(drow), r0b = row_at(16 + drow);
-        const int r1a = row_at(kTileKeys + drow), r1b = row_at(kTileKeys + 16 + drow);
+        int r0a = -1, r0b = -1, r1a = -1, r1b = -1;
+        if (nk > 0) {  // the four entries' loads issued together (no index to read otherwise)
+            const int e0 = idx[min(drow, nk - 1)], e1 = idx[min(16 + drow, nk - 1)];
+            const int e2 = idx[min(kTileKeys + drow, nk - 1)], e3 = idx[min(kTileKeys + 16 + drow, nk - 1)];
+            __builtin_amdgcn_sched_barrier(0);
+            auto valid = [&](int k, int r) { return k < nk && r >= 0 && (int64_t)r < p.pool_rows ? r : -1; };
+            r0a = valid(drow, e0);
+            r0b = valid(16 + drow, e1);
+            r1a = valid(kTileKeys + drow, e2);
+            r1b = valid(kTileKeys + 16 + drow, e3);
+        }
         issue_rows(r0a, r0b, s_b0);
         issue_rows(r1a, r1b, s_b1);
     }
