@@ -344,10 +344,13 @@ __global__ __launch_bounds__(kHeadDim) void multi_merge_kernel(MultiParams p, in
 // (sliding: the ring slots tokens 0..t-1 replace); chunk key x is seen by
 // token t iff x <= t (tokens <= 512, so the window never excludes one).
 // Rows no query may read (past the cache's live rows or the chunk) are
-// loaded from a zero row.
+// loaded from a zero row.  With p.split = S > 1 (small batches) the key
+// tiles are cut into S ranges, one workgroup each, and each writes a
+// normalised partial (o, lse) per row that multi_merge_kernel combines.
 constexpr int kPfWaves = 8;
 constexpr int kPfRows = 16 * kPfWaves;       // query rows per workgroup
-constexpr int kPfTile = 32;                  // keys per LDS tile
+constexpr int kPfTile = kPrefillTile;        // keys per LDS tile
+static_assert(kPfRows == kPrefillRows, "the host plans with the same row blocks");
 constexpr int kPfHalf = 16 * kHeadDim * 2;   // bytes of one 16-row half of K (or V)
 constexpr int kPfKSteps = kHeadDim / 32;     // 8 blocks per half
 constexpr int kPfBlocks = 4 * kPfKSteps;     // K a, K b, V a, V b
@@ -375,8 +378,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     const int RG = T * G;
     // block ids: the row blocks of a pair are congruent mod 8 (one XCD, so
     // they meet the pair's keys in its L2)
-    const int x = blockIdx.x;
-    const int rb = (x >> 3) % nrb, pair = ((x >> 3) / nrb) * 8 + (x & 7);
+    const int x = blockIdx.x, S = p.split;
+    const int rb = (x >> 3) % nrb, rest = (x >> 3) / nrb;
+    const int sp = rest % S, pair = (rest / S) * 8 + (x & 7);
     if (pair >= p.batch * Hkv) return;
     const int b = pair / Hkv, kvh = pair % Hkv;
     const int32_t p0 = p.pos[b];
@@ -387,12 +391,22 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
 
     // the wave's 16 rows: out and lse of row m at ((b, t), kvh * G + h)
     auto out_row = [&](int m) HDA_INLINE { return ((int64_t)b * T + m / G) * Hq + kvh * G + m % G; };
-    if (p0 < 0) {  // no tokens: out 0, lse -inf
+    auto part_row = [&](int m) HDA_INLINE { return ((int64_t)pair * S + sp) * RG + m; };
+    if (p0 < 0) {  // no tokens: out 0, lse -inf (split: an empty partial)
         for (int i = lane; i < 16 * D / 8; i += 64) {
             const int m = row0 + i / (D / 8);
-            if (m < RG) *reinterpret_cast<uint4 *>(p.out + out_row(m) * D + 8 * (i % (D / 8))) = make_uint4(0, 0, 0, 0);
+            if (m >= RG) continue;
+            if (S == 1)
+                *reinterpret_cast<uint4 *>(p.out + out_row(m) * D + 8 * (i % (D / 8))) = make_uint4(0, 0, 0, 0);
+            else
+                *reinterpret_cast<float4 *>(p.part_o + part_row(m) * D + 8 * (i % (D / 8))) =
+                    *reinterpret_cast<float4 *>(p.part_o + part_row(m) * D + 8 * (i % (D / 8)) + 4) =
+                        make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        if (lane < 16 && my_row < RG && p.lse) p.lse[out_row(my_row)] = -INFINITY;
+        if (lane < 16 && my_row < RG) {
+            if (S > 1) p.part_lse[part_row(my_row)] = -INFINITY;
+            else if (p.lse) p.lse[out_row(my_row)] = -INFINITY;
+        }
         return;
     }
     const int64_t cap = p.capacity;
@@ -400,6 +414,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     const int n_old = p0 == 0 ? 0 : p.sliding ? min(p0, W1) : (int)min((int64_t)p0, cap);
     const int n_ct = (n_old + kPfTile - 1) / kPfTile;         // cache tiles
     const int n_tiles = n_ct + t_hi / kPfTile + 1;            // + chunk tiles up to t_hi
+    const int i0 = sp * n_tiles / S, i1 = (sp + 1) * n_tiles / S;  // this workgroup's tiles
     const int64_t bh = (int64_t)b * Hkv + kvh;
     const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
 
@@ -430,6 +445,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     // loads behind it.
     auto issue = [&](int i, unsigned char *buf) HDA_INLINE {
         const uint16_t *k0, *v0, *k1, *v1;
+        if (i >= i1) i = n_tiles;  // past this workgroup's tiles: zero rows
         rows_of(i, 0, k0, v0);
         rows_of(i, 1, k1, v1);
 #pragma unroll
@@ -448,9 +464,9 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
 #pragma unroll
         for (int j = 0; j < kPfKSteps; ++j) qb[j] = ld16(qr + 32 * j);
     }
-    issue(0, s_buf[0]);
-    issue(1, s_buf[1]);
-    issue(2, s_buf[2]);
+    issue(i0, s_buf[0]);
+    issue(i0 + 1, s_buf[1]);
+    issue(i0 + 2, s_buf[2]);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q and tiles 0..2 in
     __syncthreads();
 
@@ -574,7 +590,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     // may still be in flight), meet the other waves (their blocks are in,
     // and all are done with tile i - 1's buffer), refill that buffer with
     // tile i + 3, score tile i.
-    auto step = [&](int i, const unsigned char *cur, unsigned char *refill) HDA_INLINE {
+    auto step = [&](int i, const unsigned char *cur, unsigned char *refill) HDA_INLINE {  // i from i0
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPfBlocksPerWave));  // tiles i + 1, i + 2 may be out
         raw_barrier();
         issue(i + 3, refill);
@@ -583,13 +599,23 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     static_assert(2 * kPfBlocksPerWave < 64, "vmcnt counts to 63");
     // (the tile loads are asm the compiler does not see, so a loop over
     // computed buffers keeps its waits exact)
-    for (int i = 0; i < n_tiles; ++i) step(i, s_buf[i % kPfBufs], s_buf[(i + kPfBufs - 1) % kPfBufs]);
+    for (int k = 0; k < i1 - i0; ++k) step(i0 + k, s_buf[k % kPfBufs], s_buf[(k + kPfBufs - 1) % kPfBufs]);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads past the end have landed
 
     // out / lse of this lane's row: dims 16d + 4kg .. +3 of every tile d
     float l = l_lane + __shfl_xor(l_lane, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (my_row >= RG) return;
+    if (S > 1) {  // this range's normalised partial and its lse (none: 0 and -inf)
+        const int64_t prow = part_row(my_row);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int d = 0; d < D / 16; ++d)
+            *reinterpret_cast<float4 *>(p.part_o + prow * D + 16 * d + 4 * kg) =
+                make_float4(acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv);
+        if (kg == 0) p.part_lse[prow] = l > 0.f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        return;
+    }
     const int64_t orow = out_row(my_row);
     const int hq = kvh * G + my_row % G;
     const float lse = (m_run + log2f(l)) * kLn2;  // every row sees its own token's key
@@ -607,8 +633,12 @@ template <int G>
 hipError_t launch_prefill_g(const MultiParams &p, hipStream_t s) {
     const int nrb = (p.tokens * G + kPfRows - 1) / kPfRows;
     const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
-    const int64_t blocks = (pairs + 7) / 8 * 8 * nrb;
+    const int64_t blocks = (pairs + 7) / 8 * 8 * nrb * p.split;
     hipLaunchKernelGGL((prefill_chunk_kernel<G>), dim3((unsigned)blocks), dim3(kPfWaves * 64), 0, s, p, nrb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.split == 1) return e;
+    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)(pairs * G * p.tokens)), dim3(kHeadDim), 0, s, p,
+                       G * p.tokens, G);
     return hipGetLastError();
 }
 

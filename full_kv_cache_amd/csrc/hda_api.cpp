@@ -809,13 +809,22 @@ hda_status check_multi_shape(const hda_cache_desc *c, int layer, int32_t tokens,
 // at least 16 rounds (8 with few pairs).  max_seq_len bounds pos + tokens; it only sizes the
 // split (every workgroup takes its share of the rounds the sequence has).
 int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_seq_len) {
-    if ((c->num_q_heads / c->num_kv_heads) * tokens > 16) return 1;  // the prefill kernel: no split
     int64_t n_old = (int64_t)max_seq_len - tokens;
     if (n_old < 0) n_old = 0;
     const int64_t lim = layer == HDA_SLIDING ? (int64_t)c->window - 1 : c->capacity;
     if (n_old > lim) n_old = lim;
-    const int64_t rounds = (n_old + 15) / 16;
     const int64_t pairs = (int64_t)c->batch * c->num_kv_heads;
+    const int64_t g = c->num_q_heads / c->num_kv_heads;
+    if (g * tokens > 16) {
+        // the prefill kernel: cut the key tiles into ranges when its row
+        // blocks leave the GPU short of 256 workgroups, keeping 8 tiles a range
+        const int64_t blocks = pairs * ((g * tokens + hda::kPrefillRows - 1) / hda::kPrefillRows);
+        const int64_t tiles = (n_old + tokens + hda::kPrefillTile - 1) / hda::kPrefillTile;
+        int s = 1;
+        while (s < hda::kPrefillMaxSplit && blocks * s < 256 && tiles / (2 * s) >= 8) s *= 2;
+        return s;
+    }
+    const int64_t rounds = (n_old + 15) / 16;
     const bool many = pairs >= 64;
     const int64_t target = many ? 256 : 128, min_rounds = many ? 16 : 8;
     int64_t s = pairs > 0 ? (target + pairs - 1) / pairs : 1;

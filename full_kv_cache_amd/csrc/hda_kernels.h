@@ -173,6 +173,9 @@ struct SparseParams {
 // Decode of a chunk of `tokens` new tokens per sequence (q [B, T, Hq, D],
 // k_new / v_new [B, T, Hkv, D]; contiguous bf16 cache; tokens <= 512).
 constexpr int kMultiMaxTokens = 512;  // a chunk's tokens: the window never drops a chunk key
+constexpr int kPrefillRows = 128;     // query rows per workgroup of the prefill kernel
+constexpr int kPrefillTile = 32;      // keys per tile of the prefill kernel
+constexpr int kPrefillMaxSplit = 4;   // key splits of the prefill kernel
 
 struct MultiParams {
     uint16_t *q;                // rotated in place

@@ -425,7 +425,9 @@ def test_multi_workspace():
     """The workspace holds the rotated new K rows (bf16 [B, T, Hkv, D]);
     long contexts also split each pair's keys over several workgroups, whose
     partials (fp32 out + lse per query row) follow.  Prefill-sized chunks
-    (more than 16 query rows per KV head) are never split."""
+    (more than 16 query rows per KV head) split their key tiles (up to 4
+    ranges, at least 8 tiles of 32 keys each) while the row blocks leave
+    fewer than 256 workgroups."""
     L = hda.lib()
     full = _desc(capacity=4096, rotary_dim=64, rope_theta=5e6)
     krot = lambda T: (2 * T * 2 * 256 * 2 + 255) // 256 * 256
@@ -438,4 +440,9 @@ def test_multi_workspace():
     assert _multi(full, layer=hda.FULL, msl=4096) == 3 and "workspace" in _msg()
     assert _multi(full, layer=hda.FULL, msl=4096, ws=FAKE, wsb=need - 1) == 3
     assert _multi(full, layer=hda.FULL, msl=4096, ws=FAKE + 4, wsb=need) == 1
-    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 4096) == krot(5)
+    # 5 tokens x 4 heads: one 128-row block per pair, 4 pairs, 128 key tiles:
+    # 4 ranges; partial rows = pairs x 4 x 20
+    prows = 2 * 2 * 4 * 5 * 4
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 4096) == \
+        krot(5) + (prows * 256 * 4 + 255) // 256 * 256 + prows * 4
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 200) == krot(5)  # 7 tiles
