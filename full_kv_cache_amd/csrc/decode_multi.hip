@@ -12,11 +12,10 @@
 //   2. attention over the cache as it was before the chunk plus the chunk's
 //      own rows: prefill_chunk_kernel (below) when the chunk's tokens x G
 //      query rows per KV head exceed one MFMA operand's 16, else
-//      decode_multi_kernel: attention over the cache as it was before the
-//      chunk plus the chunk's own rows.  `split` workgroups per (sequence,
-//      KV head) share its cache rounds; the chunk's T x G query rows (row
-//      t*G + h) fill the MFMA A operand, so every K/V row loaded serves all
-//      T tokens.  Cache keys are masked per row: on a sliding layer token t
+//      decode_multi_kernel: `split` workgroups per (sequence, KV head)
+//      share its cache rounds; the chunk's T x G query rows (row t*G + h)
+//      are the columns of both MFMA products, so every K/V row loaded
+//      serves all T tokens.  Cache keys are masked per row: on a sliding layer token t
 //      drops the t oldest entries (ring slots pos .. pos+t-1 mod window-1,
 //      which tokens 0..t-1 replace); the new tokens are one more round, key
 //      x visible to rows of token t >= x, taken by the last wave of the
@@ -128,24 +127,48 @@ __global__ __launch_bounds__(128) void append_multi_kernel(MultiParams p) {
     }
 }
 
-template <int G, int T>
-struct MultiShape {
-    static constexpr int RG = G * T;                // query rows per (sequence, KV head)
-    static constexpr int WAVES = RG >= 8 ? 4 : 8;   // merge area WAVES x RG rows; registers
-};
+// Chunk decode, tokens x G <= 16 query rows per KV head: `split`
+// workgroups of kMultiWaves waves per (sequence, KV head) share its cache
+// rounds (16 keys; two in flight per wave, whole rows loaded into
+// registers as the decode kernels load them).  The chunk's rows (row
+// m = t G + h; rows past T G repeat row 0 and are never read) are the 16
+// columns of both products, so every K/V row loaded serves all T tokens.
+// Per round a wave writes the K and V rows into its LDS tiles in the
+// prefill kernel's 1-KiB block layout, then:
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K the A operand, the
+//     rotated query rows B, read from an LDS copy in the same layout);
+//   * an online softmax per query row: lane (row m, kg) holds keys
+//     4 kg .. 4 kg + 3 of the round;
+//   * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: V^T one transposing read
+//     per 16-dim tile, P^T the lane's own four probabilities (bf16).
+// Cache keys are masked per row: on a sliding layer token t drops the t
+// oldest entries (ring slots pos .. pos+t-1 mod window-1, which tokens
+// 0..t-1 replace); the new tokens are one more round, key x visible to
+// rows of token t >= x, taken by the last wave of the last workgroup.
+// Each workgroup merges its waves in LDS and writes out directly (split 1)
+// or a partial (o, lse) per row that multi_merge_kernel combines.
+constexpr int kMultiWaves = 8;
+constexpr int kMultiTile = 16 * kHeadDim * 2;  // bytes of 16 K (or V) rows
+constexpr int kMultiPitch = kHeadDim + 4;      // floats per row of a wave's o rows
+constexpr int kMultiAhead = 3;                 // K / q operand reads in flight
+constexpr int kMultiTrAhead = 4;               // V^T reads in flight
 
 template <int G, int T>
-__global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel(MultiParams p) {
+__global__ __launch_bounds__(kMultiWaves * 64, 1) void decode_multi_kernel(MultiParams p) {
     constexpr int D = kHeadDim;
-    constexpr int RG = MultiShape<G, T>::RG;
-    constexpr int WAVES = MultiShape<G, T>::WAVES;
-    __shared__ __align__(16) float s_red[WAVES * RG * D];
-    __shared__ __align__(16) float s_pw[WAVES][16 * RG];
-    __shared__ __align__(16) uint16_t s_kt[WAVES][kKTile];
-    __shared__ float s_m[WAVES][RG], s_l[WAVES][RG];
+    constexpr int RG = G * T;
+    constexpr int WAVES = kMultiWaves;
+    static_assert(RG <= 16, "the chunk's rows fill at most one operand");
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    // a wave's K and V tiles; after its rounds, its o rows [16][kMultiPitch]
+    constexpr int kWaveLds = 16 * kMultiPitch * 4 > 2 * kMultiTile ? 16 * kMultiPitch * 4 : 2 * kMultiTile;
+    __shared__ __align__(1024) unsigned char s_tile[WAVES][kWaveLds];
+    __shared__ __align__(1024) unsigned char s_q[kMultiTile];  // the 16 query rows, block layout
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int mrow = lane & 15, kg = lane >> 4;
+    const int mrow = lane & 15, kg = lane >> 4, hw = lane >> 5, dl = lane & 31;
     const int Hkv = p.num_kv_heads, Hq = p.num_q_heads;
     const int S = p.split, pair = blockIdx.x / S, part = blockIdx.x % S;
     const int b = pair / Hkv, kvh = pair % Hkv;
@@ -161,56 +184,149 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
     const int64_t bh = (int64_t)b * Hkv + kvh;
     const uint16_t *kblk = p.k + bh * cap * D, *vblk = p.v + bh * cap * D;
     auto r0e_of = [&](int r) { return (int)((int64_t)(16 * r) < cap16 ? 16 * r : cap16); };
+    const int trow = mrow < RG ? mrow / G : 0;  // the token of this lane's row
 
-    // token of each of this lane's four score rows (4*kg + i); rows past RG
-    // repeat row 0 and are never read
-    int trow[4], ntrow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * kg + i;
-        trow[i] = m < RG ? m / G : 0;
-        ntrow[i] = -trow[i];
-    }
+    // Tile layout (1-KiB block j = dims 32j .. 32j+31): this lane's 16 bytes
+    // of row r (dims 8 dl ..) go to slot r ^ 12 (c & 1) + 16 c of block dl / 4,
+    // c = dl % 4; the K operand of row mrow, dims 32j + 8kg, is read from slot
+    // drow + 16 kg; the transposing read of dim tile d from 512 d + tr_off
+    // gives keys 4kg .. +3 of dim 16d + mrow.
+    unsigned char *const ktl = s_tile[wave], *const vtl = s_tile[wave] + kMultiTile;
+    const int wblk = 1024 * (dl >> 2) + 256 * (dl & 3), wsw = 12 * (dl & 1);
+    const int drow = mrow ^ (12 * (kg & 1));
+    const int tr_b = (mrow >> 1) & 1;
+    const int tr_off = 256 * tr_b + 16 * ((4 * kg + (mrow >> 2)) ^ (12 * tr_b)) + 8 * (mrow & 1);
 
-    WaveSoftmax<RG> st;
-    st.reset();
-    bf16x8 qa[8];
-    if (p0 >= 0) {
-        {   // A operand: row m = t*G + h is q[b, t, kvh*G + h]
-            const int m = mrow < RG ? mrow : 0, t = m / G, h = m % G;
-            const uint16_t *qr = p.q + (((int64_t)b * T + t) * Hq + kvh * G + h) * D + 8 * kg;
+    f32x4 acc[D / 16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qa[j] = as_bf16x8(ld16(qr + 32 * j));
+    for (int d = 0; d < D / 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_lane = 0.f;  // row mrow; l over this lane's keys
+
+    // One round: kt / vt the 16 rows (lane = 8 dims of row 2u + hw); key
+    // 2u + hw's V row is taken only if vkeep (masked rows may hold anything,
+    // even NaN, which a zero weight would not cancel); ok[i]: key 4kg + i
+    // is seen by this lane's row.
+    auto mround = [&](const uint4 *kt, const uint4 *vt, int lo, int hi, const bool *ok) HDA_INLINE {
+        // (the store offsets are recomputed each round: kept across the
+        // rounds they would take registers from the rounds in flight)
+        int wb = wblk + 16 * hw, wx = 16 * wsw;
+        asm volatile("" : "+v"(wb), "+v"(wx));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = 2 * u + hw;
+            const int off = wb + ((32 * u) ^ wx);
+            *reinterpret_cast<uint4 *>(ktl + off) = kt[u];
+            *reinterpret_cast<uint4 *>(vtl + off) = r >= lo && r < hi ? vt[u] : make_uint4(0, 0, 0, 0);
         }
-        // this lane's key slot s of a cache round -> dkey: token t keeps it
-        // iff dkey >= t (sliding: dkey = (s - pos) mod (window-1); full: all)
-        auto dkey_of = [&](int r0e) {
-            if (!p.sliding) return 0x7FFFFFFF;
-            const int s = r0e + mrow;
-            int d = (s - p0) % W1;
-            return d < 0 ? d + W1 : d;
+        wave_lds_fence();
+        // operand reads run kMultiAhead k-steps ahead of their products (all
+        // eight at once would take the registers of the rounds in flight)
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        uint4 ka[kMultiAhead], qa[kMultiAhead];
+        auto op_read = [&](int j) HDA_INLINE {
+            ka[j % kMultiAhead] = ld16(ktl + 1024 * j + 16 * (drow + 16 * kg));
+            qa[j % kMultiAhead] = ld16(s_q + 1024 * j + 16 * (drow + 16 * kg));
+        };
+#pragma unroll
+        for (int j = 0; j < kMultiAhead; ++j) op_read(j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bf16x8 a = as_bf16x8(ka[j % kMultiAhead]), q = as_bf16x8(qa[j % kMultiAhead]);
+            if (j + kMultiAhead < 8) op_read(j + kMultiAhead);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q, s1, 0, 0, 0);
+            else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, q, s0, 0, 0, 0);
+        }
+        float s[4], tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = ok[i] ? (s0[i] + s1[i]) * p.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, s[i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float mr = m_new == -INFINITY ? 0.f : m_new;  // no key for this row yet
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mr);  // -inf - x: 0
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int d = 0; d < D / 16; ++d) acc[d] *= alpha;
+        }
+        float pv[4], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = __builtin_amdgcn_exp2f(s[i] - mr);
+            ps += pv[i];
+        }
+        l_lane = fmaf(l_lane, alpha, ps);
+        m_run = m_new;
+        const v4i16 pb = __builtin_bit_cast(v4i16, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+        v4i16 va[kMultiTrAhead];
+#pragma unroll
+        for (int d = 0; d < kMultiTrAhead; ++d)
+            va[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vtl + 512 * d + tr_off));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < D / 16; ++d) {
+            const v4i16 a = va[d % kMultiTrAhead];
+            if (d + kMultiTrAhead < D / 16)
+                va[d % kMultiTrAhead] =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vtl + 512 * (d + kMultiTrAhead) + tr_off));
+            __builtin_amdgcn_sched_barrier(0);
+            acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, acc[d], 0, 0, 0);
+        }
+        // the next round's stores follow these reads in this wave's LDS
+        // queue, which runs in order; keep the compiler from moving them
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // B operand rows: q[row mrow][32j + 8kg .. +7] at block j, slot drow + 16 kg
+    // (wave 0 copies them; p0 is uniform over the workgroup)
+    if (p0 >= 0 && wave == 0) {
+        const int m = mrow < RG ? mrow : 0, t = m / G, h = m % G;
+        const uint16_t *qr = p.q + (((int64_t)b * T + t) * Hq + kvh * G + h) * D + 8 * kg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint4 *>(s_q + 1024 * j + 16 * (drow + 16 * kg)) = ld16(qr + 32 * j);
+    }
+    __syncthreads();
+    if (p0 >= 0) {
+        // cache round r: key x = slot r0e + x seen by token t iff lo <= x < hi
+        // and, sliding, (slot - pos) mod (window-1) >= t
+        auto cache_round = [&](int r, const uint4 *kt, const uint4 *vt) HDA_INLINE {
+            const int e = r0e_of(r), lo = 16 * r - e, hi = n_old - e;
+            bool ok[4];
+            int dk = 0;
+            if (p.sliding) {
+                dk = (e + 4 * kg - p0) % W1;
+                dk += dk < 0 ? W1 : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int x = 4 * kg + i;
+                bool v = x >= lo && x < hi;
+                if (p.sliding) {
+                    int d = dk + i;
+                    d = W1 >= 4 ? (d >= W1 ? d - W1 : d) : d % W1;
+                    v = v && d >= trow;
+                }
+                ok[i] = v;
+            }
+            mround(kt, vt, lo, hi, ok);
         };
         uint4 kA[8], vA[8], kB[8], vB[8];
         for (int r = r_lo; r < r_hi; r += 2) {
             const bool two = r + 1 < r_hi;
             issue_round(kblk, vblk, r0e_of(r), lane, kA, vA);
             issue_round(kblk, vblk, r0e_of(two ? r + 1 : r), two ? lane : 0, kB, vB);
-            int e = r0e_of(r);
-            st.template round<false, false, uint4, true, true>(qa, kA, vA, 16 * r - e, n_old - e,
-                                                         p.scale_log2, s_pw[wave], s_kt[wave],
-                                                         lane, -1, nullptr, nullptr, 1.f, 1.f,
-                                                         dkey_of(e), trow);
+            cache_round(r, kA, vA);
             if (!two) break;
-            e = r0e_of(r + 1);
-            st.template round<false, false, uint4, true, true>(qa, kB, vB, 16 * (r + 1) - e, n_old - e,
-                                                         p.scale_log2, s_pw[wave], s_kt[wave],
-                                                         lane, -1, nullptr, nullptr, 1.f, 1.f,
-                                                         dkey_of(e), trow);
+            cache_round(r + 1, kB, vB);
         }
         if (last) {
-            // the chunk's round: key x = token x (rows past T repeat token
-            // 0, masked); token t sees x <= t, i.e. -x >= -t
-            const int hw = lane >> 5, dl = lane & 31;
+            // the chunk's round: key x = token x (rows past T repeat token 0,
+            // masked); token t sees x <= t
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int x = 2 * j + hw, tok = x < T ? x : 0;
@@ -218,30 +334,26 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
                 kA[j] = ld16(p.k_rot + row);
                 vA[j] = ld16(p.v_new + row);
             }
-            st.template round<false, false, uint4, true, true>(qa, kA, vA, 0, T, p.scale_log2,
-                                                         s_pw[wave], s_kt[wave], lane, -1,
-                                                         nullptr, nullptr, 1.f, 1.f, -mrow, ntrow);
+            bool ok[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ok[i] = 4 * kg + i < T && 4 * kg + i <= trow;
+            mround(kA, vA, 0, T, ok);
         }
     }
 
-    // merge the waves (as the window kernel does), then out / lse per row
-    float m_h[RG], l_h[RG];
-    st.totals(m_h, l_h);
-    const int hw = lane >> 5, dl = lane & 31;
+    // merge the waves: each leaves its o rows (unnormalised) in its own
+    // tiles, then out / lse per row
+    float l_row = l_lane + __shfl_xor(l_lane, 16, 64);
+    l_row += __shfl_xor(l_row, 32, 64);
     const bool has = p0 >= 0 && (r_lo < r_hi || last);
+    float *red = reinterpret_cast<float *>(s_tile[wave]);
+    wave_lds_fence();
 #pragma unroll
-    for (int h = 0; h < RG; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
-            if (hw == 0) s_red[(wave * RG + h) * D + 8 * dl + e] = o;
-        }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < RG; ++h) {
-            s_m[wave][h] = has ? m_h[h] : -INFINITY;
-            s_l[wave][h] = has ? l_h[h] : 0.f;
-        }
+    for (int d = 0; d < D / 16; ++d)
+        *reinterpret_cast<f32x4 *>(red + mrow * kMultiPitch + 16 * d + 4 * kg) = acc[d];
+    if (kg == 0) {
+        s_m[wave][mrow] = has ? m_run : -INFINITY;
+        s_l[wave][mrow] = has ? l_row : 0.f;
     }
     __syncthreads();
     for (int i = tid; i < RG * D; i += WAVES * 64) {
@@ -267,7 +379,7 @@ __global__ __launch_bounds__((G * T >= 8 ? 4 : 8) * 64) void decode_multi_kernel
         for (int w = 0; w < WAVES; ++w) {
             const float sc = exp2f(s_m[w][m] - M);  // wave without keys: 2^-inf = 0
             L = fmaf(sc, s_l[w][m], L);
-            o = fmaf(sc, s_red[(w * RG + m) * D + d], o);
+            o = fmaf(sc, reinterpret_cast<const float *>(s_tile[w])[m * kMultiPitch + d], o);
         }
         const float lse = (M + log2f(L)) * kLn2;
         if (S > 1) {  // normalised partial and its lse
@@ -645,7 +757,7 @@ hipError_t launch_prefill_g(const MultiParams &p, hipStream_t s) {
 template <int G, int T>
 hipError_t launch_multi_gt(const MultiParams &p, hipStream_t s) {
     hipLaunchKernelGGL((decode_multi_kernel<G, T>), dim3(p.batch * p.num_kv_heads * p.split),
-                       dim3(MultiShape<G, T>::WAVES * 64), 0, s, p);
+                       dim3(kMultiWaves * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split == 1) return e;
     hipLaunchKernelGGL(multi_merge_kernel, dim3(p.batch * p.num_kv_heads * G * T), dim3(kHeadDim),
