@@ -86,6 +86,30 @@ __global__ __launch_bounds__(kMultiRopeThreads) void rope_multi_kernel(MultiPara
     }
 }
 
+// Where token t of a chunk at position p0 lands (the rules below).
+struct AppendSlot {
+    int64_t row;
+    bool write, evict_old, evict_new;
+};
+__device__ __forceinline__ AppendSlot append_slot(const MultiParams &p, int32_t p0, int t) {
+    const int64_t P = (int64_t)p0 + t;
+    AppendSlot a{P, true, false, false};
+    if (p.sliding) {
+        const int slots = p.window - 1;
+        const int64_t last = (int64_t)p0 + p.tokens - 1;  // the chunk's last position
+        a.row = P % slots;
+        a.write = t >= p.tokens - slots;
+        if (last >= slots) {
+            const int64_t e = last - slots;  // position the evicted-entry row ends holding
+            a.evict_old = t == p.tokens - 1 && e < p0;
+            a.evict_new = e >= p0 && P == e;
+        }
+    } else {
+        a.write = P < p.capacity;
+    }
+    return a;
+}
+
 // Block (b, token t): the token's rotated K and its V into the cache.
 // Sliding: only the last window-1 tokens land (an earlier token's slot is
 // taken again by a later one); the evicted-entry row ends holding position
@@ -98,23 +122,11 @@ __global__ __launch_bounds__(128) void append_multi_kernel(MultiParams p) {
     const int bt = blockIdx.x, b = bt / p.tokens, t = bt % p.tokens;
     const int32_t p0 = p.pos[b];
     if (p0 < 0) return;
-    const int64_t P = (int64_t)p0 + t, cap = p.capacity;
-    int64_t row;
-    bool evict_old = false, evict_new = false, write = true;
-    if (p.sliding) {
-        const int slots = p.window - 1;
-        const int64_t last = (int64_t)p0 + p.tokens - 1;  // the chunk's last position
-        row = P % slots;
-        write = t >= p.tokens - slots;
-        if (last >= slots) {
-            const int64_t e = last - slots;  // position the evicted-entry row ends holding
-            evict_old = t == p.tokens - 1 && e < p0;
-            evict_new = e >= p0 && P == e;
-        }
-    } else {
-        if (P >= cap) return;
-        row = P;
-    }
+    const int64_t cap = p.capacity;
+    const AppendSlot a = append_slot(p, p0, t);
+    if (!a.write && !a.evict_old && !a.evict_new) return;
+    const int64_t row = a.row;
+    const bool evict_old = a.evict_old, evict_new = a.evict_new, write = a.write;
     const int Hkv = p.num_kv_heads;
     for (int u = threadIdx.x; u < 2 * Hkv * (D / 8); u += 128) {
         const bool is_v = u >= Hkv * (D / 8);
@@ -392,6 +404,26 @@ __global__ __launch_bounds__(kMultiWaves * 64, 1) void decode_multi_kernel(Multi
         if (p.gate) f *= gate_factor(p.gate[orow]);
         *outp = f32_to_bf16(o * f);
         if (d == 0 && p.lse) p.lse[orow] = lse;
+    }
+    // Split 1: the append (append_multi_kernel's rules, for this KV head)
+    // is done here -- no other workgroup reads this pair's rows, and every
+    // wave's cache loads were consumed before the barrier above.  A thread
+    // per 16-byte chunk of K or V takes the tokens in order, so the
+    // evicted-entry copy reads its slot before the slot is rewritten.
+    if (S == 1 && p0 >= 0) {
+        const int W = p.window;
+        for (int u = tid; u < 2 * (D / 8); u += WAVES * 64) {
+            const bool is_v = u >= D / 8;
+            const int d = (u % (D / 8)) * 8;
+            uint16_t *blk = (is_v ? p.v : p.k) + bh * cap * D;
+            for (int t = 0; t < T; ++t) {
+                const AppendSlot a = append_slot(p, p0, t);
+                const uint16_t *src = (is_v ? p.v_new : p.k_rot) + (((int64_t)b * T + t) * Hkv + kvh) * D + d;
+                if (a.evict_old) stm(blk + (int64_t)(W - 1) * D + d, ldm(blk + a.row * D + d));
+                if (a.evict_new) stm(blk + (int64_t)(W - 1) * D + d, ldm(src));
+                if (a.write) stm(blk + a.row * D + d, ldm(src));
+            }
+        }
     }
 }
 
@@ -814,6 +846,7 @@ hipError_t launch_decode_multi(const MultiParams &p, int group, hipStream_t stre
         }
     }
     if (e != hipSuccess) return e;
+    if (p.tokens * group <= 16 && p.split == 1) return hipSuccess;  // appended by the attention kernel
     hipLaunchKernelGGL(append_multi_kernel, dim3(bt), dim3(128), 0, stream, p);
     return hipGetLastError();
 }

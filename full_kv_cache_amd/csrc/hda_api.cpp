@@ -825,6 +825,10 @@ int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_
         return s;
     }
     const int64_t rounds = (n_old + 15) / 16;
+    // sliding, 128 pairs or more: one workgroup per pair, which also does
+    // the append (measured at 128 pairs: as fast as split 2 + merge, and
+    // the append launch is saved)
+    if (layer == HDA_SLIDING && pairs >= 128) return 1;
     const bool many = pairs >= 64;
     const int64_t target = many ? 256 : 128, min_rounds = many ? 16 : 8;
     int64_t s = pairs > 0 ? (target + pairs - 1) / pairs : 1;
