@@ -781,8 +781,9 @@ def main():
         multi = {"tokens_per_chunk": T, "ms_per_step": round(m_ms, 4),
                  "tokens_per_s": round(cfg["batch"] * T / (m_ms / 1e3), 1),
                  "kv_bytes_per_step": m_bytes, "GB/s": round(m_bytes / (m_ms / 1e3) / 1e9, 1),
-                 "path": "hda_decode_multi on every layer (RoPE, attention split over workgroups "
-                         "+ merge, append: 4 launches)"}
+                 "path": "hda_decode_multi on every layer (RoPE, then sliding layers: attention "
+                         "with the append, one workgroup per pair; full layers: attention split "
+                         "over workgroups, merge, append)"}
     prefill = None
     if args.prefill_tokens:
         B, T = args.prefill_batch, args.prefill_tokens
