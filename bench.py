@@ -526,10 +526,10 @@ def sparse_kernel(steps, warmup, seed, pools=8, fp8=False):
     gathered = s.tokens * s.topk * row_bytes
     flops = s.tokens * s.num_q_heads * s.topk * 2 * (s.dqk + s.dv)
     gbs = gathered / per_call_s / 1e9
-    # a bf16 pool with up to 64 heads takes the shared-tile kernel, an fp8
-    # pool the head-group kernel (the library's sparse routing)
-    kname = ("sparse_decode_kernel<false, true> + sparse_merge_kernel" if fp8
-             else "sparse_tile_kernel<false> + sparse_merge_kernel")
+    # up to 64 heads take the shared-tile kernel, bf16 or fp8 pool (the
+    # library's sparse routing)
+    kname = ("sparse_tile_kernel<false, true> + sparse_merge_kernel" if fp8
+             else "sparse_tile_kernel<false, false> + sparse_merge_kernel")
     return {
         "kernel": f"{kname} (hda_sparse_decode_attn{'_fp8' if fp8 else ''})",
         "workload": f"{s.tokens} tokens x {s.num_q_heads} heads, dqk {s.dqk} / dv {s.dv}, pool "

@@ -209,11 +209,11 @@ hipError_t launch_rope_append_fp8(const RopeAppendParams &p, hipStream_t stream)
 // pool (kv8 / kv_scale set) takes the kernel's fp8 form.
 hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t stream);
 // Whether the sparse call runs the shared-tile kernel (one workgroup per
-// (token, split) for all heads, a bf16 pool and up to kSparseTileHeads
+// (token, split) for all heads, bf16 or fp8 pool, up to kSparseTileHeads
 // heads; its splits hold at most kSparseMaxSplitKeys keys, a multiple of 32)
 // or the head-group kernel (splits a multiple of 16).
 constexpr int kSparseTileHeads = 64;
-inline bool sparse_uses_tiles(int num_q_heads, bool fp8) { return !fp8 && num_q_heads <= kSparseTileHeads; }
+inline bool sparse_uses_tiles(int num_q_heads, bool fp8) { return num_q_heads <= kSparseTileHeads; }
 
 // Chunk kernel over grid (nsplit, Hkv, B).  final_out: nsplit must be 1 and
 // the kernel writes out/lse with the sink; otherwise it writes partials.

@@ -359,6 +359,12 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
 // Keys without a row (past the split's end, or an index outside the pool)
 // read a zero row and are masked out of the softmax, so a NaN never meets a
 // zero weight.  Softmax against a fixed reference as in the kernel above.
+// F8 (e4m3 pool, a scale per row): a wave's blocks of a tile are loaded as
+// codes into registers (8 per lane and block, with its two rows' scales),
+// widened to bf16 (exact) and stored where the bf16 form's loads would put
+// them; two tiles in flight in registers, two LDS buffers.  A key's scores
+// take its row's scale, and so do the probabilities sent to P.V (the
+// running sum keeps the unscaled ones), as the head-group kernel does.
 
 constexpr int kTileKeys = 32;
 constexpr int kHalfBytes = 16 * kSparseDqk * 2;  // one 16-row half: 18 blocks of 1 KiB
@@ -370,13 +376,14 @@ constexpr int kBlocksPerWave = kTileBlocks / kTileWaves;
 static_assert(kBlocksPerWave * kTileWaves == kTileBlocks, "blocks split evenly over the waves");
 static_assert(kTileWaves * kSparseHeadsPerWave == kSparseTileHeads, "a wave per 16 heads");
 
-template <bool FINAL>
+template <bool FINAL, bool F8>
 __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseParams p) {
     __shared__ __align__(1024) unsigned char s_b0[2 * kHalfBytes];
     __shared__ __align__(1024) unsigned char s_b1[2 * kHalfBytes];
-    __shared__ __align__(1024) unsigned char s_b2[2 * kHalfBytes];
+    __shared__ __align__(1024) unsigned char s_b2[F8 ? 16 : 2 * kHalfBytes];
     __shared__ int s_idx[kSparseMaxSplitKeys];
     __shared__ int s_over[kTileWaves];
+    __shared__ float s_tsc[2][F8 ? kTileKeys : 1];  // F8: the row scales of the tile in each buffer
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -419,6 +426,42 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
             load_to_lds(src, buf + 1024 * blk);
         }
     };
+    // F8: this wave's blocks of a tile whose halves' rows for this lane are
+    // ra and rb, as codes (the zero row for -1), and those rows' scales (1
+    // for -1); then widened into a buffer where the bf16 form's loads would
+    // put them, the scales of the tile's 32 rows beside it.
+    struct Codes {
+        uint2 c[F8 ? kBlocksPerWave : 1];
+        float sa, sb;
+    };
+    auto load_codes = [&](int ra, int rb, Codes &x) HDA_INLINE {
+        if constexpr (F8) {
+            const uint8_t *pa = ra < 0 ? reinterpret_cast<const uint8_t *>(g_zero_row) : p.kv8 + (int64_t)ra * kSparseDqk;
+            const uint8_t *pb = rb < 0 ? reinterpret_cast<const uint8_t *>(g_zero_row) : p.kv8 + (int64_t)rb * kSparseDqk;
+#pragma unroll
+            for (int m = 0; m < kBlocksPerWave; ++m) {
+                const int blk = wave + kTileWaves * m;
+                const bool hb = blk >= kKSteps;
+                const int j = hb ? blk - kKSteps : blk;
+                x.c[m] = *reinterpret_cast<const uint2 *>((hb ? pb : pa) + 32 * j + 8 * kg);
+            }
+            const float fa = p.kv_scale[ra < 0 ? 0 : ra], fb = p.kv_scale[rb < 0 ? 0 : rb];
+            x.sa = ra < 0 ? 1.f : fa;
+            x.sb = rb < 0 ? 1.f : fb;
+        }
+    };
+    auto store_codes = [&](const Codes &x, unsigned char *buf, float *tsc) HDA_INLINE {
+        if constexpr (F8) {
+#pragma unroll
+            for (int m = 0; m < kBlocksPerWave; ++m)
+                *reinterpret_cast<uint4 *>(buf + 1024 * (wave + kTileWaves * m) + 16 * lane) = e4m3x8_to_bf16x8(x.c[m]);
+            if (wave == 0 && kg == 0) {  // lane mrow holds rows mrow and 16 + mrow
+                tsc[mrow] = x.sa;
+                tsc[16 + mrow] = x.sb;
+            }
+        }
+    };
+    Codes cA, cB;
     // Tiles 0 and 1 go in flight first, their rows read straight from the
     // index row; then q and the rest of the split's rows (into s_idx).
     {
@@ -433,8 +476,13 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
             r1a = valid(kTileKeys + drow, e2);
             r1b = valid(kTileKeys + 16 + drow, e3);
         }
-        issue_rows(r0a, r0b, s_b0);
-        issue_rows(r1a, r1b, s_b1);
+        if constexpr (F8) {
+            load_codes(r0a, r0b, cA);
+            load_codes(r1a, r1b, cB);
+        } else {
+            issue_rows(r0a, r0b, s_b0);
+            issue_rows(r1a, r1b, s_b1);
+        }
     }
     for (int i = tid; i < ntile * kTileKeys; i += kTileWaves * 64) s_idx[i] = row_at(i);
     // q: lane (head mrow, c) holds dims 32j + 8c .. +7 of its head, every j
@@ -461,6 +509,14 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
         }
         issue_rows(ra, rb, buf);
     };
+    auto issue_codes = [&](int i, Codes &x) HDA_INLINE {
+        int ra = -1, rb = -1;
+        if (i < ntile) {
+            ra = s_idx[kTileKeys * i + drow];
+            rb = s_idx[kTileKeys * i + 16 + drow];
+        }
+        load_codes(ra, rb, x);
+    };
 
     f32x4 acc[kDimTiles];
 #pragma unroll
@@ -473,7 +529,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     const int tr_b = (mrow >> 1) & 1;
     const int tr_off = 256 * tr_b + 16 * ((4 * kg + (mrow >> 2)) ^ (12 * tr_b)) + 8 * (mrow & 1);
 
-    auto compute = [&](int i, const unsigned char *buf) HDA_INLINE {
+    auto compute = [&](int i, const unsigned char *buf, const float *tsc) HDA_INLINE {
         const int ra = s_idx[kTileKeys * i + mrow], rb = s_idx[kTileKeys * i + 16 + mrow];
         const uint32_t va = (uint32_t)__ballot(ra >= 0) & 0xFFFFu;
         const uint32_t vb = (uint32_t)__ballot(rb >= 0) & 0xFFFFu;
@@ -503,11 +559,15 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
                 sb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qj, sb0, 0, 0, 0);
             }
         }
+        // F8: key 4kg + e of each half's row scale (1 for a masked key)
+        float rsk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rsk[e] = F8 ? tsc[16 * (e >> 2) + 4 * kg + (e & 3)] : 1.f;
         float s[8], tmax = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            s[e] = ((va >> (4 * kg + e)) & 1u) ? (sa0[e] + sa1[e]) * p.scale_log2 : -INFINITY;
-            s[4 + e] = ((vb >> (4 * kg + e)) & 1u) ? (sb0[e] + sb1[e]) * p.scale_log2 : -INFINITY;
+            s[e] = ((va >> (4 * kg + e)) & 1u) ? (sa0[e] + sa1[e]) * (p.scale_log2 * rsk[e]) : -INFINITY;
+            s[4 + e] = ((vb >> (4 * kg + e)) & 1u) ? (sb0[e] + sb1[e]) * (p.scale_log2 * rsk[4 + e]) : -INFINITY;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
@@ -524,6 +584,10 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
             ps += pw[e];
         }
         l_lane += ps;
+        if constexpr (F8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pw[e] *= rsk[e];  // P.V reads the codes: the rows' scales here
+        }
         const uint4 pu = make_uint4(pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
                                     pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7]));
         const bf16x8 pb = as_bf16x8(pu);
@@ -560,21 +624,45 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
         __builtin_amdgcn_s_waitcnt(0x0F70 | kBlocksPerWave);  // vmcnt(9)
         raw_barrier();
         issue(i + 2, refill);
-        compute(i, cur);
+        compute(i, cur, nullptr);
     };
     static_assert(kBlocksPerWave < 16, "vmcnt immediate");
+    // F8: wait for tile i's codes (tile i + 1's 11 loads may be out), widen
+    // them into `buf`, meet the other waves (the tile's blocks are in, and
+    // all are done with tile i - 2, this buffer's last), load tile i + 2's
+    // codes into the registers just emptied, score tile i.
+    auto step8 = [&](int i, Codes &x, unsigned char *buf, float *tsc) HDA_INLINE {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBlocksPerWave + 2));
+        store_codes(x, buf, tsc);
+        wave_lds_fence();
+        raw_barrier();
+        issue_codes(i + 2, x);
+        compute(i, buf, tsc);
+    };
 
     for (int pass = 0; pass < 2; ++pass) {
-        if (pass > 0) {  // tiles 0 and 1 again
-            issue(0, s_b0);
-            issue(1, s_b1);
-        }
-        for (int i = 0; i < ntile; i += 3) {
-            step(i, s_b0, s_b2);
-            if (i + 1 >= ntile) break;
-            step(i + 1, s_b1, s_b0);
-            if (i + 2 >= ntile) break;
-            step(i + 2, s_b2, s_b1);
+        if constexpr (F8) {
+            if (pass > 0) {  // tiles 0 and 1 again
+                issue_codes(0, cA);
+                issue_codes(1, cB);
+            }
+            for (int i = 0; i < ntile; i += 2) {
+                step8(i, cA, s_b0, s_tsc[0]);
+                if (i + 1 >= ntile) break;
+                step8(i + 1, cB, s_b1, s_tsc[1]);
+            }
+        } else {
+            if (pass > 0) {  // tiles 0 and 1 again
+                issue(0, s_b0);
+                issue(1, s_b1);
+            }
+            for (int i = 0; i < ntile; i += 3) {
+                step(i, s_b0, s_b2);
+                if (i + 1 >= ntile) break;
+                step(i + 1, s_b1, s_b0);
+                if (i + 2 >= ntile) break;
+                step(i + 2, s_b2, s_b1);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads past the end have landed
         const bool any_over = __ballot(over) != 0;  // the whole wave votes
@@ -684,13 +772,14 @@ hipError_t launch_sparse(const SparseParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <bool F8>
 hipError_t launch_sparse_tile(const SparseParams &p, hipStream_t s) {
     const int64_t blocks = ((int64_t)p.tokens + 7) / 8 * 8 * p.nsplit;
     if (p.nsplit == 1) {
-        hipLaunchKernelGGL((sparse_tile_kernel<true>), dim3((unsigned)blocks), dim3(kTileWaves * 64), 0, s, p);
+        hipLaunchKernelGGL((sparse_tile_kernel<true, F8>), dim3((unsigned)blocks), dim3(kTileWaves * 64), 0, s, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((sparse_tile_kernel<false>), dim3((unsigned)blocks), dim3(kTileWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((sparse_tile_kernel<false, F8>), dim3((unsigned)blocks), dim3(kTileWaves * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sparse_merge_kernel, dim3((unsigned)((int64_t)p.tokens * p.num_q_heads)),
@@ -701,7 +790,8 @@ hipError_t launch_sparse_tile(const SparseParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_sparse_decode(const SparseParams &p, hipStream_t s) {
-    if (sparse_uses_tiles(p.num_q_heads, p.kv8 != nullptr)) return launch_sparse_tile(p, s);
+    if (sparse_uses_tiles(p.num_q_heads, p.kv8 != nullptr))
+        return p.kv8 ? launch_sparse_tile<true>(p, s) : launch_sparse_tile<false>(p, s);
     return p.kv8 ? launch_sparse<true>(p, s) : launch_sparse<false>(p, s);
 }
 

@@ -240,7 +240,13 @@ def test_sparse_late_large_score(fp8):
     got = to_f64(out)
     assert np.all(np.isfinite(got))
     assert np.all(np.abs(got - ref) <= 1e-2 * np.maximum(1.0, np.abs(ref)))
+    # the other rows: the planted row is large (entries up to ~8) and many
+    # queries put most of their weight on it, so outputs reach |out| ~ 2-8,
+    # where a bf16 output's spacing (2^-6 at 2) alone exceeds an absolute
+    # 1e-2; the bound is relative there as well, the mean stays absolute
     rest = np.ones(ref.shape[:2], bool)
     rest[0, 5] = False
-    assert_attn_close(out[torch.from_numpy(rest)], ref[rest])
+    err = np.abs(got[rest] - ref[rest])
+    assert np.all(err <= 1e-2 * np.maximum(1.0, np.abs(ref[rest])))
+    assert err.mean() <= 1e-3
     np.testing.assert_allclose(to_f64(lse), rlse, rtol=0, atol=1e-4)
