@@ -492,10 +492,16 @@ constexpr int kWindowWaves = HDA_WINDOW_WAVES;
 //     other workgroup, and the evicted-entry row it also writes is only
 //     read where the new token's row replaces what was loaded.
 //   * head split (query groups of 8 and 16, whose accumulators would not
-//     fit two rounds in flight): workgroup `part` serves query heads part
-//     GW .. +GW-1 (GW = 4) over every key; it writes out / lse itself, and the last
-//     of the S workgroups (the counter again, taken once each workgroup's
-//     loads of the block are consumed) writes the append.
+//     fit two rounds in flight, and any group once the pairs alone fill
+//     the device): workgroup `part` serves query heads part GW .. +GW-1
+//     over every key; it writes out / lse itself, and the last
+//     of the S workgroups to count in writes the append.  A workgroup
+//     counts in (the counter again) from the wave whose round holds the
+//     row the new token takes, once that round's rows are in registers:
+//     the append overwrites no other row any workgroup reads (the new
+//     token's own row is served from LDS), so the count's return and the
+//     append overlap the wave's later rounds instead of following the
+//     merge.
 // No data passes between the workgroups of a pair except the partials.
 // F8 (fp8 cache: e4m3 codes + a scale per row): rounds load codes and the
 // key scales (as the streaming kernel's fp8 form); the prologue quantizes
@@ -650,6 +656,28 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepPara
         __syncthreads();
     }
 
+    // Head split: the wave whose round holds the row the new token takes
+    // (its ring slot, or row pos below a full window) counts its workgroup
+    // in on the pair's counter as soon as that round's rows are in
+    // registers, and reads the count after its last round; the last of the
+    // pair's workgroups to count in writes the append there.
+    const int trow = srow >= 0 ? srow : vrow;
+    int cnt = 0;           // lane 0 of the counting wave: the count before its own
+    bool counted = false;  // wave-uniform
+    auto count_in = [&](int r0e, int lo, int hi) HDA_INLINE {
+        if constexpr (!KS) {
+            const int tw = trow - r0e;
+            if (tw >= lo && tw < hi && tw < 16) {
+                // the round's loads (and every later one) complete first,
+                // and no memory access moves across
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (lane == 0)
+                    cnt = __hip_atomic_fetch_add(p.counters + pr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                counted = true;
+            }
+        }
+    };
+
     WaveSoftmax<GW> st;
     st.reset();
     if (r_lo < r_hi) {
@@ -692,6 +720,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepPara
                         s_c8s[3] = vsc;
                     }
                 }
+                count_in(r0e, lo, hi);
                 return;
             } else {
             // the round holding the new token's row takes it from LDS
@@ -714,6 +743,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepPara
                         *reinterpret_cast<uint4 *>(s_oldv + 8 * dl) = vt[u];
                     }
             }
+            count_in(r0e, lo, hi);
             }
         };
         for (int r = r_lo; r < r_hi; r += 2) {
@@ -725,6 +755,33 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepPara
             one(r, kA, vA, ksA, vsA);
             if (!two) break;
             one(r + 1, kB, vB, ksB, vsB);
+        }
+    }
+    if (!KS && counted && __builtin_amdgcn_readfirstlane(cnt) == S - 1) {
+        // the last to count in: reset the counter, then the slot's old entry
+        // (kept in LDS by this wave) to the evicted-entry row and the new
+        // token to its slot -- lanes 0..31 the K row, 32..63 the V row
+        if (lane == 0) __hip_atomic_store(p.counters + pr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int c = lane & 31, row = srow >= 0 ? srow : vrow;
+        if constexpr (F8) {
+            uint8_t *blk = (hw ? p.vq : p.kq) + bh * cap * D;
+            float *sblk = (hw ? p.vs : p.ks) + bh * cap;
+            const uint2 nw = *reinterpret_cast<const uint2 *>(s_c8 + hw * D + 8 * c);
+            if (srow >= 0) {
+                const uint2 od = *reinterpret_cast<const uint2 *>(s_c8 + (2 + hw) * D + 8 * c);
+                *reinterpret_cast<uint2 *>(blk + (int64_t)(W - 1) * D + 8 * c) = od;
+                if (c == 0) sblk[W - 1] = s_c8s[2 + hw];
+            }
+            *reinterpret_cast<uint2 *>(blk + (int64_t)row * D + 8 * c) = nw;
+            if (c == 0) sblk[row] = s_c8s[hw];
+        } else {
+            uint16_t *blk = hw ? vblk : kblk;
+            const uint4 nw = *reinterpret_cast<const uint4 *>((hw ? s_vnew : s_knew) + 8 * c);
+            if (srow >= 0) {
+                const uint4 od = *reinterpret_cast<const uint4 *>((hw ? s_oldv : s_oldk) + 8 * c);
+                *reinterpret_cast<uint4 *>(blk + (int64_t)(W - 1) * D + 8 * c) = od;
+            }
+            *reinterpret_cast<uint4 *>(blk + (int64_t)row * D + 8 * c) = nw;
         }
     }
 
@@ -874,26 +931,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepPara
         }
     }
 
-    // The append: key split -- the workgroup whose rounds hold the row the
-    // new token takes; head split -- the last of the pair's workgroups to
-    // finish reading the block.
-    bool app;
-    if constexpr (KS) {
-        const int trow = srow >= 0 ? srow : vrow;
-        app = P >= 0 && (trow >> 4) >= q_lo && (trow >> 4) < q_hi;
-    } else {
-        __syncthreads();
-        if (tid == 0) {
-            s_last = 0;
-            if (P >= 0) {
-                const int old = __hip_atomic_fetch_add(p.counters + pr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_last = old == S - 1;
-                if (s_last) __hip_atomic_store(p.counters + pr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-        app = s_last;
-    }
+    // The key split's append: the workgroup whose rounds hold the row the
+    // new token takes (the head split's was written after the rounds).
+    if constexpr (!KS) return;
+    const bool app = P >= 0 && (trow >> 4) >= q_lo && (trow >> 4) < q_hi;
     if constexpr (F8) {
         if (app && tid < 128) {  // 8 code bytes per thread, K then V
             const int which = tid >> 6, c = tid & 31, half = (tid >> 5) & 1;
