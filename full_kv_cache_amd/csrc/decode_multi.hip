@@ -429,38 +429,70 @@ __global__ __launch_bounds__(kMultiWaves * 64, 1) void decode_multi_kernel(Multi
 
 // The split partials of one (sequence, KV head, query row): out = sum_s
 // e^(lse_s - lse) o_s with lse = ln sum_s e^(lse_s) (parts without keys
-// weigh 0), then the sink and the gate.  One workgroup per (pair, row), a
-// thread per dim (the row's S lse values are read by every thread: one
-// cached broadcast).
-__global__ __launch_bounds__(kHeadDim) void multi_merge_kernel(MultiParams p, int RG, int G) {
+// weigh 0), then the sink and the gate.  One wave per row, four dims a
+// lane, four rows a workgroup.  A batch of kMergeParts parts has all its
+// loads in flight at once (indices past the last part repeat it and weigh
+// 0); more parts than one batch fold in batch by batch with the running
+// maximum rescaled, as an online softmax does.
+constexpr int kMergeParts = 8;
+constexpr int kMergeRows = 4;  // rows (waves) per workgroup
+__global__ __launch_bounds__(64 * kMergeRows) void multi_merge_kernel(MultiParams p, int RG, int G) {
     constexpr int D = kHeadDim;
+    static_assert(D == 4 * 64, "a lane's four dims cover the row");
     const int S = p.split, Hkv = p.num_kv_heads, Hq = p.num_q_heads;
-    const int pair = blockIdx.x / RG, m = blockIdx.x % RG, d = threadIdx.x;
-    const int b = pair / Hkv, kvh = pair % Hkv;
-    {
-        const int t = m / G, hq = kvh * G + m % G;
-        const int64_t orow = ((int64_t)b * p.tokens + t) * Hq + hq;
-        float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, p.part_lse[((int64_t)pair * S + s) * RG + m]);
-        if (M == -INFINITY) {
-            p.out[orow * D + d] = 0;
-            if (d == 0 && p.lse) p.lse[orow] = -INFINITY;
-            return;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nrows = (int64_t)p.batch * Hkv * RG;
+    if (row >= nrows) return;
+    const int64_t pair = row / RG;
+    const int m = (int)(row % RG);
+    const int b = (int)(pair / Hkv), kvh = (int)(pair % Hkv);
+    const int t = m / G, hq = kvh * G + m % G;
+    const int64_t orow = ((int64_t)b * p.tokens + t) * Hq + hq;
+    float M = -INFINITY, L = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += kMergeParts) {
+        float lv[kMergeParts];
+        float4 ov[kMergeParts];
+#pragma unroll
+        for (int k = 0; k < kMergeParts; ++k) {
+            const int64_t prow = (pair * S + min(s0 + k, S - 1)) * RG + m;
+            lv[k] = p.part_lse[prow];
+            ov[k] = *reinterpret_cast<const float4 *>(p.part_o + prow * D + 4 * lane);
         }
-        float L = 0.f, o = 0.f;
-        for (int s = 0; s < S; ++s) {
-            const int64_t prow = ((int64_t)pair * S + s) * RG + m;
-            const float e = expf(p.part_lse[prow] - M);  // -inf part: 0
-            L += e;
-            o = fmaf(e, p.part_o[prow * D + d], o);
+        float mb = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kMergeParts; ++k)
+            if (s0 + k < S) mb = fmaxf(mb, lv[k]);
+        const float Mn = fmaxf(M, mb);
+        if (Mn == -INFINITY) continue;  // no part with keys yet
+        const float sc = M == -INFINITY ? 0.f : expf(M - Mn);
+        L *= sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] *= sc;
+#pragma unroll
+        for (int k = 0; k < kMergeParts; ++k) {
+            const float w = s0 + k < S ? expf(lv[k] - Mn) : 0.f;  // a part without keys: 0
+            L += w;
+            o[0] = fmaf(w, ov[k].x, o[0]);
+            o[1] = fmaf(w, ov[k].y, o[1]);
+            o[2] = fmaf(w, ov[k].z, o[2]);
+            o[3] = fmaf(w, ov[k].w, o[3]);
         }
-        const float lse = M + logf(L);
-        float f = 1.f / L;
-        if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
-        if (p.gate) f *= gate_factor(p.gate[orow]);
-        p.out[orow * D + d] = f32_to_bf16(o * f);
-        if (d == 0 && p.lse) p.lse[orow] = lse;
+        M = Mn;
     }
+    uint2 *dst = reinterpret_cast<uint2 *>(p.out + orow * D + 4 * lane);
+    if (M == -INFINITY) {
+        *dst = make_uint2(0u, 0u);
+        if (lane == 0 && p.lse) p.lse[orow] = -INFINITY;
+        return;
+    }
+    const float lse = M + logf(L);
+    float f = 1.f / L;
+    if (p.sinks) f *= 1.f / (1.f + expf(p.sinks[hq] - lse));
+    if (p.gate) f *= gate_factor(p.gate[orow]);
+    *dst = make_uint2(pack_bf16x2(o[0] * f, o[1] * f), pack_bf16x2(o[2] * f, o[3] * f));
+    if (lane == 0 && p.lse) p.lse[orow] = lse;
 }
 
 // ---------------------------------------------------------------------
@@ -781,8 +813,8 @@ hipError_t launch_prefill_g(const MultiParams &p, hipStream_t s) {
     hipLaunchKernelGGL((prefill_chunk_kernel<G>), dim3((unsigned)blocks), dim3(kPfWaves * 64), 0, s, p, nrb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split == 1) return e;
-    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)(pairs * G * p.tokens)), dim3(kHeadDim), 0, s, p,
-                       G * p.tokens, G);
+    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)((pairs * G * p.tokens + kMergeRows - 1) / kMergeRows)),
+                       dim3(64 * kMergeRows), 0, s, p, G * p.tokens, G);
     return hipGetLastError();
 }
 
@@ -792,8 +824,8 @@ hipError_t launch_multi_gt(const MultiParams &p, hipStream_t s) {
                        dim3(kMultiWaves * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split == 1) return e;
-    hipLaunchKernelGGL(multi_merge_kernel, dim3(p.batch * p.num_kv_heads * G * T), dim3(kHeadDim),
-                       0, s, p, G * T, G);
+    hipLaunchKernelGGL(multi_merge_kernel, dim3((p.batch * p.num_kv_heads * G * T + kMergeRows - 1) / kMergeRows),
+                       dim3(64 * kMergeRows), 0, s, p, G * T, G);
     return hipGetLastError();
 }
 
