@@ -6,7 +6,7 @@ computes the right result but streams far slower (a value-initialised
 vector in shared code once pushed the sliding-layer step from 20 to 48 us).
 Every kernel on a default path -- the one-launch window step, the
 streaming kernel (plain and in its step form) and the window kernels, bf16
-and fp8, the chunk-decode kernels, the sparse decode (bf16 and fp8 pools),
+and fp8, the chunk-decode and chunked-prefill kernels, the sparse decode (bf16 and fp8 pools),
 the merges and the appends -- and the
 one-launch step for sliding windows past one workgroup must use no scratch
 and spill nothing.
@@ -33,7 +33,8 @@ DEFAULT_PATH = {
                         "stream_merge_kernel", "lse_merge_kernel"],
     "decode_multi.hip": ["decode_multi_kernelILi4ELi1E", "decode_multi_kernelILi4ELi2E",
                          "decode_multi_kernelILi4ELi3E", "decode_multi_kernelILi4ELi4E",
-                         "multi_merge_kernel", "rope_multi_kernel", "append_multi_kernel"],
+                         "prefill_chunk_kernel", "multi_merge_kernel", "rope_multi_kernel",
+                         "append_multi_kernel"],
     "rope_append.hip": ["rope_append_kernel", "rope_append_fp8_kernel"],
     "sparse_attn.hip": ["sparse_decode_kernelILb0ELb0E", "sparse_decode_kernelILb0ELb1E",
                         "sparse_decode_kernelILb1ELb0E", "sparse_decode_kernelILb1ELb1E",
