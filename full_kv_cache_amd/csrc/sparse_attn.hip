@@ -366,6 +366,27 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
 // take its row's scale, and so do the probabilities sent to P.V (the
 // running sum keeps the unscaled ones), as the head-group kernel does.
 
+// Lane l with lane l ^ 16 (or l ^ 32) on the vector ALU: each swap hands a
+// lane both values of its pair (in some order), so max and sum, which do not
+// care about the order, come out alike on both lanes -- no LDS round trip,
+// where a shuffle would queue behind the other waves' operand reads.
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 constexpr int kTileKeys = 32;
 constexpr int kHalfBytes = 16 * kSparseDqk * 2;  // one 16-row half: 18 blocks of 1 KiB
 constexpr int kTileBlocks = 2 * kKSteps;         // 36 blocks per tile
@@ -559,10 +580,22 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
                 sb0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qj, sb0, 0, 0, 0);
             }
         }
+        // V^T reads run kTrAhead dim tiles ahead of the products that use
+        // them (each product would otherwise wait out a whole LDS round
+        // trip); the first go out before the softmax, which runs meanwhile
+        v4i16 vlo[kTrAhead], vhi[kTrAhead];
+        auto tr_read = [&](int d) HDA_INLINE {
+            vlo[d % kTrAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(buf + tr_off + 512 * d));
+            vhi[d % kTrAhead] =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(buf + kHalfBytes + tr_off + 512 * d));
+        };
         // F8: key 4kg + e of each half's row scale (1 for a masked key)
         float rsk[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) rsk[e] = F8 ? tsc[16 * (e >> 2) + 4 * kg + (e & 3)] : 1.f;
+#pragma unroll
+        for (int d = 0; d < kTrAhead; ++d) tr_read(d);
+        __builtin_amdgcn_sched_barrier(0);
         float s[8], tmax = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -571,8 +604,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = xor32_max(xor16_max(tmax));
         m_max = fmaxf(m_max, tmax);
         if (m_ref == -INFINITY) m_ref = tmax;  // first keys: nothing accumulated yet
         over |= tmax > m_ref + kSlack;
@@ -591,16 +623,6 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
         const uint4 pu = make_uint4(pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]),
                                     pack_bf16x2(pw[4], pw[5]), pack_bf16x2(pw[6], pw[7]));
         const bf16x8 pb = as_bf16x8(pu);
-        // V^T reads run kTrAhead dim tiles ahead of the products that use
-        // them (each product would otherwise wait out a whole LDS round trip)
-        v4i16 vlo[kTrAhead], vhi[kTrAhead];
-        auto tr_read = [&](int d) HDA_INLINE {
-            vlo[d % kTrAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(buf + tr_off + 512 * d));
-            vhi[d % kTrAhead] =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(buf + kHalfBytes + tr_off + 512 * d));
-        };
-#pragma unroll
-        for (int d = 0; d < kTrAhead; ++d) tr_read(d);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = 0; d < kDimTiles; ++d) {
@@ -681,8 +703,7 @@ __global__ __launch_bounds__(kTileWaves * 64, 1) void sparse_tile_kernel(SparseP
     }
     if (!active) return;
 
-    float l = l_lane + __shfl_xor(l_lane, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = xor32_sum(xor16_sum(l_lane));
     const int hq = h0 + mrow;
     const float lse = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
     float f = l > 0.f ? 1.f / l : 0.f;
