@@ -22,12 +22,14 @@
 //      last workgroup.  Each workgroup merges its waves in LDS and writes
 //      out directly (split 1) or a partial (o, lse) per row that
 //      multi_merge_kernel combines;
-//   3. append_multi_kernel: the rotated new K and V rows into the cache
-//      (full: rows pos + t; sliding: the ring slots of the last 511 tokens,
-//      and the block's evicted-entry row receives the entry of position
+//   3. the append: the rotated new K and V rows into the cache (full:
+//      rows pos + t; sliding: the ring slots of the last 511 tokens, and
+//      the block's evicted-entry row receives the entry of position
 //      pos + T - 512 -- a cached one or, for T = 512, token 0 -- as T
 //      single-token appends leave it).  It runs after the attention, which
-//      reads the slots it overwrites.
+//      reads the slots it overwrites: in the merge launch when the keys
+//      were split, in the attention kernel itself for an unsplit chunk
+//      decode, else as append_multi_kernel.
 #include <type_traits>
 
 #include "decode_wave.h"
@@ -117,9 +119,11 @@ __device__ __forceinline__ AppendSlot append_slot(const MultiParams &p, int32_t 
 // there): written by the last token's block from its slot before that
 // block overwrites it, or, when that position is in the chunk (T ==
 // window), by that token's block from the chunk.
-__global__ __launch_bounds__(128) void append_multi_kernel(MultiParams p) {
+// Token bt = b * tokens + t of the chunk: its rows for every KV head, with
+// nthreads threads (tid of them this one).
+__device__ __forceinline__ void append_token(const MultiParams &p, int bt, int tid, int nthreads) {
     constexpr int D = kHeadDim;
-    const int bt = blockIdx.x, b = bt / p.tokens, t = bt % p.tokens;
+    const int b = bt / p.tokens, t = bt % p.tokens;
     const int32_t p0 = p.pos[b];
     if (p0 < 0) return;
     const int64_t cap = p.capacity;
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(128) void append_multi_kernel(MultiParams p) {
     const int64_t row = a.row;
     const bool evict_old = a.evict_old, evict_new = a.evict_new, write = a.write;
     const int Hkv = p.num_kv_heads;
-    for (int u = threadIdx.x; u < 2 * Hkv * (D / 8); u += 128) {
+    for (int u = tid; u < 2 * Hkv * (D / 8); u += nthreads) {
         const bool is_v = u >= Hkv * (D / 8);
         const int w = is_v ? u - Hkv * (D / 8) : u, h = w / (D / 8), d = (w % (D / 8)) * 8;
         uint16_t *blk = (is_v ? p.v : p.k) + ((int64_t)b * Hkv + h) * cap * D;
@@ -137,6 +141,10 @@ __global__ __launch_bounds__(128) void append_multi_kernel(MultiParams p) {
         if (evict_new) stm(blk + (int64_t)(p.window - 1) * D + d, ldm(src + d));
         if (write) stm(blk + row * D + d, ldm(src + d));
     }
+}
+
+__global__ __launch_bounds__(128) void append_multi_kernel(MultiParams p) {
+    append_token(p, blockIdx.x, threadIdx.x, 128);
 }
 
 // Chunk decode, tokens x G <= 16 query rows per KV head: `split`
@@ -433,12 +441,19 @@ __global__ __launch_bounds__(kMultiWaves * 64, 1) void decode_multi_kernel(Multi
 // lane, four rows a workgroup.  A batch of kMergeParts parts has all its
 // loads in flight at once (indices past the last part repeat it and weigh
 // 0); more parts than one batch fold in batch by batch with the running
-// maximum rescaled, as an online softmax does.
+// maximum rescaled, as an online softmax does.  Workgroups from
+// merge_blocks on write the append instead (one per chunk token, as
+// append_multi_kernel does): nothing in this launch reads the cache, and
+// the attention kernels that read it have completed before it starts.
 constexpr int kMergeParts = 8;
 constexpr int kMergeRows = 4;  // rows (waves) per workgroup
-__global__ __launch_bounds__(64 * kMergeRows) void multi_merge_kernel(MultiParams p, int RG, int G) {
+__global__ __launch_bounds__(64 * kMergeRows) void multi_merge_kernel(MultiParams p, int RG, int G, int merge_blocks) {
     constexpr int D = kHeadDim;
     static_assert(D == 4 * 64, "a lane's four dims cover the row");
+    if ((int)blockIdx.x >= merge_blocks) {
+        append_token(p, (int)blockIdx.x - merge_blocks, threadIdx.x, 64 * kMergeRows);
+        return;
+    }
     const int S = p.split, Hkv = p.num_kv_heads, Hq = p.num_q_heads;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -813,8 +828,9 @@ hipError_t launch_prefill_g(const MultiParams &p, hipStream_t s) {
     hipLaunchKernelGGL((prefill_chunk_kernel<G>), dim3((unsigned)blocks), dim3(kPfWaves * 64), 0, s, p, nrb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split == 1) return e;
-    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)((pairs * G * p.tokens + kMergeRows - 1) / kMergeRows)),
-                       dim3(64 * kMergeRows), 0, s, p, G * p.tokens, G);
+    const int mb = (int)((pairs * G * p.tokens + kMergeRows - 1) / kMergeRows);
+    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)(mb + p.batch * p.tokens)), dim3(64 * kMergeRows), 0, s,
+                       p, G * p.tokens, G, mb);
     return hipGetLastError();
 }
 
@@ -824,8 +840,9 @@ hipError_t launch_multi_gt(const MultiParams &p, hipStream_t s) {
                        dim3(kMultiWaves * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split == 1) return e;
-    hipLaunchKernelGGL(multi_merge_kernel, dim3((p.batch * p.num_kv_heads * G * T + kMergeRows - 1) / kMergeRows),
-                       dim3(64 * kMergeRows), 0, s, p, G * T, G);
+    const int mb = (p.batch * p.num_kv_heads * G * T + kMergeRows - 1) / kMergeRows;
+    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)(mb + p.batch * T)), dim3(64 * kMergeRows), 0, s, p,
+                       G * T, G, mb);
     return hipGetLastError();
 }
 
@@ -878,7 +895,9 @@ hipError_t launch_decode_multi(const MultiParams &p, int group, hipStream_t stre
         }
     }
     if (e != hipSuccess) return e;
-    if (p.tokens * group <= 16 && p.split == 1) return hipSuccess;  // appended by the attention kernel
+    // the append: done by the merge launch (split > 1) or, for chunk decode
+    // unsplit, by the attention kernel; the unsplit prefill needs its own
+    if (p.split > 1 || p.tokens * group <= 16) return hipSuccess;
     hipLaunchKernelGGL(append_multi_kernel, dim3(bt), dim3(128), 0, stream, p);
     return hipGetLastError();
 }
