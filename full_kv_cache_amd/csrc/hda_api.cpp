@@ -825,10 +825,11 @@ int multi_split(const hda_cache_desc *c, int layer, int32_t tokens, int32_t max_
         return s;
     }
     const int64_t rounds = (n_old + 15) / 16;
-    // sliding, 128 pairs or more: one workgroup per pair, which also does
-    // the append (measured at 128 pairs: as fast as split 2 + merge, and
-    // the append launch is saved)
-    if (layer == HDA_SLIDING && pairs >= 128) return 1;
+    // sliding, 128 pairs or more, one token: one workgroup per pair, which
+    // also does the append (measured at 128 pairs: 25.2 us against 25.4 for
+    // split 2 + the merge launch, which then writes the append); two tokens
+    // or more split as below (4 tokens: 30.7 against 31.5 us)
+    if (layer == HDA_SLIDING && pairs >= 128 && tokens == 1) return 1;
     const bool many = pairs >= 64;
     const int64_t target = many ? 256 : 128, min_rounds = many ? 16 : 8;
     int64_t s = pairs > 0 ? (target + pairs - 1) / pairs : 1;
