@@ -446,3 +446,12 @@ def test_multi_workspace():
     assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 4096) == \
         krot(5) + (prows * 256 * 4 + 255) // 256 * 256 + prows * 4
     assert L.hda_decode_multi_workspace_bytes(ctypes.byref(full), hda.FULL, 5, 200) == krot(5)  # 7 tiles
+    # sliding window, 64 sequences (128 pairs): one token keeps one workgroup
+    # per pair (no partials); from two tokens on the 511 held keys (32
+    # rounds) split in 2 (256 workgroups, 16 rounds each)
+    slide = _desc(batch=64)
+    krot64 = lambda T: (64 * T * 2 * 256 * 2 + 255) // 256 * 256
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(slide), hda.SLIDING, 1, 4096) == krot64(1)
+    srows = 64 * 2 * 2 * 4 * 4  # pairs x 2 parts x (4 tokens x 4 heads)
+    assert L.hda_decode_multi_workspace_bytes(ctypes.byref(slide), hda.SLIDING, 4, 4096) == \
+        krot64(4) + (srows * 256 * 4 + 255) // 256 * 256 + srows * 4
