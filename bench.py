@@ -781,9 +781,10 @@ def main():
         multi = {"tokens_per_chunk": T, "ms_per_step": round(m_ms, 4),
                  "tokens_per_s": round(cfg["batch"] * T / (m_ms / 1e3), 1),
                  "kv_bytes_per_step": m_bytes, "GB/s": round(m_bytes / (m_ms / 1e3) / 1e9, 1),
-                 "path": "hda_decode_multi on every layer (RoPE, then sliding layers: attention "
-                         "with the append, one workgroup per pair; full layers: attention split "
-                         "over workgroups, merge, append)"}
+                 "path": "hda_decode_multi on every layer (RoPE; attention split over "
+                         "workgroups (2 per pair at this batch, one per pair for one-token "
+                         "chunks on sliding layers, which then append); merge, whose launch "
+                         "also writes the append)"}
     prefill = None
     if args.prefill_tokens:
         B, T = args.prefill_batch, args.prefill_tokens
@@ -801,7 +802,8 @@ def main():
                    "mfma_bf16_frac": round(wl.pf_flops / (p_ms / 1e3) / 2.5e15, 4),
                    "kv_GB/s": round(wl.pf_rows * wl.kv_row_bytes / (p_ms / 1e3) / 1e9, 1),
                    "path": "hda_decode_multi on every layer (RoPE, prefill_chunk_kernel: both "
-                           "products on MFMA, append: 3 launches)"}
+                           "products on MFMA, merge of the key split with the append: 3 "
+                           "launches)"}
     sparse = None
     if not args.no_sparse:
         print("# timing sparse top-k decode", file=sys.stderr, flush=True)
