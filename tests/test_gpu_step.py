@@ -212,6 +212,41 @@ def test_step_batch64_all():
         _check_cache(d, h)
 
 
+@pytest.mark.parametrize("hq", [8, 4])
+def test_step_sliding_batch64_edges(hq):
+    """A sliding layer at batch 64 takes the head split of the window step
+    (two workgroups per (sequence, KV head), each serving half the query
+    heads over every key; the last to count in appends; query groups of 4
+    and 2): the ring's edge positions
+    (empty window, first rows, the fill at 510 / 511, wrap-around) among
+    random ones, the stale evicted-entry row poisoned, sinks near lse and
+    the output gate, against the oracle; one sequence inactive (pos -1:
+    out 0, lse -inf, its block untouched)."""
+    _print_case(test="step_sliding_batch64_edges", hq=hq)
+    edge = [0, 1, 15, 16, 17, 509, 510, 511, 512, 1000, 1021, 4095]
+    g = np.random.default_rng(640)
+    pos = np.concatenate([edge, g.integers(0, 4096, 64 - len(edge))]).astype(np.int32)
+    neg = 40  # inactive on the device; the oracle runs it at its drawn position
+    case = HybridCase(1640 + hq, 64, SLIDING, pos, poison=True, num_q_heads=hq)
+    _poison_stale_evicted_row(case)
+    _, _, lse0 = case.oracle_step()
+    sinks = near_lse_sinks(lse0, 641)
+    gate = g.uniform(-3, 3, size=(64, case.shape.num_q_heads)).astype(np.float32)
+    h, ref, rlse = case.oracle_step(sinks=sinks, gate=gate)
+    case.pos = case.pos.copy()
+    case.pos[neg] = -1
+    d, out, lse = fused_step(case, sinks=sinks, gate=gate)
+    live = np.arange(64) != neg
+    assert_attn_close(out[torch.from_numpy(live)], ref[live])
+    np.testing.assert_allclose(to_f64(lse)[live], rlse[live], rtol=0, atol=1e-4)
+    assert torch.all(out[neg].float() == 0) and torch.all(torch.isneginf(lse[neg]))
+    k_gpu, v_gpu = bits_of(d["k"]), bits_of(d["v"])
+    assert np.array_equal(v_gpu[live], h["v"][live])
+    assert_rotated_close(k_gpu[live], h["k"][live])
+    assert np.array_equal(k_gpu[neg], case.host["k"][neg])
+    assert np.array_equal(v_gpu[neg], case.host["v"][neg])
+
+
 def test_step_full_rotary_256():
     """Full layer with the whole head rotated (rotary_dim 256: the q
     operand's chunk j pairs with chunk j + 4 in the step form's in-register
