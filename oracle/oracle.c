@@ -157,6 +157,8 @@ void or_rope_apply(const uint16_t *x, uint16_t *y, int64_t n_vec, int D, int rot
  *   in the side row kev/vev[b, h, :], then the slot takes the new entry.
  *   The side row is meaningful only when pos >= window-1; below that the
  *   slot was never written and the side row is left untouched.
+ * A position outside the cache (negative, or at or past capacity on a full
+ *   layer) writes no row; q is still rotated at it.
  * Layouts: k, v bf16 [B, Hkv, capacity, D]; kev, vev bf16 [B, Hkv, D];
  *   k_new, v_new bf16 [B, Hkv, D]; pos int32 [B].
  * Parity pinned bit-exact: slot arithmetic, untouched slots, side row =
@@ -175,12 +177,14 @@ void or_rope_append(uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
             uint16_t *kb = k + ((int64_t)b * Hkv + h) * capacity * D;
             uint16_t *vb = v + ((int64_t)b * Hkv + h) * capacity * D;
             if (layer_type == OR_SLIDING) {
+                if (p < 0) continue;
                 row = or_ring_slot(p, window);
                 if (p >= window - 1) {
                     memcpy(kev + ((int64_t)b * Hkv + h) * D, kb + row * D, sizeof(uint16_t) * D);
                     memcpy(vev + ((int64_t)b * Hkv + h) * D, vb + row * D, sizeof(uint16_t) * D);
                 }
             } else {
+                if (p < 0 || p >= capacity) continue;
                 row = p;
             }
             memcpy(kb + row * D, krot + (int64_t)h * D, sizeof(uint16_t) * D);

@@ -122,6 +122,36 @@ def test_full_append_bit_exact():
             assert np.array_equal(t["k"][b, h, mask], before["k"][b, h, mask])
 
 
+@pytest.mark.parametrize("lt", [workloads.SLIDING, workloads.FULL])
+def test_append_outside_cache_writes_nothing(lt):
+    """A position outside the cache -- negative (an inactive sequence), or
+    at or past capacity on a full layer -- writes no row anywhere (the
+    block, the side row, and the neighbouring sequences' blocks, which a
+    row index of -1 or capacity would reach), while q is still rotated at
+    that position; sequences in the cache append as usual."""
+    shape, t = _layer(7, 3, lt, lmax=64)
+    before = {k: v.copy() for k, v in t.items()}
+    cap = t["k"].shape[2]
+    posv = np.array([-1, 20, cap if lt == workloads.FULL else -3], dtype=np.int32)
+    kev = t.get("kev", np.zeros((3, 2, 256), np.uint16))
+    vev = t.get("vev", np.zeros((3, 2, 256), np.uint16))
+    kev0, vev0 = kev.copy(), vev.copy()
+    rot, theta = (256, 1e4) if lt == workloads.SLIDING else (64, 5e6)
+    oracle.rope_append(t["q"], t["k_new"], t["v_new"], posv, lt, rot, theta, W,
+                       t["k"], t["v"], kev, vev)
+    for b in (0, 2):
+        assert np.array_equal(t["k"][b], before["k"][b]) and np.array_equal(t["v"][b], before["v"][b])
+        assert np.array_equal(kev[b], kev0[b]) and np.array_equal(vev[b], vev0[b])
+        assert np.array_equal(t["q"][b], oracle.rope_apply(before["q"][b], rot, theta, int(posv[b])))
+    # sequence 1 appended its row and nothing else
+    row = oracle.ring_slot(20, W) if lt == workloads.SLIDING else 20
+    assert np.array_equal(t["v"][1, :, row], before["v_new"][1])
+    mask = np.ones(cap, bool)
+    mask[row] = False
+    assert np.array_equal(t["k"][1][:, mask], before["k"][1][:, mask])
+    assert np.array_equal(t["v"][1][:, mask], before["v"][1][:, mask])
+
+
 def _roll_attention(qv, keys, vals, scale):
     """Plain softmax attention over a contiguous window (fp64 torch)."""
     q = torch.from_numpy(oracle.bf16_to_f64(qv))
