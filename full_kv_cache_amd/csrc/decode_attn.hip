@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_chunk_kernel(DecodePara
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
+            const float o = xor32_sum(st.acc[h][e]);
             if (hw == 0) s_red[(wave * G + h) * D + 8 * dl + e] = o;
         }
     if (lane == 0) {
@@ -370,8 +370,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeParams p, StepA
                             d = fmaf(bf16_hi(qw4[e]), bf16_hi(kw4[e]), d);
                         }
                     }
-                    d += __shfl_xor(d, 16, 64);
-                    d += __shfl_xor(d, 32, 64);
+                    d = xor32_sum(xor16_sum(d));
                     if (kg == 0 && mrow < G) ss.s_new[pr * G + mrow] = d * (p.scale_log2 * kLn2);
                     if (mrow == 0) {
 #pragma unroll
@@ -857,7 +856,7 @@ __global__ __launch_bounds__(kPairWaves * 64) void decode_pair_kernel(DecodePara
     for (int h = 0; h < GW; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
+            const float o = xor32_sum(st.acc[h][e]);
             if (hw == 0) s_red[(wave * GW + h) * D + 8 * dl + e] = o;
         }
     if (lane == 0) {

@@ -264,8 +264,7 @@ __global__ __launch_bounds__(kMultiWaves * 64, 1) void decode_multi_kernel(Multi
             s[i] = ok[i] ? (s0[i] + s1[i]) * p.scale_log2 : -INFINITY;
             tmax = fmaxf(tmax, s[i]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = xor32_max(xor16_max(tmax));
         const float m_new = fmaxf(m_run, tmax);
         const float mr = m_new == -INFINITY ? 0.f : m_new;  // no key for this row yet
         const float alpha = __builtin_amdgcn_exp2f(m_run - mr);  // -inf - x: 0
@@ -363,8 +362,7 @@ __global__ __launch_bounds__(kMultiWaves * 64, 1) void decode_multi_kernel(Multi
 
     // merge the waves: each leaves its o rows (unnormalised) in its own
     // tiles, then out / lse per row
-    float l_row = l_lane + __shfl_xor(l_lane, 16, 64);
-    l_row += __shfl_xor(l_row, 32, 64);
+    const float l_row = xor32_sum(xor16_sum(l_lane));
     const bool has = p0 >= 0 && (r_lo < r_hi || last);
     float *red = reinterpret_cast<float *>(s_tile[wave]);
     wave_lds_fence();
@@ -733,8 +731,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, s[e]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = xor32_max(xor16_max(tmax));
         const float m_new = fmaxf(m_run, tmax);
         const float mr = m_new == -INFINITY ? 0.f : m_new;  // no key for this row yet
         const float alpha = __builtin_amdgcn_exp2f(m_run - mr);  // -inf - x: 0
@@ -794,8 +791,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void prefill_chunk_kernel(MultiPa
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loads past the end have landed
 
     // out / lse of this lane's row: dims 16d + 4kg .. +3 of every tile d
-    float l = l_lane + __shfl_xor(l_lane, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = xor32_sum(xor16_sum(l_lane));
     if (my_row >= RG) return;
     if (S > 1) {  // this range's normalised partial and its lse (none: 0 and -inf)
         const int64_t prow = part_row(my_row);

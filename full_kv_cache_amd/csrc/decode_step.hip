@@ -92,7 +92,7 @@ __device__ __forceinline__ void store_partial_coherent(const WaveSoftmax<G> &st,
         const float inv = 1.f / l;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float o = (st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64)) * inv;
+            const float o = xor32_sum(st.acc[h][e]) * inv;
             if (hw == 0) coherent_store(po + h * kHeadDim + 8 * dl + e, o);
         }
         if (lane == 0) coherent_store(plse + h, (m_h[h] + log2f(l)) * kLn2);
@@ -117,8 +117,8 @@ __device__ __forceinline__ void store_final(const WaveSoftmax<G> &st, const Step
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float a = (st.acc[h][2 * e] + __shfl_xor(st.acc[h][2 * e], 32, 64)) * f;
-            const float c = (st.acc[h][2 * e + 1] + __shfl_xor(st.acc[h][2 * e + 1], 32, 64)) * f;
+            const float a = xor32_sum(st.acc[h][2 * e]) * f;
+            const float c = xor32_sum(st.acc[h][2 * e + 1]) * f;
             w[e] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(c) << 16);
         }
         const int64_t row = (int64_t)b * p.num_q_heads + hq;
@@ -796,7 +796,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_window_step_kernel(StepPara
     for (int h = 0; h < GW; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float o = st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64);
+            const float o = xor32_sum(st.acc[h][e]);
             if (hw == 0) red[h * D + 8 * dl + e] = o;
         }
     if (lane == 0) {

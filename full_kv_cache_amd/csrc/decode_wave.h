@@ -421,7 +421,7 @@ __device__ __forceinline__ void store_partial(const WaveSoftmax<G> &st, float *p
         const float inv = 1.f / l;
         float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (st.acc[h][e] + __shfl_xor(st.acc[h][e], 32, 64)) * inv;
+        for (int e = 0; e < 8; ++e) o[e] = xor32_sum(st.acc[h][e]) * inv;
         if (hw == 0) {
             float *dst = po + h * kHeadDim + 8 * dl;
             *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);

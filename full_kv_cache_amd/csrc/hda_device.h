@@ -210,6 +210,27 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Lane l with lane l ^ 16 (or l ^ 32) on the vector ALU: each permlane swap
+// hands a lane both values of its pair (in some order), and a max or a sum
+// does not depend on it -- the same result as a shuffle, without its LDS
+// round trip (which queues behind the other waves' LDS reads).
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // Stands in for the row of a key without one (a zero weight would not
 // cancel a NaN that the row it replaces might hold); 576 bf16, the longest

@@ -208,8 +208,7 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
             s[i] = ((vmask >> (4 * kg + i)) & 1u) ? sc[i] * (p.scale_log2 * rsk[i]) : -INFINITY;
             tmax = fmaxf(tmax, s[i]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = xor32_max(xor16_max(tmax));
         m_max = fmaxf(m_max, tmax);
         if (m_ref == -INFINITY) m_ref = tmax;  // first keys: nothing accumulated yet
         over |= tmax > m_ref + kSlack;
@@ -265,8 +264,7 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
     }
 
     // merge the 4 waves: o = sum_w 2^(m_w - M) o_w, l likewise
-    float l_w = l_lane + __shfl_xor(l_lane, 16, 64);
-    l_w += __shfl_xor(l_w, 32, 64);
+    const float l_w = xor32_sum(xor16_sum(l_lane));
     if (kg == 0) {
         s_m[wave][mrow] = m_ref;
         s_l[wave][mrow] = l_w;
@@ -365,27 +363,6 @@ __global__ __launch_bounds__(kSparseWaves * 64, 1) void sparse_decode_kernel(Spa
 // them; two tiles in flight in registers, two LDS buffers.  A key's scores
 // take its row's scale, and so do the probabilities sent to P.V (the
 // running sum keeps the unscaled ones), as the head-group kernel does.
-
-// Lane l with lane l ^ 16 (or l ^ 32) on the vector ALU: each swap hands a
-// lane both values of its pair (in some order), so max and sum, which do not
-// care about the order, come out alike on both lanes -- no LDS round trip,
-// where a shuffle would queue behind the other waves' operand reads.
-__device__ __forceinline__ float xor16_max(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 constexpr int kTileKeys = 32;
 constexpr int kHalfBytes = 16 * kSparseDqk * 2;  // one 16-row half: 18 blocks of 1 KiB
