@@ -86,10 +86,37 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
     return sgn | v;
 }
 
+// Lane l with lane l ^ 16 (or l ^ 32) on the vector ALU: each permlane swap
+// hands a lane both values of its pair (in some order), and a max or a sum
+// does not depend on it -- the same result as a shuffle, without its LDS
+// round trip (which queues behind the other waves' LDS reads).
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum over the wave: within each row of 16 lanes by DPP moves (the
+// quad swaps, then the half-row and row mirrors), then across the rows by
+// the permlane swaps -- no LDS round trip; a maximum does not depend on
+// the order in which it is taken.
 __device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad [1,0,3,2]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad [2,3,0,1]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // half-row mirror
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row mirror
+    return xor32_max(xor16_max(v));
 }
 
 // One row of 4 * 64 values quantized by a wave (lane = 4 consecutive
@@ -199,37 +226,13 @@ __host__ __device__ __forceinline__ void sincos_angle(float angle, float *c, flo
 __device__ __forceinline__ float gate_factor(float logit) { return 1.f / (1.f + expf(-logit)); }
 
 // Wave64 reductions via butterfly shuffles.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_max64(v); }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
-// Lane l with lane l ^ 16 (or l ^ 32) on the vector ALU: each permlane swap
-// hands a lane both values of its pair (in some order), and a max or a sum
-// does not depend on it -- the same result as a shuffle, without its LDS
-// round trip (which queues behind the other waves' LDS reads).
-__device__ __forceinline__ float xor16_max(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // ---------------------------------------------------------------- LDS tiles
 // Stands in for the row of a key without one (a zero weight would not
